@@ -1,0 +1,197 @@
+/*
+ * ufp4.h -- C ABI of the MI355X (gfx950) UFP4 hot path: fused random
+ * Hadamard transform + blockwise 4-bit quantizer, dequantizer, and the
+ * block-scaled 4-bit GEMMs FPROP / DGRAD / WGRAD (dense and grouped for MoE).
+ *
+ * Pages (cited by title, section and equation):
+ *   [UFP4]  "Rethinking Shrinkage Bias in FP4 Pretraining of LLMs: Geometric
+ *           Origin, Systemic Impact and the UFP4 Recipe" -- hyper.ai summary
+ *           (formats and blockwise quantization; Method) and abstract.
+ *   [2DFP4] "Stable FP4 Training via Transposition-Invariant Block
+ *           Quantization" -- agifrontier tutorial (root cause; 2D square-block
+ *           quantization).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named x, codes, scales, rotated, out, Y, dX, dW are DEVICE
+ *     pointers owned by the caller; arrays named *_offsets are HOST arrays.
+ *     The library allocates no memory, keeps no state between calls and is
+ *     safe to call from several host threads.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Nothing synchronizes inside the library.
+ *   - Every function returns UFP4_OK (0) or a negative status; arguments are
+ *     validated before any HIP call, so a rejected call has no side effect.
+ *     ufp4_status_string() names a status.  Nothing is thrown across the ABI.
+ *   - A "logical operand" A is P x K with K the dimension a GEMM contracts.
+ *     Quantized operands are stored K-contiguous:
+ *       codes  : uint8 [P][K/2]; byte j of a row holds the 4-bit codes of
+ *                elements 2j (low nibble) and 2j+1 (high nibble);
+ *       scales : UFP4_SCALE_F32  -> float [P/block_rows][K/block_cols]
+ *                UFP4_SCALE_POW2 -> uint8 E8M0 [P/block_rows][K/block_cols],
+ *                                   value 2^(byte - 127).
+ *   - Code nibbles: E1M2 and E2M1 are sign-magnitude (sign*8 + level index;
+ *     E2M1 is the OCP FP4 bit pattern), INT4 is two's complement of -7..7;
+ *     zero is always code 0.
+ */
+#ifndef UFP4_H
+#define UFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Codebooks G ([UFP4] formats section; uniform grids in Method):
+ * E1M2 levels {0, +-0.25, ..., +-1.75}, INT4 {-7..7},
+ * E2M1 {0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6}. */
+enum { UFP4_E1M2 = 0, UFP4_INT4 = 1, UFP4_E2M1 = 2 };
+/* Rounding ([UFP4] formats section; [2DFP4] 2D section, E[roundS(x)] = x). */
+enum { UFP4_RTNE = 0, UFP4_SR = 1 };
+/* Scale rule: s_B = absmax / qmax in fp32 ([UFP4] formats section), or the
+ * truncation-free power of two S = 2^ceil(log2(2M / (Qp - Qn))) ([2DFP4]). */
+enum { UFP4_SCALE_F32 = 0, UFP4_SCALE_POW2 = 1 };
+
+enum {
+  UFP4_OK = 0,
+  UFP4_ERR_INVALID_ARG = -1,  /* null pointer, negative size, bad enum     */
+  UFP4_ERR_SHAPE = -2,        /* sizes not divisible by rht_n / blocks      */
+  UFP4_ERR_MISMATCH = -3,     /* GEMM operands disagree (K, rotation, grid) */
+  UFP4_ERR_UNSUPPORTED = -4,  /* valid but not implemented combination      */
+  UFP4_ERR_HIP = -5           /* the HIP runtime reported an error          */
+};
+
+/* Parameters of one quantization.
+ *   grid, rounding, scale_mode : the enums above.
+ *   block_rows x block_cols    : 1 x 16 or 1 x 32 (1D groups along K,
+ *                                [2DFP4] root cause), or 32 x 32 square
+ *                                blocks ([2DFP4] 2D section).
+ *   rht_n     : Hadamard size along K, a power of two in [1, 128]; 1 = no
+ *               rotation ([UFP4] Method, Sylvester recursion).  32 x 32
+ *               blocks accept rht_n <= 32.
+ *   sign_seed : seed of the random sign diagonal S_n ([UFP4] Method, H' = S H).
+ *               Both operands of a GEMM must use the same sign_seed and rht_n.
+ *   sr_seed, sr_stream : key and stream of the stochastic-rounding draws;
+ *               stream 0xFFFFFFFF is reserved.
+ *   reserved  : must be 0. */
+typedef struct ufp4_quant_cfg {
+  int32_t grid;
+  int32_t rounding;
+  int32_t scale_mode;
+  int32_t block_rows;
+  int32_t block_cols;
+  int32_t rht_n;
+  uint64_t sign_seed;
+  uint64_t sr_seed;
+  uint32_t sr_stream;
+  uint32_t reserved;
+} ufp4_quant_cfg;
+
+/* A quantized logical operand (device codes and scales, layout above). */
+typedef struct ufp4_qtensor {
+  const uint8_t* codes;
+  const void* scales;
+  int64_t P;
+  int64_t K;
+  ufp4_quant_cfg cfg;
+} ufp4_qtensor;
+
+/* Fused RHT + blockwise 4-bit quantization of a bf16 matrix.
+ * [UFP4] formats section (block absmax scale, RTNE / SR onto G) and Method
+ * (X H'_n with H'_n = S_n H_n along the shared GEMM dimension).
+ *   x        : bf16 [rows][ld] row-major, ld >= cols.
+ *   along    : 0 -> A = x (P = rows, K = cols), row-wise;
+ *              1 -> A = x^T (P = cols, K = rows), column-wise: the output is
+ *                   the transposed operand, written K-contiguous.
+ *   codes    : uint8 [P][K/2];  scales : see the layout above.
+ *   rotated  : optional fp32 [P][K] copy of the rotated values y = RN(c_n *
+ *              FWHT(S x)) (NULL to skip; not part of the fast path).
+ * The rotation is block-diagonal along K in chunks of rht_n; each chunk and
+ * block lies inside the operand (K % rht_n == 0, K % block_cols == 0,
+ * P % block_rows == 0, else UFP4_ERR_SHAPE).  Stochastic-rounding draw of
+ * element (p, k) is keyed by its index p*K + k.  rows == 0 or cols == 0 is a
+ * no-op. */
+int ufp4_rht_quant(const void* x, int64_t rows, int64_t cols, int64_t ld, int32_t along,
+                   const ufp4_quant_cfg* cfg, uint8_t* codes, void* scales, float* rotated,
+                   void* stream);
+
+/* Column-wise quantization of row segments (per-expert transposed operands).
+ * Segment g is rows [row_offsets[g], row_offsets[g+1]) of x [rows][ld]; it
+ * yields A_g = x[seg]^T of shape [cols][L_g], L_g = segment length, which is
+ * stored at codes + cols*row_offsets[g]/2 as [cols][L_g/2] and at scales +
+ * cols*row_offsets[g]/block_cols elements as [cols][L_g/block_cols].  Draw
+ * indices continue across segments (segment g starts at cols*row_offsets[g]).
+ * row_offsets: HOST int64 [num_segments+1], ascending, 0 .. rows, each
+ * segment length a multiple of lcm(rht_n, block_cols).  1D blocks only;
+ * num_segments <= 256. */
+int ufp4_rht_quant_segmented(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                             const int64_t* row_offsets, int32_t num_segments,
+                             const ufp4_quant_cfg* cfg, uint8_t* codes, void* scales,
+                             void* stream);
+
+/* Dequantization Q_G(T) ([UFP4] formats section: a quantized tensor stands
+ * for level * block scale), in the rotated basis: out[p][k] =
+ * RN_fp32(level(code) * s_B), written to out [P][ldo] (ldo >= K). */
+int ufp4_dequant(const ufp4_qtensor* q, float* out, int64_t ldo, void* stream);
+
+/* Block-scaled 4-bit GEMMs ([UFP4] Method: Y^ = Q(X H') Q(W H')^T, the
+ * rotation cancels on the shared dimension; [2DFP4] root cause: dX = dY W,
+ * dW = dY^T X).  Each computes C[p][q] = sum_k A[p][k] * B[q][k] over the
+ * dequantized codes, accumulating in fp32, and writes fp32 C [P_A][ldc].
+ *   fprop: A = X  (M x K_in),  B = W   (N x K_in)    -> Y  [M][N]
+ *   dgrad: A = dY (M x N),     B = W^T (K_in x N)    -> dX [M][K_in]
+ *   wgrad: A = dY^T (N x M),   B = X^T (K_in x M)    -> dW [N][K_in]
+ * Operands must agree on K, grid, scale_mode, rht_n and sign_seed
+ * (UFP4_ERR_MISMATCH otherwise).  Block shapes may differ between operands. */
+int ufp4_gemm_fprop(const ufp4_qtensor* X, const ufp4_qtensor* W, float* Y, int64_t ldy,
+                    void* stream);
+int ufp4_gemm_dgrad(const ufp4_qtensor* dY, const ufp4_qtensor* Wt, float* dX, int64_t ldx,
+                    void* stream);
+int ufp4_gemm_wgrad(const ufp4_qtensor* dYt, const ufp4_qtensor* Xt, float* dW, int64_t ldw,
+                    void* stream);
+
+/* Grouped (MoE expert) GEMMs in one launch.  offsets: HOST int64 [G+1], the
+ * padded token offsets of the experts in the expert-sorted token matrix
+ * (0 = offsets[0] <= ... <= offsets[G] = T); G <= 64.
+ *   fprop_grouped: A = X_perm [T][K_in], B = W stacked [G*N][K_in]
+ *                  (expert g = rows g*N ..), Y [T][ldy]: Y_g = X_g W_g^T.
+ *   dgrad_grouped: A = dY_perm [T][N], B = W^T stacked [G*K_in][N] (the
+ *                  segmented column-wise quantization of W [G*N][K_in] with
+ *                  offsets g*N), dX [T][ldx]: dX_g = dY_g W_g.
+ *   wgrad_grouped: A = dY^T segments (ufp4_rht_quant_segmented of dY_perm,
+ *                  P = N, K = T), B = X^T segments (of X_perm, P = K_in,
+ *                  K = T), dW stacked [G*N][ldw]: dW_g = dY_g^T X_g.
+ * The per-group B row count is B->P / G. */
+int ufp4_gemm_fprop_grouped(const ufp4_qtensor* Xp, const ufp4_qtensor* W, int32_t G,
+                            const int64_t* offsets, float* Y, int64_t ldy, void* stream);
+int ufp4_gemm_dgrad_grouped(const ufp4_qtensor* dYp, const ufp4_qtensor* Wt, int32_t G,
+                            const int64_t* offsets, float* dX, int64_t ldx, void* stream);
+int ufp4_gemm_wgrad_grouped(const ufp4_qtensor* dYt, const ufp4_qtensor* Xt, int32_t G,
+                            const int64_t* offsets, float* dW, int64_t ldw, void* stream);
+
+/* Transpose of a quantized operand whose blocks are square (2D mode): the
+ * codes of A^T are the transposed codes and, because S(B) = S(B^T) for
+ * square blocks ([2DFP4] 2D section), its scale grid is the transposed grid.
+ * dst_codes [K][P/2], dst_scales [K/b][P/b].  P and K must be multiples of
+ * the block size and of 2; rht_n must be 1. */
+int ufp4_transpose_qtensor(const ufp4_qtensor* src, uint8_t* dst_codes, void* dst_scales,
+                           void* stream);
+
+/* Size helpers (bytes) for caller allocation. */
+size_t ufp4_codes_bytes(int64_t P, int64_t K);
+size_t ufp4_scales_bytes(int64_t P, int64_t K, const ufp4_quant_cfg* cfg);
+
+/* The 16-bit stochastic-rounding draws for elements first .. first+n-1 under
+ * (seed, stream), written to out [n] (device uint16).  Exposes the device
+ * generator so it can be checked on its own. */
+int ufp4_philox_fill(uint64_t seed, uint32_t stream_id, uint64_t first, int64_t n,
+                     uint16_t* out, void* stream);
+
+/* Name of a status code (static string). */
+const char* ufp4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UFP4_H */

@@ -1,0 +1,298 @@
+"""Python binding of the UFP4 hot-path library (librht_ufp4.so, C ABI in
+include/ufp4.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the path runs in the library's HIP kernels.  There is
+no CPU fallback -- if the library is missing, every call raises.
+
+Functions carry the C names (ufp4_rht_quant, ufp4_gemm_fprop, ...).  Outputs
+that the caller does not pass are allocated with torch on the input's device.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librht_ufp4.so")
+
+UFP4_E1M2, UFP4_INT4, UFP4_E2M1 = 0, 1, 2
+UFP4_RTNE, UFP4_SR = 0, 1
+UFP4_SCALE_F32, UFP4_SCALE_POW2 = 0, 1
+UFP4_OK, UFP4_ERR_INVALID_ARG, UFP4_ERR_SHAPE = 0, -1, -2
+UFP4_ERR_MISMATCH, UFP4_ERR_UNSUPPORTED, UFP4_ERR_HIP = -3, -4, -5
+
+EXPORTED = [
+    "ufp4_rht_quant", "ufp4_rht_quant_segmented", "ufp4_dequant",
+    "ufp4_gemm_fprop", "ufp4_gemm_dgrad", "ufp4_gemm_wgrad",
+    "ufp4_gemm_fprop_grouped", "ufp4_gemm_dgrad_grouped", "ufp4_gemm_wgrad_grouped",
+    "ufp4_transpose_qtensor", "ufp4_codes_bytes", "ufp4_scales_bytes",
+    "ufp4_philox_fill", "ufp4_status_string",
+]
+
+
+class UFP4Error(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        msg = _lib().ufp4_status_string(status).decode()
+        super().__init__(f"{fn} failed: {msg} ({status})")
+
+
+class QuantCfg(ctypes.Structure):
+    _fields_ = [("grid", ctypes.c_int32), ("rounding", ctypes.c_int32),
+                ("scale_mode", ctypes.c_int32), ("block_rows", ctypes.c_int32),
+                ("block_cols", ctypes.c_int32), ("rht_n", ctypes.c_int32),
+                ("sign_seed", ctypes.c_uint64), ("sr_seed", ctypes.c_uint64),
+                ("sr_stream", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+    def copy(self, **kw):
+        c = QuantCfg()
+        ctypes.memmove(ctypes.byref(c), ctypes.byref(self), ctypes.sizeof(QuantCfg))
+        for k, v in kw.items():
+            setattr(c, k, v)
+        return c
+
+
+def make_cfg(grid=UFP4_E1M2, rounding=UFP4_RTNE, scale_mode=UFP4_SCALE_F32, block_rows=1,
+             block_cols=16, rht_n=16, sign_seed=0, sr_seed=0, sr_stream=0):
+    return QuantCfg(int(grid), int(rounding), int(scale_mode), int(block_rows), int(block_cols),
+                    int(rht_n), int(sign_seed), int(sr_seed), int(sr_stream), 0)
+
+
+class QTensorC(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("P", ctypes.c_int64), ("K", ctypes.c_int64), ("cfg", QuantCfg)]
+
+
+@dataclass
+class QTensor:
+    """A quantized logical operand: codes uint8 [P, K/2], scales (fp32 or
+    E8M0 uint8) per block, both on the GPU."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    P: int
+    K: int
+    cfg: QuantCfg
+
+    def c(self):
+        return QTensorC(self.codes.data_ptr(), self.scales.data_ptr(), self.P, self.K, self.cfg)
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() or "
+                               "python -m rht_bit_block_amd.build")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, u64, u32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                  ctypes.c_uint64, ctypes.c_uint32)
+        cfgp, qtp = ctypes.POINTER(QuantCfg), ctypes.POINTER(QTensorC)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        sig = {
+            "ufp4_rht_quant": [vp, i64, i64, i64, i32, cfgp, vp, vp, vp, vp],
+            "ufp4_rht_quant_segmented": [vp, i64, i64, i64, i64p, i32, cfgp, vp, vp, vp],
+            "ufp4_dequant": [qtp, vp, i64, vp],
+            "ufp4_gemm_fprop": [qtp, qtp, vp, i64, vp],
+            "ufp4_gemm_dgrad": [qtp, qtp, vp, i64, vp],
+            "ufp4_gemm_wgrad": [qtp, qtp, vp, i64, vp],
+            "ufp4_gemm_fprop_grouped": [qtp, qtp, i32, i64p, vp, i64, vp],
+            "ufp4_gemm_dgrad_grouped": [qtp, qtp, i32, i64p, vp, i64, vp],
+            "ufp4_gemm_wgrad_grouped": [qtp, qtp, i32, i64p, vp, i64, vp],
+            "ufp4_transpose_qtensor": [qtp, vp, vp, vp],
+            "ufp4_philox_fill": [u64, u32, u64, i64, vp, vp],
+        }
+        for name, args in sig.items():
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        lib.ufp4_codes_bytes.argtypes = [i64, i64]
+        lib.ufp4_codes_bytes.restype = ctypes.c_size_t
+        lib.ufp4_scales_bytes.argtypes = [i64, i64, cfgp]
+        lib.ufp4_scales_bytes.restype = ctypes.c_size_t
+        lib.ufp4_status_string.argtypes = [ctypes.c_int]
+        lib.ufp4_status_string.restype = ctypes.c_char_p
+        _LIB = lib
+    return _LIB
+
+
+def lib_handle():
+    """The loaded ctypes library (raises if it is not built)."""
+    return _lib()
+
+
+def _check(fn, st):
+    if st != UFP4_OK:
+        raise UFP4Error(fn, st)
+
+
+def _stream(t: Optional[torch.Tensor] = None):
+    if t is not None and t.is_cuda:
+        return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _i64arr(vals: Sequence[int]):
+    arr = (ctypes.c_int64 * len(vals))(*[int(v) for v in vals])
+    return arr
+
+
+def scales_shape(P, K, cfg):
+    return (P // cfg.block_rows, K // cfg.block_cols)
+
+
+def scales_dtype(cfg):
+    return torch.float32 if cfg.scale_mode == UFP4_SCALE_F32 else torch.uint8
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def ufp4_rht_quant(x: torch.Tensor, along: int, cfg: QuantCfg, codes=None, scales=None,
+                   rotated=False, ld: Optional[int] = None):
+    """Quantize bf16 x [rows, cols] (row-major, row pitch ld).  Returns
+    (QTensor, rotated fp32 [P, K] or None)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    rows, cols = x.shape
+    ld = x.stride(0) if ld is None else ld
+    if x.stride(1) != 1:
+        raise ValueError("x must be row-major (unit column stride)")
+    P, K = (cols, rows) if along else (rows, cols)
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((P, K // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(scales_shape(P, K, cfg), dtype=scales_dtype(cfg), device=dev)
+    rot = torch.empty((P, K), dtype=torch.float32, device=dev) if rotated is True else (
+        rotated if isinstance(rotated, torch.Tensor) else None)
+    st = _lib().ufp4_rht_quant(_ptr(x), rows, cols, ld, int(along), ctypes.byref(cfg),
+                               _ptr(codes), _ptr(scales), _ptr(rot), _stream(x))
+    _check("ufp4_rht_quant", st)
+    return QTensor(codes, scales, P, K, cfg), rot
+
+
+def ufp4_rht_quant_segmented(x: torch.Tensor, row_offsets: Sequence[int], cfg: QuantCfg,
+                             codes=None, scales=None):
+    """Column-wise quantization of row segments of x (per-expert transposed
+    operands).  Returns a QTensor with P = cols and K = rows whose storage is
+    segment-major (segment g: [cols, L_g] at element offset cols*offset_g)."""
+    rows, cols = x.shape
+    dev = x.device
+    if codes is None:
+        codes = torch.empty(cols * rows // 2, dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(cols * rows // cfg.block_cols, dtype=scales_dtype(cfg), device=dev)
+    off = _i64arr(row_offsets)
+    st = _lib().ufp4_rht_quant_segmented(_ptr(x), rows, cols, x.stride(0), off,
+                                         len(row_offsets) - 1, ctypes.byref(cfg), _ptr(codes),
+                                         _ptr(scales), _stream(x))
+    _check("ufp4_rht_quant_segmented", st)
+    return QTensor(codes, scales, cols, rows, cfg)
+
+
+def stacked(q: QTensor, groups: int) -> QTensor:
+    """View a segmented column-wise quantization with equal segments (e.g.
+    W^T of every expert) as one operand stacked along P: [G*cols, L]."""
+    return QTensor(q.codes, q.scales, q.P * groups, q.K // groups, q.cfg)
+
+
+def ufp4_dequant(q: QTensor, out=None):
+    if out is None:
+        out = torch.empty((q.P, q.K), dtype=torch.float32, device=q.codes.device)
+    qc = q.c()
+    st = _lib().ufp4_dequant(ctypes.byref(qc), _ptr(out), out.stride(0), _stream(out))
+    _check("ufp4_dequant", st)
+    return out
+
+
+def _gemm(name, A: QTensor, B: QTensor, out=None):
+    if out is None:
+        out = torch.empty((A.P, B.P), dtype=torch.float32, device=A.codes.device)
+    a, b = A.c(), B.c()
+    st = getattr(_lib(), name)(ctypes.byref(a), ctypes.byref(b), _ptr(out), out.stride(0),
+                               _stream(out))
+    _check(name, st)
+    return out
+
+
+def ufp4_gemm_fprop(X: QTensor, W: QTensor, out=None):
+    """Y = X W^T on the quantized rotated operands (fp32 [M, N])."""
+    return _gemm("ufp4_gemm_fprop", X, W, out)
+
+
+def ufp4_gemm_dgrad(dY: QTensor, Wt: QTensor, out=None):
+    """dX = dY W, with Wt the column-wise quantization of W (fp32 [M, K_in])."""
+    return _gemm("ufp4_gemm_dgrad", dY, Wt, out)
+
+
+def ufp4_gemm_wgrad(dYt: QTensor, Xt: QTensor, out=None):
+    """dW = dY^T X from the column-wise quantizations of dY and X (fp32 [N, K_in])."""
+    return _gemm("ufp4_gemm_wgrad", dYt, Xt, out)
+
+
+def _gemm_grouped(name, A: QTensor, B: QTensor, offsets, rows, cols, out=None):
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=A.codes.device)
+    a, b = A.c(), B.c()
+    off = _i64arr(offsets)
+    st = getattr(_lib(), name)(ctypes.byref(a), ctypes.byref(b), len(offsets) - 1, off,
+                               _ptr(out), out.stride(0), _stream(out))
+    _check(name, st)
+    return out
+
+
+def ufp4_gemm_fprop_grouped(Xp: QTensor, W: QTensor, offsets, out=None):
+    G = len(offsets) - 1
+    return _gemm_grouped("ufp4_gemm_fprop_grouped", Xp, W, offsets, Xp.P, W.P // G, out)
+
+
+def ufp4_gemm_dgrad_grouped(dYp: QTensor, Wt: QTensor, offsets, out=None):
+    G = len(offsets) - 1
+    return _gemm_grouped("ufp4_gemm_dgrad_grouped", dYp, Wt, offsets, dYp.P, Wt.P // G, out)
+
+
+def ufp4_gemm_wgrad_grouped(dYt: QTensor, Xt: QTensor, offsets, out=None):
+    G = len(offsets) - 1
+    return _gemm_grouped("ufp4_gemm_wgrad_grouped", dYt, Xt, offsets, G * dYt.P, Xt.P, out)
+
+
+def ufp4_transpose_qtensor(q: QTensor):
+    dev = q.codes.device
+    codes = torch.empty((q.K, q.P // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((q.K // q.cfg.block_cols, q.P // q.cfg.block_rows),
+                         dtype=q.scales.dtype, device=dev)
+    qc = q.c()
+    st = _lib().ufp4_transpose_qtensor(ctypes.byref(qc), _ptr(codes), _ptr(scales),
+                                       _stream(codes))
+    _check("ufp4_transpose_qtensor", st)
+    return QTensor(codes, scales, q.K, q.P, q.cfg)
+
+
+def ufp4_philox_fill(seed, stream_id, first, n, device="cuda"):
+    out = torch.empty(n, dtype=torch.int16, device=device)
+    st = _lib().ufp4_philox_fill(int(seed), int(stream_id), int(first), int(n), _ptr(out),
+                                 _stream(out))
+    _check("ufp4_philox_fill", st)
+    return out
+
+
+def ufp4_codes_bytes(P, K):
+    return int(_lib().ufp4_codes_bytes(int(P), int(K)))
+
+
+def ufp4_scales_bytes(P, K, cfg):
+    return int(_lib().ufp4_scales_bytes(int(P), int(K), ctypes.byref(cfg)))
+
+
+def ufp4_status_string(status):
+    return _lib().ufp4_status_string(int(status)).decode()

@@ -1,0 +1,102 @@
+// Internal interface between the C-ABI layer (api.cpp: validation, planning)
+// and the HIP kernels (quant.hip, gemm.hip, misc.hip).  Host-visible structs
+// only; every pointer is a device pointer unless named host_*.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ufp4 {
+
+constexpr int kMaxSegments = 128;  // segments per segmented quantization launch
+constexpr int kMaxGroups = 64;     // groups per grouped GEMM launch
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
+// as 1, 2, 3", SC'11): ten rounds of the 4x32 Philox S-box with the Weyl key
+// schedule.  Usable on host (sign draw) and device (stochastic rounding).
+__host__ __device__ inline void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+    const uint32_t n1 = (uint32_t)p1;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+    const uint32_t n3 = (uint32_t)p0;
+    c[0] = n0; c[1] = n1; c[2] = n2; c[3] = n3;
+  }
+}
+
+// Unsigned 32-bit division by a launch constant d >= 1, as a multiply-high
+// (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", PLDI'94): q = (umulhi(m, n) + n) >> l with l = ceil(log2 d),
+// m = floor(2^32 (2^l - d) / d) + 1, exact for every 32-bit n.
+struct FastDiv {
+  uint32_t d, m, l;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+  return FastDiv{d, (uint32_t)m, l};
+}
+
+struct QuantLaunch {
+  const uint16_t* x;
+  int64_t ld;        // row pitch of x in elements
+  int64_t rows;      // rows of x (segmented / column-wise: K extent)
+  int64_t cols;      // columns of x
+  int64_t P, K;      // logical operand (dense calls)
+  uint8_t* codes;
+  void* scales;
+  float* rotated;
+  uint32_t sign_pat[4];  // sign bits of chunk positions 32i..32i+31
+  float cn;              // RN(1/sqrt(n))
+  int32_t n;
+  int32_t grid, rounding, scale_mode, br, bc;
+  uint64_t sr_seed;
+  uint32_t sr_stream;
+  // segmented column-wise
+  int32_t nseg;
+  int64_t seg_off[kMaxSegments + 1];
+  int32_t tile_start[kMaxSegments + 1];
+};
+
+hipError_t launch_quant_rows(const QuantLaunch& q, hipStream_t s);
+hipError_t launch_quant_cols(const QuantLaunch& q, hipStream_t s);
+hipError_t launch_quant_rows_2d(const QuantLaunch& q, hipStream_t s);
+
+struct GemmLaunch {
+  const uint8_t* a_codes;
+  const void* a_scales;
+  const uint8_t* b_codes;
+  const void* b_scales;
+  float* c;
+  int64_t ldc;
+  int32_t a_br, a_bc, b_br, b_bc;
+  int32_t grid, scale_mode;
+  int32_t mode;     // 0 dense, 1 grouped along A rows, 2 grouped along K
+  int32_t ngroups;
+  int64_t PA, PB, K;
+  int64_t b_rows_per_group;
+  int64_t off[kMaxGroups + 1];
+  int32_t tile_start[kMaxGroups + 1];
+  int32_t total_tiles;
+};
+
+hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s);
+
+hipError_t launch_dequant(const uint8_t* codes, const void* scales, int64_t P, int64_t K,
+                          int32_t grid, int32_t scale_mode, int32_t br, int32_t bc, float* out,
+                          int64_t ldo, hipStream_t s);
+hipError_t launch_transpose(const uint8_t* codes, const void* scales, int64_t P, int64_t K,
+                            int32_t b, int32_t scale_mode, uint8_t* dcodes, void* dscales,
+                            hipStream_t s);
+hipError_t launch_philox_fill(uint64_t seed, uint32_t stream_id, uint64_t first, int64_t n,
+                              uint16_t* out, hipStream_t s);
+
+}  // namespace ufp4

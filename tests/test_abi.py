@@ -1,0 +1,151 @@
+"""The C-ABI library on the CPU: it loads without a GPU, exports every symbol
+include/ufp4.h declares, its structs match the header's layout, and every
+argument error is rejected before any HIP call (so these run anywhere)."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import rht_bit_block_amd as U
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ufp4.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(U.LIB_PATH), reason="library not built")
+
+FAKE = 0x10000  # aligned, never dereferenced: validation rejects first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ufp4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = U.lib_handle()
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(U.EXPORTED) == names
+
+
+def test_struct_layout_matches_header():
+    src = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "ufp4.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(ufp4_quant_cfg), offsetof(ufp4_quant_cfg, sign_seed),
+         offsetof(ufp4_quant_cfg, sr_stream), sizeof(ufp4_qtensor), offsetof(ufp4_qtensor, P),
+         offsetof(ufp4_qtensor, cfg));
+  return 0;
+}
+"""
+    d = tempfile.mkdtemp()
+    c = os.path.join(d, "layout.c")
+    open(c, "w").write(src)
+    exe = os.path.join(d, "layout")
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+    got = [int(v) for v in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
+    want = [ctypes.sizeof(U.QuantCfg), U.QuantCfg.sign_seed.offset, U.QuantCfg.sr_stream.offset,
+            ctypes.sizeof(U.QTensorC), U.QTensorC.P.offset, U.QTensorC.cfg.offset]
+    assert got == want
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4, -5):
+        assert U.ufp4_status_string(st) != "unknown status"
+    assert U.ufp4_status_string(-99) == "unknown status"
+
+
+def _quant(lib, rows=64, cols=64, ld=64, along=0, cfg=None, x=FAKE, codes=FAKE, scales=FAKE):
+    cfg = cfg or U.make_cfg()
+    return lib.ufp4_rht_quant(ctypes.c_void_p(x), rows, cols, ld, along, ctypes.byref(cfg),
+                              ctypes.c_void_p(codes), ctypes.c_void_p(scales), None, None)
+
+
+def test_quant_argument_errors():
+    lib = U.lib_handle()
+    E = U
+    assert _quant(lib, x=0) == E.UFP4_ERR_INVALID_ARG
+    assert _quant(lib, codes=0) == E.UFP4_ERR_INVALID_ARG
+    assert _quant(lib, rows=-1) == E.UFP4_ERR_INVALID_ARG
+    assert _quant(lib, ld=32) == E.UFP4_ERR_INVALID_ARG            # ld < cols
+    assert _quant(lib, along=2) == E.UFP4_ERR_INVALID_ARG
+    assert _quant(lib, x=FAKE + 2) == E.UFP4_ERR_INVALID_ARG       # misaligned
+    assert _quant(lib, cfg=U.make_cfg(grid=3)) == E.UFP4_ERR_INVALID_ARG
+    assert _quant(lib, cfg=U.make_cfg(rht_n=24)) == E.UFP4_ERR_SHAPE
+    assert _quant(lib, cfg=U.make_cfg(rht_n=256)) == E.UFP4_ERR_SHAPE
+    assert _quant(lib, cols=48, ld=48, cfg=U.make_cfg(rht_n=32, block_cols=16)) == E.UFP4_ERR_SHAPE
+    assert _quant(lib, cols=40, ld=48) == E.UFP4_ERR_SHAPE          # K % 16
+    assert _quant(lib, cfg=U.make_cfg(block_cols=8)) == E.UFP4_ERR_UNSUPPORTED
+    assert _quant(lib, cfg=U.make_cfg(sr_stream=0xFFFFFFFF)) == E.UFP4_ERR_UNSUPPORTED
+    two_d = U.make_cfg(grid=U.UFP4_E2M1, scale_mode=U.UFP4_SCALE_POW2, block_rows=32,
+                       block_cols=32, rht_n=1)
+    assert _quant(lib, along=1, cfg=two_d) == E.UFP4_ERR_UNSUPPORTED
+    assert _quant(lib, rows=48, cfg=two_d) == E.UFP4_ERR_SHAPE      # P % 32
+    bad = two_d.copy(scale_mode=U.UFP4_SCALE_F32)
+    assert _quant(lib, cfg=bad) == E.UFP4_ERR_UNSUPPORTED
+    # empty inputs are a successful no-op (no HIP call is made)
+    assert _quant(lib, rows=0) == E.UFP4_OK
+    assert _quant(lib, cols=0, ld=0) == E.UFP4_OK
+
+
+def _qt(P, K, cfg=None, codes=FAKE, scales=FAKE):
+    return U.QTensorC(codes, scales, P, K, cfg or U.make_cfg())
+
+
+def test_gemm_argument_errors():
+    lib = U.lib_handle()
+    a, b = _qt(64, 64), _qt(32, 64)
+    f = lib.ufp4_gemm_fprop
+    assert f(None, ctypes.byref(b), ctypes.c_void_p(FAKE), 32, None) == U.UFP4_ERR_INVALID_ARG
+    assert f(ctypes.byref(a), ctypes.byref(b), None, 32, None) == U.UFP4_ERR_INVALID_ARG
+    assert f(ctypes.byref(a), ctypes.byref(b), ctypes.c_void_p(FAKE), 16, None) == U.UFP4_ERR_INVALID_ARG
+    bk = _qt(32, 128)
+    assert f(ctypes.byref(a), ctypes.byref(bk), ctypes.c_void_p(FAKE), 32, None) == U.UFP4_ERR_MISMATCH
+    for kw in ({"grid": U.UFP4_INT4}, {"rht_n": 32}, {"sign_seed": 5}):
+        bm = _qt(32, 64, U.make_cfg(**kw))
+        assert f(ctypes.byref(a), ctypes.byref(bm), ctypes.c_void_p(FAKE), 32, None) == U.UFP4_ERR_MISMATCH
+    # sign seeds may differ when there is no rotation
+    a1, b1 = _qt(0, 64, U.make_cfg(rht_n=1, sign_seed=1)), _qt(32, 64, U.make_cfg(rht_n=1, sign_seed=2))
+    assert f(ctypes.byref(a1), ctypes.byref(b1), ctypes.c_void_p(FAKE), 32, None) == U.UFP4_OK
+    # grouped: offsets must start at 0, end at P, ascend, G in [1, 64]
+    g = lib.ufp4_gemm_fprop_grouped
+    wb = _qt(4 * 32, 64)
+    ok_off = (ctypes.c_int64 * 5)(0, 16, 16, 48, 64)
+    bad_off = (ctypes.c_int64 * 5)(0, 32, 16, 48, 64)
+    assert g(ctypes.byref(a), ctypes.byref(wb), 4, bad_off, ctypes.c_void_p(FAKE), 32, None) == U.UFP4_ERR_INVALID_ARG
+    assert g(ctypes.byref(a), ctypes.byref(wb), 65, ok_off, ctypes.c_void_p(FAKE), 32, None) == U.UFP4_ERR_INVALID_ARG
+    assert g(ctypes.byref(a), ctypes.byref(_qt(3 * 32 + 1, 64)), 4, ok_off, ctypes.c_void_p(FAKE), 32, None) == U.UFP4_ERR_SHAPE
+
+
+def test_segmented_and_misc_errors():
+    lib = U.lib_handle()
+    cfg = U.make_cfg(rht_n=32, block_cols=32)
+    off = (ctypes.c_int64 * 3)(0, 48, 96)                      # 48 % 32 != 0
+    st = lib.ufp4_rht_quant_segmented(ctypes.c_void_p(FAKE), 96, 64, 64, off, 2, ctypes.byref(cfg),
+                                      ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None)
+    assert st == U.UFP4_ERR_SHAPE
+    off2 = (ctypes.c_int64 * 3)(0, 32, 64)                     # does not end at rows
+    st = lib.ufp4_rht_quant_segmented(ctypes.c_void_p(FAKE), 96, 64, 64, off2, 2, ctypes.byref(cfg),
+                                      ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None)
+    assert st == U.UFP4_ERR_INVALID_ARG
+    assert lib.ufp4_philox_fill(1, 0xFFFFFFFF, 0, 8, ctypes.c_void_p(FAKE), None) == U.UFP4_ERR_UNSUPPORTED
+    assert lib.ufp4_philox_fill(1, 0, 0, -1, ctypes.c_void_p(FAKE), None) == U.UFP4_ERR_INVALID_ARG
+    q = _qt(64, 64)                                            # 1D blocks cannot be transposed
+    assert lib.ufp4_transpose_qtensor(ctypes.byref(q), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None) == U.UFP4_ERR_UNSUPPORTED
+    assert lib.ufp4_dequant(ctypes.byref(q), None, 64, None) == U.UFP4_ERR_INVALID_ARG
+
+
+def test_size_helpers():
+    cfg = U.make_cfg()
+    assert U.ufp4_codes_bytes(8192, 2048) == 8192 * 1024
+    assert U.ufp4_scales_bytes(8192, 2048, cfg) == 8192 * 128 * 4
+    c2 = U.make_cfg(scale_mode=U.UFP4_SCALE_POW2, block_rows=32, block_cols=32, rht_n=1)
+    assert U.ufp4_scales_bytes(4096, 4096, c2) == 128 * 128

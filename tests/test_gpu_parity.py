@@ -1,0 +1,240 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle at sizes the
+oracle finishes in seconds: several tiles / waves plus ragged tails, every
+grid, rounding, Hadamard size and block shape, edge values, dequant, the
+GEMMs (dense and grouped), the 2D transpose and the draw generator.
+
+Bar: bit-exact rotated values, scales, codes, draws and dequant; GEMMs within
+1e-4 relative Frobenius error of the oracle's fp64 product of its own
+dequantized operands."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import rht_bit_block_amd as U
+from gpu_helpers import (GEMM_TOL, GRIDS, compare_quant, dev_bf16, f32_bits_equal,
+                         oracle_dequant64, rand_bits, spec_of)
+
+pytestmark = pytest.mark.gpu
+
+NB = [(1, 16), (2, 16), (16, 16), (32, 16), (64, 16), (128, 16), (1, 32), (16, 32), (32, 32),
+      (128, 32)]
+
+
+def _print_case(*a):
+    print("case:", *a, flush=True)
+
+
+def test_philox_fill_matches_oracle():
+    for seed, stream, first, n in [(2201, 0, 0, 4096), (2201, 1, 12345, 1000), (2 ** 63 + 5, 7, 2 ** 40 + 3, 777)]:
+        _print_case("philox", seed, stream, first, n)
+        got = U.ufp4_philox_fill(seed, stream, first, n).cpu().numpy().view(np.uint16)
+        want = O.sr_draws(seed, stream, np.arange(first, first + n, dtype=np.uint64))
+        assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("n,b", NB)
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("rnd", [U.UFP4_RTNE, U.UFP4_SR])
+def test_quant_rows(n, b, grid, rnd):
+    _print_case("rows", n, b, grid, rnd)
+    bits = rand_bits(40, 384, seed=n * 7 + b + grid)      # 40 rows: ragged against 64-lane waves
+    cfg = U.make_cfg(grid, rnd, U.UFP4_SCALE_F32, 1, b, n, sign_seed=1000 + n, sr_seed=77, sr_stream=3)
+    compare_quant(bits, 0, cfg)
+
+
+@pytest.mark.parametrize("n,b", NB)
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("rnd", [U.UFP4_RTNE, U.UFP4_SR])
+def test_quant_cols(n, b, grid, rnd):
+    _print_case("cols", n, b, grid, rnd)
+    bits = rand_bits(384, 72, seed=n * 11 + b + grid)     # K = 384 (3 LDS tiles), P = 72 (ragged)
+    cfg = U.make_cfg(grid, rnd, U.UFP4_SCALE_F32, 1, b, n, sign_seed=2000 + n, sr_seed=78, sr_stream=4)
+    compare_quant(bits, 1, cfg)
+
+
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("rnd", [U.UFP4_RTNE, U.UFP4_SR])
+@pytest.mark.parametrize("n", [1, 16, 32])
+def test_quant_2d(grid, rnd, n):
+    _print_case("2d", grid, rnd, n)
+    bits = rand_bits(96, 160, seed=grid + 10 * rnd + n)   # K/32 = 5: odd block count
+    cfg = U.make_cfg(grid, rnd, U.UFP4_SCALE_POW2, 32, 32, n, sign_seed=5, sr_seed=5201)
+    compare_quant(bits, 0, cfg)
+
+
+def _edge_bits():
+    """Zeros, a zero block, subnormal and tiny values, huge values, exact grid
+    ties after scaling, and +-qmax multiples."""
+    rng = np.random.default_rng(99)
+    a = rng.standard_normal((64, 256)).astype(np.float32)
+    a[0] = 0.0                                            # all-zero row
+    a[1, :32] = 0.0                                       # zero blocks inside a row
+    a[2] = rng.standard_normal(256).astype(np.float32) * np.float32(1e-39)   # subnormals
+    a[3] = rng.standard_normal(256).astype(np.float32) * np.float32(1e-30)
+    a[4] = rng.standard_normal(256).astype(np.float32) * np.float32(1e30)
+    a[5] = np.tile(np.arange(16, dtype=np.float32) / 2.0, 16)               # many exact ties
+    a[6] = np.tile(np.array([7, -7, 3.5, -3.5, 0.5, 1.5, 2.5, 6, 5, -5, 1, 0, 0, 0, 0.25, 7],
+                            dtype=np.float32), 16)
+    a[7, ::2] = 0.0                                       # half zeros
+    a[8] = np.float32(1.0)                                # constant rows
+    a[9] = -np.float32(3.0)
+    a[10:12] *= np.float32(2.0 ** -100)
+    return torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("rnd", [U.UFP4_RTNE, U.UFP4_SR])
+@pytest.mark.parametrize("n", [1, 16, 128])
+def test_quant_edge_values(grid, rnd, n):
+    _print_case("edge", grid, rnd, n)
+    bits = _edge_bits()
+    cfg = U.make_cfg(grid, rnd, U.UFP4_SCALE_F32, 1, 16, n, sign_seed=3, sr_seed=4, sr_stream=0)
+    compare_quant(bits, 0, cfg)
+    compare_quant(bits, 1, cfg.copy(rht_n=min(n, 64)))     # K = 64 rows along the columns
+    cfg2 = U.make_cfg(grid, rnd, U.UFP4_SCALE_POW2, 32, 32, min(n, 32), sign_seed=3, sr_seed=4)
+    compare_quant(bits, 0, cfg2)
+
+
+def test_quant_empty():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    q, _ = U.ufp4_rht_quant(x, 0, U.make_cfg())
+    assert q.codes.numel() == 0
+
+
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("two_d", [False, True])
+def test_dequant_bit_exact(grid, two_d):
+    _print_case("dequant", grid, two_d)
+    bits = rand_bits(64, 192, seed=grid)
+    cfg = (U.make_cfg(grid, U.UFP4_SR, U.UFP4_SCALE_POW2, 32, 32, 1, sr_seed=9) if two_d
+           else U.make_cfg(grid, U.UFP4_SR, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=8, sr_seed=9))
+    q, ref = compare_quant(bits, 0, cfg, with_rotated=False)
+    d = U.ufp4_dequant(q).cpu().numpy()
+    want = O.dequant(ref["codes"], ref["scales"], spec_of(cfg), 64, 192)[0]
+    assert f32_bits_equal(d, want)
+
+
+def _gemm_case(PA, PB, K, cfg_a, cfg_b, seed):
+    ta = rand_bits(PA, K, seed)
+    tb = rand_bits(PB, K, seed + 1)
+    qa, ra = compare_quant(ta, 0, cfg_a, with_rotated=False)
+    qb, rb = compare_quant(tb, 0, cfg_b, with_rotated=False)
+    C = U.ufp4_gemm_fprop(qa, qb).cpu().numpy()
+    ref = O.gemm_ref(oracle_dequant64(ra, cfg_a), oracle_dequant64(rb, cfg_b))
+    err = O.rel_fro(C, ref)
+    assert err <= GEMM_TOL, err
+    return err
+
+
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("shape", [(256, 256, 256), (300, 270, 96), (17, 513, 48), (520, 64, 1024)])
+def test_gemm_small(grid, shape):
+    _print_case("gemm", grid, shape)
+    PA, PB, K = shape
+    n = 16 if K % 16 == 0 else 1
+    cfg = U.make_cfg(grid, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 16, n, sign_seed=21)
+    _gemm_case(PA, PB, K, cfg, cfg, seed=PA + PB + K + grid)
+
+
+def test_gemm_mixed_blocks_and_sr():
+    cfg_a = U.make_cfg(U.UFP4_E1M2, U.UFP4_SR, U.UFP4_SCALE_F32, 1, 32, 32, sign_seed=4, sr_seed=1)
+    cfg_b = U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 16, 32, sign_seed=4)
+    _gemm_case(384, 320, 640, cfg_a, cfg_b, seed=5)
+
+
+@pytest.mark.parametrize("grid", [U.UFP4_E2M1, U.UFP4_E1M2])
+def test_gemm_2d_and_transpose(grid):
+    """2D square blocks: quantize once, reuse transposed (S(B) = S(B^T))."""
+    _print_case("2d gemm", grid)
+    cfg = U.make_cfg(grid, U.UFP4_SR, U.UFP4_SCALE_POW2, 32, 32, 1, sr_seed=5201)
+    tx, tw = rand_bits(320, 256, 1), rand_bits(288, 256, 2)
+    qx, rx = compare_quant(tx, 0, cfg, with_rotated=False)
+    qw, rw = compare_quant(tw, 0, cfg, with_rotated=False)
+    # transpose utility == transposed oracle codes / scale grid
+    qwt = U.ufp4_transpose_qtensor(qw)
+    codes_t = O.unpack_nibbles(rw["codes"]).T
+    assert np.array_equal(qwt.codes.cpu().numpy(), O.pack_nibbles(codes_t))
+    assert np.array_equal(qwt.scales.cpu().numpy(), rw["scales"].T)
+    # S(B) = S(B^T): quantizing W^T directly gives the transposed scale grid
+    qwt2, _ = U.ufp4_rht_quant(dev_bf16(np.ascontiguousarray(tw.T)), 0, cfg)
+    assert np.array_equal(qwt2.scales.cpu().numpy(), qw.scales.cpu().numpy().T)
+    # FPROP with both, and a GEMM on the transposed operand (DGRAD-style)
+    C = U.ufp4_gemm_fprop(qx, qw).cpu().numpy()
+    dx, dw = oracle_dequant64(rx, cfg), oracle_dequant64(rw, cfg)
+    assert O.rel_fro(C, O.gemm_ref(dx, dw)) <= GEMM_TOL
+    tdy = rand_bits(320, 288, 3)
+    qdy, rdy = compare_quant(tdy, 0, cfg, with_rotated=False)
+    dX = U.ufp4_gemm_dgrad(qdy, qwt).cpu().numpy()
+    assert O.rel_fro(dX, O.gemm_ref(oracle_dequant64(rdy, cfg), dw.T)) <= GEMM_TOL
+
+
+def test_segmented_quant_and_grouped_gemms():
+    """Four experts (one empty), per-expert transposed operands, and the
+    three grouped GEMMs against per-expert oracle products."""
+    G, hidden, ffn = 4, 128, 96
+    off = [0, 64, 64, 160, 256]               # padded token offsets (multiples of 32)
+    T = off[-1]
+    n, b = 32, 32
+    sx, sd, sw = 31, 32, 33
+    tx = rand_bits(T, hidden, 40)
+    tw = rand_bits(G * ffn, hidden, 41)
+    tdy = rand_bits(T, ffn, 42)
+    cx = U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, b, n, sign_seed=sx)
+    cd = U.make_cfg(U.UFP4_E1M2, U.UFP4_SR, U.UFP4_SCALE_F32, 1, b, n, sign_seed=sd, sr_seed=7, sr_stream=0)
+    cw_row = cx
+    # FPROP: X_perm rows, W stacked rows (both K = hidden)
+    qx, rx = compare_quant(tx, 0, cx, with_rotated=False)
+    qw, rw = compare_quant(tw, 0, cw_row, with_rotated=False)
+    Y = U.ufp4_gemm_fprop_grouped(qx, qw, off).cpu().numpy()
+    dxq, dwq = oracle_dequant64(rx, cx), oracle_dequant64(rw, cw_row)
+    for g in range(G):
+        ref = O.gemm_ref(dxq[off[g]:off[g + 1]], dwq[g * ffn:(g + 1) * ffn])
+        if ref.size:
+            assert O.rel_fro(Y[off[g]:off[g + 1]], ref) <= GEMM_TOL
+    # DGRAD: dY_perm rows (K = ffn) x W^T per expert (segmented column-wise of W)
+    cdg = cd.copy(sign_seed=sd)
+    cwt = U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, b, n, sign_seed=sd)
+    qdy, rdy = compare_quant(tdy, 0, cdg, with_rotated=False)
+    qwt = U.stacked(U.ufp4_rht_quant_segmented(dev_bf16(tw), [g * ffn for g in range(G + 1)], cwt), G)
+    refs_wt = O.quantize_segmented(tw, [g * ffn for g in range(G + 1)], spec_of(cwt))
+    got_codes = qwt.codes.cpu().numpy()
+    want_codes = np.concatenate([r["codes"].ravel() for r in refs_wt])
+    assert np.array_equal(got_codes, want_codes)
+    dX = U.ufp4_gemm_dgrad_grouped(qdy, qwt, off).cpu().numpy()
+    ddy = oracle_dequant64(rdy, cdg)
+    for g in range(G):
+        dwt = oracle_dequant64(refs_wt[g], cwt)
+        ref = O.gemm_ref(ddy[off[g]:off[g + 1]], dwt)
+        if ref.size:
+            assert O.rel_fro(dX[off[g]:off[g + 1]], ref) <= GEMM_TOL
+    # WGRAD: dY^T and X^T segments (K = expert tokens)
+    cdt = U.make_cfg(U.UFP4_E1M2, U.UFP4_SR, U.UFP4_SCALE_F32, 1, b, n, sign_seed=sw, sr_seed=7, sr_stream=1)
+    cxt = U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, b, n, sign_seed=sw)
+    qdyt = U.ufp4_rht_quant_segmented(dev_bf16(tdy), off, cdt)
+    qxt = U.ufp4_rht_quant_segmented(dev_bf16(tx), off, cxt)
+    r_dyt = O.quantize_segmented(tdy, off, spec_of(cdt))
+    r_xt = O.quantize_segmented(tx, off, spec_of(cxt))
+    assert np.array_equal(qdyt.codes.cpu().numpy(), np.concatenate([r["codes"].ravel() for r in r_dyt]))
+    assert np.array_equal(qdyt.scales.cpu().numpy().view(np.uint32),
+                          np.concatenate([r["scales"].ravel() for r in r_dyt]).view(np.uint32))
+    dW = U.ufp4_gemm_wgrad_grouped(qdyt, qxt, off).cpu().numpy()
+    for g in range(G):
+        if off[g + 1] == off[g]:
+            assert np.all(dW[g * ffn:(g + 1) * ffn] == 0)
+            continue
+        ref = O.gemm_ref(oracle_dequant64(r_dyt[g], cdt), oracle_dequant64(r_xt[g], cxt))
+        assert O.rel_fro(dW[g * ffn:(g + 1) * ffn], ref) <= GEMM_TOL
+
+
+def test_repeat_determinism():
+    """Same inputs twice (different launch timing) give identical bits."""
+    bits = rand_bits(128, 1024, 3)
+    cfg = U.make_cfg(U.UFP4_E2M1, U.UFP4_SR, U.UFP4_SCALE_F32, 1, 16, 128, sign_seed=1, sr_seed=2)
+    x = dev_bf16(bits)
+    a, _ = U.ufp4_rht_quant(x, 0, cfg)
+    b, _ = U.ufp4_rht_quant(x, 0, cfg)
+    assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+    C1 = U.ufp4_gemm_fprop(a, b)
+    C2 = U.ufp4_gemm_fprop(a, b)
+    assert torch.equal(C1, C2)
