@@ -302,13 +302,15 @@ def _expand(blockwise, br, bc):
     return np.repeat(np.repeat(blockwise, br, axis=0), bc, axis=1)
 
 
-def quantize(t_bits, along, spec, elem_base=0, row_index=None):
+def quantize(t_bits, along, spec, elem_base=0, row_index=None, col_index=None, K_total=None):
     """Quantize a bf16 tensor given as uint16 bits [R, C].
 
     along = 0: the logical operand is A = T (K = C); along = 1: A = T^T (K = R).
-    row_index (optional): logical row number of each row of A, used only to
-    index the stochastic-rounding draws (lets a caller quantize a sample of
-    rows of a large operand).  Returns a dict with 'rotated' fp32 [P, K],
+    row_index / col_index / K_total (optional): position of the given rows
+    and columns inside a larger logical operand with K_total columns, used
+    only to index the stochastic-rounding draws (lets a caller quantize a
+    sample of a large operand; blocks and rotation chunks must lie inside
+    the sample).  Returns a dict with 'rotated' fp32 [P, K],
     'codes' uint8 [P, K/2], 'scales' (fp32 [P, K/bc] or uint8 [P/br, K/bc] as
     E8M0 = e + 127) and the unpacked 'code' nibbles.
     """
@@ -350,7 +352,9 @@ def quantize(t_bits, along, spec, elem_base=0, row_index=None):
         k = round_rtne_index(m, grid)
     else:
         rows = np.arange(P, dtype=np.int64) if row_index is None else np.asarray(row_index, np.int64)
-        e_idx = int(elem_base) + rows[:, None] * K + np.arange(K, dtype=np.int64)[None, :]
+        cols = np.arange(K, dtype=np.int64) if col_index is None else np.asarray(col_index, np.int64)
+        kt = K if K_total is None else int(K_total)
+        e_idx = int(elem_base) + rows[:, None] * kt + cols[None, :]
         r16 = sr_draws(spec.sr_seed, spec.sr_stream, e_idx)
         k = round_sr_index(m, grid, r16)
     code = encode(k, neg, grid)

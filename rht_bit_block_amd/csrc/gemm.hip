@@ -14,12 +14,18 @@
 // hi*hi + hi*lo + lo*hi with v_mfma_f32_32x32x16_bf16 (fp32 accumulate), so
 // the whole K loop stays on the matrix cores and any block shape works.
 //
-// Tiling: 256 x 256 output tile per 512-thread workgroup (8 waves as 2 x 4,
-// each wave 128 x 64 = 4 x 2 MFMA tiles of 32 x 32), K step 32.  The packed
-// codes and scales of step i+1 are fetched into registers while step i runs
-// its MFMAs; they are then decoded into the other half of a double-buffered
-// LDS tile laid out [k-chunk of 8][row] so every fragment read is 16 B per
-// lane with consecutive lanes on consecutive rows.
+// Tiling: 256 x 256 output tile per 256-thread workgroup, one wave per SIMD
+// (2 x 2 waves, each 128 x 128 = 4 x 4 MFMA tiles of 32 x 32, accumulators in
+// AGPRs), K step 32.  Each thread owns one row of A and one row of B per
+// step (32 codes each).  Software pipeline per step i:
+//   - packed codes/scales of step i+2 are fetched into registers;
+//   - the fragments of k-half 1 of step i are read from LDS buffer i&1;
+//   - the 48 MFMAs of k-half 0 run while step i+1's codes are decoded into
+//     LDS buffer (i+1)&1 (the decode VALU is interleaved with the MFMAs);
+//   - one barrier; the fragments of k-half 0 of step i+1 are read;
+//   - the 48 MFMAs of k-half 1 run.
+// The LDS tile is laid out [part][k-chunk of 8][row] x 16 B, so a fragment
+// read is 16 B per lane with consecutive lanes on consecutive rows.
 #include "ufp4_internal.h"
 
 namespace ufp4 {
@@ -27,7 +33,7 @@ namespace ufp4 {
 namespace {
 
 constexpr int TM = 256, TN = 256, TK = 32;
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -181,195 +187,231 @@ __device__ __forceinline__ void decode16(uint32_t w0, uint32_t w1, float s, cons
 }
 
 // Per-thread view of one operand inside the K loop: this thread owns row
-// `row` of the tile and the 16 codes at k = 32*step + 16*half.  All index
-// arithmetic is done once; the loop only advances pointers.  Rows past the
-// operand read row 0 with a zero scale, and steps past K re-read the last
-// valid step with a zero scale, so the loop body has no branches.
+// `row` of the tile and the 32 codes of each K step.  Index arithmetic is done
+// once; the loop only advances pointers.  Rows past the operand re-read a
+// valid row with a zero scale, and steps past K re-read the last valid step
+// with a zero scale, so the loop body has no data-dependent branches.
 struct OperandCursor {
-  const uint8_t* codes;     // row start + 8*half bytes
-  const uint8_t* scales;    // fp32 or E8M0 scale of this thread's first block
-  int32_t sstep;            // scale bytes per K step
+  const uint8_t* codes;     // start of this thread's row
+  const uint8_t* scales;    // first scale of the row (fp32 or E8M0 bytes)
   int32_t pow2;             // 1: E8M0 bytes, 0: fp32
-  int32_t last;             // last step whose k < K
+  int32_t per_step;         // fp32 scales per K step (2 for 1x16 blocks, 1 for 1x32)
+  int32_t last;             // last step with any k < K
+  int32_t half_last;        // 1 when the last step holds only 16 codes
   float valid;              // 1 for rows inside the operand, else 0
 };
 
 __device__ __forceinline__ OperandCursor make_cursor(const uint8_t* codes, const void* scales,
                                                      int smode, int br, int bc, int64_t row,
                                                      int64_t row_end, int64_t row_begin,
-                                                     int64_t K, int half) {
+                                                     int64_t K) {
   OperandCursor c;
   c.valid = (row < row_end && K > 0) ? 1.0f : 0.0f;
-  if (row >= row_end) row = row_begin;      // any in-range row (operand has >= 1 row)
-  c.last = (int32_t)((K - 16 * half + 31) / 32) - 1;
+  if (row >= row_end) row = row_begin;  // an in-range row (the operand has >= 1 row)
+  c.last = (int32_t)((K + TK - 1) / TK) - 1;
+  c.half_last = (K % TK) != 0;
   if (c.last < 0) { c.last = 0; c.valid = 0.0f; }
-  const int h = (K > 16 * half) ? half : 0;  // keep the address inside the row
-  c.codes = codes + row * (K >> 1) + 8 * h;
+  c.codes = codes + row * (K >> 1);
   const int64_t nb = K / bc;
   if (smode == 0) {
-    c.scales = reinterpret_cast<const uint8_t*>(scales) + 4 * (row * nb + (16 * h) / bc);
-    c.sstep = 4 * (32 / bc);
+    c.scales = reinterpret_cast<const uint8_t*>(scales) + 4 * row * nb;
     c.pow2 = 0;
+    c.per_step = TK / bc;
   } else {
     c.scales = reinterpret_cast<const uint8_t*>(scales) + (row / br) * nb;
-    c.sstep = 1;
     c.pow2 = 1;
+    c.per_step = 1;
   }
   return c;
 }
 
-__device__ __forceinline__ void fetch(const OperandCursor& c, int step, uint2& codes, float& s) {
+// Raw loads of one K step.  Nothing is computed from them at fetch time:
+// using a loaded value right away would make the wave wait for the memory
+// latency; they are finalized when decoded, one step later.
+struct Fetched {
+  uint2 c0, c1;       // codes 0..15 and 16..31 (c1 re-reads c0 on a half step)
+  uint32_t s0, s1;    // raw scale bits (fp32 bits, or the E8M0 byte)
+  float v0, v1;       // 1 or 0: row inside the operand and k < K
+};
+
+template <int SMODE>
+__device__ __forceinline__ Fetched fetch(const OperandCursor& c, int step) {
+  Fetched f;
   const int st = step <= c.last ? step : c.last;
   const float v = step <= c.last ? c.valid : 0.0f;
-  codes = *reinterpret_cast<const uint2*>(c.codes + 16 * st);
-  float sc;
-  if (c.pow2) {
-    // 2^(e - 127): e >= 1 -> exponent field e; e == 0 -> subnormal 2^-127
-    const uint32_t e = c.scales[st];
-    sc = __uint_as_float(e ? (e << 23) : 0x00400000u);
+  const bool half = c.half_last && st == c.last;
+  const uint8_t* p = c.codes + 16 * st;
+  f.c0 = *reinterpret_cast<const uint2*>(p);
+  f.c1 = *reinterpret_cast<const uint2*>(p + (half ? 0 : 8));
+  if constexpr (SMODE == 1) {
+    f.s0 = f.s1 = c.scales[st];
   } else {
-    sc = *reinterpret_cast<const float*>(c.scales + c.sstep * st);
+    // branch-free: 1x16 blocks -> scales 2st, 2st+1; 1x32 -> scale st twice
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(c.scales);
+    const int i0 = st * c.per_step;
+    const int i1 = i0 + ((c.per_step == 2 && !half) ? 1 : 0);
+    f.s0 = q[i0];
+    f.s1 = q[i1];
   }
-  s = sc * v;
+  f.v0 = v;
+  f.v1 = half ? 0.0f : v;
+  return f;
 }
 
-template <int GRID>
-__device__ __forceinline__ void stage(uint4* lds, int st, int row, int half, uint2 a, float sa,
-                                      uint2 b, float sb, const ResidualMasks& rm) {
-  uint4 hi[2], lo[2];
-  uint4* base = lds + st * (kParts * kChunks * TM);
-  decode16<GRID>(a.x, a.y, sa, rm, hi, lo);
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    base[(0 * kChunks + 2 * half + c) * TM + row] = hi[c];
-    base[(1 * kChunks + 2 * half + c) * TM + row] = lo[c];
+template <int SMODE>
+__device__ __forceinline__ float finalize_scale(uint32_t raw, float v) {
+  float s;
+  if constexpr (SMODE == 1) {
+    // 2^(e - 127): e >= 1 -> exponent field e; e == 0 -> subnormal 2^-127
+    s = __uint_as_float(raw ? (raw << 23) : 0x00400000u);
+  } else {
+    s = __uint_as_float(raw);
   }
-  decode16<GRID>(b.x, b.y, sb, rm, hi, lo);
+  return s * v;
+}
+
+struct Frags {
+  bf16x8 ah[4], al[4], bh[4], bl[4];
+};
+
+__device__ __forceinline__ void load_frags(const uint4* buf, int kh, int lane, int wm, int wn,
+                                           Frags& f) {
+  const int chunk = 2 * kh + (lane >> 5);
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    base[(2 * kChunks + 2 * half + c) * TM + row] = hi[c];
-    base[(3 * kChunks + 2 * half + c) * TM + row] = lo[c];
+  for (int i = 0; i < 4; ++i) {
+    const int ra = wm * 128 + i * 32 + (lane & 31);
+    f.ah[i] = __builtin_bit_cast(bf16x8, buf[(0 * kChunks + chunk) * TM + ra]);
+    f.al[i] = __builtin_bit_cast(bf16x8, buf[(1 * kChunks + chunk) * TM + ra]);
+    const int rb = wn * 128 + i * 32 + (lane & 31);
+    f.bh[i] = __builtin_bit_cast(bf16x8, buf[(2 * kChunks + chunk) * TM + rb]);
+    f.bl[i] = __builtin_bit_cast(bf16x8, buf[(3 * kChunks + chunk) * TM + rb]);
   }
 }
 
-// Scheduling groups (mask bits of __builtin_amdgcn_sched_group_barrier).
-constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100, kSgDsWrite = 0x200,
-              kSgVmemRead = 0x020;
+__device__ __forceinline__ void mfma_step(floatx16 (&acc)[4][4], const Frags& f, int m) {
+  const int prod = m / 16, t = m % 16, i = t >> 2, j = t & 3;   // hh, hl, lh
+  const bf16x8 a = prod == 2 ? f.al[i] : f.ah[i];
+  const bf16x8 b = prod == 1 ? f.bl[j] : f.bh[j];
+  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i][j], 0, 0, 0);
+}
 
-template <int GRID>
+// Decode of one thread's two rows (A and B) of a K step into an LDS buffer:
+// 8 code dwords (A0..A3, B0..B3); dword w -> k-chunk (w & 3) of operand w/4.
+// `unit` 0..39 = 5 units per dword: the byte expansion, then 4 pairs; after
+// the 4th pair the chunk's hi and lo are stored.
+struct DecodeState {
+  uint32_t ev, od;
+  uint32_t h[4], l[4];
+};
+
+template <int GRID, int SMODE>
+__device__ __forceinline__ void decode_unit(int unit, const Fetched& fa, const Fetched& fb,
+                                            const ResidualMasks& rm, DecodeState& ds,
+                                            uint4* buf, int row) {
+  const int w = unit / 5, u = unit % 5;
+  const Fetched& f = (w < 4) ? fa : fb;
+  const int cw = w & 3;
+  const uint32_t word = cw == 0 ? f.c0.x : (cw == 1 ? f.c0.y : (cw == 2 ? f.c1.x : f.c1.y));
+  const float s = cw < 2 ? finalize_scale<SMODE>(f.s0, f.v0) : finalize_scale<SMODE>(f.s1, f.v1);
+  const float su = s * Dec<GRID>::unit;
+  const float nb = -Dec<GRID>::bias * su;
+  if (u == 0) {
+    decode8<GRID>(word, ds.ev, ds.od);
+  } else {
+    const int i = u - 1;
+    decode_pair(ds.ev, ds.od, i, su, nb, rm, ds.h[i], ds.l[i]);
+    if (i == 3) {
+      const int part = (w < 4) ? 0 : 2;
+      buf[(part * kChunks + cw) * TM + row] = make_uint4(ds.h[0], ds.h[1], ds.h[2], ds.h[3]);
+      buf[((part + 1) * kChunks + cw) * TM + row] = make_uint4(ds.l[0], ds.l[1], ds.l[2], ds.l[3]);
+    }
+  }
+}
+
+template <int GRID, int SMODE>
 __global__ __launch_bounds__(kThreads) void k_gemm(GemmLaunch g) {
   extern __shared__ uint4 lds[];
   int tm, tn;
   const Problem pr = resolve(g, blockIdx.x, tm, tn);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;   // 2 x 4 waves
+  const int wm = wave >> 1, wn = wave & 1;   // 2 x 2 waves
+  const ResidualMasks rm = make_masks();
 
-  const int frow = tid >> 1, fhalf = tid & 1;
   const OperandCursor ca = make_cursor(pr.a_codes, pr.a_scales, g.scale_mode, g.a_br, g.a_bc,
-                                       pr.a_row0 + (int64_t)tm * TM + frow,
-                                       pr.a_row0 + pr.a_rows, pr.a_row0, pr.K, fhalf);
+                                       pr.a_row0 + (int64_t)tm * TM + tid,
+                                       pr.a_row0 + pr.a_rows, pr.a_row0, pr.K);
   const OperandCursor cb = make_cursor(pr.b_codes, pr.b_scales, g.scale_mode, g.b_br, g.b_bc,
-                                       pr.b_row0 + (int64_t)tn * TN + frow,
-                                       pr.b_row0 + pr.b_rows, pr.b_row0, pr.K, fhalf);
+                                       pr.b_row0 + (int64_t)tn * TN + tid,
+                                       pr.b_row0 + pr.b_rows, pr.b_row0, pr.K);
   const int nsteps = (int)((pr.K + TK - 1) / TK);
+  constexpr int kStage = kParts * kChunks * TM;   // uint4 per LDS buffer
 
-  floatx16 acc[4][2];
+  floatx16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
 
-  // Software pipeline: step i's MFMAs read LDS buffer i&1 while the codes of
-  // step i+1 (fetched during step i-1) are decoded into the other buffer and
-  // the codes of step i+2 are in flight.
-  uint2 fa, fb, na, nb;
-  float sa, sb, nsa, nsb;
-  fetch(ca, 0, fa, sa);
-  fetch(cb, 0, fb, sb);
-  const ResidualMasks rm = make_masks();
-  stage<GRID>(lds, 0, frow, fhalf, fa, sa, fb, sb, rm);
-  fetch(ca, 1, fa, sa);
-  fetch(cb, 1, fb, sb);
+  // prologue: step 0 decoded into buffer 0, step 1 fetched, k-half 0 frags
+  DecodeState ds;
+  {
+    const Fetched fa = fetch<SMODE>(ca, 0), fb = fetch<SMODE>(cb, 0);
+#pragma unroll
+    for (int u = 0; u < 40; ++u) decode_unit<GRID, SMODE>(u, fa, fb, rm, ds, lds, tid);
+  }
+  Fetched xa = fetch<SMODE>(ca, 1), xb = fetch<SMODE>(cb, 1), ya, yb;
   __syncthreads();
+  Frags f0, f1;
+  load_frags(lds, 0, lane, wm, wn, f0);
 
-  for (int step = 0; step < nsteps; ++step) {
-    const int st = step & 1;
-    fetch(ca, step + 2, na, nsa);     // re-reads the last step past the end (scale 0)
-    fetch(cb, step + 2, nb, nsb);
-
-    const uint4* base = lds + st * (kParts * kChunks * TM);
-    uint4* nxt = lds + (st ^ 1) * (kParts * kChunks * TM);
-    // Decode state of the next step: 4 dwords of codes (A w0, A w1, B w0,
-    // B w1), each expanded to even/odd level bytes, then 4 pairs each.
-    const uint32_t words[4] = {fa.x, fa.y, fb.x, fb.y};
-    const float su[2] = {sa * Dec<GRID>::unit, sb * Dec<GRID>::unit};
-    const float nbias[2] = {-Dec<GRID>::bias * su[0], -Dec<GRID>::bias * su[1]};
-    uint32_t ev[4], od[4];
-    uint32_t hreg[4][4], lreg[4][4];
-    // MFMA sequence: 2 k-halves x 3 products x 8 tiles = 48.  After every
-    // third MFMA one decode piece runs (16 pieces = 4 dwords x 4 pairs),
-    // and the byte expansion of dword w runs before its first pair.
-    bf16x8 ah[4], al[4], bh[2], bl[2];
-    // fragment loads of k-half kh for part p (0 A_hi, 1 A_lo, 2 B_hi, 3 B_lo)
-    auto load_part = [&](int kh, int p) {
-      const int chunk = 2 * kh + (lane >> 5);
-      if (p < 2) {
+  // One K step: decode (da, db) = step+1 while (la, lb) <- step+2 loads.  The
+  // loop is unrolled by two so the two register sets alternate roles and no
+  // in-flight load result is ever copied.
+  auto body = [&](int step, const Fetched& da, const Fetched& db, Fetched& la, Fetched& lb) {
+    const uint4* cur = lds + (step & 1) * kStage;
+    uint4* nxt = lds + ((step + 1) & 1) * kStage;
+    la = fetch<SMODE>(ca, step + 2);
+    lb = fetch<SMODE>(cb, step + 2);
+    load_frags(cur, 1, lane, wm, wn, f1);
+    // k-half 0: 48 MFMAs with the 40 decode units of step+1 in regions of
+    // eight MFMAs + eight units, alternated MFMA / VALU inside a region so
+    // independent decode chains fill the MFMA shadow
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = wm * 128 + i * 32 + (lane & 31);
-          const bf16x8 v = __builtin_bit_cast(bf16x8, base[(p * kChunks + chunk) * TM + r]);
-          if (p == 0) ah[i] = v; else al[i] = v;
-        }
-      } else {
+    for (int m0 = 0; m0 < 48; m0 += 8) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int r = wn * 64 + j * 32 + (lane & 31);
-          const bf16x8 v = __builtin_bit_cast(bf16x8, base[(p * kChunks + chunk) * TM + r]);
-          if (p == 2) bh[j] = v; else bl[j] = v;
-        }
+      for (int m = m0; m < m0 + 8; ++m) {
+        mfma_step(acc, f0, m);
+        if (m < 40) decode_unit<GRID, SMODE>(m, da, db, rm, ds, nxt, tid);
       }
-    };
-    // Product order per k-half: kh0 = hh, hl, lh; kh1 = hl, hh, lh.  A_hi and
-    // B_lo of kh1 are fetched at MFMA 16 (their kh0 copies are dead after
-    // hl), A_lo and B_hi of kh1 at MFMA 24.
-    load_part(0, 0); load_part(0, 2); load_part(0, 3); load_part(0, 1);
 #pragma unroll
-    for (int m = 0; m < 48; ++m) {
-      const int kh = m / 24, t = m % 8, i = t >> 1, j = t & 1;
-      const int slot = (m % 24) / 8;                        // 0, 1, 2 within the k-half
-      const int prod = kh == 0 ? slot : (slot == 0 ? 1 : (slot == 1 ? 0 : 2));  // 0 hh 1 hl 2 lh
-      if (m == 16) { load_part(1, 0); load_part(1, 3); }
-      if (m == 24) { load_part(1, 2); load_part(1, 1); }
-      const bf16x8 av = prod == 2 ? al[i] : ah[i];
-      const bf16x8 bv = prod == 1 ? bl[j] : bh[j];
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i][j], 0, 0, 0);
-      if (m % 3 == 2) {
-        const int piece = m / 3;          // 0..15
-        const int w = piece >> 2, pr2 = piece & 3;
-        if (pr2 == 0) decode8<GRID>(words[w], ev[w], od[w]);
-        decode_pair(ev[w], od[w], pr2, su[w >> 1], nbias[w >> 1], rm, hreg[w][pr2], lreg[w][pr2]);
-        if (pr2 == 3) {
-          // dword w of the codes = chunk (2*half + (w & 1)) of operand (w >> 1)
-          const int opnd = w >> 1, c = 2 * fhalf + (w & 1);
-          nxt[((2 * opnd + 0) * kChunks + c) * TM + frow] =
-              make_uint4(hreg[w][0], hreg[w][1], hreg[w][2], hreg[w][3]);
-          nxt[((2 * opnd + 1) * kChunks + c) * TM + frow] =
-              make_uint4(lreg[w][0], lreg[w][1], lreg[w][2], lreg[w][3]);
-        }
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);   // then up to nine VALU
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
-    fa = na; fb = nb; sa = nsa; sb = nsb;
+    load_frags(nxt, 0, lane, wm, wn, f0);
+#pragma unroll
+    for (int m = 0; m < 48; ++m) {
+      mfma_step(acc, f1, m);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  int step = 0;
+  for (; step + 1 < nsteps; step += 2) {
+    body(step, xa, xb, ya, yb);
+    body(step + 1, ya, yb, xa, xb);
   }
+  if (step < nsteps) body(step, xa, xb, ya, yb);
 
   // Epilogue: lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4.
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = (int64_t)tn * TN + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = (int64_t)tn * TN + wn * 128 + j * 32 + (lane & 31);
       if (col >= pr.b_rows) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -381,23 +423,30 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmLaunch g) {
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
-  if (g.total_tiles == 0) return hipSuccess;
+template <int GRID, int SMODE>
+hipError_t launch_one(const GemmLaunch& g, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    const void* fns[3] = {(const void*)k_gemm<0>, (const void*)k_gemm<1>, (const void*)k_gemm<2>};
-    for (const void* f : fns) {
-      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-      if (e != hipSuccess) return e;
-    }
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm<GRID, SMODE>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
     attr_set = true;
   }
-  switch (g.grid) {
-    case 0: hipLaunchKernelGGL(k_gemm<0>, dim3(g.total_tiles), dim3(kThreads), kLdsBytes, s, g); break;
-    case 1: hipLaunchKernelGGL(k_gemm<1>, dim3(g.total_tiles), dim3(kThreads), kLdsBytes, s, g); break;
-    default: hipLaunchKernelGGL(k_gemm<2>, dim3(g.total_tiles), dim3(kThreads), kLdsBytes, s, g); break;
-  }
+  hipLaunchKernelGGL((k_gemm<GRID, SMODE>), dim3(g.total_tiles), dim3(kThreads), kLdsBytes, s, g);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
+  if (g.total_tiles == 0) return hipSuccess;
+  const int key = g.grid * 2 + g.scale_mode;
+  switch (key) {
+    case 0: return launch_one<0, 0>(g, s);
+    case 1: return launch_one<0, 1>(g, s);
+    case 2: return launch_one<1, 0>(g, s);
+    case 3: return launch_one<1, 1>(g, s);
+    case 4: return launch_one<2, 0>(g, s);
+    default: return launch_one<2, 1>(g, s);
+  }
 }
 
 }  // namespace ufp4
