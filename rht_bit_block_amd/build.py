@@ -15,7 +15,8 @@ LIB_NAME = "librht_ufp4.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "quant.hip", "gemm.hip", "misc.hip"]
+SOURCES = ["api.cpp", "quant.hip", "quant_e1m2.hip", "quant_int4.hip", "quant_e2m1.hip",
+           "gemm.hip", "misc.hip"]
 
 # -ffp-contract=off: every fp32 operation that decides an output bit is an
 # explicit round-to-nearest op; no silent fma contraction.
@@ -46,7 +47,7 @@ def _compile(src):
 
 def build(verbose=True):
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB_PATH + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]

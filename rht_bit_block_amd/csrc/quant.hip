@@ -1,517 +1,31 @@
-// Fused random Hadamard transform + blockwise 4-bit quantizer for gfx950.
-//
-// [UFP4] = "Rethinking Shrinkage Bias in FP4 Pretraining of LLMs ... the UFP4
-// Recipe" (hyper.ai summary: formats and blockwise quantization; Method).
-// [2DFP4] = "Stable FP4 Training via Transposition-Invariant Block
-// Quantization" (agifrontier tutorial: 2D square-block quantization).
-//
-// Every lane owns W consecutive elements of one row of the logical operand
-// A (P x K, K = the GEMM's shared dimension) and runs the whole pipeline on
-// them in registers:
-//   bf16 -> fp32, random signs S_n (sign-bit XOR on packed bf16 pairs),
-//   Walsh-Hadamard butterflies h = 1, 2, ..., n/2 (in-lane for h < W, across
-//   lanes with DPP quad permutes for h >= W), one multiply by c_n = RN(n^-1/2),
-//   block absmax, scale, RN(y / s) (Markstein's reciprocal correction,
-//   falling back to IEEE division when its preconditions fail), clamp,
-//   RTNE or stochastic rounding (Philox4x32-10 keyed by the element index),
-//   nibble encoding, packing, 8/16-byte stores.
-// Row-wise calls read A straight from HBM; column-wise calls (A = X^T) stage
-// a 128 x 64 tile of X through LDS and read it down the columns.
-// All fp32 arithmetic that decides an output bit is explicit RN (no
-// contraction; the library is built with -ffp-contract=off).
-#include <utility>
-
-#include "ufp4_internal.h"
+// Quantizer dispatch by codebook; the kernels live in quant_core.h and are
+// compiled per codebook in quant_e1m2.hip, quant_int4.hip and quant_e2m1.hip.
+#include "quant_core.h"
 
 namespace ufp4 {
 
-namespace {
-
-constexpr int kThreads = 256;
-
-template <int GRID> struct Grid;
-template <> struct Grid<0> { static constexpr float qmax = 1.75f, inv_delta = 4.0f; };  // E1M2
-template <> struct Grid<1> { static constexpr float qmax = 7.0f, inv_delta = 1.0f; };   // INT4
-template <> struct Grid<2> { static constexpr float qmax = 6.0f, inv_delta = 0.0f; };   // E2M1
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// 16-byte streaming load (read once: non-temporal hint).
-__device__ __forceinline__ uint4 ld16(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ uint32_t fdiv_u32(uint32_t n, FastDiv f) {
-  const uint64_t t = (uint64_t)__umulhi(n, f.m) + n;
-  return (uint32_t)(t >> f.l);
-}
-
-// Per-pair sign masks: bit 15 flips the low bf16 of a packed pair, bit 31 the
-// high one.  Bit j of `pat` is the sign of element j of the lane's segment.
-template <int W>
-__device__ __forceinline__ void sign_masks(uint32_t pat, uint32_t (&pm)[W / 2]) {
-#pragma unroll
-  for (int i = 0; i < W / 2; ++i) {
-    const uint32_t lo = (pat >> (2 * i)) & 1u;
-    const uint32_t hi = (pat >> (2 * i + 1)) & 1u;
-    pm[i] = (lo << 15) | (hi << 31);
-  }
-}
-
-// Sign pattern of the lane's segment: word qpos of the n-bit sign vector when a
-// chunk spans several lanes, else the pattern repeated with period n (host).
-__device__ __forceinline__ uint32_t select_pattern(const QuantLaunch& q, uint32_t qpos) {
-  const uint32_t a = (qpos & 1u) ? q.sign_pat[1] : q.sign_pat[0];
-  const uint32_t b = (qpos & 1u) ? q.sign_pat[3] : q.sign_pat[2];
-  return (qpos & 2u) ? b : a;
-}
-
-// bf16 pairs (already sign-flipped) -> fp32.
-template <int W>
-__device__ __forceinline__ void unpack(const uint32_t (&w)[W / 2], const uint32_t (&pm)[W / 2],
-                                       float (&y)[W]) {
-#pragma unroll
-  for (int i = 0; i < W / 2; ++i) {
-    const uint32_t v = w[i] ^ pm[i];
-    y[2 * i] = __uint_as_float(v << 16);
-    y[2 * i + 1] = __uint_as_float(v & 0xFFFF0000u);
-  }
-}
-
-// In-lane butterflies for h < min(n, W), in the fixed order h = 1, 2, 4, ...
-template <int W>
-__device__ __forceinline__ void fwht_inlane(float (&y)[W], int n) {
-#pragma unroll
-  for (int h = 1; h < W; h <<= 1) {
-    if (h < n) {
-#pragma unroll
-      for (int i = 0; i < W; ++i) {
-        if ((i & h) == 0) {
-          const float a = y[i], b = y[i + h];
-          y[i] = __fadd_rn(a, b);
-          y[i + h] = __fsub_rn(a, b);
-        }
-      }
-    }
-  }
-}
-
-// One butterfly stage between lanes L and L ^ m (m = 1 or 2) for every
-// element: the lane with the bit clear keeps a + b, the other b - a, where
-// a is its own value and b the partner's.  Computed as b + (+-a) so both
-// lanes run the same instruction (IEEE: x - y == x + (-y), and a + b == b + a).
-template <int W, int CTRL>
-__device__ __forceinline__ void fwht_xlane(float (&y)[W], uint32_t negmask) {
-#pragma unroll
-  for (int i = 0; i < W; ++i) {
-    const float b = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y[i]), CTRL, 0xF, 0xF, false));
-    const float a = __uint_as_float(__float_as_uint(y[i]) ^ negmask);
-    y[i] = __fadd_rn(b, a);
-  }
-}
-
-// Rounding of one value v (|v| <= qmax) to a 4-bit code.
-template <int GRID, int RND>
-__device__ __forceinline__ uint32_t encode_one(float v, uint32_t r16) {
-  if constexpr (GRID != 2) {
-    constexpr float inv = Grid<GRID>::inv_delta;
-    if constexpr (RND == 0) {
-      const int k = (int)__builtin_rintf(v * inv);  // round half to even
-      if constexpr (GRID == 1) return (uint32_t)k & 15u;
-      return k < 0 ? (8u | (uint32_t)(-k)) : (uint32_t)k;
-    } else {
-      const float t = fabsf(v) * inv;
-      const float fl = floorf(t);
-      const float f = __fsub_rn(t, fl);
-      const uint32_t up = ((float)r16 < f * 65536.0f) ? 1u : 0u;
-      const uint32_t k = (uint32_t)fl + up;
-      const bool neg = v < 0.0f && k != 0u;
-      if constexpr (GRID == 1) return neg ? ((16u - k) & 15u) : k;
-      return neg ? (8u | k) : k;
-    }
-  } else {
-    const float m = fabsf(v);
-    const float mul = m < 2.0f ? 2.0f : (m < 4.0f ? 1.0f : 0.5f);
-    const uint32_t add = m < 2.0f ? 0u : (m < 4.0f ? 2u : 4u);
-    const float t = m * mul;  // exact
-    uint32_t k;
-    if constexpr (RND == 0) {
-      k = (uint32_t)__builtin_rintf(t) + add;
-    } else {
-      const float fl = floorf(t);
-      const float f = __fsub_rn(t, fl);
-      k = (uint32_t)fl + add + (((float)r16 < f * 65536.0f) ? 1u : 0u);
-    }
-    return (v < 0.0f && k != 0u) ? (8u | k) : k;
-  }
-}
-
-// 16-bit draws of the W elements starting at element index e0 (e0 % 8 == 0).
-template <int W>
-__device__ __forceinline__ void sr_draws(uint64_t e0, uint64_t seed, uint32_t stream,
-                                         uint32_t (&words)[W / 2]) {
-#pragma unroll
-  for (int t = 0; t < W / 8; ++t) {
-    const uint64_t g = (e0 >> 3) + (uint64_t)t;
-    uint32_t c[4] = {(uint32_t)g, (uint32_t)(g >> 32), stream, 0u};
-    philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) words[4 * t + i] = c[i];
-  }
-}
-
-// Quantize the W values of one lane whose blocks are 1 x B (fp32 absmax
-// scales); writes codes (W/2 bytes) and W/B scales.
-template <int W, int B, int GRID, int RND>
-__device__ __forceinline__ void quantize_1d(const float (&y)[W], uint64_t e0, uint64_t seed,
-                                            uint32_t stream, uint8_t* codes_out,
-                                            float* scales_out) {
-  constexpr float qmax = Grid<GRID>::qmax;
-  uint32_t rw[W / 2];
-  if constexpr (RND == 1) sr_draws<W>(e0, seed, stream, rw);
-  uint32_t packed[W / 8];
-#pragma unroll
-  for (int i = 0; i < W / 8; ++i) packed[i] = 0u;
-#pragma unroll
-  for (int blk = 0; blk < W / B; ++blk) {
-    float M = 0.0f;
-#pragma unroll
-    for (int j = 0; j < B; ++j) M = fmaxf(M, fabsf(y[blk * B + j]));
-    const float s = __fdiv_rn(M, qmax);  // s_B = RN(absmax / qmax)
-    scales_out[blk] = s;
-    float v[B];
-    if (s == 0.0f) {
-#pragma unroll
-      for (int j = 0; j < B; ++j) v[j] = 0.0f;
-    } else {
-      const float r = __fdiv_rn(1.0f, s);
-      // Markstein: with r = RN(1/s) and q within an ulp of y/s, the fma
-      // remainder is exact and RN(q + e r) = RN(y/s).  Preconditions: no
-      // underflow of q or of the remainder.
-      const float thr = s * 0x1p-39f;
-      bool slow = !(s >= 0x1p-60f && s <= 0x1p60f);
-#pragma unroll
-      for (int j = 0; j < B; ++j) {
-        const float yy = y[blk * B + j];
-        const float q = __fmul_rn(yy, r);
-        const float e = __fmaf_rn(-q, s, yy);
-        v[j] = __fmaf_rn(e, r, q);
-        slow |= fabsf(yy) < thr;
-      }
-      if (__builtin_expect(slow, 0)) {
-#pragma unroll
-        for (int j = 0; j < B; ++j) v[j] = __fdiv_rn(y[blk * B + j], s);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < B; ++j) {
-      const float vc = fminf(fmaxf(v[j], -qmax), qmax);
-      const int idx = blk * B + j;
-      uint32_t r16 = 0;
-      if constexpr (RND == 1) r16 = (rw[idx >> 1] >> (16 * (idx & 1))) & 0xFFFFu;
-      const uint32_t code = encode_one<GRID, RND>(vc, r16);
-      packed[idx >> 3] |= code << (4 * (idx & 7));
-    }
-  }
-  if constexpr (W == 16) {
-    *reinterpret_cast<uint2*>(codes_out) = make_uint2(packed[0], packed[1]);
-  } else {
-    *reinterpret_cast<uint4*>(codes_out) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-  }
-}
-
-template <int W>
-__device__ __forceinline__ void rotate(float (&y)[W], const QuantLaunch& q, int lpc,
-                                       uint32_t negmask1, uint32_t negmask2) {
-  fwht_inlane<W>(y, q.n);
-  if (lpc >= 2) fwht_xlane<W, 0xB1>(y, negmask1);  // quad_perm [1,0,3,2]: lane ^ 1
-  if (lpc >= 4) fwht_xlane<W, 0x4E>(y, negmask2);  // quad_perm [2,3,0,1]: lane ^ 2
-  if (q.n > 1) {
-#pragma unroll
-    for (int i = 0; i < W; ++i) y[i] = __fmul_rn(y[i], q.cn);
-  }
-}
-
-template <int W>
-__device__ __forceinline__ void store_rotated(float* dst, const float (&y)[W]) {
-#pragma unroll
-  for (int i = 0; i < W; i += 4)
-    *reinterpret_cast<float4*>(dst + i) = make_float4(y[i], y[i + 1], y[i + 2], y[i + 3]);
-}
-
-// ---------------------------------------------------------------------------
-// Row-wise, 1 x B blocks: grid-stride over segments of W elements.
-// ---------------------------------------------------------------------------
-template <int W, int B, int GRID, int RND>
-__global__ __launch_bounds__(kThreads) void k_quant_rows(QuantLaunch q, FastDiv segs_per_row,
-                                                         uint32_t nseg) {
-  const int lpc = q.n > W ? q.n / W : 1;
-  const uint32_t tid = blockIdx.x * kThreads + threadIdx.x;
-  const uint32_t stride = gridDim.x * kThreads;
-  // Position of this lane inside its chunk of n elements; constant across the
-  // grid-stride loop because stride and segs_per_row are multiples of lpc.
-  const uint32_t qpos = tid & (uint32_t)(lpc - 1);
-  const uint32_t pat = select_pattern(q, qpos);
-  uint32_t pm[W / 2];
-  sign_masks<W>(pat, pm);
-  const uint32_t neg1 = (qpos & 1u) ? 0x80000000u : 0u;
-  const uint32_t neg2 = (qpos & 2u) ? 0x80000000u : 0u;
-  const uint32_t K = (uint32_t)q.K;
-  for (uint32_t seg = tid; seg < nseg; seg += stride) {
-    const uint32_t p = fdiv_u32(seg, segs_per_row);
-    const uint32_t kseg = seg - p * segs_per_row.d;
-    const uint32_t k0 = kseg * W;
-    const uint16_t* src = q.x + (int64_t)p * q.ld + k0;
-    uint32_t w[W / 2];
-#pragma unroll
-    for (int i = 0; i < W / 8; ++i) {
-      const uint4 v = ld16(reinterpret_cast<const uint4*>(src) + i);
-      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-    }
-    float y[W];
-    unpack<W>(w, pm, y);
-    rotate<W>(y, q, lpc, neg1, neg2);
-    const uint64_t e0 = (uint64_t)p * K + k0;
-    if (q.rotated) store_rotated<W>(q.rotated + e0, y);
-    quantize_1d<W, B, GRID, RND>(y, e0, q.sr_seed, q.sr_stream, q.codes + (e0 >> 1),
-                                 reinterpret_cast<float*>(q.scales) + (uint64_t)p * (K / B) + k0 / B);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Column-wise (and segmented column-wise), 1 x B blocks.  A = X^T: a work-
-// group stages X[k0 : k0+128, p0 : p0+64] in LDS and each lane pulls W
-// consecutive k of one column p.
-// ---------------------------------------------------------------------------
-constexpr int kTK = 128, kTP = 64, kLdsPitch = kTP + 2;
-
-template <int W, int B, int GRID, int RND>
-__global__ __launch_bounds__(kThreads) void k_quant_cols(QuantLaunch q) {
-  __shared__ uint16_t tile[kTK * kLdsPitch];
-  const int lpc = q.n > W ? q.n / W : 1;
-  // which segment / tile
-  const int bid = blockIdx.x;
-  int g = 0;
-  while (g + 1 < q.nseg && q.tile_start[g + 1] <= bid) ++g;
-  const int64_t seg0 = q.seg_off[g], seg1 = q.seg_off[g + 1];
-  const int64_t L = seg1 - seg0;                       // K of this segment's operand
-  const int64_t C = q.cols;                            // P of the operand
-  const int tiles_p = (int)((C + kTP - 1) / kTP);
-  const int local = bid - q.tile_start[g];
-  const int tk = local / tiles_p, tp = local - tk * tiles_p;
-  const int64_t k0 = (int64_t)tk * kTK;                // within the segment
-  const int64_t p0 = (int64_t)tp * kTP;
-  const int krows = (int)min<int64_t>(kTK, L - k0);
-  const int pcols = (int)min<int64_t>(kTP, C - p0);
-
-  // Stage the tile: 128 rows x 64 columns of bf16, 16-byte loads.
-  for (int i = threadIdx.x; i < kTK * (kTP / 8); i += kThreads) {
-    const int r = i / (kTP / 8), c8 = (i % (kTP / 8)) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < krows) {
-      const uint16_t* src = q.x + (seg0 + k0 + r) * q.ld + p0 + c8;
-      if (c8 + 8 <= pcols) {
-        v = ld16(src);
-      } else {
-        uint16_t tmp[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int j = 0; j < 8 && c8 + j < pcols; ++j) tmp[j] = src[j];
-        v = make_uint4(tmp[0] | (tmp[1] << 16), tmp[2] | (tmp[3] << 16), tmp[4] | (tmp[5] << 16),
-                       tmp[6] | (tmp[7] << 16));
-      }
-    }
-    uint32_t* d = reinterpret_cast<uint32_t*>(&tile[r * kLdsPitch + c8]);
-    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-  }
-  __syncthreads();
-
-  constexpr int kSegsPerCol = kTK / W;
-  const uint32_t qpos = threadIdx.x & (uint32_t)(lpc - 1);
-  const uint32_t pat = select_pattern(q, qpos);
-  uint32_t pm[W / 2];
-  sign_masks<W>(pat, pm);
-  const uint32_t neg1 = (qpos & 1u) ? 0x80000000u : 0u;
-  const uint32_t neg2 = (qpos & 2u) ? 0x80000000u : 0u;
-  for (int u = threadIdx.x; u < kTP * kSegsPerCol; u += kThreads) {
-    // lanes of one chunk are adjacent: u = ((kgroup * 64) + col) * lpc + qpos
-    const int qq = u % lpc;
-    const int rest = u / lpc;
-    const int col = rest % kTP;
-    const int kseg = (rest / kTP) * lpc + qq;
-    const int kr = kseg * W;
-    if (kr >= krows || col >= pcols) continue;  // whole chunks drop out together
-    uint32_t w[W / 2];
-#pragma unroll
-    for (int i = 0; i < W / 2; ++i)
-      w[i] = (uint32_t)tile[(kr + 2 * i) * kLdsPitch + col] |
-             ((uint32_t)tile[(kr + 2 * i + 1) * kLdsPitch + col] << 16);
-    float y[W];
-    unpack<W>(w, pm, y);
-    rotate<W>(y, q, lpc, neg1, neg2);
-    const int64_t p = p0 + col;
-    const int64_t k = k0 + kr;
-    const uint64_t e_local = (uint64_t)p * L + k;            // inside segment g
-    if (q.rotated) store_rotated<W>(q.rotated + (uint64_t)C * seg0 + e_local, y);
-    const uint64_t e0 = (uint64_t)C * seg0 + e_local;        // global draw index
-    quantize_1d<W, B, GRID, RND>(y, e0, q.sr_seed, q.sr_stream, q.codes + (e0 >> 1),
-                                 reinterpret_cast<float*>(q.scales) +
-                                     ((uint64_t)C * seg0 + (uint64_t)p * L + k) / B);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Row-wise, 32 x 32 square blocks with power-of-two (E8M0) scales
-// ([2DFP4] 2D section).  A wave covers 32 rows x 64 columns: lane l takes
-// row (l & 31) of the block in column half (l >> 5); the block absmax is a
-// 32-lane reduction.  The scale is the least e with M <= qmax 2^e.
-// ---------------------------------------------------------------------------
-template <int GRID, int RND>
-__global__ __launch_bounds__(kThreads) void k_quant_rows_2d(QuantLaunch q, uint32_t kpairs,
-                                                            uint32_t nwaves) {
-  constexpr int W = 32;
-  constexpr float qmax = Grid<GRID>::qmax;
-  const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  uint32_t pm[W / 2];
-  sign_masks<W>(q.sign_pat[0], pm);
-  const uint32_t K = (uint32_t)q.K;
-  const uint32_t kblocks = K / 32;
-  for (uint32_t wv = wave; wv < nwaves; wv += gridDim.x * (kThreads / 64)) {
-    const uint32_t pb = wv / kpairs;
-    const uint32_t kb = (wv - pb * kpairs) * 2 + (lane >> 5);
-    const bool valid = kb < kblocks;
-    const uint32_t p = pb * 32 + (lane & 31u);
-    const uint32_t k0 = kb * 32;
-    float y[W];
-    float M = 0.0f;
-    if (valid) {
-      const uint16_t* src = q.x + (int64_t)p * q.ld + k0;
-      uint32_t w[W / 2];
-#pragma unroll
-      for (int i = 0; i < W / 8; ++i) {
-        const uint4 v = ld16(reinterpret_cast<const uint4*>(src) + i);
-        w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-      }
-      unpack<W>(w, pm, y);
-      fwht_inlane<W>(y, q.n);
-      if (q.n > 1) {
-#pragma unroll
-        for (int i = 0; i < W; ++i) y[i] = __fmul_rn(y[i], q.cn);
-      }
-#pragma unroll
-      for (int j = 0; j < W; ++j) M = fmaxf(M, fabsf(y[j]));
-    }
-    // absmax over the 32 rows of the block (lanes sharing bit 5)
-#pragma unroll
-    for (int m = 1; m < 32; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
-    if (!valid) continue;
-    int e = -127;
-    if (M > 0.0f) {
-      e = ilogbf(M) - 3;  // qmax < 8, so M > qmax * 2^(ilogb(M) - 3)
-      if (e < -127) e = -127;
-      while (e < 127 && M > ldexpf(qmax, e)) ++e;
-    }
-    const float inv = ldexpf(1.0f, -e);  // exact power of two (2^-127 is a subnormal)
-    const uint64_t e0 = (uint64_t)p * K + k0;
-    if (q.rotated) store_rotated<W>(q.rotated + e0, y);
-    uint32_t rw[W / 2];
-    if constexpr (RND == 1) sr_draws<W>(e0, q.sr_seed, q.sr_stream, rw);
-    uint32_t packed[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < W; ++j) {
-      const float v = fminf(fmaxf(__fmul_rn(y[j], inv), -qmax), qmax);
-      uint32_t r16 = 0;
-      if constexpr (RND == 1) r16 = (rw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-      packed[j >> 3] |= encode_one<GRID, RND>(v, r16) << (4 * (j & 7));
-    }
-    *reinterpret_cast<uint4*>(q.codes + (e0 >> 1)) =
-        make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    if ((lane & 31u) == 0u)
-      reinterpret_cast<uint8_t*>(q.scales)[(uint64_t)pb * kblocks + kb] = (uint8_t)(e + 127);
-  }
-}
-
-int device_grid_limit() {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      cus = 256;
-  }
-  return cus;
-}
-
-template <template <int, int, int, int> class Launcher, typename... Args>
-hipError_t dispatch_1d(int W, int B, int grid, int rnd, Args&&... args) {
-#define UFP4_CASE(W_, B_, G_, R_)                                  \
-  if (W == W_ && B == B_ && grid == G_ && rnd == R_)               \
-    return Launcher<W_, B_, G_, R_>::run(std::forward<Args>(args)...);
-#define UFP4_GR(W_, B_) \
-  UFP4_CASE(W_, B_, 0, 0) UFP4_CASE(W_, B_, 0, 1) UFP4_CASE(W_, B_, 1, 0) \
-  UFP4_CASE(W_, B_, 1, 1) UFP4_CASE(W_, B_, 2, 0) UFP4_CASE(W_, B_, 2, 1)
-  UFP4_GR(16, 16)
-  UFP4_GR(32, 16)
-  UFP4_GR(32, 32)
-#undef UFP4_GR
-#undef UFP4_CASE
-  return hipErrorInvalidValue;
-}
-
-template <int W, int B, int G, int R>
-struct RowsLauncher {
-  static hipError_t run(const QuantLaunch& q, hipStream_t s) {
-    const uint32_t segs_per_row = (uint32_t)(q.K / W);
-    const uint64_t nseg = (uint64_t)q.P * segs_per_row;
-    if (nseg == 0) return hipSuccess;
-    const uint64_t blocks_needed = (nseg + kThreads - 1) / kThreads;
-    const uint64_t cap = (uint64_t)device_grid_limit() * 16;
-    const uint32_t blocks = (uint32_t)(blocks_needed < cap ? blocks_needed : cap);
-    hipLaunchKernelGGL((k_quant_rows<W, B, G, R>), dim3(blocks), dim3(kThreads), 0, s, q,
-                       make_fastdiv(segs_per_row), (uint32_t)nseg);
-    return hipGetLastError();
-  }
-};
-
-template <int W, int B, int G, int R>
-struct ColsLauncher {
-  static hipError_t run(const QuantLaunch& q, hipStream_t s) {
-    const int total = q.tile_start[q.nseg];
-    if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_quant_cols<W, B, G, R>), dim3(total), dim3(kThreads), 0, s, q);
-    return hipGetLastError();
-  }
-};
-
-int lane_width(int n, int bc) { return (bc == 32 || n >= 32) ? 32 : 16; }
-
-}  // namespace
-
 hipError_t launch_quant_rows(const QuantLaunch& q, hipStream_t s) {
-  return dispatch_1d<RowsLauncher>(lane_width(q.n, q.bc), q.bc, q.grid, q.rounding, q, s);
+  switch (q.grid) {
+    case 0: return quant_rows_grid<0>(q, s);
+    case 1: return quant_rows_grid<1>(q, s);
+    default: return quant_rows_grid<2>(q, s);
+  }
 }
 
 hipError_t launch_quant_cols(const QuantLaunch& q, hipStream_t s) {
-  return dispatch_1d<ColsLauncher>(lane_width(q.n, q.bc), q.bc, q.grid, q.rounding, q, s);
+  switch (q.grid) {
+    case 0: return quant_cols_grid<0>(q, s);
+    case 1: return quant_cols_grid<1>(q, s);
+    default: return quant_cols_grid<2>(q, s);
+  }
 }
 
 hipError_t launch_quant_rows_2d(const QuantLaunch& q, hipStream_t s) {
-  const uint32_t kblocks = (uint32_t)(q.K / 32);
-  const uint32_t kpairs = (kblocks + 1) / 2;
-  const uint64_t nwaves = (uint64_t)(q.P / 32) * kpairs;
-  if (nwaves == 0) return hipSuccess;
-  const uint64_t blocks_needed = (nwaves + 3) / 4;
-  const uint64_t cap = (uint64_t)device_grid_limit() * 16;
-  const uint32_t blocks = (uint32_t)(blocks_needed < cap ? blocks_needed : cap);
-#define UFP4_2D(G_, R_)                                                                     \
-  if (q.grid == G_ && q.rounding == R_) {                                                   \
-    hipLaunchKernelGGL((k_quant_rows_2d<G_, R_>), dim3(blocks), dim3(kThreads), 0, s, q,   \
-                       kpairs, (uint32_t)nwaves);                                           \
-    return hipGetLastError();                                                               \
+  switch (q.grid) {
+    case 0: return quant_rows_2d_grid<0>(q, s);
+    case 1: return quant_rows_2d_grid<1>(q, s);
+    default: return quant_rows_2d_grid<2>(q, s);
   }
-  UFP4_2D(0, 0) UFP4_2D(0, 1) UFP4_2D(1, 0) UFP4_2D(1, 1) UFP4_2D(2, 0) UFP4_2D(2, 1)
-#undef UFP4_2D
-  return hipErrorInvalidValue;
 }
 
 }  // namespace ufp4

@@ -1,0 +1,19 @@
+// Quantizer kernels for the E2M1 codebook (see quant_core.h).
+#include "quant_core.h"
+
+namespace ufp4 {
+
+template <>
+hipError_t quant_rows_grid<2>(const QuantLaunch& q, hipStream_t s) {
+  return qk::run_1d<2, false>(q, s);
+}
+template <>
+hipError_t quant_cols_grid<2>(const QuantLaunch& q, hipStream_t s) {
+  return qk::run_1d<2, true>(q, s);
+}
+template <>
+hipError_t quant_rows_2d_grid<2>(const QuantLaunch& q, hipStream_t s) {
+  return qk::run_2d<2>(q, s);
+}
+
+}  // namespace ufp4
