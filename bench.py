@@ -7,10 +7,18 @@ RTNE on X/W, stochastic rounding on dY; n = 16, 1 x 16 fp32-scale blocks,
 E1M2 grid by default) followed by the three block-scaled 4-bit GEMMs
 FPROP Y = X W^T, DGRAD dX = dY W, WGRAD dW = dY^T X.
 
-Inputs are synthetic (seeded), resident in HBM before the timed region.
+Inputs are synthetic (seeded), resident in HBM before the timed region, and
+rotated over several buffer sets (> the 256 MB last-level cache) so no step
+reads inputs cached by the previous one.  Library calls go through the C ABI
+with prebuilt ctypes arguments (the Python binding's allocation and
+marshalling stay outside the timed region).  Kernel times are HIP events on
+the stream the kernels run on (torch's current stream); per-kernel averages
+come from back-to-back launches of that call alone.
+
 Prints ONE JSON line.  --gpus N > 1 is not supported (one GPU only).
 """
 import argparse
+import ctypes
 import json
 import os
 import platform
@@ -23,6 +31,41 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0     # dense bf16 MFMA (the family the GEMM issues)
 FP4_PEAK_TFLOPS = 10100.0     # dense fp4/fp6 MFMA, context only
+QBYTES_PER_ELEM = 2.75        # bf16 in (2) + 4-bit code (0.5) + fp32 scale / 16 (0.25)
+
+# HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per
+# dispatch, one counter per run) on this workload with the E1M2 grid, scaled by
+# what the same counters read for a plain 1 GiB device copy (bench.py
+# --calibrate-copy).  A figure holds only for the kernel source it was taken
+# on: the sources' hash is recorded and a mismatch reports null.
+FETCH_SCALE, WRITE_SCALE = 1048576 / 524302.3, 1048576 / 1048576.0
+MEASURED_TRAFFIC = {
+    # kernel: (sources, sha256[:16] of them, FETCH_SIZE KiB, WRITE_SIZE KiB)
+    "fprop": (("gemm.hip", "ufp4_internal.h"), "2abdb5ff4ba07787", 74055.3, 262144.0),
+    "dgrad": (("gemm.hip", "ufp4_internal.h"), "2abdb5ff4ba07787", 203094.6, 65536.0),
+    "wgrad": (("gemm.hip", "ufp4_internal.h"), "2abdb5ff4ba07787", 203094.6, 65536.0),
+    "quant_x_row": (("quant_core.h", "ufp4_internal.h"), "78a066d590344e24", 16436.2, 12288.0),
+    "quant_dy_row": (("quant_core.h", "ufp4_internal.h"), "78a066d590344e24", 65606.7, 49152.0),
+    "quant_dy_col": (("quant_core.h", "ufp4_internal.h"), "78a066d590344e24", 65686.4, 71276.4),
+    "quant_x_col": (("quant_core.h", "ufp4_internal.h"), "78a066d590344e24", 16434.6, 12288.9),
+}
+
+
+def measured_traffic(kernel, grid):
+    """HBM bytes per launch of `kernel` as last counted, or None when the
+    counters were not taken for it or its source has changed since."""
+    import hashlib
+    ent = MEASURED_TRAFFIC.get(kernel)
+    if ent is None or grid != "e1m2":
+        return None
+    files, digest, fetch_kib, write_kib = ent
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "rht_bit_block_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != digest:
+        return None
+    return int(round((fetch_kib * FETCH_SCALE + write_kib * WRITE_SCALE) * 1024))
 
 
 def parse():
@@ -32,100 +75,110 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--grid", default="e1m2", choices=["e1m2", "int4", "e2m1"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain device-to-device copy of 1 GiB five times (known "
+                        "bytes, to scale the profiler's FETCH_SIZE / WRITE_SIZE counters)")
     p.add_argument("--sets", type=int, default=3,
                    help="input buffer sets rotated across steps (defeats the 256 MB MALL)")
     return p.parse_args()
 
 
-def build_step(U, wl, grid, device):
-    X, W, dY = wl.tensors["X"], wl.tensors["W"], wl.tensors["dY"]
-    sf, sd, sw = wl.meta["sign_seeds"]
-    sr = wl.meta["sr_seed"]
-    mk = lambda seed, rnd, stream=0: U.make_cfg(grid, rnd, U.UFP4_SCALE_F32, 1, 16, 16,  # noqa: E731
-                                                  sign_seed=seed, sr_seed=sr, sr_stream=stream)
-    cfg = {
-        "x_row": mk(sf, U.UFP4_RTNE), "w_row": mk(sf, U.UFP4_RTNE),
-        "dy_row": mk(sd, U.UFP4_SR, 0), "w_col": mk(sd, U.UFP4_RTNE),
-        "dy_col": mk(sw, U.UFP4_SR, 1), "x_col": mk(sw, U.UFP4_RTNE),
-    }
-    M, K = X.shape
-    N = W.shape[0]
+class Workload:
+    """The dense layer's 9 library calls, as raw C-ABI calls with prebuilt
+    ctypes arguments, for each input buffer set."""
 
-    def alloc(P, Kd):
-        return (torch.empty((P, Kd // 2), dtype=torch.uint8, device=device),
-                torch.empty((P, Kd // 16), dtype=torch.float32, device=device))
+    def __init__(self, U, torch, grid, nsets):
+        import workloads
+        self.U, self.torch = U, torch
+        base = workloads.config2("cuda")
+        self.sets = [base.tensors] + [{k: v.clone() for k, v in base.tensors.items()}
+                                      for _ in range(nsets - 1)]
+        X = base.tensors["X"]
+        self.M, self.K = X.shape
+        self.N = base.tensors["W"].shape[0]
+        sf, sd, sw = base.meta["sign_seeds"]
+        sr = base.meta["sr_seed"]
+        mk = lambda seed, rnd, st=0: U.make_cfg(grid, rnd, U.UFP4_SCALE_F32, 1, 16, 16,  # noqa: E731
+                                                  sign_seed=seed, sr_seed=sr, sr_stream=st)
+        # (name, tensor, along, cfg)
+        self.qcalls = [("x_row", "X", 0, mk(sf, U.UFP4_RTNE)), ("w_row", "W", 0, mk(sf, U.UFP4_RTNE)),
+                       ("dy_row", "dY", 0, mk(sd, U.UFP4_SR, 0)), ("w_col", "W", 1, mk(sd, U.UFP4_RTNE)),
+                       ("dy_col", "dY", 1, mk(sw, U.UFP4_SR, 1)), ("x_col", "X", 1, mk(sw, U.UFP4_RTNE))]
+        self.lib = U.lib_handle()
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        dev = "cuda"
+        self.q = {}
+        for name, tn, along, cfg in self.qcalls:
+            rows, cols = base.tensors[tn].shape
+            P, Kd = (cols, rows) if along else (rows, cols)
+            codes = torch.empty((P, Kd // 2), dtype=torch.uint8, device=dev)
+            scales = torch.empty((P, Kd // 16), dtype=torch.float32, device=dev)
+            self.q[name] = U.QTensor(codes, scales, P, Kd, cfg)
+        M, K, N = self.M, self.K, self.N
+        self.out = {"fprop": torch.empty((M, N), dtype=torch.float32, device=dev),
+                    "dgrad": torch.empty((M, K), dtype=torch.float32, device=dev),
+                    "wgrad": torch.empty((N, K), dtype=torch.float32, device=dev)}
+        self.gcalls = [("fprop", "x_row", "w_row"), ("dgrad", "dy_row", "w_col"),
+                       ("wgrad", "dy_col", "x_col")]
+        self._keep = []
+        self.calls = [self._build_calls(s) for s in self.sets]
+        self.elems = {name: base.tensors[tn].numel() for name, tn, _, _ in self.qcalls}
+        self.flops = {"fprop": 2.0 * M * N * K, "dgrad": 2.0 * M * K * N, "wgrad": 2.0 * N * K * M}
 
-    bufs = {"x_row": alloc(M, K), "w_row": alloc(N, K), "dy_row": alloc(M, N),
-            "w_col": alloc(K, N), "dy_col": alloc(N, M), "x_col": alloc(K, M)}
-    Y = torch.empty((M, N), dtype=torch.float32, device=device)
-    dX = torch.empty((M, K), dtype=torch.float32, device=device)
-    dW = torch.empty((N, K), dtype=torch.float32, device=device)
-    src = {"x_row": (X, 0), "w_row": (W, 0), "dy_row": (dY, 0), "w_col": (W, 1),
-           "dy_col": (dY, 1), "x_col": (X, 1)}
-    q = {}
+    def _build_calls(self, tensors):
+        lib, calls = self.lib, []
+        for name, tn, along, cfg in self.qcalls:
+            t = tensors[tn]
+            rows, cols = t.shape
+            q = self.q[name]
+            args = (ctypes.c_void_p(t.data_ptr()), rows, cols, t.stride(0), along,
+                    ctypes.byref(cfg), ctypes.c_void_p(q.codes.data_ptr()),
+                    ctypes.c_void_p(q.scales.data_ptr()), None, self.stream)
+            calls.append(("quant_" + name, lib.ufp4_rht_quant, args))
+        for name, a, b in self.gcalls:
+            qa, qb = self.q[a].c(), self.q[b].c()
+            self._keep += [qa, qb]
+            out = self.out[name]
+            fn = getattr(lib, "ufp4_gemm_" + name)
+            calls.append((name, fn, (ctypes.byref(qa), ctypes.byref(qb),
+                                     ctypes.c_void_p(out.data_ptr()), out.stride(0), self.stream)))
+        return calls
 
-    def quant(name, inputs):
-        t, along = inputs[name]
-        c, s = bufs[name]
-        q[name], _ = U.ufp4_rht_quant(t, along, cfg[name], codes=c, scales=s)
+    def step(self, i):
+        for name, fn, args in self.calls[i % len(self.calls)]:
+            st = fn(*args)
+            if st:
+                raise RuntimeError(f"{name} failed: {self.U.ufp4_status_string(st)}")
 
-    order = ["x_row", "w_row", "dy_row", "w_col", "dy_col", "x_col"]
-
-    def step(inputs, timer=None):
-        for name in order:
-            if timer:
-                timer.begin("quant_" + name)
-            quant(name, inputs)
-            if timer:
-                timer.end("quant_" + name)
-        for name, fn, a, b, out in (("fprop", U.ufp4_gemm_fprop, "x_row", "w_row", Y),
-                                    ("dgrad", U.ufp4_gemm_dgrad, "dy_row", "w_col", dX),
-                                    ("wgrad", U.ufp4_gemm_wgrad, "dy_col", "x_col", dW)):
-            if timer:
-                timer.begin(name)
-            fn(q[a], q[b], out)
-            if timer:
-                timer.end(name)
-
-    sizes = {"M": M, "K": K, "N": N}
-    quant_elems = {"x_row": M * K, "w_row": N * K, "dy_row": M * N, "w_col": N * K,
-                   "dy_col": M * N, "x_col": M * K}
-    return step, src, sizes, quant_elems
-
-
-class EventTimer:
-    """HIP events on torch's current stream (the stream the library launches on)."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pending = {}
-        self.samples = {}
-
-    def begin(self, name):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        self.pending[name] = e
-
-    def end(self, name):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        self.samples.setdefault(name, []).append((self.pending.pop(name), e))
-
-    def mean_ms(self):
-        self.torch.cuda.synchronize()
-        return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in self.samples.items()}
+    def time_call(self, idx, reps):
+        """Average duration of call idx over reps back-to-back launches
+        (rotating input sets), HIP events on the launch stream."""
+        torch = self.torch
+        for i in range(2):
+            _, fn, args = self.calls[i % len(self.calls)][idx]
+            fn(*args)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            _, fn, args = self.calls[i % len(self.calls)][idx]
+            fn(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
 
 
 def cpu_oracle_baseline(grid):
     """The oracle as it stands on a bounded sample of the same workload: the
-    dense step restricted to M' = 256 tokens and N' = 256 output features
-    (full K = 2048): six quantizations and three fp64 GEMMs."""
-    import numpy as np
-
+    dense step restricted to M' = 6144 tokens and N' = 6144 output features
+    (full K = 2048): six quantizations, six dequantizations and three fp64
+    GEMMs.  The quantizer is single-threaded numpy; the GEMMs use numpy's
+    BLAS thread pool, whose size is reported as the cores used."""
     import oracle as O
     import workloads
     gi = {"e1m2": 0, "int4": 1, "e2m1": 2}[grid]
-    Mp, Np, K = 256, 256, 2048
+    Mp, Np, K = 6144, 6144, 2048
     wl = workloads.config2("cpu", M=Mp, K=K, N=Np)
     X, W, dY = (workloads.bits(wl.tensors[k]) for k in ("X", "W", "dY"))
     sf, sd, sw = wl.meta["sign_seeds"]
@@ -145,12 +198,18 @@ def cpu_oracle_baseline(grid):
     O.gemm_ref(deq(qdyt, spec(sw, 1)), deq(qxt, spec(sw, 0)))
     t = time.perf_counter() - t0
     flops = 3 * 2.0 * Mp * Np * K
-    qbytes = 2.75 * (2 * Mp * K + 2 * Np * K + 2 * Mp * Np)
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    qbytes = QBYTES_PER_ELEM * (2 * Mp * K + 2 * Np * K + 2 * Mp * Np)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"dense step at M'={Mp}, N'={Np}, K={K} (6 quantizations + 3 fp64 GEMMs), "
-                      f"{t:.2f} s; quantizer part {qbytes / tq / 1e9:.4f} GB/s on 1 core",
+            "sample": f"dense step at M'={Mp}, N'={Np}, K={K} (6 quantizations + 3 fp64 "
+                      f"GEMMs) in {t:.2f} s; its quantizer part ran at "
+                      f"{qbytes / tq / 1e9:.4f} GB/s (numpy, single-threaded); "
+                      "value is the sample's GEMM flops over its whole time",
             "quant_GBps": round(qbytes / tq / 1e9, 6), "seconds": round(t, 3),
             "cpu": platform.processor() or platform.machine()}
 
@@ -159,72 +218,70 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no collectives; see the design notes on sharding)", file=sys.stderr)
+              "(the path has no collectives; the design notes describe how it would shard)",
+              file=sys.stderr)
         sys.exit(2)
     global torch
     import torch
 
-    import rht_bit_block_amd as U
-    import workloads
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
+        return
 
-    device = "cuda"
+    import rht_bit_block_amd as U
+
     grid = {"e1m2": U.UFP4_E1M2, "int4": U.UFP4_INT4, "e2m1": U.UFP4_E2M1}[args.grid]
-    sets = []
-    for i in range(max(1, args.sets)):
-        wl = workloads.config2(device)
-        if i:   # distinct buffers with the same contents (defeats cache reuse across steps)
-            wl.tensors = {k: v.clone() for k, v in wl.tensors.items()}
-        sets.append(wl)
-    step, _, sz, quant_elems = build_step(U, sets[0], grid, device)
-    inputs = [{"x_row": (s.tensors["X"], 0), "w_row": (s.tensors["W"], 0),
-               "dy_row": (s.tensors["dY"], 0), "w_col": (s.tensors["W"], 1),
-               "dy_col": (s.tensors["dY"], 1), "x_col": (s.tensors["X"], 1)} for s in sets]
+    wl = Workload(U, torch, grid, max(1, args.sets))
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
-        step(inputs[i % len(inputs)])
+        wl.step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(args.steps):
-        step(inputs[i % len(inputs)])
+        wl.step(i)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(stop) / args.steps
 
-    # per-kernel averages (separate pass, events around every launch)
-    timer = EventTimer(torch)
-    for i in range(max(5, args.steps // 2)):
-        step(inputs[i % len(inputs)], timer)
-    per = timer.mean_ms()
+    # per-kernel averages: each call alone, back to back
+    names = [c[0] for c in wl.calls[0]]
+    per = {n: wl.time_call(i, max(10, args.steps)) for i, n in enumerate(names)}
 
-    M, K, N = sz["M"], sz["K"], sz["N"]
-    gemm_flops = {"fprop": 2.0 * M * N * K, "dgrad": 2.0 * M * K * N, "wgrad": 2.0 * N * K * M}
-    total_flops = sum(gemm_flops.values())
-    qbytes = {k: 2.75 * v for k, v in quant_elems.items()}  # 2 B in + 0.5 B codes + 0.25 B scales
-    gemm_ms = sum(per[k] for k in gemm_flops)
-    quant_ms = sum(per["quant_" + k] for k in qbytes)
     kernels = {}
-    for k, f in gemm_flops.items():
+    for k, f in wl.flops.items():
         kernels[k] = {"ms": round(per[k], 4), "TFLOP/s": round(f / per[k] / 1e9, 2),
                       "frac_bf16_peak": round(f / per[k] / 1e9 / BF16_PEAK_TFLOPS, 4)}
+    qbytes = {k: QBYTES_PER_ELEM * v for k, v in wl.elems.items()}
     for k, b in qbytes.items():
         kernels["quant_" + k] = {"ms": round(per["quant_" + k], 4),
                                  "GB/s": round(b / per["quant_" + k] / 1e6, 1),
                                  "frac_hbm_peak": round(b / per["quant_" + k] / 1e6 / HBM_PEAK_GBPS, 4)}
+    gemm_ms = sum(per[k] for k in wl.flops)
+    quant_ms = sum(per["quant_" + k] for k in qbytes)
+    total_flops = sum(wl.flops.values())
     # dominant kernel: the one with the largest share of the step
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
-    if dom in gemm_flops:
-        ach = gemm_flops[dom] / per[dom] / 1e9
+    if dom in wl.flops:
+        ach = wl.flops[dom] / per[dom] / 1e9
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(dom, args.grid), "traffic_unit": "B/launch"}
     else:
         ach = qbytes[dom[6:]] / per[dom] / 1e6
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(dom, args.grid), "traffic_unit": "B/launch"}
     quant_gbps = sum(qbytes.values()) / quant_ms / 1e6
     value = total_flops / (ms_step * 1e-3) / 1e12
 
@@ -243,12 +300,12 @@ def main():
         "vs_baseline": None, "dtype": args.grid,
         "dtype_detail": "bf16 in; fp32 rotate/scale/round; 4-bit codes; split-bf16 MFMA, fp32 accumulate",
         "data": "synthetic (seeded torch generators; dense linear-layer tensors)",
-        "config": {"workload": f"dense linear layer M={M} K={K} N={N}: 6 fused RHT(n=16)+1x16 "
-                               f"{args.grid} quantizations (SR on dY) + FPROP/DGRAD/WGRAD",
-                   "global_batch": M, "seq_len": None, "parallelism": "single GPU"},
+        "config": {"workload": f"dense linear layer M={wl.M} K={wl.K} N={wl.N}: 6 fused RHT(n=16)"
+                               f"+1x16 {args.grid} quantizations (SR on dY) + FPROP/DGRAD/WGRAD",
+                   "global_batch": wl.M, "seq_len": None, "parallelism": "single GPU"},
         "roofline": roof,
         "quant": {"GB/s": round(quant_gbps, 1), "frac_hbm_peak": round(quant_gbps / HBM_PEAK_GBPS, 4),
-                  "ms": round(quant_ms, 4), "bytes_per_elem": 2.75},
+                  "ms": round(quant_ms, 4), "bytes_per_elem": QBYTES_PER_ELEM},
         "gemm": {"TFLOP/s": round(total_flops / gemm_ms / 1e9, 2),
                  "frac_bf16_peak": round(total_flops / gemm_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
                  "frac_fp4_peak": round(total_flops / gemm_ms / 1e9 / FP4_PEAK_TFLOPS, 4),

@@ -123,7 +123,7 @@ int ufp4_rht_quant(const void* x, int64_t rows, int64_t cols, int64_t ld, int32_
  * indices continue across segments (segment g starts at cols*row_offsets[g]).
  * row_offsets: HOST int64 [num_segments+1], ascending, 0 .. rows, each
  * segment length a multiple of lcm(rht_n, block_cols).  1D blocks only;
- * num_segments <= 256. */
+ * 1 <= num_segments <= 128 (else UFP4_ERR_INVALID_ARG). */
 int ufp4_rht_quant_segmented(const void* x, int64_t rows, int64_t cols, int64_t ld,
                              const int64_t* row_offsets, int32_t num_segments,
                              const ufp4_quant_cfg* cfg, uint8_t* codes, void* scales,
