@@ -149,6 +149,9 @@ int gemm_dense(const ufp4_qtensor* A, const ufp4_qtensor* B, float* C, int64_t l
   g.tile_start[0] = 0;
   g.tile_start[1] = (int32_t)tiles;
   g.total_tiles = (int32_t)tiles;
+  if (gemm_mx_supported(g) && aligned(g.a_scales, 4) && aligned(g.b_scales, 4) &&
+      aligned(g.a_codes, 16) && aligned(g.b_codes, 16))
+    return hip_status(launch_gemm_mx(g, (hipStream_t)stream));
   return hip_status(launch_gemm(g, (hipStream_t)stream));
 }
 

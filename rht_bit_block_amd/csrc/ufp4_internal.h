@@ -89,6 +89,10 @@ struct GemmLaunch {
 };
 
 hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s);
+// Power-of-two (E8M0) scales on the scaled matrix cores; only for launches
+// gemm_mx_supported() accepts.
+bool gemm_mx_supported(const GemmLaunch& g);
+hipError_t launch_gemm_mx(const GemmLaunch& g, hipStream_t s);
 
 hipError_t launch_dequant(const uint8_t* codes, const void* scales, int64_t P, int64_t K,
                           int32_t grid, int32_t scale_mode, int32_t br, int32_t bc, float* out,

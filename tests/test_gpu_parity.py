@@ -169,6 +169,22 @@ def test_gemm_2d_and_transpose(grid):
     assert O.rel_fro(dX, O.gemm_ref(oracle_dequant64(rdy, cfg), dw.T)) <= GEMM_TOL
 
 
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("K", [160, 384, 512])
+def test_gemm_pow2_paths(grid, K):
+    """Power-of-two 32 x 32 blocks through every GEMM path: K % 256 == 0
+    (wide-step FP4 / FP8 scaled matrix cores), K % 128 == 0, and K = 160
+    (split-bf16 fallback); 3 ragged row tiles of A, 2 of B."""
+    _print_case("pow2 gemm", grid, K)
+    cfg = U.make_cfg(grid, U.UFP4_SR, U.UFP4_SCALE_POW2, 32, 32, 1, sr_seed=77)
+    ta, tb = rand_bits(544, K, 11), rand_bits(288, K, 12)
+    qa, ra = compare_quant(ta, 0, cfg, with_rotated=False)
+    qb, rb = compare_quant(tb, 0, cfg, with_rotated=False)
+    C = U.ufp4_gemm_fprop(qa, qb).cpu().numpy()
+    ref = O.gemm_ref(oracle_dequant64(ra, cfg), oracle_dequant64(rb, cfg))
+    assert O.rel_fro(C, ref) <= GEMM_TOL
+
+
 def test_segmented_quant_and_grouped_gemms():
     """Four experts (one empty), per-expert transposed operands, and the
     three grouped GEMMs against per-expert oracle products."""
