@@ -421,23 +421,147 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmLaunch g) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Two waves per SIMD: 8 waves of 128 x 64 (4 x 2 MFMA tiles, 128 AGPRs each)
+// cover the 256 x 256 tile, and each thread decodes one row of one operand
+// per step (waves 0-3: A, 4-7: B).  With two waves resident on every SIMD the
+// hardware issues one wave's decode VALU while the other wave's MFMAs run,
+// instead of relying on the instruction order inside a single wave.
+// ---------------------------------------------------------------------------
+constexpr int kThreads8 = 512;
+
+template <int GRID, int SMODE>
+__device__ __forceinline__ void decode_row(const Fetched& f, const ResidualMasks& rm, uint4* buf,
+                                           int part, int row) {
+  const float s0 = finalize_scale<SMODE>(f.s0, f.v0);
+  const float s1 = finalize_scale<SMODE>(f.s1, f.v1);
+#pragma unroll
+  for (int cw = 0; cw < 4; ++cw) {
+    const uint32_t word = cw == 0 ? f.c0.x : (cw == 1 ? f.c0.y : (cw == 2 ? f.c1.x : f.c1.y));
+    const float su = (cw < 2 ? s0 : s1) * Dec<GRID>::unit;
+    const float nb = -Dec<GRID>::bias * su;
+    uint32_t ev, od, h[4], l[4];
+    decode8<GRID>(word, ev, od);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) decode_pair(ev, od, i, su, nb, rm, h[i], l[i]);
+    buf[(part * kChunks + cw) * TM + row] = make_uint4(h[0], h[1], h[2], h[3]);
+    buf[((part + 1) * kChunks + cw) * TM + row] = make_uint4(l[0], l[1], l[2], l[3]);
+  }
+}
+
+struct Frags8 {
+  bf16x8 ah[4], al[4], bh[2], bl[2];
+};
+
+__device__ __forceinline__ void load_frags8(const uint4* buf, int kh, int lane, int wm, int wn,
+                                            Frags8& f) {
+  const int chunk = 2 * kh + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ra = wm * 128 + i * 32 + (lane & 31);
+    f.ah[i] = __builtin_bit_cast(bf16x8, buf[(0 * kChunks + chunk) * TM + ra]);
+    f.al[i] = __builtin_bit_cast(bf16x8, buf[(1 * kChunks + chunk) * TM + ra]);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int rb = wn * 64 + j * 32 + (lane & 31);
+    f.bh[j] = __builtin_bit_cast(bf16x8, buf[(2 * kChunks + chunk) * TM + rb]);
+    f.bl[j] = __builtin_bit_cast(bf16x8, buf[(3 * kChunks + chunk) * TM + rb]);
+  }
+}
+
+__device__ __forceinline__ void mfma_khalf8(floatx16 (&acc)[4][2], const Frags8& f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ah[i], f.bh[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.ah[i], f.bl[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.al[i], f.bh[j], acc[i][j], 0, 0, 0);
+    }
+}
+
+template <int GRID, int SMODE>
+__global__ __launch_bounds__(kThreads8) void k_gemm8(GemmLaunch g) {
+  extern __shared__ uint4 lds[];
+  int tm, tn;
+  const Problem pr = resolve(g, blockIdx.x, tm, tn);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;   // 2 x 4 waves of 128 x 64
+  const int op = tid >> 8, row = tid & 255;  // the operand row this thread decodes
+  const ResidualMasks rm = make_masks();
+
+  const OperandCursor cur = op == 0
+      ? make_cursor(pr.a_codes, pr.a_scales, g.scale_mode, g.a_br, g.a_bc,
+                    pr.a_row0 + (int64_t)tm * TM + row, pr.a_row0 + pr.a_rows, pr.a_row0, pr.K)
+      : make_cursor(pr.b_codes, pr.b_scales, g.scale_mode, g.b_br, g.b_bc,
+                    pr.b_row0 + (int64_t)tn * TN + row, pr.b_row0 + pr.b_rows, pr.b_row0, pr.K);
+  const int part = 2 * op;
+  const int nsteps = (int)((pr.K + TK - 1) / TK);
+  constexpr int kStage = kParts * kChunks * TM;
+
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
+
+  decode_row<GRID, SMODE>(fetch<SMODE>(cur, 0), rm, lds, part, row);
+  Fetched x = fetch<SMODE>(cur, 1), y;
+  __syncthreads();
+
+  auto body = [&](int step, const Fetched& d, Fetched& l) {
+    const uint4* cb = lds + (step & 1) * kStage;
+    uint4* nb = lds + ((step + 1) & 1) * kStage;
+    l = fetch<SMODE>(cur, step + 2);
+    Frags8 f;
+    load_frags8(cb, 0, lane, wm, wn, f);
+    mfma_khalf8(acc, f);
+    decode_row<GRID, SMODE>(d, rm, nb, part, row);
+    load_frags8(cb, 1, lane, wm, wn, f);
+    mfma_khalf8(acc, f);
+    __syncthreads();
+  };
+  int step = 0;
+  for (; step + 1 < nsteps; step += 2) {
+    body(step, x, y);
+    body(step + 1, y, x);
+  }
+  if (step < nsteps) body(step, x, y);
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t col = (int64_t)tn * TN + wn * 64 + j * 32 + (lane & 31);
+      if (col >= pr.b_rows) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t rr = (int64_t)tm * TM + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (rr < pr.a_rows) pr.c[rr * g.ldc + col] = acc[i][j][r];
+      }
+    }
+}
+
 }  // namespace
 
 template <int GRID, int SMODE>
 hipError_t launch_one(const GemmLaunch& g, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm<GRID, SMODE>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm8<GRID, SMODE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_gemm<GRID, SMODE>), dim3(g.total_tiles), dim3(kThreads), kLdsBytes, s, g);
+  hipLaunchKernelGGL((k_gemm8<GRID, SMODE>), dim3(g.total_tiles), dim3(kThreads8), kLdsBytes, s, g);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
   if (g.total_tiles == 0) return hipSuccess;
+  if (gemm_rd_supported(g)) return launch_gemm_rd(g, s);
   const int key = g.grid * 2 + g.scale_mode;
   switch (key) {
     case 0: return launch_one<0, 0>(g, s);
