@@ -199,26 +199,43 @@ __device__ __forceinline__ void issue_stage(const RdCtx& c, int stage, int slot)
   }
 }
 
-// Decode row `row` of operand `op` (0 A, 1 B) for 16-wide K step j (0..7) of
-// the raw stage at `raw` into the decoded buffer `hl`.
+// Raw inputs of one row of operand `op` (0 A, 1 B) for 16-wide K step j
+// (0..7) of the raw stage at `raw`: two code dwords (elements 16 j .. +15)
+// and the block scale (zero past K).
+struct RawRow {
+  uint2 w;
+  float s;
+};
+
+template <int BC>
+__device__ __forceinline__ RawRow read_row(const uint8_t* raw, int op, int row, int j,
+                                           bool valid) {
+  using L = Layout<BC>;
+  RawRow r;
+  r.w = *reinterpret_cast<const uint2*>(raw + op * TM * 64 + code_off(row, j >> 1) + 8 * (j & 1));
+  const float sc = *reinterpret_cast<const float*>(raw + L::CODES + op * TM * L::SB + row * L::SB +
+                                                   4 * ((j * 16) / BC));
+  r.s = valid ? sc : 0.0f;
+  return r;
+}
+
+// Decode half `hf` (8 elements) of a raw row into the decoded buffer `hl`.
+template <int GRID>
+__device__ __forceinline__ void decode_half(const RawRow& r, uint8_t* hl, int op, int row, int hf,
+                                            const ResidualMasks& rm) {
+  bf16x8 hi, lo;
+  decode_frag<GRID>(hf ? r.w.y : r.w.x, r.s, rm, hi, lo);
+  uint8_t* base = hl + op * 2 * (2 * TM * 16);
+  *reinterpret_cast<bf16x8*>(base + (hf * TM + row) * 16) = hi;
+  *reinterpret_cast<bf16x8*>(base + ((2 + hf) * TM + row) * 16) = lo;
+}
+
 template <int GRID, int BC>
 __device__ __forceinline__ void decode_row(const uint8_t* raw, uint8_t* hl, int op, int row,
                                            int j, bool valid, const ResidualMasks& rm) {
-  using L = Layout<BC>;
-  // elements 16 j .. 16 j + 15: dwords 2 (j & 1), +1 of chunk j / 2
-  const uint2 w = *reinterpret_cast<const uint2*>(raw + op * TM * 64 + code_off(row, j >> 1) +
-                                                  8 * (j & 1));
-  float sc = *reinterpret_cast<const float*>(raw + L::CODES + op * TM * L::SB + row * L::SB +
-                                             4 * ((j * 16) / BC));
-  sc = valid ? sc : 0.0f;
-  bf16x8 h0, l0, h1, l1;
-  decode_frag<GRID>(w.x, sc, rm, h0, l0);
-  decode_frag<GRID>(w.y, sc, rm, h1, l1);
-  uint8_t* base = hl + op * 2 * (2 * TM * 16);
-  *reinterpret_cast<bf16x8*>(base + (0 * TM + row) * 16) = h0;
-  *reinterpret_cast<bf16x8*>(base + (1 * TM + row) * 16) = h1;
-  *reinterpret_cast<bf16x8*>(base + (2 * TM + row) * 16) = l0;
-  *reinterpret_cast<bf16x8*>(base + (3 * TM + row) * 16) = l1;
+  const RawRow r = read_row<BC>(raw, op, row, j, valid);
+  decode_half<GRID>(r, hl, op, row, 0, rm);
+  decode_half<GRID>(r, hl, op, row, 1, rm);
 }
 
 struct Frags {
@@ -354,28 +371,44 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
     decode_row<GRID, BC>(lds, hlb, 0, tid, 0, 0 < nkb, rm);
     decode_row<GRID, BC>(lds, hlb, 1, tid, 0, 0 < nkb, rm);
     __syncthreads();
-    // Step i: the 48 MFMAs of K step i (decoded buffer i & 1) run while this
-    // thread decodes its A and B rows of step i+1 into the other buffer.  Raw
-    // stage s (8 steps) is issued at step 8 (s - 1), so it has landed long
-    // before step 8 s - 1 decodes from it.
+    // Step i (fragments F of step i in registers):
+    //   24 MFMAs of step i, while this thread decodes its A and B rows of
+    //   step i+1 into the other decoded buffer;
+    //   barrier (step i+1 fully decoded; every wave has read step i's buffer);
+    //   fragment reads of step i+1, in flight during the other 24 MFMAs of step i.
+    // Raw stage s (8 steps) is issued at step 8 (s - 1) and waited for two
+    // steps before its first decode.
+    Frags f, fn;
+    load_frags(hlb, lane, wm, wn, f);
     for (int i = 0; i < nsteps; ++i) {
       if (i > 0 && (i & 7) == 0) issue_stage<BC>(c, (i >> 3) + 1, ((i >> 3) + 1) & 1);
-      Frags f;
-      load_frags(hlb + (i & 1) * L::HL, lane, wm, wn, f);
       const int n = i + 1;                                   // step being decoded
       const uint8_t* raw = lds + ((n >> 3) & 1) * L::RAW;
       const bool vn = n < nsteps && (n * 16) / BC < nkb;
       uint8_t* hn = hlb + (n & 1) * L::HL;
+      const RawRow ra = read_row<BC>(raw, 0, tid, n & 7, vn);
+      const RawRow rb = read_row<BC>(raw, 1, tid, n & 7, vn);
+      // four 8-element decodes, each spread over five MFMAs
 #pragma unroll
-      for (int m = 0; m < 8; ++m) mfma_step(acc, f, m);
-      decode_row<GRID, BC>(raw, hn, 0, tid, n & 7, vn, rm);
+      for (int p = 0; p < 4; ++p) {
 #pragma unroll
-      for (int m = 8; m < 28; ++m) mfma_step(acc, f, m);
-      decode_row<GRID, BC>(raw, hn, 1, tid, n & 7, vn, rm);
+        for (int m = 5 * p; m < 5 * p + 5; ++m) mfma_step(acc, f, m);
+        decode_half<GRID>(p < 2 ? ra : rb, hn, p >> 1, tid, p & 1, rm);
 #pragma unroll
-      for (int m = 28; m < 48; ++m) mfma_step(acc, f, m);
+        for (int q = 0; q < 5; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // then up to 8 VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int m = 20; m < 24; ++m) mfma_step(acc, f, m);
       if (((i + 2) & 7) == 0) wait_vmcnt<0>();   // raw stage of step i+2 has landed
       __syncthreads();
+      load_frags(hn, lane, wm, wn, fn);
+#pragma unroll
+      for (int m = 24; m < 48; ++m) mfma_step(acc, f, m);
+      f = fn;
     }
   }
 
