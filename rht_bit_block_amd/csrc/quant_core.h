@@ -352,13 +352,22 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantLaunch q, FastDiv 
 // ---------------------------------------------------------------------------
 // Column-wise (and segmented column-wise), 1 x B blocks.  A = X^T: a work-
 // group stages X[k0 : k0+128, p0 : p0+64] in LDS and each lane pulls W
-// consecutive k of one column p.
+// consecutive k of one column p.  The tile is stored as 32-bit words holding
+// rows (2i, 2i+1) of one column -- exactly the packed bf16 pairs the
+// quantizer consumes -- so a lane reads W/2 words; the staging thread forms
+// the pairs of 8 columns from two 16-byte row loads with 8 byte permutes.
+// Words are [pair row][column], columns XOR-swizzled in groups of 4 by bits
+// 3..5 of the pair row: the 4-word staging writes stay contiguous, and lanes
+// reading pair rows 8 apart (one Hadamard chunk spread over adjacent lanes)
+// hit different banks.
 // ---------------------------------------------------------------------------
-constexpr int kTK = 128, kTP = 64, kLdsPitch = kTP + 2;
+constexpr int kTK = 128, kTP = 64;
+
+__device__ __forceinline__ int col_swz(int pr, int col) { return col ^ (((pr >> 3) & 7) << 2); }
 
 template <int W, int B, int N, int GRID, int RND>
 __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantLaunch q) {
-  __shared__ uint16_t tile[kTK * kLdsPitch];
+  __shared__ uint32_t tile[(kTK / 2) * kTP];
   constexpr int lpc = N > W ? N / W : 1;
   // which segment / tile
   const int bid = blockIdx.x;
@@ -375,23 +384,36 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantLaunch q) {
   const int krows = (int)min<int64_t>(kTK, L - k0);
   const int pcols = (int)min<int64_t>(kTP, C - p0);
 
-  // Stage the tile: 128 rows x 64 columns of bf16, 16-byte loads.
-  for (int i = threadIdx.x; i < kTK * (kTP / 8); i += kThreads) {
-    const int r = i / (kTP / 8), c8 = (i % (kTP / 8)) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < krows) {
-      const uint16_t* src = q.x + (seg0 + k0 + r) * q.ld + p0 + c8;
-      if (c8 + 8 <= pcols) {
-        v = ld16(src);
-      } else {
-        uint16_t tmp[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int j = 0; j < 8 && c8 + j < pcols; ++j) tmp[j] = src[j];
-        v = make_uint4(tmp[0] | (tmp[1] << 16), tmp[2] | (tmp[3] << 16), tmp[4] | (tmp[5] << 16),
-                       tmp[6] | (tmp[7] << 16));
+  // Stage: task = (pair row i, group of 8 columns); 64 x 8 tasks, 2 per thread.
+  for (int t = threadIdx.x; t < (kTK / 2) * (kTP / 8); t += kThreads) {
+    const int i = t / (kTP / 8), c8 = (t % (kTP / 8)) * 8;
+    uint4 ra = make_uint4(0, 0, 0, 0), rb = ra;
+    const int r = 2 * i;
+    const uint16_t* src = q.x + (seg0 + k0 + r) * q.ld + p0 + c8;
+    if (c8 + 8 <= pcols) {
+      if (r < krows) ra = ld16(src);
+      if (r + 1 < krows) rb = ld16(src + q.ld);
+    } else {
+      uint16_t ta[8] = {0, 0, 0, 0, 0, 0, 0, 0}, tb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int j = 0; j < 8 && c8 + j < pcols; ++j) {
+        if (r < krows) ta[j] = src[j];
+        if (r + 1 < krows) tb[j] = src[q.ld + j];
       }
+      ra = make_uint4(ta[0] | (ta[1] << 16), ta[2] | (ta[3] << 16), ta[4] | (ta[5] << 16),
+                      ta[6] | (ta[7] << 16));
+      rb = make_uint4(tb[0] | (tb[1] << 16), tb[2] | (tb[3] << 16), tb[4] | (tb[5] << 16),
+                      tb[6] | (tb[7] << 16));
     }
-    uint32_t* d = reinterpret_cast<uint32_t*>(&tile[r * kLdsPitch + c8]);
-    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    const uint32_t a4[4] = {ra.x, ra.y, ra.z, ra.w}, b4[4] = {rb.x, rb.y, rb.z, rb.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[2 * j] = __builtin_amdgcn_perm(b4[j], a4[j], 0x05040100u);       // column 2j
+      o[2 * j + 1] = __builtin_amdgcn_perm(b4[j], a4[j], 0x07060302u);   // column 2j+1
+    }
+    uint32_t* d = tile + i * kTP;
+    *reinterpret_cast<uint4*>(d + col_swz(i, c8)) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(d + col_swz(i, c8 + 4)) = make_uint4(o[4], o[5], o[6], o[7]);
   }
   __syncthreads();
 
@@ -402,18 +424,19 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantLaunch q) {
   const uint32_t neg1 = (qpos & 1u) ? 0x80000000u : 0u;
   const uint32_t neg2 = (qpos & 2u) ? 0x80000000u : 0u;
   for (int u = threadIdx.x; u < kTP * kSegsPerCol; u += kThreads) {
-    // lanes of one chunk are adjacent: u = ((kgroup * 64) + col) * lpc + qpos
-    const int qq = u % lpc;
-    const int rest = u / lpc;
-    const int col = rest % kTP;
-    const int kseg = (rest / kTP) * lpc + qq;
+    // consecutive lanes take consecutive W-segments of one column, so a
+    // column's codes and scales are written by adjacent lanes (contiguous
+    // stores), and the lanes of one Hadamard chunk are adjacent
+    const int kseg = u % kSegsPerCol;
+    const int col = u / kSegsPerCol;
     const int kr = kseg * W;
     if (kr >= krows || col >= pcols) continue;  // whole chunks drop out together
     uint32_t w[W / 2];
 #pragma unroll
-    for (int i = 0; i < W / 2; ++i)
-      w[i] = (uint32_t)tile[(kr + 2 * i) * kLdsPitch + col] |
-             ((uint32_t)tile[(kr + 2 * i + 1) * kLdsPitch + col] << 16);
+    for (int i = 0; i < W / 2; ++i) {
+      const int pr = kr / 2 + i;
+      w[i] = tile[pr * kTP + col_swz(pr, col)];
+    }
     float y[W];
     unpack<W>(w, pm, y);
     fwht<W, N>(y, neg1, neg2);
