@@ -115,6 +115,27 @@ int ufp4_rht_quant(const void* x, int64_t rows, int64_t cols, int64_t ld, int32_
                    const ufp4_quant_cfg* cfg, uint8_t* codes, void* scales, float* rotated,
                    void* stream);
 
+/* Both quantizations of one tensor X [rows][ld] from a single read: the
+ * row-wise one (A = X, K = cols; as ufp4_rht_quant with along = 0 and
+ * cfg_row) and the column-wise one (A = X^T, K = rows; as ufp4_rht_quant with
+ * along = 1 and cfg_col, or as ufp4_rht_quant_segmented when row_offsets is
+ * given).  [UFP4] Method: the recipe quantizes X, W and dY along both axes,
+ * since each takes part in two GEMMs with different shared dimensions.
+ * Outputs are bit-identical to the single-axis calls.  cfg_row and cfg_col
+ * must be 1D and agree in grid, rounding, scale mode, block_cols and rht_n
+ * (<= 64); they may differ in sign_seed, sr_seed and sr_stream (else
+ * UFP4_ERR_UNSUPPORTED).  rows (or every segment) and cols must be multiples
+ * of lcm(rht_n, block_cols) (UFP4_ERR_SHAPE).  row_offsets: HOST int64
+ * [num_segments+1] or NULL; 1 <= num_segments <= 128.  Buffers: codes_row
+ * [rows][cols/2], scales_row [rows][cols/block_cols], codes_col /
+ * scales_col as the column-wise call; device pointers, codes 16-byte and
+ * scales 4-byte aligned, x 16-byte aligned with ld % 8 == 0. */
+int ufp4_rht_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                        const int64_t* row_offsets, int32_t num_segments,
+                        const ufp4_quant_cfg* cfg_row, const ufp4_quant_cfg* cfg_col,
+                        uint8_t* codes_row, void* scales_row, uint8_t* codes_col,
+                        void* scales_col, void* stream);
+
 /* Column-wise quantization of row segments (per-expert transposed operands).
  * Segment g is rows [row_offsets[g], row_offsets[g+1]) of x [rows][ld]; it
  * yields A_g = x[seg]^T of shape [cols][L_g], L_g = segment length, which is

@@ -25,7 +25,7 @@ UFP4_OK, UFP4_ERR_INVALID_ARG, UFP4_ERR_SHAPE = 0, -1, -2
 UFP4_ERR_MISMATCH, UFP4_ERR_UNSUPPORTED, UFP4_ERR_HIP = -3, -4, -5
 
 EXPORTED = [
-    "ufp4_rht_quant", "ufp4_rht_quant_segmented", "ufp4_dequant",
+    "ufp4_rht_quant", "ufp4_rht_quant_segmented", "ufp4_rht_quant_dual", "ufp4_dequant",
     "ufp4_gemm_fprop", "ufp4_gemm_dgrad", "ufp4_gemm_wgrad",
     "ufp4_gemm_fprop_grouped", "ufp4_gemm_dgrad_grouped", "ufp4_gemm_wgrad_grouped",
     "ufp4_transpose_qtensor", "ufp4_codes_bytes", "ufp4_scales_bytes",
@@ -97,6 +97,7 @@ def _lib():
         sig = {
             "ufp4_rht_quant": [vp, i64, i64, i64, i32, cfgp, vp, vp, vp, vp],
             "ufp4_rht_quant_segmented": [vp, i64, i64, i64, i64p, i32, cfgp, vp, vp, vp],
+            "ufp4_rht_quant_dual": [vp, i64, i64, i64, i64p, i32, cfgp, cfgp, vp, vp, vp, vp, vp],
             "ufp4_dequant": [qtp, vp, i64, vp],
             "ufp4_gemm_fprop": [qtp, qtp, vp, i64, vp],
             "ufp4_gemm_dgrad": [qtp, qtp, vp, i64, vp],
@@ -198,6 +199,29 @@ def ufp4_rht_quant_segmented(x: torch.Tensor, row_offsets: Sequence[int], cfg: Q
                                          _ptr(scales), _stream(x))
     _check("ufp4_rht_quant_segmented", st)
     return QTensor(codes, scales, cols, rows, cfg)
+
+
+def ufp4_rht_quant_dual(x: torch.Tensor, cfg_row: QuantCfg, cfg_col: QuantCfg,
+                        row_offsets: Optional[Sequence[int]] = None, out_row=None, out_col=None):
+    """Row-wise (A = x, K = cols) and column-wise (A = x^T, K = rows, or per
+    row segment when row_offsets is given) quantization from one read of x.
+    Returns (QTensor row, QTensor col); out_row / out_col: optional
+    (codes, scales) pairs to write into."""
+    rows, cols = x.shape
+    dev = x.device
+    cr, sr = out_row if out_row is not None else (
+        torch.empty(rows * cols // 2, dtype=torch.uint8, device=dev),
+        torch.empty(rows * cols // cfg_row.block_cols, dtype=scales_dtype(cfg_row), device=dev))
+    cc, sc = out_col if out_col is not None else (
+        torch.empty(rows * cols // 2, dtype=torch.uint8, device=dev),
+        torch.empty(rows * cols // cfg_col.block_cols, dtype=scales_dtype(cfg_col), device=dev))
+    off = _i64arr(row_offsets) if row_offsets is not None else None
+    nseg = len(row_offsets) - 1 if row_offsets is not None else 1
+    st = _lib().ufp4_rht_quant_dual(_ptr(x), rows, cols, x.stride(0), off, nseg,
+                                    ctypes.byref(cfg_row), ctypes.byref(cfg_col), _ptr(cr),
+                                    _ptr(sr), _ptr(cc), _ptr(sc), _stream(x))
+    _check("ufp4_rht_quant_dual", st)
+    return QTensor(cr, sr, rows, cols, cfg_row), QTensor(cc, sc, cols, rows, cfg_col)
 
 
 def stacked(q: QTensor, groups: int) -> QTensor:

@@ -261,6 +261,70 @@ int ufp4_rht_quant(const void* x, int64_t rows, int64_t cols, int64_t ld, int32_
   return hip_status(launch_quant_cols(q, (hipStream_t)stream));
 }
 
+int ufp4_rht_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                        const int64_t* row_offsets, int32_t num_segments,
+                        const ufp4_quant_cfg* cfg_row, const ufp4_quant_cfg* cfg_col,
+                        uint8_t* codes_row, void* scales_row, uint8_t* codes_col,
+                        void* scales_col, void* stream) {
+  if (rows < 0 || cols < 0 || (rows > 0 && ld < cols)) return UFP4_ERR_INVALID_ARG;
+  if (row_offsets && (num_segments < 1 || num_segments > kMaxSegments))
+    return UFP4_ERR_INVALID_ARG;
+  int st = check_cfg(cfg_row);
+  if (st) return st;
+  st = check_cfg(cfg_col);
+  if (st) return st;
+  // one kernel instance serves both sides: they may differ only in signs and draws
+  if (cfg_row->block_rows != 1 || cfg_col->block_rows != 1 || cfg_row->grid != cfg_col->grid ||
+      cfg_row->rounding != cfg_col->rounding || cfg_row->scale_mode != cfg_col->scale_mode ||
+      cfg_row->block_cols != cfg_col->block_cols || cfg_row->rht_n != cfg_col->rht_n ||
+      cfg_row->rht_n > 64)
+    return UFP4_ERR_UNSUPPORTED;
+  const int64_t n = cfg_row->rht_n, b = cfg_row->block_cols;
+  const int64_t align = n > b ? n : b;
+  const int nseg = row_offsets ? num_segments : 1;
+  if (row_offsets) {
+    if (row_offsets[0] != 0 || row_offsets[nseg] != rows) return UFP4_ERR_INVALID_ARG;
+    for (int g = 0; g < nseg; ++g) {
+      if (row_offsets[g + 1] < row_offsets[g]) return UFP4_ERR_INVALID_ARG;
+      if ((row_offsets[g + 1] - row_offsets[g]) % align) return UFP4_ERR_SHAPE;
+    }
+  } else if (rows % align) {
+    return UFP4_ERR_SHAPE;
+  }
+  if (cols % align) return UFP4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return UFP4_OK;
+  if (!x || !codes_row || !scales_row || !codes_col || !scales_col) return UFP4_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || ld % 8 || !aligned(codes_row, 16) || !aligned(scales_row, 4) ||
+      !aligned(codes_col, 16) || !aligned(scales_col, 4))
+    return UFP4_ERR_INVALID_ARG;
+  QuantLaunch q;
+  fill_common(q, x, rows, cols, ld, cfg_col, codes_col, scales_col, nullptr);
+  q.P = cols;
+  q.K = rows;
+  q.nseg = nseg;
+  int64_t t = 0;
+  const int64_t tp = cdiv(cols, 64);
+  for (int g = 0; g < nseg; ++g) {
+    const int64_t a = row_offsets ? row_offsets[g] : 0, e = row_offsets ? row_offsets[g + 1] : rows;
+    q.seg_off[g] = a;
+    q.tile_start[g] = (int32_t)t;
+    t += cdiv(e - a, 128) * tp;
+    if (t > INT32_MAX) return UFP4_ERR_UNSUPPORTED;
+  }
+  q.seg_off[nseg] = rows;
+  q.tile_start[nseg] = (int32_t)t;
+  RowSide r;
+  std::memset(&r, 0, sizeof(r));
+  r.codes = codes_row;
+  r.scales = scales_row;
+  r.rotated = nullptr;
+  r.cn = q.cn;
+  r.sr_seed = cfg_row->sr_seed;
+  r.sr_stream = cfg_row->sr_stream;
+  sign_patterns(cfg_row, lane_width(cfg_row->rht_n, cfg_row->block_cols), r.sign_pat);
+  return hip_status(launch_quant_dual(q, r, (hipStream_t)stream));
+}
+
 int ufp4_rht_quant_segmented(const void* x, int64_t rows, int64_t cols, int64_t ld,
                              const int64_t* row_offsets, int32_t num_segments,
                              const ufp4_quant_cfg* cfg, uint8_t* codes, void* scales,

@@ -28,4 +28,12 @@ hipError_t launch_quant_rows_2d(const QuantLaunch& q, hipStream_t s) {
   }
 }
 
+hipError_t launch_quant_dual(const QuantLaunch& q, const RowSide& r, hipStream_t s) {
+  switch (q.grid) {
+    case 0: return quant_dual_grid<0>(q, r, s);
+    case 1: return quant_dual_grid<1>(q, r, s);
+    default: return quant_dual_grid<2>(q, r, s);
+  }
+}
+
 }  // namespace ufp4

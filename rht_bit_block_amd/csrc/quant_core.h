@@ -66,7 +66,8 @@ __device__ __forceinline__ void sign_masks(uint32_t pat, uint32_t (&pm)[W / 2]) 
 
 // Sign pattern of the lane's segment: word qpos of the n-bit sign vector when a
 // chunk spans several lanes, else the pattern repeated with period n (host).
-__device__ __forceinline__ uint32_t select_pattern(const QuantLaunch& q, uint32_t qpos) {
+template <class Q>
+__device__ __forceinline__ uint32_t select_pattern(const Q& q, uint32_t qpos) {
   const uint32_t a = (qpos & 1u) ? q.sign_pat[1] : q.sign_pat[0];
   const uint32_t b = (qpos & 1u) ? q.sign_pat[3] : q.sign_pat[2];
   return (qpos & 2u) ? b : a;
@@ -297,8 +298,8 @@ __device__ __forceinline__ void store_rotated(float* dst, const float (&y)[W]) {
 
 // After the butterflies: normalize (or fold), optionally store the rotated
 // values, quantize.
-template <int W, int B, int N, int GRID, int RND>
-__device__ __forceinline__ void finish_lane(float (&y)[W], const QuantLaunch& q, uint64_t e0,
+template <int W, int B, int N, int GRID, int RND, class Q>
+__device__ __forceinline__ void finish_lane(float (&y)[W], const Q& q, uint64_t e0,
                                             uint8_t* codes_out, float* scales_out) {
   if constexpr (Rht<N>::fold) {
     if (q.rotated == nullptr) {
@@ -344,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantLaunch q, FastDiv 
     unpack<W>(w, pm, y);
     fwht<W, N>(y, neg1, neg2);
     const uint64_t e0 = (uint64_t)p * K + k0;
-    finish_lane<W, B, N, GRID, RND>(y, q, e0, q.codes + (e0 >> 1),
+    finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, q, e0, q.codes + (e0 >> 1),
                                     reinterpret_cast<float*>(q.scales) + (uint64_t)p * (K / B) + k0 / B);
   }
 }
@@ -443,8 +444,123 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantLaunch q) {
     const int64_t p = p0 + col;
     const int64_t k = k0 + kr;
     const uint64_t e0 = (uint64_t)C * seg0 + (uint64_t)p * L + k;   // global draw index
-    finish_lane<W, B, N, GRID, RND>(y, q, e0, q.codes + (e0 >> 1),
+    finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, q, e0, q.codes + (e0 >> 1),
                                     reinterpret_cast<float*>(q.scales) + e0 / B);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Both axes from one read of X (1 x B blocks): the column-wise quantization
+// of the tile exactly as k_quant_cols, then the row-wise quantization of the
+// same 128 x 64 tile (A = X, K = the columns) from the staged words -- a lane
+// takes W consecutive columns of one row and keeps its row's bf16 half of
+// each word.  The row side has its own signs, SR stream and outputs.  Hadamard
+// chunks along the row must fit the tile width (n <= 64).
+// ---------------------------------------------------------------------------
+template <int W, int B, int N, int GRID, int RND>
+__global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide rside) {
+  __shared__ uint32_t tile[(kTK / 2) * kTP];
+  static_assert(N <= kTP, "row-wise Hadamard chunks must fit the tile width");
+  constexpr int lpc = N > W ? N / W : 1;
+  const int bid = blockIdx.x;
+  int g = 0;
+  while (g + 1 < q.nseg && q.tile_start[g + 1] <= bid) ++g;
+  const int64_t seg0 = q.seg_off[g], seg1 = q.seg_off[g + 1];
+  const int64_t L = seg1 - seg0;
+  const int64_t C = q.cols;
+  const int tiles_p = (int)((C + kTP - 1) / kTP);
+  const int local = bid - q.tile_start[g];
+  const int tk = local / tiles_p, tp = local - tk * tiles_p;
+  const int64_t k0 = (int64_t)tk * kTK;
+  const int64_t p0 = (int64_t)tp * kTP;
+  const int krows = (int)min<int64_t>(kTK, L - k0);
+  const int pcols = (int)min<int64_t>(kTP, C - p0);
+
+  for (int t = threadIdx.x; t < (kTK / 2) * (kTP / 8); t += kThreads) {
+    const int i = t / (kTP / 8), c8 = (t % (kTP / 8)) * 8;
+    uint4 ra = make_uint4(0, 0, 0, 0), rb = ra;
+    const int r = 2 * i;
+    const uint16_t* src = q.x + (seg0 + k0 + r) * q.ld + p0 + c8;
+    if (c8 + 8 <= pcols) {
+      if (r < krows) ra = ld16(src);
+      if (r + 1 < krows) rb = ld16(src + q.ld);
+    } else {
+      uint16_t ta[8] = {0, 0, 0, 0, 0, 0, 0, 0}, tb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int j = 0; j < 8 && c8 + j < pcols; ++j) {
+        if (r < krows) ta[j] = src[j];
+        if (r + 1 < krows) tb[j] = src[q.ld + j];
+      }
+      ra = make_uint4(ta[0] | (ta[1] << 16), ta[2] | (ta[3] << 16), ta[4] | (ta[5] << 16),
+                      ta[6] | (ta[7] << 16));
+      rb = make_uint4(tb[0] | (tb[1] << 16), tb[2] | (tb[3] << 16), tb[4] | (tb[5] << 16),
+                      tb[6] | (tb[7] << 16));
+    }
+    const uint32_t a4[4] = {ra.x, ra.y, ra.z, ra.w}, b4[4] = {rb.x, rb.y, rb.z, rb.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[2 * j] = __builtin_amdgcn_perm(b4[j], a4[j], 0x05040100u);
+      o[2 * j + 1] = __builtin_amdgcn_perm(b4[j], a4[j], 0x07060302u);
+    }
+    uint32_t* d = tile + i * kTP;
+    *reinterpret_cast<uint4*>(d + col_swz(i, c8)) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(d + col_swz(i, c8 + 4)) = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+  __syncthreads();
+
+  const uint32_t qpos = threadIdx.x & (uint32_t)(lpc - 1);
+  const uint32_t neg1 = (qpos & 1u) ? 0x80000000u : 0u;
+  const uint32_t neg2 = (qpos & 2u) ? 0x80000000u : 0u;
+  // column-wise: A = X^T, K = the segment's rows
+  {
+    uint32_t pm[W / 2];
+    sign_masks<W>(select_pattern(q, qpos), pm);
+    constexpr int kSegsPerCol = kTK / W;
+    for (int u = threadIdx.x; u < kTP * kSegsPerCol; u += kThreads) {
+      const int kseg = u % kSegsPerCol;
+      const int col = u / kSegsPerCol;
+      const int kr = kseg * W;
+      if (kr >= krows || col >= pcols) continue;
+      uint32_t w[W / 2];
+#pragma unroll
+      for (int i = 0; i < W / 2; ++i) {
+        const int pr = kr / 2 + i;
+        w[i] = tile[pr * kTP + col_swz(pr, col)];
+      }
+      float y[W];
+      unpack<W>(w, pm, y);
+      fwht<W, N>(y, neg1, neg2);
+      const uint64_t e0 = (uint64_t)C * seg0 + (uint64_t)(p0 + col) * L + (k0 + kr);
+      finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, q, e0, q.codes + (e0 >> 1),
+                                                   reinterpret_cast<float*>(q.scales) + e0 / B);
+    }
+  }
+  // row-wise: A = X, K = the columns
+  {
+    uint32_t pm[W / 2];
+    sign_masks<W>(select_pattern(rside, qpos), pm);
+    constexpr int kSegsPerRow = kTP / W;
+    for (int u = threadIdx.x; u < kTK * kSegsPerRow; u += kThreads) {
+      const int seg = u % kSegsPerRow;
+      const int row = u / kSegsPerRow;
+      const int c0 = seg * W;
+      if (row >= krows || c0 >= pcols) continue;   // whole chunks drop out together
+      const int pr = row >> 1;
+      const uint32_t sel = (row & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t w[W / 2];
+#pragma unroll
+      for (int j = 0; j < W / 4; ++j) {
+        const uint4 v = *reinterpret_cast<const uint4*>(tile + pr * kTP + col_swz(pr, c0 + 4 * j));
+        w[2 * j] = __builtin_amdgcn_perm(v.y, v.x, sel);
+        w[2 * j + 1] = __builtin_amdgcn_perm(v.w, v.z, sel);
+      }
+      float y[W];
+      unpack<W>(w, pm, y);
+      fwht<W, N>(y, neg1, neg2);
+      const uint64_t e0 = (uint64_t)(seg0 + k0 + row) * (uint64_t)C + (uint64_t)(p0 + c0);
+      finish_lane<W, B, N, GRID, RND, RowSide>(y, rside, e0, rside.codes + (e0 >> 1),
+                                               reinterpret_cast<float*>(rside.scales) + e0 / B);
+    }
   }
 }
 
@@ -558,6 +674,32 @@ hipError_t run_cols(const QuantLaunch& q, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int W, int B, int N, int G, int R>
+hipError_t run_dual(const QuantLaunch& q, const RowSide& r, hipStream_t s) {
+  const int total = q.tile_start[q.nseg];
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_quant_dual<W, B, N, G, R>), dim3(total), dim3(kThreads), 0, s, q, r);
+  return hipGetLastError();
+}
+
+template <int G>
+hipError_t run_dual_1d(const QuantLaunch& q, const RowSide& r, hipStream_t s) {
+#define UFP4_RUN(B_, N_)                                                       \
+  if (q.bc == B_ && q.n == N_) {                                              \
+    constexpr int W_ = (B_ == 32 || N_ >= 32) ? 32 : 16;                      \
+    if (q.rounding == 0) return run_dual<W_, B_, N_, G, 0>(q, r, s);           \
+    return run_dual<W_, B_, N_, G, 1>(q, r, s);                                \
+  }
+#define UFP4_RUN_B(B_) \
+  UFP4_RUN(B_, 1) UFP4_RUN(B_, 2) UFP4_RUN(B_, 4) UFP4_RUN(B_, 8) UFP4_RUN(B_, 16) \
+  UFP4_RUN(B_, 32) UFP4_RUN(B_, 64)
+  UFP4_RUN_B(16)
+  UFP4_RUN_B(32)
+#undef UFP4_RUN_B
+#undef UFP4_RUN
+  return hipErrorInvalidValue;
+}
+
 // Dispatch over (n, block, rounding) for one codebook; W follows from n, b.
 template <int G, bool COLS>
 hipError_t run_1d(const QuantLaunch& q, hipStream_t s) {
@@ -609,5 +751,6 @@ hipError_t run_2d(const QuantLaunch& q, hipStream_t s) {
 template <int G> hipError_t quant_rows_grid(const QuantLaunch& q, hipStream_t s);
 template <int G> hipError_t quant_cols_grid(const QuantLaunch& q, hipStream_t s);
 template <int G> hipError_t quant_rows_2d_grid(const QuantLaunch& q, hipStream_t s);
+template <int G> hipError_t quant_dual_grid(const QuantLaunch& q, const RowSide& r, hipStream_t s);
 
 }  // namespace ufp4

@@ -16,4 +16,9 @@ hipError_t quant_rows_2d_grid<0>(const QuantLaunch& q, hipStream_t s) {
   return qk::run_2d<0>(q, s);
 }
 
+template <>
+hipError_t quant_dual_grid<0>(const QuantLaunch& q, const RowSide& r, hipStream_t s) {
+  return qk::run_dual_1d<0>(q, r, s);
+}
+
 }  // namespace ufp4

@@ -16,4 +16,9 @@ hipError_t quant_rows_2d_grid<2>(const QuantLaunch& q, hipStream_t s) {
   return qk::run_2d<2>(q, s);
 }
 
+template <>
+hipError_t quant_dual_grid<2>(const QuantLaunch& q, const RowSide& r, hipStream_t s) {
+  return qk::run_dual_1d<2>(q, r, s);
+}
+
 }  // namespace ufp4

@@ -66,7 +66,20 @@ struct QuantLaunch {
   int32_t tile_start[kMaxSegments + 1];
 };
 
+// Row-wise side of a two-axis quantization: its own outputs, signs and draws
+// (the geometry and the column-wise side live in the QuantLaunch).
+struct RowSide {
+  uint8_t* codes;
+  void* scales;
+  float* rotated;   // always null (no debug output for the fused call)
+  uint32_t sign_pat[4];
+  float cn;
+  uint64_t sr_seed;
+  uint32_t sr_stream;
+};
+
 hipError_t launch_quant_rows(const QuantLaunch& q, hipStream_t s);
+hipError_t launch_quant_dual(const QuantLaunch& q, const RowSide& r, hipStream_t s);
 hipError_t launch_quant_cols(const QuantLaunch& q, hipStream_t s);
 hipError_t launch_quant_rows_2d(const QuantLaunch& q, hipStream_t s);
 

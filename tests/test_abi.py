@@ -149,3 +149,35 @@ def test_size_helpers():
     assert U.ufp4_scales_bytes(8192, 2048, cfg) == 8192 * 128 * 4
     c2 = U.make_cfg(scale_mode=U.UFP4_SCALE_POW2, block_rows=32, block_cols=32, rht_n=1)
     assert U.ufp4_scales_bytes(4096, 4096, c2) == 128 * 128
+
+
+def _dual(lib, rows=64, cols=64, ld=64, offs=None, cfg_r=None, cfg_c=None, x=FAKE, ptr=FAKE):
+    cr, cc = cfg_r or U.make_cfg(sign_seed=1), cfg_c or U.make_cfg(sign_seed=2)
+    off = (ctypes.c_int64 * len(offs))(*offs) if offs is not None else None
+    n = len(offs) - 1 if offs is not None else 1
+    p = ctypes.c_void_p(ptr)
+    return lib.ufp4_rht_quant_dual(ctypes.c_void_p(x), rows, cols, ld, off, n, ctypes.byref(cr),
+                                   ctypes.byref(cc), p, p, p, p, None)
+
+
+def test_dual_quant_argument_errors():
+    lib = U.lib_handle()
+    E = U
+    assert _dual(lib, x=0) == E.UFP4_ERR_INVALID_ARG
+    assert _dual(lib, ptr=0) == E.UFP4_ERR_INVALID_ARG
+    assert _dual(lib, ld=32) == E.UFP4_ERR_INVALID_ARG
+    # the two sides may differ only in signs and draws
+    assert _dual(lib, cfg_c=U.make_cfg(grid=U.UFP4_INT4)) == E.UFP4_ERR_UNSUPPORTED
+    assert _dual(lib, cfg_c=U.make_cfg(rounding=U.UFP4_SR)) == E.UFP4_ERR_UNSUPPORTED
+    assert _dual(lib, cfg_c=U.make_cfg(rht_n=32)) == E.UFP4_ERR_UNSUPPORTED
+    big = U.make_cfg(rht_n=128)
+    assert _dual(lib, rows=128, cols=128, ld=128, cfg_r=big, cfg_c=big) == E.UFP4_ERR_UNSUPPORTED
+    assert _dual(lib, rows=40) == E.UFP4_ERR_SHAPE                  # rows % 16
+    assert _dual(lib, cols=40, ld=48) == E.UFP4_ERR_SHAPE           # cols % 16
+    assert _dual(lib, offs=[0, 24, 64]) == E.UFP4_ERR_SHAPE         # segment % 16
+    assert _dual(lib, offs=[0, 32, 48]) == E.UFP4_ERR_INVALID_ARG   # must end at rows
+    assert _dual(lib, offs=[8, 64]) == E.UFP4_ERR_INVALID_ARG       # must start at 0
+    two_d = U.make_cfg(grid=U.UFP4_E2M1, scale_mode=U.UFP4_SCALE_POW2, block_rows=32,
+                       block_cols=32, rht_n=1)
+    assert _dual(lib, cfg_r=two_d, cfg_c=two_d) == E.UFP4_ERR_UNSUPPORTED
+    assert _dual(lib, rows=0) == E.UFP4_OK

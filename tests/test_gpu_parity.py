@@ -185,6 +185,50 @@ def test_gemm_pow2_paths(grid, K):
     assert O.rel_fro(C, ref) <= GEMM_TOL
 
 
+def _assert_q_equal(q, ref, tag):
+    codes = q.codes.cpu().numpy().reshape(-1)
+    scales = q.scales.cpu().numpy().reshape(-1)
+    rc, rs = np.asarray(ref["codes"]).reshape(-1), np.asarray(ref["scales"]).reshape(-1)
+    assert f32_bits_equal(scales, rs), (tag, "scales", first_diff(scales.view(np.uint32), rs.view(np.uint32)))
+    assert np.array_equal(codes, rc), (tag, "codes", first_diff(codes, rc))
+
+
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("rnd", [U.UFP4_RTNE, U.UFP4_SR])
+@pytest.mark.parametrize("n,b", [(1, 16), (16, 16), (32, 32), (64, 16)])
+def test_quant_dual(grid, rnd, n, b):
+    """Both axes from one read == the oracle's row-wise and column-wise
+    quantizations with their own signs and SR streams (ragged tiles on both
+    axes: 272 = 2 x 128 + 16 rows, 80 = 64 + 16 columns; 320 x 192 for n > 16)."""
+    _print_case("dual", grid, rnd, n, b)
+    rows, cols = (272, 80) if n <= 16 else (320, 192)
+    bits = rand_bits(rows, cols, 40 + n)
+    cr = U.make_cfg(grid, rnd, U.UFP4_SCALE_F32, 1, b, n, sign_seed=11, sr_seed=3, sr_stream=0)
+    cc = U.make_cfg(grid, rnd, U.UFP4_SCALE_F32, 1, b, n, sign_seed=12, sr_seed=3, sr_stream=1)
+    qr, qc = U.ufp4_rht_quant_dual(dev_bf16(bits), cr, cc)
+    torch.cuda.synchronize()
+    _assert_q_equal(qr, O.quantize(bits, 0, spec_of(cr)), "row")
+    _assert_q_equal(qc, O.quantize(bits, 1, spec_of(cc)), "col")
+
+
+def test_quant_dual_segmented():
+    """Dual call with expert segments (one empty) == the oracle's row-wise
+    quantization and per-segment column-wise quantization."""
+    _print_case("dual segmented")
+    offs = [0, 96, 96, 160, 320]
+    bits = rand_bits(320, 64, 77)
+    cr = U.make_cfg(U.UFP4_E1M2, U.UFP4_SR, U.UFP4_SCALE_F32, 1, 32, 32, sign_seed=5, sr_seed=9, sr_stream=2)
+    cc = U.make_cfg(U.UFP4_E1M2, U.UFP4_SR, U.UFP4_SCALE_F32, 1, 32, 32, sign_seed=6, sr_seed=9, sr_stream=3)
+    qr, qc = U.ufp4_rht_quant_dual(dev_bf16(bits), cr, cc, row_offsets=offs)
+    torch.cuda.synchronize()
+    _assert_q_equal(qr, O.quantize(bits, 0, spec_of(cr)), "row")
+    segs = [O.quantize(bits[lo:hi], 1, spec_of(cc), elem_base=bits.shape[1] * lo)
+            for lo, hi in zip(offs[:-1], offs[1:]) if hi > lo]
+    ref = {"codes": np.concatenate([np.asarray(r["codes"]).reshape(-1) for r in segs]),
+           "scales": np.concatenate([np.asarray(r["scales"]).reshape(-1) for r in segs])}
+    _assert_q_equal(qc, ref, "col")
+
+
 def test_segmented_quant_and_grouped_gemms():
     """Four experts (one empty), per-expert transposed operands, and the
     three grouped GEMMs against per-expert oracle products."""
