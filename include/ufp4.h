@@ -65,7 +65,12 @@ enum {
  *   grid, rounding, scale_mode : the enums above.
  *   block_rows x block_cols    : 1 x 16 or 1 x 32 (1D groups along K,
  *                                [2DFP4] root cause), or 32 x 32 square
- *                                blocks ([2DFP4] 2D section).
+ *                                blocks ([2DFP4] 2D section).  Power-of-two
+ *                                scales go with 32 x 32 blocks or 1 x 32
+ *                                blocks (the OCP-MX block: one E8M0 byte
+ *                                per row and 32 elements); fp32 scales
+ *                                with 1 x 16 or 1 x 32 blocks; any other
+ *                                pairing is UFP4_ERR_UNSUPPORTED.
  *   rht_n     : Hadamard size along K, a power of two in [1, 128]; 1 = no
  *               rotation ([UFP4] Method, Sylvester recursion).  32 x 32
  *               blocks accept rht_n <= 32.

@@ -31,7 +31,8 @@ int check_cfg(const ufp4_quant_cfg* c) {
   const bool one_d = c->block_rows == 1 && (c->block_cols == 16 || c->block_cols == 32);
   const bool two_d = c->block_rows == 32 && c->block_cols == 32;
   if (!one_d && !two_d) return UFP4_ERR_UNSUPPORTED;
-  if (one_d && c->scale_mode != UFP4_SCALE_F32) return UFP4_ERR_UNSUPPORTED;
+  // 1D power-of-two scales only for the MX block shape 1 x 32
+  if (one_d && c->scale_mode != UFP4_SCALE_F32 && c->block_cols != 32) return UFP4_ERR_UNSUPPORTED;
   if (two_d && (c->scale_mode != UFP4_SCALE_POW2 || c->rht_n > 32)) return UFP4_ERR_UNSUPPORTED;
   return UFP4_OK;
 }

@@ -206,18 +206,37 @@ __device__ __forceinline__ void sr_draws(uint64_t e0, uint64_t seed, uint32_t st
   }
 }
 
-// Quantize the W values of one lane whose blocks are 1 x B (fp32 absmax
-// scales); writes codes (W/2 bytes) and W/B scales.  FOLD: y holds the
+// Least e in [-127, 127] with M <= qmax * 2^e ([2DFP4] power-of-two scale
+// equation; the clamp is the E8M0 range).  M = 0 gives -127.
+template <int GRID>
+__device__ __forceinline__ int pow2_exponent(float M) {
+  constexpr float qmax = Grid<GRID>::qmax;
+  int e = -127;
+  if (M > 0.0f) {
+    e = ilogbf(M) - 3;  // qmax < 8, so M > qmax * 2^(ilogb(M) - 3)
+    if (e < -127) e = -127;
+    while (e < 127 && M > ldexpf(qmax, e)) ++e;
+  }
+  return e;
+}
+
+// Quantize the W values of one lane whose blocks are 1 x B; writes codes
+// (W/2 bytes) and W/B scales.  RND bit 0: stochastic rounding; RND bit 1:
+// power-of-two scales stored as E8M0 bytes (1 x 32 blocks), else fp32
+// absmax scales.  FOLD (fp32 scales only): y holds the
 // unnormalized transform x, the rotated values are c * x with c a power of
 // two, and RN(c x / s_c) = RN(x / s_x), s_c = c s_x whenever nothing
 // underflows; blocks with c * absmax < 2^-100 redo the literal computation.
 template <int W, int B, int GRID, int RND, bool FOLD>
 __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64_t e0,
                                             uint64_t seed, uint32_t stream, uint8_t* codes_out,
-                                            float* scales_out) {
+                                            void* scales_out) {
   constexpr float qmax = Grid<GRID>::qmax;
+  constexpr int RM = RND & 1;
+  constexpr bool POW2 = (RND & 2) != 0;
+  static_assert(!(POW2 && FOLD), "power-of-two scales take the normalized values");
   uint32_t rw[W / 2];
-  if constexpr (RND == 1) sr_draws<W>(e0, seed, stream, rw);
+  if constexpr (RM == 1) sr_draws<W>(e0, seed, stream, rw);
   uint32_t packed[W / 8];
 #pragma unroll
   for (int i = 0; i < W / 8; ++i) packed[i] = 0u;
@@ -226,8 +245,19 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
     float M = 0.0f;
 #pragma unroll
     for (int j = 0; j < B; ++j) M = fmaxf(M, fabsf(y[blk * B + j]));
-    float s = __fdiv_rn(M, qmax);  // s_B = RN(absmax / qmax)
     float v[B];
+    if constexpr (POW2) {
+      const int e = pow2_exponent<GRID>(M);
+      const float inv = ldexpf(1.0f, -e);   // exact power of two
+#pragma unroll
+      for (int j = 0; j < B; ++j) v[j] = __fmul_rn(y[blk * B + j], inv);
+      if (e == 127) {   // only there can |v| exceed qmax
+#pragma unroll
+        for (int j = 0; j < B; ++j) v[j] = fminf(fmaxf(v[j], -qmax), qmax);
+      }
+      reinterpret_cast<uint8_t*>(scales_out)[blk] = (uint8_t)(e + 127);
+    } else {
+    float s = __fdiv_rn(M, qmax);  // s_B = RN(absmax / qmax)
     if (s == 0.0f) {
 #pragma unroll
       for (int j = 0; j < B; ++j) v[j] = 0.0f;
@@ -265,12 +295,13 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
         s = __fmul_rn(s, c);   // exact: power of two, no underflow
       }
     }
-    scales_out[blk] = s;
+    reinterpret_cast<float*>(scales_out)[blk] = s;
+    }
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const int idx = blk * B + j;
       uint32_t nib;
-      if constexpr (RND == 0) {
+      if constexpr (RM == 0) {
         nib = rtne_nibble<GRID>(v[j]);   // no clamp needed: qmax + 1 ulp rounds to qmax
       } else {
         const float vc = fminf(fmaxf(v[j], -qmax), qmax);
@@ -297,11 +328,12 @@ __device__ __forceinline__ void store_rotated(float* dst, const float (&y)[W]) {
 }
 
 // After the butterflies: normalize (or fold), optionally store the rotated
-// values, quantize.
+// values, quantize.  scales_out points at the lane's first scale (fp32 or
+// E8M0 byte, by RND bit 1).
 template <int W, int B, int N, int GRID, int RND, class Q>
 __device__ __forceinline__ void finish_lane(float (&y)[W], const Q& q, uint64_t e0,
-                                            uint8_t* codes_out, float* scales_out) {
-  if constexpr (Rht<N>::fold) {
+                                            uint8_t* codes_out, void* scales_out) {
+  if constexpr (Rht<N>::fold && (RND & 2) == 0) {
     if (q.rotated == nullptr) {
       quantize_1d<W, B, GRID, RND, true>(y, Rht<N>::c, e0, q.sr_seed, q.sr_stream, codes_out,
                                          scales_out);
@@ -311,6 +343,13 @@ __device__ __forceinline__ void finish_lane(float (&y)[W], const Q& q, uint64_t 
   if constexpr (N > 1) scale_by<W>(y, q.cn);
   if (q.rotated) store_rotated<W>(q.rotated + e0, y);
   quantize_1d<W, B, GRID, RND, false>(y, 1.0f, e0, q.sr_seed, q.sr_stream, codes_out, scales_out);
+}
+
+// Address of scale number i of a 1D quantization (fp32 or E8M0 byte).
+template <int RND>
+__device__ __forceinline__ void* scale_at(void* base, uint64_t i) {
+  if constexpr ((RND & 2) != 0) return reinterpret_cast<uint8_t*>(base) + i;
+  else return reinterpret_cast<float*>(base) + i;
 }
 
 // ---------------------------------------------------------------------------
@@ -346,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantLaunch q, FastDiv 
     fwht<W, N>(y, neg1, neg2);
     const uint64_t e0 = (uint64_t)p * K + k0;
     finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, q, e0, q.codes + (e0 >> 1),
-                                    reinterpret_cast<float*>(q.scales) + (uint64_t)p * (K / B) + k0 / B);
+                                    scale_at<RND>(q.scales, (uint64_t)p * (K / B) + k0 / B));
   }
 }
 
@@ -445,7 +484,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantLaunch q) {
     const int64_t k = k0 + kr;
     const uint64_t e0 = (uint64_t)C * seg0 + (uint64_t)p * L + k;   // global draw index
     finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, q, e0, q.codes + (e0 >> 1),
-                                    reinterpret_cast<float*>(q.scales) + e0 / B);
+                                    scale_at<RND>(q.scales, e0 / B));
   }
 }
 
@@ -532,7 +571,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide 
       fwht<W, N>(y, neg1, neg2);
       const uint64_t e0 = (uint64_t)C * seg0 + (uint64_t)(p0 + col) * L + (k0 + kr);
       finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, q, e0, q.codes + (e0 >> 1),
-                                                   reinterpret_cast<float*>(q.scales) + e0 / B);
+                                                   scale_at<RND>(q.scales, e0 / B));
     }
   }
   // row-wise: A = X, K = the columns
@@ -559,7 +598,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide 
       fwht<W, N>(y, neg1, neg2);
       const uint64_t e0 = (uint64_t)(seg0 + k0 + row) * (uint64_t)C + (uint64_t)(p0 + c0);
       finish_lane<W, B, N, GRID, RND, RowSide>(y, rside, e0, rside.codes + (e0 >> 1),
-                                               reinterpret_cast<float*>(rside.scales) + e0 / B);
+                                               scale_at<RND>(rside.scales, e0 / B));
     }
   }
 }
@@ -607,12 +646,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows_2d(QuantLaunch q, uint3
 #pragma unroll
     for (int m = 1; m < 32; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
     if (!valid) continue;
-    int e = -127;
-    if (M > 0.0f) {
-      e = ilogbf(M) - 3;  // qmax < 8, so M > qmax * 2^(ilogb(M) - 3)
-      if (e < -127) e = -127;
-      while (e < 127 && M > ldexpf(qmax, e)) ++e;
-    }
+    const int e = pow2_exponent<GRID>(M);
     const float inv = ldexpf(1.0f, -e);  // exact power of two (2^-127 is a subnormal)
     const uint64_t e0 = (uint64_t)p * K + k0;
     if (q.rotated) store_rotated<W>(q.rotated + e0, y);
@@ -621,8 +655,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows_2d(QuantLaunch q, uint3
     uint32_t packed[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < W; ++j) {
-      // power-of-two scale: |v| <= qmax exactly, no clamp needed
-      const float v = __fmul_rn(y[j], inv);
+      // power-of-two scale: |v| <= qmax exactly unless e hit its clamp at 127
+      float v = __fmul_rn(y[j], inv);
+      if (e == 127) v = fminf(fmaxf(v, -qmax), qmax);
       uint32_t nib;
       if constexpr (RND == 0) {
         nib = rtne_nibble<GRID>(v);
@@ -687,6 +722,10 @@ hipError_t run_dual_1d(const QuantLaunch& q, const RowSide& r, hipStream_t s) {
 #define UFP4_RUN(B_, N_)                                                       \
   if (q.bc == B_ && q.n == N_) {                                              \
     constexpr int W_ = (B_ == 32 || N_ >= 32) ? 32 : 16;                      \
+    if (B_ == 32 && q.scale_mode == 1) {                                       \
+      if (q.rounding == 0) return run_dual<W_, B_, N_, G, 2>(q, r, s);         \
+      return run_dual<W_, B_, N_, G, 3>(q, r, s);                              \
+    }                                                                          \
     if (q.rounding == 0) return run_dual<W_, B_, N_, G, 0>(q, r, s);           \
     return run_dual<W_, B_, N_, G, 1>(q, r, s);                                \
   }
@@ -706,6 +745,11 @@ hipError_t run_1d(const QuantLaunch& q, hipStream_t s) {
 #define UFP4_RUN(B_, N_)                                                                    \
   if (q.bc == B_ && q.n == N_) {                                                           \
     constexpr int W_ = (B_ == 32 || N_ >= 32) ? 32 : 16;                                   \
+    if (B_ == 32 && q.scale_mode == 1) {                                                   \
+      if (q.rounding == 0)                                                                 \
+        return COLS ? run_cols<W_, B_, N_, G, 2>(q, s) : run_rows<W_, B_, N_, G, 2>(q, s); \
+      return COLS ? run_cols<W_, B_, N_, G, 3>(q, s) : run_rows<W_, B_, N_, G, 3>(q, s);   \
+    }                                                                                      \
     if (q.rounding == 0)                                                                   \
       return COLS ? run_cols<W_, B_, N_, G, 0>(q, s) : run_rows<W_, B_, N_, G, 0>(q, s);   \
     return COLS ? run_cols<W_, B_, N_, G, 1>(q, s) : run_rows<W_, B_, N_, G, 1>(q, s);     \

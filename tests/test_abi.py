@@ -91,6 +91,8 @@ def test_quant_argument_errors():
     assert _quant(lib, rows=48, cfg=two_d) == E.UFP4_ERR_SHAPE      # P % 32
     bad = two_d.copy(scale_mode=U.UFP4_SCALE_F32)
     assert _quant(lib, cfg=bad) == E.UFP4_ERR_UNSUPPORTED
+    # 1D power-of-two scales only with the 1 x 32 MX block
+    assert _quant(lib, cfg=U.make_cfg(scale_mode=U.UFP4_SCALE_POW2, block_cols=16)) == E.UFP4_ERR_UNSUPPORTED
     # empty inputs are a successful no-op (no HIP call is made)
     assert _quant(lib, rows=0) == E.UFP4_OK
     assert _quant(lib, cols=0, ld=0) == E.UFP4_OK

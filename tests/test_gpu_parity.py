@@ -229,6 +229,63 @@ def test_quant_dual_segmented():
     _assert_q_equal(qc, ref, "col")
 
 
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("rnd", [U.UFP4_RTNE, U.UFP4_SR])
+@pytest.mark.parametrize("n", [1, 16, 32, 128])
+@pytest.mark.parametrize("along", [0, 1])
+def test_quant_pow2_1x32(grid, rnd, n, along):
+    """1 x 32 blocks with power-of-two (E8M0) scales, row- and column-wise,
+    bit-exact with the oracle (rotated values, E8M0 bytes, codes)."""
+    _print_case("pow2 1x32", grid, rnd, n, along)
+    cfg = U.make_cfg(grid, rnd, U.UFP4_SCALE_POW2, 1, 32, n, sign_seed=21, sr_seed=4, sr_stream=1)
+    rows, cols = (288, 416) if n <= 32 else (384, 384)
+    compare_quant(rand_bits(rows, cols, 60 + n), along, cfg)
+
+
+@pytest.mark.parametrize("grid", GRIDS)
+def test_quant_dual_pow2(grid):
+    _print_case("dual pow2", grid)
+    bits = rand_bits(320, 192, 91)
+    cr = U.make_cfg(grid, U.UFP4_SR, U.UFP4_SCALE_POW2, 1, 32, 32, sign_seed=1, sr_seed=2, sr_stream=0)
+    cc = U.make_cfg(grid, U.UFP4_SR, U.UFP4_SCALE_POW2, 1, 32, 32, sign_seed=3, sr_seed=2, sr_stream=1)
+    qr, qc = U.ufp4_rht_quant_dual(dev_bf16(bits), cr, cc)
+    torch.cuda.synchronize()
+    for q, ref in ((qr, O.quantize(bits, 0, spec_of(cr))), (qc, O.quantize(bits, 1, spec_of(cc)))):
+        assert np.array_equal(q.scales.cpu().numpy().reshape(-1), np.asarray(ref["scales"]).reshape(-1))
+        assert np.array_equal(q.codes.cpu().numpy().reshape(-1), np.asarray(ref["codes"]).reshape(-1))
+
+
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("K", [160, 384, 512])
+def test_gemm_pow2_1x32(grid, K):
+    """GEMMs on 1 x 32 power-of-two operands: the scaled matrix cores take
+    one E8M0 byte per row and 32-element block (K % 128 == 0), split-bf16
+    otherwise."""
+    _print_case("gemm pow2 1x32", grid, K)
+    cfg = U.make_cfg(grid, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 32, sign_seed=8)
+    ta, tb = rand_bits(544, K, 31), rand_bits(288, K, 32)
+    qa, ra = compare_quant(ta, 0, cfg, with_rotated=False)
+    qb, rb = compare_quant(tb, 0, cfg, with_rotated=False)
+    C = U.ufp4_gemm_fprop(qa, qb).cpu().numpy()
+    ref = O.gemm_ref(oracle_dequant64(ra, cfg), oracle_dequant64(rb, cfg))
+    assert O.rel_fro(C, ref) <= GEMM_TOL
+
+
+def test_pow2_2d_exponent_clamp():
+    """Blocks whose absmax exceeds qmax * 2^127 (bf16 values near the top of
+    the range): the E8M0 exponent clamps at 127 and the values clamp at
+    qmax, as in the oracle."""
+    _print_case("pow2 clamp")
+    bits = rand_bits(64, 64, 5)
+    big = np.array([0x7F7F, 0xFF7F, 0x7F70, 0x7F60], dtype=np.uint16)   # ~3.39e38, -3.39e38, ...
+    bits[0, 0:4] = big
+    bits[40, 40:44] = big
+    for grid in GRIDS:
+        for cfg in (U.make_cfg(grid, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 32, 32, 1),
+                    U.make_cfg(grid, U.UFP4_SR, U.UFP4_SCALE_POW2, 1, 32, 1, sr_seed=3)):
+            compare_quant(bits, 0, cfg)
+
+
 def test_segmented_quant_and_grouped_gemms():
     """Four experts (one empty), per-expert transposed operands, and the
     three grouped GEMMs against per-expert oracle products."""

@@ -409,3 +409,26 @@ def test_segmented_draw_indices_continue():
     assert np.array_equal(segs[0]["codes"], whole_first["codes"])
     second = O.quantize(t[32:], 1, spec, elem_base=16 * 32)
     assert np.array_equal(segs[1]["codes"], second["codes"])
+
+
+@pytest.mark.parametrize("grid", [O.E1M2, O.INT4, O.E2M1])
+def test_pow2_1x32_lossless_on_grid(grid):
+    """1 x 32 power-of-two blocks ([2DFP4] scale equation applied to 1D
+    blocks): a tensor whose blocks are codebook levels times 2^e, with the
+    largest level present in every block, is reproduced exactly by
+    quantization + dequantization, and the stored exponent is e."""
+    rng = np.random.default_rng(5)
+    lv = O.LEVELS[grid]
+    P, K = 8, 128
+    e = rng.integers(-20, 20, size=(P, K // 32))
+    idx = rng.integers(0, len(lv), size=(P, K))
+    sgn = rng.choice([-1.0, 1.0], size=(P, K))
+    idx[:, ::32] = len(lv) - 1                       # qmax in every block
+    vals = sgn * lv[idx] * np.repeat(2.0 ** e, 32, axis=1)
+    bits = torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.bf16_bits_to_f32(bits).astype(np.float64), vals)   # exact in bf16
+    spec = O.QuantSpec(grid, O.RTNE, O.SCALE_POW2, 1, 32, 1)
+    r = O.quantize(bits, 0, spec)
+    assert np.array_equal(r["scales"].astype(np.int64), e + 127)
+    d32, d64 = O.dequant(r["codes"], r["scales"], spec, P, K)
+    assert np.array_equal(d64, vals)
