@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0     # dense bf16 MFMA (the family the GEMM issues)
-FP4_PEAK_TFLOPS = 10100.0     # dense fp4/fp6 MFMA, context only
+FP4_PEAK_TFLOPS = 10100.0     # dense fp4/fp6 MFMA
+FP8_PEAK_TFLOPS = 5000.0      # dense fp8 MFMA
 QBYTES_PER_ELEM = 2.75        # bf16 in (2) + 4-bit code (0.5) + fp32 scale / 16 (0.25)
 
 # HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per
@@ -75,6 +76,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--grid", default="e1m2", choices=["e1m2", "int4", "e2m1"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-mx", action="store_true",
+                   help="skip the power-of-two (scaled matrix core) GEMM figures")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain device-to-device copy of 1 GiB five times (known "
                         "bytes, to scale the profiler's FETCH_SIZE / WRITE_SIZE counters)")
@@ -167,6 +170,71 @@ class Workload:
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
+
+
+def mx_gemms(U, torch, reps=10):
+    """The GEMMs of the power-of-two configurations on the scaled matrix
+    cores, each timed over back-to-back launches (context; not part of the
+    step): the square-block layer M=16384 K=4096 N=4096 (32 x 32 E8M0 blocks,
+    W quantized once and reused transposed, SR, no rotation) with E2M1 and
+    E1M2 codes, and FPROP of the dense layer with 1 x 32 E8M0 blocks."""
+    import workloads
+    out = {}
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    lib = U.lib_handle()
+
+    def timed(fn, a, b, c):
+        qa, qb = a.c(), b.c()
+        args = (ctypes.byref(qa), ctypes.byref(qb), ctypes.c_void_p(c.data_ptr()), c.stride(0), stream)
+        for _ in range(2):
+            fn(*args)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    wl = workloads.config5("cuda")
+    X, W, dY = wl.tensors["X"], wl.tensors["W"], wl.tensors["dY"]
+    M, K = X.shape
+    N = W.shape[0]
+    for gname, grid in (("e2m1", U.UFP4_E2M1), ("e1m2", U.UFP4_E1M2)):
+        mk = lambda st: U.make_cfg(grid, U.UFP4_SR, U.UFP4_SCALE_POW2, 32, 32, 1,  # noqa: E731
+                                   sr_seed=wl.meta["sr_seed"], sr_stream=st)
+        qx, _ = U.ufp4_rht_quant(X, 0, mk(0))
+        qw, _ = U.ufp4_rht_quant(W, 0, mk(1))
+        qdy, _ = U.ufp4_rht_quant(dY, 0, mk(2))
+        qwt, qxt, qdyt = (U.ufp4_transpose_qtensor(q) for q in (qw, qx, qdy))
+        peak = FP4_PEAK_TFLOPS if grid == U.UFP4_E2M1 else FP8_PEAK_TFLOPS
+        for name, a, b, shp in (("fprop", qx, qw, (M, N)), ("dgrad", qdy, qwt, (M, K)),
+                                ("wgrad", qdyt, qxt, (N, K))):
+            c = torch.empty(shp, dtype=torch.float32, device="cuda")
+            ms = timed(getattr(lib, "ufp4_gemm_" + name), a, b, c)
+            tf = 2.0 * M * N * K / ms / 1e9
+            out[f"square_blocks_{M}x{K}x{N}_{gname}_{name}"] = {
+                "ms": round(ms, 4), "TFLOP/s": round(tf, 1), "peak": peak,
+                "frac": round(tf / peak, 4),
+                "mfma": "v_mfma_scale_f32_32x32x64_f8f6f4 (" + ("FP4" if grid == U.UFP4_E2M1 else "FP8 E4M3") + ")"}
+        del qx, qw, qdy, qwt, qxt, qdyt
+    # dense layer FPROP with 1 x 32 E8M0 blocks, n = 32 rotation
+    wl2 = workloads.config2("cuda")
+    X2, W2 = wl2.tensors["X"], wl2.tensors["W"]
+    M2, K2 = X2.shape
+    N2 = W2.shape[0]
+    for gname, grid in (("e2m1", U.UFP4_E2M1), ("e1m2", U.UFP4_E1M2)):
+        cfg = U.make_cfg(grid, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 32, sign_seed=wl2.meta["sign_seeds"][0])
+        qx, _ = U.ufp4_rht_quant(X2, 0, cfg)
+        qw, _ = U.ufp4_rht_quant(W2, 0, cfg)
+        c = torch.empty((M2, N2), dtype=torch.float32, device="cuda")
+        ms = timed(lib.ufp4_gemm_fprop, qx, qw, c)
+        tf = 2.0 * M2 * N2 * K2 / ms / 1e9
+        peak = FP4_PEAK_TFLOPS if grid == U.UFP4_E2M1 else FP8_PEAK_TFLOPS
+        out[f"dense_1x32_e8m0_{M2}x{K2}x{N2}_{gname}_fprop"] = {
+            "ms": round(ms, 4), "TFLOP/s": round(tf, 1), "peak": peak, "frac": round(tf / peak, 4)}
+    return out
 
 
 def cpu_oracle_baseline(grid):
@@ -285,6 +353,13 @@ def main():
     quant_gbps = sum(qbytes.values()) / quant_ms / 1e6
     value = total_flops / (ms_step * 1e-3) / 1e12
 
+    wl_m, wl_k, wl_n = wl.M, wl.K, wl.N
+    mx = None
+    if not args.no_mx:
+        del wl   # free the step's buffers first
+        torch.cuda.empty_cache()
+        mx = mx_gemms(U, torch)
+
     cpu = None
     if not args.no_cpu:
         try:
@@ -300,9 +375,9 @@ def main():
         "vs_baseline": None, "dtype": args.grid,
         "dtype_detail": "bf16 in; fp32 rotate/scale/round; 4-bit codes; split-bf16 MFMA, fp32 accumulate",
         "data": "synthetic (seeded torch generators; dense linear-layer tensors)",
-        "config": {"workload": f"dense linear layer M={wl.M} K={wl.K} N={wl.N}: 6 fused RHT(n=16)"
+        "config": {"workload": f"dense linear layer M={wl_m} K={wl_k} N={wl_n}: 6 fused RHT(n=16)"
                                f"+1x16 {args.grid} quantizations (SR on dY) + FPROP/DGRAD/WGRAD",
-                   "global_batch": wl.M, "seq_len": None, "parallelism": "single GPU"},
+                   "global_batch": wl_m, "seq_len": None, "parallelism": "single GPU"},
         "roofline": roof,
         "quant": {"GB/s": round(quant_gbps, 1), "frac_hbm_peak": round(quant_gbps / HBM_PEAK_GBPS, 4),
                   "ms": round(quant_ms, 4), "bytes_per_elem": QBYTES_PER_ELEM},
@@ -312,6 +387,7 @@ def main():
                  "ms": round(gemm_ms, 4)},
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "mx_gemms": mx,
         "wall_s": round(wall, 3),
     }
     print(json.dumps(line), flush=True)

@@ -27,6 +27,7 @@
 // The LDS tile is laid out [part][k-chunk of 8][row] x 16 B, so a fragment
 // read is 16 B per lane with consecutive lanes on consecutive rows.
 #include "ufp4_internal.h"
+#include "gemm_epilogue.h"
 
 namespace ufp4 {
 
@@ -530,18 +531,12 @@ __global__ __launch_bounds__(kThreads8) void k_gemm8(GemmLaunch g) {
   }
   if (step < nsteps) body(step, x, y);
 
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = (int64_t)tn * TN + wn * 64 + j * 32 + (lane & 31);
-      if (col >= pr.b_rows) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t rr = (int64_t)tm * TM + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (rr < pr.a_rows) pr.c[rr * g.ldc + col] = acc[i][j][r];
-      }
-    }
+  {
+    const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
+    const int rv = (int)(pr.a_rows - row0 < TM ? pr.a_rows - row0 : TM);
+    const int cv = (int)(pr.b_rows - col0 < TN ? pr.b_rows - col0 : TN);
+    store_c<4, 2>(pr.c + row0 * g.ldc + col0, g.ldc, rv, cv, wm * 128, wn * 64, lane, acc);
+  }
 }
 
 }  // namespace

@@ -1,0 +1,84 @@
+// Store of a wave's fp32 C block for the 256 x 256-tile GEMM kernels.
+//
+// The accumulators of a 32 x 32 MFMA tile hold, in lane l and register r,
+// column l % 32 and row 8 (r / 4) + 4 (l / 32) + r % 4.  The stores go
+// through a buffer resource whose base is the tile's first element and whose
+// size ends at the last valid row, so rows past the operand are dropped by
+// the hardware bound check; lanes whose column is past the operand get an
+// offset beyond the bound.  Each store is then one 32-bit add and one
+// buffer_store_dword, instead of 64-bit address arithmetic and a branch per
+// element.
+#pragma once
+
+#include "ufp4_internal.h"
+
+namespace ufp4 {
+
+typedef float c_floatx16 __attribute__((ext_vector_type(16)));
+
+// True when a tile's C region fits a 32-bit buffer offset (else the caller
+// uses plain stores).
+__device__ __forceinline__ bool c_fits_buffer(int64_t ldc, int rows) {
+  return (int64_t)rows * ldc * 4 < ((int64_t)1 << 31);
+}
+
+// Store the NI x NJ MFMA tiles of one wave.  c_tile: C + row0 * ldc + col0;
+// rows_valid / cols_valid: extent of C inside the tile; r0 / c0: the wave's
+// first row / column inside the tile.
+template <int NI, int NJ>
+__device__ __forceinline__ void store_c_tile(float* c_tile, int64_t ldc, int rows_valid,
+                                             int cols_valid, int r0, int c0, int lane,
+                                             const c_floatx16 (&acc)[NI][NJ]) {
+  const uint32_t ld4 = (uint32_t)ldc * 4u;
+  const uint32_t bound = (uint32_t)rows_valid * ld4;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(c_tile, (short)0, (int)bound, 0x00020000);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int col = c0 + j * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t row = (uint32_t)(r0 + i * 32 + 4 * (lane >> 5));
+      const uint32_t base = col < cols_valid ? row * ld4 + 4u * (uint32_t)col : bound;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t off = base + (uint32_t)(8 * (r >> 2) + (r & 3)) * ld4;
+        // __float_as_uint, not __builtin_bit_cast: the bit cast of an
+        // accumulator element reaching this intrinsic was lowered to the same
+        // register for every element
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rs, (int)off, 0, 0);
+      }
+    }
+  }
+}
+
+// Plain stores with explicit bounds (large leading dimensions).
+template <int NI, int NJ>
+__device__ __forceinline__ void store_c_plain(float* c_tile, int64_t ldc, int rows_valid,
+                                              int cols_valid, int r0, int c0, int lane,
+                                              const c_floatx16 (&acc)[NI][NJ]) {
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int col = c0 + j * 32 + (lane & 31);
+    if (col >= cols_valid) continue;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = r0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < rows_valid) c_tile[(int64_t)row * ldc + col] = acc[i][j][r];
+      }
+  }
+}
+
+template <int NI, int NJ>
+__device__ __forceinline__ void store_c(float* c_tile, int64_t ldc, int rows_valid,
+                                        int cols_valid, int r0, int c0, int lane,
+                                        const c_floatx16 (&acc)[NI][NJ]) {
+  if (c_fits_buffer(ldc, 256))
+    store_c_tile<NI, NJ>(c_tile, ldc, rows_valid, cols_valid, r0, c0, lane, acc);
+  else
+    store_c_plain<NI, NJ>(c_tile, ldc, rows_valid, cols_valid, r0, c0, lane, acc);
+}
+
+}  // namespace ufp4

@@ -45,6 +45,7 @@
 //   k_gemm_mx<GRID> (E1M2, INT4): K step 128; codes are loaded into registers
 //     two steps ahead, converted to E4M3 and written to LDS (two stages).
 #include "ufp4_internal.h"
+#include "gemm_epilogue.h"
 
 namespace ufp4 {
 
@@ -297,18 +298,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(GemmLaunch g) {
   }
   if (step < c.nsteps) body(step, y, x);
 
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = col0 + wn * 128 + j * 32 + (lane & 31);
-      if (col >= g.PB) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = row0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < g.PA) g.c[row * g.ldc + col] = acc[i][j][r];
-      }
-    }
+  store_c<4, 4>(g.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
+                lane, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -519,18 +510,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx4(GemmLaunch g) {
   for (; step < c.nsteps; ++step) body(step, step & 3);
   wait_vmcnt<0>();   // drain the clamped prefetches before the workgroup ends
 
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = col0 + wn * 128 + j * 32 + (lane & 31);
-      if (col >= g.PB) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = row0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < g.PA) g.c[row * g.ldc + col] = acc[i][j][r];
-      }
-    }
+  store_c<4, 4>(g.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
+                lane, acc);
 }
 
 hipError_t launch_mx4(const GemmLaunch& g, hipStream_t s) {
@@ -685,18 +666,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx4w(GemmLaunch g) {
     w4_scales(nxt, lane, wm, wn, sa, sb);
   }
 
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = col0 + wn * 128 + j * 32 + (lane & 31);
-      if (col >= g.PB) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = row0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < g.PA) g.c[row * g.ldc + col] = acc[i][j][r];
-      }
-    }
+  store_c<4, 4>(g.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
+                lane, acc);
 }
 
 hipError_t launch_mx4w(const GemmLaunch& g, hipStream_t s) {

@@ -29,6 +29,7 @@
 // strips in its L2.  K need only be a multiple of 16: k-blocks past K get a
 // zero scale, and rows past the operand read as zeros (buffer bound).
 #include "ufp4_internal.h"
+#include "gemm_epilogue.h"
 
 namespace ufp4 {
 
@@ -412,18 +413,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
     }
   }
 
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = col0 + wn * 128 + j * 32 + (lane & 31);
-      if (col >= o.b_rows) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = row0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < o.a_rows) o.c[row * g.ldc + col] = acc[i][j][r];
-      }
-    }
+  store_c<4, 4>(o.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
+                lane, acc);
 }
 
 template <int GRID, int BC>
