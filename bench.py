@@ -40,15 +40,19 @@ QBYTES_PER_ELEM = 2.75        # bf16 in (2) + 4-bit code (0.5) + fp32 scale / 16
 # --calibrate-copy).  A figure holds only for the kernel source it was taken
 # on: the sources' hash is recorded and a mismatch reports null.
 FETCH_SCALE, WRITE_SCALE = 1048576 / 524302.3, 1048576 / 1048576.0
+_GEMM_SRC = ("gemm_rd.hip", "gemm_epilogue.h", "ufp4_internal.h")
+_QUANT_SRC = ("quant_core.h", "ufp4_internal.h")
 MEASURED_TRAFFIC = {
     # kernel: (sources, sha256[:16] of them, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "fprop": (("gemm.hip", "ufp4_internal.h"), "2abdb5ff4ba07787", 74055.3, 262144.0),
-    "dgrad": (("gemm.hip", "ufp4_internal.h"), "2abdb5ff4ba07787", 203094.6, 65536.0),
-    "wgrad": (("gemm.hip", "ufp4_internal.h"), "2abdb5ff4ba07787", 203094.6, 65536.0),
-    "quant_x_row": (("quant_core.h", "ufp4_internal.h"), "78a066d590344e24", 16436.2, 12288.0),
-    "quant_dy_row": (("quant_core.h", "ufp4_internal.h"), "78a066d590344e24", 65606.7, 49152.0),
-    "quant_dy_col": (("quant_core.h", "ufp4_internal.h"), "78a066d590344e24", 65686.4, 71276.4),
-    "quant_x_col": (("quant_core.h", "ufp4_internal.h"), "78a066d590344e24", 16434.6, 12288.9),
+    "fprop": (_GEMM_SRC, "69a0dd8a174253a5", 74041.9, 262144.0),
+    "dgrad": (_GEMM_SRC, "69a0dd8a174253a5", 73860.2, 65536.0),
+    "wgrad": (_GEMM_SRC, "69a0dd8a174253a5", 73860.2, 65536.0),
+    "quant_x_row": (_QUANT_SRC, "d1c5c161c8474b6f", 16423.8, 12288.0),
+    "quant_w_row": (_QUANT_SRC, "d1c5c161c8474b6f", 16423.8, 12288.0),
+    "quant_dy_row": (_QUANT_SRC, "d1c5c161c8474b6f", 65604.9, 49152.0),
+    "quant_x_col": (_QUANT_SRC, "d1c5c161c8474b6f", 16450.1, 12288.1),
+    "quant_w_col": (_QUANT_SRC, "d1c5c161c8474b6f", 16450.1, 12288.1),
+    "quant_dy_col": (_QUANT_SRC, "d1c5c161c8474b6f", 65626.7, 50629.7),
 }
 
 
@@ -185,7 +189,10 @@ def mx_gemms(U, torch, reps=10):
 
     def timed(fn, a, b, c):
         qa, qb = a.c(), b.c()
-        args = (ctypes.byref(qa), ctypes.byref(qb), ctypes.c_void_p(c.data_ptr()), c.stride(0), stream)
+        return timed_args(fn, (ctypes.byref(qa), ctypes.byref(qb), ctypes.c_void_p(c.data_ptr()),
+                               c.stride(0), stream))
+
+    def timed_args(fn, args):
         for _ in range(2):
             fn(*args)
         torch.cuda.synchronize()
@@ -208,6 +215,15 @@ def mx_gemms(U, torch, reps=10):
         qw, _ = U.ufp4_rht_quant(W, 0, mk(1))
         qdy, _ = U.ufp4_rht_quant(dY, 0, mk(2))
         qwt, qxt, qdyt = (U.ufp4_transpose_qtensor(q) for q in (qw, qx, qdy))
+        if grid == U.UFP4_E2M1:   # the transpose that reuses dY for WGRAD
+            qd = qdy.c()
+            ms = timed_args(lib.ufp4_transpose_qtensor,
+                            (ctypes.byref(qd), ctypes.c_void_p(qdyt.codes.data_ptr()),
+                             ctypes.c_void_p(qdyt.scales.data_ptr()), stream))
+            nbytes = 2 * (qdy.codes.numel() + qdy.scales.numel() * qdy.scales.element_size())
+            out[f"transpose_square_blocks_{M}x{N}_codes_scales"] = {
+                "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
+                "frac_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBPS, 4)}
         peak = FP4_PEAK_TFLOPS if grid == U.UFP4_E2M1 else FP8_PEAK_TFLOPS
         for name, a, b, shp in (("fprop", qx, qw, (M, N)), ("dgrad", qdy, qwt, (M, K)),
                                 ("wgrad", qdyt, qxt, (N, K))):

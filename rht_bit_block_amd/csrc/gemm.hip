@@ -88,6 +88,10 @@ __device__ __forceinline__ Problem resolve(const GemmLaunch& g, int tile, int& t
     pr.c = g.c + (int64_t)grp * g.PA * g.ldc;
   }
   const int tiles_n = (int)((pr.b_rows + TN - 1) / TN);
+  if (g.mode == 0) {   // one dense problem: XCD-aware grouped order
+    tile_order(tile, g.total_tiles, (int)((pr.a_rows + TM - 1) / TM), tiles_n, tm, tn);
+    return pr;
+  }
   tm = local / max(tiles_n, 1);
   tn = local - tm * tiles_n;
   return pr;

@@ -1,4 +1,5 @@
-// Store of a wave's fp32 C block for the 256 x 256-tile GEMM kernels.
+// Tile order and the store of a wave's fp32 C block, shared by the
+// 256 x 256-tile GEMM kernels.
 //
 // The accumulators of a 32 x 32 MFMA tile hold, in lane l and register r,
 // column l % 32 and row 8 (r / 4) + 4 (l / 32) + r % 4.  The stores go
@@ -15,6 +16,26 @@
 namespace ufp4 {
 
 typedef float c_floatx16 __attribute__((ext_vector_type(16)));
+
+// Tile (tm, tn) that workgroup b of a dense T-tile launch computes.
+// Workgroups are dispatched round-robin over the 8 XCDs (b runs on XCD b % 8)
+// and each XCD has its own L2.  The tiles are first put in grouped order
+// (kGroupRows tile rows at a time, walking down a group's rows before moving
+// one tile column right), and each XCD then takes a contiguous range of that
+// order.  The 32 tiles one XCD runs at once then cover about 8 rows x 4
+// columns of C and share 12 operand strips, where a row-major range shares one
+// A strip and reads up to 32 B strips.
+constexpr int kGroupRows = 8;
+__device__ __forceinline__ void tile_order(int b, int T, int tiles_m, int tiles_n, int& tm,
+                                           int& tn) {
+  const int v = T % 8 == 0 ? (b % 8) * (T / 8) + b / 8 : b;
+  const int group = v / (kGroupRows * tiles_n);
+  const int first = group * kGroupRows;
+  const int gm = tiles_m - first < kGroupRows ? tiles_m - first : kGroupRows;
+  const int w = v - first * tiles_n;
+  tm = first + w % gm;
+  tn = w / gm;
+}
 
 // True when a tile's C region fits a 32-bit buffer offset (else the caller
 // uses plain stores).

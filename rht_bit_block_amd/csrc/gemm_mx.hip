@@ -215,16 +215,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(GemmLaunch g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int STAGE = 2 * TM * 128;
 
-  // XCD-aware tile order: workgroup b runs on XCD b % 8; give each XCD a
-  // contiguous range of tiles, row-major over (tm, tn), so tiles resident at
-  // the same time on one XCD share A strips (and B strips across rows).
-  const int T = g.total_tiles;
-  const int b = blockIdx.x;
-  const int per = (T + 7) / 8;
-  int t = (b % 8) * per + b / 8;
-  if (T % 8) t = b;   // uneven split: keep the plain order
-  const int tiles_n = (int)((g.PB + TN - 1) / TN);
-  const int tm = t / tiles_n, tn = t - tm * tiles_n;
+  int tm, tn;
+  tile_order(blockIdx.x, g.total_tiles, (int)((g.PA + TM - 1) / TM), (int)((g.PB + TN - 1) / TN),
+             tm, tn);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
@@ -426,13 +419,9 @@ __device__ __forceinline__ void f4_mfma(floatx16 (&acc)[4][4], const F4Frags& f,
 __global__ __launch_bounds__(kThreads) void k_gemm_mx4(GemmLaunch g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  const int T = g.total_tiles;
-  const int b = blockIdx.x;
-  const int per = (T + 7) / 8;
-  int t = (b % 8) * per + b / 8;
-  if (T % 8) t = b;
-  const int tiles_n = (int)((g.PB + TN - 1) / TN);
-  const int tm = t / tiles_n, tn = t - tm * tiles_n;
+  int tm, tn;
+  tile_order(blockIdx.x, g.total_tiles, (int)((g.PA + TM - 1) / TM), (int)((g.PB + TN - 1) / TN),
+             tm, tn);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
@@ -594,13 +583,9 @@ __device__ __forceinline__ void w4_scales(const uint8_t* stage, int lane, int wm
 __global__ __launch_bounds__(kThreads) void k_gemm_mx4w(GemmLaunch g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  const int T = g.total_tiles;
-  const int b = blockIdx.x;
-  const int per = (T + 7) / 8;
-  int t = (b % 8) * per + b / 8;
-  if (T % 8) t = b;
-  const int tiles_n = (int)((g.PB + TN - 1) / TN);
-  const int tm = t / tiles_n, tn = t - tm * tiles_n;
+  int tm, tn;
+  tile_order(blockIdx.x, g.total_tiles, (int)((g.PA + TM - 1) / TM), (int)((g.PB + TN - 1) / TN),
+             tm, tn);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;

@@ -315,11 +315,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
   using L = Layout<BC>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  int b = blockIdx.x;
-  if (g.mode == 0 && g.total_tiles % 8 == 0)   // XCD b % 8 gets a contiguous tile range
-    b = (b % 8) * (g.total_tiles / 8) + b / 8;
   int tm, tn;
-  const Operands o = resolve(g, b, tm, tn);
+  const Operands o = resolve(g, blockIdx.x, tm, tn);
+  if (g.mode == 0)   // one dense problem: XCD-aware grouped order
+    tile_order(blockIdx.x, g.total_tiles, (int)((o.a_rows + TM - 1) / TM),
+               (int)((o.b_rows + TN - 1) / TN), tm, tn);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;

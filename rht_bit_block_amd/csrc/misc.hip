@@ -64,6 +64,88 @@ __global__ void k_transpose_codes(const uint8_t* src, int64_t P, int64_t K, uint
   }
 }
 
+// 8 x 8 nibble transpose in registers: r[i] holds row i (column c at bits
+// 4c); afterwards r[c] holds column c (row i at bits 4i).  Three rounds swap
+// the off-diagonal 4 x 4, then 2 x 2, then 1 x 1 blocks.
+__device__ __forceinline__ void transpose_nibbles8(uint32_t (&r)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t t = ((r[i] >> 16) ^ r[i + 4]) & 0x0000FFFFu;
+    r[i] ^= t << 16;
+    r[i + 4] ^= t;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = (q & 1) + 4 * (q >> 1);   // 0, 1, 4, 5
+    const uint32_t t = ((r[i] >> 8) ^ r[i + 2]) & 0x00FF00FFu;
+    r[i] ^= t << 8;
+    r[i + 2] ^= t;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const uint32_t t = ((r[i] >> 4) ^ r[i + 1]) & 0x0F0F0F0Fu;
+    r[i] ^= t << 4;
+    r[i + 1] ^= t;
+  }
+}
+
+constexpr int kTE = 256;   // transpose tile edge, in nibbles
+
+// Word w of staged tile row `row`, XOR-swizzled so that the 16-byte staging
+// writes (8 lanes per row) and the block reads (32 lanes, one row each 8
+// apart) both fall on distinct banks.
+__device__ __forceinline__ int staged_word(int row, int w) {
+  return row * 32 + (w ^ (((row >> 3) ^ (row & 7)) & 31));
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Tiled codes transpose (P, K multiples of 8; P * K / 2 < 2^31): one
+// workgroup per 256 x 256-nibble tile.  The source tile (256 rows x 128 B)
+// is staged in LDS with full 16-byte row loads; each thread then transposes
+// four 8 x 8 nibble blocks in registers and 32 consecutive lanes store one
+// 128-byte run of a destination row.  Rows past P read as zero (buffer bound)
+// and nothing past P or K is stored.
+__global__ __launch_bounds__(256) void k_transpose_codes_tiled(const uint8_t* src, int64_t P,
+                                                               int64_t K, uint8_t* dst,
+                                                               int tiles_k) {
+  __shared__ uint32_t t[kTE * 32];
+  const int tid = threadIdx.x;
+  const int64_t p0 = (int64_t)(blockIdx.x / tiles_k) * kTE;
+  const int64_t k0 = (int64_t)(blockIdx.x % tiles_k) * kTE;
+  const uint32_t row_bytes = (uint32_t)(K / 2);
+  const uint32_t bound = (uint32_t)(P * (K / 2));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(src), (short)0, (int)bound, 0x00020000);
+  const int c = tid & 7;
+#pragma unroll
+  for (int ps = 0; ps < 8; ++ps) {
+    const int r = ps * 32 + (tid >> 3);
+    const int64_t p = p0 + r;
+    const uint32_t off = p < P ? (uint32_t)p * row_bytes + (uint32_t)(k0 / 2) + 16u * c : bound;
+    const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[staged_word(r, 4 * c + e)] = v[e];
+  }
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6, pb = lane & 31;
+  const bool p_ok = p0 + 8 * pb < P;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int kb = (lane >> 5) + 2 * wave + 8 * j;
+    uint32_t r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = t[staged_word(8 * pb + i, kb)];
+    transpose_nibbles8(r);
+    if (!p_ok) continue;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t k = k0 + 8 * kb + e;
+      if (k < K) *reinterpret_cast<uint32_t*>(dst + k * (P / 2) + p0 / 2 + 4 * pb) = r[e];
+    }
+  }
+}
+
 __global__ void k_transpose_scales(const uint8_t* src, int64_t rb, int64_t cb, int esize,
                                    uint8_t* dst) {
   const int64_t n = rb * cb;
@@ -110,8 +192,17 @@ hipError_t launch_transpose(const uint8_t* codes, const void* scales, int64_t P,
                             hipStream_t s) {
   const int64_t nbytes = K * (P / 2);
   if (nbytes == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_transpose_codes, dim3(grid_for(nbytes, 256)), dim3(256), 0, s, codes, P, K,
-                     dcodes);
+  const bool tiled = P % 8 == 0 && K % 8 == 0 && P * (K / 2) < ((int64_t)1 << 31) &&
+                     reinterpret_cast<uintptr_t>(codes) % 4 == 0 &&
+                     reinterpret_cast<uintptr_t>(dcodes) % 4 == 0;
+  if (tiled) {
+    const int64_t tiles_k = (K + kTE - 1) / kTE, tiles = ((P + kTE - 1) / kTE) * tiles_k;
+    hipLaunchKernelGGL(k_transpose_codes_tiled, dim3((unsigned)tiles), dim3(256), 0, s, codes, P,
+                       K, dcodes, (int)tiles_k);
+  } else {
+    hipLaunchKernelGGL(k_transpose_codes, dim3(grid_for(nbytes, 256)), dim3(256), 0, s, codes, P,
+                       K, dcodes);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rb = P / b, cb = K / b;

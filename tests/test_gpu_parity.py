@@ -169,6 +169,25 @@ def test_gemm_2d_and_transpose(grid):
     assert O.rel_fro(dX, O.gemm_ref(oracle_dequant64(rdy, cfg), dw.T)) <= GEMM_TOL
 
 
+@pytest.mark.parametrize("P,K", [(32, 32), (288, 544), (1056, 800), (4096, 4096)])
+def test_transpose_shapes(P, K):
+    """The square-block transpose on tile-ragged shapes and a full-size
+    operand: codes and scale grid exactly the transposed ones.  The operand is
+    built from seeded random codes and E8M0 scales (a transpose only moves
+    them)."""
+    _print_case("transpose", P, K)
+    rng = np.random.default_rng(P * 7 + K)
+    codes = rng.integers(0, 16, (P, K), dtype=np.uint8)
+    scales = rng.integers(100, 150, (P // 32, K // 32), dtype=np.uint8)
+    cfg = U.make_cfg(U.UFP4_E2M1, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 32, 32, 1)
+    q = U.QTensor(torch.from_numpy(O.pack_nibbles(codes)).cuda(), torch.from_numpy(scales).cuda(),
+                  P, K, cfg)
+    qt = U.ufp4_transpose_qtensor(q)
+    assert (qt.P, qt.K) == (K, P)
+    assert np.array_equal(qt.codes.cpu().numpy(), O.pack_nibbles(np.ascontiguousarray(codes.T)))
+    assert np.array_equal(qt.scales.cpu().numpy(), scales.T)
+
+
 @pytest.mark.parametrize("grid", GRIDS)
 @pytest.mark.parametrize("K", [160, 384, 512])
 def test_gemm_pow2_paths(grid, K):
