@@ -432,3 +432,56 @@ def test_pow2_1x32_lossless_on_grid(grid):
     assert np.array_equal(r["scales"].astype(np.int64), e + 127)
     d32, d64 = O.dequant(r["codes"], r["scales"], spec, P, K)
     assert np.array_equal(d64, vals)
+
+
+# ---------------------------------------------------------------------------
+# Worked examples of the printed equations (tests/golden/, each file cites
+# its passage; the numbers were worked out by hand, not by the oracle).
+# ---------------------------------------------------------------------------
+GOLDEN = os.path.join(HERE, "golden")
+GRID_NAMES = {"e1m2": O.E1M2, "int4": O.INT4, "e2m1": O.E2M1}
+
+
+def _golden_rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+def _golden_blocks(name):
+    blocks, cur = {}, None
+    with open(os.path.join(GOLDEN, name)) as f:
+        for ln in f:
+            if ln.startswith("# n="):
+                cur = int(ln[4:])
+                blocks[cur] = []
+            elif ln.strip() and not ln.startswith("#"):
+                blocks[cur].append([float(v) for v in ln.split()])
+    return {n: np.array(m) for n, m in blocks.items()}
+
+
+def test_golden_sylvester_matrices():
+    """[UFP4] Method, Sylvester recursion from H_1 = [1]."""
+    for n, m in _golden_blocks("sylvester_h4.txt").items():
+        assert np.array_equal(O.fwht(np.eye(n, dtype=np.float64), n), m)
+
+
+def test_golden_bin_bias():
+    """[UFP4] Method, bin-asymmetry equation: the oracle's rounding, averaged
+    over a locally uniform density in each bin, gives the worked values."""
+    rows = _golden_rows("bin_bias.txt")
+    by_grid = {}
+    for g, q, b in rows:
+        by_grid.setdefault(GRID_NAMES[g], []).append((float(q), float(b)))
+    for grid, entries in by_grid.items():
+        L = O.LEVELS[grid]
+        assert len(entries) == L.size - 2          # every interior level listed
+        got = _bin_bias(grid)
+        for q, b in entries:
+            assert abs(got[q] - b) <= 1e-5 * max(1.0, float(L[-1]))
+
+
+def test_golden_pow2_scale_exponents():
+    """[2DFP4] truncation-free scale equation, worked by hand."""
+    for g, m, e in _golden_rows("pow2_scale.txt"):
+        got = O.scale_pow2_exponent(np.array([float(m)], dtype=np.float32), GRID_NAMES[g])
+        assert int(got[0]) == int(e), (g, m)
