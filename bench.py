@@ -82,6 +82,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-mx", action="store_true",
                    help="skip the power-of-two (scaled matrix core) GEMM figures")
+    p.add_argument("--no-diag", action="store_true",
+                   help="skip the quantization diagnostics (level statistics) figures")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain device-to-device copy of 1 GiB five times (known "
                         "bytes, to scale the profiler's FETCH_SIZE / WRITE_SIZE counters)")
@@ -253,6 +255,63 @@ def mx_gemms(U, torch, reps=10):
     return out
 
 
+def diagnostics(U, torch, reps=10):
+    """Quantization diagnostics on the dense layer's X (context; not part of
+    the step): for E2M1 / E1M2 / INT4, without and with the RHT (n = 1, 16),
+    RTNE with 1 x 16 fp32 scales -- the fraction of elements on each
+    magnitude level, the mean rounding error E[rho(t) - t] per level in grid
+    units (bin-asymmetry equation), and FPROP's relative Frobenius error
+    against the fp32 product of the unquantized bf16 inputs.  Also the
+    level-statistics kernel's time (reads 2 B per element, writes nothing)."""
+    import numpy as np
+    import workloads
+    wl = workloads.config2("cuda")
+    X, W = wl.tensors["X"], wl.tensors["W"]
+    M, K = X.shape
+    ref = X.float() @ W.float().t()
+    ref_norm = torch.linalg.vector_norm(ref).item()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    lib = U.lib_handle()
+    out = {}
+    names = (("e2m1", U.UFP4_E2M1), ("e1m2", U.UFP4_E1M2), ("int4", U.UFP4_INT4))
+    stats = torch.empty(16, dtype=torch.int64, device="cuda")
+    for gname, grid in names:
+        for n in (1, 16):
+            cfg = U.make_cfg(grid, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 16, n,
+                             sign_seed=wl.meta["sign_seeds"][0])
+            U.ufp4_quant_diag(X, cfg, stats=stats)
+            st = stats.cpu().numpy()
+            cnt = st[:8].astype(np.float64)
+            util = (cnt / cnt.sum()).round(5).tolist()
+            mean = [round(float(st[8 + k]) * 2.0 ** -28 / cnt[k], 6) if cnt[k] else None
+                    for k in range(8)]
+            qx, _ = U.ufp4_rht_quant(X, 0, cfg)
+            qw, _ = U.ufp4_rht_quant(W, 0, cfg)
+            y = U.ufp4_gemm_fprop(qx, qw)
+            err = torch.linalg.vector_norm(y - ref).item() / ref_norm
+            out[f"X_{gname}_n{n}"] = {"level_util": util, "level_mean_err": mean,
+                                      "fprop_rel_err_vs_bf16": round(err, 6)}
+            del qx, qw, y
+    cfg = U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=1)
+    args = (ctypes.c_void_p(X.data_ptr()), M, K, K, ctypes.byref(cfg),
+            ctypes.c_void_p(stats.data_ptr()), stream)
+    for _ in range(2):
+        lib.ufp4_quant_diag(*args)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        lib.ufp4_quant_diag(*args)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbps = 2.0 * M * K / ms / 1e6
+    out["kernel_e1m2_n16"] = {"ms": round(ms, 4), "GB/s": round(gbps, 1),
+                              "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                              "bytes_per_elem": 2.0}
+    return out
+
+
 def cpu_oracle_baseline(grid):
     """The oracle as it stands on a bounded sample of the same workload: the
     dense step restricted to M' = 6144 tokens and N' = 6144 output features
@@ -375,6 +434,12 @@ def main():
         del wl   # free the step's buffers first
         torch.cuda.empty_cache()
         mx = mx_gemms(U, torch)
+    diag = None
+    if not args.no_diag:
+        if args.no_mx:
+            del wl
+            torch.cuda.empty_cache()
+        diag = diagnostics(U, torch)
 
     cpu = None
     if not args.no_cpu:
@@ -404,6 +469,7 @@ def main():
         "kernels": kernels,
         "cpu_baseline": cpu,
         "mx_gemms": mx,
+        "diagnostics": diag,
         "wall_s": round(wall, 3),
     }
     print(json.dumps(line), flush=True)

@@ -141,6 +141,23 @@ int ufp4_rht_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ld,
                         uint8_t* codes_row, void* scales_row, uint8_t* codes_col,
                         void* scales_col, void* stream);
 
+/* Level statistics of a row-wise quantization (diagnostics): the same
+ * transform, scale and rounding as ufp4_rht_quant with along = 0 and cfg, but
+ * nothing is stored except, for each magnitude level index k = 0..7 of the
+ * codebook, stats[k] = the number of elements rounded to level k and
+ * stats[8 + k] = the sum over those elements of rint((L_k - |t|) * 2^28) as a
+ * two's-complement int64, t the clamped normalized value the rounding acts on
+ * and L_k the level's magnitude in grid units.  stats[8+k] / stats[k] * 2^-28
+ * is then the per-level mean rounding error E[rho(t) - t] that [UFP4]'s
+ * bin-asymmetry equation (Method, Shrinkage Bias) predicts -- zero for the
+ * uniform grids, negative at E2M1's spacing changes under RTNE -- and the
+ * counts are the bucket utilisation the Method section attributes to the RHT.
+ * The sums are exact integers, so the result does not depend on launch order.
+ * stats: DEVICE uint64 [16], 8-byte aligned, overwritten.  cfg must be 1D
+ * (block_rows == 1); shapes and errors as ufp4_rht_quant. */
+int ufp4_quant_diag(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                    const ufp4_quant_cfg* cfg, uint64_t* stats, void* stream);
+
 /* Column-wise quantization of row segments (per-expert transposed operands).
  * Segment g is rows [row_offsets[g], row_offsets[g+1]) of x [rows][ld]; it
  * yields A_g = x[seg]^T of shape [cols][L_g], L_g = segment length, which is

@@ -17,6 +17,9 @@ Parity status per function (pins live in tests/test_oracle_*.py):
                     closed form, exact SR probabilities, SR mean error
   encode/pack       pinned: round trip of every level, canonical zero
   dequant/gemm_ref  pinned: brute-force triple loop, lossless on-grid case
+  level_stats       pinned: exact brute force (Fractions, exhaustive nearest
+                    level) on tiny inputs, SR unbiasedness, bin-asymmetry
+                    values of tests/golden/bin_bias.txt
 """
 from .ufp4 import *  # noqa: F401,F403
 from .philox import philox4x32_10, split_seed  # noqa: F401

@@ -312,7 +312,8 @@ def quantize(t_bits, along, spec, elem_base=0, row_index=None, col_index=None, K
     sample of a large operand; blocks and rotation chunks must lie inside
     the sample).  Returns a dict with 'rotated' fp32 [P, K],
     'codes' uint8 [P, K/2], 'scales' (fp32 [P, K/bc] or uint8 [P/br, K/bc] as
-    E8M0 = e + 127) and the unpacked 'code' nibbles.
+    E8M0 = e + 127), the unpacked 'code' nibbles, the clamped normalized
+    values 'v' the rounding acts on and the chosen level indices 'k'.
     """
     t = np.asarray(t_bits, dtype=np.uint16)
     A = t.T if along == 1 else t
@@ -359,7 +360,7 @@ def quantize(t_bits, along, spec, elem_base=0, row_index=None, col_index=None, K
         k = round_sr_index(m, grid, r16)
     code = encode(k, neg, grid)
     return {"rotated": y, "code": code, "codes": pack_nibbles(code), "scales": scales,
-            "P": P, "K": K}
+            "P": P, "K": K, "v": v, "k": k}
 
 
 def quantize_segmented(t_bits, offsets, spec):
@@ -372,6 +373,29 @@ def quantize_segmented(t_bits, offsets, spec):
         lo, hi = int(offsets[g]), int(offsets[g + 1])
         out.append(quantize(np.asarray(t_bits)[lo:hi], 1, spec,
                             elem_base=np.asarray(t_bits).shape[1] * lo))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Quantization diagnostics.  [UFP4] Method, Shrinkage Bias: for a level q_i
+# the mean rounding error over its bin, E[rho(t) - t | t in B_i], is what the
+# bin-asymmetry equation predicts; the Method section also speaks of the
+# bucket utilisation the RHT improves.  READING: per magnitude level index k,
+# count the elements rounded to level k and sum rint((L_k - |t|) * 2^28) over
+# them (t = the clamped normalized value, magnitudes so both signs pool;
+# integer units of 2^-28 make the sum exact and order-free).
+# ---------------------------------------------------------------------------
+def level_stats(q, grid):
+    """q: a quantize() result.  Returns int64 [16]: counts [0:8], error sums
+    in units of 2^-28 [8:16]."""
+    k = np.asarray(q["k"], dtype=np.int64).reshape(-1)
+    t = np.abs(np.asarray(q["v"], dtype=np.float32).astype(np.float64)).reshape(-1)
+    err = LEVELS[grid][k] - t                    # exact in float64
+    efx = np.rint(err * 2.0 ** 28).astype(np.int64)
+    out = np.zeros(16, dtype=np.int64)
+    out[:8] = np.bincount(k, minlength=8)
+    for lev in range(8):
+        out[8 + lev] = int(efx[k == lev].sum())
     return out
 
 

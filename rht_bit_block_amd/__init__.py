@@ -25,7 +25,8 @@ UFP4_OK, UFP4_ERR_INVALID_ARG, UFP4_ERR_SHAPE = 0, -1, -2
 UFP4_ERR_MISMATCH, UFP4_ERR_UNSUPPORTED, UFP4_ERR_HIP = -3, -4, -5
 
 EXPORTED = [
-    "ufp4_rht_quant", "ufp4_rht_quant_segmented", "ufp4_rht_quant_dual", "ufp4_dequant",
+    "ufp4_rht_quant", "ufp4_rht_quant_segmented", "ufp4_rht_quant_dual", "ufp4_quant_diag",
+    "ufp4_dequant",
     "ufp4_gemm_fprop", "ufp4_gemm_dgrad", "ufp4_gemm_wgrad",
     "ufp4_gemm_fprop_grouped", "ufp4_gemm_dgrad_grouped", "ufp4_gemm_wgrad_grouped",
     "ufp4_transpose_qtensor", "ufp4_codes_bytes", "ufp4_scales_bytes",
@@ -98,6 +99,7 @@ def _lib():
             "ufp4_rht_quant": [vp, i64, i64, i64, i32, cfgp, vp, vp, vp, vp],
             "ufp4_rht_quant_segmented": [vp, i64, i64, i64, i64p, i32, cfgp, vp, vp, vp],
             "ufp4_rht_quant_dual": [vp, i64, i64, i64, i64p, i32, cfgp, cfgp, vp, vp, vp, vp, vp],
+            "ufp4_quant_diag": [vp, i64, i64, i64, cfgp, vp, vp],
             "ufp4_dequant": [qtp, vp, i64, vp],
             "ufp4_gemm_fprop": [qtp, qtp, vp, i64, vp],
             "ufp4_gemm_dgrad": [qtp, qtp, vp, i64, vp],
@@ -180,6 +182,22 @@ def ufp4_rht_quant(x: torch.Tensor, along: int, cfg: QuantCfg, codes=None, scale
                                _ptr(codes), _ptr(scales), _ptr(rot), _stream(x))
     _check("ufp4_rht_quant", st)
     return QTensor(codes, scales, P, K, cfg), rot
+
+
+def ufp4_quant_diag(x: torch.Tensor, cfg: QuantCfg, stats=None, ld: Optional[int] = None):
+    """Level statistics of the row-wise quantization of bf16 x [rows, cols]:
+    int64 [16] on x's device -- [0:8] element counts per magnitude level index,
+    [8:16] sums of rint((L_k - |t|) * 2^28) (see the C header)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a row-major 2-D bfloat16 tensor")
+    rows, cols = x.shape
+    ld = x.stride(0) if ld is None else ld
+    if stats is None:
+        stats = torch.empty(16, dtype=torch.int64, device=x.device)
+    st = _lib().ufp4_quant_diag(_ptr(x), rows, cols, ld, ctypes.byref(cfg), _ptr(stats),
+                                _stream(x))
+    _check("ufp4_quant_diag", st)
+    return stats
 
 
 def ufp4_rht_quant_segmented(x: torch.Tensor, row_offsets: Sequence[int], cfg: QuantCfg,

@@ -262,6 +262,30 @@ int ufp4_rht_quant(const void* x, int64_t rows, int64_t cols, int64_t ld, int32_
   return hip_status(launch_quant_cols(q, (hipStream_t)stream));
 }
 
+int ufp4_quant_diag(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                    const ufp4_quant_cfg* cfg, uint64_t* stats, void* stream) {
+  if (rows < 0 || cols < 0 || (rows > 0 && ld < cols)) return UFP4_ERR_INVALID_ARG;
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if (!stats || !aligned(stats, 8)) return UFP4_ERR_INVALID_ARG;
+  if (cfg->block_rows != 1) return UFP4_ERR_UNSUPPORTED;
+  const int64_t P = rows, K = cols;
+  if (P > 0 && K > 0) {
+    if (!x) return UFP4_ERR_INVALID_ARG;
+    if (K % cfg->rht_n || K % cfg->block_cols) return UFP4_ERR_SHAPE;
+    if (!aligned(x, 16) || ld % 8) return UFP4_ERR_INVALID_ARG;
+    const int W = lane_width(cfg->rht_n, cfg->block_cols);
+    if (P * (K / W) > (int64_t)UINT32_MAX || K > (int64_t)UINT32_MAX) return UFP4_ERR_UNSUPPORTED;
+  }
+  QuantLaunch q;
+  fill_common(q, x, rows, cols, ld, cfg, nullptr, nullptr, nullptr);
+  q.P = P;
+  q.K = K;
+  // an empty operand still zeroes stats (the zeroing kernel runs first)
+  return hip_status(launch_quant_diag(q, reinterpret_cast<unsigned long long*>(stats),
+                                      (hipStream_t)stream));
+}
+
 int ufp4_rht_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ld,
                         const int64_t* row_offsets, int32_t num_segments,
                         const ufp4_quant_cfg* cfg_row, const ufp4_quant_cfg* cfg_col,

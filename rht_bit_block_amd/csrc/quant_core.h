@@ -227,10 +227,43 @@ __device__ __forceinline__ int pow2_exponent(float M) {
 // unnormalized transform x, the rotated values are c * x with c a power of
 // two, and RN(c x / s_c) = RN(x / s_x), s_c = c s_x whenever nothing
 // underflows; blocks with c * absmax < 2^-100 redo the literal computation.
-template <int W, int B, int GRID, int RND, bool FOLD>
+// Per-thread level statistics of the diagnostics kernel, in LDS: for every
+// magnitude level index k, the number of elements rounded to level k and the
+// sum over them of rint((L_k - |t|) * 2^28), t the clamped normalized value
+// the rounding acts on ([UFP4] Method, bin-asymmetry equation: the mean of
+// rho(t) - t per bin; integer sums, so the totals do not depend on order).
+struct DiagLds {
+  uint32_t cnt[8][kThreads];
+  long long sum[8][kThreads];
+};
+
+// Magnitude of level index k (0..7) in grid units.
+template <int GRID>
+__device__ __forceinline__ float level_magnitude(int k) {
+  if constexpr (GRID == 0) return 0.25f * (float)k;
+  else if constexpr (GRID == 1) return (float)k;
+  else return k < 4 ? 0.5f * (float)k : (float)((2 + (k & 1)) << ((k >> 1) - 2));
+}
+
+template <int GRID>
+__device__ __forceinline__ void diag_accumulate(DiagLds* d, uint32_t nib, float t) {
+  const int sk = ((int)(nib << 28)) >> 28;   // signed level index, in [-7, 7]
+  const int k = (sk < 0 ? -sk : sk) & 7;     // (the mask only bounds the LDS index)
+  const double err = (double)level_magnitude<GRID>(k) - (double)fabsf(t);   // exact
+  const int efx = (int)rint(err * 268435456.0);                             // |err| <= 2
+  const int tid = threadIdx.x;
+  // LDS atomic adds on the thread's own column: no contention, and unlike a
+  // read-modify-write they do not serialize consecutive elements of a lane
+  // on the LDS latency
+  atomicAdd(&d->cnt[k][tid], 1u);
+  atomicAdd(reinterpret_cast<unsigned long long*>(&d->sum[k][tid]),
+            (unsigned long long)(long long)efx);
+}
+
+template <int W, int B, int GRID, int RND, bool FOLD, bool DIAG = false>
 __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64_t e0,
                                             uint64_t seed, uint32_t stream, uint8_t* codes_out,
-                                            void* scales_out) {
+                                            void* scales_out, DiagLds* diag = nullptr) {
   constexpr float qmax = Grid<GRID>::qmax;
   constexpr int RM = RND & 1;
   constexpr bool POW2 = (RND & 2) != 0;
@@ -255,7 +288,7 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
 #pragma unroll
         for (int j = 0; j < B; ++j) v[j] = fminf(fmaxf(v[j], -qmax), qmax);
       }
-      reinterpret_cast<uint8_t*>(scales_out)[blk] = (uint8_t)(e + 127);
+      if constexpr (!DIAG) reinterpret_cast<uint8_t*>(scales_out)[blk] = (uint8_t)(e + 127);
     } else {
     float s = __fdiv_rn(M, qmax);  // s_B = RN(absmax / qmax)
     if (s == 0.0f) {
@@ -295,7 +328,7 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
         s = __fmul_rn(s, c);   // exact: power of two, no underflow
       }
     }
-    reinterpret_cast<float*>(scales_out)[blk] = s;
+    if constexpr (!DIAG) reinterpret_cast<float*>(scales_out)[blk] = s;
     }
 #pragma unroll
     for (int j = 0; j < B; ++j) {
@@ -308,9 +341,11 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
         const uint32_t r16 = (rw[idx >> 1] >> (16 * (idx & 1))) & 0xFFFFu;
         nib = sr_nibble<GRID>(vc, r16);
       }
+      if constexpr (DIAG) diag_accumulate<GRID>(diag, nib, fminf(fmaxf(v[j], -qmax), qmax));
       packed[idx >> 3] |= nib << (4 * (idx & 7));
     }
   }
+  if constexpr (DIAG) return;
 #pragma unroll
   for (int i = 0; i < W / 8; ++i) packed[i] = finish_codes<GRID>(packed[i]);
   if constexpr (W == 16) {
@@ -386,6 +421,77 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantLaunch q, FastDiv 
     const uint64_t e0 = (uint64_t)p * K + k0;
     finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, q, e0, q.codes + (e0 >> 1),
                                     scale_at<RND>(q.scales, (uint64_t)p * (K / B) + k0 / B));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Level statistics of a row-wise 1 x B quantization (diagnostics): the same
+// pipeline as k_quant_rows, each element's level index and rounding error
+// accumulated in the thread's LDS column instead of being stored; at the end
+// the workgroup sums its columns and adds them to stats[0..7] (counts) and
+// stats[8..15] (error sums) with 64-bit integer atomics.
+// ---------------------------------------------------------------------------
+template <int W, int B, int N, int GRID, int RND>
+__global__ __launch_bounds__(kThreads) void k_quant_diag(QuantLaunch q, FastDiv segs_per_row,
+                                                         uint32_t nseg,
+                                                         unsigned long long* stats) {
+  __shared__ DiagLds d;
+  constexpr int lpc = N > W ? N / W : 1;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    d.cnt[k][threadIdx.x] = 0u;
+    d.sum[k][threadIdx.x] = 0;
+  }
+  const uint32_t tid = blockIdx.x * kThreads + threadIdx.x;
+  const uint32_t stride = gridDim.x * kThreads;
+  const uint32_t qpos = tid & (uint32_t)(lpc - 1);
+  uint32_t pm[W / 2];
+  sign_masks<W>(select_pattern(q, qpos), pm);
+  const uint32_t neg1 = (qpos & 1u) ? 0x80000000u : 0u;
+  const uint32_t neg2 = (qpos & 2u) ? 0x80000000u : 0u;
+  const uint32_t K = (uint32_t)q.K;
+  for (uint32_t seg = tid; seg < nseg; seg += stride) {
+    const uint32_t p = fdiv_u32(seg, segs_per_row);
+    const uint32_t k0 = (seg - p * segs_per_row.d) * W;
+    const uint16_t* src = q.x + (int64_t)p * q.ld + k0;
+    uint32_t w[W / 2];
+#pragma unroll
+    for (int i = 0; i < W / 8; ++i) {
+      const uint4 v = ld16(reinterpret_cast<const uint4*>(src) + i);
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+    float y[W];
+    unpack<W>(w, pm, y);
+    fwht<W, N>(y, neg1, neg2);
+    const uint64_t e0 = (uint64_t)p * K + k0;
+    if constexpr (Rht<N>::fold && (RND & 2) == 0) {
+      quantize_1d<W, B, GRID, RND, true, true>(y, Rht<N>::c, e0, q.sr_seed, q.sr_stream,
+                                               nullptr, nullptr, &d);
+    } else {
+      if constexpr (N > 1) scale_by<W>(y, q.cn);
+      quantize_1d<W, B, GRID, RND, false, true>(y, 1.0f, e0, q.sr_seed, q.sr_stream, nullptr,
+                                                nullptr, &d);
+    }
+  }
+  __syncthreads();
+  // thread t sums level t / 32 over the columns t % 32 + 32 i, then the 32
+  // threads of that level (one half of a wave) reduce by butterflies
+  const int lev = threadIdx.x >> 5, part = threadIdx.x & 31;
+  unsigned long long c = 0;
+  long long sm = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 32; ++i) {
+    c += d.cnt[lev][part + 32 * i];
+    sm += d.sum[lev][part + 32 * i];
+  }
+#pragma unroll
+  for (int off = 16; off > 0; off >>= 1) {
+    c += __shfl_xor(c, off);
+    sm += __shfl_xor(sm, off);
+  }
+  if (part == 0) {
+    atomicAdd(stats + lev, c);
+    atomicAdd(stats + 8 + lev, (unsigned long long)sm);
   }
 }
 
@@ -701,6 +807,49 @@ hipError_t run_rows(const QuantLaunch& q, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int G>
+__global__ void k_diag_zero(unsigned long long* stats) {
+  if (threadIdx.x < 16) stats[threadIdx.x] = 0ull;
+}
+
+template <int W, int B, int N, int G, int R>
+hipError_t run_diag(const QuantLaunch& q, unsigned long long* stats, hipStream_t s) {
+  hipLaunchKernelGGL(k_diag_zero<G>, dim3(1), dim3(64), 0, s, stats);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint32_t segs_per_row = (uint32_t)(q.K / W);
+  const uint64_t nseg = (uint64_t)q.P * segs_per_row;
+  if (nseg == 0) return hipSuccess;
+  const uint64_t blocks_needed = (nseg + kThreads - 1) / kThreads;
+  const uint64_t cap = (uint64_t)device_grid_limit() * 8;
+  const uint32_t blocks = (uint32_t)(blocks_needed < cap ? blocks_needed : cap);
+  hipLaunchKernelGGL((k_quant_diag<W, B, N, G, R>), dim3(blocks), dim3(kThreads), 0, s, q,
+                     make_fastdiv(segs_per_row), (uint32_t)nseg, stats);
+  return hipGetLastError();
+}
+
+template <int G>
+hipError_t run_diag_1d(const QuantLaunch& q, unsigned long long* stats, hipStream_t s) {
+#define UFP4_RUN(B_, N_)                                                       \
+  if (q.bc == B_ && q.n == N_) {                                              \
+    constexpr int W_ = (B_ == 32 || N_ >= 32) ? 32 : 16;                      \
+    if (B_ == 32 && q.scale_mode == 1) {                                       \
+      if (q.rounding == 0) return run_diag<W_, B_, N_, G, 2>(q, stats, s);     \
+      return run_diag<W_, B_, N_, G, 3>(q, stats, s);                          \
+    }                                                                          \
+    if (q.rounding == 0) return run_diag<W_, B_, N_, G, 0>(q, stats, s);       \
+    return run_diag<W_, B_, N_, G, 1>(q, stats, s);                            \
+  }
+#define UFP4_RUN_B(B_) \
+  UFP4_RUN(B_, 1) UFP4_RUN(B_, 2) UFP4_RUN(B_, 4) UFP4_RUN(B_, 8) UFP4_RUN(B_, 16) \
+  UFP4_RUN(B_, 32) UFP4_RUN(B_, 64) UFP4_RUN(B_, 128)
+  UFP4_RUN_B(16)
+  UFP4_RUN_B(32)
+#undef UFP4_RUN_B
+#undef UFP4_RUN
+  return hipErrorInvalidValue;
+}
+
 template <int W, int B, int N, int G, int R>
 hipError_t run_cols(const QuantLaunch& q, hipStream_t s) {
   const int total = q.tile_start[q.nseg];
@@ -796,5 +945,7 @@ template <int G> hipError_t quant_rows_grid(const QuantLaunch& q, hipStream_t s)
 template <int G> hipError_t quant_cols_grid(const QuantLaunch& q, hipStream_t s);
 template <int G> hipError_t quant_rows_2d_grid(const QuantLaunch& q, hipStream_t s);
 template <int G> hipError_t quant_dual_grid(const QuantLaunch& q, const RowSide& r, hipStream_t s);
+template <int G> hipError_t quant_diag_grid(const QuantLaunch& q, unsigned long long* stats,
+                                           hipStream_t s);
 
 }  // namespace ufp4

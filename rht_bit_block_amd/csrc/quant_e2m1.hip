@@ -21,4 +21,9 @@ hipError_t quant_dual_grid<2>(const QuantLaunch& q, const RowSide& r, hipStream_
   return qk::run_dual_1d<2>(q, r, s);
 }
 
+template <>
+hipError_t quant_diag_grid<2>(const QuantLaunch& q, unsigned long long* stats, hipStream_t s) {
+  return qk::run_diag_1d<2>(q, stats, s);
+}
+
 }  // namespace ufp4

@@ -21,4 +21,9 @@ hipError_t quant_dual_grid<1>(const QuantLaunch& q, const RowSide& r, hipStream_
   return qk::run_dual_1d<1>(q, r, s);
 }
 
+template <>
+hipError_t quant_diag_grid<1>(const QuantLaunch& q, unsigned long long* stats, hipStream_t s) {
+  return qk::run_diag_1d<1>(q, stats, s);
+}
+
 }  // namespace ufp4

@@ -80,6 +80,7 @@ struct RowSide {
 
 hipError_t launch_quant_rows(const QuantLaunch& q, hipStream_t s);
 hipError_t launch_quant_dual(const QuantLaunch& q, const RowSide& r, hipStream_t s);
+hipError_t launch_quant_diag(const QuantLaunch& q, unsigned long long* stats, hipStream_t s);
 hipError_t launch_quant_cols(const QuantLaunch& q, hipStream_t s);
 hipError_t launch_quant_rows_2d(const QuantLaunch& q, hipStream_t s);
 

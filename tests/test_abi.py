@@ -183,3 +183,30 @@ def test_dual_quant_argument_errors():
                        block_cols=32, rht_n=1)
     assert _dual(lib, cfg_r=two_d, cfg_c=two_d) == E.UFP4_ERR_UNSUPPORTED
     assert _dual(lib, rows=0) == E.UFP4_OK
+
+
+def _diag(lib, x=FAKE, rows=64, cols=64, ld=64, cfg=None, stats=FAKE):
+    c = cfg or U.make_cfg()
+    return lib.ufp4_quant_diag(ctypes.c_void_p(x), rows, cols, ld, ctypes.byref(c),
+                               ctypes.c_void_p(stats), None)
+
+
+def test_diag_argument_errors():
+    """Every call here fails validation (a valid call launches a kernel even
+    for an empty operand, since it zeroes stats)."""
+    lib = U.lib_handle()
+    E = U
+    assert _diag(lib, stats=0) == E.UFP4_ERR_INVALID_ARG
+    assert _diag(lib, stats=FAKE + 4) == E.UFP4_ERR_INVALID_ARG     # 8-byte alignment
+    assert _diag(lib, rows=0, stats=0) == E.UFP4_ERR_INVALID_ARG
+    assert _diag(lib, x=0) == E.UFP4_ERR_INVALID_ARG
+    assert _diag(lib, x=FAKE + 2) == E.UFP4_ERR_INVALID_ARG
+    assert _diag(lib, rows=-1) == E.UFP4_ERR_INVALID_ARG
+    assert _diag(lib, ld=32) == E.UFP4_ERR_INVALID_ARG
+    assert _diag(lib, ld=68) == E.UFP4_ERR_INVALID_ARG              # ld % 8
+    assert _diag(lib, cols=40, ld=48) == E.UFP4_ERR_SHAPE            # K % 16
+    assert _diag(lib, cfg=U.make_cfg(rht_n=24)) == E.UFP4_ERR_SHAPE
+    two_d = U.make_cfg(grid=U.UFP4_E2M1, scale_mode=U.UFP4_SCALE_POW2, block_rows=32,
+                       block_cols=32, rht_n=1)
+    assert _diag(lib, cfg=two_d) == E.UFP4_ERR_UNSUPPORTED
+    assert _diag(lib, cfg=U.make_cfg(scale_mode=U.UFP4_SCALE_POW2, block_cols=16)) == E.UFP4_ERR_UNSUPPORTED

@@ -113,6 +113,34 @@ def test_config2_dense_layer(grid):
     assert_gemm(dW, rN, rK, deq(odyt, c_dyc), deq(oxt, c_xc), "wgrad")
 
 
+@pytest.mark.parametrize("grid", [U.UFP4_E1M2, U.UFP4_E2M1])
+@pytest.mark.parametrize("n", [1, 16])
+def test_config2_diag(grid, n):
+    """Level statistics of config 2's X at full size: counts cover every
+    element and equal the level histogram of the quantizer's own codes; a
+    64-row slice quantized as its own operand matches the oracle exactly."""
+    _case("config2 diag", grid, n)
+    wl = workloads.config2("cuda")
+    X = wl.tensors["X"]
+    M, K = X.shape
+    cfg = U.make_cfg(grid, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 16, n, sign_seed=wl.meta["sign_seeds"][0])
+    st = U.ufp4_quant_diag(X, cfg).cpu().numpy()
+    assert st[:8].sum() == M * K
+    q, _ = U.ufp4_rht_quant(X, 0, cfg)
+    codes = q.codes
+    nib = torch.stack([codes & 15, codes >> 4], dim=-1).reshape(-1).long()
+    if grid == U.UFP4_INT4:
+        mag = torch.where(nib >= 8, 16 - nib, nib)
+    else:
+        mag = nib & 7
+    assert np.array_equal(torch.bincount(mag, minlength=8).cpu().numpy(), st[:8])
+    r0 = int(pick(M // 64, 1, 7)[0]) * 64
+    Xs = X[r0:r0 + 64].contiguous()
+    got = U.ufp4_quant_diag(Xs, cfg).cpu().numpy()
+    want = O.level_stats(O.quantize(host_bits(Xs), 0, spec_of(cfg)), grid)
+    assert np.array_equal(got, want)
+
+
 # ---------------------------------------------------------------------------
 def _seg_codes(q, C, off, g, L, p_idx):
     """Rows p_idx of segment g of a segmented column-wise quantization."""

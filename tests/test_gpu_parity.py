@@ -169,6 +169,38 @@ def test_gemm_2d_and_transpose(grid):
     assert O.rel_fro(dX, O.gemm_ref(oracle_dequant64(rdy, cfg), dw.T)) <= GEMM_TOL
 
 
+DIAG_CASES = [(1, 16, U.UFP4_SCALE_F32), (16, 16, U.UFP4_SCALE_F32), (32, 32, U.UFP4_SCALE_F32),
+              (128, 16, U.UFP4_SCALE_F32), (32, 32, U.UFP4_SCALE_POW2), (1, 32, U.UFP4_SCALE_POW2)]
+
+
+@pytest.mark.parametrize("n,b,smode", DIAG_CASES)
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("rnd", [U.UFP4_RTNE, U.UFP4_SR])
+def test_quant_diag(n, b, smode, grid, rnd):
+    """Level statistics (counts and exact error sums per level) equal the
+    oracle's on several grid-stride waves plus a ragged row count."""
+    _print_case("diag", n, b, smode, grid, rnd)
+    bits = rand_bits(72, 512, seed=n + b + 5 * grid + rnd)
+    cfg = U.make_cfg(grid, rnd, smode, 1, b, n, sign_seed=300 + n, sr_seed=91, sr_stream=2)
+    got = U.ufp4_quant_diag(dev_bf16(bits), cfg).cpu().numpy()
+    want = O.level_stats(O.quantize(bits, 0, spec_of(cfg)), grid)
+    assert np.array_equal(got, want), (got, want)
+
+
+def test_quant_diag_empty_and_reuse():
+    """An empty operand yields zeros (the buffer is overwritten, not
+    accumulated), and a second call on the same buffer starts from zero."""
+    cfg = U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=1)
+    stats = torch.full((16,), 7, dtype=torch.int64, device="cuda")
+    U.ufp4_quant_diag(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), cfg, stats=stats)
+    assert torch.count_nonzero(stats).item() == 0
+    bits = rand_bits(16, 256, seed=5)
+    for _ in range(2):
+        U.ufp4_quant_diag(dev_bf16(bits), cfg, stats=stats)
+        want = O.level_stats(O.quantize(bits, 0, spec_of(cfg)), U.UFP4_E1M2)
+        assert np.array_equal(stats.cpu().numpy(), want)
+
+
 @pytest.mark.parametrize("P,K", [(32, 32), (288, 544), (1056, 800), (4096, 4096)])
 def test_transpose_shapes(P, K):
     """The square-block transpose on tile-ragged shapes and a full-size

@@ -485,3 +485,93 @@ def test_golden_pow2_scale_exponents():
     for g, m, e in _golden_rows("pow2_scale.txt"):
         got = O.scale_pow2_exponent(np.array([float(m)], dtype=np.float32), GRID_NAMES[g])
         assert int(got[0]) == int(e), (g, m)
+
+
+# ---------------------------------------------------------------------------
+# Quantization diagnostics (level statistics).  [UFP4] Method: bin-asymmetry
+# equation and bucket utilisation.
+# ---------------------------------------------------------------------------
+def _pow2_scale_blocks(grid, P, K, seed, j=0):
+    """bf16 bits whose 1 x 16 blocks each hold q_max * 2^j as their largest
+    magnitude, so s = 2^j exactly and t = y / 2^j."""
+    rng = np.random.default_rng(seed)
+    qmax = O.QMAX[grid]
+    x = rng.uniform(-qmax, qmax, (P, K)) * 2.0 ** j
+    x[:, ::16] = qmax * 2.0 ** j * np.where(rng.random((P, K // 16)) < 0.5, -1.0, 1.0)
+    return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _brute_stats(bits, grid, rounding, j, spec):
+    """Exact rationals: t = y / 2^j, level by exhaustive nearest search (ties
+    to the even index) or k_lo + [r16 < f 2^16], error rounded half-even."""
+    L = [Fraction(float(v)) for v in O.LEVELS[grid]]
+    P, K = bits.shape
+    y = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    r16 = O.sr_draws(spec.sr_seed, spec.sr_stream, np.arange(P * K, dtype=np.uint64)).reshape(P, K)
+    cnt, tot = [0] * 8, [0] * 8
+    for p in range(P):
+        for k in range(K):
+            t = abs(Fraction(float(y[p, k])) / Fraction(2) ** j)
+            if rounding == O.RTNE:
+                d = [abs(t - lv) for lv in L]
+                best = min(d)
+                cand = [i for i in range(8) if d[i] == best]
+                idx = next((i for i in cand if i % 2 == 0), cand[0])
+            else:
+                lo = max(i for i in range(8) if L[i] <= t)
+                if lo == 7:
+                    idx = 7
+                else:
+                    f = (t - L[lo]) / (L[lo + 1] - L[lo])
+                    idx = lo + (1 if int(r16[p, k]) < f * 65536 else 0)
+            cnt[idx] += 1
+            tot[idx] += round((L[idx] - t) * 2 ** 28)
+    return np.array(cnt + tot, dtype=np.int64)
+
+
+@pytest.mark.parametrize("grid", [O.E1M2, O.INT4, O.E2M1])
+@pytest.mark.parametrize("rounding", [O.RTNE, O.SR])
+def test_level_stats_brute_force(grid, rounding):
+    spec = O.QuantSpec(grid, rounding, O.SCALE_F32, 1, 16, 1, 0, 4242, 3)
+    for j in (0, -5):
+        bits = _pow2_scale_blocks(grid, 6, 64, seed=11 + grid + 3 * rounding - j, j=j)
+        q = O.quantize(bits, 0, spec)
+        assert np.array_equal(O.level_stats(q, grid), _brute_stats(bits, grid, rounding, j, spec))
+
+
+@pytest.mark.parametrize("grid", [O.E1M2, O.INT4, O.E2M1])
+def test_level_stats_sr_unbiased(grid):
+    """[2DFP4] SR equation E[roundS(x)] = x: the pooled error mean vanishes."""
+    t = _tensor_bits(128, 1024, 9)
+    st = O.level_stats(O.quantize(t, 0, O.QuantSpec(grid, O.SR, O.SCALE_F32, 1, 16, 16, 3, 77, 1)), grid)
+    n = st[:8].sum()
+    assert n == t.size
+    gap = float(np.max(np.diff(O.LEVELS[grid])))
+    mean = st[8:].sum() * 2.0 ** -28 / n
+    assert abs(mean) < 5 * gap / np.sqrt(n)
+
+
+def test_level_stats_match_bin_asymmetry_values():
+    """RTNE on a uniform spread of t (s = 1 blocks): each interior level's
+    mean error is the worked value of tests/golden/bin_bias.txt, up to the
+    spacing h of the spread."""
+    rows = _golden_rows("bin_bias.txt")
+    for gname, grid in GRID_NAMES.items():
+        qmax = O.QMAX[grid]
+        h = 2.0 ** -7 if grid == O.E1M2 else 2.0 ** -5
+        vals = np.arange(0.0, qmax, h)
+        n_blk = -(-vals.size // 15)
+        x = np.zeros((n_blk, 16))
+        flat = np.concatenate([vals, np.zeros(n_blk * 15 - vals.size)])
+        x[:, 1:] = flat.reshape(n_blk, 15)
+        x[:, 0] = qmax                                  # block max: s = 1
+        bits = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy(), x)
+        st = O.level_stats(O.quantize(bits, 0, O.QuantSpec(grid, O.RTNE, O.SCALE_F32, 1, 16, 1)), grid)
+        L = list(O.LEVELS[grid])
+        for g, q, b in rows:
+            if g != gname:
+                continue
+            i = L.index(float(q))
+            mean = st[8 + i] * 2.0 ** -28 / st[i]
+            assert abs(mean - float(b)) <= h, (gname, q, mean)
