@@ -16,6 +16,8 @@ Parity status per function (pins live in tests/test_oracle_*.py):
   round_*           pinned: rint-based and frexp-based reformulations, bin-bias
                     closed form, exact SR probabilities, SR mean error
   encode/pack       pinned: round trip of every level, canonical zero
+  E4M3 (MXFP8)      pinned: level set and RNE rounding equal torch's
+                    float8_e4m3fn, error bound, lossless on-grid values
   dequant/gemm_ref  pinned: brute-force triple loop, lossless on-grid case
   level_stats       pinned: exact brute force (Fractions, exhaustive nearest
                     level) on tiny inputs, SR unbiasedness, bin-asymmetry

@@ -35,7 +35,7 @@ from .philox import philox4x32_10, split_seed
 # its levels are k/4), INT4 = {-7..7} (symmetric, -8 unused), E2M1 = the
 # OCP-MX FP4 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}.
 # ---------------------------------------------------------------------------
-E1M2, INT4, E2M1 = 0, 1, 2
+E1M2, INT4, E2M1, E4M3 = 0, 1, 2, 3
 RTNE, SR = 0, 1
 SCALE_F32, SCALE_POW2 = 0, 1
 SIGN_STREAM = 0xFFFFFFFF  # Philox counter word reserved for the sign draw
@@ -45,7 +45,26 @@ LEVELS = {
     INT4: np.arange(8, dtype=np.float64),
     E2M1: np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]),
 }
+
+
+def _e4m3_magnitudes():
+    """OCP FP8 E4M3 (the MXFP8 element format): bit pattern b = 8 e + m with
+    e = 0 subnormal (m/8 * 2^-6), else (1 + m/8) * 2^(e - 7); pattern 0x7F is
+    NaN, so 127 finite magnitudes, 0 .. 448, ascending in b."""
+    out = []
+    for b in range(127):
+        e, m = b >> 3, b & 7
+        out.append(m / 8.0 * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(out)
+
+
+# [2DFP4] mixed-precision section: the Query/Key projections keep MXFP8 (E4M3
+# elements, power-of-two scale per 1 x 32 block).  READING: the level set is
+# every finite E4M3 magnitude and the scale follows the same truncation-free
+# power-of-two rule with q_max = 448; ties go to the even pattern (IEEE RNE).
+LEVELS[E4M3] = _e4m3_magnitudes()
 QMAX = {g: float(LEVELS[g][-1]) for g in LEVELS}
+SIGN_BIT = {E1M2: 8, INT4: 8, E2M1: 8, E4M3: 128}
 
 
 @dataclass(frozen=True)
@@ -268,7 +287,7 @@ def encode(k, neg, grid):
     neg = np.asarray(neg, dtype=bool) & (k > 0)
     if grid == INT4:
         return np.where(neg, (-k) & 0xF, k).astype(np.uint8)
-    return (np.where(neg, 8, 0) + k).astype(np.uint8)
+    return (np.where(neg, SIGN_BIT[grid], 0) + k).astype(np.uint8)
 
 
 def decode_index(code, grid):
@@ -277,7 +296,19 @@ def decode_index(code, grid):
     if grid == INT4:
         sv = np.where(c >= 8, c - 16, c)
         return np.abs(sv), sv < 0
-    return c & 7, (c & 8) != 0
+    sb = SIGN_BIT[grid]
+    return c & (sb - 1), (c & sb) != 0
+
+
+def code_bytes(code, grid):
+    """Stored codes: 4-bit codes two per byte, E4M3 codes one per byte."""
+    return np.asarray(code, dtype=np.uint8) if grid == E4M3 else pack_nibbles(code)
+
+
+def code_values(codes, grid, P, K):
+    """Inverse of code_bytes: the per-element codes [P, K]."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return c.reshape(P, K) if grid == E4M3 else unpack_nibbles(c.reshape(P, K // 2))
 
 
 def pack_nibbles(codes):
@@ -359,7 +390,7 @@ def quantize(t_bits, along, spec, elem_base=0, row_index=None, col_index=None, K
         r16 = sr_draws(spec.sr_seed, spec.sr_stream, e_idx)
         k = round_sr_index(m, grid, r16)
     code = encode(k, neg, grid)
-    return {"rotated": y, "code": code, "codes": pack_nibbles(code), "scales": scales,
+    return {"rotated": y, "code": code, "codes": code_bytes(code, grid), "scales": scales,
             "P": P, "K": K, "v": v, "k": k}
 
 
@@ -420,7 +451,7 @@ def scale_per_element(scales, spec, P, K):
 
 def dequant(codes_packed, scales, spec, P, K):
     """Returns (fp32 RN(level * s), exact float64 level * s)."""
-    code = unpack_nibbles(np.asarray(codes_packed).reshape(P, K // 2))
+    code = code_values(codes_packed, spec.grid, P, K)
     lv = level_values(code, spec.grid)                       # exact
     s = scale_per_element(scales, spec, P, K)               # exact fp32 values
     exact = lv * s                                          # <= 27 significant bits

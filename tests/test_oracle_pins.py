@@ -171,8 +171,8 @@ def test_f32_scale_within_one_ulp():
 def test_pow2_exponent_brackets_block_max_exactly():
     rng = np.random.default_rng(2)
     M = np.concatenate([np.abs(rng.standard_normal(500)) * 10.0 ** rng.integers(-30, 30, 500),
-                        [6.0, 1.75, 7.0, 12.0, 3.5, 0.0, 1e-40]]).astype(np.float32)
-    for g in (O.E1M2, O.INT4, O.E2M1):
+                        [6.0, 1.75, 7.0, 12.0, 3.5, 448.0, 896.0, 0.0, 1e-40]]).astype(np.float32)
+    for g in (O.E1M2, O.INT4, O.E2M1, O.E4M3):
         e = O.scale_pow2_exponent(M, g)
         assert np.array_equal(e, O.scale_pow2_exponent_exact(M, g))
         q = Fraction(O.QMAX[g]).limit_denominator(8)
@@ -575,3 +575,62 @@ def test_level_stats_match_bin_asymmetry_values():
             i = L.index(float(q))
             mean = st[8 + i] * 2.0 ** -28 / st[i]
             assert abs(mean - float(b)) <= h, (gname, q, mean)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 (E4M3 elements, 1 x 32 power-of-two scales).  [2DFP4] mixed-precision
+# section: Query/Key projections stay in MXFP8.  The format itself is pinned
+# to torch's float8_e4m3fn (an independent implementation of OCP E4M3).
+# ---------------------------------------------------------------------------
+def test_e4m3_levels_are_torch_e4m3fn():
+    codes = torch.arange(127, dtype=torch.uint8)
+    want = codes.view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(O.LEVELS[O.E4M3], want)
+    assert O.QMAX[O.E4M3] == 448.0
+
+
+def test_e4m3_rtne_matches_torch_cast():
+    rng = np.random.default_rng(12)
+    v = np.concatenate([rng.uniform(-448, 448, 20000), rng.uniform(-0.02, 0.02, 20000),
+                        [0.0, 448.0, -448.0, 1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10]])
+    v = v.astype(np.float32)
+    k = O.round_rtne_index(np.abs(v).astype(np.float64), O.E4M3)
+    got = O.encode(k, v < 0, O.E4M3)
+    want = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    want = np.where(want == 0x80, 0, want)          # canonical zero (no -0)
+    assert np.array_equal(got, want)
+
+
+def test_mxfp8_quantize_dequant_bound():
+    """Power-of-two 1 x 32 blocks: every |v| <= 448 and the dequantized value
+    is within half an E4M3 spacing of y (relative 2^-4, or 2^-10 * 2^e in the
+    subnormal range)."""
+    t = _tensor_bits(64, 256, 21, scale=3.0)
+    spec = O.QuantSpec(O.E4M3, O.RTNE, O.SCALE_POW2, 1, 32, 1)
+    q = O.quantize(t, 0, spec)
+    assert q["codes"].shape == (64, 256) and q["codes"].dtype == np.uint8
+    e = q["scales"].astype(np.int64) - 127
+    y = O.bf16_bits_to_f32(t).astype(np.float64)
+    d = O.dequant(q["codes"], q["scales"], spec, 64, 256)[1]
+    s = np.repeat(np.exp2(e.astype(np.float64)), 32, axis=1)
+    bound = np.maximum(np.abs(y) * 2.0 ** -4, s * 2.0 ** -10)
+    assert np.all(np.abs(d - y) <= bound)
+    M = np.abs(y).reshape(64, 8, 32).max(axis=2)
+    assert np.all(M <= 448.0 * np.exp2(e.astype(np.float64)))
+    assert np.all((M == 0) | (M > 448.0 * np.exp2(e.astype(np.float64) - 1)) | (e == -127))
+
+
+def test_mxfp8_lossless_on_grid():
+    """Values already on the scaled E4M3 grid come back exactly."""
+    rng = np.random.default_rng(5)
+    L = O.LEVELS[O.E4M3]
+    k = rng.integers(0, 127, (16, 64))
+    k[:, ::32] = 126                                  # block max 448: e = 0
+    sign = np.where(rng.random((16, 64)) < 0.5, -1.0, 1.0)
+    y = (sign * L[k]).astype(np.float32)
+    bits = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.bf16_bits_to_f32(bits), y)         # E4M3 values are bf16 values
+    spec = O.QuantSpec(O.E4M3, O.RTNE, O.SCALE_POW2, 1, 32, 1)
+    q = O.quantize(bits, 0, spec)
+    assert np.all(q["scales"] == 127)
+    assert np.array_equal(O.dequant(q["codes"], q["scales"], spec, 16, 64)[1], y.astype(np.float64))
