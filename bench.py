@@ -183,7 +183,8 @@ def mx_gemms(U, torch, reps=10):
     cores, each timed over back-to-back launches (context; not part of the
     step): the square-block layer M=16384 K=4096 N=4096 (32 x 32 E8M0 blocks,
     W quantized once and reused transposed, SR, no rotation) with E2M1 and
-    E1M2 codes, and FPROP of the dense layer with 1 x 32 E8M0 blocks."""
+    E1M2 codes, FPROP of the dense layer with 1 x 32 E8M0 blocks, and the
+    dense layer in MXFP8 (E4M3 elements): its FPROP and X's quantization."""
     import workloads
     out = {}
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -252,6 +253,25 @@ def mx_gemms(U, torch, reps=10):
         peak = FP4_PEAK_TFLOPS if grid == U.UFP4_E2M1 else FP8_PEAK_TFLOPS
         out[f"dense_1x32_e8m0_{M2}x{K2}x{N2}_{gname}_fprop"] = {
             "ms": round(ms, 4), "TFLOP/s": round(tf, 1), "peak": peak, "frac": round(tf / peak, 4)}
+    # MXFP8 (E4M3, 1 x 32 E8M0): the dense layer's FPROP and X's quantization
+    cfg = U.make_cfg(U.UFP4_E4M3, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 1)
+    qx, _ = U.ufp4_rht_quant(X2, 0, cfg)
+    qw, _ = U.ufp4_rht_quant(W2, 0, cfg)
+    c = torch.empty((M2, N2), dtype=torch.float32, device="cuda")
+    ms = timed(lib.ufp4_gemm_fprop, qx, qw, c)
+    tf = 2.0 * M2 * N2 * K2 / ms / 1e9
+    out[f"mxfp8_{M2}x{K2}x{N2}_fprop"] = {
+        "ms": round(ms, 4), "TFLOP/s": round(tf, 1), "peak": FP8_PEAK_TFLOPS,
+        "frac": round(tf / FP8_PEAK_TFLOPS, 4),
+        "mfma": "v_mfma_scale_f32_32x32x64_f8f6f4 (FP8 E4M3)"}
+    qargs = (ctypes.c_void_p(X2.data_ptr()), M2, K2, K2, 0, ctypes.byref(cfg),
+             ctypes.c_void_p(qx.codes.data_ptr()), ctypes.c_void_p(qx.scales.data_ptr()), None,
+             stream)
+    ms = timed_args(lib.ufp4_rht_quant, qargs)
+    nbytes = M2 * K2 * (2 + 1 + 1 / 32)
+    out[f"mxfp8_quant_rows_{M2}x{K2}"] = {"ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
+                                          "frac_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBPS, 4),
+                                          "bytes_per_elem": round(2 + 1 + 1 / 32, 4)}
     return out
 
 

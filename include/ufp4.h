@@ -44,8 +44,15 @@ extern "C" {
 
 /* Codebooks G ([UFP4] formats section; uniform grids in Method):
  * E1M2 levels {0, +-0.25, ..., +-1.75}, INT4 {-7..7},
- * E2M1 {0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6}. */
-enum { UFP4_E1M2 = 0, UFP4_INT4 = 1, UFP4_E2M1 = 2 };
+ * E2M1 {0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6}.
+ * E4M3 is the MXFP8 element format ([2DFP4] mixed-precision section keeps
+ * the Query/Key projections in MXFP8): every finite OCP FP8 E4M3 value
+ * (|v| <= 448), one byte per code (the OCP bit pattern, zero as 0x00), only
+ * with 1 x 32 power-of-two scales and RTNE (ties to the even pattern); its
+ * codes take P*K bytes (ufp4_codes_bytes covers the 4-bit codebooks).  Its
+ * quantizations are row- or column-wise (ufp4_rht_quant) and its GEMMs dense
+ * with K % 128 == 0; other entry points return UFP4_ERR_UNSUPPORTED. */
+enum { UFP4_E1M2 = 0, UFP4_INT4 = 1, UFP4_E2M1 = 2, UFP4_E4M3 = 3 };
 /* Rounding ([UFP4] formats section; [2DFP4] 2D section, E[roundS(x)] = x). */
 enum { UFP4_RTNE = 0, UFP4_SR = 1 };
 /* Scale rule: s_B = absmax / qmax in fp32 ([UFP4] formats section), or the
@@ -101,14 +108,14 @@ typedef struct ufp4_qtensor {
   ufp4_quant_cfg cfg;
 } ufp4_qtensor;
 
-/* Fused RHT + blockwise 4-bit quantization of a bf16 matrix.
+/* Fused RHT + blockwise 4-bit (or MXFP8) quantization of a bf16 matrix.
  * [UFP4] formats section (block absmax scale, RTNE / SR onto G) and Method
  * (X H'_n with H'_n = S_n H_n along the shared GEMM dimension).
  *   x        : bf16 [rows][ld] row-major, ld >= cols.
  *   along    : 0 -> A = x (P = rows, K = cols), row-wise;
  *              1 -> A = x^T (P = cols, K = rows), column-wise: the output is
  *                   the transposed operand, written K-contiguous.
- *   codes    : uint8 [P][K/2];  scales : see the layout above.
+ *   codes    : uint8 [P][K/2] ([P][K] for E4M3);  scales : see the layout above.
  *   rotated  : optional fp32 [P][K] copy of the rotated values y = RN(c_n *
  *              FWHT(S x)) (NULL to skip; not part of the fast path).
  * The rotation is block-diagonal along K in chunks of rht_n; each chunk and
@@ -154,7 +161,10 @@ int ufp4_rht_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ld,
  * counts are the bucket utilisation the Method section attributes to the RHT.
  * The sums are exact integers, so the result does not depend on launch order.
  * stats: DEVICE uint64 [16], 8-byte aligned, overwritten.  cfg must be 1D
- * (block_rows == 1); shapes and errors as ufp4_rht_quant. */
+ * (block_rows == 1) with a 4-bit codebook; shapes and errors as
+ * ufp4_rht_quant.  The workgroups' partial sums go through a small array
+ * the library keeps on each GPU, so diagnostics calls that overlap on one GPU
+ * (different streams) race; calls on one stream are ordered. */
 int ufp4_quant_diag(const void* x, int64_t rows, int64_t cols, int64_t ld,
                     const ufp4_quant_cfg* cfg, uint64_t* stats, void* stream);
 

@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librht_ufp4.so")
 
-UFP4_E1M2, UFP4_INT4, UFP4_E2M1 = 0, 1, 2
+UFP4_E1M2, UFP4_INT4, UFP4_E2M1, UFP4_E4M3 = 0, 1, 2, 3
 UFP4_RTNE, UFP4_SR = 0, 1
 UFP4_SCALE_F32, UFP4_SCALE_POW2 = 0, 1
 UFP4_OK, UFP4_ERR_INVALID_ARG, UFP4_ERR_SHAPE = 0, -1, -2
@@ -149,6 +149,11 @@ def _i64arr(vals: Sequence[int]):
     return arr
 
 
+def codes_shape(P, K, cfg):
+    """4-bit codes two per byte; E4M3 (MXFP8) codes one per byte."""
+    return (P, K) if cfg.grid == UFP4_E4M3 else (P, K // 2)
+
+
 def scales_shape(P, K, cfg):
     return (P // cfg.block_rows, K // cfg.block_cols)
 
@@ -173,7 +178,7 @@ def ufp4_rht_quant(x: torch.Tensor, along: int, cfg: QuantCfg, codes=None, scale
     P, K = (cols, rows) if along else (rows, cols)
     dev = x.device
     if codes is None:
-        codes = torch.empty((P, K // 2), dtype=torch.uint8, device=dev)
+        codes = torch.empty(codes_shape(P, K, cfg), dtype=torch.uint8, device=dev)
     if scales is None:
         scales = torch.empty(scales_shape(P, K, cfg), dtype=scales_dtype(cfg), device=dev)
     rot = torch.empty((P, K), dtype=torch.float32, device=dev) if rotated is True else (

@@ -23,7 +23,7 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 int check_cfg(const ufp4_quant_cfg* c) {
   if (!c) return UFP4_ERR_INVALID_ARG;
-  if (c->grid < 0 || c->grid > 2 || c->rounding < 0 || c->rounding > 1 || c->scale_mode < 0 ||
+  if (c->grid < 0 || c->grid > 3 || c->rounding < 0 || c->rounding > 1 || c->scale_mode < 0 ||
       c->scale_mode > 1 || c->reserved != 0)
     return UFP4_ERR_INVALID_ARG;
   if (!is_pow2(c->rht_n) || c->rht_n > 128) return UFP4_ERR_SHAPE;
@@ -34,6 +34,10 @@ int check_cfg(const ufp4_quant_cfg* c) {
   // 1D power-of-two scales only for the MX block shape 1 x 32
   if (one_d && c->scale_mode != UFP4_SCALE_F32 && c->block_cols != 32) return UFP4_ERR_UNSUPPORTED;
   if (two_d && (c->scale_mode != UFP4_SCALE_POW2 || c->rht_n > 32)) return UFP4_ERR_UNSUPPORTED;
+  // MXFP8 (E4M3 elements): 1 x 32 power-of-two blocks, round to nearest even
+  if (c->grid == UFP4_E4M3 && (!one_d || c->block_cols != 32 || c->scale_mode != UFP4_SCALE_POW2 ||
+                               c->rounding != UFP4_RTNE))
+    return UFP4_ERR_UNSUPPORTED;
   return UFP4_OK;
 }
 
@@ -150,9 +154,10 @@ int gemm_dense(const ufp4_qtensor* A, const ufp4_qtensor* B, float* C, int64_t l
   g.tile_start[0] = 0;
   g.tile_start[1] = (int32_t)tiles;
   g.total_tiles = (int32_t)tiles;
-  if (gemm_mx_supported(g) && aligned(g.a_scales, 4) && aligned(g.b_scales, 4) &&
-      aligned(g.a_codes, 16) && aligned(g.b_codes, 16))
-    return hip_status(launch_gemm_mx(g, (hipStream_t)stream));
+  const bool mx = gemm_mx_supported(g) && aligned(g.a_scales, 4) && aligned(g.b_scales, 4) &&
+                  aligned(g.a_codes, 16) && aligned(g.b_codes, 16);
+  if (mx) return hip_status(launch_gemm_mx(g, (hipStream_t)stream));
+  if (g.grid == UFP4_E4M3) return UFP4_ERR_UNSUPPORTED;   // MXFP8 runs on the scaled MFMA only
   return hip_status(launch_gemm(g, (hipStream_t)stream));
 }
 
@@ -171,6 +176,7 @@ int gemm_grouped_rows(const ufp4_qtensor* A, const ufp4_qtensor* B, int32_t G,
                       const int64_t* off, float* C, int64_t ldc, void* stream) {
   int st = check_pair(A, B);
   if (st) return st;
+  if (A->cfg.grid == UFP4_E4M3) return UFP4_ERR_UNSUPPORTED;
   if (G < 1 || G > kMaxGroups || B->P % G) return G < 1 || G > kMaxGroups ? UFP4_ERR_INVALID_ARG
                                                                           : UFP4_ERR_SHAPE;
   st = check_offsets(off, G, A->P, A->cfg.block_rows);
@@ -268,7 +274,7 @@ int ufp4_quant_diag(const void* x, int64_t rows, int64_t cols, int64_t ld,
   int st = check_cfg(cfg);
   if (st) return st;
   if (!stats || !aligned(stats, 8)) return UFP4_ERR_INVALID_ARG;
-  if (cfg->block_rows != 1) return UFP4_ERR_UNSUPPORTED;
+  if (cfg->block_rows != 1 || cfg->grid == UFP4_E4M3) return UFP4_ERR_UNSUPPORTED;
   const int64_t P = rows, K = cols;
   if (P > 0 && K > 0) {
     if (!x) return UFP4_ERR_INVALID_ARG;
@@ -302,7 +308,7 @@ int ufp4_rht_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ld,
   if (cfg_row->block_rows != 1 || cfg_col->block_rows != 1 || cfg_row->grid != cfg_col->grid ||
       cfg_row->rounding != cfg_col->rounding || cfg_row->scale_mode != cfg_col->scale_mode ||
       cfg_row->block_cols != cfg_col->block_cols || cfg_row->rht_n != cfg_col->rht_n ||
-      cfg_row->rht_n > 64)
+      cfg_row->rht_n > 64 || cfg_row->grid == UFP4_E4M3)
     return UFP4_ERR_UNSUPPORTED;
   const int64_t n = cfg_row->rht_n, b = cfg_row->block_cols;
   const int64_t align = n > b ? n : b;
@@ -359,7 +365,7 @@ int ufp4_rht_quant_segmented(const void* x, int64_t rows, int64_t cols, int64_t 
   if (num_segments < 1 || num_segments > kMaxSegments) return UFP4_ERR_INVALID_ARG;
   int st = check_cfg(cfg);
   if (st) return st;
-  if (cfg->block_rows != 1) return UFP4_ERR_UNSUPPORTED;
+  if (cfg->block_rows != 1 || cfg->grid == UFP4_E4M3) return UFP4_ERR_UNSUPPORTED;
   if (row_offsets[0] != 0 || row_offsets[num_segments] != rows) return UFP4_ERR_INVALID_ARG;
   const int64_t align = cfg->rht_n > cfg->block_cols ? cfg->rht_n : cfg->block_cols;
   for (int g = 0; g < num_segments; ++g) {
@@ -394,7 +400,7 @@ int ufp4_dequant(const ufp4_qtensor* q, float* out, int64_t ldo, void* stream) {
   if (ldo < q->K) return UFP4_ERR_INVALID_ARG;
   if (q->P == 0 || q->K == 0) return UFP4_OK;
   if (!out) return UFP4_ERR_INVALID_ARG;
-  if (!aligned(q->codes, 4)) return UFP4_ERR_INVALID_ARG;
+  if (!aligned(q->codes, q->cfg.grid == UFP4_E4M3 ? 8 : 4)) return UFP4_ERR_INVALID_ARG;
   return hip_status(launch_dequant(q->codes, q->scales, q->P, q->K, q->cfg.grid,
                                    q->cfg.scale_mode, q->cfg.block_rows, q->cfg.block_cols, out,
                                    ldo, (hipStream_t)stream));
@@ -429,6 +435,7 @@ int ufp4_gemm_wgrad_grouped(const ufp4_qtensor* dYt, const ufp4_qtensor* Xt, int
                             const int64_t* offsets, float* dW, int64_t ldw, void* stream) {
   int st = check_pair(dYt, Xt);
   if (st) return st;
+  if (dYt->cfg.grid == UFP4_E4M3) return UFP4_ERR_UNSUPPORTED;
   if (dYt->cfg.scale_mode != UFP4_SCALE_F32 || dYt->cfg.block_rows != 1 ||
       Xt->cfg.block_rows != 1)
     return UFP4_ERR_UNSUPPORTED;

@@ -655,6 +655,162 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx4w(GemmLaunch g) {
                 lane, acc);
 }
 
+// ---------------------------------------------------------------------------
+// MXFP8 kernel (E4M3 codes, one byte per element, 1 x 32 E8M0 scales): the
+// codes are already FP8 operands, so they are copied HBM -> LDS untouched as
+// in k_gemm_mx4w.  K step 128 = one 128-byte line per row; two 66 KiB stages
+// (codes 2 x 32 KiB, one scale word per row and operand).  Fragments and the
+// scale operand as the FP8 path of k_gemm_mx: lane l takes 16 bytes of blocks
+// 2s and 2s+1 (chunks 4s + h and 4s + 2 + h) and supplies the scale of row
+// l % 32, block 2s + h.
+// ---------------------------------------------------------------------------
+constexpr int K8 = 128;
+constexpr int W8_CODES = 2 * TM * 128;
+constexpr int W8_STAGE = W8_CODES + 2 * TM * 4;   // 66 KiB
+
+__device__ __forceinline__ void w8_issue(const W4Ctx& c, int step, int st) {
+  const int s = step < c.nsteps ? step : c.nsteps - 1;   // past the end: re-read, unused
+  const uint32_t base = c.lds0 + (uint32_t)st * W8_STAGE;
+  const uint32_t koff = (uint32_t)s * 128u;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint32_t blk = (uint32_t)(c.wave * 8 + q) * 1024u;   // 8 rows x 128 B
+    lds_load16(base + blk, c.ra, c.code_voff[q], koff);
+    lds_load16(base + TM * 128 + blk, c.rb, c.code_voff[q], koff);
+  }
+  const uint32_t swave = (uint32_t)c.wave * 256u;
+  lds_load4(base + W8_CODES + swave, c.rsa, c.sa_voff, (uint32_t)s * 4u);
+  lds_load4(base + W8_CODES + TM * 4 + swave, c.rsb, c.sb_voff, (uint32_t)s * 4u);
+}
+
+__device__ __forceinline__ void w8_frags(const uint8_t* stage, int s, int lane, int wm, int wn,
+                                         F4Frags& f) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ra = wm * 128 + i * 32 + (lane & 31);
+    const int rb = wn * 128 + i * 32 + (lane & 31);
+    const uint8_t* b = stage + TM * 128;
+    const v4i x0 = *reinterpret_cast<const v4i*>(stage + off128(ra, 4 * s + h));
+    const v4i x1 = *reinterpret_cast<const v4i*>(stage + off128(ra, 4 * s + 2 + h));
+    const v4i y0 = *reinterpret_cast<const v4i*>(b + off128(rb, 4 * s + h));
+    const v4i y1 = *reinterpret_cast<const v4i*>(b + off128(rb, 4 * s + 2 + h));
+    f.a[i] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    f.b[i] = v8i{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+  }
+}
+
+__device__ __forceinline__ void w8_scales(const uint8_t* stage, int lane, int wm, int wn,
+                                          uint32_t (&sa)[4], uint32_t (&sb)[4]) {
+  const uint32_t* sw = reinterpret_cast<const uint32_t*>(stage + W8_CODES);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sa[i] = sw[wm * 128 + i * 32 + (lane & 31)];
+    sb[i] = sw[TM + wn * 128 + i * 32 + (lane & 31)];
+  }
+}
+
+__device__ __forceinline__ void f8_mfma(floatx16 (&acc)[4][4], const F4Frags& f,
+                                        const uint32_t (&sa)[4], const uint32_t (&sb)[4],
+                                        int s, int h) {
+  const uint32_t sh = 8u * (uint32_t)(2 * s + h);
+  int xa[4], xb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    xa[i] = (int)__builtin_amdgcn_ubfe(sa[i], sh, 8);
+    xb[i] = (int)__builtin_amdgcn_ubfe(sb[i], sh, 8);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0,
+                                                                  0, xa[i], 0, xb[j]);
+}
+
+__global__ __launch_bounds__(kThreads) void k_gemm_mx8(GemmLaunch g) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+  int tm, tn;
+  tile_order(blockIdx.x, g.total_tiles, (int)((g.PA + TM - 1) / TM), (int)((g.PB + TN - 1) / TN),
+             tm, tn);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
+  const int64_t K = g.K;
+  const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
+  const int64_t rows_a = g.PA - row0 < TM ? g.PA - row0 : TM;
+  const int64_t rows_b = g.PB - col0 < TN ? g.PB - col0 : TN;
+  const uint32_t rs = (uint32_t)K;            // one byte per element
+  const int64_t nkb = K / 32;
+
+  W4Ctx c;
+  c.wave = wave;
+  c.nsteps = (int)(K / K8);
+  c.ra = rsrc4(g.a_codes + row0 * rs, (uint32_t)(rows_a * rs));
+  c.rb = rsrc4(g.b_codes + col0 * rs, (uint32_t)(rows_b * rs));
+  c.rsa = rsrc4(g.a_scales, (uint32_t)(g.PA * nkb));
+  c.rsb = rsrc4(g.b_scales, (uint32_t)(g.PB * nkb));
+  c.lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds;
+  // lane i of wave load q: tile row 64 w + 8 q + i / 8, the chunk whose
+  // swizzled slot is i % 8
+  const int lrow = lane >> 3;
+  const uint32_t chunk = (uint32_t)((lane & 7) ^ lrow);
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    c.code_voff[q] = (uint32_t)(wave * 64 + q * 8 + lrow) * rs + 16u * chunk;
+  {
+    int64_t ra = row0 + wave * 64 + lane, rb = col0 + wave * 64 + lane;
+    if (ra >= g.PA) ra = g.PA - 1;   // codes of such rows read as zero; any scale works
+    if (rb >= g.PB) rb = g.PB - 1;
+    c.sa_voff = (uint32_t)(ra * nkb);
+    c.sb_voff = (uint32_t)(rb * nkb);
+  }
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
+
+  w8_issue(c, 0, 0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  F4Frags f0, f1;
+  uint32_t sa[4], sb[4];
+  w8_frags(lds, 0, lane, wm, wn, f0);
+  w8_scales(lds, lane, wm, wn, sa, sb);
+
+  for (int step = 0; step < c.nsteps; ++step) {
+    const uint8_t* cur = lds + (step & 1) * W8_STAGE;
+    w8_issue(c, step + 1, (step + 1) & 1);
+    w8_frags(cur, 1, lane, wm, wn, f1);
+    f8_mfma(acc, f0, sa, sb, 0, h);
+    f8_mfma(acc, f1, sa, sb, 1, h);
+    wait_vmcnt<0>();
+    __syncthreads();
+    const uint8_t* nxt = lds + ((step + 1) & 1) * W8_STAGE;
+    w8_frags(nxt, 0, lane, wm, wn, f0);
+    w8_scales(nxt, lane, wm, wn, sa, sb);
+  }
+
+  store_c<4, 4>(g.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
+                lane, acc);
+}
+
+hipError_t launch_mx8(const GemmLaunch& g, hipStream_t s) {
+  constexpr int bytes = 2 * W8_STAGE;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mx8,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_gemm_mx8, dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
+  return hipGetLastError();
+}
+
 hipError_t launch_mx4w(const GemmLaunch& g, hipStream_t s) {
   constexpr int bytes = 2 * W4_STAGE;
   static bool attr_set = false;
@@ -685,6 +841,10 @@ hipError_t launch_mx(const GemmLaunch& g, hipStream_t s) {
 }  // namespace
 
 bool gemm_mx_supported(const GemmLaunch& g) {
+  if (g.grid == 3)   // MXFP8: 1 x 32 blocks, byte codes
+    return g.mode == 0 && g.scale_mode == 1 && g.a_bc == 32 && g.b_bc == 32 && g.a_br == 1 &&
+           g.b_br == 1 && g.K % K8 == 0 && g.K * (int64_t)TM <= INT32_MAX &&
+           g.PA * (g.K / 32) <= INT32_MAX && g.PB * (g.K / 32) <= INT32_MAX;
   return g.mode == 0 && g.scale_mode == 1 && g.a_bc == 32 && g.b_bc == 32 &&
          (g.a_br == 1 || g.a_br == 32) && (g.b_br == 1 || g.b_br == 32) && g.K % KS == 0 &&
          g.K / 2 * (int64_t)TM <= INT32_MAX;
@@ -695,6 +855,7 @@ hipError_t launch_gemm_mx(const GemmLaunch& g, hipStream_t s) {
   switch (g.grid) {
     case 0: return launch_mx<0>(g, s);
     case 1: return launch_mx<1>(g, s);
+    case 3: return launch_mx8(g, s);
     default: return g.K % KW == 0 ? launch_mx4w(g, s) : launch_mx4(g, s);
   }
 }

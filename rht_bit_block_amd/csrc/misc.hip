@@ -14,6 +14,11 @@ namespace ufp4 {
 namespace {
 
 __device__ __forceinline__ float level_of(uint32_t c, int grid) {
+  if (grid == 3) {                                                 // E4M3 byte (MXFP8)
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const float mag = e == 0u ? ldexpf((float)m, -9) : ldexpf((float)(8u + m), (int)e - 10);
+    return (c & 0x80u) ? -mag : mag;
+  }
   if (grid == 1) return (float)(((int)(c << 28)) >> 28);          // INT4 two's complement
   const uint32_t k = c & 7u;
   float m;
@@ -33,9 +38,13 @@ __global__ void k_dequant(const uint8_t* codes, const void* scales, int64_t P, i
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t p = i / (K / 8), k0 = (i - p * (K / 8)) * 8;
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + p * (K / 2) + k0 / 2);
+    uint2 cw;
+    if (grid == 3) cw = *reinterpret_cast<const uint2*>(codes + p * K + k0);
+    else cw.x = *reinterpret_cast<const uint32_t*>(codes + p * (K / 2) + k0 / 2);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
+      const uint32_t c = grid == 3 ? (((j < 4 ? cw.x : cw.y) >> (8 * (j & 3))) & 0xFFu)
+                                   : ((cw.x >> (4 * j)) & 15u);
       const int64_t k = k0 + j;
       float s;
       if (smode == 0) {
@@ -44,7 +53,7 @@ __global__ void k_dequant(const uint8_t* codes, const void* scales, int64_t P, i
         const uint8_t e = reinterpret_cast<const uint8_t*>(scales)[(p / br) * (K / bc) + k / bc];
         s = ldexpf(1.0f, (int)e - 127);
       }
-      out[p * ldo + k] = __fmul_rn(level_of((w >> (4 * j)) & 15u, grid), s);
+      out[p * ldo + k] = __fmul_rn(level_of(c, grid), s);
     }
   }
 }

@@ -38,6 +38,8 @@ template <int GRID> struct Grid;
 template <> struct Grid<0> { static constexpr float qmax = 1.75f, inv_delta = 4.0f; };  // E1M2
 template <> struct Grid<1> { static constexpr float qmax = 7.0f, inv_delta = 1.0f; };   // INT4
 template <> struct Grid<2> { static constexpr float qmax = 6.0f, inv_delta = 0.0f; };   // E2M1
+// MXFP8: OCP E4M3 elements (one byte per code), 1 x 32 power-of-two scales only
+template <> struct Grid<3> { static constexpr float qmax = 448.0f, inv_delta = 0.0f; };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -213,11 +215,35 @@ __device__ __forceinline__ int pow2_exponent(float M) {
   constexpr float qmax = Grid<GRID>::qmax;
   int e = -127;
   if (M > 0.0f) {
-    e = ilogbf(M) - 3;  // qmax < 8, so M > qmax * 2^(ilogb(M) - 3)
+    // qmax < 2^QE, so M > qmax * 2^(ilogb(M) - QE)
+    constexpr int QE = GRID == 3 ? 9 : 3;
+    e = ilogbf(M) - QE;
     if (e < -127) e = -127;
     while (e < 127 && M > ldexpf(qmax, e)) ++e;
   }
   return e;
+}
+
+// RTNE onto E4M3 (|v| <= 448): the pattern b = 8 e + m of the nearest
+// value, ties to even m.  Subnormal range (|v| < 2^-6, spacing 2^-9): the
+// magic-number rint of |v| * 2^9 is b itself (b = 8 is 2^-6).  Normal range:
+// the fp32 mantissa rounded to 3 bits (RNE, the carry may step the exponent)
+// gives (biased exponent << 3 | m); b subtracts the bias difference 120 << 3.
+// Sign bit 0x80, zero always 0x00.
+__device__ __forceinline__ uint32_t e4m3_rtne(float v) {
+  const float m = fabsf(v);
+  const uint32_t sub = __float_as_uint(__fmaf_rn(m, 512.0f, kMagic)) & 0xFFu;
+  const uint32_t bits = __float_as_uint(m);
+  const uint32_t r = bits + 0x7FFFFu + ((bits >> 20) & 1u);
+  const uint32_t nrm = (r >> 20) - (120u << 3);
+  const uint32_t b = m < 0x1p-6f ? sub : nrm;
+  return b | ((v < 0.0f && b != 0u) ? 0x80u : 0u);
+}
+
+// Byte offset of element e0's code: 4-bit codes two per byte, E4M3 one.
+template <int GRID>
+__device__ __forceinline__ uint8_t* code_ptr(uint8_t* base, uint64_t e0) {
+  return base + (GRID == 3 ? e0 : (e0 >> 1));
 }
 
 // Quantize the W values of one lane whose blocks are 1 x B; writes codes
@@ -273,6 +299,9 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
   uint32_t packed[W / 8];
 #pragma unroll
   for (int i = 0; i < W / 8; ++i) packed[i] = 0u;
+  uint32_t bytes[GRID == 3 ? W / 4 : 1];   // E4M3 codes, four per word
+#pragma unroll
+  for (int i = 0; i < (GRID == 3 ? W / 4 : 1); ++i) bytes[i] = 0u;
 #pragma unroll
   for (int blk = 0; blk < W / B; ++blk) {
     float M = 0.0f;
@@ -333,6 +362,11 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const int idx = blk * B + j;
+      if constexpr (GRID == 3) {
+        static_assert(RM == 0 && POW2 && !DIAG, "E4M3: RTNE with power-of-two scales");
+        bytes[idx >> 2] |= e4m3_rtne(v[j]) << (8 * (idx & 3));
+        continue;
+      }
       uint32_t nib;
       if constexpr (RM == 0) {
         nib = rtne_nibble<GRID>(v[j]);   // no clamp needed: qmax + 1 ulp rounds to qmax
@@ -346,6 +380,13 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
     }
   }
   if constexpr (DIAG) return;
+  if constexpr (GRID == 3) {
+#pragma unroll
+    for (int i = 0; i < W / 16; ++i)
+      reinterpret_cast<uint4*>(codes_out)[i] =
+          make_uint4(bytes[4 * i], bytes[4 * i + 1], bytes[4 * i + 2], bytes[4 * i + 3]);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < W / 8; ++i) packed[i] = finish_codes<GRID>(packed[i]);
   if constexpr (W == 16) {
@@ -419,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantLaunch q, FastDiv 
     unpack<W>(w, pm, y);
     fwht<W, N>(y, neg1, neg2);
     const uint64_t e0 = (uint64_t)p * K + k0;
-    finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, q, e0, q.codes + (e0 >> 1),
+    finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, q, e0, code_ptr<GRID>(q.codes, e0),
                                     scale_at<RND>(q.scales, (uint64_t)p * (K / B) + k0 / B));
   }
 }
@@ -428,13 +469,21 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantLaunch q, FastDiv 
 // Level statistics of a row-wise 1 x B quantization (diagnostics): the same
 // pipeline as k_quant_rows, each element's level index and rounding error
 // accumulated in the thread's LDS column instead of being stored; at the end
-// the workgroup sums its columns and adds them to stats[0..7] (counts) and
-// stats[8..15] (error sums) with 64-bit integer atomics.
+// the workgroup sums its columns and adds them (64-bit integer atomics) to
+// a partial set: counts [0..7], error sums [8..15].
 // ---------------------------------------------------------------------------
+// Partial statistics of the workgroups (one file-scope array per translation
+// unit, used only by name inside the kernels below): the zeroing kernel
+// clears them, workgroup b adds into set b % kDiagSlots, and the final
+// kernel sums the sets into the caller's stats.  Diagnostics calls that
+// overlap on one GPU therefore race; the three launches of one call are
+// ordered by its stream.
+constexpr int kDiagSlots = 64;
+static __device__ unsigned long long g_diag_partials[kDiagSlots * 16];
+
 template <int W, int B, int N, int GRID, int RND>
 __global__ __launch_bounds__(kThreads) void k_quant_diag(QuantLaunch q, FastDiv segs_per_row,
-                                                         uint32_t nseg,
-                                                         unsigned long long* stats) {
+                                                         uint32_t nseg) {
   __shared__ DiagLds d;
   constexpr int lpc = N > W ? N / W : 1;
 #pragma unroll
@@ -489,9 +538,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_diag(QuantLaunch q, FastDiv 
     c += __shfl_xor(c, off);
     sm += __shfl_xor(sm, off);
   }
-  if (part == 0) {
-    atomicAdd(stats + lev, c);
-    atomicAdd(stats + 8 + lev, (unsigned long long)sm);
+  if (part == 0) {   // one of kDiagSlots partial sets, so few workgroups share an address
+    unsigned long long* slot = g_diag_partials + (blockIdx.x % kDiagSlots) * 16;
+    atomicAdd(slot + lev, c);
+    atomicAdd(slot + 8 + lev, (unsigned long long)sm);
   }
 }
 
@@ -589,7 +639,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantLaunch q) {
     const int64_t p = p0 + col;
     const int64_t k = k0 + kr;
     const uint64_t e0 = (uint64_t)C * seg0 + (uint64_t)p * L + k;   // global draw index
-    finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, q, e0, q.codes + (e0 >> 1),
+    finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, q, e0, code_ptr<GRID>(q.codes, e0),
                                     scale_at<RND>(q.scales, e0 / B));
   }
 }
@@ -676,7 +726,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide 
       unpack<W>(w, pm, y);
       fwht<W, N>(y, neg1, neg2);
       const uint64_t e0 = (uint64_t)C * seg0 + (uint64_t)(p0 + col) * L + (k0 + kr);
-      finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, q, e0, q.codes + (e0 >> 1),
+      finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, q, e0, code_ptr<GRID>(q.codes, e0),
                                                    scale_at<RND>(q.scales, e0 / B));
     }
   }
@@ -703,7 +753,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide 
       unpack<W>(w, pm, y);
       fwht<W, N>(y, neg1, neg2);
       const uint64_t e0 = (uint64_t)(seg0 + k0 + row) * (uint64_t)C + (uint64_t)(p0 + c0);
-      finish_lane<W, B, N, GRID, RND, RowSide>(y, rside, e0, rside.codes + (e0 >> 1),
+      finish_lane<W, B, N, GRID, RND, RowSide>(y, rside, e0, code_ptr<GRID>(rside.codes, e0),
                                                scale_at<RND>(rside.scales, e0 / B));
     }
   }
@@ -808,23 +858,35 @@ hipError_t run_rows(const QuantLaunch& q, hipStream_t s) {
 }
 
 template <int G>
-__global__ void k_diag_zero(unsigned long long* stats) {
-  if (threadIdx.x < 16) stats[threadIdx.x] = 0ull;
+__global__ void k_diag_zero() {
+  for (int i = threadIdx.x; i < kDiagSlots * 16; i += blockDim.x) g_diag_partials[i] = 0ull;
+}
+
+template <int G>
+__global__ void k_diag_final(unsigned long long* stats) {
+  if (threadIdx.x >= 16) return;
+  unsigned long long t = 0;
+  for (int s = 0; s < kDiagSlots; ++s) t += g_diag_partials[s * 16 + threadIdx.x];
+  stats[threadIdx.x] = t;
 }
 
 template <int W, int B, int N, int G, int R>
 hipError_t run_diag(const QuantLaunch& q, unsigned long long* stats, hipStream_t s) {
-  hipLaunchKernelGGL(k_diag_zero<G>, dim3(1), dim3(64), 0, s, stats);
+  hipLaunchKernelGGL(k_diag_zero<G>, dim3(1), dim3(256), 0, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t segs_per_row = (uint32_t)(q.K / W);
   const uint64_t nseg = (uint64_t)q.P * segs_per_row;
-  if (nseg == 0) return hipSuccess;
-  const uint64_t blocks_needed = (nseg + kThreads - 1) / kThreads;
-  const uint64_t cap = (uint64_t)device_grid_limit() * 8;
-  const uint32_t blocks = (uint32_t)(blocks_needed < cap ? blocks_needed : cap);
-  hipLaunchKernelGGL((k_quant_diag<W, B, N, G, R>), dim3(blocks), dim3(kThreads), 0, s, q,
-                     make_fastdiv(segs_per_row), (uint32_t)nseg, stats);
+  if (nseg > 0) {
+    const uint64_t blocks_needed = (nseg + kThreads - 1) / kThreads;
+    const uint64_t cap = (uint64_t)device_grid_limit() * 8;
+    const uint32_t blocks = (uint32_t)(blocks_needed < cap ? blocks_needed : cap);
+    hipLaunchKernelGGL((k_quant_diag<W, B, N, G, R>), dim3(blocks), dim3(kThreads), 0, s, q,
+                       make_fastdiv(segs_per_row), (uint32_t)nseg);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_diag_final<G>, dim3(1), dim3(64), 0, s, stats);
   return hipGetLastError();
 }
 

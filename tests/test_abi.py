@@ -78,7 +78,7 @@ def test_quant_argument_errors():
     assert _quant(lib, ld=32) == E.UFP4_ERR_INVALID_ARG            # ld < cols
     assert _quant(lib, along=2) == E.UFP4_ERR_INVALID_ARG
     assert _quant(lib, x=FAKE + 2) == E.UFP4_ERR_INVALID_ARG       # misaligned
-    assert _quant(lib, cfg=U.make_cfg(grid=3)) == E.UFP4_ERR_INVALID_ARG
+    assert _quant(lib, cfg=U.make_cfg(grid=4)) == E.UFP4_ERR_INVALID_ARG
     assert _quant(lib, cfg=U.make_cfg(rht_n=24)) == E.UFP4_ERR_SHAPE
     assert _quant(lib, cfg=U.make_cfg(rht_n=256)) == E.UFP4_ERR_SHAPE
     assert _quant(lib, cols=48, ld=48, cfg=U.make_cfg(rht_n=32, block_cols=16)) == E.UFP4_ERR_SHAPE
@@ -210,3 +210,26 @@ def test_diag_argument_errors():
                        block_cols=32, rht_n=1)
     assert _diag(lib, cfg=two_d) == E.UFP4_ERR_UNSUPPORTED
     assert _diag(lib, cfg=U.make_cfg(scale_mode=U.UFP4_SCALE_POW2, block_cols=16)) == E.UFP4_ERR_UNSUPPORTED
+
+
+def test_mxfp8_argument_errors():
+    """MXFP8 (E4M3) only with 1 x 32 power-of-two blocks and RTNE, only on
+    the row/column quantizer, dequant and the dense GEMMs."""
+    lib = U.lib_handle()
+    E = U
+    mx = U.make_cfg(grid=U.UFP4_E4M3, scale_mode=U.UFP4_SCALE_POW2, block_cols=32, rht_n=16)
+    assert _quant(lib, cfg=mx.copy(rounding=U.UFP4_SR)) == E.UFP4_ERR_UNSUPPORTED
+    assert _quant(lib, cfg=mx.copy(scale_mode=U.UFP4_SCALE_F32)) == E.UFP4_ERR_UNSUPPORTED
+    assert _quant(lib, cfg=mx.copy(block_cols=16)) == E.UFP4_ERR_UNSUPPORTED
+    assert _quant(lib, cfg=mx.copy(block_rows=32, rht_n=1)) == E.UFP4_ERR_UNSUPPORTED
+    assert _quant(lib, cfg=U.make_cfg(grid=4)) == E.UFP4_ERR_INVALID_ARG
+    assert _diag(lib, cfg=mx) == E.UFP4_ERR_UNSUPPORTED
+    assert _dual(lib, cfg_r=mx, cfg_c=mx) == E.UFP4_ERR_UNSUPPORTED
+    a = _qt(64, 160, mx.copy(rht_n=1))
+    b = _qt(64, 160, mx.copy(rht_n=1))
+    assert lib.ufp4_gemm_fprop(ctypes.byref(a), ctypes.byref(b), ctypes.c_void_p(FAKE), 64, None) == E.UFP4_ERR_UNSUPPORTED
+    a = _qt(64, 256, mx)
+    b = _qt(64, 256, mx)
+    offs = (ctypes.c_int64 * 3)(0, 32, 64)
+    assert lib.ufp4_gemm_fprop_grouped(ctypes.byref(a), ctypes.byref(b), 2, offs, ctypes.c_void_p(FAKE), 32, None) == E.UFP4_ERR_UNSUPPORTED
+    assert lib.ufp4_gemm_wgrad_grouped(ctypes.byref(a), ctypes.byref(b), 2, offs, ctypes.c_void_p(FAKE), 64, None) == E.UFP4_ERR_UNSUPPORTED

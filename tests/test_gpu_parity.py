@@ -406,3 +406,63 @@ def test_repeat_determinism():
     C1 = U.ufp4_gemm_fprop(a, b)
     C2 = U.ufp4_gemm_fprop(a, b)
     assert torch.equal(C1, C2)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 (E4M3 elements, 1 x 32 E8M0 scales): [2DFP4] mixed-precision section.
+# ---------------------------------------------------------------------------
+def _mxfp8_cfg(n, sign_seed=0):
+    return U.make_cfg(U.UFP4_E4M3, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, n, sign_seed=sign_seed)
+
+
+@pytest.mark.parametrize("n", [1, 16, 32, 128])
+@pytest.mark.parametrize("along", [0, 1])
+def test_quant_mxfp8(n, along):
+    """Bit-exact E4M3 codes, E8M0 scales and rotated values, row- and
+    column-wise (40 rows / 72 columns: ragged against the lane and tile
+    shapes)."""
+    _print_case("mxfp8", n, along)
+    bits = rand_bits(40, 384, seed=n + 3) if along == 0 else rand_bits(384, 72, seed=n + 4)
+    q, ref = compare_quant(bits, along, _mxfp8_cfg(n, sign_seed=40 + n))
+    assert q.codes.shape == (q.P, q.K)
+    d = U.ufp4_dequant(q).cpu().numpy()
+    assert f32_bits_equal(d, O.dequant(ref["codes"], ref["scales"], spec_of(q.cfg), q.P, q.K)[0])
+
+
+def test_quant_mxfp8_edge_values():
+    """Subnormal E4M3 results (elements 2^-7..2^-12 of their block maximum),
+    ties between E4M3 neighbours, blocks at exactly 448 * 2^e, all-zero
+    blocks and huge blocks at the exponent clamp."""
+    _print_case("mxfp8 edges")
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((64, 256)).astype(np.float32)
+    x[0:8, :32] *= np.float32(2.0 ** -12)
+    x[0:8, 0] = 448.0                                   # e = 0, the rest subnormal E4M3
+    x[8:16, 32:64] = np.float32(1.0625) * np.sign(x[8:16, 32:64])   # ties at e = -8
+    x[8:16, 32] = 448.0 * 2.0 ** -8
+    x[16:24, 64:96] = 0.0
+    x[24:32, 96:128] = np.float32(3.0e38) * np.sign(x[24:32, 96:128])
+    x[32:40, 128:160] = np.float32(2.0 ** -130)         # fp32/bf16 subnormals
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for along in (0, 1):
+        compare_quant(bits if along == 0 else np.ascontiguousarray(bits.T), along, _mxfp8_cfg(1))
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 128), (300, 270, 384), (520, 64, 1024), (17, 513, 256)])
+def test_gemm_mxfp8(shape):
+    """MXFP8 x MXFP8 on the scaled matrix cores vs the oracle's fp64 product
+    (several tiles, ragged rows; K a multiple of 128)."""
+    _print_case("gemm mxfp8", shape)
+    PA, PB, K = shape
+    cfg = _mxfp8_cfg(16, sign_seed=5)
+    _gemm_case(PA, PB, K, cfg, cfg, seed=PA + PB + K)
+
+
+def test_gemm_mxfp8_unsupported_k():
+    """K not a multiple of 128 is rejected before any launch."""
+    cfg = _mxfp8_cfg(1)
+    qa, _ = U.ufp4_rht_quant(dev_bf16(rand_bits(64, 160, 1)), 0, cfg)
+    qb, _ = U.ufp4_rht_quant(dev_bf16(rand_bits(64, 160, 2)), 0, cfg)
+    with pytest.raises(U.UFP4Error) as ei:
+        U.ufp4_gemm_fprop(qa, qb)
+    assert ei.value.status == U.UFP4_ERR_UNSUPPORTED
