@@ -82,6 +82,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-mx", action="store_true",
                    help="skip the power-of-two (scaled matrix core) GEMM figures")
+    p.add_argument("--streams", type=int, default=1, choices=[1, 2],
+                   help="2: run the quantizations FPROP does not need on a second stream")
     p.add_argument("--no-diag", action="store_true",
                    help="skip the quantization diagnostics (level statistics) figures")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -96,9 +98,17 @@ class Workload:
     """The dense layer's 9 library calls, as raw C-ABI calls with prebuilt
     ctypes arguments, for each input buffer set."""
 
-    def __init__(self, U, torch, grid, nsets):
+    # With two streams, the quantizations that FPROP does not need (dY row-wise,
+    # W, dY and X column-wise) run on a second stream beside X/W row-wise and
+    # FPROP; DGRAD waits for them.  Same calls, same bytes, one GPU.
+    AUX = ("quant_dy_row", "quant_w_col", "quant_dy_col", "quant_x_col")
+
+    def __init__(self, U, torch, grid, nsets, streams=1):
         import workloads
         self.U, self.torch = U, torch
+        self.streams = streams
+        self.main = torch.cuda.current_stream()
+        self.aux = torch.cuda.Stream() if streams == 2 else self.main   # default priority
         base = workloads.config2("cuda")
         self.sets = [base.tensors] + [{k: v.clone() for k, v in base.tensors.items()}
                                       for _ in range(nsets - 1)]
@@ -114,7 +124,8 @@ class Workload:
                        ("dy_row", "dY", 0, mk(sd, U.UFP4_SR, 0)), ("w_col", "W", 1, mk(sd, U.UFP4_RTNE)),
                        ("dy_col", "dY", 1, mk(sw, U.UFP4_SR, 1)), ("x_col", "X", 1, mk(sw, U.UFP4_RTNE))]
         self.lib = U.lib_handle()
-        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.stream = ctypes.c_void_p(self.main.cuda_stream)
+        self.aux_stream = ctypes.c_void_p(self.aux.cuda_stream)
         dev = "cuda"
         self.q = {}
         for name, tn, along, cfg in self.qcalls:
@@ -140,9 +151,10 @@ class Workload:
             t = tensors[tn]
             rows, cols = t.shape
             q = self.q[name]
+            st = self.aux_stream if "quant_" + name in self.AUX else self.stream
             args = (ctypes.c_void_p(t.data_ptr()), rows, cols, t.stride(0), along,
                     ctypes.byref(cfg), ctypes.c_void_p(q.codes.data_ptr()),
-                    ctypes.c_void_p(q.scales.data_ptr()), None, self.stream)
+                    ctypes.c_void_p(q.scales.data_ptr()), None, st)
             calls.append(("quant_" + name, lib.ufp4_rht_quant, args))
         for name, a, b in self.gcalls:
             qa, qb = self.q[a].c(), self.q[b].c()
@@ -154,7 +166,16 @@ class Workload:
         return calls
 
     def step(self, i):
-        for name, fn, args in self.calls[i % len(self.calls)]:
+        calls = self.calls[i % len(self.calls)]
+        if self.streams == 2:
+            ev0 = self.torch.cuda.Event()
+            ev0.record(self.main)
+            self.aux.wait_event(ev0)      # buffers of earlier steps are done with
+        for name, fn, args in calls:
+            if self.streams == 2 and name == "dgrad":
+                ev1 = self.torch.cuda.Event()
+                ev1.record(self.aux)
+                self.main.wait_event(ev1)
             st = fn(*args)
             if st:
                 raise RuntimeError(f"{name} failed: {self.U.ufp4_status_string(st)}")
@@ -167,13 +188,15 @@ class Workload:
             _, fn, args = self.calls[i % len(self.calls)][idx]
             fn(*args)
         torch.cuda.synchronize()
+        name = self.calls[0][idx][0]
+        st = self.aux if name in self.AUX else self.main   # events on the launch stream
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
+        e0.record(st)
         for i in range(reps):
             _, fn, args = self.calls[i % len(self.calls)][idx]
             fn(*args)
-        e1.record()
+        e1.record(st)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
@@ -400,7 +423,7 @@ def main():
     import rht_bit_block_amd as U
 
     grid = {"e1m2": U.UFP4_E1M2, "int4": U.UFP4_INT4, "e2m1": U.UFP4_E2M1}[args.grid]
-    wl = Workload(U, torch, grid, max(1, args.sets))
+    wl = Workload(U, torch, grid, max(1, args.sets), streams=args.streams)
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
@@ -478,7 +501,8 @@ def main():
         "data": "synthetic (seeded torch generators; dense linear-layer tensors)",
         "config": {"workload": f"dense linear layer M={wl_m} K={wl_k} N={wl_n}: 6 fused RHT(n=16)"
                                f"+1x16 {args.grid} quantizations (SR on dY) + FPROP/DGRAD/WGRAD",
-                   "global_batch": wl_m, "seq_len": None, "parallelism": "single GPU"},
+                   "global_batch": wl_m, "seq_len": None, "parallelism": "single GPU",
+                   "streams": args.streams},
         "roofline": roof,
         "quant": {"GB/s": round(quant_gbps, 1), "frac_hbm_peak": round(quant_gbps / HBM_PEAK_GBPS, 4),
                   "ms": round(quant_ms, 4), "bytes_per_elem": QBYTES_PER_ELEM},

@@ -590,10 +590,14 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantLaunch q) {
       if (r < krows) ra = ld16(src);
       if (r + 1 < krows) rb = ld16(src + q.ld);
     } else {
-      uint16_t ta[8] = {0, 0, 0, 0, 0, 0, 0, 0}, tb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int j = 0; j < 8 && c8 + j < pcols; ++j) {
-        if (r < krows) ta[j] = src[j];
-        if (r + 1 < krows) tb[j] = src[q.ld + j];
+      // ragged columns: element loads with compile-time indices (a runtime
+      // index into a local array would place it in scratch memory)
+      uint32_t ta[8], tb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool in = c8 + j < pcols;
+        ta[j] = (in && r < krows) ? (uint32_t)src[j] : 0u;
+        tb[j] = (in && r + 1 < krows) ? (uint32_t)src[q.ld + j] : 0u;
       }
       ra = make_uint4(ta[0] | (ta[1] << 16), ta[2] | (ta[3] << 16), ta[4] | (ta[5] << 16),
                       ta[6] | (ta[7] << 16));
@@ -680,10 +684,14 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide 
       if (r < krows) ra = ld16(src);
       if (r + 1 < krows) rb = ld16(src + q.ld);
     } else {
-      uint16_t ta[8] = {0, 0, 0, 0, 0, 0, 0, 0}, tb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int j = 0; j < 8 && c8 + j < pcols; ++j) {
-        if (r < krows) ta[j] = src[j];
-        if (r + 1 < krows) tb[j] = src[q.ld + j];
+      // ragged columns: element loads with compile-time indices (a runtime
+      // index into a local array would place it in scratch memory)
+      uint32_t ta[8], tb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool in = c8 + j < pcols;
+        ta[j] = (in && r < krows) ? (uint32_t)src[j] : 0u;
+        tb[j] = (in && r + 1 < krows) ? (uint32_t)src[q.ld + j] : 0u;
       }
       ra = make_uint4(ta[0] | (ta[1] << 16), ta[2] | (ta[3] << 16), ta[4] | (ta[5] << 16),
                       ta[6] | (ta[7] << 16));
