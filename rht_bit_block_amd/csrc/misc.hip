@@ -172,7 +172,7 @@ __global__ void k_philox_fill(uint64_t seed, uint32_t stream, uint64_t first, in
     const uint64_t e = first + (uint64_t)i;
     const uint64_t g = e >> 3;
     uint32_t c[4] = {(uint32_t)g, (uint32_t)(g >> 32), stream, 0u};
-    philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+    philox4x32_10_dev(c, (uint32_t)seed, (uint32_t)(seed >> 32));
     const uint32_t w = c[(e & 7) >> 1];
     out[i] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
   }

@@ -202,7 +202,7 @@ __device__ __forceinline__ void sr_draws(uint64_t e0, uint64_t seed, uint32_t st
   for (int t = 0; t < W / 8; ++t) {
     const uint64_t g = (e0 >> 3) + (uint64_t)t;
     uint32_t c[4] = {(uint32_t)g, (uint32_t)(g >> 32), stream, 0u};
-    philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+    philox4x32_10_dev(c, (uint32_t)seed, (uint32_t)(seed >> 32));
 #pragma unroll
     for (int i = 0; i < 4; ++i) words[4 * t + i] = c[i];
   }

@@ -31,6 +31,32 @@ __host__ __device__ inline void philox4x32_10(uint32_t c[4], uint32_t k0, uint32
   }
 }
 
+// The same generator in device code: each round's two three-input XORs
+// are one gfx950 three-input bitwise op each (truth table 0x96 = a ^ b ^ c;
+// the compiler emits two two-input XORs for them otherwise).
+__device__ __forceinline__ uint32_t xor3_key(uint32_t a, uint32_t b, uint32_t key) {
+  return __builtin_amdgcn_bitop3_b32(a, b, key, 0x96);
+}
+
+__device__ __forceinline__ void philox4x32_10_dev(uint32_t c[4], uint32_t k0,
+                                                          uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t n0 = xor3_key((uint32_t)(p1 >> 32), c[1], k0);
+    const uint32_t n2 = xor3_key((uint32_t)(p0 >> 32), c[3], k1);
+    c[1] = (uint32_t)p1;
+    c[3] = (uint32_t)p0;
+    c[0] = n0;
+    c[2] = n2;
+  }
+}
+
 // Unsigned 32-bit division by a launch constant d >= 1, as a multiply-high
 // (Granlund & Montgomery, "Division by invariant integers using
 // multiplication", PLDI'94): q = (umulhi(m, n) + n) >> l with l = ceil(log2 d),
