@@ -84,6 +84,9 @@ def parse():
                    help="skip the power-of-two (scaled matrix core) GEMM figures")
     p.add_argument("--streams", type=int, default=1, choices=[1, 2],
                    help="2: run the quantizations FPROP does not need on a second stream")
+    p.add_argument("--dual", type=int, default=1, choices=[0, 1],
+                   help="1 (default): each of X, W, dY quantized along both axes by one fused "
+                        "call; 0: six single-axis calls (bit-identical outputs)")
     p.add_argument("--no-diag", action="store_true",
                    help="skip the quantization diagnostics (level statistics) figures")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -103,10 +106,11 @@ class Workload:
     # FPROP; DGRAD waits for them.  Same calls, same bytes, one GPU.
     AUX = ("quant_dy_row", "quant_w_col", "quant_dy_col", "quant_x_col")
 
-    def __init__(self, U, torch, grid, nsets, streams=1):
+    def __init__(self, U, torch, grid, nsets, streams=1, dual=False):
         import workloads
         self.U, self.torch = U, torch
         self.streams = streams
+        self.dual = dual
         self.main = torch.cuda.current_stream()
         self.aux = torch.cuda.Stream() if streams == 2 else self.main   # default priority
         base = workloads.config2("cuda")
@@ -142,12 +146,30 @@ class Workload:
                        ("wgrad", "dy_col", "x_col")]
         self._keep = []
         self.calls = [self._build_calls(s) for s in self.sets]
-        self.elems = {name: base.tensors[tn].numel() for name, tn, _, _ in self.qcalls}
+        if dual:   # one fused dual-axis call per tensor: bf16 read once, two code sets
+            self.elems = {"x": X.numel(), "w": base.tensors["W"].numel(),
+                          "dy": base.tensors["dY"].numel()}
+            self.qbpe = {k: 2.0 + 2 * (QBYTES_PER_ELEM - 2.0) for k in self.elems}
+        else:
+            self.elems = {name: base.tensors[tn].numel() for name, tn, _, _ in self.qcalls}
+            self.qbpe = {k: QBYTES_PER_ELEM for k in self.elems}
         self.flops = {"fprop": 2.0 * M * N * K, "dgrad": 2.0 * M * K * N, "wgrad": 2.0 * N * K * M}
 
     def _build_calls(self, tensors):
         lib, calls = self.lib, []
-        for name, tn, along, cfg in self.qcalls:
+        if self.dual:
+            cfgs = {name: cfg for name, _, _, cfg in self.qcalls}
+            for name, tn in (("x", "X"), ("w", "W"), ("dy", "dY")):
+                t = tensors[tn]
+                rows, cols = t.shape
+                qr, qc = self.q[name + "_row"], self.q[name + "_col"]
+                args = (ctypes.c_void_p(t.data_ptr()), rows, cols, t.stride(0), None, 1,
+                        ctypes.byref(cfgs[name + "_row"]), ctypes.byref(cfgs[name + "_col"]),
+                        ctypes.c_void_p(qr.codes.data_ptr()), ctypes.c_void_p(qr.scales.data_ptr()),
+                        ctypes.c_void_p(qc.codes.data_ptr()), ctypes.c_void_p(qc.scales.data_ptr()),
+                        self.stream)
+                calls.append(("quant_" + name, lib.ufp4_rht_quant_dual, args))
+        for name, tn, along, cfg in ([] if self.dual else self.qcalls):
             t = tensors[tn]
             rows, cols = t.shape
             q = self.q[name]
@@ -423,7 +445,7 @@ def main():
     import rht_bit_block_amd as U
 
     grid = {"e1m2": U.UFP4_E1M2, "int4": U.UFP4_INT4, "e2m1": U.UFP4_E2M1}[args.grid]
-    wl = Workload(U, torch, grid, max(1, args.sets), streams=args.streams)
+    wl = Workload(U, torch, grid, max(1, args.sets), streams=args.streams, dual=args.dual)
     torch.cuda.synchronize()
 
     for i in range(args.warmup):
@@ -448,7 +470,7 @@ def main():
     for k, f in wl.flops.items():
         kernels[k] = {"ms": round(per[k], 4), "TFLOP/s": round(f / per[k] / 1e9, 2),
                       "frac_bf16_peak": round(f / per[k] / 1e9 / BF16_PEAK_TFLOPS, 4)}
-    qbytes = {k: QBYTES_PER_ELEM * v for k, v in wl.elems.items()}
+    qbytes = {k: wl.qbpe[k] * v for k, v in wl.elems.items()}
     for k, b in qbytes.items():
         kernels["quant_" + k] = {"ms": round(per["quant_" + k], 4),
                                  "GB/s": round(b / per["quant_" + k] / 1e6, 1),
@@ -499,13 +521,14 @@ def main():
         "vs_baseline": None, "dtype": args.grid,
         "dtype_detail": "bf16 in; fp32 rotate/scale/round; 4-bit codes; split-bf16 MFMA, fp32 accumulate",
         "data": "synthetic (seeded torch generators; dense linear-layer tensors)",
-        "config": {"workload": f"dense linear layer M={wl_m} K={wl_k} N={wl_n}: 6 fused RHT(n=16)"
-                               f"+1x16 {args.grid} quantizations (SR on dY) + FPROP/DGRAD/WGRAD",
+        "config": {"workload": f"dense linear layer M={wl_m} K={wl_k} N={wl_n}: "
+                               + ("3 dual-axis fused RHT(n=16)+1x16 " if args.dual else "6 fused RHT(n=16)+1x16 ")
+                               + f"{args.grid} quantizations (6 quantized copies, SR on dY) + FPROP/DGRAD/WGRAD",
                    "global_batch": wl_m, "seq_len": None, "parallelism": "single GPU",
-                   "streams": args.streams},
+                   "streams": args.streams, "dual_axis_quant": bool(args.dual)},
         "roofline": roof,
         "quant": {"GB/s": round(quant_gbps, 1), "frac_hbm_peak": round(quant_gbps / HBM_PEAK_GBPS, 4),
-                  "ms": round(quant_ms, 4), "bytes_per_elem": QBYTES_PER_ELEM},
+                  "ms": round(quant_ms, 4), "bytes_per_elem": next(iter(wl.qbpe.values()))},
         "gemm": {"TFLOP/s": round(total_flops / gemm_ms / 1e9, 2),
                  "frac_bf16_peak": round(total_flops / gemm_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
                  "frac_fp4_peak": round(total_flops / gemm_ms / 1e9 / FP4_PEAK_TFLOPS, 4),
