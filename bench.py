@@ -39,20 +39,17 @@ QBYTES_PER_ELEM = 2.75        # bf16 in (2) + 4-bit code (0.5) + fp32 scale / 16
 # what the same counters read for a plain 1 GiB device copy (bench.py
 # --calibrate-copy).  A figure holds only for the kernel source it was taken
 # on: the sources' hash is recorded and a mismatch reports null.
-FETCH_SCALE, WRITE_SCALE = 1048576 / 524302.3, 1048576 / 1048576.0
+FETCH_SCALE, WRITE_SCALE = 1048576 / 524302.8, 1048576 / 1048576.0
 _GEMM_SRC = ("gemm_rd.hip", "gemm_epilogue.h", "ufp4_internal.h")
 _QUANT_SRC = ("quant_core.h", "ufp4_internal.h")
 MEASURED_TRAFFIC = {
     # kernel: (sources, sha256[:16] of them, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "fprop": (_GEMM_SRC, "69a0dd8a174253a5", 74041.9, 262144.0),
-    "dgrad": (_GEMM_SRC, "69a0dd8a174253a5", 73860.2, 65536.0),
-    "wgrad": (_GEMM_SRC, "69a0dd8a174253a5", 73860.2, 65536.0),
-    "quant_x_row": (_QUANT_SRC, "d1c5c161c8474b6f", 16423.8, 12288.0),
-    "quant_w_row": (_QUANT_SRC, "d1c5c161c8474b6f", 16423.8, 12288.0),
-    "quant_dy_row": (_QUANT_SRC, "d1c5c161c8474b6f", 65604.9, 49152.0),
-    "quant_x_col": (_QUANT_SRC, "d1c5c161c8474b6f", 16450.1, 12288.1),
-    "quant_w_col": (_QUANT_SRC, "d1c5c161c8474b6f", 16450.1, 12288.1),
-    "quant_dy_col": (_QUANT_SRC, "d1c5c161c8474b6f", 65626.7, 50629.7),
+    "fprop": (_GEMM_SRC, "722628b1ba290f6a", 73907.0, 262144.0),
+    "dgrad": (_GEMM_SRC, "722628b1ba290f6a", 73860.1, 65536.0),
+    "wgrad": (_GEMM_SRC, "722628b1ba290f6a", 73860.1, 65536.0),
+    "quant_x": (_QUANT_SRC, "695bd45a80b0e05d", 16502.2, 28802.5),
+    "quant_w": (_QUANT_SRC, "695bd45a80b0e05d", 16502.2, 28802.5),
+    "quant_dy": (_QUANT_SRC, "695bd45a80b0e05d", 65698.6, 116835.2),
 }
 
 
@@ -475,6 +472,8 @@ def main():
         kernels["quant_" + k] = {"ms": round(per["quant_" + k], 4),
                                  "GB/s": round(b / per["quant_" + k] / 1e6, 1),
                                  "frac_hbm_peak": round(b / per["quant_" + k] / 1e6 / HBM_PEAK_GBPS, 4)}
+    for k in kernels:   # HBM bytes per launch as last counted (null if the kernel changed)
+        kernels[k]["traffic_B"] = measured_traffic(k, args.grid)
     gemm_ms = sum(per[k] for k in wl.flops)
     quant_ms = sum(per["quant_" + k] for k in qbytes)
     total_flops = sum(wl.flops.values())
@@ -494,6 +493,7 @@ def main():
     value = total_flops / (ms_step * 1e-3) / 1e12
 
     wl_m, wl_k, wl_n = wl.M, wl.K, wl.N
+    qbpe = next(iter(wl.qbpe.values()))
     mx = None
     if not args.no_mx:
         del wl   # free the step's buffers first
@@ -528,7 +528,7 @@ def main():
                    "streams": args.streams, "dual_axis_quant": bool(args.dual)},
         "roofline": roof,
         "quant": {"GB/s": round(quant_gbps, 1), "frac_hbm_peak": round(quant_gbps / HBM_PEAK_GBPS, 4),
-                  "ms": round(quant_ms, 4), "bytes_per_elem": next(iter(wl.qbpe.values()))},
+                  "ms": round(quant_ms, 4), "bytes_per_elem": qbpe},
         "gemm": {"TFLOP/s": round(total_flops / gemm_ms / 1e9, 2),
                  "frac_bf16_peak": round(total_flops / gemm_ms / 1e9 / BF16_PEAK_TFLOPS, 4),
                  "frac_fp4_peak": round(total_flops / gemm_ms / 1e9 / FP4_PEAK_TFLOPS, 4),
