@@ -84,6 +84,8 @@ def parse():
     p.add_argument("--dual", type=int, default=1, choices=[0, 1],
                    help="1 (default): each of X, W, dY quantized along both axes by one fused "
                         "call; 0: six single-axis calls (bit-identical outputs)")
+    p.add_argument("--no-moe", action="store_true",
+                   help="skip the grouped (MoE) layer figures")
     p.add_argument("--no-diag", action="store_true",
                    help="skip the quantization diagnostics (level statistics) figures")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -374,6 +376,77 @@ def diagnostics(U, torch, reps=10):
     return out
 
 
+def moe_layers(U, torch, reps=5):
+    """The MoE layers of the grouped configurations (context; not part of the
+    step): 64 experts (Zipf routing, top-6; E1M2, n = 32, 1 x 32 fp32 scales)
+    and 16 experts (uniform top-8; INT4, n = 128, 1 x 16), each as its six
+    quantizations (X_perm, W, dY_perm row-wise; W^T per expert, dY_perm^T and
+    X_perm^T per expert segment) and its three grouped GEMMs.  TFLOP/s count
+    the unpadded token rows; back-to-back launches timed with HIP events."""
+    import workloads
+    out = {}
+    cases = (("moe64_zipf_e1m2_1x32_n32", workloads.config3, U.UFP4_E1M2, 32, 32),
+             ("moe16_share_int4_1x16_n128", workloads.config4, U.UFP4_INT4, 128, 16))
+    for name, mkwl, grid, n, b in cases:
+        wl = mkwl("cuda")
+        X, W, dYp = wl.tensors["X"], wl.tensors["W"], wl.tensors["dY_perm"]
+        off = wl.meta["offsets"].tolist()
+        counts = wl.meta["counts"]
+        E, H, F = wl.meta["experts"], wl.meta["hidden"], wl.meta["ffn"]
+        Xp = workloads.gather_rows(X, wl.meta["gather"].to(X.device))
+        del X
+        sf, sd, sw = wl.meta["sign_seeds"]
+        sr = wl.meta["sr_seed"]
+        mk = lambda seed, rnd, st=0: U.make_cfg(grid, rnd, U.UFP4_SCALE_F32, 1, b, n,  # noqa: E731
+                                                  sign_seed=seed, sr_seed=sr, sr_stream=st)
+        woff = [g * F for g in range(E + 1)]
+        q = {}
+        quant = {
+            "quant_x_row": (lambda: U.ufp4_rht_quant(Xp, 0, mk(sf, U.UFP4_RTNE))[0], Xp.numel()),
+            "quant_w_row": (lambda: U.ufp4_rht_quant(W, 0, mk(sf, U.UFP4_RTNE))[0], W.numel()),
+            "quant_dy_row": (lambda: U.ufp4_rht_quant(dYp, 0, mk(sd, U.UFP4_SR, 0))[0], dYp.numel()),
+            "quant_w_col": (lambda: U.ufp4_rht_quant_segmented(W, woff, mk(sd, U.UFP4_RTNE)), W.numel()),
+            "quant_dy_col": (lambda: U.ufp4_rht_quant_segmented(dYp, off, mk(sw, U.UFP4_SR, 1)), dYp.numel()),
+            "quant_x_col": (lambda: U.ufp4_rht_quant_segmented(Xp, off, mk(sw, U.UFP4_RTNE)), Xp.numel()),
+        }
+        res = {}
+        bpe = 2.0 + 0.5 + 4.0 / b
+
+        def timed(fn):
+            r = fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                r = fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps, r
+
+        for k, (fn, elems) in quant.items():
+            ms, q[k] = timed(fn)
+            res[k] = {"ms": round(ms, 4), "GB/s": round(bpe * elems / ms / 1e6, 1)}
+        tokens = int(sum(int(c) for c in counts))
+        flops = 2.0 * tokens * F * H
+        gemms = {
+            "fprop": lambda: U.ufp4_gemm_fprop_grouped(q["quant_x_row"], q["quant_w_row"], off),
+            "dgrad": lambda: U.ufp4_gemm_dgrad_grouped(q["quant_dy_row"], U.stacked(q["quant_w_col"], E), off),
+            "wgrad": lambda: U.ufp4_gemm_wgrad_grouped(q["quant_dy_col"], q["quant_x_col"], off),
+        }
+        for k, fn in gemms.items():
+            ms, r = timed(fn)
+            del r
+            tf = flops / ms / 1e9
+            res[k] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                      "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+        res["tokens_x_topk"] = tokens
+        res["padded_rows"] = int(off[-1])
+        out[name] = res
+        del wl, Xp, W, dYp, q
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_oracle_baseline(grid):
     """The oracle as it stands on a bounded sample of the same workload: the
     dense step restricted to M' = 6144 tokens and N' = 6144 output features
@@ -496,14 +569,19 @@ def main():
     qbpe = next(iter(wl.qbpe.values()))
     mx = None
     if not args.no_mx:
-        del wl   # free the step's buffers first
+        wl = None   # free the step's buffers first
         torch.cuda.empty_cache()
         mx = mx_gemms(U, torch)
+    moe = None
+    if not args.no_moe:
+        if args.no_mx:
+            wl = None
+            torch.cuda.empty_cache()
+        moe = moe_layers(U, torch)
     diag = None
     if not args.no_diag:
-        if args.no_mx:
-            del wl
-            torch.cuda.empty_cache()
+        wl = None
+        torch.cuda.empty_cache()
         diag = diagnostics(U, torch)
 
     cpu = None
@@ -536,6 +614,7 @@ def main():
         "kernels": kernels,
         "cpu_baseline": cpu,
         "mx_gemms": mx,
+        "moe_layers": moe,
         "diagnostics": diag,
         "wall_s": round(wall, 3),
     }
