@@ -14,18 +14,17 @@
 // hi*hi + hi*lo + lo*hi with v_mfma_f32_32x32x16_bf16 (fp32 accumulate), so
 // the whole K loop stays on the matrix cores and any block shape works.
 //
-// Tiling: 256 x 256 output tile per 256-thread workgroup, one wave per SIMD
-// (2 x 2 waves, each 128 x 128 = 4 x 4 MFMA tiles of 32 x 32, accumulators in
-// AGPRs), K step 32.  Each thread owns one row of A and one row of B per
-// step (32 codes each).  Software pipeline per step i:
-//   - packed codes/scales of step i+2 are fetched into registers;
-//   - the fragments of k-half 1 of step i are read from LDS buffer i&1;
-//   - the 48 MFMAs of k-half 0 run while step i+1's codes are decoded into
-//     LDS buffer (i+1)&1 (the decode VALU is interleaved with the MFMAs);
-//   - one barrier; the fragments of k-half 0 of step i+1 are read;
-//   - the 48 MFMAs of k-half 1 run.
-// The LDS tile is laid out [part][k-chunk of 8][row] x 16 B, so a fragment
-// read is 16 B per lane with consecutive lanes on consecutive rows.
+// This file holds the general kernel, used for every case the specialised
+// kernels do not take (mixed block shapes between the operands, fp32 scales on
+// 32 x 32 blocks, power-of-two scales with K % 128 != 0 or in grouped GEMMs):
+// 256 x 256 output tile per 512-thread workgroup, two waves per SIMD (8 waves
+// of 128 x 64 = 4 x 2 MFMA tiles, 128 accumulators each), K step 32.  Each
+// thread owns one row of one operand per step (waves 0-3: A, 4-7: B): the
+// packed codes and scales of step i+2 are fetched into registers, step i+1 is
+// decoded into the other LDS buffer between the two k-halves of step i, one
+// barrier per step.  The LDS tile is laid out [part][k-chunk of 8][row] x
+// 16 B, so a fragment read is 16 B per lane with consecutive lanes on
+// consecutive rows.
 #include "ufp4_internal.h"
 #include "gemm_epilogue.h"
 
@@ -34,7 +33,6 @@ namespace ufp4 {
 namespace {
 
 constexpr int TM = 256, TN = 256, TK = 32;
-constexpr int kThreads = 256;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -174,23 +172,6 @@ __device__ __forceinline__ void decode_pair(uint32_t ev, uint32_t od, int i, flo
   lo = pk_bf16(r0, r1);
 }
 
-// Whole-chunk decode used outside the K loop (prologue).
-template <int GRID>
-__device__ __forceinline__ void decode16(uint32_t w0, uint32_t w1, float s, const ResidualMasks& rm,
-                                         uint4 (&hi)[2], uint4 (&lo)[2]) {
-  const float su = s * Dec<GRID>::unit;
-  const float nb = -Dec<GRID>::bias * su;
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    uint32_t ev, od, h[4], l[4];
-    decode8<GRID>(c ? w1 : w0, ev, od);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) decode_pair(ev, od, i, su, nb, rm, h[i], l[i]);
-    hi[c] = make_uint4(h[0], h[1], h[2], h[3]);
-    lo[c] = make_uint4(l[0], l[1], l[2], l[3]);
-  }
-}
-
 // Per-thread view of one operand inside the K loop: this thread owns row
 // `row` of the tile and the 32 codes of each K step.  Index arithmetic is done
 // once; the loop only advances pointers.  Rows past the operand re-read a
@@ -275,163 +256,9 @@ __device__ __forceinline__ float finalize_scale(uint32_t raw, float v) {
   return s * v;
 }
 
-struct Frags {
-  bf16x8 ah[4], al[4], bh[4], bl[4];
-};
-
-__device__ __forceinline__ void load_frags(const uint4* buf, int kh, int lane, int wm, int wn,
-                                           Frags& f) {
-  const int chunk = 2 * kh + (lane >> 5);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ra = wm * 128 + i * 32 + (lane & 31);
-    f.ah[i] = __builtin_bit_cast(bf16x8, buf[(0 * kChunks + chunk) * TM + ra]);
-    f.al[i] = __builtin_bit_cast(bf16x8, buf[(1 * kChunks + chunk) * TM + ra]);
-    const int rb = wn * 128 + i * 32 + (lane & 31);
-    f.bh[i] = __builtin_bit_cast(bf16x8, buf[(2 * kChunks + chunk) * TM + rb]);
-    f.bl[i] = __builtin_bit_cast(bf16x8, buf[(3 * kChunks + chunk) * TM + rb]);
-  }
-}
-
-__device__ __forceinline__ void mfma_step(floatx16 (&acc)[4][4], const Frags& f, int m) {
-  const int prod = m / 16, t = m % 16, i = t >> 2, j = t & 3;   // hh, hl, lh
-  const bf16x8 a = prod == 2 ? f.al[i] : f.ah[i];
-  const bf16x8 b = prod == 1 ? f.bl[j] : f.bh[j];
-  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i][j], 0, 0, 0);
-}
-
-// Decode of one thread's two rows (A and B) of a K step into an LDS buffer:
-// 8 code dwords (A0..A3, B0..B3); dword w -> k-chunk (w & 3) of operand w/4.
-// `unit` 0..39 = 5 units per dword: the byte expansion, then 4 pairs; after
-// the 4th pair the chunk's hi and lo are stored.
-struct DecodeState {
-  uint32_t ev, od;
-  uint32_t h[4], l[4];
-};
-
-template <int GRID, int SMODE>
-__device__ __forceinline__ void decode_unit(int unit, const Fetched& fa, const Fetched& fb,
-                                            const ResidualMasks& rm, DecodeState& ds,
-                                            uint4* buf, int row) {
-  const int w = unit / 5, u = unit % 5;
-  const Fetched& f = (w < 4) ? fa : fb;
-  const int cw = w & 3;
-  const uint32_t word = cw == 0 ? f.c0.x : (cw == 1 ? f.c0.y : (cw == 2 ? f.c1.x : f.c1.y));
-  const float s = cw < 2 ? finalize_scale<SMODE>(f.s0, f.v0) : finalize_scale<SMODE>(f.s1, f.v1);
-  const float su = s * Dec<GRID>::unit;
-  const float nb = -Dec<GRID>::bias * su;
-  if (u == 0) {
-    decode8<GRID>(word, ds.ev, ds.od);
-  } else {
-    const int i = u - 1;
-    decode_pair(ds.ev, ds.od, i, su, nb, rm, ds.h[i], ds.l[i]);
-    if (i == 3) {
-      const int part = (w < 4) ? 0 : 2;
-      buf[(part * kChunks + cw) * TM + row] = make_uint4(ds.h[0], ds.h[1], ds.h[2], ds.h[3]);
-      buf[((part + 1) * kChunks + cw) * TM + row] = make_uint4(ds.l[0], ds.l[1], ds.l[2], ds.l[3]);
-    }
-  }
-}
-
-template <int GRID, int SMODE>
-__global__ __launch_bounds__(kThreads) void k_gemm(GemmLaunch g) {
-  extern __shared__ uint4 lds[];
-  int tm, tn;
-  const Problem pr = resolve(g, blockIdx.x, tm, tn);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;   // 2 x 2 waves
-  const ResidualMasks rm = make_masks();
-
-  const OperandCursor ca = make_cursor(pr.a_codes, pr.a_scales, g.scale_mode, g.a_br, g.a_bc,
-                                       pr.a_row0 + (int64_t)tm * TM + tid,
-                                       pr.a_row0 + pr.a_rows, pr.a_row0, pr.K);
-  const OperandCursor cb = make_cursor(pr.b_codes, pr.b_scales, g.scale_mode, g.b_br, g.b_bc,
-                                       pr.b_row0 + (int64_t)tn * TN + tid,
-                                       pr.b_row0 + pr.b_rows, pr.b_row0, pr.K);
-  const int nsteps = (int)((pr.K + TK - 1) / TK);
-  constexpr int kStage = kParts * kChunks * TM;   // uint4 per LDS buffer
-
-  floatx16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
-
-  // prologue: step 0 decoded into buffer 0, step 1 fetched, k-half 0 frags
-  DecodeState ds;
-  {
-    const Fetched fa = fetch<SMODE>(ca, 0), fb = fetch<SMODE>(cb, 0);
-#pragma unroll
-    for (int u = 0; u < 40; ++u) decode_unit<GRID, SMODE>(u, fa, fb, rm, ds, lds, tid);
-  }
-  Fetched xa = fetch<SMODE>(ca, 1), xb = fetch<SMODE>(cb, 1), ya, yb;
-  __syncthreads();
-  Frags f0, f1;
-  load_frags(lds, 0, lane, wm, wn, f0);
-
-  // One K step: decode (da, db) = step+1 while (la, lb) <- step+2 loads.  The
-  // loop is unrolled by two so the two register sets alternate roles and no
-  // in-flight load result is ever copied.
-  auto body = [&](int step, const Fetched& da, const Fetched& db, Fetched& la, Fetched& lb) {
-    const uint4* cur = lds + (step & 1) * kStage;
-    uint4* nxt = lds + ((step + 1) & 1) * kStage;
-    la = fetch<SMODE>(ca, step + 2);
-    lb = fetch<SMODE>(cb, step + 2);
-    load_frags(cur, 1, lane, wm, wn, f1);
-    // k-half 0: 48 MFMAs with the 40 decode units of step+1 in regions of
-    // eight MFMAs + eight units, alternated MFMA / VALU inside a region so
-    // independent decode chains fill the MFMA shadow
-#pragma unroll
-    for (int m0 = 0; m0 < 48; m0 += 8) {
-#pragma unroll
-      for (int m = m0; m < m0 + 8; ++m) {
-        mfma_step(acc, f0, m);
-        if (m < 40) decode_unit<GRID, SMODE>(m, da, db, rm, ds, nxt, tid);
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);   // then up to nine VALU
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __syncthreads();
-    load_frags(nxt, 0, lane, wm, wn, f0);
-#pragma unroll
-    for (int m = 0; m < 48; ++m) {
-      mfma_step(acc, f1, m);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  int step = 0;
-  for (; step + 1 < nsteps; step += 2) {
-    body(step, xa, xb, ya, yb);
-    body(step + 1, ya, yb, xa, xb);
-  }
-  if (step < nsteps) body(step, xa, xb, ya, yb);
-
-  // Epilogue: lane holds column (lane & 31) and rows 8*(r/4) + 4*(lane/32) + r%4.
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = (int64_t)tn * TN + wn * 128 + j * 32 + (lane & 31);
-      if (col >= pr.b_rows) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = (int64_t)tm * TM + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < pr.a_rows) pr.c[row * g.ldc + col] = acc[i][j][r];
-      }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Two waves per SIMD: 8 waves of 128 x 64 (4 x 2 MFMA tiles, 128 AGPRs each)
-// cover the 256 x 256 tile, and each thread decodes one row of one operand
-// per step (waves 0-3: A, 4-7: B).  With two waves resident on every SIMD the
-// hardware issues one wave's decode VALU while the other wave's MFMAs run,
-// instead of relying on the instruction order inside a single wave.
+// The kernel.  With two waves resident on every SIMD the hardware issues one
+// wave's decode VALU while the other wave's MFMAs run.
 // ---------------------------------------------------------------------------
 constexpr int kThreads8 = 512;
 

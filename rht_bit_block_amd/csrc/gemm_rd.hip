@@ -13,15 +13,16 @@
 // hi*hi + hi*lo + lo*hi with v_mfma_f32_32x32x16_bf16.  The dropped lo*lo term
 // and the rounding of lo leave about 2^-16 relative error per product.
 //
-// Data flow (this kernel): the packed codes and the fp32 scales are copied
-// HBM -> LDS untouched by buffer_load ... lds (four threads per row, so a
-// wave load covers 16 rows x 64 contiguous bytes), three stages of 128 K
-// elements deep.  Each wave then reads, for every 16-wide k-half, the code
-// dword and the scale of each of its 4 A and 4 B MFMA row tiles and decodes
-// them in registers straight into MFMA fragments: there is no decoded copy
-// in LDS and one barrier per 128 K elements.  The decode of k-half j+1 is
-// interleaved with the 48 MFMAs of k-half j inside the wave, whose VALU work
-// runs in the shadow of the matrix core.
+// Data flow (this kernel, 1 x 16 or 1 x 32 fp32-scale blocks): the packed
+// codes and the fp32 scales are copied HBM -> LDS untouched by buffer_load ...
+// lds (M0-based direct loads; four lanes per 64-byte code row, chunks
+// XOR-swizzled), two raw stages of 128 K elements.  Each thread decodes one A
+// row and one B row per 16-wide K step into a decoded double buffer
+// [A_hi, A_lo, B_hi, B_lo][8-element half][row] x 16 B (32 KiB each), so
+// every element is decoded once per tile; the waves read their MFMA fragments
+// from it.  Step i: 24 MFMAs with the decode of step i+1 interleaved (one
+// MFMA, then up to 8 VALU), one barrier, the fragment reads of step i+1, the
+// other 24 MFMAs.
 //
 // Tiling: 256 x 256 output tile per 256-thread workgroup, 2 x 2 waves of
 // 128 x 128 (4 x 4 tiles of 32 x 32, accumulators in AGPRs).  Dense launches
