@@ -277,3 +277,26 @@ def test_config5_square_blocks(grid):
     ox_strip = O.quantize(host_bits(X[:, 32 * cstrip:32 * cstrip + 32]), 0, spec_of(cx),
                           col_index=ccols, K_total=K)
     assert_gemm(dW, rrows, ccols, deq(ody_strip, cdy).T, deq(ox_strip, cx).T, "wgrad")
+
+
+# ---------------------------------------------------------------------------
+def test_config2_mxfp8():
+    """The dense layer's FPROP in MXFP8 (E4M3, 1 x 32 E8M0) at full size:
+    sampled rows of both operands bit-exact, sampled outputs within 1e-4."""
+    _case("config2 mxfp8")
+    wl = workloads.config2("cuda")
+    X, W = wl.tensors["X"], wl.tensors["W"]
+    M, K = X.shape
+    N = W.shape[0]
+    cfg = U.make_cfg(U.UFP4_E4M3, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 16,
+                     sign_seed=wl.meta["sign_seeds"][0])
+    qx, _ = U.ufp4_rht_quant(X, 0, cfg)
+    qw, _ = U.ufp4_rht_quant(W, 0, cfg)
+    Y = U.ufp4_gemm_fprop(qx, qw)
+    torch.cuda.synchronize()
+    rM, rN = pick(M, 24, 41), pick(N, 24, 42)
+    ox = O.quantize(rows_bits(X, rM), 0, spec_of(cfg), row_index=rM)
+    ow = O.quantize(rows_bits(W, rN), 0, spec_of(cfg), row_index=rN)
+    assert_quant_rows(qx.codes, qx.scales, ox, rM, "X row (MXFP8)")
+    assert_quant_rows(qw.codes, qw.scales, ow, rN, "W row (MXFP8)")
+    assert_gemm(Y, rM, rN, deq(ox, cfg), deq(ow, cfg), "fprop (MXFP8)")

@@ -466,3 +466,34 @@ def test_gemm_mxfp8_unsupported_k():
     with pytest.raises(U.UFP4Error) as ei:
         U.ufp4_gemm_fprop(qa, qb)
     assert ei.value.status == U.UFP4_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# Output leading dimension: C written into a wider buffer (ldc > P_B) by every
+# kernel family; the columns past P_B keep their sentinel.
+# ---------------------------------------------------------------------------
+LDC_CASES = [
+    ("split-bf16 1x16", U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=3), 384),
+    ("split-bf16 1x32", U.make_cfg(U.UFP4_INT4, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 32, 32, sign_seed=3), 384),
+    ("scaled FP4 K%256", U.make_cfg(U.UFP4_E2M1, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 1), 512),
+    ("scaled FP4 K%128", U.make_cfg(U.UFP4_E2M1, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 1), 384),
+    ("scaled FP8 E1M2", U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 1), 384),
+    ("MXFP8", U.make_cfg(U.UFP4_E4M3, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 1), 384),
+    ("general (pow2, K%128 != 0)", U.make_cfg(U.UFP4_E2M1, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 1), 160),
+]
+
+
+@pytest.mark.parametrize("name,cfg,K", LDC_CASES, ids=[c[0] for c in LDC_CASES])
+def test_gemm_output_leading_dimension(name, cfg, K):
+    _print_case("ldc", name, K)
+    PA, PB, pad = 300, 270, 50
+    ta, tb = rand_bits(PA, K, 61), rand_bits(PB, K, 62)
+    qa, ra = compare_quant(ta, 0, cfg, with_rotated=False)
+    qb, rb = compare_quant(tb, 0, cfg, with_rotated=False)
+    buf = torch.full((PA, PB + pad), 12345.0, dtype=torch.float32, device="cuda")
+    C = U.ufp4_gemm_fprop(qa, qb, out=buf[:, :PB])
+    assert C.stride(0) == PB + pad
+    host = buf.cpu().numpy()
+    assert np.all(host[:, PB:] == 12345.0)
+    ref = O.gemm_ref(oracle_dequant64(ra, cfg), oracle_dequant64(rb, cfg))
+    assert O.rel_fro(host[:, :PB], ref) <= GEMM_TOL
