@@ -597,7 +597,7 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": args.grid,
-        "dtype_detail": "bf16 in; fp32 rotate/scale/round; 4-bit codes; split-bf16 MFMA, fp32 accumulate",
+        "dtype_detail": "bf16 in; fp32 rotate/scale/round; 4-bit codes; GEMM: exact E4M3 level products (fp8 MFMA) x bf16 scale products (bf16 MFMA), fp32 fma accumulate",
         "data": "synthetic (seeded torch generators; dense linear-layer tensors)",
         "config": {"workload": f"dense linear layer M={wl_m} K={wl_k} N={wl_n}: "
                                + ("3 dual-axis fused RHT(n=16)+1x16 " if args.dual else "6 fused RHT(n=16)+1x16 ")

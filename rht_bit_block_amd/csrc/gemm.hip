@@ -6,13 +6,13 @@
 // [2DFP4] = "Stable FP4 Training via Transposition-Invariant Block
 // Quantization" (root cause: dX = dY W, dW = dY^T X).
 //
-// Scheme ("split-bf16"): the fp32 block scales are not powers of two, so the
-// matrix cores cannot apply them and a per-block fp32 epilogue would leave the
-// VALU as the bottleneck.  Instead every operand element is dequantized on the
-// fly to d = RN(level * s) (the oracle's fp32 dequant value) and split into
-// bf16 hi + lo (d - hi - lo = O(2^-17 d)); the product is accumulated as
-// hi*hi + hi*lo + lo*hi with v_mfma_f32_32x32x16_bf16 (fp32 accumulate), so
-// the whole K loop stays on the matrix cores and any block shape works.
+// Scheme of this general kernel ("split-bf16"): every operand element is
+// dequantized on the fly to d = RN(level * s) (the oracle's fp32 dequant
+// value) and split into bf16 hi + lo (d - hi - lo = O(2^-17 d)); the product
+// is accumulated as hi*hi + hi*lo + lo*hi with v_mfma_f32_32x32x16_bf16 (fp32
+// accumulate), so the whole K loop stays on the matrix cores and any pair of
+// block shapes works.  1 x 16 and 1 x 32 fp32-scale operands go to the
+// scale-product kernel instead (exact level products, fp32 scale epilogue).
 //
 // This file holds the general kernel, used for every case the specialised
 // kernels do not take (mixed block shapes between the operands, fp32 scales on

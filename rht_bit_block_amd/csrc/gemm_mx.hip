@@ -19,7 +19,7 @@
 //         rate).  The scale bytes are used unchanged in both cases.
 // Both operands must have 32-element K blocks (2D 32 x 32 blocks, or 1 x 32
 // rows) and K % 128 == 0; the dispatcher sends anything else to the
-// split-bf16 kernel.
+// general split-bf16 kernel.
 //
 // Operand layout inside the instruction (verified against a host model):
 //   FP4: lane l holds row l % 32 and K elements 32 (l / 32) .. +31 of the

@@ -1,34 +1,41 @@
 // Block-scaled 4-bit GEMM with fp32 block scales (1 x 16 or 1 x 32 blocks):
-// C[p][q] = sum_k A[p][k] * B[q][k], the products of the dequantized
-// operands accumulated in fp32 on the bf16 matrix cores.
+// C[p][q] = sum_k dA[p][k] * dB[q][k], d = level * s, accumulated in fp32.
 //
 // [UFP4] = "Rethinking Shrinkage Bias in FP4 Pretraining of LLMs ... the UFP4
 // Recipe" (hyper.ai summary: formats and blockwise quantization -- a block's
 // elements are its scale times a codebook level; Method: both GEMM operands
 // are quantized in the rotated basis and contracted directly).
 //
-// Arithmetic ("split-bf16"): every operand element is dequantized to the
-// oracle's fp32 value d = RN(level * s), split into bf16 hi = RN(d) and
-// lo = RN(d - hi) (the residual d - hi is exact), and C accumulates
-// hi*hi + hi*lo + lo*hi with v_mfma_f32_32x32x16_bf16.  The dropped lo*lo term
-// and the rounding of lo leave about 2^-16 relative error per product.
+// Arithmetic ("scale product").  Inside one 16-wide K step every element of
+// a row shares one block scale, so
+//   sum_k dA[p][k] dB[q][k] = (sA[p] sB[q]) * sum_k lA[p][k] lB[q][k].
+// The level dot products P come from v_mfma_f32_32x32x16_fp8_fp8 on the
+// levels as E4M3 bytes: every level of the three codebooks is an E4M3 number,
+// so P is exact in fp32.  The scale products S come from a second MFMA,
+// v_mfma_f32_32x32x16_bf16, on bf16 pieces of the scales: s = s0 + s1 + s2
+// exactly (s0 = bf16(s), s1 = bf16(s - s0), s2 = s - s0 - s1), and the K
+// slots pair six of the nine cross products (all but s1 t2, s2 t1, s2 t2,
+// each below 2^-25 of s t).  C += P * S is one fp32 fma per element.  The
+// result differs from the exact one by fp32 rounding only (a few 2^-24
+// relative per step).
 //
-// Data flow (this kernel, 1 x 16 or 1 x 32 fp32-scale blocks): the packed
-// codes and the fp32 scales are copied HBM -> LDS untouched by buffer_load ...
-// lds (M0-based direct loads; four lanes per 64-byte code row, chunks
-// XOR-swizzled), two raw stages of 128 K elements.  Each thread decodes one A
-// row and one B row per 16-wide K step into a decoded double buffer
-// [A_hi, A_lo, B_hi, B_lo][8-element half][row] x 16 B (32 KiB each), so
-// every element is decoded once per tile; the waves read their MFMA fragments
-// from it.  Step i: 24 MFMAs with the decode of step i+1 interleaved (one
-// MFMA, then up to 8 VALU), one barrier, the fragment reads of step i+1, the
-// other 24 MFMAs.
+// Both MFMAs take fresh accumulators and are independent, and the 16 fmas of
+// a tile run on the vector ALU alongside the next tile's MFMAs, so a step
+// costs about two MFMAs per 32 x 32 tile.
 //
-// Tiling: 256 x 256 output tile per 256-thread workgroup, 2 x 2 waves of
-// 128 x 128 (4 x 4 tiles of 32 x 32, accumulators in AGPRs).  Dense launches
+// Data flow: the packed codes and the fp32 scales are copied HBM -> LDS
+// untouched by buffer_load ... lds (M0-based direct loads; four lanes per
+// 64-byte code row, chunks XOR-swizzled), two raw stages of 128 K elements.
+// Per 16-wide K step, each of the 512 threads turns one A or B row into
+// 2 x 16 bytes of a decoded double buffer [op][K half][row]: the row's eight
+// E4M3 levels of that half and its four bf16 scale pieces.  Within a step the
+// order of the K elements does not change the sum, so a half holds the even
+// elements then the odd ones, the same for A and B.
+//
+// Tiling: 256 x 256 output tile per 512-thread workgroup, 2 x 4 waves of
+// 128 x 64 (4 x 2 tiles of 32 x 32, accumulators in VGPRs).  Dense launches
 // order tiles so that the tiles resident at once on an XCD share operand
-// strips in its L2.  K need only be a multiple of 16: k-blocks past K get a
-// zero scale, and rows past the operand read as zeros (buffer bound).
+// strips in its L2.  Rows past the operand read as zeros (buffer bound).
 #include "ufp4_internal.h"
 #include "gemm_epilogue.h"
 
@@ -37,52 +44,48 @@ namespace ufp4 {
 namespace {
 
 constexpr int TM = 256, TN = 256, KST = 128;   // tile, K elements per LDS stage
-constexpr int kThreads = 256, NRAW = 2;
+constexpr int kThreads = 512, NRAW = 2;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef int sgpr4 __attribute__((ext_vector_type(4)));
 
-// --- codebook decode -------------------------------------------------------
-// Codes become offset-binary bytes u with level = (u - bias) * unit, bias a
-// power of two so that -bias * s * unit is exact:
-//   INT4 (two's complement nibble):  u = c ^ 8                    (bias 8)
-//   E1M2 (sign-magnitude, unit 1/4): u = 8 + k or 8 - k           (bias 8)
-//   E2M1 (sign-magnitude, unit 1/2): u = 16 +- {0,1,2,3,4,6,8,12} (bias 16)
-// and d = fma(u, s*unit, -bias*s*unit) = RN(level * s).
-template <int GRID> struct Dec;
-template <> struct Dec<0> { static constexpr float unit = 0.25f, bias = 8.0f; };
-template <> struct Dec<1> { static constexpr float unit = 1.0f, bias = 8.0f; };
-template <> struct Dec<2> { static constexpr float unit = 0.5f, bias = 16.0f; };
+// --- codes -> E4M3 levels ------------------------------------------------------
+// E4M3 bytes of the codebook magnitudes 0..7 (byte i = magnitude index i):
+//   E1M2 levels k/4:                 0, .25, .5, .75, 1, 1.25, 1.5, 1.75
+//   E2M1 levels:                     0, .5, 1, 1.5, 2, 3, 4, 6
+// and for INT4 (two's complement) the values of nibbles 0..7 and 8..15:
+//   0..7 and -8..-1.
+template <int GRID> struct Lut;
+template <> struct Lut<0> { static constexpr uint32_t lo = 0x34302800u, hi = 0x3E3C3A38u; };
+template <> struct Lut<2> { static constexpr uint32_t lo = 0x3C383000u, hi = 0x4C484440u; };
+template <> struct Lut<1> {
+  static constexpr uint32_t lo = 0x44403800u, hi = 0x4E4C4A48u;     // 0..7
+  static constexpr uint32_t nlo = 0xCACCCED0u, nhi = 0xB8C0C4C8u;   // -8..-1
+};
 
-// 8 code nibbles (element j at bits 4j) -> offset-binary bytes of elements
-// 0, 2, 4, 6 (ev) and 1, 3, 5, 7 (od).
+// Nibbles in the low half of each byte of v (bit 3 the sign or the INT4
+// high bit) -> E4M3 bytes.
 template <int GRID>
-__device__ __forceinline__ void decode8(uint32_t w, uint32_t& ev, uint32_t& od) {
+__device__ __forceinline__ uint32_t nib_to_e4m3(uint32_t v) {
+  const uint32_t m = v & 0x07070707u;
+  const uint32_t pos = __builtin_amdgcn_perm(Lut<GRID>::hi, Lut<GRID>::lo, m);
   if constexpr (GRID == 1) {
-    const uint32_t x = w ^ 0x88888888u;
-    ev = x & 0x0F0F0F0Fu;
-    od = (x >> 4) & 0x0F0F0F0Fu;
-  } else if constexpr (GRID == 0) {
-    const uint32_t sgn = w & 0x88888888u;
-    const uint32_t neg7 = sgn - (sgn >> 3);   // 7 in the negative nibbles
-    const uint32_t x = ((w & 0x77777777u) ^ neg7) + (0x88888888u - neg7);
-    ev = x & 0x0F0F0F0Fu;
-    od = (x >> 4) & 0x0F0F0F0Fu;
+    const uint32_t neg = __builtin_amdgcn_perm(Lut<1>::nhi, Lut<1>::nlo, m);
+    const uint32_t b = (v >> 3) & 0x01010101u;
+    const uint32_t sel = (b << 8) - b;   // 0xFF in the bytes of negative nibbles
+    return (neg & sel) | (pos & ~sel);
   } else {
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-    auto map = [](uint32_t v) {
-      const uint32_t idx = v & 0x07070707u;
-      const uint32_t pos = __builtin_amdgcn_perm(0x1C181614u, 0x13121110u, idx);
-      const uint32_t neg = __builtin_amdgcn_perm(0x04080A0Cu, 0x0D0E0F10u, idx);
-      const uint32_t b = (v >> 3) & 0x01010101u;
-      const uint32_t m = (b << 8) - b;   // 0xFF in negative bytes
-      return (neg & m) | (pos & ~m);
-    };
-    ev = map(lo);
-    od = map(hi);
+    return pos | ((v & 0x08080808u) << 4);
   }
+}
+
+// 8 code nibbles (element j at bits 4j) -> {E4M3 of elements 0, 2, 4, 6;
+// E4M3 of elements 1, 3, 5, 7}.
+template <int GRID>
+__device__ __forceinline__ uint2 levels8(uint32_t w) {
+  return make_uint2(nib_to_e4m3<GRID>(w & 0x0F0F0F0Fu), nib_to_e4m3<GRID>((w >> 4) & 0x0F0F0F0Fu));
 }
 
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
@@ -90,41 +93,21 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Selector pairs (-1, 0) and (0, -1) for the exact residual dot products,
-// kept in registers (as packed bf16 they must not become inline constants).
-struct ResidualMasks {
-  bf16x2 m0, m1;
-};
-__device__ __forceinline__ ResidualMasks make_masks() {
-  uint32_t a = 0x0000BF80u, b = 0xBF800000u;
-  asm volatile("" : "+s"(a), "+s"(b));
-  return {__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b)};
-}
-
-// One MFMA fragment: 8 consecutive elements (one code dword) with scale s
-// -> bf16 hi and lo.
-template <int GRID>
-__device__ __forceinline__ void decode_frag(uint32_t w, float s, const ResidualMasks& rm,
-                                            bf16x8& hi, bf16x8& lo) {
-  const float su = s * Dec<GRID>::unit;
-  const float nb = -Dec<GRID>::bias * su;
-  uint32_t ev, od, h[4], l[4];
-  decode8<GRID>(w, ev, od);
-  // opaque to the compiler, so each byte converts with one v_cvt_f32_ubyteN
-  // instead of a bit-field extract plus a conversion
-  asm("" : "+v"(ev), "+v"(od));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float d0 = __fmaf_rn((float)((ev >> (8 * i)) & 0xFFu), su, nb);
-    const float d1 = __fmaf_rn((float)((od >> (8 * i)) & 0xFFu), su, nb);
-    h[i] = pk_bf16(d0, d1);
-    const bf16x2 hh = __builtin_bit_cast(bf16x2, h[i]);
-    const float r0 = __builtin_amdgcn_fdot2_f32_bf16(hh, rm.m0, d0, false);   // d0 - hi0
-    const float r1 = __builtin_amdgcn_fdot2_f32_bf16(hh, rm.m1, d1, false);   // d1 - hi1
-    l[i] = pk_bf16(r0, r1);
-  }
-  hi = __builtin_bit_cast(bf16x8, make_uint4(h[0], h[1], h[2], h[3]));
-  lo = __builtin_bit_cast(bf16x8, make_uint4(l[0], l[1], l[2], l[3]));
+// bf16 pieces of a block scale for the scale-product MFMA: s = s0 + s1 + s2
+// (each rounding leaves an exact fp32 residual).  K slots 0..7 (lower lane
+// half; the upper half is zero), A side x B side:
+//   A: s0 s0 s0 s1 s1 s2 0 0        B: t0 t1 t2 t0 t1 t0 0 0
+// sum = s0 (t0 + t1 + t2) + s1 (t0 + t1) + s2 t0.
+template <int OP>
+__device__ __forceinline__ uint4 scale_pieces(float s) {
+  const uint32_t p00 = pk_bf16(s, s);
+  const float r1 = s - __uint_as_float(p00 << 16);
+  const uint32_t p11 = pk_bf16(r1, r1);
+  const float r2 = r1 - __uint_as_float(p11 << 16);
+  if constexpr (OP == 0)
+    return make_uint4(p00, __builtin_amdgcn_perm(p11, p00, 0x05040100u), pk_bf16(r1, r2), 0u);
+  else
+    return make_uint4(pk_bf16(s, r1), pk_bf16(r2, s), pk_bf16(r1, s), 0u);
 }
 
 // --- direct HBM -> LDS loads -----------------------------------------------
@@ -161,22 +144,26 @@ __device__ __forceinline__ uint32_t code_off(int row, int c) {
 }
 
 template <int BC> struct Layout {
-  static constexpr int SB = (KST / BC) * 4;                // scale bytes per row per stage
-  static constexpr int CODES = 2 * TM * 64;                // A then B
+  static constexpr int SB = (KST / BC) * 4;       // scale bytes per row per stage
+  static constexpr int CODES = 2 * TM * 64;       // A then B
   static constexpr int SCALES = 2 * TM * SB;
-  static constexpr int RAW = CODES + SCALES;               // one raw stage
-  static constexpr int SCALE_LOADS = TM * SB / 1024;       // wave loads per operand
-  static constexpr int VMEM = 2 * 4 + 2 * SCALE_LOADS / 4;  // loads per wave per raw stage
-  // decoded buffer: [A_hi, A_lo, B_hi, B_lo][8-element half][row] x 16 B
-  static constexpr int HL = 4 * 2 * TM * 16;               // 32 KiB
-  static constexpr int TOTAL = NRAW * RAW + 2 * HL;
+  static constexpr int RAW = CODES + SCALES;      // one raw stage
+  static constexpr int SLOADS = SCALES / 1024;    // 1 KiB wave loads of scales
+  static constexpr int SPW = SLOADS / 8;          // per wave
+  static constexpr int VMEM = 4 + SPW;            // loads per wave per raw stage
+  // decoded buffer: levels [op][K half][row] x 8 E4M3, then scale pieces
+  // [op][row] x 8 bf16, then one zero 16-byte slot (read by the upper lane half)
+  static constexpr int LEV = 2 * 2 * TM * 8;
+  static constexpr int PCS = 2 * TM * 16;
+  static constexpr int DEC = LEV + PCS + 16;
+  static constexpr int TOTAL = NRAW * RAW + 2 * DEC;
 };
 
 struct RdCtx {
   sgpr4 ra, rb, rsa, rsb;
   uint32_t lds0;
-  uint32_t code_voff[4];     // wave load q: row * (K/2) + 16 * chunk
-  uint32_t scale_voff[2];    // wave load q of the scales
+  uint32_t code_voff[2];     // wave code load q: row * (K/2) + 16 * chunk
+  uint32_t scale_voff[2];    // wave scale load q
   int wave, nst;
 };
 
@@ -187,81 +174,59 @@ __device__ __forceinline__ void issue_stage(const RdCtx& c, int stage, int slot)
   const uint32_t base = c.lds0 + (uint32_t)slot * L::RAW;
   const uint32_t koff = (uint32_t)s * 64u;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t blk = (uint32_t)(c.wave * 4 + q) * 1024u;   // 16 rows x 64 B
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t blk = (uint32_t)(c.wave * 2 + q) * 1024u;   // 16 rows x 64 B
     lds_load16(base + blk, c.ra, c.code_voff[q], koff);
     lds_load16(base + TM * 64 + blk, c.rb, c.code_voff[q], koff);
   }
   const uint32_t soff = (uint32_t)s * L::SB;
 #pragma unroll
-  for (int q = 0; q < L::SCALE_LOADS / 4; ++q) {
-    const uint32_t blk = (uint32_t)(c.wave * (L::SCALE_LOADS / 4) + q) * 1024u;
-    lds_load16(base + L::CODES + blk, c.rsa, c.scale_voff[q], soff);
-    lds_load16(base + L::CODES + TM * L::SB + blk, c.rsb, c.scale_voff[q], soff);
+  for (int q = 0; q < L::SPW; ++q) {
+    const int g = c.wave + 8 * q;                 // scale wave load, A loads first
+    const bool is_b = g >= L::SLOADS / 2;
+    lds_load16(base + L::CODES + (uint32_t)g * 1024u, is_b ? c.rsb : c.rsa, c.scale_voff[q], soff);
   }
 }
 
-// Raw inputs of one row of operand `op` (0 A, 1 B) for 16-wide K step j
-// (0..7) of the raw stage at `raw`: two code dwords (elements 16 j .. +15)
-// and the block scale (zero past K).
-struct RawRow {
-  uint2 w;
-  float s;
-};
-
-template <int BC>
-__device__ __forceinline__ RawRow read_row(const uint8_t* raw, int op, int row, int j,
-                                           bool valid) {
+// Decode thread t's row (operand t / 256) of 16-wide K step j (0..7) of the raw
+// stage at `raw` into the decoded buffer `dec`; s_valid false: zero scale.
+template <int GRID, int BC, int OP>
+__device__ __forceinline__ void decode_row(const uint8_t* raw, uint8_t* dec, int row, int j,
+                                           bool s_valid) {
   using L = Layout<BC>;
-  RawRow r;
-  r.w = *reinterpret_cast<const uint2*>(raw + op * TM * 64 + code_off(row, j >> 1) + 8 * (j & 1));
-  const float sc = *reinterpret_cast<const float*>(raw + L::CODES + op * TM * L::SB + row * L::SB +
+  const uint2 w = *reinterpret_cast<const uint2*>(raw + OP * TM * 64 + code_off(row, j >> 1) +
+                                                  8 * (j & 1));
+  const float sc = *reinterpret_cast<const float*>(raw + L::CODES + OP * TM * L::SB + row * L::SB +
                                                    4 * ((j * 16) / BC));
-  r.s = valid ? sc : 0.0f;
-  return r;
-}
-
-// Decode half `hf` (8 elements) of a raw row into the decoded buffer `hl`.
-template <int GRID>
-__device__ __forceinline__ void decode_half(const RawRow& r, uint8_t* hl, int op, int row, int hf,
-                                            const ResidualMasks& rm) {
-  bf16x8 hi, lo;
-  decode_frag<GRID>(hf ? r.w.y : r.w.x, r.s, rm, hi, lo);
-  uint8_t* base = hl + op * 2 * (2 * TM * 16);
-  *reinterpret_cast<bf16x8*>(base + (hf * TM + row) * 16) = hi;
-  *reinterpret_cast<bf16x8*>(base + ((2 + hf) * TM + row) * 16) = lo;
+  *reinterpret_cast<uint2*>(dec + ((OP * 2 + 0) * TM + row) * 8) = levels8<GRID>(w.x);
+  *reinterpret_cast<uint2*>(dec + ((OP * 2 + 1) * TM + row) * 8) = levels8<GRID>(w.y);
+  *reinterpret_cast<uint4*>(dec + L::LEV + (OP * TM + row) * 16) = scale_pieces<OP>(s_valid ? sc : 0.0f);
 }
 
 template <int GRID, int BC>
-__device__ __forceinline__ void decode_row(const uint8_t* raw, uint8_t* hl, int op, int row,
-                                           int j, bool valid, const ResidualMasks& rm) {
-  const RawRow r = read_row<BC>(raw, op, row, j, valid);
-  decode_half<GRID>(r, hl, op, row, 0, rm);
-  decode_half<GRID>(r, hl, op, row, 1, rm);
+__device__ __forceinline__ void decode_step(const uint8_t* raw, uint8_t* dec, int tid, int j,
+                                            bool s_valid) {
+  if (tid < TM) decode_row<GRID, BC, 0>(raw, dec, tid, j, s_valid);
+  else decode_row<GRID, BC, 1>(raw, dec, tid - TM, j, s_valid);
 }
 
-struct Frags {
-  bf16x8 ah[4], al[4], bh[4], bl[4];
+struct Frag {
+  long code;      // 8 E4M3 levels
+  bf16x8 pc;      // scale pieces (lower lane half) or zeros (upper half)
 };
 
-__device__ __forceinline__ void load_frags(const uint8_t* hl, int lane, int wm, int wn, Frags& f) {
-  const int h = lane >> 5;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int ra = wm * 128 + t * 32 + (lane & 31);
-    const int rb = wn * 128 + t * 32 + (lane & 31);
-    f.ah[t] = *reinterpret_cast<const bf16x8*>(hl + ((0 + h) * TM + ra) * 16);
-    f.al[t] = *reinterpret_cast<const bf16x8*>(hl + ((2 + h) * TM + ra) * 16);
-    f.bh[t] = *reinterpret_cast<const bf16x8*>(hl + 4 * TM * 16 + ((0 + h) * TM + rb) * 16);
-    f.bl[t] = *reinterpret_cast<const bf16x8*>(hl + 4 * TM * 16 + ((2 + h) * TM + rb) * 16);
-  }
+template <int BC>
+__device__ __forceinline__ Frag read_frag(const uint8_t* dec, int op, int h, int row) {
+  using L = Layout<BC>;
+  Frag f;
+  f.code = *reinterpret_cast<const long*>(dec + ((op * 2 + h) * TM + row) * 8);
+  f.pc = *reinterpret_cast<const bf16x8*>(dec + (h ? L::LEV + L::PCS : L::LEV + (op * TM + row) * 16));
+  return f;
 }
 
-__device__ __forceinline__ void mfma_step(floatx16 (&acc)[4][4], const Frags& f, int m) {
-  const int prod = m >> 4, i = (m >> 2) & 3, j = m & 3;   // hh, hl, lh
-  const bf16x8 a = prod == 2 ? f.al[i] : f.ah[i];
-  const bf16x8 b = prod == 1 ? f.bl[j] : f.bh[j];
-  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i][j], 0, 0, 0);
+__device__ __forceinline__ void mfma_tile(const Frag& a, const Frag& b, floatx16& p, floatx16& q) {
+  p = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a.code, b.code, floatx16{}, 0, 0, 0);
+  q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.pc, b.pc, floatx16{}, 0, 0, 0);
 }
 
 struct Operands {
@@ -322,8 +287,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
     tile_order(blockIdx.x, g.total_tiles, (int)((o.a_rows + TM - 1) / TM),
                (int)((o.b_rows + TN - 1) / TN), tm, tn);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
   const int64_t K = o.K;
   const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
   const int64_t rows_a = o.a_rows - row0 < TM ? o.a_rows - row0 : TM;
@@ -340,81 +306,87 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
   c.rsb = rsrc4(reinterpret_cast<const uint8_t*>(o.b_scales) + col0 * srs, (uint32_t)(rows_b * srs));
   c.lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds;
   {
-    // codes: lane i of wave load q -> row 64 w + 16 q + i / 4, the chunk whose
+    // codes: lane i of wave load q -> row 32 w + 16 q + i / 4, the chunk whose
     // swizzled slot is i % 4
     const int lr = lane >> 2;
     const uint32_t chunk = (uint32_t)((lane & 3) ^ ((lr >> 1) & 3));
 #pragma unroll
-    for (int q = 0; q < 4; ++q) c.code_voff[q] = (uint32_t)(wave * 64 + q * 16 + lr) * rs + 16u * chunk;
-    // scales: a wave load is 1 KiB = 1024 / SB rows; lane i -> row i / (SB/16), part i % (SB/16)
+    for (int q = 0; q < 2; ++q) c.code_voff[q] = (uint32_t)(wave * 32 + q * 16 + lr) * rs + 16u * chunk;
+    // scales: wave load g covers 1024 / SB rows of operand g / (SLOADS/2);
+    // lane i -> row i / (SB/16), part i % (SB/16)
     constexpr int PER = L::SB / 16;
     constexpr int ROWS = 64 / PER;
 #pragma unroll
-    for (int q = 0; q < L::SCALE_LOADS / 4; ++q) {
-      const int row = (wave * (L::SCALE_LOADS / 4) + q) * ROWS + lane / PER;
+    for (int q = 0; q < L::SPW; ++q) {
+      const int g = wave + 8 * q;
+      const int row = (g % (L::SLOADS / 2)) * ROWS + lane / PER;
       c.scale_voff[q] = (uint32_t)row * srs + 16u * (uint32_t)(lane % PER);
     }
   }
-  const ResidualMasks rm = make_masks();
-  uint8_t* hlb = lds + NRAW * L::RAW;   // two decoded buffers
+  uint8_t* decb = lds + NRAW * L::RAW;   // two decoded buffers
 
-  floatx16 acc[4][4];
+  if (tid < 2) *reinterpret_cast<uint4*>(decb + tid * L::DEC + L::LEV + L::PCS) = make_uint4(0, 0, 0, 0);
+
+  floatx16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
+    for (int j = 0; j < 2; ++j) {
+      acc[i][j] = floatx16{};
+      asm volatile("" : "+v"(acc[i][j]));   // no peeled first step
+    }
 
   const int nsteps = (int)(K / 16);
+  const int h = lane >> 5, r32 = lane & 31;
   if (nsteps > 0) {
     issue_stage<BC>(c, 0, 0);
     issue_stage<BC>(c, 1, 1);
     wait_vmcnt<L::VMEM>();
     __syncthreads();
-    decode_row<GRID, BC>(lds, hlb, 0, tid, 0, 0 < nkb, rm);
-    decode_row<GRID, BC>(lds, hlb, 1, tid, 0, 0 < nkb, rm);
+    decode_step<GRID, BC>(lds, decb, tid, 0, 0 < nkb);
     __syncthreads();
-    // Step i (fragments F of step i in registers):
-    //   24 MFMAs of step i, while this thread decodes its A and B rows of
-    //   step i+1 into the other decoded buffer;
-    //   barrier (step i+1 fully decoded; every wave has read step i's buffer);
-    //   fragment reads of step i+1, in flight during the other 24 MFMAs of step i.
-    // Raw stage s (8 steps) is issued at step 8 (s - 1) and waited for two
-    // steps before its first decode.
-    Frags f, fn;
-    load_frags(hlb, lane, wm, wn, f);
+    // Step i: read the fragments of step i; decode step i+1 into the other
+    // buffer (the fragment reads are in flight meanwhile); 8 tiles x (level
+    // MFMA, scale MFMA, 16 fmas); barrier.  Raw stage s (8 steps) is issued at
+    // step 8 (s - 1) and waited for two steps before its first decode.
+#pragma clang loop unroll(disable)
     for (int i = 0; i < nsteps; ++i) {
       if (i > 0 && (i & 7) == 0) issue_stage<BC>(c, (i >> 3) + 1, ((i >> 3) + 1) & 1);
-      const int n = i + 1;                                   // step being decoded
-      const uint8_t* raw = lds + ((n >> 3) & 1) * L::RAW;
-      const bool vn = n < nsteps && (n * 16) / BC < nkb;
-      uint8_t* hn = hlb + (n & 1) * L::HL;
-      const RawRow ra = read_row<BC>(raw, 0, tid, n & 7, vn);
-      const RawRow rb = read_row<BC>(raw, 1, tid, n & 7, vn);
-      // four 8-element decodes, each spread over five MFMAs
+      const uint8_t* dc = decb + (i & 1) * L::DEC;
+      Frag fa[4], fb[2];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
+      for (int t = 0; t < 4; ++t) fa[t] = read_frag<BC>(dc, 0, h, wm * 128 + t * 32 + r32);
 #pragma unroll
-        for (int m = 5 * p; m < 5 * p + 5; ++m) mfma_step(acc, f, m);
-        decode_half<GRID>(p < 2 ? ra : rb, hn, p >> 1, tid, p & 1, rm);
+      for (int t = 0; t < 2; ++t) fb[t] = read_frag<BC>(dc, 1, h, wn * 64 + t * 32 + r32);
+      const int n = i + 1;
+      decode_step<GRID, BC>(lds + ((n >> 3) & 1) * L::RAW, decb + (n & 1) * L::DEC, tid, n & 7,
+                            n < nsteps && (n * 16) / BC < nkb);
+      // tile t = (t / 2, t % 2): the MFMAs of tile t+1 are issued before the
+      // fmas of tile t, so the matrix cores and the vector ALU overlap with
+      // two tiles' products live
+      floatx16 p[2], q[2];
+      mfma_tile(fa[0], fb[0], p[0], q[0]);
 #pragma unroll
-        for (int q = 0; q < 5; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // then up to 8 VALU
+      for (int t = 0; t < 8; ++t) {
+        if (t + 1 < 8) mfma_tile(fa[(t + 1) >> 1], fb[(t + 1) & 1], p[(t + 1) & 1], q[(t + 1) & 1]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[t >> 1][t & 1][r] = __builtin_fmaf(p[t & 1][r], q[t & 1][r], acc[t >> 1][t & 1][r]);
+        asm volatile("" : "+v"(acc[t >> 1][t & 1]));   // the fmas stay here
+        if (t + 1 < 8) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // 8 VALU
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int m = 20; m < 24; ++m) mfma_step(acc, f, m);
       if (((i + 2) & 7) == 0) wait_vmcnt<0>();   // raw stage of step i+2 has landed
       __syncthreads();
-      load_frags(hn, lane, wm, wn, fn);
-#pragma unroll
-      for (int m = 24; m < 48; ++m) mfma_step(acc, f, m);
-      f = fn;
     }
   }
 
-  store_c<4, 4>(o.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
+  store_c<4, 2>(o.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 64,
                 lane, acc);
 }
 

@@ -132,8 +132,9 @@ hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s);
 // Power-of-two (E8M0) scales on the scaled matrix cores; only for launches
 // gemm_mx_supported() accepts.
 bool gemm_mx_supported(const GemmLaunch& g);
-// fp32 scales, 1 x 16 / 1 x 32 blocks: codes staged through LDS, fragments
-// decoded in registers; only for launches gemm_rd_supported() accepts.
+// fp32 scales, 1 x 16 / 1 x 32 blocks: per 16-wide K step, exact level dot
+// products on the fp8 matrix cores times scale products from the bf16 ones;
+// only for launches gemm_rd_supported() accepts.
 bool gemm_rd_supported(const GemmLaunch& g);
 hipError_t launch_gemm_rd(const GemmLaunch& g, hipStream_t s);
 hipError_t launch_gemm_mx(const GemmLaunch& g, hipStream_t s);

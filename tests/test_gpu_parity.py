@@ -473,8 +473,8 @@ def test_gemm_mxfp8_unsupported_k():
 # kernel family; the columns past P_B keep their sentinel.
 # ---------------------------------------------------------------------------
 LDC_CASES = [
-    ("split-bf16 1x16", U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=3), 384),
-    ("split-bf16 1x32", U.make_cfg(U.UFP4_INT4, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 32, 32, sign_seed=3), 384),
+    ("fp32-scale 1x16", U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=3), 384),
+    ("fp32-scale 1x32", U.make_cfg(U.UFP4_INT4, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 32, 32, sign_seed=3), 384),
     ("scaled FP4 K%256", U.make_cfg(U.UFP4_E2M1, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 1), 512),
     ("scaled FP4 K%128", U.make_cfg(U.UFP4_E2M1, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 1), 384),
     ("scaled FP8 E1M2", U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 1), 384),
