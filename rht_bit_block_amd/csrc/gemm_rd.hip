@@ -20,17 +20,25 @@
 // relative per step).
 //
 // Both MFMAs take fresh accumulators and are independent, and the 16 fmas of
-// a tile run on the vector ALU alongside the next tile's MFMAs, so a step
-// costs about two MFMAs per 32 x 32 tile.
+// a tile run on the vector ALU while the next tile's MFMAs execute: a step
+// costs two MFMAs (64 matrix-core cycles) and 16 fmas (64 VALU cycles) per
+// 32 x 32 tile.
 //
 // Data flow: the packed codes and the fp32 scales are copied HBM -> LDS
 // untouched by buffer_load ... lds (M0-based direct loads; four lanes per
 // 64-byte code row, chunks XOR-swizzled), two raw stages of 128 K elements.
-// Per 16-wide K step, each of the 512 threads turns one A or B row into
-// 2 x 16 bytes of a decoded double buffer [op][K half][row]: the row's eight
-// E4M3 levels of that half and its four bf16 scale pieces.  Within a step the
-// order of the K elements does not change the sum, so a half holds the even
-// elements then the odd ones, the same for A and B.
+// Per 16-wide K step, each of the 512 threads turns one A or B row into a
+// decoded double buffer: the row's 16 E4M3 levels, [op][K half][row] x 8 B,
+// and its bf16 scale pieces, [op][row] x 16 B.  Lanes of the upper half read
+// a zero slot for the scale operand.  Within a step the order of the K
+// elements does not change the sum, so a K half holds its even elements then
+// its odd ones, the same for A and B.
+//
+// Pipeline of step i (its fragments in registers): the decode of step i+1
+// during tiles 0-1, one barrier, then the fragments of step i+1 are read as
+// registers free up (B into a second set, each A fragment after its last
+// tile), so the LDS reads of a step are hidden under the tiles of the one
+// before.
 //
 // Tiling: 256 x 256 output tile per 512-thread workgroup, 2 x 4 waves of
 // 128 x 64 (4 x 2 tiles of 32 x 32, accumulators in VGPRs).  Dense launches
@@ -155,7 +163,10 @@ template <int BC> struct Layout {
   // [op][row] x 8 bf16, then one zero 16-byte slot (read by the upper lane half)
   static constexpr int LEV = 2 * 2 * TM * 8;
   static constexpr int PCS = 2 * TM * 16;
-  static constexpr int DEC = LEV + PCS + 16;
+  // zero slots for the upper lane half at ZERO + 512 t, t = 0..3 (the stride
+  // of a 32-row tile of scale pieces, so a fragment address is base + 512 t)
+  static constexpr int ZERO = LEV + PCS;
+  static constexpr int DEC = ZERO + 3 * 512 + 16;
   static constexpr int TOTAL = NRAW * RAW + 2 * DEC;
 };
 
@@ -188,26 +199,31 @@ __device__ __forceinline__ void issue_stage(const RdCtx& c, int stage, int slot)
   }
 }
 
-// Decode thread t's row (operand t / 256) of 16-wide K step j (0..7) of the raw
-// stage at `raw` into the decoded buffer `dec`; s_valid false: zero scale.
-template <int GRID, int BC, int OP>
-__device__ __forceinline__ void decode_row(const uint8_t* raw, uint8_t* dec, int row, int j,
-                                           bool s_valid) {
+// Raw inputs of one row for one 16-wide K step: two code dwords and the scale.
+struct DecIn {
+  uint2 w;
+  float s;
+};
+
+// Row `row` of operand `op` for 16-wide K step j (0..7) of the raw stage `raw`.
+template <int BC>
+__device__ __forceinline__ DecIn decode_load(const uint8_t* raw, int op, int row, int j) {
   using L = Layout<BC>;
-  const uint2 w = *reinterpret_cast<const uint2*>(raw + OP * TM * 64 + code_off(row, j >> 1) +
-                                                  8 * (j & 1));
-  const float sc = *reinterpret_cast<const float*>(raw + L::CODES + OP * TM * L::SB + row * L::SB +
-                                                   4 * ((j * 16) / BC));
-  *reinterpret_cast<uint2*>(dec + ((OP * 2 + 0) * TM + row) * 8) = levels8<GRID>(w.x);
-  *reinterpret_cast<uint2*>(dec + ((OP * 2 + 1) * TM + row) * 8) = levels8<GRID>(w.y);
-  *reinterpret_cast<uint4*>(dec + L::LEV + (OP * TM + row) * 16) = scale_pieces<OP>(s_valid ? sc : 0.0f);
+  DecIn d;
+  d.w = *reinterpret_cast<const uint2*>(raw + op * TM * 64 + code_off(row, j >> 1) + 8 * (j & 1));
+  d.s = *reinterpret_cast<const float*>(raw + L::CODES + op * TM * L::SB + row * L::SB +
+                                        4 * ((j * 16) / BC));
+  return d;
 }
 
+// E4M3 levels and scale pieces of the row into the decoded buffer `dec`.
 template <int GRID, int BC>
-__device__ __forceinline__ void decode_step(const uint8_t* raw, uint8_t* dec, int tid, int j,
-                                            bool s_valid) {
-  if (tid < TM) decode_row<GRID, BC, 0>(raw, dec, tid, j, s_valid);
-  else decode_row<GRID, BC, 1>(raw, dec, tid - TM, j, s_valid);
+__device__ __forceinline__ void decode_store(const DecIn& d, uint8_t* dec, int op, int row) {
+  using L = Layout<BC>;
+  *reinterpret_cast<uint2*>(dec + ((op * 2 + 0) * TM + row) * 8) = levels8<GRID>(d.w.x);
+  *reinterpret_cast<uint2*>(dec + ((op * 2 + 1) * TM + row) * 8) = levels8<GRID>(d.w.y);
+  *reinterpret_cast<uint4*>(dec + L::LEV + (op * TM + row) * 16) =
+      op ? scale_pieces<1>(d.s) : scale_pieces<0>(d.s);
 }
 
 struct Frag {
@@ -215,12 +231,10 @@ struct Frag {
   bf16x8 pc;      // scale pieces (lower lane half) or zeros (upper half)
 };
 
-template <int BC>
-__device__ __forceinline__ Frag read_frag(const uint8_t* dec, int op, int h, int row) {
-  using L = Layout<BC>;
+__device__ __forceinline__ Frag frag_at(const uint8_t* dec, uint32_t code_off, uint32_t pc_off) {
   Frag f;
-  f.code = *reinterpret_cast<const long*>(dec + ((op * 2 + h) * TM + row) * 8);
-  f.pc = *reinterpret_cast<const bf16x8*>(dec + (h ? L::LEV + L::PCS : L::LEV + (op * TM + row) * 16));
+  f.code = *reinterpret_cast<const long*>(dec + code_off);
+  f.pc = *reinterpret_cast<const bf16x8*>(dec + pc_off);
   return f;
 }
 
@@ -294,7 +308,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
   const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
   const int64_t rows_a = o.a_rows - row0 < TM ? o.a_rows - row0 : TM;
   const int64_t rows_b = o.b_rows - col0 < TN ? o.b_rows - col0 : TN;
-  const int nkb = (int)(K / BC);
   const uint32_t rs = (uint32_t)(K / 2), srs = (uint32_t)(K / BC) * 4u;
 
   RdCtx c;
@@ -325,7 +338,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
   }
   uint8_t* decb = lds + NRAW * L::RAW;   // two decoded buffers
 
-  if (tid < 2) *reinterpret_cast<uint4*>(decb + tid * L::DEC + L::LEV + L::PCS) = make_uint4(0, 0, 0, 0);
+  if (tid < 8)
+    *reinterpret_cast<uint4*>(decb + (tid >> 2) * L::DEC + L::ZERO + (tid & 3) * 512) = make_uint4(0, 0, 0, 0);
 
   floatx16 acc[4][2];
 #pragma unroll
@@ -338,32 +352,37 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
 
   const int nsteps = (int)(K / 16);
   const int h = lane >> 5, r32 = lane & 31;
+  const int dop = wave >> 2, drow = tid & (TM - 1);   // the row this thread decodes
+  // fragment offsets in a decoded buffer; tile t adds 256 t (levels), 512 t (pieces)
+  const uint32_t code_a = (uint32_t)(((0 + h) * TM + wm * 128 + r32) * 8);
+  const uint32_t code_b = (uint32_t)(((2 + h) * TM + wn * 64 + r32) * 8);
+  const uint32_t pc_a = h ? (uint32_t)L::ZERO : (uint32_t)(L::LEV + (wm * 128 + r32) * 16);
+  const uint32_t pc_b = h ? (uint32_t)L::ZERO : (uint32_t)(L::LEV + (TM + wn * 64 + r32) * 16);
   if (nsteps > 0) {
     issue_stage<BC>(c, 0, 0);
     issue_stage<BC>(c, 1, 1);
     wait_vmcnt<L::VMEM>();
     __syncthreads();
-    decode_step<GRID, BC>(lds, decb, tid, 0, 0 < nkb);
+    decode_store<GRID, BC>(decode_load<BC>(lds, dop, drow, 0), decb, dop, drow);
     __syncthreads();
-    // Step i: read the fragments of step i; decode step i+1 into the other
-    // buffer (the fragment reads are in flight meanwhile); 8 tiles x (level
-    // MFMA, scale MFMA, 16 fmas); barrier.  Raw stage s (8 steps) is issued at
-    // step 8 (s - 1) and waited for two steps before its first decode.
+    Frag fa[4], fb[2], fbn[2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) fa[t] = frag_at(decb, code_a + 256 * t, pc_a + 512 * t);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) fb[t] = frag_at(decb, code_b + 256 * t, pc_b + 512 * t);
+    // Step i (its fragments in registers): decode step i+1 into the other
+    // buffer during tiles 0-1; barrier; then step i+1's fragments are read as
+    // registers free up (B right after the barrier into a second set, A[t]
+    // after its last tile), hidden under tiles 2-7.  Tile t = (t / 2, t % 2):
+    // the MFMAs of tile t+1 are issued before the fmas of tile t.  Raw stage s
+    // (8 steps) is issued at step 8 (s - 1) and waited for at the barrier of
+    // the step that decodes its first step.
 #pragma clang loop unroll(disable)
     for (int i = 0; i < nsteps; ++i) {
       if (i > 0 && (i & 7) == 0) issue_stage<BC>(c, (i >> 3) + 1, ((i >> 3) + 1) & 1);
-      const uint8_t* dc = decb + (i & 1) * L::DEC;
-      Frag fa[4], fb[2];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) fa[t] = read_frag<BC>(dc, 0, h, wm * 128 + t * 32 + r32);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) fb[t] = read_frag<BC>(dc, 1, h, wn * 64 + t * 32 + r32);
-      const int n = i + 1;
-      decode_step<GRID, BC>(lds + ((n >> 3) & 1) * L::RAW, decb + (n & 1) * L::DEC, tid, n & 7,
-                            n < nsteps && (n * 16) / BC < nkb);
-      // tile t = (t / 2, t % 2): the MFMAs of tile t+1 are issued before the
-      // fmas of tile t, so the matrix cores and the vector ALU overlap with
-      // two tiles' products live
+      const int n = i + 1;   // decoded during this step (past the end: unused)
+      const DecIn din = decode_load<BC>(lds + ((n >> 3) & 1) * L::RAW, dop, drow, n & 7);
+      const uint8_t* dn = decb + (n & 1) * L::DEC;
       floatx16 p[2], q[2];
       mfma_tile(fa[0], fb[0], p[0], q[0]);
 #pragma unroll
@@ -373,16 +392,18 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
         for (int r = 0; r < 16; ++r)
           acc[t >> 1][t & 1][r] = __builtin_fmaf(p[t & 1][r], q[t & 1][r], acc[t >> 1][t & 1][r]);
         asm volatile("" : "+v"(acc[t >> 1][t & 1]));   // the fmas stay here
-        if (t + 1 < 8) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // 8 VALU
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        if (t == 0) decode_store<GRID, BC>(din, decb + (n & 1) * L::DEC, dop, drow);
+        if (t == 1) {
+          if (((i + 2) & 7) == 0) wait_vmcnt<0>();   // raw stage of step i+2 has landed
+          __syncthreads();
+#pragma unroll
+          for (int u = 0; u < 2; ++u) fbn[u] = frag_at(dn, code_b + 256 * u, pc_b + 512 * u);
         }
+        if (t & 1) fa[t >> 1] = frag_at(dn, code_a + 256 * (t >> 1), pc_a + 512 * (t >> 1));
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (((i + 2) & 7) == 0) wait_vmcnt<0>();   // raw stage of step i+2 has landed
-      __syncthreads();
+      fb[0] = fbn[0];
+      fb[1] = fbn[1];
     }
   }
 
