@@ -497,3 +497,40 @@ def test_gemm_output_leading_dimension(name, cfg, K):
     assert np.all(host[:, PB:] == 12345.0)
     ref = O.gemm_ref(oracle_dequant64(ra, cfg), oracle_dequant64(rb, cfg))
     assert O.rel_fro(host[:, :PB], ref) <= GEMM_TOL
+
+
+# ---------------------------------------------------------------------------
+# fp32-scale GEMMs compute the exact sum of level products times scale
+# products, rounded in fp32 only (the level dot products are exact, the scale
+# products come from three-piece bf16 splits): against the oracle's fp64
+# product of its fp32 dequantized operands the error is a few fp32 roundings,
+# far inside the 1e-4 bar.  Rows span 10^+-4 and blocks within a row 10^+-2,
+# so the scale pieces cover a wide exponent range.
+# ---------------------------------------------------------------------------
+F32_SCALE_TOL = 2e-6
+
+
+def _wide_range_bits(rows, cols, seed, bc):
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((rows, cols))
+    a *= 10.0 ** rng.uniform(-4, 4, size=(rows, 1))
+    a *= np.repeat(10.0 ** rng.uniform(-2, 2, size=(rows, cols // bc)), bc, axis=1)
+    a[rng.random((rows, cols)) < 0.01] *= 30.0
+    t = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("bc", [16, 32])
+@pytest.mark.parametrize("rnd", [U.UFP4_RTNE, U.UFP4_SR])
+def test_gemm_fp32_scale_accuracy(grid, bc, rnd):
+    _print_case("fp32-scale gemm accuracy", grid, bc, rnd)
+    PA, PB, K = 290, 300, 512
+    cfg = U.make_cfg(grid, rnd, U.UFP4_SCALE_F32, 1, bc, 16, sign_seed=17, sr_seed=23)
+    qa, ra = compare_quant(_wide_range_bits(PA, K, 100 + grid, bc), 0, cfg, with_rotated=False)
+    qb, rb = compare_quant(_wide_range_bits(PB, K, 200 + grid, bc), 0, cfg, with_rotated=False)
+    C = U.ufp4_gemm_fprop(qa, qb).cpu().numpy()
+    ref = O.gemm_ref(oracle_dequant64(ra, cfg), oracle_dequant64(rb, cfg))
+    err = O.rel_fro(C, ref)
+    print(f"  rel. Frobenius error {err:.3e}", flush=True)
+    assert err <= F32_SCALE_TOL, err
