@@ -160,11 +160,11 @@ template <int BC> struct Layout {
   static constexpr int SPW = SLOADS / 8;          // per wave
   static constexpr int VMEM = 4 + SPW;            // loads per wave per raw stage
   // decoded buffer: levels [op][K half][row] x 8 E4M3, then scale pieces
-  // [op][row] x 8 bf16, then one zero 16-byte slot (read by the upper lane half)
+  // [op][row] x 8 bf16, then the zero slots the upper lane half reads for the
+  // scale operand, at ZERO + 512 t for t = 0..3 (the stride of a 32-row tile of
+  // scale pieces, so every fragment address is a base plus 512 t)
   static constexpr int LEV = 2 * 2 * TM * 8;
   static constexpr int PCS = 2 * TM * 16;
-  // zero slots for the upper lane half at ZERO + 512 t, t = 0..3 (the stride
-  // of a 32-row tile of scale pieces, so a fragment address is base + 512 t)
   static constexpr int ZERO = LEV + PCS;
   static constexpr int DEC = ZERO + 3 * 512 + 16;
   static constexpr int TOTAL = NRAW * RAW + 2 * DEC;
