@@ -425,6 +425,187 @@ hipError_t launch_rd(const GemmLaunch& g, hipStream_t s) {
   return hipGetLastError();
 }
 
+
+// --- 1 x 32 blocks: 32-wide K steps -------------------------------------------
+// One block scale covers 32 K elements, so a step takes two chained level
+// MFMAs (K halves 0-15 and 16-31 of the block), one scale-product MFMA and one
+// set of 16 fmas per tile: half the fmas and three quarters of the MFMAs of
+// two 16-wide steps.  Decoded buffer: levels [op][16-wide half][K half][row] x
+// 8 E4M3, scale pieces [op][row] x 8 bf16, zero slots at ZERO + 512 t.
+struct Layout32 {
+  static constexpr int LEV = 2 * 2 * 2 * TM * 8;
+  static constexpr int PCS = 2 * TM * 16;
+  static constexpr int ZERO = LEV + PCS;
+  static constexpr int DEC = ZERO + 3 * 512 + 16;
+  static constexpr int TOTAL = NRAW * Layout<32>::RAW + 2 * DEC;
+};
+
+// Raw inputs of one row for one 32-wide K step: four code dwords (elements
+// 8 i .. 8 i + 7 in dword i) and the block scale.
+struct DecIn32 {
+  uint4 w;
+  float s;
+};
+
+// Row `row` of operand `op` for 32-wide K step j (0..3) of the raw stage `raw`.
+__device__ __forceinline__ DecIn32 decode_load32(const uint8_t* raw, int op, int row, int j) {
+  using L = Layout<32>;
+  DecIn32 d;
+  d.w = *reinterpret_cast<const uint4*>(raw + op * TM * 64 + code_off(row, j));
+  d.s = *reinterpret_cast<const float*>(raw + L::CODES + op * TM * L::SB + row * L::SB + 4 * j);
+  return d;
+}
+
+template <int GRID>
+__device__ __forceinline__ void decode_store32(const DecIn32& d, uint8_t* dec, int op, int row) {
+  using L = Layout32;
+  *reinterpret_cast<uint2*>(dec + (((op * 2 + 0) * 2 + 0) * TM + row) * 8) = levels8<GRID>(d.w.x);
+  *reinterpret_cast<uint2*>(dec + (((op * 2 + 0) * 2 + 1) * TM + row) * 8) = levels8<GRID>(d.w.y);
+  *reinterpret_cast<uint2*>(dec + (((op * 2 + 1) * 2 + 0) * TM + row) * 8) = levels8<GRID>(d.w.z);
+  *reinterpret_cast<uint2*>(dec + (((op * 2 + 1) * 2 + 1) * TM + row) * 8) = levels8<GRID>(d.w.w);
+  *reinterpret_cast<uint4*>(dec + L::LEV + (op * TM + row) * 16) =
+      op ? scale_pieces<1>(d.s) : scale_pieces<0>(d.s);
+}
+
+struct Frag32 {
+  long c0, c1;    // E4M3 levels of the two 16-wide halves
+  bf16x8 pc;      // scale pieces (lower lane half) or zeros (upper half)
+};
+
+// code_off: the first half's levels; the second half's are 2 TM x 8 bytes on.
+__device__ __forceinline__ Frag32 frag32_at(const uint8_t* dec, uint32_t code_off, uint32_t pc_off) {
+  Frag32 f;
+  f.c0 = *reinterpret_cast<const long*>(dec + code_off);
+  f.c1 = *reinterpret_cast<const long*>(dec + code_off + 2 * TM * 8);
+  f.pc = *reinterpret_cast<const bf16x8*>(dec + pc_off);
+  return f;
+}
+
+template <int GRID>
+__global__ __launch_bounds__(kThreads) void k_gemm_rd32(GemmLaunch g) {
+  using L = Layout<32>;
+  using D = Layout32;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+  int tm, tn;
+  const Operands o = resolve(g, blockIdx.x, tm, tn);
+  if (g.mode == 0)   // one dense problem: XCD-aware grouped order
+    tile_order(blockIdx.x, g.total_tiles, (int)((o.a_rows + TM - 1) / TM),
+               (int)((o.b_rows + TN - 1) / TN), tm, tn);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int64_t K = o.K;
+  const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
+  const int64_t rows_a = o.a_rows - row0 < TM ? o.a_rows - row0 : TM;
+  const int64_t rows_b = o.b_rows - col0 < TN ? o.b_rows - col0 : TN;
+  const uint32_t rs = (uint32_t)(K / 2), srs = (uint32_t)(K / 32) * 4u;
+
+  RdCtx c;
+  c.wave = wave;
+  c.nst = (int)((K + KST - 1) / KST);
+  c.ra = rsrc4(o.a_codes + row0 * rs, (uint32_t)(rows_a * rs));
+  c.rb = rsrc4(o.b_codes + col0 * rs, (uint32_t)(rows_b * rs));
+  c.rsa = rsrc4(reinterpret_cast<const uint8_t*>(o.a_scales) + row0 * srs, (uint32_t)(rows_a * srs));
+  c.rsb = rsrc4(reinterpret_cast<const uint8_t*>(o.b_scales) + col0 * srs, (uint32_t)(rows_b * srs));
+  c.lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds;
+  {
+    const int lr = lane >> 2;
+    const uint32_t chunk = (uint32_t)((lane & 3) ^ ((lr >> 1) & 3));
+#pragma unroll
+    for (int q = 0; q < 2; ++q) c.code_voff[q] = (uint32_t)(wave * 32 + q * 16 + lr) * rs + 16u * chunk;
+    // scales: 16 bytes per row and stage, one lane per row
+    c.scale_voff[0] = (uint32_t)((wave & 3) * 64 + lane) * srs;
+  }
+  uint8_t* decb = lds + NRAW * L::RAW;   // two decoded buffers
+
+  if (tid < 8)
+    *reinterpret_cast<uint4*>(decb + (tid >> 2) * D::DEC + D::ZERO + (tid & 3) * 512) = make_uint4(0, 0, 0, 0);
+
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      acc[i][j] = floatx16{};
+      asm volatile("" : "+v"(acc[i][j]));   // no peeled first step
+    }
+
+  const int nsteps = (int)(K / 32);
+  const int h = lane >> 5, r32 = lane & 31;
+  const int dop = wave >> 2, drow = tid & (TM - 1);   // the row this thread decodes
+  // fragment offsets in a decoded buffer; tile t adds 256 t (levels), 512 t (pieces)
+  const uint32_t code_a = (uint32_t)(((0 + h) * TM + wm * 128 + r32) * 8);
+  const uint32_t code_b = (uint32_t)(((4 + h) * TM + wn * 64 + r32) * 8);
+  const uint32_t pc_a = h ? (uint32_t)D::ZERO : (uint32_t)(D::LEV + (wm * 128 + r32) * 16);
+  const uint32_t pc_b = h ? (uint32_t)D::ZERO : (uint32_t)(D::LEV + (TM + wn * 64 + r32) * 16);
+  if (nsteps > 0) {
+    issue_stage<32>(c, 0, 0);
+    issue_stage<32>(c, 1, 1);
+    wait_vmcnt<L::VMEM>();
+    __syncthreads();
+    decode_store32<GRID>(decode_load32(lds, dop, drow, 0), decb, dop, drow);
+    __syncthreads();
+    Frag32 fa[4], fb[2], fbn[2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) fa[t] = frag32_at(decb, code_a + 256 * t, pc_a + 512 * t);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) fb[t] = frag32_at(decb, code_b + 256 * t, pc_b + 512 * t);
+    // Step i as in the 16-wide kernel: decode of step i+1 during tiles 0-1,
+    // barrier, then step i+1's fragments as registers free up.  A raw stage
+    // holds 4 steps: stage s is issued at step 4 (s - 1) and waited for two
+    // steps later.
+#pragma clang loop unroll(disable)
+    for (int i = 0; i < nsteps; ++i) {
+      if (i > 0 && (i & 3) == 0) issue_stage<32>(c, (i >> 2) + 1, ((i >> 2) + 1) & 1);
+      const int n = i + 1;   // decoded during this step (past the end: unused)
+      const DecIn32 din = decode_load32(lds + ((n >> 2) & 1) * L::RAW, dop, drow, n & 3);
+      const uint8_t* dn = decb + (n & 1) * D::DEC;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const Frag32& a = fa[t >> 1];
+        const Frag32& b = fb[t & 1];
+        floatx16 p = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a.c0, b.c0, floatx16{}, 0, 0, 0);
+        const floatx16 q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.pc, b.pc, floatx16{}, 0, 0, 0);
+        p = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a.c1, b.c1, p, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[t >> 1][t & 1][r] = __builtin_fmaf(p[r], q[r], acc[t >> 1][t & 1][r]);
+        asm volatile("" : "+v"(acc[t >> 1][t & 1]));   // the fmas stay here
+        if (t == 0) decode_store32<GRID>(din, decb + (n & 1) * D::DEC, dop, drow);
+        if (t == 1) {
+          if (((i + 2) & 3) == 0) wait_vmcnt<0>();   // raw stage of step i+2 has landed
+          __syncthreads();
+#pragma unroll
+          for (int u = 0; u < 2; ++u) fbn[u] = frag32_at(dn, code_b + 256 * u, pc_b + 512 * u);
+        }
+        if (t & 1) fa[t >> 1] = frag32_at(dn, code_a + 256 * (t >> 1), pc_a + 512 * (t >> 1));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      fb[0] = fbn[0];
+      fb[1] = fbn[1];
+    }
+  }
+
+  store_c<4, 2>(o.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 64,
+                lane, acc);
+}
+
+template <int GRID>
+hipError_t launch_rd32(const GemmLaunch& g, hipStream_t s) {
+  constexpr int bytes = Layout32::TOTAL;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_rd32<GRID>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((k_gemm_rd32<GRID>), dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool gemm_rd_supported(const GemmLaunch& g) {
@@ -438,11 +619,11 @@ hipError_t launch_gemm_rd(const GemmLaunch& g, hipStream_t s) {
   const int key = g.grid * 2 + (g.a_bc == 32 ? 1 : 0);
   switch (key) {
     case 0: return launch_rd<0, 16>(g, s);
-    case 1: return launch_rd<0, 32>(g, s);
+    case 1: return launch_rd32<0>(g, s);
     case 2: return launch_rd<1, 16>(g, s);
-    case 3: return launch_rd<1, 32>(g, s);
+    case 3: return launch_rd32<1>(g, s);
     case 4: return launch_rd<2, 16>(g, s);
-    default: return launch_rd<2, 32>(g, s);
+    default: return launch_rd32<2>(g, s);
   }
 }
 
