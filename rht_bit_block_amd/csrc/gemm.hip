@@ -374,13 +374,9 @@ __global__ __launch_bounds__(kThreads8) void k_gemm8(GemmLaunch g) {
 
 template <int GRID, int SMODE>
 hipError_t launch_one(const GemmLaunch& g, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm8<GRID, SMODE>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = set_lds_limit((const void*)k_gemm8<GRID, SMODE>, kLdsBytes, lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_gemm8<GRID, SMODE>), dim3(g.total_tiles), dim3(kThreads8), kLdsBytes, s, g);
   return hipGetLastError();
 }

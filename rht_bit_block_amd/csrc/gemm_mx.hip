@@ -505,13 +505,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx4(GemmLaunch g) {
 
 hipError_t launch_mx4(const GemmLaunch& g, hipStream_t s) {
   constexpr int bytes = NST * F4_STAGE;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mx4,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = set_lds_limit((const void*)k_gemm_mx4, bytes, lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_gemm_mx4, dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
   return hipGetLastError();
 }
@@ -800,26 +796,18 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx8(GemmLaunch g) {
 
 hipError_t launch_mx8(const GemmLaunch& g, hipStream_t s) {
   constexpr int bytes = 2 * W8_STAGE;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mx8,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = set_lds_limit((const void*)k_gemm_mx8, bytes, lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_gemm_mx8, dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
   return hipGetLastError();
 }
 
 hipError_t launch_mx4w(const GemmLaunch& g, hipStream_t s) {
   constexpr int bytes = 2 * W4_STAGE;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mx4w,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = set_lds_limit((const void*)k_gemm_mx4w, bytes, lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_gemm_mx4w, dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
   return hipGetLastError();
 }
@@ -827,13 +815,9 @@ hipError_t launch_mx4w(const GemmLaunch& g, hipStream_t s) {
 template <int GRID>
 hipError_t launch_mx(const GemmLaunch& g, hipStream_t s) {
   constexpr int bytes = 2 * 2 * TM * 128;   // 2 stages x 2 operands
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mx<GRID>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = set_lds_limit((const void*)k_gemm_mx<GRID>, bytes, lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_gemm_mx<GRID>), dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
   return hipGetLastError();
 }

@@ -414,13 +414,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
 template <int GRID, int BC>
 hipError_t launch_rd(const GemmLaunch& g, hipStream_t s) {
   constexpr int bytes = Layout<BC>::TOTAL;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_rd<GRID, BC>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = set_lds_limit((const void*)k_gemm_rd<GRID, BC>, bytes, lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_gemm_rd<GRID, BC>), dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
   return hipGetLastError();
 }
@@ -595,13 +591,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd32(GemmLaunch g) {
 template <int GRID>
 hipError_t launch_rd32(const GemmLaunch& g, hipStream_t s) {
   constexpr int bytes = Layout32::TOTAL;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_rd32<GRID>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = set_lds_limit((const void*)k_gemm_rd32<GRID>, bytes, lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_gemm_rd32<GRID>), dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
   return hipGetLastError();
 }

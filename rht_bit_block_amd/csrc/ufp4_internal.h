@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace ufp4 {
 
 constexpr int kMaxSegments = 128;  // segments per segmented quantization launch
@@ -127,6 +129,21 @@ struct GemmLaunch {
   int32_t tile_start[kMaxGroups + 1];
   int32_t total_tiles;
 };
+
+// Raises a kernel's dynamic LDS limit to `bytes` once per kernel and device
+// (the attribute belongs to the device that is current); `done` holds one bit
+// per device id.  Two threads racing on the first call both set it, which is
+// harmless.
+inline hipError_t set_lds_limit(const void* kernel, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s);
 // Power-of-two (E8M0) scales on the scaled matrix cores; only for launches
