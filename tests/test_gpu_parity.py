@@ -534,3 +534,16 @@ def test_gemm_fp32_scale_accuracy(grid, bc, rnd):
     err = O.rel_fro(C, ref)
     print(f"  rel. Frobenius error {err:.3e}", flush=True)
     assert err <= F32_SCALE_TOL, err
+
+
+# ---------------------------------------------------------------------------
+# fp32-scale GEMMs whose K ends inside a 128-wide raw stage (and K of a single
+# step), for 16- and 32-wide K steps; ragged row tiles on both operands.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("bc,K", [(16, 16), (16, 48), (16, 208), (32, 32), (32, 96), (32, 160), (32, 224)])
+def test_gemm_fp32_partial_stage(grid, bc, K):
+    _print_case("fp32-scale gemm, partial stage", grid, bc, K)
+    n = 16 if K % 16 == 0 else 1
+    cfg = U.make_cfg(grid, U.UFP4_SR, U.UFP4_SCALE_F32, 1, bc, n, sign_seed=31, sr_seed=37)
+    _gemm_case(272, 300, K, cfg, cfg, seed=K + 7 * bc + grid)
