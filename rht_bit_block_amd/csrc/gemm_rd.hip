@@ -40,6 +40,10 @@
 // tile), so the LDS reads of a step are hidden under the tiles of the one
 // before.
 //
+// With 1 x 32 blocks one scale covers two 16-wide halves, so k_gemm_rd32
+// takes 32-wide steps: two chained level MFMAs, one scale product and one set
+// of fmas per tile and step.
+//
 // Tiling: 256 x 256 output tile per 512-thread workgroup, 2 x 4 waves of
 // 128 x 64 (4 x 2 tiles of 32 x 32, accumulators in VGPRs).  Dense launches
 // order tiles so that the tiles resident at once on an XCD share operand
