@@ -499,6 +499,27 @@ def test_gemm_output_leading_dimension(name, cfg, K):
     assert O.rel_fro(host[:, :PB], ref) <= GEMM_TOL
 
 
+@pytest.mark.parametrize("name,cfg,K", LDC_CASES, ids=[c[0] for c in LDC_CASES])
+def test_gemm_output_huge_leading_dimension(name, cfg, K):
+    """ldc so large that a 256-row tile of C spans 2 GiB or more: the epilogue
+    takes its plain-store path (64-bit addresses, explicit bounds)."""
+    _print_case("huge ldc", name, K)
+    PA, PB = 40, 270
+    ldc = (1 << 21) + 64
+    ta, tb = rand_bits(PA, K, 63), rand_bits(PB, K, 64)
+    qa, ra = compare_quant(ta, 0, cfg, with_rotated=False)
+    qb, rb = compare_quant(tb, 0, cfg, with_rotated=False)
+    buf = torch.full((PA, ldc), 12345.0, dtype=torch.float32, device="cuda")
+    C = U.ufp4_gemm_fprop(qa, qb, out=buf[:, :PB])
+    assert C.stride(0) == ldc
+    assert torch.all(buf[:, PB:PB + 64] == 12345.0).item()
+    assert torch.all(buf[:, ldc - 64:] == 12345.0).item()
+    ref = O.gemm_ref(oracle_dequant64(ra, cfg), oracle_dequant64(rb, cfg))
+    assert O.rel_fro(buf[:, :PB].cpu().numpy(), ref) <= GEMM_TOL
+    del buf, C
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------------------
 # fp32-scale GEMMs compute the exact sum of level products times scale
 # products, rounded in fp32 only (the level dot products are exact, the scale
