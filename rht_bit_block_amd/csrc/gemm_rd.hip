@@ -294,52 +294,75 @@ __device__ __forceinline__ Operands resolve(const GemmLaunch& g, int tile, int& 
   return o;
 }
 
+// Per-tile state shared by the 16- and 32-wide kernels: the problem and the
+// tile's place in it, and the direct-load context for its raw stages (wave w
+// loads code rows 32 w .. 32 w + 31 of both operands and 1 KiB pieces of the
+// scales).
+struct TileCtx {
+  Operands o;
+  int64_t row0, col0, rows_a, rows_b;
+  RdCtx c;
+  int wave, wm, wn;
+};
+
+template <int BC>
+__device__ __forceinline__ TileCtx tile_ctx(const GemmLaunch& g, const uint8_t* lds, int tid) {
+  using L = Layout<BC>;
+  TileCtx t;
+  int tm, tn;
+  t.o = resolve(g, blockIdx.x, tm, tn);
+  if (g.mode == 0)   // one dense problem: XCD-aware grouped order
+    tile_order(blockIdx.x, g.total_tiles, (int)((t.o.a_rows + TM - 1) / TM),
+               (int)((t.o.b_rows + TN - 1) / TN), tm, tn);
+  const int lane = tid & 63;
+  t.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  t.wm = t.wave >> 2;
+  t.wn = t.wave & 3;
+  const int64_t K = t.o.K;
+  t.row0 = (int64_t)tm * TM;
+  t.col0 = (int64_t)tn * TN;
+  t.rows_a = t.o.a_rows - t.row0 < TM ? t.o.a_rows - t.row0 : TM;
+  t.rows_b = t.o.b_rows - t.col0 < TN ? t.o.b_rows - t.col0 : TN;
+  const uint32_t rs = (uint32_t)(K / 2), srs = (uint32_t)(K / BC) * 4u;
+  RdCtx& c = t.c;
+  c.wave = t.wave;
+  c.nst = (int)((K + KST - 1) / KST);
+  c.ra = rsrc4(t.o.a_codes + t.row0 * rs, (uint32_t)(t.rows_a * rs));
+  c.rb = rsrc4(t.o.b_codes + t.col0 * rs, (uint32_t)(t.rows_b * rs));
+  c.rsa = rsrc4(reinterpret_cast<const uint8_t*>(t.o.a_scales) + t.row0 * srs,
+                (uint32_t)(t.rows_a * srs));
+  c.rsb = rsrc4(reinterpret_cast<const uint8_t*>(t.o.b_scales) + t.col0 * srs,
+                (uint32_t)(t.rows_b * srs));
+  c.lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds;
+  // codes: lane i of wave load q -> row 32 w + 16 q + i / 4, the chunk whose
+  // swizzled slot is i % 4
+  const int lr = lane >> 2;
+  const uint32_t chunk = (uint32_t)((lane & 3) ^ ((lr >> 1) & 3));
+#pragma unroll
+  for (int q = 0; q < 2; ++q) c.code_voff[q] = (uint32_t)(t.wave * 32 + q * 16 + lr) * rs + 16u * chunk;
+  // scales: wave load g covers 1024 / SB rows of operand g / (SLOADS/2);
+  // lane i -> row i / (SB/16), part i % (SB/16)
+  constexpr int PER = L::SB / 16;
+  constexpr int ROWS = 64 / PER;
+#pragma unroll
+  for (int q = 0; q < L::SPW; ++q) {
+    const int gl = t.wave + 8 * q;
+    const int row = (gl % (L::SLOADS / 2)) * ROWS + lane / PER;
+    c.scale_voff[q] = (uint32_t)row * srs + 16u * (uint32_t)(lane % PER);
+  }
+  return t;
+}
+
 template <int GRID, int BC>
 __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
   using L = Layout<BC>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  int tm, tn;
-  const Operands o = resolve(g, blockIdx.x, tm, tn);
-  if (g.mode == 0)   // one dense problem: XCD-aware grouped order
-    tile_order(blockIdx.x, g.total_tiles, (int)((o.a_rows + TM - 1) / TM),
-               (int)((o.b_rows + TN - 1) / TN), tm, tn);
-
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
-  const int64_t K = o.K;
-  const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
-  const int64_t rows_a = o.a_rows - row0 < TM ? o.a_rows - row0 : TM;
-  const int64_t rows_b = o.b_rows - col0 < TN ? o.b_rows - col0 : TN;
-  const uint32_t rs = (uint32_t)(K / 2), srs = (uint32_t)(K / BC) * 4u;
-
-  RdCtx c;
-  c.wave = wave;
-  c.nst = (int)((K + KST - 1) / KST);
-  c.ra = rsrc4(o.a_codes + row0 * rs, (uint32_t)(rows_a * rs));
-  c.rb = rsrc4(o.b_codes + col0 * rs, (uint32_t)(rows_b * rs));
-  c.rsa = rsrc4(reinterpret_cast<const uint8_t*>(o.a_scales) + row0 * srs, (uint32_t)(rows_a * srs));
-  c.rsb = rsrc4(reinterpret_cast<const uint8_t*>(o.b_scales) + col0 * srs, (uint32_t)(rows_b * srs));
-  c.lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds;
-  {
-    // codes: lane i of wave load q -> row 32 w + 16 q + i / 4, the chunk whose
-    // swizzled slot is i % 4
-    const int lr = lane >> 2;
-    const uint32_t chunk = (uint32_t)((lane & 3) ^ ((lr >> 1) & 3));
-#pragma unroll
-    for (int q = 0; q < 2; ++q) c.code_voff[q] = (uint32_t)(wave * 32 + q * 16 + lr) * rs + 16u * chunk;
-    // scales: wave load g covers 1024 / SB rows of operand g / (SLOADS/2);
-    // lane i -> row i / (SB/16), part i % (SB/16)
-    constexpr int PER = L::SB / 16;
-    constexpr int ROWS = 64 / PER;
-#pragma unroll
-    for (int q = 0; q < L::SPW; ++q) {
-      const int g = wave + 8 * q;
-      const int row = (g % (L::SLOADS / 2)) * ROWS + lane / PER;
-      c.scale_voff[q] = (uint32_t)row * srs + 16u * (uint32_t)(lane % PER);
-    }
-  }
+  const TileCtx ts = tile_ctx<BC>(g, lds, tid);
+  const RdCtx& c = ts.c;
+  const int wave = ts.wave, wm = ts.wm, wn = ts.wn;
+  const int64_t K = ts.o.K;
   uint8_t* decb = lds + NRAW * L::RAW;   // two decoded buffers
 
   if (tid < 8)
@@ -411,8 +434,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
     }
   }
 
-  store_c<4, 2>(o.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 64,
-                lane, acc);
+  store_c<4, 2>(ts.o.c + ts.row0 * g.ldc + ts.col0, g.ldc, (int)ts.rows_a, (int)ts.rows_b,
+                wm * 128, wn * 64, lane, acc);
 }
 
 template <int GRID, int BC>
@@ -487,37 +510,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd32(GemmLaunch g) {
   using D = Layout32;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  int tm, tn;
-  const Operands o = resolve(g, blockIdx.x, tm, tn);
-  if (g.mode == 0)   // one dense problem: XCD-aware grouped order
-    tile_order(blockIdx.x, g.total_tiles, (int)((o.a_rows + TM - 1) / TM),
-               (int)((o.b_rows + TN - 1) / TN), tm, tn);
-
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
-  const int64_t K = o.K;
-  const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
-  const int64_t rows_a = o.a_rows - row0 < TM ? o.a_rows - row0 : TM;
-  const int64_t rows_b = o.b_rows - col0 < TN ? o.b_rows - col0 : TN;
-  const uint32_t rs = (uint32_t)(K / 2), srs = (uint32_t)(K / 32) * 4u;
-
-  RdCtx c;
-  c.wave = wave;
-  c.nst = (int)((K + KST - 1) / KST);
-  c.ra = rsrc4(o.a_codes + row0 * rs, (uint32_t)(rows_a * rs));
-  c.rb = rsrc4(o.b_codes + col0 * rs, (uint32_t)(rows_b * rs));
-  c.rsa = rsrc4(reinterpret_cast<const uint8_t*>(o.a_scales) + row0 * srs, (uint32_t)(rows_a * srs));
-  c.rsb = rsrc4(reinterpret_cast<const uint8_t*>(o.b_scales) + col0 * srs, (uint32_t)(rows_b * srs));
-  c.lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds;
-  {
-    const int lr = lane >> 2;
-    const uint32_t chunk = (uint32_t)((lane & 3) ^ ((lr >> 1) & 3));
-#pragma unroll
-    for (int q = 0; q < 2; ++q) c.code_voff[q] = (uint32_t)(wave * 32 + q * 16 + lr) * rs + 16u * chunk;
-    // scales: 16 bytes per row and stage, one lane per row
-    c.scale_voff[0] = (uint32_t)((wave & 3) * 64 + lane) * srs;
-  }
+  const TileCtx ts = tile_ctx<32>(g, lds, tid);
+  const RdCtx& c = ts.c;
+  const int wave = ts.wave, wm = ts.wm, wn = ts.wn;
+  const int64_t K = ts.o.K;
   uint8_t* decb = lds + NRAW * L::RAW;   // two decoded buffers
 
   if (tid < 8)
@@ -588,8 +585,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd32(GemmLaunch g) {
     }
   }
 
-  store_c<4, 2>(o.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 64,
-                lane, acc);
+  store_c<4, 2>(ts.o.c + ts.row0 * g.ldc + ts.col0, g.ldc, (int)ts.rows_a, (int)ts.rows_b,
+                wm * 128, wn * 64, lane, acc);
 }
 
 template <int GRID>
