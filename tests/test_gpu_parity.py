@@ -337,13 +337,16 @@ def test_pow2_2d_exponent_clamp():
             compare_quant(bits, 0, cfg)
 
 
-def test_segmented_quant_and_grouped_gemms():
+@pytest.mark.parametrize("b", [16, 32])
+def test_segmented_quant_and_grouped_gemms(b):
     """Four experts (one empty), per-expert transposed operands, and the
-    three grouped GEMMs against per-expert oracle products."""
+    three grouped GEMMs against per-expert oracle products (1 x 16 blocks: the
+    16-wide GEMM kernel; 1 x 32: the 32-wide one)."""
+    _print_case("grouped gemms", b)
     G, hidden, ffn = 4, 128, 96
     off = [0, 64, 64, 160, 256]               # padded token offsets (multiples of 32)
     T = off[-1]
-    n, b = 32, 32
+    n = 32
     sx, sd, sw = 31, 32, 33
     tx = rand_bits(T, hidden, 40)
     tw = rand_bits(G * ffn, hidden, 41)
