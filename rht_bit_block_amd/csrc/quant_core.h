@@ -139,42 +139,59 @@ __device__ __forceinline__ void scale_by(float (&y)[W], float c) {
 
 // ---------------------------------------------------------------------------
 // Rounding and encoding.  Every path first produces the signed level index k
-// (level = k * spacing unit) as the low bits of a "magic" float: for an
-// integer-valued or rounding fp32 x with |x| < 2^22, RN(x + 1.5 * 2^23) has
-// the nearest integer to x (ties to even) in its low mantissa bits, so
-// bits & 15 is the two's-complement nibble of k (one rounding, exact).
-// INT4 codes are that nibble; E1M2 / E2M1 codes are sign-magnitude, obtained
-// for eight packed nibbles at once (tc_to_sm).
+// (level = k * spacing unit) inside a "magic" float: for an integer-valued or
+// rounding fp32 x with |x| < 2^22, RN(x + 1.5 * 2^23 + 8) = 1.5 * 2^23 + 8 +
+// rint(x) (ties to even: the offset is even), so for k in [-8, 7] the float's
+// bits are 0x4B400000 + (k + 8) -- a constant upper part and the offset-binary
+// nibble k + 8 (one rounding, exact).  Eight such words are packed with one
+// shift-add each: sum_j word_j << 4j = sum_j 0x4B400000 << 4j + sum_j
+// (k_j + 8) << 4j (mod 2^32, no carries between nibbles), so subtracting the
+// constant part leaves the offset-binary nibbles.  INT4 codes are their two's-
+// complement form (bit 3 flipped); E1M2 / E2M1 codes are sign-magnitude,
+// obtained for eight packed nibbles at once (ob_to_sm).
 // ---------------------------------------------------------------------------
-constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+constexpr float kMagic = 12582912.0f;    // 1.5 * 2^23
+constexpr float kMagicOB = 12582920.0f;  // 1.5 * 2^23 + 8
+constexpr uint32_t kMagicHi = 0x4B400000u;
+constexpr uint32_t kPackBias = kMagicHi + (kMagicHi << 4) + (kMagicHi << 8) + (kMagicHi << 12) +
+                               (kMagicHi << 16) + (kMagicHi << 20) + (kMagicHi << 24) +
+                               (kMagicHi << 28);
 
-// Two's-complement nibbles of k in [-7, 7] -> sign-magnitude (8 | |k| for k < 0;
-// zero stays 0).  Per nibble x: negative iff bit 3; |k| = (~x + 1) & 7.
-__device__ __forceinline__ uint32_t tc_to_sm(uint32_t w) {
-  const uint32_t n = (w >> 3) & 0x11111111u;     // 1 in negative nibbles
-  const uint32_t m = (n << 4) - n;               // 0xF in negative nibbles
-  return (((w ^ m) + n) & 0x77777777u) | (n << 3);
+// Two's-complement nibble of a magic word.
+__device__ __forceinline__ uint32_t word_nibble(uint32_t f) { return (f & 15u) ^ 8u; }
+
+// Sum of word_j << 4j over a lane's eight elements -> offset-binary nibbles k + 8.
+__device__ __forceinline__ uint32_t unbias_words(uint32_t acc) { return acc - kPackBias; }
+
+// Offset-binary nibbles k + 8, k in [-7, 7] -> sign-magnitude (8 | |k| for
+// k < 0; zero stays 0).  Per nibble o: k >= 0 iff bit 3, then the code is
+// o ^ 8; else it is 16 - o = (o ^ 15) + 1.  t holds 8 in the negative
+// nibbles, t - (t >> 3) holds 7 there (no borrows), t >> 3 the +1.
+__device__ __forceinline__ uint32_t ob_to_sm(uint32_t o) {
+  const uint32_t t = ~o & 0x88888888u;
+  const uint32_t one = t >> 3;
+  return (o ^ 0x88888888u ^ (t - one)) + one;
 }
 
-// RTNE: nibble of k = rint(v / spacing) for the uniform grids (|v| <= qmax,
+// RTNE: magic word of k = rint(v / spacing) for the uniform grids (|v| <= qmax,
 // or one ulp above, which rounds to the same k); E2M1 by magnitude region.
 template <int GRID>
-__device__ __forceinline__ uint32_t rtne_nibble(float v) {
+__device__ __forceinline__ uint32_t rtne_word(float v) {
   if constexpr (GRID != 2) {
-    return __float_as_uint(__fmaf_rn(v, Grid<GRID>::inv_delta, kMagic)) & 15u;
+    return __float_as_uint(__fmaf_rn(v, Grid<GRID>::inv_delta, kMagicOB));
   } else {
     // spacing 0.5 below 2, 1 below 4, 2 above; index = rint(m/spacing) + add
     const float m = fabsf(v);
     const float mul = m < 2.0f ? 2.0f : (m < 4.0f ? 1.0f : 0.5f);
     const float add = m < 2.0f ? 0.0f : (m < 4.0f ? 2.0f : 4.0f);
     const float k = (__fmaf_rn(m, mul, kMagic) - kMagic) + add;   // exact integers
-    return __float_as_uint(copysignf(k, v) + kMagic) & 15u;
+    return __float_as_uint(copysignf(k, v) + kMagicOB);
   }
 }
 
-// SR: k = k_lo + [r16 < f 2^16] on the magnitude, sign restored; nibble of k.
+// SR: k = k_lo + [r16 < f 2^16] on the magnitude, sign restored; magic word of k.
 template <int GRID>
-__device__ __forceinline__ uint32_t sr_nibble(float v, uint32_t r16) {
+__device__ __forceinline__ uint32_t sr_word(float v, uint32_t r16) {
   const float m = fabsf(v);
   float mul = Grid<GRID>::inv_delta, add = 0.0f;
   if constexpr (GRID == 2) {
@@ -185,13 +202,14 @@ __device__ __forceinline__ uint32_t sr_nibble(float v, uint32_t r16) {
   const float fl = floorf(t);
   const float f = __fsub_rn(t, fl);               // exact
   const float k = fl + add + (((float)r16 < f * 65536.0f) ? 1.0f : 0.0f);
-  return __float_as_uint(copysignf(k, v) + kMagic) & 15u;
+  return __float_as_uint(copysignf(k, v) + kMagicOB);
 }
 
-// Eight nibbles (element j at bits 4j, two's complement) -> final codes.
+// Eight offset-binary nibbles (element j at bits 4j) -> final codes: INT4
+// two's complement, E1M2 / E2M1 sign-magnitude.
 template <int GRID>
-__device__ __forceinline__ uint32_t finish_codes(uint32_t w) {
-  return GRID == 1 ? w : tc_to_sm(w);
+__device__ __forceinline__ uint32_t finish_codes(uint32_t o) {
+  return GRID == 1 ? (o ^ 0x88888888u) : ob_to_sm(o);
 }
 
 // 16-bit draws of the W elements starting at element index e0 (e0 % 8 == 0).
@@ -296,7 +314,7 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
   static_assert(!(POW2 && FOLD), "power-of-two scales take the normalized values");
   uint32_t rw[W / 2];
   if constexpr (RM == 1) sr_draws<W>(e0, seed, stream, rw);
-  uint32_t packed[W / 8];
+  uint32_t packed[W / 8];   // sums of magic words (shift-added), see unbias_words
 #pragma unroll
   for (int i = 0; i < W / 8; ++i) packed[i] = 0u;
   uint32_t bytes[GRID == 3 ? W / 4 : 1];   // E4M3 codes, four per word
@@ -320,27 +338,34 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
       if constexpr (!DIAG) reinterpret_cast<uint8_t*>(scales_out)[blk] = (uint8_t)(e + 127);
     } else {
     float s = __fdiv_rn(M, qmax);  // s_B = RN(absmax / qmax)
-    if (s == 0.0f) {
-#pragma unroll
-      for (int j = 0; j < B; ++j) v[j] = 0.0f;
-    } else {
-      const float r = __fdiv_rn(1.0f, s);
+    {
+      // s = 0 (all-zero block, or absmax / qmax below the subnormal range):
+      // every v is 0.  Running the quotient below with divisor 1 and
+      // reciprocal 0 gives q = +-0, e = y, v = e * 0 + q = +-0 without a branch.
+      const bool zero = s == 0.0f;
+      const float sd = zero ? 1.0f : s;
+      const float r = zero ? 0.0f : __fdiv_rn(1.0f, sd);
       // Markstein: with r = RN(1/s) and q within an ulp of y/s, the fma
       // remainder is exact and RN(q + e r) = RN(y/s).  Preconditions: no
       // underflow of q or of the remainder.
-      const float thr = s * 0x1p-39f;
-      bool slow = !(s >= 0x1p-60f && s <= 0x1p60f);
+      // An element with |y| < s 2^-39 may break the no-underflow condition;
+      // RTNE sends it to level 0 whatever its quotient (every candidate is
+      // below 2^-36 in size), so only SR and the diagnostics, which use v
+      // itself, take the exact division for it.
+      constexpr bool kTinyExact = RM == 1 || DIAG;
+      const float thr = sd * 0x1p-39f;
+      bool slow = !(sd >= 0x1p-60f && sd <= 0x1p60f);
 #pragma unroll
       for (int j = 0; j < B; ++j) {
         const float yy = y[blk * B + j];
         const float q = __fmul_rn(yy, r);
-        const float e = __fmaf_rn(-q, s, yy);
+        const float e = __fmaf_rn(-q, sd, yy);
         v[j] = __fmaf_rn(e, r, q);
-        slow |= fabsf(yy) < thr;
+        if constexpr (kTinyExact) slow |= fabsf(yy) < thr;
       }
       if (__builtin_expect(slow, 0)) {
 #pragma unroll
-        for (int j = 0; j < B; ++j) v[j] = __fdiv_rn(y[blk * B + j], s);
+        for (int j = 0; j < B; ++j) v[j] = zero ? 0.0f : __fdiv_rn(y[blk * B + j], sd);
       }
     }
     if constexpr (FOLD) {
@@ -367,16 +392,17 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
         bytes[idx >> 2] |= e4m3_rtne(v[j]) << (8 * (idx & 3));
         continue;
       }
-      uint32_t nib;
+      uint32_t word;
       if constexpr (RM == 0) {
-        nib = rtne_nibble<GRID>(v[j]);   // no clamp needed: qmax + 1 ulp rounds to qmax
+        word = rtne_word<GRID>(v[j]);   // no clamp needed: qmax + 1 ulp rounds to qmax
       } else {
         const float vc = fminf(fmaxf(v[j], -qmax), qmax);
         const uint32_t r16 = (rw[idx >> 1] >> (16 * (idx & 1))) & 0xFFFFu;
-        nib = sr_nibble<GRID>(vc, r16);
+        word = sr_word<GRID>(vc, r16);
       }
-      if constexpr (DIAG) diag_accumulate<GRID>(diag, nib, fminf(fmaxf(v[j], -qmax), qmax));
-      packed[idx >> 3] |= nib << (4 * (idx & 7));
+      if constexpr (DIAG)
+        diag_accumulate<GRID>(diag, word_nibble(word), fminf(fmaxf(v[j], -qmax), qmax));
+      packed[idx >> 3] += word << (4 * (idx & 7));
     }
   }
   if constexpr (DIAG) return;
@@ -388,7 +414,7 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
     return;
   }
 #pragma unroll
-  for (int i = 0; i < W / 8; ++i) packed[i] = finish_codes<GRID>(packed[i]);
+  for (int i = 0; i < W / 8; ++i) packed[i] = finish_codes<GRID>(unbias_words(packed[i]));
   if constexpr (W == 16) {
     *reinterpret_cast<uint2*>(codes_out) = make_uint2(packed[0], packed[1]);
   } else {
@@ -822,16 +848,16 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows_2d(QuantLaunch q, uint3
       // power-of-two scale: |v| <= qmax exactly unless e hit its clamp at 127
       float v = __fmul_rn(y[j], inv);
       if (e == 127) v = fminf(fmaxf(v, -qmax), qmax);
-      uint32_t nib;
+      uint32_t word;
       if constexpr (RND == 0) {
-        nib = rtne_nibble<GRID>(v);
+        word = rtne_word<GRID>(v);
       } else {
-        nib = sr_nibble<GRID>(v, (rw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+        word = sr_word<GRID>(v, (rw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
       }
-      packed[j >> 3] |= nib << (4 * (j & 7));
+      packed[j >> 3] += word << (4 * (j & 7));
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) packed[i] = finish_codes<GRID>(packed[i]);
+    for (int i = 0; i < 4; ++i) packed[i] = finish_codes<GRID>(unbias_words(packed[i]));
     *reinterpret_cast<uint4*>(q.codes + (e0 >> 1)) =
         make_uint4(packed[0], packed[1], packed[2], packed[3]);
     if ((lane & 31u) == 0u)
