@@ -190,6 +190,12 @@ __device__ __forceinline__ uint32_t rtne_word(float v) {
 }
 
 // SR: k = k_lo + [r16 < f 2^16] on the magnitude, sign restored; magic word of k.
+// With t = |v| / spacing (exact) and u = r16 2^-16, k_lo + [f > u] =
+// ceil(t - u).  The fma below rounds t - u once: it is exact for t >= 1/2
+// (t < 8 and u on a 2^-16 grid fit 24 bits at t's ulp), and for smaller t
+// the result lies in (-1, 1/2), where rounding keeps its sign, keeps it
+// nonzero and keeps it above -1 (-1 + 2^-16 is a float), so the ceiling is
+// unchanged.
 template <int GRID>
 __device__ __forceinline__ uint32_t sr_word(float v, uint32_t r16) {
   const float m = fabsf(v);
@@ -199,9 +205,8 @@ __device__ __forceinline__ uint32_t sr_word(float v, uint32_t r16) {
     add = m < 2.0f ? 0.0f : (m < 4.0f ? 2.0f : 4.0f);
   }
   const float t = m * mul;                        // exact
-  const float fl = floorf(t);
-  const float f = __fsub_rn(t, fl);               // exact
-  const float k = fl + add + (((float)r16 < f * 65536.0f) ? 1.0f : 0.0f);
+  float k = ceilf(__fmaf_rn((float)r16, -0x1p-16f, t));
+  if constexpr (GRID == 2) k += add;
   return __float_as_uint(copysignf(k, v) + kMagicOB);
 }
 
