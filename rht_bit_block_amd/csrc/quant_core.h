@@ -681,67 +681,115 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantLaunch q) {
 
 // ---------------------------------------------------------------------------
 // Both axes from one read of X (1 x B blocks): the column-wise quantization
-// of the tile exactly as k_quant_cols, then the row-wise quantization of the
-// same 128 x 64 tile (A = X, K = the columns) from the staged words -- a lane
-// takes W consecutive columns of one row and keeps its row's bf16 half of
-// each word.  The row side has its own signs, SR stream and outputs.  Hadamard
-// chunks along the row must fit the tile width (n <= 64).
+// of a staged 128 x 64 tile exactly as k_quant_cols, then the row-wise
+// quantization of the same tile (A = X, K = the columns) from the staged
+// words -- a lane takes W consecutive columns of one row and keeps its row's
+// bf16 half of each word.  The row side has its own signs, SR stream and
+// outputs.  Hadamard chunks along the row must fit the tile width (n <= 64).
+//
+// A workgroup takes two consecutive tiles.  When both are whole (no ragged
+// rows or columns) the second tile's HBM loads are issued together with the
+// first's and are in flight while the first is quantized; otherwise each
+// tile is loaded and staged in turn.
 // ---------------------------------------------------------------------------
-template <int W, int B, int N, int GRID, int RND>
-__global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide rside) {
-  __shared__ uint32_t tile[(kTK / 2) * kTP];
-  static_assert(N <= kTP, "row-wise Hadamard chunks must fit the tile width");
-  constexpr int lpc = N > W ? N / W : 1;
-  const int bid = blockIdx.x;
+struct DualTile {
+  int64_t seg0, L, k0, p0;
+  int krows, pcols;
+};
+
+__device__ __forceinline__ DualTile dual_tile(const QuantLaunch& q, int bid) {
   int g = 0;
   while (g + 1 < q.nseg && q.tile_start[g + 1] <= bid) ++g;
-  const int64_t seg0 = q.seg_off[g], seg1 = q.seg_off[g + 1];
-  const int64_t L = seg1 - seg0;
-  const int64_t C = q.cols;
-  const int tiles_p = (int)((C + kTP - 1) / kTP);
+  DualTile d;
+  d.seg0 = q.seg_off[g];
+  d.L = q.seg_off[g + 1] - d.seg0;
+  const int tiles_p = (int)((q.cols + kTP - 1) / kTP);
   const int local = bid - q.tile_start[g];
   const int tk = local / tiles_p, tp = local - tk * tiles_p;
-  const int64_t k0 = (int64_t)tk * kTK;
-  const int64_t p0 = (int64_t)tp * kTP;
-  const int krows = (int)min<int64_t>(kTK, L - k0);
-  const int pcols = (int)min<int64_t>(kTP, C - p0);
+  d.k0 = (int64_t)tk * kTK;
+  d.p0 = (int64_t)tp * kTP;
+  d.krows = (int)min<int64_t>(kTK, d.L - d.k0);
+  d.pcols = (int)min<int64_t>(kTP, q.cols - d.p0);
+  return d;
+}
 
+// Staging task j of this thread: pair row i, columns c8 .. c8+7.
+constexpr int kStageTasks = (kTK / 2) * (kTP / 8) / kThreads;   // 2
+
+// Two bf16 rows (2i, 2i+1) x 8 columns -> 8 paired-row words in LDS.
+__device__ __forceinline__ void stage_pairs(uint32_t* tile, int i, int c8, uint4 ra, uint4 rb) {
+  const uint32_t a4[4] = {ra.x, ra.y, ra.z, ra.w}, b4[4] = {rb.x, rb.y, rb.z, rb.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    o[2 * j] = __builtin_amdgcn_perm(b4[j], a4[j], 0x05040100u);
+    o[2 * j + 1] = __builtin_amdgcn_perm(b4[j], a4[j], 0x07060302u);
+  }
+  uint32_t* d = tile + i * kTP;
+  *reinterpret_cast<uint4*>(d + col_swz(i, c8)) = make_uint4(o[0], o[1], o[2], o[3]);
+  *reinterpret_cast<uint4*>(d + col_swz(i, c8 + 4)) = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// The 16-byte row loads of a whole tile (all rows and columns inside X).
+struct DualRegs {
+  uint4 a[kStageTasks], b[kStageTasks];
+};
+
+__device__ __forceinline__ void load_whole(const QuantLaunch& q, const DualTile& d, DualRegs& r) {
+#pragma unroll
+  for (int j = 0; j < kStageTasks; ++j) {
+    const int t = threadIdx.x + j * kThreads;
+    const int i = t / (kTP / 8), c8 = (t % (kTP / 8)) * 8;
+    const uint16_t* src = q.x + (d.seg0 + d.k0 + 2 * i) * q.ld + d.p0 + c8;
+    r.a[j] = ld16(src);
+    r.b[j] = ld16(src + q.ld);
+  }
+}
+
+__device__ __forceinline__ void stage_whole(const DualRegs& r, uint32_t* tile) {
+#pragma unroll
+  for (int j = 0; j < kStageTasks; ++j) {
+    const int t = threadIdx.x + j * kThreads;
+    stage_pairs(tile, t / (kTP / 8), (t % (kTP / 8)) * 8, r.a[j], r.b[j]);
+  }
+}
+
+// Any tile, ragged rows and columns read as zeros.
+__device__ __forceinline__ void load_stage_any(const QuantLaunch& q, const DualTile& d,
+                                               uint32_t* tile) {
   for (int t = threadIdx.x; t < (kTK / 2) * (kTP / 8); t += kThreads) {
     const int i = t / (kTP / 8), c8 = (t % (kTP / 8)) * 8;
     uint4 ra = make_uint4(0, 0, 0, 0), rb = ra;
     const int r = 2 * i;
-    const uint16_t* src = q.x + (seg0 + k0 + r) * q.ld + p0 + c8;
-    if (c8 + 8 <= pcols) {
-      if (r < krows) ra = ld16(src);
-      if (r + 1 < krows) rb = ld16(src + q.ld);
+    const uint16_t* src = q.x + (d.seg0 + d.k0 + r) * q.ld + d.p0 + c8;
+    if (c8 + 8 <= d.pcols) {
+      if (r < d.krows) ra = ld16(src);
+      if (r + 1 < d.krows) rb = ld16(src + q.ld);
     } else {
       // ragged columns: element loads with compile-time indices (a runtime
       // index into a local array would place it in scratch memory)
       uint32_t ta[8], tb[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const bool in = c8 + j < pcols;
-        ta[j] = (in && r < krows) ? (uint32_t)src[j] : 0u;
-        tb[j] = (in && r + 1 < krows) ? (uint32_t)src[q.ld + j] : 0u;
+        const bool in = c8 + j < d.pcols;
+        ta[j] = (in && r < d.krows) ? (uint32_t)src[j] : 0u;
+        tb[j] = (in && r + 1 < d.krows) ? (uint32_t)src[q.ld + j] : 0u;
       }
       ra = make_uint4(ta[0] | (ta[1] << 16), ta[2] | (ta[3] << 16), ta[4] | (ta[5] << 16),
                       ta[6] | (ta[7] << 16));
       rb = make_uint4(tb[0] | (tb[1] << 16), tb[2] | (tb[3] << 16), tb[4] | (tb[5] << 16),
                       tb[6] | (tb[7] << 16));
     }
-    const uint32_t a4[4] = {ra.x, ra.y, ra.z, ra.w}, b4[4] = {rb.x, rb.y, rb.z, rb.w};
-    uint32_t o[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      o[2 * j] = __builtin_amdgcn_perm(b4[j], a4[j], 0x05040100u);
-      o[2 * j + 1] = __builtin_amdgcn_perm(b4[j], a4[j], 0x07060302u);
-    }
-    uint32_t* d = tile + i * kTP;
-    *reinterpret_cast<uint4*>(d + col_swz(i, c8)) = make_uint4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<uint4*>(d + col_swz(i, c8 + 4)) = make_uint4(o[4], o[5], o[6], o[7]);
+    stage_pairs(tile, i, c8, ra, rb);
   }
-  __syncthreads();
+}
 
+// Both quantizations of one staged tile.
+template <int W, int B, int N, int GRID, int RND>
+__device__ __forceinline__ void dual_quantize(const QuantLaunch& q, const RowSide& rside,
+                                              const DualTile& d, const uint32_t* tile) {
+  constexpr int lpc = N > W ? N / W : 1;
+  const int64_t C = q.cols;
   const uint32_t qpos = threadIdx.x & (uint32_t)(lpc - 1);
   const uint32_t neg1 = (qpos & 1u) ? 0x80000000u : 0u;
   const uint32_t neg2 = (qpos & 2u) ? 0x80000000u : 0u;
@@ -754,7 +802,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide 
       const int kseg = u % kSegsPerCol;
       const int col = u / kSegsPerCol;
       const int kr = kseg * W;
-      if (kr >= krows || col >= pcols) continue;
+      if (kr >= d.krows || col >= d.pcols) continue;
       uint32_t w[W / 2];
 #pragma unroll
       for (int i = 0; i < W / 2; ++i) {
@@ -764,7 +812,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide 
       float y[W];
       unpack<W>(w, pm, y);
       fwht<W, N>(y, neg1, neg2);
-      const uint64_t e0 = (uint64_t)C * seg0 + (uint64_t)(p0 + col) * L + (k0 + kr);
+      const uint64_t e0 = (uint64_t)C * d.seg0 + (uint64_t)(d.p0 + col) * d.L + (d.k0 + kr);
       finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, q, e0, code_ptr<GRID>(q.codes, e0),
                                                    scale_at<RND>(q.scales, e0 / B));
     }
@@ -778,7 +826,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide 
       const int seg = u % kSegsPerRow;
       const int row = u / kSegsPerRow;
       const int c0 = seg * W;
-      if (row >= krows || c0 >= pcols) continue;   // whole chunks drop out together
+      if (row >= d.krows || c0 >= d.pcols) continue;   // whole chunks drop out together
       const int pr = row >> 1;
       const uint32_t sel = (row & 1) ? 0x07060302u : 0x05040100u;
       uint32_t w[W / 2];
@@ -791,9 +839,46 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide 
       float y[W];
       unpack<W>(w, pm, y);
       fwht<W, N>(y, neg1, neg2);
-      const uint64_t e0 = (uint64_t)(seg0 + k0 + row) * (uint64_t)C + (uint64_t)(p0 + c0);
+      const uint64_t e0 = (uint64_t)(d.seg0 + d.k0 + row) * (uint64_t)C + (uint64_t)(d.p0 + c0);
       finish_lane<W, B, N, GRID, RND, RowSide>(y, rside, e0, code_ptr<GRID>(rside.codes, e0),
                                                scale_at<RND>(rside.scales, e0 / B));
+    }
+  }
+}
+
+template <int W, int B, int N, int GRID, int RND>
+__global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide rside) {
+  __shared__ uint32_t tile[(kTK / 2) * kTP];
+  static_assert(N <= kTP, "row-wise Hadamard chunks must fit the tile width");
+  static_assert(kStageTasks * kThreads == (kTK / 2) * (kTP / 8), "staging tasks per thread");
+  const int total = q.tile_start[q.nseg];
+  const int b0 = 2 * blockIdx.x;
+  const bool two = b0 + 1 < total;
+  const DualTile d0 = dual_tile(q, b0);
+  const DualTile d1 = dual_tile(q, two ? b0 + 1 : b0);
+  const bool whole = d0.krows == kTK && d0.pcols == kTP && d1.krows == kTK && d1.pcols == kTP;
+  if (whole) {
+    DualRegs r0, r1;
+    load_whole(q, d0, r0);
+    load_whole(q, d1, r1);   // (the first tile again when there is no second)
+    stage_whole(r0, tile);
+    __syncthreads();
+    dual_quantize<W, B, N, GRID, RND>(q, rside, d0, tile);
+    if (two) {
+      __syncthreads();   // every lane is done reading the first tile
+      stage_whole(r1, tile);
+      __syncthreads();
+      dual_quantize<W, B, N, GRID, RND>(q, rside, d1, tile);
+    }
+  } else {
+    load_stage_any(q, d0, tile);
+    __syncthreads();
+    dual_quantize<W, B, N, GRID, RND>(q, rside, d0, tile);
+    if (two) {
+      __syncthreads();
+      load_stage_any(q, d1, tile);
+      __syncthreads();
+      dual_quantize<W, B, N, GRID, RND>(q, rside, d1, tile);
     }
   }
 }
@@ -963,7 +1048,8 @@ template <int W, int B, int N, int G, int R>
 hipError_t run_dual(const QuantLaunch& q, const RowSide& r, hipStream_t s) {
   const int total = q.tile_start[q.nseg];
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_quant_dual<W, B, N, G, R>), dim3(total), dim3(kThreads), 0, s, q, r);
+  hipLaunchKernelGGL((k_quant_dual<W, B, N, G, R>), dim3((total + 1) / 2), dim3(kThreads), 0, s,
+                     q, r);
   return hipGetLastError();
 }
 

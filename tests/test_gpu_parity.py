@@ -262,6 +262,33 @@ def test_quant_dual(grid, rnd, n, b):
     _assert_q_equal(qc, O.quantize(bits, 1, spec_of(cc)), "col")
 
 
+@pytest.mark.parametrize("rnd", [U.UFP4_RTNE, U.UFP4_SR])
+def test_quant_dual_whole_tiles(rnd):
+    """The dual kernel's path for workgroups whose two 128 x 64 tiles are both
+    whole (second tile loaded during the first): 384 x 192 = 9 whole tiles,
+    the last workgroup with one; segments of 384, 0 and 256 rows x 192 columns
+    = 9 + 6 whole tiles, one workgroup taking the last tile of the first
+    segment and the first of the third."""
+    _print_case("dual whole tiles", rnd)
+    cr = U.make_cfg(U.UFP4_E1M2, rnd, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=21, sr_seed=7, sr_stream=0)
+    cc = U.make_cfg(U.UFP4_E1M2, rnd, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=22, sr_seed=7, sr_stream=1)
+    bits = rand_bits(384, 192, 123)
+    qr, qc = U.ufp4_rht_quant_dual(dev_bf16(bits), cr, cc)
+    torch.cuda.synchronize()
+    _assert_q_equal(qr, O.quantize(bits, 0, spec_of(cr)), "row")
+    _assert_q_equal(qc, O.quantize(bits, 1, spec_of(cc)), "col")
+    offs = [0, 384, 384, 640]
+    bits = rand_bits(640, 192, 124)
+    qr, qc = U.ufp4_rht_quant_dual(dev_bf16(bits), cr, cc, row_offsets=offs)
+    torch.cuda.synchronize()
+    _assert_q_equal(qr, O.quantize(bits, 0, spec_of(cr)), "row")
+    segs = [O.quantize(bits[lo:hi], 1, spec_of(cc), elem_base=bits.shape[1] * lo)
+            for lo, hi in zip(offs[:-1], offs[1:]) if hi > lo]
+    ref = {"codes": np.concatenate([np.asarray(r["codes"]).reshape(-1) for r in segs]),
+           "scales": np.concatenate([np.asarray(r["scales"]).reshape(-1) for r in segs])}
+    _assert_q_equal(qc, ref, "col")
+
+
 def test_quant_dual_segmented():
     """Dual call with expert segments (one empty) == the oracle's row-wise
     quantization and per-segment column-wise quantization."""
