@@ -222,6 +222,41 @@ class Workload:
         return e0.elapsed_time(e1) / reps
 
 
+def single_axis(U, torch, wl, reps=20):
+    """The dense layer's six quantizations as single-axis fused calls
+    (context; the step uses the dual-axis call): each timed over back-to-back
+    launches on the step's rotating input sets, with prebuilt C-ABI
+    arguments; GB/s count 2.75 B per element (bf16 in, code, fp32 scale)."""
+    lib = U.lib_handle()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = {}
+    for name, tn, along, cfg in wl.qcalls:
+        q = wl.q[name]
+        calls = []
+        for t in (ts[tn] for ts in wl.sets):
+            rows, cols = t.shape
+            calls.append((ctypes.c_void_p(t.data_ptr()), rows, cols, t.stride(0), along,
+                          ctypes.byref(cfg), ctypes.c_void_p(q.codes.data_ptr()),
+                          ctypes.c_void_p(q.scales.data_ptr()), None, stream))
+        for a in calls:
+            lib.ufp4_rht_quant(*a)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            st = lib.ufp4_rht_quant(*calls[i % len(calls)])
+            if st:
+                raise RuntimeError(f"{name} failed: {U.ufp4_status_string(st)}")
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbps = QBYTES_PER_ELEM * wl.sets[0][tn].numel() / ms / 1e6
+        rnd = "sr" if cfg.rounding == U.UFP4_SR else "rtne"
+        out[f"{name}_{rnd}"] = {"ms": round(ms, 4), "GB/s": round(gbps, 1),
+                                "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    return out
+
+
 def mx_gemms(U, torch, reps=10):
     """The GEMMs of the power-of-two configurations on the scaled matrix
     cores, each timed over back-to-back launches (context; not part of the
@@ -565,6 +600,7 @@ def main():
     quant_gbps = sum(qbytes.values()) / quant_ms / 1e6
     value = total_flops / (ms_step * 1e-3) / 1e12
 
+    single = single_axis(U, torch, wl)
     wl_m, wl_k, wl_n = wl.M, wl.K, wl.N
     qbpe = next(iter(wl.qbpe.values()))
     mx = None
@@ -612,6 +648,7 @@ def main():
                  "frac_fp4_peak": round(total_flops / gemm_ms / 1e9 / FP4_PEAK_TFLOPS, 4),
                  "ms": round(gemm_ms, 4)},
         "kernels": kernels,
+        "quant_single_axis": single,
         "cpu_baseline": cpu,
         "mx_gemms": mx,
         "moe_layers": moe,

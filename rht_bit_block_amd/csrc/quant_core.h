@@ -27,6 +27,8 @@
 // contraction; the library is built with -ffp-contract=off).
 #pragma once
 
+#include <atomic>
+
 #include "ufp4_internal.h"
 
 namespace ufp4 {
@@ -974,7 +976,19 @@ hipError_t run_rows(const QuantLaunch& q, hipStream_t s) {
   const uint64_t nseg = (uint64_t)q.P * segs_per_row;
   if (nseg == 0) return hipSuccess;
   const uint64_t blocks_needed = (nseg + kThreads - 1) / kThreads;
-  const uint64_t cap = (uint64_t)device_grid_limit() * 8;
+  // grid-stride: as many workgroups as fit on the chip at once (register use
+  // differs between instances), at most 8 per CU
+  static std::atomic<int> per_cu_cached{0};
+  int per_cu = per_cu_cached.load(std::memory_order_relaxed);
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)k_quant_rows<W, B, N, G, R>,
+                                                     kThreads, 0) != hipSuccess || n < 1)
+      n = 1;
+    per_cu = n < 8 ? n : 8;
+    per_cu_cached.store(per_cu, std::memory_order_relaxed);
+  }
+  const uint64_t cap = (uint64_t)device_grid_limit() * (uint64_t)per_cu;
   const uint32_t blocks = (uint32_t)(blocks_needed < cap ? blocks_needed : cap);
   hipLaunchKernelGGL((k_quant_rows<W, B, N, G, R>), dim3(blocks), dim3(kThreads), 0, s, q,
                      make_fastdiv(segs_per_row), (uint32_t)nseg);
