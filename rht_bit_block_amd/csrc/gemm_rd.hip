@@ -19,10 +19,10 @@
 // result differs from the exact one by fp32 rounding only (a few 2^-24
 // relative per step).
 //
-// Both MFMAs take fresh accumulators and are independent, and the 16 fmas of
-// a tile run on the vector ALU while the next tile's MFMAs execute: a step
-// costs two MFMAs (64 matrix-core cycles) and 16 fmas (64 VALU cycles) per
-// 32 x 32 tile.
+// Both MFMAs take fresh accumulators and are independent: a step costs two
+// MFMAs (64 matrix-core cycles) and 16 fmas (64 VALU cycles) per 32 x 32
+// tile, and the two units work side by side across the two waves of a SIMD
+// (one wave's fmas while the other's MFMAs execute).
 //
 // Data flow: the packed codes and the fp32 scales are copied HBM -> LDS
 // untouched by buffer_load ... lds (M0-based direct loads; four lanes per
@@ -401,7 +401,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
     // buffer during tiles 0-1; barrier; then step i+1's fragments are read as
     // registers free up (B right after the barrier into a second set, A[t]
     // after its last tile), hidden under tiles 2-7.  Tile t = (t / 2, t % 2):
-    // the MFMAs of tile t+1 are issued before the fmas of tile t.  Raw stage s
+    // one scheduling region holds the fmas of tile t and the MFMAs of tile
+    // t+1 (the compiler issues the fmas first; issuing tile t+1's level MFMA
+    // ahead of them, with the level products double-buffered, measured the
+    // same, so the order inside a wave is not what bounds a step).  Raw stage s
     // (8 steps) is issued at step 8 (s - 1) and waited for at the barrier of
     // the step that decodes its first step.
 #pragma clang loop unroll(disable)
