@@ -175,6 +175,26 @@ __device__ __forceinline__ uint32_t ob_to_sm(uint32_t o) {
   return (o ^ 0x88888888u ^ (t - one)) + one;
 }
 
+// E2M1 codes from the hardware FP4 conversion, which rounds to nearest even
+// exactly as the E2M1 codebook does (levels 0, 0.5, .. 6 are the FP4 values,
+// the even index is the even mantissa; saturating at 6) but keeps the sign
+// of a value that rounds to zero.  Codes of magnitude 0 lose their sign bit.
+__device__ __forceinline__ uint32_t fp4_clear_negzero(uint32_t w) {
+  const uint32_t m = w & 0x77777777u;
+  return m | (w & ((m + 0x77777777u) & 0x88888888u));
+}
+
+// Codes of (a, b) into byte sel of w (a in the low nibble); sel is a constant
+// once the caller's loops are unrolled.
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t w, float a, float b, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, 3);
+  }
+}
+
 // RTNE: magic word of k = rint(v / spacing) for the uniform grids (|v| <= qmax,
 // or one ulp above, which rounds to the same k); E2M1 by magnitude region.
 template <int GRID>
@@ -324,6 +344,9 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
   uint32_t packed[W / 8];   // sums of magic words (shift-added), see unbias_words
 #pragma unroll
   for (int i = 0; i < W / 8; ++i) packed[i] = 0u;
+  // E2M1 RTNE: two elements per hardware FP4 conversion (scale 1: v is
+  // already in grid units), codes written into byte (idx & 7) / 2 of the word
+  constexpr bool kHwFp4 = GRID == 2 && RM == 0 && !DIAG;
   uint32_t bytes[GRID == 3 ? W / 4 : 1];   // E4M3 codes, four per word
 #pragma unroll
   for (int i = 0; i < (GRID == 3 ? W / 4 : 1); ++i) bytes[i] = 0u;
@@ -391,6 +414,14 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
     }
     if constexpr (!DIAG) reinterpret_cast<float*>(scales_out)[blk] = s;
     }
+    if constexpr (kHwFp4) {
+#pragma unroll
+      for (int j = 0; j < B; j += 2) {
+        const int idx = blk * B + j;
+        packed[idx >> 3] = fp4_pair(packed[idx >> 3], v[j], v[j + 1], (idx & 7) >> 1);
+      }
+      continue;
+    }
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const int idx = blk * B + j;
@@ -421,7 +452,8 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
     return;
   }
 #pragma unroll
-  for (int i = 0; i < W / 8; ++i) packed[i] = finish_codes<GRID>(unbias_words(packed[i]));
+  for (int i = 0; i < W / 8; ++i)
+    packed[i] = kHwFp4 ? fp4_clear_negzero(packed[i]) : finish_codes<GRID>(unbias_words(packed[i]));
   if constexpr (W == 16) {
     *reinterpret_cast<uint2*>(codes_out) = make_uint2(packed[0], packed[1]);
   } else {
