@@ -195,6 +195,21 @@ __device__ __forceinline__ uint32_t fp4_pair(uint32_t w, float a, float b, int s
   }
 }
 
+// E4M3 bytes of (a, b) into half hi of w from the hardware FP8 conversion
+// (scale 1), which rounds to nearest even onto the OCP E4M3 values exactly as
+// the codebook rounding does, but keeps the sign of a value that rounds to
+// zero; e4m3_clear_negzero drops it.
+typedef short short2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t fp8_pair(uint32_t w, float a, float b, int hi) {
+  const short2_t o = __builtin_bit_cast(short2_t, w);
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, a, b, 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, a, b, 1.0f, false));
+}
+__device__ __forceinline__ uint32_t e4m3_clear_negzero(uint32_t w) {
+  const uint32_t m = w & 0x7F7F7F7Fu;
+  return m | (w & ((m + 0x7F7F7F7Fu) & 0x80808080u));
+}
+
 // RTNE: magic word of k = rint(v / spacing) for the uniform grids (|v| <= qmax,
 // or one ulp above, which rounds to the same k); E2M1 by magnitude region.
 template <int GRID>
@@ -267,22 +282,6 @@ __device__ __forceinline__ int pow2_exponent(float M) {
     while (e < 127 && M > ldexpf(qmax, e)) ++e;
   }
   return e;
-}
-
-// RTNE onto E4M3 (|v| <= 448): the pattern b = 8 e + m of the nearest
-// value, ties to even m.  Subnormal range (|v| < 2^-6, spacing 2^-9): the
-// magic-number rint of |v| * 2^9 is b itself (b = 8 is 2^-6).  Normal range:
-// the fp32 mantissa rounded to 3 bits (RNE, the carry may step the exponent)
-// gives (biased exponent << 3 | m); b subtracts the bias difference 120 << 3.
-// Sign bit 0x80, zero always 0x00.
-__device__ __forceinline__ uint32_t e4m3_rtne(float v) {
-  const float m = fabsf(v);
-  const uint32_t sub = __float_as_uint(__fmaf_rn(m, 512.0f, kMagic)) & 0xFFu;
-  const uint32_t bits = __float_as_uint(m);
-  const uint32_t r = bits + 0x7FFFFu + ((bits >> 20) & 1u);
-  const uint32_t nrm = (r >> 20) - (120u << 3);
-  const uint32_t b = m < 0x1p-6f ? sub : nrm;
-  return b | ((v < 0.0f && b != 0u) ? 0x80u : 0u);
 }
 
 // Byte offset of element e0's code: 4-bit codes two per byte, E4M3 one.
@@ -414,6 +413,15 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
     }
     if constexpr (!DIAG) reinterpret_cast<float*>(scales_out)[blk] = s;
     }
+    if constexpr (GRID == 3) {
+      static_assert(RM == 0 && POW2 && !DIAG, "E4M3: RTNE with power-of-two scales");
+#pragma unroll
+      for (int j = 0; j < B; j += 2) {
+        const int idx = blk * B + j;
+        bytes[idx >> 2] = fp8_pair(bytes[idx >> 2], v[j], v[j + 1], (idx & 3) >> 1);
+      }
+      continue;
+    }
     if constexpr (kHwFp4) {
 #pragma unroll
       for (int j = 0; j < B; j += 2) {
@@ -425,11 +433,6 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const int idx = blk * B + j;
-      if constexpr (GRID == 3) {
-        static_assert(RM == 0 && POW2 && !DIAG, "E4M3: RTNE with power-of-two scales");
-        bytes[idx >> 2] |= e4m3_rtne(v[j]) << (8 * (idx & 3));
-        continue;
-      }
       uint32_t word;
       if constexpr (RM == 0) {
         word = rtne_word<GRID>(v[j]);   // no clamp needed: qmax + 1 ulp rounds to qmax
@@ -448,7 +451,8 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
 #pragma unroll
     for (int i = 0; i < W / 16; ++i)
       reinterpret_cast<uint4*>(codes_out)[i] =
-          make_uint4(bytes[4 * i], bytes[4 * i + 1], bytes[4 * i + 2], bytes[4 * i + 3]);
+          make_uint4(e4m3_clear_negzero(bytes[4 * i]), e4m3_clear_negzero(bytes[4 * i + 1]),
+                     e4m3_clear_negzero(bytes[4 * i + 2]), e4m3_clear_negzero(bytes[4 * i + 3]));
     return;
   }
 #pragma unroll
