@@ -17,7 +17,9 @@
 //   block absmax, scale, RN(y / s) (Markstein's reciprocal correction,
 //   falling back to IEEE division when its preconditions fail), RTNE or
 //   stochastic rounding (Philox4x32-10 keyed by the element index), nibble
-//   encoding, packing, 8/16-byte stores.
+//   encoding, packing, 8/16-byte stores.  E2M1 round-to-nearest and E4M3
+//   (MXFP8) codes come from gfx950's FP4 / FP8 conversion instructions,
+//   whose rounding is the codebooks' (negative zero cleared afterwards).
 // For n = 4^j, c_n is a power of two: multiplying by it commutes exactly with
 // the absmax, the scale and the quotient, so it is folded into the stored
 // scale (blocks so small that the fold could underflow take the literal path).
