@@ -88,6 +88,8 @@ def parse():
                    help="skip the grouped (MoE) layer figures")
     p.add_argument("--no-diag", action="store_true",
                    help="skip the quantization diagnostics (level statistics) figures")
+    p.add_argument("--no-stream", action="store_true",
+                   help="skip the large-tensor streaming quantizer figures and the device-copy reference")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain device-to-device copy of 1 GiB five times (known "
                         "bytes, to scale the profiler's FETCH_SIZE / WRITE_SIZE counters)")
@@ -254,6 +256,60 @@ def single_axis(U, torch, wl, reps=20):
         rnd = "sr" if cfg.rounding == U.UFP4_SR else "rtne"
         out[f"{name}_{rnd}"] = {"ms": round(ms, 4), "GB/s": round(gbps, 1),
                                 "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    return out
+
+
+def quant_stream(U, torch, reps=10):
+    """The row-wise fused quantizer on one large bf16 tensor (32768 x 8192,
+    N(0,1) from a seeded generator; n = 16, 1 x 16 fp32 scales, E1M2), RTNE
+    and SR, next to a plain 1 GiB device-to-device copy timed the same way:
+    what the streaming kernel reaches against what the memory system gives a
+    copy on this machine (context; GB/s count 2.75 B per element, the copy 2 B
+    per byte copied)."""
+    lib = U.lib_handle()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7001)
+    rows, cols = 32768, 8192
+    x = torch.randn((rows, cols), device="cuda", dtype=torch.float32, generator=g).to(torch.bfloat16)
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((rows, cols // 16), dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {"shape": [rows, cols]}
+    for name, rnd in (("row_rtne_n16", U.UFP4_RTNE), ("row_sr_n16", U.UFP4_SR)):
+        cfg = U.make_cfg(U.UFP4_E1M2, rnd, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=7002, sr_seed=7003)
+        args = (ctypes.c_void_p(x.data_ptr()), rows, cols, x.stride(0), 0, ctypes.byref(cfg),
+                ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()), None, stream)
+
+        def call(a=args):
+            st = lib.ufp4_rht_quant(*a)
+            if st:
+                raise RuntimeError(f"{name} failed: {U.ufp4_status_string(st)}")
+        ms = timed(call)
+        gbps = QBYTES_PER_ELEM * rows * cols / ms / 1e6
+        out[name] = {"ms": round(ms, 4), "GB/s": round(gbps, 1),
+                     "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    del x, codes, scales
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms = timed(lambda: dst.copy_(src))
+    gbps = 2.0 * n / ms / 1e6
+    out["device_copy_1GiB"] = {"ms": round(ms, 4), "GB/s": round(gbps, 1),
+                               "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    del src, dst
+    torch.cuda.empty_cache()
     return out
 
 
@@ -603,6 +659,11 @@ def main():
     single = single_axis(U, torch, wl)
     wl_m, wl_k, wl_n = wl.M, wl.K, wl.N
     qbpe = next(iter(wl.qbpe.values()))
+    stream_q = None
+    if not args.no_stream:
+        wl = None   # free the step's buffers first
+        torch.cuda.empty_cache()
+        stream_q = quant_stream(U, torch)
     mx = None
     if not args.no_mx:
         wl = None   # free the step's buffers first
@@ -649,6 +710,7 @@ def main():
                  "ms": round(gemm_ms, 4)},
         "kernels": kernels,
         "quant_single_axis": single,
+        "quant_stream": stream_q,
         "cpu_baseline": cpu,
         "mx_gemms": mx,
         "moe_layers": moe,
