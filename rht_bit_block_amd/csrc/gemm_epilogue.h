@@ -66,8 +66,11 @@ __device__ __forceinline__ void store_c_tile(float* c_tile, int64_t ldc, int row
         const uint32_t off = base + (uint32_t)(8 * (r >> 2) + (r & 3)) * ld4;
         // __float_as_uint, not __builtin_bit_cast: the bit cast of an
         // accumulator element reaching this intrinsic was lowered to the same
-        // register for every element
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rs, (int)off, 0, 0);
+        // register for every element.  Cache policy 2 = non-temporal: C is
+        // written once and not read back by the kernel, so it streams out
+        // without displacing the operand strips other tiles still read
+        // (the dense layer's step measured 0.8 % faster, 3 of 3 pairs).
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rs, (int)off, 0, 2);
       }
     }
   }
