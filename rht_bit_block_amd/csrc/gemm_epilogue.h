@@ -69,7 +69,7 @@ __device__ __forceinline__ void store_c_tile(float* c_tile, int64_t ldc, int row
         // register for every element.  Cache policy 2 = non-temporal: C is
         // written once and not read back by the kernel, so it streams out
         // without displacing the operand strips other tiles still read
-        // (the dense layer's step measured 0.8 % faster, 3 of 3 pairs).
+        // (the dense layer's step measured 0.8 % faster, 6 of 6 same-box pairs).
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rs, (int)off, 0, 2);
       }
     }
