@@ -12,10 +12,12 @@
  *           quantization).
  *
  * Conventions shared by every entry point
- *   - Pointers named x, codes, scales, rotated, out, Y, dX, dW are DEVICE
- *     pointers owned by the caller; arrays named *_offsets are HOST arrays.
- *     The library allocates no memory, keeps no state between calls and is
- *     safe to call from several host threads.
+ *   - Pointers named x, codes, scales, rotated, out, workspace, Y, dX, dW
+ *     are DEVICE pointers owned by the caller; arrays named *_offsets are
+ *     HOST arrays.  The library allocates no memory and keeps no data
+ *     between calls (only per-device kernel attributes, set once), so every
+ *     entry point is safe to call from several host threads and on several
+ *     streams at once, as long as the calls do not write the same buffers.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *     default stream).  Nothing synchronizes inside the library.
  *   - Every function returns UFP4_OK (0) or a negative status; arguments are
@@ -148,6 +150,10 @@ int ufp4_rht_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ld,
                         uint8_t* codes_row, void* scales_row, uint8_t* codes_col,
                         void* scales_col, void* stream);
 
+/* Size in bytes of the device workspace ufp4_quant_diag takes (the partial
+ * sums of its workgroups). */
+#define UFP4_DIAG_WORKSPACE_BYTES 8192
+
 /* Level statistics of a row-wise quantization (diagnostics): the same
  * transform, scale and rounding as ufp4_rht_quant with along = 0 and cfg, but
  * nothing is stored except, for each magnitude level index k = 0..7 of the
@@ -160,15 +166,22 @@ int ufp4_rht_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ld,
  * uniform grids, negative at E2M1's spacing changes under RTNE -- and the
  * counts are the bucket utilisation the Method section attributes to the RHT.
  * The sums are exact integers, so the result does not depend on launch order.
- * stats: DEVICE uint64 [16], 8-byte aligned, overwritten.  cfg must be 1D
- * (block_rows == 1) with a 4-bit codebook; shapes and errors as
- * ufp4_rht_quant.  The workgroups' partial sums go through a small array
- * the library keeps on each GPU, so diagnostics calls that overlap on one GPU
- * (different streams) race; calls on one stream are ordered. */
+ * stats: DEVICE uint64 [16], 8-byte aligned, overwritten.  workspace:
+ * DEVICE buffer of UFP4_DIAG_WORKSPACE_BYTES, 8-byte aligned, owned by the
+ * caller; the call clears it and keeps the workgroups' partial sums there,
+ * so calls that overlap in time need workspaces of their own (its contents
+ * after the call mean nothing).  cfg must be 1D (block_rows == 1) with a
+ * 4-bit codebook; shapes and errors as ufp4_rht_quant; a null or misaligned
+ * workspace is UFP4_ERR_INVALID_ARG. */
 int ufp4_quant_diag(const void* x, int64_t rows, int64_t cols, int64_t ld,
-                    const ufp4_quant_cfg* cfg, uint64_t* stats, void* stream);
+                    const ufp4_quant_cfg* cfg, uint64_t* stats, void* workspace,
+                    void* stream);
 
-/* Column-wise quantization of row segments (per-expert transposed operands).
+/* Column-wise quantization of row segments (per-expert transposed operands):
+ * the quantizer of ufp4_rht_quant ([UFP4] formats section; Method: X H'
+ * along the shared dimension) applied to each expert's token range on its
+ * own, since in an MoE layer ([UFP4] abstract: the MoE 7.9B and 124B runs)
+ * WGRAD contracts over the tokens routed to one expert.
  * Segment g is rows [row_offsets[g], row_offsets[g+1]) of x [rows][ld]; it
  * yields A_g = x[seg]^T of shape [cols][L_g], L_g = segment length, which is
  * stored at codes + cols*row_offsets[g]/2 as [cols][L_g/2] and at scales +
@@ -203,9 +216,12 @@ int ufp4_gemm_dgrad(const ufp4_qtensor* dY, const ufp4_qtensor* Wt, float* dX, i
 int ufp4_gemm_wgrad(const ufp4_qtensor* dYt, const ufp4_qtensor* Xt, float* dW, int64_t ldw,
                     void* stream);
 
-/* Grouped (MoE expert) GEMMs in one launch.  offsets: HOST int64 [G+1], the
- * padded token offsets of the experts in the expert-sorted token matrix
- * (0 = offsets[0] <= ... <= offsets[G] = T); G <= 64.
+/* Grouped (MoE expert) GEMMs in one launch: one FPROP / DGRAD / WGRAD of
+ * [UFP4] Method (Y^ = Q(X H') Q(W H')^T per expert) for each expert of an
+ * MoE layer ([UFP4] abstract: MoE 7.9B and 124B pretraining).
+ * offsets: HOST int64 [G+1], the padded token offsets of the experts in
+ * the expert-sorted token matrix (0 = offsets[0] <= ... <= offsets[G] = T);
+ * G <= 64.
  *   fprop_grouped: A = X_perm [T][K_in], B = W stacked [G*N][K_in]
  *                  (expert g = rows g*N ..), Y [T][ldy]: Y_g = X_g W_g^T.
  *   dgrad_grouped: A = dY_perm [T][N], B = W^T stacked [G*K_in][N] (the
@@ -236,7 +252,9 @@ size_t ufp4_scales_bytes(int64_t P, int64_t K, const ufp4_quant_cfg* cfg);
 
 /* The 16-bit stochastic-rounding draws for elements first .. first+n-1 under
  * (seed, stream), written to out [n] (device uint16).  Exposes the device
- * generator so it can be checked on its own. */
+ * generator so it can be checked on its own: stochastic rounding ([UFP4]
+ * formats section; [2DFP4] 2D section, E[roundS(x)] = x) rounds up when the
+ * element's draw falls below its fractional position between two levels. */
 int ufp4_philox_fill(uint64_t seed, uint32_t stream_id, uint64_t first, int64_t n,
                      uint16_t* out, void* stream);
 

@@ -78,6 +78,12 @@ class QTensor:
     cfg: QuantCfg
 
     def c(self):
+        dev = self.codes.device if isinstance(self.codes, torch.Tensor) else None
+        _check_buffer("codes", self.codes, torch.uint8, _codes_elems(self.P, self.K, self.cfg), dev)
+        _check_buffer("scales", self.scales, scales_dtype(self.cfg),
+                      _scales_elems(self.P, self.K, self.cfg), dev)
+        if self.P and self.K:
+            _on_gpu(self.codes, "codes")
         return QTensorC(self.codes.data_ptr(), self.scales.data_ptr(), self.P, self.K, self.cfg)
 
 
@@ -99,7 +105,7 @@ def _lib():
             "ufp4_rht_quant": [vp, i64, i64, i64, i32, cfgp, vp, vp, vp, vp],
             "ufp4_rht_quant_segmented": [vp, i64, i64, i64, i64p, i32, cfgp, vp, vp, vp],
             "ufp4_rht_quant_dual": [vp, i64, i64, i64, i64p, i32, cfgp, cfgp, vp, vp, vp, vp, vp],
-            "ufp4_quant_diag": [vp, i64, i64, i64, cfgp, vp, vp],
+            "ufp4_quant_diag": [vp, i64, i64, i64, cfgp, vp, vp, vp],
             "ufp4_dequant": [qtp, vp, i64, vp],
             "ufp4_gemm_fprop": [qtp, qtp, vp, i64, vp],
             "ufp4_gemm_dgrad": [qtp, qtp, vp, i64, vp],
@@ -149,6 +155,67 @@ def _i64arr(vals: Sequence[int]):
     return arr
 
 
+# ---------------------------------------------------------------------------
+# Buffer checks.  The C ABI takes raw device pointers and cannot know buffer
+# sizes, so the binding checks every tensor it hands over (dtype, device,
+# unit inner stride, size) and raises ValueError before the call.
+# ---------------------------------------------------------------------------
+def _codes_elems(P, K, cfg):
+    return P * K if cfg.grid == UFP4_E4M3 else P * ((K + 1) // 2)
+
+
+def _scales_elems(P, K, cfg):
+    br, bc = max(1, cfg.block_rows), max(1, cfg.block_cols)
+    return ((P + br - 1) // br) * ((K + bc - 1) // bc)
+
+
+def _check_buffer(name, t, dtype, min_elems, device=None):
+    """A flat buffer of at least min_elems elements: dtype, device, and
+    contiguous storage (the library writes it densely)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if min_elems == 0:
+        return
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < min_elems:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {min_elems}")
+    if (device is None and not t.is_cuda) or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be on {device if device is not None else 'a GPU'}")
+
+
+def _check_matrix(name, t, rows, cols, device):
+    """An fp32 output matrix of at least rows x cols, unit column stride
+    (the row pitch is passed to the library as its leading dimension)."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D float32 tensor")
+    if rows == 0 or cols == 0:
+        return
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    if t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, needs at least ({rows}, {cols})")
+    if t.stride(0) < cols:
+        raise ValueError(f"{name} row pitch {t.stride(0)} is below its {cols} columns")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+
+
+def _check_x(x):
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    if x.stride(1) != 1:
+        raise ValueError("x must be row-major (unit column stride)")
+
+
+def _on_gpu(x, name="x"):
+    """Checked last, after the outputs (which must sit on x's device)."""
+    if x.numel() and not x.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+
+
 def codes_shape(P, K, cfg):
     """4-bit codes two per byte; E4M3 (MXFP8) codes one per byte."""
     return (P, K) if cfg.grid == UFP4_E4M3 else (P, K // 2)
@@ -169,38 +236,51 @@ def ufp4_rht_quant(x: torch.Tensor, along: int, cfg: QuantCfg, codes=None, scale
                    rotated=False, ld: Optional[int] = None):
     """Quantize bf16 x [rows, cols] (row-major, row pitch ld).  Returns
     (QTensor, rotated fp32 [P, K] or None)."""
-    if x.dtype != torch.bfloat16 or x.dim() != 2:
-        raise ValueError("x must be a 2-D bfloat16 tensor")
+    _check_x(x)
     rows, cols = x.shape
     ld = x.stride(0) if ld is None else ld
-    if x.stride(1) != 1:
-        raise ValueError("x must be row-major (unit column stride)")
     P, K = (cols, rows) if along else (rows, cols)
     dev = x.device
     if codes is None:
         codes = torch.empty(codes_shape(P, K, cfg), dtype=torch.uint8, device=dev)
     if scales is None:
         scales = torch.empty(scales_shape(P, K, cfg), dtype=scales_dtype(cfg), device=dev)
+    _check_buffer("codes", codes, torch.uint8, _codes_elems(P, K, cfg), dev)
+    _check_buffer("scales", scales, scales_dtype(cfg), _scales_elems(P, K, cfg), dev)
     rot = torch.empty((P, K), dtype=torch.float32, device=dev) if rotated is True else (
         rotated if isinstance(rotated, torch.Tensor) else None)
+    if rot is not None:
+        _check_matrix("rotated", rot, P, K, dev)
+        if rot.stride(0) != K:
+            raise ValueError("rotated must be a dense [P, K] tensor")
+    _on_gpu(x)
     st = _lib().ufp4_rht_quant(_ptr(x), rows, cols, ld, int(along), ctypes.byref(cfg),
                                _ptr(codes), _ptr(scales), _ptr(rot), _stream(x))
     _check("ufp4_rht_quant", st)
     return QTensor(codes, scales, P, K, cfg), rot
 
 
-def ufp4_quant_diag(x: torch.Tensor, cfg: QuantCfg, stats=None, ld: Optional[int] = None):
+DIAG_WORKSPACE_BYTES = 8192   # UFP4_DIAG_WORKSPACE_BYTES
+
+
+def ufp4_quant_diag(x: torch.Tensor, cfg: QuantCfg, stats=None, ld: Optional[int] = None,
+                    workspace=None):
     """Level statistics of the row-wise quantization of bf16 x [rows, cols]:
     int64 [16] on x's device -- [0:8] element counts per magnitude level index,
-    [8:16] sums of rint((L_k - |t|) * 2^28) (see the C header)."""
-    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x must be a row-major 2-D bfloat16 tensor")
+    [8:16] sums of rint((L_k - |t|) * 2^28) (see the C header).  workspace:
+    uint8 device buffer of DIAG_WORKSPACE_BYTES (allocated when not given)."""
+    _check_x(x)
     rows, cols = x.shape
     ld = x.stride(0) if ld is None else ld
     if stats is None:
         stats = torch.empty(16, dtype=torch.int64, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(DIAG_WORKSPACE_BYTES, dtype=torch.uint8, device=x.device)
+    _check_buffer("stats", stats, torch.int64, 16, x.device)
+    _check_buffer("workspace", workspace, torch.uint8, DIAG_WORKSPACE_BYTES, x.device)
+    _on_gpu(x)
     st = _lib().ufp4_quant_diag(_ptr(x), rows, cols, ld, ctypes.byref(cfg), _ptr(stats),
-                                _stream(x))
+                                _ptr(workspace), _stream(x))
     _check("ufp4_quant_diag", st)
     return stats
 
@@ -210,12 +290,16 @@ def ufp4_rht_quant_segmented(x: torch.Tensor, row_offsets: Sequence[int], cfg: Q
     """Column-wise quantization of row segments of x (per-expert transposed
     operands).  Returns a QTensor with P = cols and K = rows whose storage is
     segment-major (segment g: [cols, L_g] at element offset cols*offset_g)."""
+    _check_x(x)
     rows, cols = x.shape
     dev = x.device
     if codes is None:
         codes = torch.empty(cols * rows // 2, dtype=torch.uint8, device=dev)
     if scales is None:
         scales = torch.empty(cols * rows // cfg.block_cols, dtype=scales_dtype(cfg), device=dev)
+    _check_buffer("codes", codes, torch.uint8, _codes_elems(cols, rows, cfg), dev)
+    _check_buffer("scales", scales, scales_dtype(cfg), _scales_elems(cols, rows, cfg), dev)
+    _on_gpu(x)
     off = _i64arr(row_offsets)
     st = _lib().ufp4_rht_quant_segmented(_ptr(x), rows, cols, x.stride(0), off,
                                          len(row_offsets) - 1, ctypes.byref(cfg), _ptr(codes),
@@ -230,6 +314,7 @@ def ufp4_rht_quant_dual(x: torch.Tensor, cfg_row: QuantCfg, cfg_col: QuantCfg,
     row segment when row_offsets is given) quantization from one read of x.
     Returns (QTensor row, QTensor col); out_row / out_col: optional
     (codes, scales) pairs to write into."""
+    _check_x(x)
     rows, cols = x.shape
     dev = x.device
     cr, sr = out_row if out_row is not None else (
@@ -238,6 +323,11 @@ def ufp4_rht_quant_dual(x: torch.Tensor, cfg_row: QuantCfg, cfg_col: QuantCfg,
     cc, sc = out_col if out_col is not None else (
         torch.empty(rows * cols // 2, dtype=torch.uint8, device=dev),
         torch.empty(rows * cols // cfg_col.block_cols, dtype=scales_dtype(cfg_col), device=dev))
+    _check_buffer("codes_row", cr, torch.uint8, _codes_elems(rows, cols, cfg_row), dev)
+    _check_buffer("scales_row", sr, scales_dtype(cfg_row), _scales_elems(rows, cols, cfg_row), dev)
+    _check_buffer("codes_col", cc, torch.uint8, _codes_elems(cols, rows, cfg_col), dev)
+    _check_buffer("scales_col", sc, scales_dtype(cfg_col), _scales_elems(cols, rows, cfg_col), dev)
+    _on_gpu(x)
     off = _i64arr(row_offsets) if row_offsets is not None else None
     nseg = len(row_offsets) - 1 if row_offsets is not None else 1
     st = _lib().ufp4_rht_quant_dual(_ptr(x), rows, cols, x.stride(0), off, nseg,
@@ -257,6 +347,7 @@ def ufp4_dequant(q: QTensor, out=None):
     if out is None:
         out = torch.empty((q.P, q.K), dtype=torch.float32, device=q.codes.device)
     qc = q.c()
+    _check_matrix("out", out, q.P, q.K, q.codes.device)
     st = _lib().ufp4_dequant(ctypes.byref(qc), _ptr(out), out.stride(0), _stream(out))
     _check("ufp4_dequant", st)
     return out
@@ -266,6 +357,7 @@ def _gemm(name, A: QTensor, B: QTensor, out=None):
     if out is None:
         out = torch.empty((A.P, B.P), dtype=torch.float32, device=A.codes.device)
     a, b = A.c(), B.c()
+    _check_matrix("out", out, A.P, B.P, A.codes.device)
     st = getattr(_lib(), name)(ctypes.byref(a), ctypes.byref(b), _ptr(out), out.stride(0),
                                _stream(out))
     _check(name, st)
@@ -291,6 +383,7 @@ def _gemm_grouped(name, A: QTensor, B: QTensor, offsets, rows, cols, out=None):
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.float32, device=A.codes.device)
     a, b = A.c(), B.c()
+    _check_matrix("out", out, rows, cols, A.codes.device)
     off = _i64arr(offsets)
     st = getattr(_lib(), name)(ctypes.byref(a), ctypes.byref(b), len(offsets) - 1, off,
                                _ptr(out), out.stride(0), _stream(out))

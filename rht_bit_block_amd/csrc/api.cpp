@@ -145,6 +145,8 @@ int gemm_dense(const ufp4_qtensor* A, const ufp4_qtensor* B, float* C, int64_t l
   if (ldc < B->P) return UFP4_ERR_INVALID_ARG;
   if (A->P == 0 || B->P == 0) return UFP4_OK;
   if (!C) return UFP4_ERR_INVALID_ARG;
+  // empty shared dimension: C = 0, no operand storage is read (it may be null)
+  if (A->K == 0) return hip_status(launch_zero_c(C, A->P, B->P, ldc, (hipStream_t)stream));
   GemmLaunch g;
   fill_gemm(g, A, B, C, ldc);
   g.mode = 0;
@@ -183,6 +185,7 @@ int gemm_grouped_rows(const ufp4_qtensor* A, const ufp4_qtensor* B, int32_t G,
   if (st) return st;
   const int64_t R = B->P / G;
   if (!C || ldc < R) return UFP4_ERR_INVALID_ARG;
+  if (A->K == 0) return hip_status(launch_zero_c(C, A->P, R, ldc, (hipStream_t)stream));
   GemmLaunch g;
   fill_gemm(g, A, B, C, ldc);
   g.mode = 1;
@@ -202,6 +205,35 @@ int gemm_grouped_rows(const ufp4_qtensor* A, const ufp4_qtensor* B, int32_t G,
 }
 
 }  // namespace
+
+namespace ufp4 {
+
+static_assert(kDiagWorkspaceBytes == UFP4_DIAG_WORKSPACE_BYTES, "diagnostics workspace size");
+
+// Validation and launch description of a level-statistics call (shared by
+// ufp4_quant_diag and its variant on the library's own scratch array).
+int diag_prepare(const void* x, int64_t rows, int64_t cols, int64_t ld, const ufp4_quant_cfg* cfg,
+                 const uint64_t* stats, QuantLaunch& q) {
+  if (rows < 0 || cols < 0 || (rows > 0 && ld < cols)) return UFP4_ERR_INVALID_ARG;
+  int st = check_cfg(cfg);
+  if (st) return st;
+  if (!stats || !aligned(stats, 8)) return UFP4_ERR_INVALID_ARG;
+  if (cfg->block_rows != 1 || cfg->grid == UFP4_E4M3) return UFP4_ERR_UNSUPPORTED;
+  const int64_t P = rows, K = cols;
+  if (P > 0 && K > 0) {
+    if (!x) return UFP4_ERR_INVALID_ARG;
+    if (K % cfg->rht_n || K % cfg->block_cols) return UFP4_ERR_SHAPE;
+    if (!aligned(x, 16) || ld % 8) return UFP4_ERR_INVALID_ARG;
+    const int W = lane_width(cfg->rht_n, cfg->block_cols);
+    if (P * (K / W) > (int64_t)UINT32_MAX || K > (int64_t)UINT32_MAX) return UFP4_ERR_UNSUPPORTED;
+  }
+  fill_common(q, x, rows, cols, ld, cfg, nullptr, nullptr, nullptr);
+  q.P = P;
+  q.K = K;
+  return UFP4_OK;
+}
+
+}  // namespace ufp4
 
 extern "C" {
 
@@ -269,26 +301,15 @@ int ufp4_rht_quant(const void* x, int64_t rows, int64_t cols, int64_t ld, int32_
 }
 
 int ufp4_quant_diag(const void* x, int64_t rows, int64_t cols, int64_t ld,
-                    const ufp4_quant_cfg* cfg, uint64_t* stats, void* stream) {
-  if (rows < 0 || cols < 0 || (rows > 0 && ld < cols)) return UFP4_ERR_INVALID_ARG;
-  int st = check_cfg(cfg);
-  if (st) return st;
-  if (!stats || !aligned(stats, 8)) return UFP4_ERR_INVALID_ARG;
-  if (cfg->block_rows != 1 || cfg->grid == UFP4_E4M3) return UFP4_ERR_UNSUPPORTED;
-  const int64_t P = rows, K = cols;
-  if (P > 0 && K > 0) {
-    if (!x) return UFP4_ERR_INVALID_ARG;
-    if (K % cfg->rht_n || K % cfg->block_cols) return UFP4_ERR_SHAPE;
-    if (!aligned(x, 16) || ld % 8) return UFP4_ERR_INVALID_ARG;
-    const int W = lane_width(cfg->rht_n, cfg->block_cols);
-    if (P * (K / W) > (int64_t)UINT32_MAX || K > (int64_t)UINT32_MAX) return UFP4_ERR_UNSUPPORTED;
-  }
+                    const ufp4_quant_cfg* cfg, uint64_t* stats, void* workspace,
+                    void* stream) {
   QuantLaunch q;
-  fill_common(q, x, rows, cols, ld, cfg, nullptr, nullptr, nullptr);
-  q.P = P;
-  q.K = K;
+  const int st = ufp4::diag_prepare(x, rows, cols, ld, cfg, stats, q);
+  if (st) return st;
+  if (!workspace || !aligned(workspace, 8)) return UFP4_ERR_INVALID_ARG;
   // an empty operand still zeroes stats (the zeroing kernel runs first)
   return hip_status(launch_quant_diag(q, reinterpret_cast<unsigned long long*>(stats),
+                                      reinterpret_cast<unsigned long long*>(workspace),
                                       (hipStream_t)stream));
 }
 

@@ -339,28 +339,32 @@ __global__ __launch_bounds__(kThreads8) void k_gemm8(GemmLaunch g) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
 
-  decode_row<GRID, SMODE>(fetch<SMODE>(cur, 0), rm, lds, part, row);
-  Fetched x = fetch<SMODE>(cur, 1), y;
-  __syncthreads();
-
-  auto body = [&](int step, const Fetched& d, Fetched& l) {
-    const uint4* cb = lds + (step & 1) * kStage;
-    uint4* nb = lds + ((step + 1) & 1) * kStage;
-    l = fetch<SMODE>(cur, step + 2);
-    Frags8 f;
-    load_frags8(cb, 0, lane, wm, wn, f);
-    mfma_khalf8(acc, f);
-    decode_row<GRID, SMODE>(d, rm, nb, part, row);
-    load_frags8(cb, 1, lane, wm, wn, f);
-    mfma_khalf8(acc, f);
+  // K == 0 (an empty expert, or an empty operand whose storage may be null):
+  // no code or scale is read and the tile stores zeros.
+  if (nsteps > 0) {
+    decode_row<GRID, SMODE>(fetch<SMODE>(cur, 0), rm, lds, part, row);
+    Fetched x = fetch<SMODE>(cur, 1), y;
     __syncthreads();
-  };
-  int step = 0;
-  for (; step + 1 < nsteps; step += 2) {
-    body(step, x, y);
-    body(step + 1, y, x);
+
+    auto body = [&](int step, const Fetched& d, Fetched& l) {
+      const uint4* cb = lds + (step & 1) * kStage;
+      uint4* nb = lds + ((step + 1) & 1) * kStage;
+      l = fetch<SMODE>(cur, step + 2);
+      Frags8 f;
+      load_frags8(cb, 0, lane, wm, wn, f);
+      mfma_khalf8(acc, f);
+      decode_row<GRID, SMODE>(d, rm, nb, part, row);
+      load_frags8(cb, 1, lane, wm, wn, f);
+      mfma_khalf8(acc, f);
+      __syncthreads();
+    };
+    int step = 0;
+    for (; step + 1 < nsteps; step += 2) {
+      body(step, x, y);
+      body(step + 1, y, x);
+    }
+    if (step < nsteps) body(step, x, y);
   }
-  if (step < nsteps) body(step, x, y);
 
   {
     const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;

@@ -178,6 +178,17 @@ __global__ void k_philox_fill(uint64_t seed, uint32_t stream, uint64_t first, in
   }
 }
 
+// C[r][c] = 0 for r < rows, c < cols of a row-major fp32 matrix with pitch
+// ld: the product over an empty shared dimension.
+__global__ void k_zero_c(float* c, int64_t rows, int64_t cols, int64_t ld) {
+  const int64_t n = rows * cols;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / cols;
+    c[r * ld + (i - r * cols)] = 0.0f;
+  }
+}
+
 int grid_for(int64_t work, int threads) {
   int64_t b = (work + threads - 1) / threads;
   if (b > 65536) b = 65536;
@@ -218,6 +229,13 @@ hipError_t launch_transpose(const uint8_t* codes, const void* scales, int64_t P,
   hipLaunchKernelGGL(k_transpose_scales, dim3(grid_for(rb * cb, 256)), dim3(256), 0, s,
                      reinterpret_cast<const uint8_t*>(scales), rb, cb, smode == 0 ? 4 : 1,
                      reinterpret_cast<uint8_t*>(dscales));
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_c(float* c, int64_t rows, int64_t cols, int64_t ld, hipStream_t s) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_c, dim3(grid_for(rows * cols, 256)), dim3(256), 0, s, c, rows, cols,
+                     ld);
   return hipGetLastError();
 }
 

@@ -39,11 +39,12 @@ hipError_t launch_quant_dual(const QuantLaunch& q, const RowSide& r, hipStream_t
   }
 }
 
-hipError_t launch_quant_diag(const QuantLaunch& q, unsigned long long* stats, hipStream_t s) {
+hipError_t launch_quant_diag(const QuantLaunch& q, unsigned long long* stats,
+                             unsigned long long* partials, hipStream_t s) {
   switch (q.grid) {
-    case 0: return quant_diag_grid<0>(q, stats, s);
-    case 1: return quant_diag_grid<1>(q, stats, s);
-    default: return quant_diag_grid<2>(q, stats, s);
+    case 0: return quant_diag_grid<0>(q, stats, partials, s);
+    case 1: return quant_diag_grid<1>(q, stats, partials, s);
+    default: return quant_diag_grid<2>(q, stats, partials, s);
   }
 }
 

@@ -543,18 +543,17 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantLaunch q, FastDiv 
 // the workgroup sums its columns and adds them (64-bit integer atomics) to
 // a partial set: counts [0..7], error sums [8..15].
 // ---------------------------------------------------------------------------
-// Partial statistics of the workgroups (one file-scope array per translation
-// unit, used only by name inside the kernels below): the zeroing kernel
-// clears them, workgroup b adds into set b % kDiagSlots, and the final
-// kernel sums the sets into the caller's stats.  Diagnostics calls that
-// overlap on one GPU therefore race; the three launches of one call are
-// ordered by its stream.
-constexpr int kDiagSlots = 64;
-static __device__ unsigned long long g_diag_partials[kDiagSlots * 16];
+// Partial statistics of the workgroups live in a device buffer of
+// kDiagSlots sets of 16 words (kDiagWorkspaceBytes) that the caller passes:
+// the zeroing kernel clears them, workgroup b adds into set b % kDiagSlots,
+// and the final kernel sums the sets into the caller's stats.  The three
+// launches of one call are ordered by its stream; two calls may overlap only
+// with different buffers.
 
 template <int W, int B, int N, int GRID, int RND>
 __global__ __launch_bounds__(kThreads) void k_quant_diag(QuantLaunch q, FastDiv segs_per_row,
-                                                         uint32_t nseg) {
+                                                         uint32_t nseg,
+                                                         unsigned long long* partials) {
   __shared__ DiagLds d;
   constexpr int lpc = N > W ? N / W : 1;
 #pragma unroll
@@ -610,7 +609,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_diag(QuantLaunch q, FastDiv 
     sm += __shfl_xor(sm, off);
   }
   if (part == 0) {   // one of kDiagSlots partial sets, so few workgroups share an address
-    unsigned long long* slot = g_diag_partials + (blockIdx.x % kDiagSlots) * 16;
+    unsigned long long* slot = partials + (blockIdx.x % kDiagSlots) * 16;
     atomicAdd(slot + lev, c);
     atomicAdd(slot + 8 + lev, (unsigned long long)sm);
   }
@@ -1034,21 +1033,22 @@ hipError_t run_rows(const QuantLaunch& q, hipStream_t s) {
 }
 
 template <int G>
-__global__ void k_diag_zero() {
-  for (int i = threadIdx.x; i < kDiagSlots * 16; i += blockDim.x) g_diag_partials[i] = 0ull;
+__global__ void k_diag_zero(unsigned long long* partials) {
+  for (int i = threadIdx.x; i < kDiagSlots * 16; i += blockDim.x) partials[i] = 0ull;
 }
 
 template <int G>
-__global__ void k_diag_final(unsigned long long* stats) {
+__global__ void k_diag_final(const unsigned long long* partials, unsigned long long* stats) {
   if (threadIdx.x >= 16) return;
   unsigned long long t = 0;
-  for (int s = 0; s < kDiagSlots; ++s) t += g_diag_partials[s * 16 + threadIdx.x];
+  for (int s = 0; s < kDiagSlots; ++s) t += partials[s * 16 + threadIdx.x];
   stats[threadIdx.x] = t;
 }
 
 template <int W, int B, int N, int G, int R>
-hipError_t run_diag(const QuantLaunch& q, unsigned long long* stats, hipStream_t s) {
-  hipLaunchKernelGGL(k_diag_zero<G>, dim3(1), dim3(256), 0, s);
+hipError_t run_diag(const QuantLaunch& q, unsigned long long* stats,
+                    unsigned long long* partials, hipStream_t s) {
+  hipLaunchKernelGGL(k_diag_zero<G>, dim3(1), dim3(256), 0, s, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t segs_per_row = (uint32_t)(q.K / W);
@@ -1058,25 +1058,26 @@ hipError_t run_diag(const QuantLaunch& q, unsigned long long* stats, hipStream_t
     const uint64_t cap = (uint64_t)device_grid_limit() * 8;
     const uint32_t blocks = (uint32_t)(blocks_needed < cap ? blocks_needed : cap);
     hipLaunchKernelGGL((k_quant_diag<W, B, N, G, R>), dim3(blocks), dim3(kThreads), 0, s, q,
-                       make_fastdiv(segs_per_row), (uint32_t)nseg);
+                       make_fastdiv(segs_per_row), (uint32_t)nseg, partials);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_diag_final<G>, dim3(1), dim3(64), 0, s, stats);
+  hipLaunchKernelGGL(k_diag_final<G>, dim3(1), dim3(64), 0, s, partials, stats);
   return hipGetLastError();
 }
 
 template <int G>
-hipError_t run_diag_1d(const QuantLaunch& q, unsigned long long* stats, hipStream_t s) {
-#define UFP4_RUN(B_, N_)                                                       \
-  if (q.bc == B_ && q.n == N_) {                                              \
-    constexpr int W_ = (B_ == 32 || N_ >= 32) ? 32 : 16;                      \
-    if (B_ == 32 && q.scale_mode == 1) {                                       \
-      if (q.rounding == 0) return run_diag<W_, B_, N_, G, 2>(q, stats, s);     \
-      return run_diag<W_, B_, N_, G, 3>(q, stats, s);                          \
-    }                                                                          \
-    if (q.rounding == 0) return run_diag<W_, B_, N_, G, 0>(q, stats, s);       \
-    return run_diag<W_, B_, N_, G, 1>(q, stats, s);                            \
+hipError_t run_diag_1d(const QuantLaunch& q, unsigned long long* stats,
+                       unsigned long long* partials, hipStream_t s) {
+#define UFP4_RUN(B_, N_)                                                                \
+  if (q.bc == B_ && q.n == N_) {                                                       \
+    constexpr int W_ = (B_ == 32 || N_ >= 32) ? 32 : 16;                               \
+    if (B_ == 32 && q.scale_mode == 1) {                                                \
+      if (q.rounding == 0) return run_diag<W_, B_, N_, G, 2>(q, stats, partials, s);    \
+      return run_diag<W_, B_, N_, G, 3>(q, stats, partials, s);                         \
+    }                                                                                   \
+    if (q.rounding == 0) return run_diag<W_, B_, N_, G, 0>(q, stats, partials, s);      \
+    return run_diag<W_, B_, N_, G, 1>(q, stats, partials, s);                           \
   }
 #define UFP4_RUN_B(B_) \
   UFP4_RUN(B_, 1) UFP4_RUN(B_, 2) UFP4_RUN(B_, 4) UFP4_RUN(B_, 8) UFP4_RUN(B_, 16) \
@@ -1185,6 +1186,6 @@ template <int G> hipError_t quant_cols_grid(const QuantLaunch& q, hipStream_t s)
 template <int G> hipError_t quant_rows_2d_grid(const QuantLaunch& q, hipStream_t s);
 template <int G> hipError_t quant_dual_grid(const QuantLaunch& q, const RowSide& r, hipStream_t s);
 template <int G> hipError_t quant_diag_grid(const QuantLaunch& q, unsigned long long* stats,
-                                           hipStream_t s);
+                                           unsigned long long* partials, hipStream_t s);
 
 }  // namespace ufp4

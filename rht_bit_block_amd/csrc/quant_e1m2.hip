@@ -22,8 +22,9 @@ hipError_t quant_dual_grid<0>(const QuantLaunch& q, const RowSide& r, hipStream_
 }
 
 template <>
-hipError_t quant_diag_grid<0>(const QuantLaunch& q, unsigned long long* stats, hipStream_t s) {
-  return qk::run_diag_1d<0>(q, stats, s);
+hipError_t quant_diag_grid<0>(const QuantLaunch& q, unsigned long long* stats,
+                             unsigned long long* partials, hipStream_t s) {
+  return qk::run_diag_1d<0>(q, stats, partials, s);
 }
 
 }  // namespace ufp4

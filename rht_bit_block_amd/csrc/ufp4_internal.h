@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ufp4.h"
+
 #include <atomic>
 
 namespace ufp4 {
@@ -108,7 +110,18 @@ struct RowSide {
 
 hipError_t launch_quant_rows(const QuantLaunch& q, hipStream_t s);
 hipError_t launch_quant_dual(const QuantLaunch& q, const RowSide& r, hipStream_t s);
-hipError_t launch_quant_diag(const QuantLaunch& q, unsigned long long* stats, hipStream_t s);
+// Level statistics: `partials` is a device buffer of kDiagWorkspaceBytes,
+// 8-byte aligned, cleared and used by the call (partial sums of the
+// workgroups); calls that overlap must not share it.
+constexpr int kDiagSlots = 64;
+constexpr size_t kDiagWorkspaceBytes = (size_t)kDiagSlots * 16 * sizeof(unsigned long long);
+hipError_t launch_quant_diag(const QuantLaunch& q, unsigned long long* stats,
+                             unsigned long long* partials, hipStream_t s);
+// Argument checks and launch description of a level-statistics call (the
+// arguments of ufp4_quant_diag without its workspace); UFP4_OK or a status.
+int diag_prepare(const void* x, int64_t rows, int64_t cols, int64_t ld, const ufp4_quant_cfg* cfg,
+                 const uint64_t* stats, QuantLaunch& q);
+
 hipError_t launch_quant_cols(const QuantLaunch& q, hipStream_t s);
 hipError_t launch_quant_rows_2d(const QuantLaunch& q, hipStream_t s);
 
@@ -162,6 +175,9 @@ hipError_t launch_dequant(const uint8_t* codes, const void* scales, int64_t P, i
 hipError_t launch_transpose(const uint8_t* codes, const void* scales, int64_t P, int64_t K,
                             int32_t b, int32_t scale_mode, uint8_t* dcodes, void* dscales,
                             hipStream_t s);
+// Writes zeros into C [rows][ld] (columns 0 .. cols-1): a GEMM whose shared
+// dimension is empty.
+hipError_t launch_zero_c(float* c, int64_t rows, int64_t cols, int64_t ld, hipStream_t s);
 hipError_t launch_philox_fill(uint64_t seed, uint32_t stream_id, uint64_t first, int64_t n,
                               uint16_t* out, hipStream_t s);
 

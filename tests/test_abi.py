@@ -185,10 +185,10 @@ def test_dual_quant_argument_errors():
     assert _dual(lib, rows=0) == E.UFP4_OK
 
 
-def _diag(lib, x=FAKE, rows=64, cols=64, ld=64, cfg=None, stats=FAKE):
+def _diag(lib, x=FAKE, rows=64, cols=64, ld=64, cfg=None, stats=FAKE, ws=FAKE):
     c = cfg or U.make_cfg()
     return lib.ufp4_quant_diag(ctypes.c_void_p(x), rows, cols, ld, ctypes.byref(c),
-                               ctypes.c_void_p(stats), None)
+                               ctypes.c_void_p(stats), ctypes.c_void_p(ws), None)
 
 
 def test_diag_argument_errors():
@@ -197,6 +197,9 @@ def test_diag_argument_errors():
     lib = U.lib_handle()
     E = U
     assert _diag(lib, stats=0) == E.UFP4_ERR_INVALID_ARG
+    assert _diag(lib, ws=0) == E.UFP4_ERR_INVALID_ARG               # workspace required
+    assert _diag(lib, ws=FAKE + 4) == E.UFP4_ERR_INVALID_ARG        # 8-byte alignment
+    assert _diag(lib, rows=0, ws=0) == E.UFP4_ERR_INVALID_ARG
     assert _diag(lib, stats=FAKE + 4) == E.UFP4_ERR_INVALID_ARG     # 8-byte alignment
     assert _diag(lib, rows=0, stats=0) == E.UFP4_ERR_INVALID_ARG
     assert _diag(lib, x=0) == E.UFP4_ERR_INVALID_ARG

@@ -300,3 +300,71 @@ def test_config2_mxfp8():
     assert_quant_rows(qx.codes, qx.scales, ox, rM, "X row (MXFP8)")
     assert_quant_rows(qw.codes, qw.scales, ow, rN, "W row (MXFP8)")
     assert_gemm(Y, rM, rN, deq(ox, cfg), deq(ow, cfg), "fprop (MXFP8)")
+
+
+# ---------------------------------------------------------------------------
+# The dense layer's quantizations exactly as bench.py's step makes them: one
+# dual-axis call per tensor (X, W row- and column-wise RTNE; dY with SR on
+# streams 0 / 1).  Sampled rows of the row-wise outputs and sampled columns
+# of the column-wise ones are bit-exact against the oracle; every output is
+# also identical to the corresponding single-axis call's.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("grid", [U.UFP4_E1M2, U.UFP4_INT4, U.UFP4_E2M1])
+def test_config2_dual_calls(grid):
+    _case("config2 dual", grid)
+    wl = workloads.config2("cuda")
+    sf, sd, sw = wl.meta["sign_seeds"]
+    sr = wl.meta["sr_seed"]
+    mk = lambda seed, rnd, st=0: U.make_cfg(grid, rnd, U.UFP4_SCALE_F32, 1, 16, 16,  # noqa: E731
+                                              sign_seed=seed, sr_seed=sr, sr_stream=st)
+    calls = (("X", mk(sf, U.UFP4_RTNE), mk(sw, U.UFP4_RTNE)),
+             ("W", mk(sf, U.UFP4_RTNE), mk(sd, U.UFP4_RTNE)),
+             ("dY", mk(sd, U.UFP4_SR, 0), mk(sw, U.UFP4_SR, 1)))
+    for i, (name, cr, cc) in enumerate(calls):
+        t = wl.tensors[name]
+        R, C = t.shape
+        qr, qc = U.ufp4_rht_quant_dual(t, cr, cc)
+        torch.cuda.synchronize()
+        rr, rc = pick(R, 24, 100 + i), pick(C, 24, 200 + i)
+        o_r = O.quantize(rows_bits(t, rr), 0, spec_of(cr), row_index=rr)
+        o_c = O.quantize(cols_bits(t, rc), 1, spec_of(cc), row_index=rc)
+        assert_quant_rows(qr.codes.view(R, C // 2), qr.scales.view(R, C // 16), o_r, rr,
+                          f"{name} dual row")
+        assert_quant_rows(qc.codes.view(C, R // 2), qc.scales.view(C, R // 16), o_c, rc,
+                          f"{name} dual col")
+        sr_, _ = U.ufp4_rht_quant(t, 0, cr)
+        sc_, _ = U.ufp4_rht_quant(t, 1, cc)
+        assert torch.equal(qr.codes.view(R, C // 2), sr_.codes), f"{name}: row codes vs single-axis"
+        assert torch.equal(qr.scales.view(R, C // 16), sr_.scales), f"{name}: row scales"
+        assert torch.equal(qc.codes.view(C, R // 2), sc_.codes), f"{name}: col codes vs single-axis"
+        assert torch.equal(qc.scales.view(C, R // 16), sc_.scales), f"{name}: col scales"
+        del qr, qc, sr_, sc_
+
+
+# ---------------------------------------------------------------------------
+# Every element of the dense layer's FPROP (E1M2, 8192 x 8192 x 2048, the
+# XCD-grouped tile order over all 1024 tiles) against the oracle's fp64
+# product of its own full quantizations of X and W.
+# ---------------------------------------------------------------------------
+def test_config2_fprop_full_output():
+    _case("config2 full fprop")
+    wl = workloads.config2("cuda")
+    X, W = wl.tensors["X"], wl.tensors["W"]
+    sf = wl.meta["sign_seeds"][0]
+    cfg = U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=sf)
+    qx, _ = U.ufp4_rht_quant(X, 0, cfg)
+    qw, _ = U.ufp4_rht_quant(W, 0, cfg)
+    Y = U.ufp4_gemm_fprop(qx, qw).cpu().numpy()
+    ox = O.quantize(host_bits(X), 0, spec_of(cfg))
+    ow = O.quantize(host_bits(W), 0, spec_of(cfg))
+    assert np.array_equal(qx.codes.cpu().numpy(), ox["codes"])
+    assert np.array_equal(qw.codes.cpu().numpy(), ow["codes"])
+    ref = O.gemm_ref(deq(ox, cfg), deq(ow, cfg))
+    err = O.rel_fro(Y, ref)
+    # every 256 x 256 tile on its own, so a misplaced or skipped tile shows
+    tiles = Y.shape[0] // 256, Y.shape[1] // 256
+    worst = max(O.rel_fro(Y[256 * i:256 * i + 256, 256 * j:256 * j + 256],
+                          ref[256 * i:256 * i + 256, 256 * j:256 * j + 256])
+                for i in range(tiles[0]) for j in range(tiles[1]))
+    print(f"  rel. Frobenius error {err:.3e}, worst tile {worst:.3e}", flush=True)
+    assert err <= GEMM_TOL and worst <= GEMM_TOL

@@ -598,3 +598,127 @@ def test_gemm_fp32_partial_stage(grid, bc, K):
     n = 16 if K % 16 == 0 else 1
     cfg = U.make_cfg(grid, U.UFP4_SR, U.UFP4_SCALE_F32, 1, bc, n, sign_seed=31, sr_seed=37)
     _gemm_case(272, 300, K, cfg, cfg, seed=K + 7 * bc + grid)
+
+
+# ---------------------------------------------------------------------------
+# An empty shared dimension (K = 0): C = 0 and no operand storage is read
+# (it may be null, as torch's empty tensors are).  Covers the kernel families
+# whose first K step used to be fetched before the loop: the general
+# split-bf16 kernel (mixed block widths; grouped power-of-two operands) and
+# the scaled-MFMA kernel of the uniform grids; grouped WGRAD with empty
+# experts in the middle and at the end, with mixed block widths.
+# ---------------------------------------------------------------------------
+def _empty_q(P, cfg):
+    return U.QTensor(torch.empty((P, 0), dtype=torch.uint8, device="cuda"),
+                     torch.empty((P, 0), dtype=U.scales_dtype(cfg), device="cuda"), P, 0, cfg)
+
+
+K0_CASES = [
+    ("mixed 1x16 / 1x32 fp32", U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=1),
+     U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 32, 16, sign_seed=1)),
+    ("1x16 fp32", U.make_cfg(U.UFP4_INT4, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=1), None),
+    ("1x32 E8M0 E1M2", U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 1), None),
+    ("1x32 E8M0 E2M1", U.make_cfg(U.UFP4_E2M1, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 1), None),
+    ("32x32 E8M0 INT4", U.make_cfg(U.UFP4_INT4, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 32, 32, 1), None),
+    ("MXFP8", U.make_cfg(U.UFP4_E4M3, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 1), None),
+]
+
+
+@pytest.mark.parametrize("name,cfg_a,cfg_b", K0_CASES, ids=[c[0] for c in K0_CASES])
+def test_gemm_empty_k(name, cfg_a, cfg_b):
+    _print_case("K = 0", name)
+    cfg_b = cfg_b or cfg_a
+    PA, PB = 96, 64
+    qa, qb = _empty_q(PA, cfg_a), _empty_q(PB, cfg_b)
+    C = torch.full((PA, PB + 8), 7.0, dtype=torch.float32, device="cuda")
+    U.ufp4_gemm_fprop(qa, qb, out=C[:, :PB])
+    host = C.cpu().numpy()
+    assert np.all(host[:, :PB] == 0.0) and np.all(host[:, PB:] == 7.0)
+    if cfg_a.grid == U.UFP4_E4M3:
+        return                                   # MXFP8 GEMMs are dense only
+    G = 2
+    Y = torch.full((PA, 32), 7.0, dtype=torch.float32, device="cuda")
+    U.ufp4_gemm_fprop_grouped(qa, _empty_q(G * 32, cfg_b), [0, 32, PA], out=Y)
+    assert torch.count_nonzero(Y).item() == 0
+
+
+@pytest.mark.parametrize("bc_a,bc_b", [(16, 32), (32, 16), (16, 16)])
+def test_grouped_wgrad_empty_experts(bc_a, bc_b):
+    """Experts 1 and 3 (the last) have no tokens: their dW is zero and the
+    others match per-expert oracle products (mixed block widths run on the
+    general kernel, equal ones on the scale-product kernel)."""
+    _print_case("wgrad empty experts", bc_a, bc_b)
+    off = [0, 64, 64, 128, 128]
+    G, N, H = 4, 96, 160
+    T = off[-1]
+    tdy, tx = rand_bits(T, N, 81), rand_bits(T, H, 82)
+    ca = U.make_cfg(U.UFP4_E1M2, U.UFP4_SR, U.UFP4_SCALE_F32, 1, bc_a, 32, sign_seed=9, sr_seed=3, sr_stream=1)
+    cb = U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, bc_b, 32, sign_seed=9)
+    qdyt = U.ufp4_rht_quant_segmented(dev_bf16(tdy), off, ca)
+    qxt = U.ufp4_rht_quant_segmented(dev_bf16(tx), off, cb)
+    dW = torch.full((G * N, H), 7.0, dtype=torch.float32, device="cuda")
+    U.ufp4_gemm_wgrad_grouped(qdyt, qxt, off, out=dW)
+    dW = dW.cpu().numpy()
+    r_dyt = O.quantize_segmented(tdy, off, spec_of(ca))
+    r_xt = O.quantize_segmented(tx, off, spec_of(cb))
+    for g in range(G):
+        blk = dW[g * N:(g + 1) * N]
+        if off[g + 1] == off[g]:
+            assert np.all(blk == 0.0), g
+            continue
+        ref = O.gemm_ref(oracle_dequant64(r_dyt[g], ca), oracle_dequant64(r_xt[g], cb))
+        assert O.rel_fro(blk, ref) <= GEMM_TOL, g
+
+
+# ---------------------------------------------------------------------------
+# Grouped FPROP / DGRAD with power-of-two (E8M0) scales, 1 x 32 and 32 x 32
+# blocks, every grid: per-expert products against the oracle's (one expert
+# empty, experts of 32, 96 and 160 tokens).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("br", [1, 32])
+def test_grouped_gemms_pow2(grid, br):
+    _print_case("grouped pow2", grid, br)
+    G, H, F = 4, 256, 128
+    off = [0, 32, 32, 128, 288]
+    T = off[-1]
+    n = 1 if br == 32 else 32
+    cx = U.make_cfg(grid, U.UFP4_RTNE, U.UFP4_SCALE_POW2, br, 32, n, sign_seed=44)
+    cd = U.make_cfg(grid, U.UFP4_SR, U.UFP4_SCALE_POW2, br, 32, n, sign_seed=45, sr_seed=5, sr_stream=0)
+    tx, tw, tdy = rand_bits(T, H, 51), rand_bits(G * F, H, 52), rand_bits(T, F, 53)
+    qx, rx = compare_quant(tx, 0, cx, with_rotated=False)
+    qw, rw = compare_quant(tw, 0, cx, with_rotated=False)
+    Y = U.ufp4_gemm_fprop_grouped(qx, qw, off).cpu().numpy()
+    dxq, dwq = oracle_dequant64(rx, cx), oracle_dequant64(rw, cx)
+    for g in range(G):
+        if off[g + 1] > off[g]:
+            ref = O.gemm_ref(dxq[off[g]:off[g + 1]], dwq[g * F:(g + 1) * F])
+            assert O.rel_fro(Y[off[g]:off[g + 1]], ref) <= GEMM_TOL, ("fprop", g)
+    # DGRAD: B = W^T of every expert.  1 x 32: per-expert column-wise
+    # quantization (segmented); 32 x 32: each expert's W quantized once and
+    # reused transposed (S(B) = S(B^T)), stacked.
+    qdy, rdy = compare_quant(tdy, 0, cd.copy(sign_seed=46), with_rotated=False)
+    cwt = cx.copy(sign_seed=46)
+    if br == 1:
+        qwt = U.stacked(U.ufp4_rht_quant_segmented(dev_bf16(tw), [g * F for g in range(G + 1)], cwt), G)
+        refs = O.quantize_segmented(tw, [g * F for g in range(G + 1)], spec_of(cwt))
+        dwt = [oracle_dequant64(r, cwt) for r in refs]
+    else:
+        qwe = U.ufp4_rht_quant(dev_bf16(tw), 0, cwt)[0]
+        t = U.ufp4_transpose_qtensor(U.QTensor(qwe.codes[:F], qwe.scales[:F // 32], F, H, cwt))
+        parts = [t]
+        for g in range(1, G):
+            parts.append(U.ufp4_transpose_qtensor(U.QTensor(qwe.codes[g * F:(g + 1) * F],
+                                                            qwe.scales[g * F // 32:(g + 1) * F // 32],
+                                                            F, H, cwt)))
+        qwt = U.QTensor(torch.cat([p.codes for p in parts]), torch.cat([p.scales for p in parts]),
+                        G * H, F, cwt)
+        rwe = O.quantize(tw, 0, spec_of(cwt))
+        dwe = oracle_dequant64(rwe, cwt)
+        dwt = [np.ascontiguousarray(dwe[g * F:(g + 1) * F].T) for g in range(G)]
+    dX = U.ufp4_gemm_dgrad_grouped(qdy, qwt, off).cpu().numpy()
+    ddy = oracle_dequant64(rdy, cd.copy(sign_seed=46))
+    for g in range(G):
+        if off[g + 1] > off[g]:
+            ref = O.gemm_ref(ddy[off[g]:off[g + 1]], dwt[g])
+            assert O.rel_fro(dX[off[g]:off[g + 1]], ref) <= GEMM_TOL, ("dgrad", g)
