@@ -177,6 +177,19 @@ int ufp4_quant_diag(const void* x, int64_t rows, int64_t cols, int64_t ld,
                     const ufp4_quant_cfg* cfg, uint64_t* stats, void* workspace,
                     void* stream);
 
+/* ufp4_quant_diag without the workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, statistics and errors as
+ * ufp4_quant_diag; the partial sums live in a scratch array of
+ * UFP4_DIAG_WORKSPACE_BYTES that the library holds on each GPU it runs on
+ * until the process ends (its address is looked up on the first call on a
+ * device).  The scratch does not grow with the input, so no size is refused
+ * for it.  The call allocates nothing; each call clears the scratch before
+ * use, and calls that overlap on one GPU (different streams or host threads)
+ * race on it -- order them on one stream. */
+int ufp4_quant_diag_noalloc(const void* x, int64_t rows, int64_t cols, int64_t ld,
+                            const ufp4_quant_cfg* cfg, uint64_t* stats, void* stream);
+
 /* Column-wise quantization of row segments (per-expert transposed operands):
  * the quantizer of ufp4_rht_quant ([UFP4] formats section; Method: X H'
  * along the shared dimension) applied to each expert's token range on its

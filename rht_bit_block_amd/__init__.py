@@ -26,6 +26,7 @@ UFP4_ERR_MISMATCH, UFP4_ERR_UNSUPPORTED, UFP4_ERR_HIP = -3, -4, -5
 
 EXPORTED = [
     "ufp4_rht_quant", "ufp4_rht_quant_segmented", "ufp4_rht_quant_dual", "ufp4_quant_diag",
+    "ufp4_quant_diag_noalloc",
     "ufp4_dequant",
     "ufp4_gemm_fprop", "ufp4_gemm_dgrad", "ufp4_gemm_wgrad",
     "ufp4_gemm_fprop_grouped", "ufp4_gemm_dgrad_grouped", "ufp4_gemm_wgrad_grouped",
@@ -106,6 +107,7 @@ def _lib():
             "ufp4_rht_quant_segmented": [vp, i64, i64, i64, i64p, i32, cfgp, vp, vp, vp],
             "ufp4_rht_quant_dual": [vp, i64, i64, i64, i64p, i32, cfgp, cfgp, vp, vp, vp, vp, vp],
             "ufp4_quant_diag": [vp, i64, i64, i64, cfgp, vp, vp, vp],
+            "ufp4_quant_diag_noalloc": [vp, i64, i64, i64, cfgp, vp, vp],
             "ufp4_dequant": [qtp, vp, i64, vp],
             "ufp4_gemm_fprop": [qtp, qtp, vp, i64, vp],
             "ufp4_gemm_dgrad": [qtp, qtp, vp, i64, vp],
@@ -282,6 +284,23 @@ def ufp4_quant_diag(x: torch.Tensor, cfg: QuantCfg, stats=None, ld: Optional[int
     st = _lib().ufp4_quant_diag(_ptr(x), rows, cols, ld, ctypes.byref(cfg), _ptr(stats),
                                 _ptr(workspace), _stream(x))
     _check("ufp4_quant_diag", st)
+    return stats
+
+
+def ufp4_quant_diag_noalloc(x: torch.Tensor, cfg: QuantCfg, stats=None, ld: Optional[int] = None):
+    """ufp4_quant_diag on the library's per-GPU scratch array instead of a
+    workspace (for callers that cannot allocate; calls that overlap on one
+    GPU race).  Returns the int64 [16] statistics."""
+    _check_x(x)
+    rows, cols = x.shape
+    ld = x.stride(0) if ld is None else ld
+    if stats is None:
+        stats = torch.empty(16, dtype=torch.int64, device=x.device)
+    _check_buffer("stats", stats, torch.int64, 16, x.device)
+    _on_gpu(x)
+    st = _lib().ufp4_quant_diag_noalloc(_ptr(x), rows, cols, ld, ctypes.byref(cfg), _ptr(stats),
+                                        _stream(x))
+    _check("ufp4_quant_diag_noalloc", st)
     return stats
 
 

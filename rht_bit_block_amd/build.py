@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "quant.hip", "quant_e1m2.hip", "quant_int4.hip", "quant_e2m1.hip", "quant_e4m3.hip",
-           "gemm.hip", "gemm_rd.hip", "gemm_mx.hip", "misc.hip"]
+           "gemm.hip", "gemm_rd.hip", "gemm_mx.hip", "misc.hip", "noalloc.hip"]
 
 # -ffp-contract=off: every fp32 operation that decides an output bit is an
 # explicit round-to-nearest op; no silent fma contraction.
