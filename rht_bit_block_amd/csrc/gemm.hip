@@ -52,7 +52,8 @@ struct Problem {
 };
 
 // Resolve which group a tile belongs to and the group's operand views.
-__device__ __forceinline__ Problem resolve(const GemmLaunch& g, int tile, int& tm, int& tn) {
+__device__ __forceinline__ Problem resolve(const GemmLaunch& g, int b, int& tm, int& tn) {
+  const int tile = xcd_linear(b, g.total_tiles);   // XCD-contiguous tile ranges
   int grp = 0;
   while (grp + 1 < g.ngroups && g.tile_start[grp + 1] <= tile) ++grp;
   const int local = tile - g.tile_start[grp];
@@ -86,12 +87,7 @@ __device__ __forceinline__ Problem resolve(const GemmLaunch& g, int tile, int& t
     pr.c = g.c + (int64_t)grp * g.PA * g.ldc;
   }
   const int tiles_n = (int)((pr.b_rows + TN - 1) / TN);
-  if (g.mode == 0) {   // one dense problem: XCD-aware grouped order
-    tile_order(tile, g.total_tiles, (int)((pr.a_rows + TM - 1) / TM), tiles_n, tm, tn);
-    return pr;
-  }
-  tm = local / max(tiles_n, 1);
-  tn = local - tm * tiles_n;
+  grouped_order(local, (int)((pr.a_rows + TM - 1) / TM), max(tiles_n, 1), tm, tn);
   return pr;
 }
 

@@ -17,24 +17,35 @@ namespace ufp4 {
 
 typedef float c_floatx16 __attribute__((ext_vector_type(16)));
 
-// Tile (tm, tn) that workgroup b of a dense T-tile launch computes.
-// Workgroups are dispatched round-robin over the 8 XCDs (b runs on XCD b % 8)
-// and each XCD has its own L2.  The tiles are first put in grouped order
-// (kGroupRows tile rows at a time, walking down a group's rows before moving
-// one tile column right), and each XCD then takes a contiguous range of that
-// order.  The 32 tiles one XCD runs at once then cover about 8 rows x 4
-// columns of C and share 12 operand strips, where a row-major range shares one
-// A strip and reads up to 32 B strips.
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
+// XCD b % 8) and each XCD has its own L2.  xcd_linear gives every XCD a
+// contiguous range of the launch's T tiles: XCD x takes T / 8 tiles, one more
+// when x < T % 8, and workgroup b is the (b / 8)-th of its XCD -- a bijection
+// of 0 .. T-1 for any T.
+__device__ __forceinline__ int xcd_linear(int b, int T) {
+  const int q = T / 8, r = T % 8, x = b % 8;
+  return x * q + (x < r ? x : r) + b / 8;
+}
+
+// Tile (tm, tn) at position w of the grouped order of a tiles_m x tiles_n
+// problem: kGroupRows tile rows at a time, walking down a group's rows before
+// moving one tile column right.  The 32 tiles one XCD runs at once then cover
+// about 8 rows x 4 columns of C and share 12 operand strips, where a
+// row-major range shares one A strip and reads up to 32 B strips.
 constexpr int kGroupRows = 8;
-__device__ __forceinline__ void tile_order(int b, int T, int tiles_m, int tiles_n, int& tm,
-                                           int& tn) {
-  const int v = T % 8 == 0 ? (b % 8) * (T / 8) + b / 8 : b;
-  const int group = v / (kGroupRows * tiles_n);
+__device__ __forceinline__ void grouped_order(int w, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int group = w / (kGroupRows * tiles_n);
   const int first = group * kGroupRows;
   const int gm = tiles_m - first < kGroupRows ? tiles_m - first : kGroupRows;
-  const int w = v - first * tiles_n;
-  tm = first + w % gm;
-  tn = w / gm;
+  const int u = w - first * tiles_n;
+  tm = first + u % gm;
+  tn = u / gm;
+}
+
+// Tile (tm, tn) that workgroup b of a dense T-tile launch computes.
+__device__ __forceinline__ void tile_order(int b, int T, int tiles_m, int tiles_n, int& tm,
+                                           int& tn) {
+  grouped_order(xcd_linear(b, T), tiles_m, tiles_n, tm, tn);
 }
 
 // True when a tile's C region fits a 32-bit buffer offset (else the caller

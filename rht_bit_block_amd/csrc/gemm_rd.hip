@@ -35,19 +35,23 @@
 // its odd ones, the same for A and B.
 //
 // Pipeline of step i (its fragments in registers): the decode of step i+1
-// during tiles 0-1, one barrier, then the fragments of step i+1 are read as
-// registers free up (B into a second set, each A fragment after its last
-// tile), so the LDS reads of a step are hidden under the tiles of the one
-// before.
+// during the first tile (its raw inputs were read from LDS during step i-1),
+// one barrier, then the fragments of step i+1 are read as registers free up,
+// so the LDS reads of a step are hidden under the tiles of the one before.
+// Inside a step the 16-wide kernel walks its 8 tiles column by column and
+// issues the level product of tile t+1 before the fmas of tile t (level
+// products double-buffered, the scale product of tile t+1 after them); each
+// operand fragment is reloaded right after its last product is issued.
 //
 // With 1 x 32 blocks one scale covers two 16-wide halves, so k_gemm_rd32
 // takes 32-wide steps: two chained level MFMAs, one scale product and one set
 // of fmas per tile and step.
 //
 // Tiling: 256 x 256 output tile per 512-thread workgroup, 2 x 4 waves of
-// 128 x 64 (4 x 2 tiles of 32 x 32, accumulators in VGPRs).  Dense launches
-// order tiles so that the tiles resident at once on an XCD share operand
-// strips in its L2.  Rows past the operand read as zeros (buffer bound).
+// 128 x 64 (4 x 2 tiles of 32 x 32, accumulators in VGPRs).  Every launch
+// gives each XCD a contiguous range of tiles in grouped order, so the tiles
+// resident at once on an XCD share operand strips in its L2.  Rows past the
+// operand read as zeros (buffer bound).
 #include "ufp4_internal.h"
 #include "gemm_epilogue.h"
 
@@ -257,8 +261,11 @@ struct Operands {
 };
 
 // The problem a tile belongs to (dense, grouped along A's rows, or grouped
-// along K) and the tile's coordinates inside it.
-__device__ __forceinline__ Operands resolve(const GemmLaunch& g, int tile, int& tm, int& tn) {
+// along K) and the tile's coordinates inside it.  Workgroup b takes position
+// xcd_linear(b) of the launch's tiles, so each XCD works through a contiguous
+// range (whole experts of a grouped launch), each problem in grouped order.
+__device__ __forceinline__ Operands resolve(const GemmLaunch& g, int b, int& tm, int& tn) {
+  const int tile = xcd_linear(b, g.total_tiles);
   int grp = 0;
   while (grp + 1 < g.ngroups && g.tile_start[grp + 1] <= tile) ++grp;
   const int local = tile - g.tile_start[grp];
@@ -289,8 +296,8 @@ __device__ __forceinline__ Operands resolve(const GemmLaunch& g, int tile, int& 
     o.c = g.c + (int64_t)grp * g.PA * g.ldc;
   }
   const int tiles_n = (int)((o.b_rows + TN - 1) / TN);
-  tm = local / (tiles_n > 0 ? tiles_n : 1);
-  tn = local - tm * tiles_n;
+  const int tiles_m = (int)((o.a_rows + TM - 1) / TM);
+  grouped_order(local, tiles_m, tiles_n > 0 ? tiles_n : 1, tm, tn);
   return o;
 }
 
@@ -311,9 +318,6 @@ __device__ __forceinline__ TileCtx tile_ctx(const GemmLaunch& g, const uint8_t* 
   TileCtx t;
   int tm, tn;
   t.o = resolve(g, blockIdx.x, tm, tn);
-  if (g.mode == 0)   // one dense problem: XCD-aware grouped order
-    tile_order(blockIdx.x, g.total_tiles, (int)((t.o.a_rows + TM - 1) / TM),
-               (int)((t.o.b_rows + TN - 1) / TN), tm, tn);
   const int lane = tid & 63;
   t.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   t.wm = t.wave >> 2;
@@ -391,56 +395,56 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
     wait_vmcnt<L::VMEM>();
     __syncthreads();
     decode_store<GRID, BC>(decode_load<BC>(lds, dop, drow, 0), decb, dop, drow);
+    DecIn dnx = decode_load<BC>(lds, dop, drow, 1);   // step 1 (stage 0 has landed)
     __syncthreads();
-    Frag fa[4], fb[2], fbn[2];
+    Frag fa[4], fb[2];
 #pragma unroll
     for (int t = 0; t < 4; ++t) fa[t] = frag_at(decb, code_a + 256 * t, pc_a + 512 * t);
 #pragma unroll
     for (int t = 0; t < 2; ++t) fb[t] = frag_at(decb, code_b + 256 * t, pc_b + 512 * t);
-    // Step i (its fragments in registers): decode step i+1 into the other
-    // buffer during tiles 0-1; barrier; then step i+1's fragments are read as
-    // registers free up (B right after the barrier into a second set, A[t]
-    // after its last tile), hidden under tiles 2-7.  Tile t = (t / 2, t % 2):
-    // one scheduling region holds the fmas of tile t and the MFMAs of tile
-    // t+1 (the compiler issues the fmas first; issuing tile t+1's level MFMA
-    // ahead of them, with the level products double-buffered, measured the
-    // same, so the order inside a wave is not what bounds a step).  Raw stage s
-    // (8 steps) is issued at step 8 (s - 1) and waited for at the barrier of
-    // the step that decodes its first step.
+    // Tiles of a step in column order: u = 0..7 is (A tile u & 3, B tile u >> 2).
+    // The products of tile u+1 are issued before the fmas of tile u (two sets
+    // in flight), the next step's tile 0 during tile 7.  An operand is
+    // reloaded for the next step after its last product was issued: fb[0]
+    // after u = 2, fa[k] after u = 3 + k, fb[1] after u = 6 -- all after the
+    // step's barrier, which follows the decode of the next step (u = 0).
+    floatx16 p[2], q;
+    p[0] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(fa[0].code, fb[0].code, floatx16{}, 0, 0, 0);
+    q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0].pc, fb[0].pc, floatx16{}, 0, 0, 0);
 #pragma clang loop unroll(disable)
     for (int i = 0; i < nsteps; ++i) {
       if (i > 0 && (i & 7) == 0) issue_stage<BC>(c, (i >> 3) + 1, ((i >> 3) + 1) & 1);
       const int n = i + 1;   // decoded during this step (past the end: unused)
-      const DecIn din = decode_load<BC>(lds + ((n >> 3) & 1) * L::RAW, dop, drow, n & 7);
+      const DecIn din = dnx;   // step n's raw inputs, loaded during the step before
       const uint8_t* dn = decb + (n & 1) * L::DEC;
-      floatx16 p[2], q[2];
-      mfma_tile(fa[0], fb[0], p[0], q[0]);
+      const bool more = i + 1 < nsteps;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        // INT4 puts tile t+1's MFMAs after tile t's fmas in the source: the
-        // compiler then keeps one set of products live (243 VGPRs instead of
-        // spilling; its decode needs a second byte table), 5-7 % faster; the
-        // other grids measure 1-2 % faster with the MFMAs first.
-        if constexpr (GRID != 1)
-          if (t + 1 < 8) mfma_tile(fa[(t + 1) >> 1], fb[(t + 1) & 1], p[(t + 1) & 1], q[(t + 1) & 1]);
+      for (int u = 0; u < 8; ++u) {
+        // level product of the next tile first, then this tile's fmas, then
+        // the next tile's scale product (only the level products are
+        // double-buffered)
+        const Frag& na = u + 1 < 8 ? fa[(u + 1) & 3] : fa[0];
+        const Frag& nb = u + 1 < 8 ? fb[(u + 1) >> 2] : fb[0];
+        if (u + 1 < 8 || more)
+          p[(u + 1) & 1] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(na.code, nb.code, floatx16{}, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          acc[t >> 1][t & 1][r] = __builtin_fmaf(p[t & 1][r], q[t & 1][r], acc[t >> 1][t & 1][r]);
-        asm volatile("" : "+v"(acc[t >> 1][t & 1]));   // the fmas stay here
-        if constexpr (GRID == 1)
-          if (t + 1 < 8) mfma_tile(fa[(t + 1) >> 1], fb[(t + 1) & 1], p[(t + 1) & 1], q[(t + 1) & 1]);
-        if (t == 0) decode_store<GRID, BC>(din, decb + (n & 1) * L::DEC, dop, drow);
-        if (t == 1) {
+          acc[u & 3][u >> 2][r] = __builtin_fmaf(p[u & 1][r], q[r], acc[u & 3][u >> 2][r]);
+        asm volatile("" : "+v"(acc[u & 3][u >> 2]));   // the fmas stay here
+        if (u + 1 < 8 || more)
+          q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(na.pc, nb.pc, floatx16{}, 0, 0, 0);
+        if (u == 0) decode_store<GRID, BC>(din, decb + (n & 1) * L::DEC, dop, drow);
+        if (u == 1) {
           if (((i + 2) & 7) == 0) wait_vmcnt<0>();   // raw stage of step i+2 has landed
           __syncthreads();
-#pragma unroll
-          for (int u = 0; u < 2; ++u) fbn[u] = frag_at(dn, code_b + 256 * u, pc_b + 512 * u);
+          // raw inputs of step i+2 (its stage has landed for every wave)
+          dnx = decode_load<BC>(lds + (((i + 2) >> 3) & 1) * L::RAW, dop, drow, (i + 2) & 7);
         }
-        if (t & 1) fa[t >> 1] = frag_at(dn, code_a + 256 * (t >> 1), pc_a + 512 * (t >> 1));
+        if (u == 3) fb[0] = frag_at(dn, code_b, pc_b);
+        if (u >= 4) fa[u - 4] = frag_at(dn, code_a + 256 * (u - 4), pc_a + 512 * (u - 4));
+        if (u == 7) fb[1] = frag_at(dn, code_b + 256, pc_b + 512);
         __builtin_amdgcn_sched_barrier(0);
       }
-      fb[0] = fbn[0];
-      fb[1] = fbn[1];
     }
   }
 
