@@ -4,11 +4,12 @@ One step = one MoE layer of the large-MoE single-GPU share: 16 local
 experts, hidden 5120, expert FFN 1536, 32768 tokens routed top-8 uniformly
 (262144 token rows, each expert padded to a multiple of 128), INT4 grid,
 RHT n = 128 along every GEMM's shared dimension, 1 x 16 fp32-scale blocks,
-RTNE on X / W and stochastic rounding on dY.  The step is the path's nine
-library calls: six fused RHT + 4-bit quantizations (X_perm, W, dY_perm
-row-wise; W^T per expert, dY_perm^T and X_perm^T per expert segment) and the
-three grouped GEMMs FPROP Y_e = X_e W_e^T, DGRAD dX_e = dY_e W_e and WGRAD
-dW_e = dY_e^T X_e.
+RTNE on X / W and stochastic rounding on dY.  The step is six library
+calls: three dual-axis fused RHT + 4-bit quantizations (one read each of
+X_perm, W and dY_perm gives its row-wise copy and its per-expert column-wise
+copy: W^T per expert, dY_perm^T and X_perm^T per expert segment -- six
+quantized operands) and the three grouped GEMMs FPROP Y_e = X_e W_e^T, DGRAD
+dX_e = dY_e W_e and WGRAD dW_e = dY_e^T X_e.
 
 Inputs are synthetic (seeded), resident in HBM before the timed region and
 rotated over buffer sets, so no step reads inputs cached by the one before.
@@ -129,7 +130,7 @@ class MoELayer:
     calls with prebuilt ctypes arguments, for each input buffer set.  Used for
     the 16-expert share (the step) and the 64-expert Zipf layer (context)."""
 
-    def __init__(self, U, torch, wl, grid, n, b, nsets=1):
+    def __init__(self, U, torch, wl, grid, n, b, nsets=1, dual=True):
         import workloads
         self.U, self.torch = U, torch
         self.stream = torch.cuda.current_stream()
@@ -158,6 +159,7 @@ class MoELayer:
                        ("dy_col", "dY", self.off, mk(sw, U.UFP4_SR, 1)),
                        ("x_col", "X", self.off, mk(sw, U.UFP4_RTNE))]
         lib = U.lib_handle()
+        self.dual = dual
         self.q = {}
         for name, tn, seg, cfg in self.qcalls:
             rows, cols = base[tn].shape
@@ -176,10 +178,23 @@ class MoELayer:
             self._keep.append(arr)
             offs[key] = arr
         goff = offs["tok"]
+        cfgs = {name: cfg for name, _, _, cfg in self.qcalls}
         self.calls = []
         for ts in self.sets:
             calls = []
-            for name, tn, seg, cfg in self.qcalls:
+            # dual: one read of each tensor for its row-wise copy and its
+            # per-expert (segmented) column-wise copy
+            for k, tn in ((("x", "X"), ("w", "W"), ("dy", "dY")) if dual else ()):
+                t, qr, qc = ts[tn], self.q[k + "_row"], self.q[k + "_col"]
+                rows, cols = t.shape
+                arr = offs["w"] if k == "w" else offs["tok"]
+                nseg = len(woff) - 1 if k == "w" else len(self.off) - 1
+                args = (ctypes.c_void_p(t.data_ptr()), rows, cols, t.stride(0), arr, nseg,
+                        ctypes.byref(cfgs[k + "_row"]), ctypes.byref(cfgs[k + "_col"]),
+                        ctypes.c_void_p(qr.codes.data_ptr()), ctypes.c_void_p(qr.scales.data_ptr()),
+                        ctypes.c_void_p(qc.codes.data_ptr()), ctypes.c_void_p(qc.scales.data_ptr()), cs)
+                calls.append(("quant_" + k, _raw(U, k, lib.ufp4_rht_quant_dual, args)))
+            for name, tn, seg, cfg in ([] if dual else self.qcalls):
                 t, q = ts[tn], self.q[name]
                 rows, cols = t.shape
                 if seg is None:
@@ -207,8 +222,13 @@ class MoELayer:
         self.tokens = tokens
         f = 2.0 * tokens * F * H                 # unpadded token rows
         self.flops = {"fprop": f, "dgrad": f, "wgrad": f}
-        bpe = 2.0 + 0.5 + 4.0 / b                # bf16 in, 4-bit code, fp32 scale per block
-        self.qbytes = {"quant_" + name: bpe * base[tn].numel() for name, tn, _, _ in self.qcalls}
+        if dual:   # bf16 read once, two code and scale sets written
+            bpe = 2.0 + 2 * (0.5 + 4.0 / b)
+            self.qbytes = {"quant_" + k: bpe * base[tn].numel()
+                           for k, tn in (("x", "X"), ("w", "W"), ("dy", "dY"))}
+        else:      # bf16 in, 4-bit code, fp32 scale per block
+            bpe = 2.0 + 0.5 + 4.0 / b
+            self.qbytes = {"quant_" + name: bpe * base[tn].numel() for name, tn, _, _ in self.qcalls}
         self.bpe = bpe
 
     def step(self, i):
@@ -701,6 +721,7 @@ def main():
             "frac_fp4_peak": round(ach / FP4_PEAK_TFLOPS, 4),
             "scheme_ceiling_tflops": round(RD_CEILING_TFLOPS, 1),
             "frac_scheme_ceiling": round(ach / RD_CEILING_TFLOPS, 4)}
+    layer_bpe = layer.bpe
     step_info = {"ms_per_step": round(ms_step, 4), "tokens_x_topk": layer.tokens,
                  "padded_rows": layer.T, "experts": layer.E}
     del layer
@@ -746,15 +767,15 @@ def main():
         "data": "synthetic (seeded torch generators; MoE layer tensors: X N(0,1) with 0.1% entries "
                 "x100, W N(0,0.02), dY N(0,1e-3); uniform top-8 routing)",
         "config": {"workload": "large-MoE single-GPU share: 16 experts, hidden 5120, FFN 1536, 32768 "
-                               "tokens top-8 (262144 token rows, padded per expert to 128); 6 fused "
-                               "RHT(n=128)+1x16 INT4 quantizations (SR on dY) + grouped "
-                               "FPROP/DGRAD/WGRAD",
+                               "tokens top-8 (262144 token rows, padded per expert to 128); 3 dual-axis "
+                               "fused RHT(n=128)+1x16 INT4 quantizations (6 quantized operands, SR on "
+                               "dY) + grouped FPROP/DGRAD/WGRAD",
                    "global_batch": 32768, "seq_len": None, "parallelism": "single GPU",
                    "experts": step_info["experts"], "tokens_x_topk": step_info["tokens_x_topk"],
                    "padded_rows": step_info["padded_rows"], "input_sets": max(1, args.sets)},
         "roofline": roof,
         "quant": {"GB/s": round(quant_gbps, 1), "frac_hbm_peak": round(quant_gbps / HBM_PEAK_GBPS, 4),
-                  "ms": round(quant_ms, 4), "bytes_per_elem": 2.75},
+                  "ms": round(quant_ms, 4), "bytes_per_elem": round(layer_bpe, 4)},
         "gemm": {"TFLOP/s": round(total_flops / gemm_ms / 1e9, 2),
                  "frac_fp8_peak": round(total_flops / gemm_ms / 1e9 / FP8_PEAK_TFLOPS, 4),
                  "frac_bf16_peak": round(total_flops / gemm_ms / 1e9 / BF16_PEAK_TFLOPS, 4),

@@ -136,8 +136,8 @@ int ufp4_rht_quant(const void* x, int64_t rows, int64_t cols, int64_t ld, int32_
  * given).  [UFP4] Method: the recipe quantizes X, W and dY along both axes,
  * since each takes part in two GEMMs with different shared dimensions.
  * Outputs are bit-identical to the single-axis calls.  cfg_row and cfg_col
- * must be 1D and agree in grid, rounding, scale mode, block_cols and rht_n
- * (<= 64); they may differ in sign_seed, sr_seed and sr_stream (else
+ * must be 1D and agree in grid, rounding, scale mode, block_cols and rht_n;
+ * they may differ in sign_seed, sr_seed and sr_stream (else
  * UFP4_ERR_UNSUPPORTED).  rows (or every segment) and cols must be multiples
  * of lcm(rht_n, block_cols) (UFP4_ERR_SHAPE).  row_offsets: HOST int64
  * [num_segments+1] or NULL; 1 <= num_segments <= 128.  Buffers: codes_row

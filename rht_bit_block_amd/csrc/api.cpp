@@ -329,7 +329,7 @@ int ufp4_rht_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ld,
   if (cfg_row->block_rows != 1 || cfg_col->block_rows != 1 || cfg_row->grid != cfg_col->grid ||
       cfg_row->rounding != cfg_col->rounding || cfg_row->scale_mode != cfg_col->scale_mode ||
       cfg_row->block_cols != cfg_col->block_cols || cfg_row->rht_n != cfg_col->rht_n ||
-      cfg_row->rht_n > 64 || cfg_row->grid == UFP4_E4M3)
+      cfg_row->grid == UFP4_E4M3)
     return UFP4_ERR_UNSUPPORTED;
   const int64_t n = cfg_row->rht_n, b = cfg_row->block_cols;
   const int64_t align = n > b ? n : b;
@@ -355,7 +355,7 @@ int ufp4_rht_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ld,
   q.K = rows;
   q.nseg = nseg;
   int64_t t = 0;
-  const int64_t tp = cdiv(cols, 64);
+  const int64_t tp = cdiv(cols, dual_tile_cols(cfg_row->rht_n));
   for (int g = 0; g < nseg; ++g) {
     const int64_t a = row_offsets ? row_offsets[g] : 0, e = row_offsets ? row_offsets[g + 1] : rows;
     q.seg_off[g] = a;

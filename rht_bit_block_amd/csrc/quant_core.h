@@ -724,7 +724,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantLaunch q) {
 // quantization of the same tile (A = X, K = the columns) from the staged
 // words -- a lane takes W consecutive columns of one row and keeps its row's
 // bf16 half of each word.  The row side has its own signs, SR stream and
-// outputs.  Hadamard chunks along the row must fit the tile width (n <= 64).
+// outputs.  Hadamard chunks along the row must fit the tile width: tiles are
+// 128 x 64 for n <= 64 and 128 x 128 for n = 128 (dual_tile_cols).
 //
 // A workgroup takes two consecutive tiles.  When both are whole (no ragged
 // rows or columns) the second tile's HBM loads are issued together with the
@@ -736,26 +737,29 @@ struct DualTile {
   int krows, pcols;
 };
 
+template <int TP>
 __device__ __forceinline__ DualTile dual_tile(const QuantLaunch& q, int bid) {
   int g = 0;
   while (g + 1 < q.nseg && q.tile_start[g + 1] <= bid) ++g;
   DualTile d;
   d.seg0 = q.seg_off[g];
   d.L = q.seg_off[g + 1] - d.seg0;
-  const int tiles_p = (int)((q.cols + kTP - 1) / kTP);
+  const int tiles_p = (int)((q.cols + TP - 1) / TP);
   const int local = bid - q.tile_start[g];
   const int tk = local / tiles_p, tp = local - tk * tiles_p;
   d.k0 = (int64_t)tk * kTK;
-  d.p0 = (int64_t)tp * kTP;
+  d.p0 = (int64_t)tp * TP;
   d.krows = (int)min<int64_t>(kTK, d.L - d.k0);
-  d.pcols = (int)min<int64_t>(kTP, q.cols - d.p0);
+  d.pcols = (int)min<int64_t>(TP, q.cols - d.p0);
   return d;
 }
 
-// Staging task j of this thread: pair row i, columns c8 .. c8+7.
-constexpr int kStageTasks = (kTK / 2) * (kTP / 8) / kThreads;   // 2
+// Staging task j of this thread: pair row i, columns c8 .. c8+7 (2 tasks per
+// thread for 64-column tiles, 4 for 128).
+template <int TP> constexpr int stage_tasks() { return (kTK / 2) * (TP / 8) / kThreads; }
 
 // Two bf16 rows (2i, 2i+1) x 8 columns -> 8 paired-row words in LDS.
+template <int TP>
 __device__ __forceinline__ void stage_pairs(uint32_t* tile, int i, int c8, uint4 ra, uint4 rb) {
   const uint32_t a4[4] = {ra.x, ra.y, ra.z, ra.w}, b4[4] = {rb.x, rb.y, rb.z, rb.w};
   uint32_t o[8];
@@ -764,40 +768,45 @@ __device__ __forceinline__ void stage_pairs(uint32_t* tile, int i, int c8, uint4
     o[2 * j] = __builtin_amdgcn_perm(b4[j], a4[j], 0x05040100u);
     o[2 * j + 1] = __builtin_amdgcn_perm(b4[j], a4[j], 0x07060302u);
   }
-  uint32_t* d = tile + i * kTP;
+  uint32_t* d = tile + i * TP;
   *reinterpret_cast<uint4*>(d + col_swz(i, c8)) = make_uint4(o[0], o[1], o[2], o[3]);
   *reinterpret_cast<uint4*>(d + col_swz(i, c8 + 4)) = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
 // The 16-byte row loads of a whole tile (all rows and columns inside X).
+template <int TP>
 struct DualRegs {
-  uint4 a[kStageTasks], b[kStageTasks];
+  uint4 a[stage_tasks<TP>()], b[stage_tasks<TP>()];
 };
 
-__device__ __forceinline__ void load_whole(const QuantLaunch& q, const DualTile& d, DualRegs& r) {
+template <int TP>
+__device__ __forceinline__ void load_whole(const QuantLaunch& q, const DualTile& d,
+                                           DualRegs<TP>& r) {
 #pragma unroll
-  for (int j = 0; j < kStageTasks; ++j) {
+  for (int j = 0; j < stage_tasks<TP>(); ++j) {
     const int t = threadIdx.x + j * kThreads;
-    const int i = t / (kTP / 8), c8 = (t % (kTP / 8)) * 8;
+    const int i = t / (TP / 8), c8 = (t % (TP / 8)) * 8;
     const uint16_t* src = q.x + (d.seg0 + d.k0 + 2 * i) * q.ld + d.p0 + c8;
     r.a[j] = ld16(src);
     r.b[j] = ld16(src + q.ld);
   }
 }
 
-__device__ __forceinline__ void stage_whole(const DualRegs& r, uint32_t* tile) {
+template <int TP>
+__device__ __forceinline__ void stage_whole(const DualRegs<TP>& r, uint32_t* tile) {
 #pragma unroll
-  for (int j = 0; j < kStageTasks; ++j) {
+  for (int j = 0; j < stage_tasks<TP>(); ++j) {
     const int t = threadIdx.x + j * kThreads;
-    stage_pairs(tile, t / (kTP / 8), (t % (kTP / 8)) * 8, r.a[j], r.b[j]);
+    stage_pairs<TP>(tile, t / (TP / 8), (t % (TP / 8)) * 8, r.a[j], r.b[j]);
   }
 }
 
 // Any tile, ragged rows and columns read as zeros.
+template <int TP>
 __device__ __forceinline__ void load_stage_any(const QuantLaunch& q, const DualTile& d,
                                                uint32_t* tile) {
-  for (int t = threadIdx.x; t < (kTK / 2) * (kTP / 8); t += kThreads) {
-    const int i = t / (kTP / 8), c8 = (t % (kTP / 8)) * 8;
+  for (int t = threadIdx.x; t < (kTK / 2) * (TP / 8); t += kThreads) {
+    const int i = t / (TP / 8), c8 = (t % (TP / 8)) * 8;
     uint4 ra = make_uint4(0, 0, 0, 0), rb = ra;
     const int r = 2 * i;
     const uint16_t* src = q.x + (d.seg0 + d.k0 + r) * q.ld + d.p0 + c8;
@@ -819,12 +828,12 @@ __device__ __forceinline__ void load_stage_any(const QuantLaunch& q, const DualT
       rb = make_uint4(tb[0] | (tb[1] << 16), tb[2] | (tb[3] << 16), tb[4] | (tb[5] << 16),
                       tb[6] | (tb[7] << 16));
     }
-    stage_pairs(tile, i, c8, ra, rb);
+    stage_pairs<TP>(tile, i, c8, ra, rb);
   }
 }
 
 // Both quantizations of one staged tile.
-template <int W, int B, int N, int GRID, int RND>
+template <int W, int B, int N, int GRID, int RND, int TP>
 __device__ __forceinline__ void dual_quantize(const QuantLaunch& q, const RowSide& rside,
                                               const DualTile& d, const uint32_t* tile) {
   constexpr int lpc = N > W ? N / W : 1;
@@ -837,7 +846,7 @@ __device__ __forceinline__ void dual_quantize(const QuantLaunch& q, const RowSid
     uint32_t pm[W / 2];
     sign_masks<W>(select_pattern(q, qpos), pm);
     constexpr int kSegsPerCol = kTK / W;
-    for (int u = threadIdx.x; u < kTP * kSegsPerCol; u += kThreads) {
+    for (int u = threadIdx.x; u < TP * kSegsPerCol; u += kThreads) {
       const int kseg = u % kSegsPerCol;
       const int col = u / kSegsPerCol;
       const int kr = kseg * W;
@@ -846,7 +855,7 @@ __device__ __forceinline__ void dual_quantize(const QuantLaunch& q, const RowSid
 #pragma unroll
       for (int i = 0; i < W / 2; ++i) {
         const int pr = kr / 2 + i;
-        w[i] = tile[pr * kTP + col_swz(pr, col)];
+        w[i] = tile[pr * TP + col_swz(pr, col)];
       }
       float y[W];
       unpack<W>(w, pm, y);
@@ -860,7 +869,7 @@ __device__ __forceinline__ void dual_quantize(const QuantLaunch& q, const RowSid
   {
     uint32_t pm[W / 2];
     sign_masks<W>(select_pattern(rside, qpos), pm);
-    constexpr int kSegsPerRow = kTP / W;
+    constexpr int kSegsPerRow = TP / W;
     for (int u = threadIdx.x; u < kTK * kSegsPerRow; u += kThreads) {
       const int seg = u % kSegsPerRow;
       const int row = u / kSegsPerRow;
@@ -871,7 +880,7 @@ __device__ __forceinline__ void dual_quantize(const QuantLaunch& q, const RowSid
       uint32_t w[W / 2];
 #pragma unroll
       for (int j = 0; j < W / 4; ++j) {
-        const uint4 v = *reinterpret_cast<const uint4*>(tile + pr * kTP + col_swz(pr, c0 + 4 * j));
+        const uint4 v = *reinterpret_cast<const uint4*>(tile + pr * TP + col_swz(pr, c0 + 4 * j));
         w[2 * j] = __builtin_amdgcn_perm(v.y, v.x, sel);
         w[2 * j + 1] = __builtin_amdgcn_perm(v.w, v.z, sel);
       }
@@ -887,37 +896,38 @@ __device__ __forceinline__ void dual_quantize(const QuantLaunch& q, const RowSid
 
 template <int W, int B, int N, int GRID, int RND>
 __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide rside) {
-  __shared__ uint32_t tile[(kTK / 2) * kTP];
-  static_assert(N <= kTP, "row-wise Hadamard chunks must fit the tile width");
-  static_assert(kStageTasks * kThreads == (kTK / 2) * (kTP / 8), "staging tasks per thread");
+  constexpr int TP = dual_tile_cols(N);
+  __shared__ uint32_t tile[(kTK / 2) * TP];
+  static_assert(N <= TP, "row-wise Hadamard chunks must fit the tile width");
+  static_assert(stage_tasks<TP>() * kThreads == (kTK / 2) * (TP / 8), "staging tasks per thread");
   const int total = q.tile_start[q.nseg];
   const int b0 = 2 * blockIdx.x;
   const bool two = b0 + 1 < total;
-  const DualTile d0 = dual_tile(q, b0);
-  const DualTile d1 = dual_tile(q, two ? b0 + 1 : b0);
-  const bool whole = d0.krows == kTK && d0.pcols == kTP && d1.krows == kTK && d1.pcols == kTP;
+  const DualTile d0 = dual_tile<TP>(q, b0);
+  const DualTile d1 = dual_tile<TP>(q, two ? b0 + 1 : b0);
+  const bool whole = d0.krows == kTK && d0.pcols == TP && d1.krows == kTK && d1.pcols == TP;
   if (whole) {
-    DualRegs r0, r1;
-    load_whole(q, d0, r0);
-    load_whole(q, d1, r1);   // (the first tile again when there is no second)
-    stage_whole(r0, tile);
+    DualRegs<TP> r0, r1;
+    load_whole<TP>(q, d0, r0);
+    load_whole<TP>(q, d1, r1);   // (the first tile again when there is no second)
+    stage_whole<TP>(r0, tile);
     __syncthreads();
-    dual_quantize<W, B, N, GRID, RND>(q, rside, d0, tile);
+    dual_quantize<W, B, N, GRID, RND, TP>(q, rside, d0, tile);
     if (two) {
       __syncthreads();   // every lane is done reading the first tile
-      stage_whole(r1, tile);
+      stage_whole<TP>(r1, tile);
       __syncthreads();
-      dual_quantize<W, B, N, GRID, RND>(q, rside, d1, tile);
+      dual_quantize<W, B, N, GRID, RND, TP>(q, rside, d1, tile);
     }
   } else {
-    load_stage_any(q, d0, tile);
+    load_stage_any<TP>(q, d0, tile);
     __syncthreads();
-    dual_quantize<W, B, N, GRID, RND>(q, rside, d0, tile);
+    dual_quantize<W, B, N, GRID, RND, TP>(q, rside, d0, tile);
     if (two) {
       __syncthreads();
-      load_stage_any(q, d1, tile);
+      load_stage_any<TP>(q, d1, tile);
       __syncthreads();
-      dual_quantize<W, B, N, GRID, RND>(q, rside, d1, tile);
+      dual_quantize<W, B, N, GRID, RND, TP>(q, rside, d1, tile);
     }
   }
 }
@@ -1120,7 +1130,7 @@ hipError_t run_dual_1d(const QuantLaunch& q, const RowSide& r, hipStream_t s) {
   }
 #define UFP4_RUN_B(B_) \
   UFP4_RUN(B_, 1) UFP4_RUN(B_, 2) UFP4_RUN(B_, 4) UFP4_RUN(B_, 8) UFP4_RUN(B_, 16) \
-  UFP4_RUN(B_, 32) UFP4_RUN(B_, 64)
+  UFP4_RUN(B_, 32) UFP4_RUN(B_, 64) UFP4_RUN(B_, 128)
   UFP4_RUN_B(16)
   UFP4_RUN_B(32)
 #undef UFP4_RUN_B

@@ -96,6 +96,10 @@ struct QuantLaunch {
   int32_t tile_start[kMaxSegments + 1];
 };
 
+// Column extent of a dual-axis quantization tile (its row extent is 128):
+// the row-wise Hadamard chunks must fit inside a tile.
+constexpr int dual_tile_cols(int n) { return n > 64 ? 128 : 64; }
+
 // Row-wise side of a two-axis quantization: its own outputs, signs and draws
 // (the geometry and the column-wise side live in the QuantLaunch).
 struct RowSide {

@@ -172,8 +172,9 @@ def test_dual_quant_argument_errors():
     assert _dual(lib, cfg_c=U.make_cfg(grid=U.UFP4_INT4)) == E.UFP4_ERR_UNSUPPORTED
     assert _dual(lib, cfg_c=U.make_cfg(rounding=U.UFP4_SR)) == E.UFP4_ERR_UNSUPPORTED
     assert _dual(lib, cfg_c=U.make_cfg(rht_n=32)) == E.UFP4_ERR_UNSUPPORTED
-    big = U.make_cfg(rht_n=128)
-    assert _dual(lib, rows=128, cols=128, ld=128, cfg_r=big, cfg_c=big) == E.UFP4_ERR_UNSUPPORTED
+    big = U.make_cfg(rht_n=128)   # n = 128: both axes in multiples of 128
+    assert _dual(lib, rows=64, cols=128, ld=128, cfg_r=big, cfg_c=big) == E.UFP4_ERR_SHAPE
+    assert _dual(lib, rows=128, cols=64, ld=64, cfg_r=big, cfg_c=big) == E.UFP4_ERR_SHAPE
     assert _dual(lib, rows=40) == E.UFP4_ERR_SHAPE                  # rows % 16
     assert _dual(lib, cols=40, ld=48) == E.UFP4_ERR_SHAPE           # cols % 16
     assert _dual(lib, offs=[0, 24, 64]) == E.UFP4_ERR_SHAPE         # segment % 16

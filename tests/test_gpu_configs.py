@@ -174,6 +174,18 @@ def _moe(wl, grid, n, b):
     dX = U.ufp4_gemm_dgrad_grouped(qdyr, U.stacked(qwc, E), off)
     dW = U.ufp4_gemm_wgrad_grouped(qdyc, qxc, off)
     torch.cuda.synchronize()
+    # the dual-axis calls bench.py times (one read per tensor, per-expert
+    # column-wise side) give the same bits as the single-axis calls, which
+    # are checked against the oracle below
+    for t, cr, cc, o, (qr, qc), what in ((Xp, c_xr, c_xc, off, (qxr, qxc), "X_perm"),
+                                         (W, c_wr, c_wc, woff, (qwr, qwc), "W"),
+                                         (dYp, c_dyr, c_dyc, off, (qdyr, qdyc), "dY_perm")):
+        dr, dc = U.ufp4_rht_quant_dual(t, cr, cc, row_offsets=o)
+        assert torch.equal(dr.codes.view(-1), qr.codes.view(-1)), f"{what}: dual row codes"
+        assert torch.equal(dr.scales.view(-1), qr.scales.view(-1)), f"{what}: dual row scales"
+        assert torch.equal(dc.codes.view(-1), qc.codes.view(-1)), f"{what}: dual column codes"
+        assert torch.equal(dc.scales.view(-1), qc.scales.view(-1)), f"{what}: dual column scales"
+        del dr, dc
     # experts to sample: the largest, a median one and the smallest non-empty
     nz = [g for g in range(E) if off[g + 1] > off[g]]
     sizes = sorted(nz, key=lambda g: off[g + 1] - off[g])

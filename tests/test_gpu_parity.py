@@ -12,7 +12,7 @@ import torch
 
 import oracle as O
 import rht_bit_block_amd as U
-from gpu_helpers import (GEMM_TOL, GRIDS, compare_quant, dev_bf16, f32_bits_equal,
+from gpu_helpers import (GEMM_TOL, GRIDS, compare_quant, dev_bf16, f32_bits_equal, first_diff,
                          oracle_dequant64, rand_bits, spec_of)
 
 pytestmark = pytest.mark.gpu
@@ -722,3 +722,32 @@ def test_grouped_gemms_pow2(grid, br):
         if off[g + 1] > off[g]:
             ref = O.gemm_ref(ddy[off[g]:off[g + 1]], dwt[g])
             assert O.rel_fro(dX[off[g]:off[g + 1]], ref) <= GEMM_TOL, ("dgrad", g)
+
+
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("rnd", [U.UFP4_RTNE, U.UFP4_SR])
+@pytest.mark.parametrize("b", [16, 32])
+def test_quant_dual_n128(grid, rnd, b):
+    """Dual-axis calls with n = 128 (128 x 128 tiles): 384 x 256 (six tiles, the
+    workgroup pairs whole) and 384 x 128 (three tiles, the last workgroup with
+    one), and expert segments of 256, 0 and 128 rows, against the oracle's
+    row-wise and (per-segment) column-wise quantizations."""
+    _print_case("dual n128", grid, rnd, b)
+    cr = U.make_cfg(grid, rnd, U.UFP4_SCALE_F32, 1, b, 128, sign_seed=61, sr_seed=5, sr_stream=0)
+    cc = U.make_cfg(grid, rnd, U.UFP4_SCALE_F32, 1, b, 128, sign_seed=62, sr_seed=5, sr_stream=1)
+    for rows, cols in ((384, 256), (384, 128)):
+        bits = rand_bits(rows, cols, 70 + cols)
+        qr, qc = U.ufp4_rht_quant_dual(dev_bf16(bits), cr, cc)
+        torch.cuda.synchronize()
+        _assert_q_equal(qr, O.quantize(bits, 0, spec_of(cr)), "row")
+        _assert_q_equal(qc, O.quantize(bits, 1, spec_of(cc)), "col")
+    offs = [0, 256, 256, 384]
+    bits = rand_bits(384, 256, 79)
+    qr, qc = U.ufp4_rht_quant_dual(dev_bf16(bits), cr, cc, row_offsets=offs)
+    torch.cuda.synchronize()
+    _assert_q_equal(qr, O.quantize(bits, 0, spec_of(cr)), "row")
+    segs = [O.quantize(bits[lo:hi], 1, spec_of(cc), elem_base=bits.shape[1] * lo)
+            for lo, hi in zip(offs[:-1], offs[1:]) if hi > lo]
+    ref = {"codes": np.concatenate([np.asarray(r["codes"]).reshape(-1) for r in segs]),
+           "scales": np.concatenate([np.asarray(r["scales"]).reshape(-1) for r in segs])}
+    _assert_q_equal(qc, ref, "col")
