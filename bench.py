@@ -60,6 +60,12 @@ _GEMM_SRC = ("gemm_rd.hip", "gemm_epilogue.h", "ufp4_internal.h")
 _QUANT_SRC = ("quant_core.h", "ufp4_internal.h")
 MEASURED_TRAFFIC = {
     # (workload, kernel): (sources, sha256[:16] of them, FETCH_SIZE KiB, WRITE_SIZE KiB)
+    ("moe16", "fprop"): (_GEMM_SRC, "1eb0178d37334500", 1570891.2, 1577653.4),
+    ("moe16", "dgrad"): (_GEMM_SRC, "1eb0178d37334500", 720534.1, 5258887.4),
+    ("moe16", "wgrad"): (_GEMM_SRC, "1eb0178d37334500", 1226832.1, 491564.8),
+    ("moe16", "quant_x"): (_QUANT_SRC, "283dd653997b2047", 1314809.9, 2300145.0),
+    ("moe16", "quant_w"): (_QUANT_SRC, "283dd653997b2047", 123117.2, 218186.4),
+    ("moe16", "quant_dy"): (_QUANT_SRC, "283dd653997b2047", 395237.2, 702726.2),
 }
 
 
