@@ -474,6 +474,15 @@ def square_blocks(U, torch, reps=10):
         return _raw(U, name, getattr(lib, "ufp4_gemm_" + name),
                     (ctypes.byref(qa), ctypes.byref(qb), ctypes.c_void_p(c.data_ptr()), c.stride(0), cs))
 
+    def gemm_ws_call(op, a, b, c):
+        qa, qb = a.c(), b.c()
+        need = U.ufp4_gemm_workspace_bytes(op, a, b)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        keep.extend([qa, qb, ws])
+        return _raw(U, "gemm_ws", lib.ufp4_gemm_ws,
+                    (op, ctypes.byref(qa), ctypes.byref(qb), 0, None, ctypes.c_void_p(c.data_ptr()),
+                     c.stride(0), ctypes.c_void_p(ws.data_ptr()), need, cs))
+
     keep = []
     wl = workloads.config5("cuda")
     X, W, dY = wl.tensors["X"], wl.tensors["W"], wl.tensors["dY"]
@@ -517,6 +526,16 @@ def square_blocks(U, torch, reps=10):
                 "ms": round(ms, 4), "TFLOP/s": round(tf, 1), "peak": peak,
                 "frac": round(tf / peak, 4),
                 "mfma": "v_mfma_scale_f32_32x32x64_f8f6f4 (" + ("FP4" if grid == U.UFP4_E2M1 else "FP8 E4M3") + ")"}
+            if grid != U.UFP4_E2M1:   # the same GEMM as FP6 operands (workspace entry point)
+                op = {"fprop": U.UFP4_GEMM_FPROP, "dgrad": U.UFP4_GEMM_DGRAD,
+                      "wgrad": U.UFP4_GEMM_WGRAD}[name]
+                ms = _timed(torch, gemm_ws_call(op, a, b, c), reps)
+                tf = 2.0 * M * N * K / ms / 1e9
+                out[f"gemm_2d_{M}x{K}x{N}_{gname}_{name}_fp6"] = {
+                    "ms": round(ms, 4), "TFLOP/s": round(tf, 1), "peak": FP4_PEAK_TFLOPS,
+                    "frac": round(tf / FP4_PEAK_TFLOPS, 4),
+                    "mfma": "v_mfma_scale_f32_32x32x64_f8f6f4 (FP6 E2M3; ms includes the "
+                            "expansion of both operands into the workspace)"}
             del c
         del qs, qwt, qxt, qdyt
     del wl, X, W, dY
@@ -535,6 +554,12 @@ def square_blocks(U, torch, reps=10):
         peak = FP4_PEAK_TFLOPS if grid == U.UFP4_E2M1 else FP8_PEAK_TFLOPS
         out[f"dense_1x32_e8m0_{M2}x{K2}x{N2}_{gname}_fprop"] = {
             "ms": round(ms, 4), "TFLOP/s": round(tf, 1), "peak": peak, "frac": round(tf / peak, 4)}
+        if grid != U.UFP4_E2M1:
+            ms = _timed(torch, gemm_ws_call(U.UFP4_GEMM_FPROP, qx, qw, c), reps)
+            tf = 2.0 * M2 * N2 * K2 / ms / 1e9
+            out[f"dense_1x32_e8m0_{M2}x{K2}x{N2}_{gname}_fprop_fp6"] = {
+                "ms": round(ms, 4), "TFLOP/s": round(tf, 1), "peak": FP4_PEAK_TFLOPS,
+                "frac": round(tf / FP4_PEAK_TFLOPS, 4)}
     cfg = U.make_cfg(U.UFP4_E4M3, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 1)
     qx, _ = U.ufp4_rht_quant(X2, 0, cfg)
     qw, _ = U.ufp4_rht_quant(W2, 0, cfg)

@@ -251,6 +251,31 @@ int ufp4_gemm_dgrad_grouped(const ufp4_qtensor* dYp, const ufp4_qtensor* Wt, int
 int ufp4_gemm_wgrad_grouped(const ufp4_qtensor* dYt, const ufp4_qtensor* Xt, int32_t G,
                             const int64_t* offsets, float* dW, int64_t ldw, void* stream);
 
+/* The three GEMMs above with a caller workspace.  op: UFP4_GEMM_FPROP,
+ * UFP4_GEMM_DGRAD or UFP4_GEMM_WGRAD; G = 0 for the dense call (offsets may
+ * be NULL), G >= 1 for the grouped one (same arguments and rules as above).
+ * Same operation, result contract and errors as the call without a
+ * workspace.  The uniform grids (E1M2, INT4) with power-of-two scales on
+ * 32-element K blocks (1 x 32 or 32 x 32) are contracted on the scaled
+ * matrix cores as FP6 E2M3 operands -- every E1M2 level k/4 and every INT4
+ * level n/2 is an E2M3 value ([UFP4] chatpaper abstract: uniform grids as
+ * first-class hardware primitives; [UFP4] Method: the GEMM contracts the
+ * quantized operands): both operands are first expanded from their codes
+ * into `workspace` (device memory, 256-byte aligned, at least
+ * ufp4_gemm_workspace_bytes(op, A, B, G) bytes; its contents on entry do not
+ * matter and are overwritten).  A smaller or misaligned workspace for such
+ * a call is UFP4_ERR_INVALID_ARG; workspace = NULL (workspace_bytes 0) or
+ * any other operand kind runs the call without it.  Calls that share a
+ * workspace must be ordered on one stream. */
+#define UFP4_GEMM_FPROP 0
+#define UFP4_GEMM_DGRAD 1
+#define UFP4_GEMM_WGRAD 2
+size_t ufp4_gemm_workspace_bytes(int32_t op, const ufp4_qtensor* A, const ufp4_qtensor* B,
+                                 int32_t G);
+int ufp4_gemm_ws(int32_t op, const ufp4_qtensor* A, const ufp4_qtensor* B, int32_t G,
+                 const int64_t* offsets, float* C, int64_t ldc, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
 /* Transpose of a quantized operand whose blocks are square (2D mode): the
  * codes of A^T are the transposed codes and, because S(B) = S(B^T) for
  * square blocks ([2DFP4] 2D section), its scale grid is the transposed grid.

@@ -23,6 +23,7 @@ UFP4_RTNE, UFP4_SR = 0, 1
 UFP4_SCALE_F32, UFP4_SCALE_POW2 = 0, 1
 UFP4_OK, UFP4_ERR_INVALID_ARG, UFP4_ERR_SHAPE = 0, -1, -2
 UFP4_ERR_MISMATCH, UFP4_ERR_UNSUPPORTED, UFP4_ERR_HIP = -3, -4, -5
+UFP4_GEMM_FPROP, UFP4_GEMM_DGRAD, UFP4_GEMM_WGRAD = 0, 1, 2
 
 EXPORTED = [
     "ufp4_rht_quant", "ufp4_rht_quant_segmented", "ufp4_rht_quant_dual", "ufp4_quant_diag",
@@ -30,6 +31,7 @@ EXPORTED = [
     "ufp4_dequant",
     "ufp4_gemm_fprop", "ufp4_gemm_dgrad", "ufp4_gemm_wgrad",
     "ufp4_gemm_fprop_grouped", "ufp4_gemm_dgrad_grouped", "ufp4_gemm_wgrad_grouped",
+    "ufp4_gemm_workspace_bytes", "ufp4_gemm_ws",
     "ufp4_transpose_qtensor", "ufp4_codes_bytes", "ufp4_scales_bytes",
     "ufp4_philox_fill", "ufp4_status_string",
 ]
@@ -115,6 +117,7 @@ def _lib():
             "ufp4_gemm_fprop_grouped": [qtp, qtp, i32, i64p, vp, i64, vp],
             "ufp4_gemm_dgrad_grouped": [qtp, qtp, i32, i64p, vp, i64, vp],
             "ufp4_gemm_wgrad_grouped": [qtp, qtp, i32, i64p, vp, i64, vp],
+            "ufp4_gemm_ws": [i32, qtp, qtp, i32, i64p, vp, i64, vp, ctypes.c_size_t, vp],
             "ufp4_transpose_qtensor": [qtp, vp, vp, vp],
             "ufp4_philox_fill": [u64, u32, u64, i64, vp, vp],
         }
@@ -122,6 +125,8 @@ def _lib():
             f = getattr(lib, name)
             f.argtypes = args
             f.restype = ctypes.c_int
+        lib.ufp4_gemm_workspace_bytes.argtypes = [i32, qtp, qtp, i32]
+        lib.ufp4_gemm_workspace_bytes.restype = ctypes.c_size_t
         lib.ufp4_codes_bytes.argtypes = [i64, i64]
         lib.ufp4_codes_bytes.restype = ctypes.c_size_t
         lib.ufp4_scales_bytes.argtypes = [i64, i64, cfgp]
@@ -423,6 +428,41 @@ def ufp4_gemm_dgrad_grouped(dYp: QTensor, Wt: QTensor, offsets, out=None):
 def ufp4_gemm_wgrad_grouped(dYt: QTensor, Xt: QTensor, offsets, out=None):
     G = len(offsets) - 1
     return _gemm_grouped("ufp4_gemm_wgrad_grouped", dYt, Xt, offsets, G * dYt.P, Xt.P, out)
+
+
+def ufp4_gemm_workspace_bytes(op, A: QTensor, B: QTensor, groups=0):
+    a, b = A.c(), B.c()
+    return int(_lib().ufp4_gemm_workspace_bytes(op, ctypes.byref(a), ctypes.byref(b), groups))
+
+
+def ufp4_gemm_ws(op, A: QTensor, B: QTensor, offsets=None, out=None, workspace=None):
+    """One of the GEMMs above (op = UFP4_GEMM_FPROP / DGRAD / WGRAD; dense when
+    offsets is None, else grouped) through the workspace entry point.  With
+    workspace=None a uint8 device buffer of the size the library asks for is
+    allocated here (none when it asks for 0 bytes)."""
+    G = 0 if offsets is None else len(offsets) - 1
+    if G == 0:
+        rows, cols = A.P, B.P
+    elif op == UFP4_GEMM_WGRAD:
+        rows, cols = G * A.P, B.P
+    else:
+        rows, cols = A.P, B.P // G
+    dev = A.codes.device
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    a, b = A.c(), B.c()
+    _check_matrix("out", out, rows, cols, dev)
+    need = int(_lib().ufp4_gemm_workspace_bytes(op, ctypes.byref(a), ctypes.byref(b), G))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check_buffer("workspace", workspace, torch.uint8, need, dev)
+    off = _i64arr(offsets) if G else None
+    st = _lib().ufp4_gemm_ws(op, ctypes.byref(a), ctypes.byref(b), G, off, _ptr(out),
+                             out.stride(0), _ptr(workspace) if workspace is not None else None,
+                             workspace.numel() if workspace is not None else 0, _stream(out))
+    _check("ufp4_gemm_ws", st)
+    return out
 
 
 def ufp4_transpose_qtensor(q: QTensor):

@@ -139,7 +139,22 @@ void fill_gemm(GemmLaunch& g, const ufp4_qtensor* a, const ufp4_qtensor* b, floa
 constexpr int64_t kTile = 256;
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-int gemm_dense(const ufp4_qtensor* A, const ufp4_qtensor* B, float* C, int64_t ldc, void* stream) {
+// FP6 workspace bytes a dense GEMM of A and B can use (0: no workspace path).
+int64_t dense_fp6_bytes(const ufp4_qtensor* A, const ufp4_qtensor* B) {
+  if (check_pair(A, B) || A->P == 0 || B->P == 0 || A->K == 0) return 0;
+  if (!aligned(A->codes, 16) || !aligned(B->codes, 16) || !aligned(A->scales, 4) ||
+      !aligned(B->scales, 4))
+    return 0;
+  GemmLaunch g;
+  fill_gemm(g, A, B, nullptr, B->P);
+  g.mode = 0;
+  return gemm_mx6_supported(g) ? gemm_mx6_workspace(g) : 0;
+}
+
+// Dense C = A B^T.  With a workspace (ws != null) E1M2 / INT4 operands with
+// 32-element E8M0 blocks run as FP6 operands; every other case ignores it.
+int gemm_dense(const ufp4_qtensor* A, const ufp4_qtensor* B, float* C, int64_t ldc, void* stream,
+               void* ws = nullptr, size_t ws_bytes = 0) {
   int st = check_pair(A, B);
   if (st) return st;
   if (ldc < B->P) return UFP4_ERR_INVALID_ARG;
@@ -156,6 +171,13 @@ int gemm_dense(const ufp4_qtensor* A, const ufp4_qtensor* B, float* C, int64_t l
   g.tile_start[0] = 0;
   g.tile_start[1] = (int32_t)tiles;
   g.total_tiles = (int32_t)tiles;
+  if (ws) {
+    const int64_t need = dense_fp6_bytes(A, B);
+    if (need > 0) {
+      if ((uint64_t)need > (uint64_t)ws_bytes || !aligned(ws, 256)) return UFP4_ERR_INVALID_ARG;
+      return hip_status(launch_gemm_mx6(g, static_cast<uint8_t*>(ws), (hipStream_t)stream));
+    }
+  }
   const bool mx = gemm_mx_supported(g) && aligned(g.a_scales, 4) && aligned(g.b_scales, 4) &&
                   aligned(g.a_codes, 16) && aligned(g.b_codes, 16);
   if (mx) return hip_status(launch_gemm_mx(g, (hipStream_t)stream));
@@ -482,6 +504,22 @@ int ufp4_gemm_wgrad_grouped(const ufp4_qtensor* dYt, const ufp4_qtensor* Xt, int
   }
   g.total_tiles = (int32_t)(per * G);
   return hip_status(launch_gemm(g, (hipStream_t)stream));
+}
+
+size_t ufp4_gemm_workspace_bytes(int32_t op, const ufp4_qtensor* A, const ufp4_qtensor* B,
+                                 int32_t G) {
+  if (op < UFP4_GEMM_FPROP || op > UFP4_GEMM_WGRAD || G != 0) return 0;
+  return (size_t)dense_fp6_bytes(A, B);
+}
+
+int ufp4_gemm_ws(int32_t op, const ufp4_qtensor* A, const ufp4_qtensor* B, int32_t G,
+                 const int64_t* offsets, float* C, int64_t ldc, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  if (op < UFP4_GEMM_FPROP || op > UFP4_GEMM_WGRAD || G < 0) return UFP4_ERR_INVALID_ARG;
+  if (!workspace && workspace_bytes) return UFP4_ERR_INVALID_ARG;
+  if (G == 0) return gemm_dense(A, B, C, ldc, stream, workspace, workspace_bytes);
+  if (op == UFP4_GEMM_WGRAD) return ufp4_gemm_wgrad_grouped(A, B, G, offsets, C, ldc, stream);
+  return gemm_grouped_rows(A, B, G, offsets, C, ldc, stream);
 }
 
 int ufp4_transpose_qtensor(const ufp4_qtensor* src, uint8_t* dst_codes, void* dst_scales,

@@ -44,6 +44,21 @@
 //   k_gemm_mx4 (E2M1, K % 128 == 0): K step 128, the same copy with 4 stages.
 //   k_gemm_mx<GRID> (E1M2, INT4): K step 128; codes are loaded into registers
 //     two steps ahead, converted to E4M3 and written to LDS (two stages).
+//   k_gemm_mxrow<FMT, X4> (one byte per element per row, copied HBM -> LDS
+//     untouched, K step 128): FMT 0 = MXFP8 E4M3 codes; FMT 2 = E1M2 / INT4
+//     levels as FP6 E2M3 operands, written beforehand by k_fp6_expand into a
+//     caller workspace (32-byte slot per 32-element block: 24 bytes of 6-bit
+//     fields, element j at bits 6j..6j+5, then 8 zero bytes), so the matrix
+//     cores run at the FP6 rate with no decode in the main loop.
+//
+// FP6 E2M3 embedding (sign, 2 exponent bits with bias 1, 3 mantissa bits; the
+// subnormal step is 1/8): E1M2 level k/4 is the E2M3 code 2k; INT4 level n is
+// taken as n/2 (|n|/2 in {0, 0.5, ..., 3.5}, all E2M3 values; the nibble 8,
+// no code of the symmetric grid, would still come out as -8) and the product
+// of two INT4 operands is multiplied by 4 on the way out.  FP6 operand in the instruction (checked on the GPU against a
+// host model): lane l holds row l % 32 and the 32 elements of one 32-element
+// block (lane half h = block 2s + h of the 64-wide substep s) as 6-bit
+// fields in its first 6 registers.
 #include "ufp4_internal.h"
 #include "gemm_epilogue.h"
 
@@ -652,17 +667,20 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx4w(GemmLaunch g) {
 }
 
 // ---------------------------------------------------------------------------
-// MXFP8 kernel (E4M3 codes, one byte per element, 1 x 32 E8M0 scales): the
-// codes are already FP8 operands, so they are copied HBM -> LDS untouched as
-// in k_gemm_mx4w.  K step 128 = one 128-byte line per row; two 66 KiB stages
-// (codes 2 x 32 KiB, one scale word per row and operand).  Fragments and the
-// scale operand as the FP8 path of k_gemm_mx: lane l takes 16 bytes of blocks
-// 2s and 2s+1 (chunks 4s + h and 4s + 2 + h) and supplies the scale of row
-// l % 32, block 2s + h.
+// Byte-row kernels: one byte per element (MXFP8 E4M3 codes, or FP6 E2M3
+// fields in 32-byte slots), copied HBM -> LDS untouched as in k_gemm_mx4w.
+// K step 128 = one 128-byte line per row; two 66 KiB stages (codes 2 x 32 KiB,
+// one scale word per row and operand).  FP8 fragments and the scale operand
+// as in the FP8 path of k_gemm_mx: lane l takes 16 bytes of blocks 2s and
+// 2s+1 (chunks 4s + h and 4s + 2 + h) and supplies the scale of row l % 32,
+// block 2s + h.  FP6 fragments: lane l takes the 24 bytes of block 2s + h
+// (chunk 4s + 2h and the first half of chunk 4s + 2h + 1), same scale.
 // ---------------------------------------------------------------------------
 constexpr int K8 = 128;
 constexpr int W8_CODES = 2 * TM * 128;
 constexpr int W8_STAGE = W8_CODES + 2 * TM * 4;   // 66 KiB
+
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void w8_issue(const W4Ctx& c, int step, int st) {
   const int s = step < c.nsteps ? step : c.nsteps - 1;   // past the end: re-read, unused
@@ -679,20 +697,30 @@ __device__ __forceinline__ void w8_issue(const W4Ctx& c, int step, int st) {
   lds_load4(base + W8_CODES + TM * 4 + swave, c.rsb, c.sb_voff, (uint32_t)s * 4u);
 }
 
+template <int FMT>
 __device__ __forceinline__ void w8_frags(const uint8_t* stage, int s, int lane, int wm, int wn,
                                          F4Frags& f) {
   const int h = lane >> 5;
+  const uint8_t* b = stage + TM * 128;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ra = wm * 128 + i * 32 + (lane & 31);
     const int rb = wn * 128 + i * 32 + (lane & 31);
-    const uint8_t* b = stage + TM * 128;
-    const v4i x0 = *reinterpret_cast<const v4i*>(stage + off128(ra, 4 * s + h));
-    const v4i x1 = *reinterpret_cast<const v4i*>(stage + off128(ra, 4 * s + 2 + h));
-    const v4i y0 = *reinterpret_cast<const v4i*>(b + off128(rb, 4 * s + h));
-    const v4i y1 = *reinterpret_cast<const v4i*>(b + off128(rb, 4 * s + 2 + h));
-    f.a[i] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-    f.b[i] = v8i{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+    if constexpr (FMT == 0) {
+      const v4i x0 = *reinterpret_cast<const v4i*>(stage + off128(ra, 4 * s + h));
+      const v4i x1 = *reinterpret_cast<const v4i*>(stage + off128(ra, 4 * s + 2 + h));
+      const v4i y0 = *reinterpret_cast<const v4i*>(b + off128(rb, 4 * s + h));
+      const v4i y1 = *reinterpret_cast<const v4i*>(b + off128(rb, 4 * s + 2 + h));
+      f.a[i] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      f.b[i] = v8i{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+    } else {
+      const v4i x0 = *reinterpret_cast<const v4i*>(stage + off128(ra, 4 * s + 2 * h));
+      const v2i x1 = *reinterpret_cast<const v2i*>(stage + off128(ra, 4 * s + 2 * h + 1));
+      const v4i y0 = *reinterpret_cast<const v4i*>(b + off128(rb, 4 * s + 2 * h));
+      const v2i y1 = *reinterpret_cast<const v2i*>(b + off128(rb, 4 * s + 2 * h + 1));
+      f.a[i] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], 0, 0};
+      f.b[i] = v8i{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], 0, 0};
+    }
   }
 }
 
@@ -706,6 +734,8 @@ __device__ __forceinline__ void w8_scales(const uint8_t* stage, int lane, int wm
   }
 }
 
+// FMT is the operand format code of the instruction (0 = FP8 E4M3, 2 = FP6 E2M3).
+template <int FMT>
 __device__ __forceinline__ void f8_mfma(floatx16 (&acc)[4][4], const F4Frags& f,
                                         const uint32_t (&sa)[4], const uint32_t (&sb)[4],
                                         int s, int h) {
@@ -720,11 +750,12 @@ __device__ __forceinline__ void f8_mfma(floatx16 (&acc)[4][4], const F4Frags& f,
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0,
-                                                                  0, xa[i], 0, xb[j]);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], FMT,
+                                                                  FMT, 0, xa[i], 0, xb[j]);
 }
 
-__global__ __launch_bounds__(kThreads) void k_gemm_mx8(GemmLaunch g) {
+template <int FMT, bool X4>
+__global__ __launch_bounds__(kThreads) void k_gemm_mxrow(GemmLaunch g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   int tm, tn;
@@ -739,14 +770,15 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx8(GemmLaunch g) {
   const int64_t rows_b = g.PB - col0 < TN ? g.PB - col0 : TN;
   const uint32_t rs = (uint32_t)K;            // one byte per element
   const int64_t nkb = K / 32;
+  const int sha = g.a_br == 32 ? 5 : 0, shb = g.b_br == 32 ? 5 : 0;
 
   W4Ctx c;
   c.wave = wave;
   c.nsteps = (int)(K / K8);
   c.ra = rsrc4(g.a_codes + row0 * rs, (uint32_t)(rows_a * rs));
   c.rb = rsrc4(g.b_codes + col0 * rs, (uint32_t)(rows_b * rs));
-  c.rsa = rsrc4(g.a_scales, (uint32_t)(g.PA * nkb));
-  c.rsb = rsrc4(g.b_scales, (uint32_t)(g.PB * nkb));
+  c.rsa = rsrc4(g.a_scales, (uint32_t)(((g.PA - 1) >> sha) + 1) * (uint32_t)nkb);
+  c.rsb = rsrc4(g.b_scales, (uint32_t)(((g.PB - 1) >> shb) + 1) * (uint32_t)nkb);
   c.lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds;
   // lane i of wave load q: tile row 64 w + 8 q + i / 8, the chunk whose
   // swizzled slot is i % 8
@@ -759,8 +791,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx8(GemmLaunch g) {
     int64_t ra = row0 + wave * 64 + lane, rb = col0 + wave * 64 + lane;
     if (ra >= g.PA) ra = g.PA - 1;   // codes of such rows read as zero; any scale works
     if (rb >= g.PB) rb = g.PB - 1;
-    c.sa_voff = (uint32_t)(ra * nkb);
-    c.sb_voff = (uint32_t)(rb * nkb);
+    c.sa_voff = (uint32_t)((ra >> sha) * nkb);
+    c.sb_voff = (uint32_t)((rb >> shb) * nkb);
   }
 
   floatx16 acc[4][4];
@@ -774,32 +806,84 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx8(GemmLaunch g) {
   __syncthreads();
   F4Frags f0, f1;
   uint32_t sa[4], sb[4];
-  w8_frags(lds, 0, lane, wm, wn, f0);
+  w8_frags<FMT>(lds, 0, lane, wm, wn, f0);
   w8_scales(lds, lane, wm, wn, sa, sb);
 
   for (int step = 0; step < c.nsteps; ++step) {
     const uint8_t* cur = lds + (step & 1) * W8_STAGE;
     w8_issue(c, step + 1, (step + 1) & 1);
-    w8_frags(cur, 1, lane, wm, wn, f1);
-    f8_mfma(acc, f0, sa, sb, 0, h);
-    f8_mfma(acc, f1, sa, sb, 1, h);
+    w8_frags<FMT>(cur, 1, lane, wm, wn, f1);
+    f8_mfma<FMT>(acc, f0, sa, sb, 0, h);
+    f8_mfma<FMT>(acc, f1, sa, sb, 1, h);
     wait_vmcnt<0>();
     __syncthreads();
     const uint8_t* nxt = lds + ((step + 1) & 1) * W8_STAGE;
-    w8_frags(nxt, 0, lane, wm, wn, f0);
+    w8_frags<FMT>(nxt, 0, lane, wm, wn, f0);
     w8_scales(nxt, lane, wm, wn, sa, sb);
   }
 
+  if constexpr (X4) {   // INT4 operands entered as n / 2
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] *= 4.0f;
+  }
   store_c<4, 4>(g.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
                 lane, acc);
 }
 
-hipError_t launch_mx8(const GemmLaunch& g, hipStream_t s) {
+// E2M3 field of a 4-bit code (see the header): E1M2 sign-magnitude s|k ->
+// s<<5 | 2k; INT4 two's complement n -> sign<<5 | E2M3(|n| / 2).
+template <int GRID>
+__device__ __forceinline__ uint32_t fp6_field(uint32_t c) {
+  if constexpr (GRID == 0) {
+    return ((c & 8u) << 2) | ((c & 7u) << 1);
+  } else {
+    const uint32_t neg = c >> 3;
+    const uint32_t m = neg ? 16u - c : c;       // |n| in 0..8
+    return (neg << 5) | (m <= 4u ? 4u * m : 2u * m + 8u);
+  }
+}
+
+// One thread per 32-element block: 16 code bytes in, one 32-byte FP6 slot out.
+template <int GRID>
+__global__ __launch_bounds__(256) void k_fp6_expand(const uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ out, int64_t nblk) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t bk = (int64_t)blockIdx.x * 256 + threadIdx.x; bk < nblk; bk += stride) {
+    const v4i w = *reinterpret_cast<const v4i*>(codes + bk * 16);
+    uint32_t o[7] = {0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t f = fp6_field<GRID>(((uint32_t)w[j >> 3] >> (4 * (j & 7))) & 15u);
+      const int bit = 6 * j, wi = bit >> 5, sh = bit & 31;
+      o[wi] |= f << sh;
+      if (sh > 26) o[wi + 1] |= f >> (32 - sh);
+    }
+    v4i* dst = reinterpret_cast<v4i*>(out + bk * 32);
+    dst[0] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+    dst[1] = v4i{(int)o[4], (int)o[5], 0, 0};
+  }
+}
+
+template <int FMT, bool X4>
+hipError_t launch_mxrow(const GemmLaunch& g, hipStream_t s) {
   constexpr int bytes = 2 * W8_STAGE;
   static std::atomic<uint64_t> lds_set{0};
-  const hipError_t e = set_lds_limit((const void*)k_gemm_mx8, bytes, lds_set);
+  const hipError_t e = set_lds_limit((const void*)k_gemm_mxrow<FMT, X4>, bytes, lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_gemm_mx8, dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
+  hipLaunchKernelGGL((k_gemm_mxrow<FMT, X4>), dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
+  return hipGetLastError();
+}
+
+template <int GRID>
+hipError_t launch_fp6_expand(const uint8_t* codes, uint8_t* out, int64_t P, int64_t K,
+                             hipStream_t s) {
+  const int64_t nblk = P * (K / 32);
+  if (nblk == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((nblk + 255) / 256, 8192);
+  hipLaunchKernelGGL((k_fp6_expand<GRID>), dim3((unsigned)blocks), dim3(256), 0, s, codes, out,
+                     nblk);
   return hipGetLastError();
 }
 
@@ -834,12 +918,38 @@ bool gemm_mx_supported(const GemmLaunch& g) {
          g.K / 2 * (int64_t)TM <= INT32_MAX;
 }
 
+bool gemm_mx6_supported(const GemmLaunch& g) {
+  return g.mode == 0 && (g.grid == 0 || g.grid == 1) && g.scale_mode == 1 && g.a_bc == 32 &&
+         g.b_bc == 32 && (g.a_br == 1 || g.a_br == 32) && (g.b_br == 1 || g.b_br == 32) &&
+         g.K % K8 == 0 && g.K * (int64_t)TM <= INT32_MAX &&
+         ((g.PA - 1) / g.a_br + 1) * (g.K / 32) <= INT32_MAX &&
+         ((g.PB - 1) / g.b_br + 1) * (g.K / 32) <= INT32_MAX;
+}
+
+int64_t gemm_mx6_workspace(const GemmLaunch& g) {
+  return ((g.PA * g.K + 255) / 256) * 256 + g.PB * g.K;
+}
+
+hipError_t launch_gemm_mx6(const GemmLaunch& g, uint8_t* ws, hipStream_t s) {
+  if (g.total_tiles == 0) return hipSuccess;
+  GemmLaunch x = g;
+  x.a_codes = ws;
+  x.b_codes = ws + ((g.PA * g.K + 255) / 256) * 256;
+  hipError_t e = g.grid == 0 ? launch_fp6_expand<0>(g.a_codes, ws, g.PA, g.K, s)
+                             : launch_fp6_expand<1>(g.a_codes, ws, g.PA, g.K, s);
+  if (e != hipSuccess) return e;
+  e = g.grid == 0 ? launch_fp6_expand<0>(g.b_codes, const_cast<uint8_t*>(x.b_codes), g.PB, g.K, s)
+                  : launch_fp6_expand<1>(g.b_codes, const_cast<uint8_t*>(x.b_codes), g.PB, g.K, s);
+  if (e != hipSuccess) return e;
+  return g.grid == 0 ? launch_mxrow<2, false>(x, s) : launch_mxrow<2, true>(x, s);
+}
+
 hipError_t launch_gemm_mx(const GemmLaunch& g, hipStream_t s) {
   if (g.total_tiles == 0) return hipSuccess;
   switch (g.grid) {
     case 0: return launch_mx<0>(g, s);
     case 1: return launch_mx<1>(g, s);
-    case 3: return launch_mx8(g, s);
+    case 3: return launch_mxrow<0, false>(g, s);
     default: return g.K % KW == 0 ? launch_mx4w(g, s) : launch_mx4(g, s);
   }
 }

@@ -172,6 +172,12 @@ bool gemm_mx_supported(const GemmLaunch& g);
 bool gemm_rd_supported(const GemmLaunch& g);
 hipError_t launch_gemm_rd(const GemmLaunch& g, hipStream_t s);
 hipError_t launch_gemm_mx(const GemmLaunch& g, hipStream_t s);
+// E1M2 / INT4 with 32-element E8M0 blocks as FP6 E2M3 operands: both
+// operands are first expanded into `ws` (gemm_mx6_workspace bytes, 256-byte
+// aligned), then multiplied on the scaled matrix cores at the FP6 rate.
+bool gemm_mx6_supported(const GemmLaunch& g);
+int64_t gemm_mx6_workspace(const GemmLaunch& g);
+hipError_t launch_gemm_mx6(const GemmLaunch& g, uint8_t* ws, hipStream_t s);
 
 hipError_t launch_dequant(const uint8_t* codes, const void* scales, int64_t P, int64_t K,
                           int32_t grid, int32_t scale_mode, int32_t br, int32_t bc, float* out,

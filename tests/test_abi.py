@@ -127,6 +127,41 @@ def test_gemm_argument_errors():
     assert g(ctypes.byref(a), ctypes.byref(_qt(3 * 32 + 1, 64)), 4, ok_off, ctypes.c_void_p(FAKE), 32, None) == U.UFP4_ERR_SHAPE
 
 
+def test_gemm_workspace_errors():
+    """ufp4_gemm_ws / ufp4_gemm_workspace_bytes: sizes come from metadata
+    alone; a bad op, a null workspace with a size, a workspace smaller than
+    asked for or not 256-byte aligned are rejected before any HIP call."""
+    lib = U.lib_handle()
+    pow2 = U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 1)
+    a, b = _qt(300, 256, pow2), _qt(64, 256, pow2)
+    wb = lib.ufp4_gemm_workspace_bytes
+    need = (300 * 256 + 255) // 256 * 256 + 64 * 256
+    for op in (U.UFP4_GEMM_FPROP, U.UFP4_GEMM_DGRAD, U.UFP4_GEMM_WGRAD):
+        assert wb(op, ctypes.byref(a), ctypes.byref(b), 0) == need
+    assert wb(3, ctypes.byref(a), ctypes.byref(b), 0) == 0
+    assert wb(0, ctypes.byref(a), ctypes.byref(b), 2) == 0          # grouped: none yet
+    e2m1 = pow2.copy(grid=U.UFP4_E2M1)
+    assert wb(0, ctypes.byref(_qt(300, 256, e2m1)), ctypes.byref(_qt(64, 256, e2m1)), 0) == 0
+    assert wb(0, ctypes.byref(_qt(300, 160, pow2)), ctypes.byref(_qt(64, 160, pow2)), 0) == 0
+    assert wb(0, ctypes.byref(_qt(300, 256)), ctypes.byref(_qt(64, 256)), 0) == 0   # fp32 scales
+    assert wb(0, None, ctypes.byref(b), 0) == 0
+    f = lib.ufp4_gemm_ws
+    C = ctypes.c_void_p(FAKE)
+    ab = (ctypes.byref(a), ctypes.byref(b))
+    assert f(3, *ab, 0, None, C, 64, ctypes.c_void_p(FAKE), need, None) == U.UFP4_ERR_INVALID_ARG
+    assert f(0, *ab, -1, None, C, 64, ctypes.c_void_p(FAKE), need, None) == U.UFP4_ERR_INVALID_ARG
+    assert f(0, *ab, 0, None, C, 64, None, need, None) == U.UFP4_ERR_INVALID_ARG
+    assert f(0, *ab, 0, None, C, 64, ctypes.c_void_p(FAKE), need - 1, None) == U.UFP4_ERR_INVALID_ARG
+    assert f(0, *ab, 0, None, C, 64, ctypes.c_void_p(FAKE + 16), need, None) == U.UFP4_ERR_INVALID_ARG
+    assert f(0, *ab, 0, None, None, 64, ctypes.c_void_p(FAKE), need, None) == U.UFP4_ERR_INVALID_ARG
+    assert f(0, *ab, 0, None, C, 63, ctypes.c_void_p(FAKE), need, None) == U.UFP4_ERR_INVALID_ARG
+    assert f(0, ctypes.byref(a), ctypes.byref(_qt(64, 128, pow2)), 0, None, C, 64,
+             ctypes.c_void_p(FAKE), need, None) == U.UFP4_ERR_MISMATCH
+    # empty operands: nothing to do, the workspace is not touched
+    assert f(0, ctypes.byref(_qt(0, 256, pow2)), ctypes.byref(b), 0, None, C, 64,
+             ctypes.c_void_p(FAKE), 1, None) == U.UFP4_OK
+
+
 def test_segmented_and_misc_errors():
     lib = U.lib_handle()
     cfg = U.make_cfg(rht_n=32, block_cols=32)

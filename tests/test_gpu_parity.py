@@ -751,3 +751,67 @@ def test_quant_dual_n128(grid, rnd, b):
     ref = {"codes": np.concatenate([np.asarray(r["codes"]).reshape(-1) for r in segs]),
            "scales": np.concatenate([np.asarray(r["scales"]).reshape(-1) for r in segs])}
     _assert_q_equal(qc, ref, "col")
+
+
+@pytest.mark.parametrize("grid", [U.UFP4_E1M2, U.UFP4_INT4, U.UFP4_E2M1])
+@pytest.mark.parametrize("br", [1, 32])
+@pytest.mark.parametrize("K", [128, 384, 160])
+def test_gemm_ws_fp6(grid, br, K):
+    """The workspace entry point: E1M2 / INT4 with 32-element E8M0 blocks and
+    K % 128 == 0 run as FP6 E2M3 operands after the expansion into the
+    workspace; E2M1 and K = 160 take no workspace (0 bytes) and run as the
+    plain call.  3 ragged row tiles of A, 2 of B; all three operations."""
+    _print_case("gemm ws fp6", grid, br, K)
+    cfg = U.make_cfg(grid, U.UFP4_SR if br == 32 else U.UFP4_RTNE, U.UFP4_SCALE_POW2, br, 32,
+                     1 if br == 32 else 32, sign_seed=6, sr_seed=91)
+    ta, tb = rand_bits(544, K, 41), rand_bits(288, K, 42)
+    qa, ra = compare_quant(ta, 0, cfg, with_rotated=False)
+    qb, rb = compare_quant(tb, 0, cfg, with_rotated=False)
+    need = U.ufp4_gemm_workspace_bytes(U.UFP4_GEMM_FPROP, qa, qb)
+    fp6 = grid != U.UFP4_E2M1 and K % 128 == 0
+    assert need == ((544 * K + 255) // 256 * 256 + 288 * K if fp6 else 0)
+    ref = O.gemm_ref(oracle_dequant64(ra, cfg), oracle_dequant64(rb, cfg))
+    for op in (U.UFP4_GEMM_FPROP, U.UFP4_GEMM_DGRAD, U.UFP4_GEMM_WGRAD):
+        C = U.ufp4_gemm_ws(op, qa, qb).cpu().numpy()
+        err = O.rel_fro(C, ref)
+        assert err <= GEMM_TOL, (op, err)
+    # a workspace reused by a second, smaller call on the same stream
+    if fp6:
+        ws = torch.full((need,), 0xAB, dtype=torch.uint8, device="cuda")
+        U.ufp4_gemm_ws(U.UFP4_GEMM_FPROP, qa, qb, workspace=ws)
+        qa2 = U.QTensor(qa.codes[:256], qa.scales[:256 // br], 256, K, qa.cfg)
+        C2 = U.ufp4_gemm_ws(U.UFP4_GEMM_FPROP, qa2, qb, workspace=ws).cpu().numpy()
+        ra2 = dict(ra, codes=ra["codes"][:256], scales=ra["scales"][:256 // br], P=256)
+        assert O.rel_fro(C2, O.gemm_ref(oracle_dequant64(ra2, cfg), oracle_dequant64(rb, cfg))) <= GEMM_TOL
+
+
+@pytest.mark.parametrize("grid", [U.UFP4_E1M2, U.UFP4_INT4])
+def test_gemm_ws_fp6_every_code(grid):
+    """Random code bytes (every code of the grid, E1M2's negative zero
+    included; INT4's nibble 8 is no code of {-7..7} and is replaced by 0) and
+    random E8M0 scales straight into the FP6 path, against the oracle's decode
+    of the same codes; the plain call agrees as well."""
+    _print_case("gemm ws fp6 codes", grid)
+    rng = np.random.default_rng(grid + 3)
+    P_a, P_b, K = 320, 96, 256
+    cfg = U.make_cfg(grid, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 1)
+    ca = rng.integers(0, 256, size=(P_a, K // 2), dtype=np.uint8)
+    cb = rng.integers(0, 256, size=(P_b, K // 2), dtype=np.uint8)
+    if grid == U.UFP4_INT4:
+        for c in (ca, cb):
+            c[(c & 0x0F) == 8] &= 0xF0
+            c[(c >> 4) == 8] &= 0x0F
+    sa = rng.integers(118, 136, size=(P_a, K // 32), dtype=np.uint8)
+    sb = rng.integers(118, 136, size=(P_b, K // 32), dtype=np.uint8)
+    dev = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+    qa = U.QTensor(dev(ca), dev(sa), P_a, K, cfg)
+    qb = U.QTensor(dev(cb), dev(sb), P_b, K, cfg)
+    spec = spec_of(cfg)
+    da = O.dequant(ca, sa, spec, P_a, K)[1]
+    db = O.dequant(cb, sb, spec, P_b, K)[1]
+    ref = O.gemm_ref(da, db)
+    assert U.ufp4_gemm_workspace_bytes(U.UFP4_GEMM_FPROP, qa, qb) > 0
+    C = U.ufp4_gemm_ws(U.UFP4_GEMM_FPROP, qa, qb).cpu().numpy()
+    assert O.rel_fro(C, ref) <= GEMM_TOL
+    C0 = U.ufp4_gemm_fprop(qa, qb).cpu().numpy()
+    assert O.rel_fro(C0, ref) <= GEMM_TOL
