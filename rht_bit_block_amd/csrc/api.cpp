@@ -139,16 +139,43 @@ void fill_gemm(GemmLaunch& g, const ufp4_qtensor* a, const ufp4_qtensor* b, floa
 constexpr int64_t kTile = 256;
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// FP6 workspace bytes a dense GEMM of A and B can use (0: no workspace path).
-int64_t dense_fp6_bytes(const ufp4_qtensor* A, const ufp4_qtensor* B) {
-  if (check_pair(A, B) || A->P == 0 || B->P == 0 || A->K == 0) return 0;
+// FP6 workspace bytes a GEMM of A and B described by `g` can use (0: none).
+int64_t fp6_bytes(const ufp4_qtensor* A, const ufp4_qtensor* B, const GemmLaunch& g) {
   if (!aligned(A->codes, 16) || !aligned(B->codes, 16) || !aligned(A->scales, 4) ||
       !aligned(B->scales, 4))
     return 0;
+  return gemm_mx6_supported(g) ? gemm_mx6_workspace(g) : 0;
+}
+
+int64_t dense_fp6_bytes(const ufp4_qtensor* A, const ufp4_qtensor* B) {
+  if (check_pair(A, B) || A->P == 0 || B->P == 0 || A->K == 0) return 0;
   GemmLaunch g;
   fill_gemm(g, A, B, nullptr, B->P);
   g.mode = 0;
-  return gemm_mx6_supported(g) ? gemm_mx6_workspace(g) : 0;
+  return fp6_bytes(A, B, g);
+}
+
+// The scaled-MFMA kernels take this launch (shape, blocks and alignment).
+bool mx_route(const GemmLaunch& g) {
+  return gemm_mx_supported(g) && aligned(g.a_scales, 4) && aligned(g.b_scales, 4) &&
+         aligned(g.a_codes, 16) && aligned(g.b_codes, 16);
+}
+
+// Launch of a filled GemmLaunch: FP6 operands through the workspace when one
+// is given and the operands qualify, else the scaled matrix cores for
+// E8M0 blocks they take, else the general kernels.
+int launch_any(const ufp4_qtensor* A, const ufp4_qtensor* B, const GemmLaunch& g, void* ws,
+               size_t ws_bytes, void* stream) {
+  if (ws) {
+    const int64_t need = fp6_bytes(A, B, g);
+    if (need > 0) {
+      if ((uint64_t)need > (uint64_t)ws_bytes || !aligned(ws, 256)) return UFP4_ERR_INVALID_ARG;
+      return hip_status(launch_gemm_mx6(g, static_cast<uint8_t*>(ws), (hipStream_t)stream));
+    }
+  }
+  if (mx_route(g)) return hip_status(launch_gemm_mx(g, (hipStream_t)stream));
+  if (g.grid == UFP4_E4M3) return UFP4_ERR_UNSUPPORTED;   // MXFP8 runs on the scaled MFMA only
+  return hip_status(launch_gemm(g, (hipStream_t)stream));
 }
 
 // Dense C = A B^T.  With a workspace (ws != null) E1M2 / INT4 operands with
@@ -171,18 +198,7 @@ int gemm_dense(const ufp4_qtensor* A, const ufp4_qtensor* B, float* C, int64_t l
   g.tile_start[0] = 0;
   g.tile_start[1] = (int32_t)tiles;
   g.total_tiles = (int32_t)tiles;
-  if (ws) {
-    const int64_t need = dense_fp6_bytes(A, B);
-    if (need > 0) {
-      if ((uint64_t)need > (uint64_t)ws_bytes || !aligned(ws, 256)) return UFP4_ERR_INVALID_ARG;
-      return hip_status(launch_gemm_mx6(g, static_cast<uint8_t*>(ws), (hipStream_t)stream));
-    }
-  }
-  const bool mx = gemm_mx_supported(g) && aligned(g.a_scales, 4) && aligned(g.b_scales, 4) &&
-                  aligned(g.a_codes, 16) && aligned(g.b_codes, 16);
-  if (mx) return hip_status(launch_gemm_mx(g, (hipStream_t)stream));
-  if (g.grid == UFP4_E4M3) return UFP4_ERR_UNSUPPORTED;   // MXFP8 runs on the scaled MFMA only
-  return hip_status(launch_gemm(g, (hipStream_t)stream));
+  return launch_any(A, B, g, ws, ws_bytes, stream);
 }
 
 int check_offsets(const int64_t* off, int32_t G, int64_t total, int64_t align) {
@@ -197,7 +213,8 @@ int check_offsets(const int64_t* off, int32_t G, int64_t total, int64_t align) {
 
 // Grouped along A's rows: fprop (B = W stacked) and dgrad (B = W^T stacked).
 int gemm_grouped_rows(const ufp4_qtensor* A, const ufp4_qtensor* B, int32_t G,
-                      const int64_t* off, float* C, int64_t ldc, void* stream) {
+                      const int64_t* off, float* C, int64_t ldc, void* stream,
+                      void* ws = nullptr, size_t ws_bytes = 0) {
   int st = check_pair(A, B);
   if (st) return st;
   if (A->cfg.grid == UFP4_E4M3) return UFP4_ERR_UNSUPPORTED;
@@ -223,7 +240,44 @@ int gemm_grouped_rows(const ufp4_qtensor* A, const ufp4_qtensor* B, int32_t G,
   g.off[G] = off[G];
   g.tile_start[G] = (int32_t)t;
   g.total_tiles = (int32_t)t;
-  return hip_status(launch_gemm(g, (hipStream_t)stream));
+  return launch_any(A, B, g, ws, ws_bytes, stream);
+}
+
+// Grouped along K: wgrad (segmented column-wise operands).  fp32 scales run
+// on the general kernels; 1 x 32 E8M0 blocks on the scaled matrix cores when
+// every segment length is a multiple of 128, else UFP4_ERR_UNSUPPORTED.
+int gemm_grouped_k(const ufp4_qtensor* dYt, const ufp4_qtensor* Xt, int32_t G,
+                   const int64_t* offsets, float* dW, int64_t ldw, void* stream,
+                   void* ws = nullptr, size_t ws_bytes = 0) {
+  int st = check_pair(dYt, Xt);
+  if (st) return st;
+  if (dYt->cfg.grid == UFP4_E4M3) return UFP4_ERR_UNSUPPORTED;
+  if (dYt->cfg.block_rows != 1 || Xt->cfg.block_rows != 1) return UFP4_ERR_UNSUPPORTED;
+  const int64_t align = 16;
+  st = check_offsets(offsets, G, dYt->K, align);
+  if (st) return st;
+  for (int i = 0; i < G; ++i) {
+    const int64_t L = offsets[i + 1] - offsets[i];
+    if (L % dYt->cfg.block_cols || L % Xt->cfg.block_cols || L % dYt->cfg.rht_n || L % 16)
+      return UFP4_ERR_SHAPE;
+  }
+  if (!dW || ldw < Xt->P) return UFP4_ERR_INVALID_ARG;
+  if (dYt->P == 0 || Xt->P == 0) return UFP4_OK;
+  GemmLaunch g;
+  fill_gemm(g, dYt, Xt, dW, ldw);
+  g.mode = 2;
+  g.ngroups = G;
+  const int64_t per = cdiv(dYt->P, kTile) * cdiv(Xt->P, kTile);
+  if (per * G > INT32_MAX) return UFP4_ERR_UNSUPPORTED;
+  for (int i = 0; i <= G; ++i) {
+    g.off[i] = offsets[i];
+    g.tile_start[i] = (int32_t)(per * i);
+  }
+  g.total_tiles = (int32_t)(per * G);
+  // the general kernels take fp32 scales only when grouped along K
+  if (g.scale_mode == UFP4_SCALE_POW2 && !(mx_route(g) || (ws && fp6_bytes(dYt, Xt, g) > 0)))
+    return UFP4_ERR_UNSUPPORTED;
+  return launch_any(dYt, Xt, g, ws, ws_bytes, stream);
 }
 
 }  // namespace
@@ -476,40 +530,28 @@ int ufp4_gemm_dgrad_grouped(const ufp4_qtensor* dYp, const ufp4_qtensor* Wt, int
 
 int ufp4_gemm_wgrad_grouped(const ufp4_qtensor* dYt, const ufp4_qtensor* Xt, int32_t G,
                             const int64_t* offsets, float* dW, int64_t ldw, void* stream) {
-  int st = check_pair(dYt, Xt);
-  if (st) return st;
-  if (dYt->cfg.grid == UFP4_E4M3) return UFP4_ERR_UNSUPPORTED;
-  if (dYt->cfg.scale_mode != UFP4_SCALE_F32 || dYt->cfg.block_rows != 1 ||
-      Xt->cfg.block_rows != 1)
-    return UFP4_ERR_UNSUPPORTED;
-  const int64_t align = 16;
-  st = check_offsets(offsets, G, dYt->K, align);
-  if (st) return st;
-  for (int i = 0; i < G; ++i) {
-    const int64_t L = offsets[i + 1] - offsets[i];
-    if (L % dYt->cfg.block_cols || L % Xt->cfg.block_cols || L % dYt->cfg.rht_n || L % 16)
-      return UFP4_ERR_SHAPE;
-  }
-  if (!dW || ldw < Xt->P) return UFP4_ERR_INVALID_ARG;
-  if (dYt->P == 0 || Xt->P == 0) return UFP4_OK;
-  GemmLaunch g;
-  fill_gemm(g, dYt, Xt, dW, ldw);
-  g.mode = 2;
-  g.ngroups = G;
-  const int64_t per = cdiv(dYt->P, kTile) * cdiv(Xt->P, kTile);
-  if (per * G > INT32_MAX) return UFP4_ERR_UNSUPPORTED;
-  for (int i = 0; i <= G; ++i) {
-    g.off[i] = offsets[i];
-    g.tile_start[i] = (int32_t)(per * i);
-  }
-  g.total_tiles = (int32_t)(per * G);
-  return hip_status(launch_gemm(g, (hipStream_t)stream));
+  return gemm_grouped_k(dYt, Xt, G, offsets, dW, ldw, stream);
 }
 
 size_t ufp4_gemm_workspace_bytes(int32_t op, const ufp4_qtensor* A, const ufp4_qtensor* B,
                                  int32_t G) {
-  if (op < UFP4_GEMM_FPROP || op > UFP4_GEMM_WGRAD || G != 0) return 0;
-  return (size_t)dense_fp6_bytes(A, B);
+  if (op < UFP4_GEMM_FPROP || op > UFP4_GEMM_WGRAD || G < 0 || G > kMaxGroups) return 0;
+  if (G == 0) return (size_t)dense_fp6_bytes(A, B);
+  if (check_pair(A, B) || A->P == 0 || B->P == 0 || A->K == 0) return 0;
+  GemmLaunch g;
+  fill_gemm(g, A, B, nullptr, B->P);
+  g.ngroups = 1;
+  if (op == UFP4_GEMM_WGRAD) {   // segment lengths are the call's to check
+    g.mode = 2;
+    g.off[0] = 0;
+    g.off[1] = A->K;
+  } else {
+    if (B->P % G) return 0;
+    g.mode = 1;
+    g.ngroups = G;
+    g.b_rows_per_group = B->P / G;
+  }
+  return (size_t)fp6_bytes(A, B, g);
 }
 
 int ufp4_gemm_ws(int32_t op, const ufp4_qtensor* A, const ufp4_qtensor* B, int32_t G,
@@ -518,8 +560,9 @@ int ufp4_gemm_ws(int32_t op, const ufp4_qtensor* A, const ufp4_qtensor* B, int32
   if (op < UFP4_GEMM_FPROP || op > UFP4_GEMM_WGRAD || G < 0) return UFP4_ERR_INVALID_ARG;
   if (!workspace && workspace_bytes) return UFP4_ERR_INVALID_ARG;
   if (G == 0) return gemm_dense(A, B, C, ldc, stream, workspace, workspace_bytes);
-  if (op == UFP4_GEMM_WGRAD) return ufp4_gemm_wgrad_grouped(A, B, G, offsets, C, ldc, stream);
-  return gemm_grouped_rows(A, B, G, offsets, C, ldc, stream);
+  if (op == UFP4_GEMM_WGRAD)
+    return gemm_grouped_k(A, B, G, offsets, C, ldc, stream, workspace, workspace_bytes);
+  return gemm_grouped_rows(A, B, G, offsets, C, ldc, stream, workspace, workspace_bytes);
 }
 
 int ufp4_transpose_qtensor(const ufp4_qtensor* src, uint8_t* dst_codes, void* dst_scales,

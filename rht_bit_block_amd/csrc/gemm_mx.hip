@@ -121,6 +121,56 @@ __device__ __forceinline__ uint32_t off128(int row, int c) {   // 128-byte rows
   return (uint32_t)(row * 128 + 16 * (c ^ (row & 7)));
 }
 
+// The operands of one output tile.  mode 0: the dense operands; mode 1
+// (grouped along A's rows): rows off[g] .. off[g+1] of A against rows
+// g*R .. g*R + R of B; mode 2 (grouped along K): segment g of both operands,
+// stored [P][L_g] at element offset P*off[g] with 1 x 32 scales at P*off[g]/32.
+// CPE2 = code bytes per two elements (1: packed nibbles, 2: byte rows).
+struct MxTile {
+  const uint8_t* a_codes;
+  const uint8_t* b_codes;
+  const uint8_t* a_scales;
+  const uint8_t* b_scales;
+  int64_t a_rows, b_rows, K;
+  float* c;
+  int tm, tn;
+};
+
+template <int CPE2>
+__device__ __forceinline__ MxTile mx_resolve(const GemmLaunch& g, int b) {
+  const int tile = xcd_linear(b, g.total_tiles);
+  int grp = 0;
+  while (grp + 1 < g.ngroups && g.tile_start[grp + 1] <= tile) ++grp;
+  const int local = tile - g.tile_start[grp];
+  const uint8_t* sa = reinterpret_cast<const uint8_t*>(g.a_scales);
+  const uint8_t* sb = reinterpret_cast<const uint8_t*>(g.b_scales);
+  MxTile t;
+  if (g.mode == 0) {
+    t.a_codes = g.a_codes; t.b_codes = g.b_codes; t.a_scales = sa; t.b_scales = sb;
+    t.a_rows = g.PA; t.b_rows = g.PB; t.K = g.K; t.c = g.c;
+  } else if (g.mode == 1) {
+    const int64_t r0 = g.off[grp], rb0 = (int64_t)grp * g.b_rows_per_group;
+    t.a_codes = g.a_codes + r0 * g.K * CPE2 / 2;
+    t.b_codes = g.b_codes + rb0 * g.K * CPE2 / 2;
+    t.a_scales = sa + (r0 / g.a_br) * (g.K / 32);
+    t.b_scales = sb + (rb0 / g.b_br) * (g.K / 32);
+    t.a_rows = g.off[grp + 1] - r0; t.b_rows = g.b_rows_per_group; t.K = g.K;
+    t.c = g.c + r0 * g.ldc;
+  } else {
+    const int64_t e = g.off[grp];
+    t.a_codes = g.a_codes + g.PA * e * CPE2 / 2;
+    t.b_codes = g.b_codes + g.PB * e * CPE2 / 2;
+    t.a_scales = sa + g.PA * (e / 32);
+    t.b_scales = sb + g.PB * (e / 32);
+    t.a_rows = g.PA; t.b_rows = g.PB; t.K = g.off[grp + 1] - e;
+    t.c = g.c + (int64_t)grp * g.PA * g.ldc;
+  }
+  const int tiles_m = (int)((t.a_rows + TM - 1) / TM);
+  const int tiles_n = (int)((t.b_rows + TN - 1) / TN);
+  grouped_order(local, tiles_m, tiles_n > 0 ? tiles_n : 1, t.tm, t.tn);
+  return t;
+}
+
 // Raw loads of one K step for this thread: 4 code chunks of A and of B (rows
 // t/4 + 64q, block t%4) and the scale words of the wave's rows.
 struct StepLoads {
@@ -230,32 +280,31 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(GemmLaunch g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int STAGE = 2 * TM * 128;
 
-  int tm, tn;
-  tile_order(blockIdx.x, g.total_tiles, (int)((g.PA + TM - 1) / TM), (int)((g.PB + TN - 1) / TN),
-             tm, tn);
+  const MxTile t = mx_resolve<1>(g, blockIdx.x);
+  const int tm = t.tm, tn = t.tn;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
-  const int64_t K = g.K;
+  const int64_t K = t.K;
   const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
-  const int64_t rows_a = g.PA - row0 < TM ? g.PA - row0 : TM;
-  const int64_t rows_b = g.PB - col0 < TN ? g.PB - col0 : TN;
+  const int64_t rows_a = t.a_rows - row0 < TM ? t.a_rows - row0 : TM;
+  const int64_t rows_b = t.b_rows - col0 < TN ? t.b_rows - col0 : TN;
 
   Ctx c;
   c.row_stride = (uint32_t)(K / 2);
-  c.ra = make_rsrc(g.a_codes + row0 * (K / 2), (uint32_t)(rows_a * (K / 2)));
-  c.rb = make_rsrc(g.b_codes + col0 * (K / 2), (uint32_t)(rows_b * (K / 2)));
+  c.ra = make_rsrc(t.a_codes + row0 * (K / 2), (uint32_t)(rows_a * (K / 2)));
+  c.rb = make_rsrc(t.b_codes + col0 * (K / 2), (uint32_t)(rows_b * (K / 2)));
   c.ld_off = (uint32_t)(tid >> 2) * c.row_stride + 16u * (uint32_t)(tid & 3);
   c.nsteps = (int)(K / KS);
   const int64_t nkb = K / 32;
-  const uint8_t* sa = reinterpret_cast<const uint8_t*>(g.a_scales);
-  const uint8_t* sb = reinterpret_cast<const uint8_t*>(g.b_scales);
+  const uint8_t* sa = t.a_scales;
+  const uint8_t* sb = t.b_scales;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     int64_t ra = row0 + wm * 128 + i * 32 + (lane & 31);
     int64_t rb = col0 + wn * 128 + i * 32 + (lane & 31);
-    if (ra >= g.PA) ra = g.PA - 1;   // codes of such rows are zero; any scale works
-    if (rb >= g.PB) rb = g.PB - 1;
+    if (ra >= t.a_rows) ra = t.a_rows - 1;   // codes of such rows are zero; any scale works
+    if (rb >= t.b_rows) rb = t.b_rows - 1;
     c.sa_row[i] = sa + (ra / g.a_br) * nkb;
     c.sb_row[i] = sb + (rb / g.b_br) * nkb;
   }
@@ -266,47 +315,49 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(GemmLaunch g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
 
-  StepLoads x, y;
-  uint32_t cs_a[4], cs_b[4];     // scale words of the step being multiplied
-  fetch(c, 0, x);
-  fetch(c, 1, y);
-  stage<GRID>(lds, x, tid);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { cs_a[i] = x.sa[i]; cs_b[i] = x.sb[i]; }
-  __syncthreads();
-  Frags f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f.a[i] = load_frag(lds, 0, 0, lane, wm, i);
-    f.b[i] = load_frag(lds, 1, 0, lane, wn, i);
-  }
-
-  // Step i: LDS stage i&1 holds step i; `nx` holds the loads of step i+1;
-  // `fr` receives the loads of step i+2.
-  auto body = [&](int step, StepLoads& nx, StepLoads& fr) {
-    const uint8_t* cur = lds + (step & 1) * STAGE;
-    uint8_t* nxt = lds + ((step + 1) & 1) * STAGE;
-    fetch(c, step + 2, fr);
-    mfma_substep<GRID>(acc, f, cs_a, cs_b, 0, h, cur, 1, lane, wm, wn);
-    stage<GRID>(nxt, nx, tid);
-    mfma_substep<GRID>(acc, f, cs_a, cs_b, 1, h, nullptr, 0, lane, wm, wn);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { cs_a[i] = nx.sa[i]; cs_b[i] = nx.sb[i]; }
+  if (c.nsteps > 0) {   // an empty K segment leaves C = 0
+    StepLoads x, y;
+    uint32_t cs_a[4], cs_b[4];     // scale words of the step being multiplied
+    fetch(c, 0, x);
+    fetch(c, 1, y);
+    stage<GRID>(lds, x, tid);
+  #pragma unroll
+    for (int i = 0; i < 4; ++i) { cs_a[i] = x.sa[i]; cs_b[i] = x.sb[i]; }
     __syncthreads();
-#pragma unroll
+    Frags f;
+  #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f.a[i] = load_frag(nxt, 0, 0, lane, wm, i);
-      f.b[i] = load_frag(nxt, 1, 0, lane, wn, i);
+      f.a[i] = load_frag(lds, 0, 0, lane, wm, i);
+      f.b[i] = load_frag(lds, 1, 0, lane, wn, i);
     }
-  };
-  int step = 0;
-  for (; step + 1 < c.nsteps; step += 2) {
-    body(step, y, x);
-    body(step + 1, x, y);
-  }
-  if (step < c.nsteps) body(step, y, x);
 
-  store_c<4, 4>(g.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
+    // Step i: LDS stage i&1 holds step i; `nx` holds the loads of step i+1;
+    // `fr` receives the loads of step i+2.
+    auto body = [&](int step, StepLoads& nx, StepLoads& fr) {
+      const uint8_t* cur = lds + (step & 1) * STAGE;
+      uint8_t* nxt = lds + ((step + 1) & 1) * STAGE;
+      fetch(c, step + 2, fr);
+      mfma_substep<GRID>(acc, f, cs_a, cs_b, 0, h, cur, 1, lane, wm, wn);
+      stage<GRID>(nxt, nx, tid);
+      mfma_substep<GRID>(acc, f, cs_a, cs_b, 1, h, nullptr, 0, lane, wm, wn);
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) { cs_a[i] = nx.sa[i]; cs_b[i] = nx.sb[i]; }
+      __syncthreads();
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f.a[i] = load_frag(nxt, 0, 0, lane, wm, i);
+        f.b[i] = load_frag(nxt, 1, 0, lane, wn, i);
+      }
+    };
+    int step = 0;
+    for (; step + 1 < c.nsteps; step += 2) {
+      body(step, y, x);
+      body(step + 1, x, y);
+    }
+    if (step < c.nsteps) body(step, y, x);
+  }
+
+  store_c<4, 4>(t.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
                 lane, acc);
 }
 
@@ -434,16 +485,15 @@ __device__ __forceinline__ void f4_mfma(floatx16 (&acc)[4][4], const F4Frags& f,
 __global__ __launch_bounds__(kThreads) void k_gemm_mx4(GemmLaunch g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  int tm, tn;
-  tile_order(blockIdx.x, g.total_tiles, (int)((g.PA + TM - 1) / TM), (int)((g.PB + TN - 1) / TN),
-             tm, tn);
+  const MxTile t = mx_resolve<1>(g, blockIdx.x);
+  const int tm = t.tm, tn = t.tn;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
-  const int64_t K = g.K;
+  const int64_t K = t.K;
   const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
-  const int64_t rows_a = g.PA - row0 < TM ? g.PA - row0 : TM;
-  const int64_t rows_b = g.PB - col0 < TN ? g.PB - col0 : TN;
+  const int64_t rows_a = t.a_rows - row0 < TM ? t.a_rows - row0 : TM;
+  const int64_t rows_b = t.b_rows - col0 < TN ? t.b_rows - col0 : TN;
   const uint32_t rs = (uint32_t)(K / 2);
   const int64_t nkb = K / 32;
   const int sha = g.a_br == 32 ? 5 : 0, shb = g.b_br == 32 ? 5 : 0;
@@ -451,11 +501,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx4(GemmLaunch g) {
   F4Ctx c;
   c.wave = wave;
   c.nsteps = (int)(K / KS);
-  c.ra = rsrc4(g.a_codes + row0 * rs, (uint32_t)(rows_a * rs));
-  c.rb = rsrc4(g.b_codes + col0 * rs, (uint32_t)(rows_b * rs));
+  c.ra = rsrc4(t.a_codes + row0 * rs, (uint32_t)(rows_a * rs));
+  c.rb = rsrc4(t.b_codes + col0 * rs, (uint32_t)(rows_b * rs));
   // scale arrays: rows of nkb bytes, one row per block row
-  c.rsa = rsrc4(g.a_scales, (uint32_t)(((g.PA - 1) >> sha) + 1) * (uint32_t)nkb);
-  c.rsb = rsrc4(g.b_scales, (uint32_t)(((g.PB - 1) >> shb) + 1) * (uint32_t)nkb);
+  c.rsa = rsrc4(t.a_scales, (uint32_t)(((t.a_rows - 1) >> sha) + 1) * (uint32_t)nkb);
+  c.rsb = rsrc4(t.b_scales, (uint32_t)(((t.b_rows - 1) >> shb) + 1) * (uint32_t)nkb);
   c.lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds;
   // code loads: lane i of wave load q covers tile row 64 w + 16 q + i / 4 and
   // the block whose swizzled LDS chunk is i % 4 (rows past the operand fall
@@ -468,8 +518,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx4(GemmLaunch g) {
   // scale loads: lane i covers tile row 64 w + i (clamped into the operand)
   {
     int64_t ra = row0 + wave * 64 + lane, rb = col0 + wave * 64 + lane;
-    if (ra >= g.PA) ra = g.PA - 1;
-    if (rb >= g.PB) rb = g.PB - 1;
+    if (ra >= t.a_rows) ra = t.a_rows - 1;
+    if (rb >= t.b_rows) rb = t.b_rows - 1;
     c.sa_voff = (uint32_t)((ra >> sha) * nkb);
     c.sb_voff = (uint32_t)((rb >> shb) * nkb);
   }
@@ -480,41 +530,43 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx4(GemmLaunch g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
 
-  f4_issue(c, 0, 0);
-  f4_issue(c, 1, 1);
-  f4_issue(c, 2, 2);
-  wait_vmcnt<2 * F4_VMEM_PER_STEP>();
-  __syncthreads();
-  F4Frags f0, f1;
-  uint32_t sa[4], sb[4];
-  f4_frags(lds, 0, lane, wm, wn, f0);
-  f4_scales(lds, lane, wm, wn, sa, sb);
+  if (c.nsteps > 0) {   // an empty K segment leaves C = 0
+    f4_issue(c, 0, 0);
+    f4_issue(c, 1, 1);
+    f4_issue(c, 2, 2);
+    wait_vmcnt<2 * F4_VMEM_PER_STEP>();
+    __syncthreads();
+    F4Frags f0, f1;
+    uint32_t sa[4], sb[4];
+    f4_frags(lds, 0, lane, wm, wn, f0);
+    f4_scales(lds, lane, wm, wn, sa, sb);
 
-  // Step i computes from stage i % 4 while steps i+1, i+2 are in flight and
-  // step i+3 is issued into the stage step i-1 used.
-  auto body = [&](int step, int st) {
-    const uint8_t* cur = lds + st * F4_STAGE;
-    f4_issue(c, step + 3, (st + 3) & 3);
-    f4_frags(cur, 1, lane, wm, wn, f1);
-    f4_mfma(acc, f0, sa, sb, 0, h);
-    f4_mfma(acc, f1, sa, sb, 1, h);
-    wait_vmcnt<2 * F4_VMEM_PER_STEP>();   // step i+1 has landed (this wave's part)
-    __syncthreads();                      // ... and every other wave's
-    const uint8_t* nxt = lds + ((st + 1) & 3) * F4_STAGE;
-    f4_frags(nxt, 0, lane, wm, wn, f0);
-    f4_scales(nxt, lane, wm, wn, sa, sb);
-  };
-  int step = 0;
-  for (; step + 3 < c.nsteps; step += 4) {
-    body(step, 0);
-    body(step + 1, 1);
-    body(step + 2, 2);
-    body(step + 3, 3);
+    // Step i computes from stage i % 4 while steps i+1, i+2 are in flight and
+    // step i+3 is issued into the stage step i-1 used.
+    auto body = [&](int step, int st) {
+      const uint8_t* cur = lds + st * F4_STAGE;
+      f4_issue(c, step + 3, (st + 3) & 3);
+      f4_frags(cur, 1, lane, wm, wn, f1);
+      f4_mfma(acc, f0, sa, sb, 0, h);
+      f4_mfma(acc, f1, sa, sb, 1, h);
+      wait_vmcnt<2 * F4_VMEM_PER_STEP>();   // step i+1 has landed (this wave's part)
+      __syncthreads();                      // ... and every other wave's
+      const uint8_t* nxt = lds + ((st + 1) & 3) * F4_STAGE;
+      f4_frags(nxt, 0, lane, wm, wn, f0);
+      f4_scales(nxt, lane, wm, wn, sa, sb);
+    };
+    int step = 0;
+    for (; step + 3 < c.nsteps; step += 4) {
+      body(step, 0);
+      body(step + 1, 1);
+      body(step + 2, 2);
+      body(step + 3, 3);
+    }
+    for (; step < c.nsteps; ++step) body(step, step & 3);
+    wait_vmcnt<0>();   // drain the clamped prefetches before the workgroup ends
   }
-  for (; step < c.nsteps; ++step) body(step, step & 3);
-  wait_vmcnt<0>();   // drain the clamped prefetches before the workgroup ends
 
-  store_c<4, 4>(g.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
+  store_c<4, 4>(t.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
                 lane, acc);
 }
 
@@ -594,16 +646,15 @@ __device__ __forceinline__ void w4_scales(const uint8_t* stage, int lane, int wm
 __global__ __launch_bounds__(kThreads) void k_gemm_mx4w(GemmLaunch g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  int tm, tn;
-  tile_order(blockIdx.x, g.total_tiles, (int)((g.PA + TM - 1) / TM), (int)((g.PB + TN - 1) / TN),
-             tm, tn);
+  const MxTile t = mx_resolve<1>(g, blockIdx.x);
+  const int tm = t.tm, tn = t.tn;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
-  const int64_t K = g.K;
+  const int64_t K = t.K;
   const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
-  const int64_t rows_a = g.PA - row0 < TM ? g.PA - row0 : TM;
-  const int64_t rows_b = g.PB - col0 < TN ? g.PB - col0 : TN;
+  const int64_t rows_a = t.a_rows - row0 < TM ? t.a_rows - row0 : TM;
+  const int64_t rows_b = t.b_rows - col0 < TN ? t.b_rows - col0 : TN;
   const uint32_t rs = (uint32_t)(K / 2);
   const int64_t nkb = K / 32;
   const int sha = g.a_br == 32 ? 5 : 0, shb = g.b_br == 32 ? 5 : 0;
@@ -611,10 +662,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx4w(GemmLaunch g) {
   W4Ctx c;
   c.wave = wave;
   c.nsteps = (int)(K / KW);
-  c.ra = rsrc4(g.a_codes + row0 * rs, (uint32_t)(rows_a * rs));
-  c.rb = rsrc4(g.b_codes + col0 * rs, (uint32_t)(rows_b * rs));
-  c.rsa = rsrc4(g.a_scales, (uint32_t)(((g.PA - 1) >> sha) + 1) * (uint32_t)nkb);
-  c.rsb = rsrc4(g.b_scales, (uint32_t)(((g.PB - 1) >> shb) + 1) * (uint32_t)nkb);
+  c.ra = rsrc4(t.a_codes + row0 * rs, (uint32_t)(rows_a * rs));
+  c.rb = rsrc4(t.b_codes + col0 * rs, (uint32_t)(rows_b * rs));
+  c.rsa = rsrc4(t.a_scales, (uint32_t)(((t.a_rows - 1) >> sha) + 1) * (uint32_t)nkb);
+  c.rsb = rsrc4(t.b_scales, (uint32_t)(((t.b_rows - 1) >> shb) + 1) * (uint32_t)nkb);
   c.lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds;
   // lane i of wave load q: tile row 64 w + 8 q + i / 8, the chunk whose
   // swizzled slot is i % 8
@@ -625,8 +676,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx4w(GemmLaunch g) {
     c.code_voff[q] = (uint32_t)(wave * 64 + q * 8 + lrow) * rs + 16u * chunk;
   {
     int64_t ra = row0 + wave * 64 + lane, rb = col0 + wave * 64 + lane;
-    if (ra >= g.PA) ra = g.PA - 1;
-    if (rb >= g.PB) rb = g.PB - 1;
+    if (ra >= t.a_rows) ra = t.a_rows - 1;
+    if (rb >= t.b_rows) rb = t.b_rows - 1;
     c.sa_voff = (uint32_t)((ra >> sha) * nkb);
     c.sb_voff = (uint32_t)((rb >> shb) * nkb);
   }
@@ -637,32 +688,34 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx4w(GemmLaunch g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
 
-  w4_issue(c, 0, 0);
-  wait_vmcnt<0>();
-  __syncthreads();
-  F4Frags f0, f1;
-  uint32_t sa[2][4], sb[2][4];
-  w4_frags(lds, 0, lane, wm, wn, f0);
-  w4_scales(lds, lane, wm, wn, sa, sb);
-
-  for (int step = 0; step < c.nsteps; ++step) {
-    const uint8_t* cur = lds + (step & 1) * W4_STAGE;
-    w4_issue(c, step + 1, (step + 1) & 1);
-    w4_frags(cur, 1, lane, wm, wn, f1);
-    f4_mfma(acc, f0, sa[0], sb[0], 0, h);
-    w4_frags(cur, 2, lane, wm, wn, f0);
-    f4_mfma(acc, f1, sa[0], sb[0], 1, h);
-    w4_frags(cur, 3, lane, wm, wn, f1);
-    f4_mfma(acc, f0, sa[1], sb[1], 0, h);
-    f4_mfma(acc, f1, sa[1], sb[1], 1, h);
+  if (c.nsteps > 0) {   // an empty K segment leaves C = 0
+    w4_issue(c, 0, 0);
     wait_vmcnt<0>();
     __syncthreads();
-    const uint8_t* nxt = lds + ((step + 1) & 1) * W4_STAGE;
-    w4_frags(nxt, 0, lane, wm, wn, f0);
-    w4_scales(nxt, lane, wm, wn, sa, sb);
+    F4Frags f0, f1;
+    uint32_t sa[2][4], sb[2][4];
+    w4_frags(lds, 0, lane, wm, wn, f0);
+    w4_scales(lds, lane, wm, wn, sa, sb);
+
+    for (int step = 0; step < c.nsteps; ++step) {
+      const uint8_t* cur = lds + (step & 1) * W4_STAGE;
+      w4_issue(c, step + 1, (step + 1) & 1);
+      w4_frags(cur, 1, lane, wm, wn, f1);
+      f4_mfma(acc, f0, sa[0], sb[0], 0, h);
+      w4_frags(cur, 2, lane, wm, wn, f0);
+      f4_mfma(acc, f1, sa[0], sb[0], 1, h);
+      w4_frags(cur, 3, lane, wm, wn, f1);
+      f4_mfma(acc, f0, sa[1], sb[1], 0, h);
+      f4_mfma(acc, f1, sa[1], sb[1], 1, h);
+      wait_vmcnt<0>();
+      __syncthreads();
+      const uint8_t* nxt = lds + ((step + 1) & 1) * W4_STAGE;
+      w4_frags(nxt, 0, lane, wm, wn, f0);
+      w4_scales(nxt, lane, wm, wn, sa, sb);
+    }
   }
 
-  store_c<4, 4>(g.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
+  store_c<4, 4>(t.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
                 lane, acc);
 }
 
@@ -758,16 +811,15 @@ template <int FMT, bool X4>
 __global__ __launch_bounds__(kThreads) void k_gemm_mxrow(GemmLaunch g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  int tm, tn;
-  tile_order(blockIdx.x, g.total_tiles, (int)((g.PA + TM - 1) / TM), (int)((g.PB + TN - 1) / TN),
-             tm, tn);
+  const MxTile t = mx_resolve<2>(g, blockIdx.x);
+  const int tm = t.tm, tn = t.tn;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
-  const int64_t K = g.K;
+  const int64_t K = t.K;
   const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
-  const int64_t rows_a = g.PA - row0 < TM ? g.PA - row0 : TM;
-  const int64_t rows_b = g.PB - col0 < TN ? g.PB - col0 : TN;
+  const int64_t rows_a = t.a_rows - row0 < TM ? t.a_rows - row0 : TM;
+  const int64_t rows_b = t.b_rows - col0 < TN ? t.b_rows - col0 : TN;
   const uint32_t rs = (uint32_t)K;            // one byte per element
   const int64_t nkb = K / 32;
   const int sha = g.a_br == 32 ? 5 : 0, shb = g.b_br == 32 ? 5 : 0;
@@ -775,10 +827,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxrow(GemmLaunch g) {
   W4Ctx c;
   c.wave = wave;
   c.nsteps = (int)(K / K8);
-  c.ra = rsrc4(g.a_codes + row0 * rs, (uint32_t)(rows_a * rs));
-  c.rb = rsrc4(g.b_codes + col0 * rs, (uint32_t)(rows_b * rs));
-  c.rsa = rsrc4(g.a_scales, (uint32_t)(((g.PA - 1) >> sha) + 1) * (uint32_t)nkb);
-  c.rsb = rsrc4(g.b_scales, (uint32_t)(((g.PB - 1) >> shb) + 1) * (uint32_t)nkb);
+  c.ra = rsrc4(t.a_codes + row0 * rs, (uint32_t)(rows_a * rs));
+  c.rb = rsrc4(t.b_codes + col0 * rs, (uint32_t)(rows_b * rs));
+  c.rsa = rsrc4(t.a_scales, (uint32_t)(((t.a_rows - 1) >> sha) + 1) * (uint32_t)nkb);
+  c.rsb = rsrc4(t.b_scales, (uint32_t)(((t.b_rows - 1) >> shb) + 1) * (uint32_t)nkb);
   c.lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds;
   // lane i of wave load q: tile row 64 w + 8 q + i / 8, the chunk whose
   // swizzled slot is i % 8
@@ -789,8 +841,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxrow(GemmLaunch g) {
     c.code_voff[q] = (uint32_t)(wave * 64 + q * 8 + lrow) * rs + 16u * chunk;
   {
     int64_t ra = row0 + wave * 64 + lane, rb = col0 + wave * 64 + lane;
-    if (ra >= g.PA) ra = g.PA - 1;   // codes of such rows read as zero; any scale works
-    if (rb >= g.PB) rb = g.PB - 1;
+    if (ra >= t.a_rows) ra = t.a_rows - 1;   // codes of such rows read as zero; any scale works
+    if (rb >= t.b_rows) rb = t.b_rows - 1;
     c.sa_voff = (uint32_t)((ra >> sha) * nkb);
     c.sb_voff = (uint32_t)((rb >> shb) * nkb);
   }
@@ -801,25 +853,27 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxrow(GemmLaunch g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
 
-  w8_issue(c, 0, 0);
-  wait_vmcnt<0>();
-  __syncthreads();
-  F4Frags f0, f1;
-  uint32_t sa[4], sb[4];
-  w8_frags<FMT>(lds, 0, lane, wm, wn, f0);
-  w8_scales(lds, lane, wm, wn, sa, sb);
-
-  for (int step = 0; step < c.nsteps; ++step) {
-    const uint8_t* cur = lds + (step & 1) * W8_STAGE;
-    w8_issue(c, step + 1, (step + 1) & 1);
-    w8_frags<FMT>(cur, 1, lane, wm, wn, f1);
-    f8_mfma<FMT>(acc, f0, sa, sb, 0, h);
-    f8_mfma<FMT>(acc, f1, sa, sb, 1, h);
+  if (c.nsteps > 0) {   // an empty K segment leaves C = 0
+    w8_issue(c, 0, 0);
     wait_vmcnt<0>();
     __syncthreads();
-    const uint8_t* nxt = lds + ((step + 1) & 1) * W8_STAGE;
-    w8_frags<FMT>(nxt, 0, lane, wm, wn, f0);
-    w8_scales(nxt, lane, wm, wn, sa, sb);
+    F4Frags f0, f1;
+    uint32_t sa[4], sb[4];
+    w8_frags<FMT>(lds, 0, lane, wm, wn, f0);
+    w8_scales(lds, lane, wm, wn, sa, sb);
+
+    for (int step = 0; step < c.nsteps; ++step) {
+      const uint8_t* cur = lds + (step & 1) * W8_STAGE;
+      w8_issue(c, step + 1, (step + 1) & 1);
+      w8_frags<FMT>(cur, 1, lane, wm, wn, f1);
+      f8_mfma<FMT>(acc, f0, sa, sb, 0, h);
+      f8_mfma<FMT>(acc, f1, sa, sb, 1, h);
+      wait_vmcnt<0>();
+      __syncthreads();
+      const uint8_t* nxt = lds + ((step + 1) & 1) * W8_STAGE;
+      w8_frags<FMT>(nxt, 0, lane, wm, wn, f0);
+      w8_scales(nxt, lane, wm, wn, sa, sb);
+    }
   }
 
   if constexpr (X4) {   // INT4 operands entered as n / 2
@@ -828,7 +882,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxrow(GemmLaunch g) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] *= 4.0f;
   }
-  store_c<4, 4>(g.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
+  store_c<4, 4>(t.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
                 lane, acc);
 }
 
@@ -908,22 +962,40 @@ hipError_t launch_mx(const GemmLaunch& g, hipStream_t s) {
 
 }  // namespace
 
+namespace {
+
+// Every shared-dimension length of the launch (K, or each segment's length
+// when grouped along K) is a multiple of `step`.
+bool k_multiple(const GemmLaunch& g, int64_t step) {
+  if (g.mode != 2) return g.K % step == 0;
+  for (int i = 0; i < g.ngroups; ++i)
+    if ((g.off[i + 1] - g.off[i]) % step) return false;
+  return true;
+}
+
+// Block shapes, grouping and 32-bit buffer sizes the scaled-MFMA kernels
+// take (`bpe2`: code bytes per two elements of the kernel's operand rows).
+bool mx_layout_ok(const GemmLaunch& g, int64_t step, int64_t bpe2) {
+  if (g.scale_mode != 1 || g.a_bc != 32 || g.b_bc != 32) return false;
+  const bool rows_ok = (g.a_br == 1 || g.a_br == 32) && (g.b_br == 1 || g.b_br == 32);
+  if (g.mode == 0 && !rows_ok) return false;
+  if (g.mode == 1 && !(rows_ok && g.b_rows_per_group % g.b_br == 0)) return false;
+  if (g.mode == 2 && !(g.a_br == 1 && g.b_br == 1)) return false;
+  return k_multiple(g, step) && g.K * bpe2 / 2 * (int64_t)TM <= INT32_MAX &&
+         ((g.PA - 1) / g.a_br + 1) * (g.K / 32) <= INT32_MAX &&
+         ((g.PB - 1) / g.b_br + 1) * (g.K / 32) <= INT32_MAX;
+}
+
+}  // namespace
+
 bool gemm_mx_supported(const GemmLaunch& g) {
-  if (g.grid == 3)   // MXFP8: 1 x 32 blocks, byte codes
-    return g.mode == 0 && g.scale_mode == 1 && g.a_bc == 32 && g.b_bc == 32 && g.a_br == 1 &&
-           g.b_br == 1 && g.K % K8 == 0 && g.K * (int64_t)TM <= INT32_MAX &&
-           g.PA * (g.K / 32) <= INT32_MAX && g.PB * (g.K / 32) <= INT32_MAX;
-  return g.mode == 0 && g.scale_mode == 1 && g.a_bc == 32 && g.b_bc == 32 &&
-         (g.a_br == 1 || g.a_br == 32) && (g.b_br == 1 || g.b_br == 32) && g.K % KS == 0 &&
-         g.K / 2 * (int64_t)TM <= INT32_MAX;
+  if (g.grid == 3)   // MXFP8: dense, 1 x 32 blocks, byte codes
+    return g.mode == 0 && g.a_br == 1 && g.b_br == 1 && mx_layout_ok(g, K8, 2);
+  return mx_layout_ok(g, KS, 1);
 }
 
 bool gemm_mx6_supported(const GemmLaunch& g) {
-  return g.mode == 0 && (g.grid == 0 || g.grid == 1) && g.scale_mode == 1 && g.a_bc == 32 &&
-         g.b_bc == 32 && (g.a_br == 1 || g.a_br == 32) && (g.b_br == 1 || g.b_br == 32) &&
-         g.K % K8 == 0 && g.K * (int64_t)TM <= INT32_MAX &&
-         ((g.PA - 1) / g.a_br + 1) * (g.K / 32) <= INT32_MAX &&
-         ((g.PB - 1) / g.b_br + 1) * (g.K / 32) <= INT32_MAX;
+  return (g.grid == 0 || g.grid == 1) && mx_layout_ok(g, K8, 2);
 }
 
 int64_t gemm_mx6_workspace(const GemmLaunch& g) {
@@ -950,7 +1022,7 @@ hipError_t launch_gemm_mx(const GemmLaunch& g, hipStream_t s) {
     case 0: return launch_mx<0>(g, s);
     case 1: return launch_mx<1>(g, s);
     case 3: return launch_mxrow<0, false>(g, s);
-    default: return g.K % KW == 0 ? launch_mx4w(g, s) : launch_mx4(g, s);
+    default: return k_multiple(g, KW) ? launch_mx4w(g, s) : launch_mx4(g, s);
   }
 }
 

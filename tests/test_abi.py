@@ -139,7 +139,6 @@ def test_gemm_workspace_errors():
     for op in (U.UFP4_GEMM_FPROP, U.UFP4_GEMM_DGRAD, U.UFP4_GEMM_WGRAD):
         assert wb(op, ctypes.byref(a), ctypes.byref(b), 0) == need
     assert wb(3, ctypes.byref(a), ctypes.byref(b), 0) == 0
-    assert wb(0, ctypes.byref(a), ctypes.byref(b), 2) == 0          # grouped: none yet
     e2m1 = pow2.copy(grid=U.UFP4_E2M1)
     assert wb(0, ctypes.byref(_qt(300, 256, e2m1)), ctypes.byref(_qt(64, 256, e2m1)), 0) == 0
     assert wb(0, ctypes.byref(_qt(300, 160, pow2)), ctypes.byref(_qt(64, 160, pow2)), 0) == 0
@@ -157,6 +156,16 @@ def test_gemm_workspace_errors():
     assert f(0, *ab, 0, None, C, 63, ctypes.c_void_p(FAKE), need, None) == U.UFP4_ERR_INVALID_ARG
     assert f(0, ctypes.byref(a), ctypes.byref(_qt(64, 128, pow2)), 0, None, C, 64,
              ctypes.c_void_p(FAKE), need, None) == U.UFP4_ERR_MISMATCH
+    # grouped WGRAD with E8M0 blocks: segments must be multiples of 128
+    seg = (ctypes.c_int64 * 3)(0, 96, 256)
+    g = lib.ufp4_gemm_wgrad_grouped
+    assert g(*ab, 2, seg, C, 256, None) == U.UFP4_ERR_UNSUPPORTED
+    assert f(2, *ab, 2, seg, C, 256, ctypes.c_void_p(FAKE), need, None) == U.UFP4_ERR_UNSUPPORTED
+    assert wb(2, ctypes.byref(a), ctypes.byref(b), 2) == need
+    sq = U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 32, 32, 1)   # 32 x 32 blocks
+    assert wb(0, ctypes.byref(_qt(320, 256, sq)), ctypes.byref(_qt(96, 256, sq)), 4) == 0   # 24-row groups
+    assert wb(0, ctypes.byref(_qt(320, 256, sq)), ctypes.byref(_qt(128, 256, sq)), 4) > 0
+    assert wb(0, ctypes.byref(a), ctypes.byref(_qt(128, 256, pow2)), 4) == need - 64 * 256 + 128 * 256
     # empty operands: nothing to do, the workspace is not touched
     assert f(0, ctypes.byref(_qt(0, 256, pow2)), ctypes.byref(b), 0, None, C, 64,
              ctypes.c_void_p(FAKE), 1, None) == U.UFP4_OK

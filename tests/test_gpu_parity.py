@@ -688,12 +688,16 @@ def test_grouped_gemms_pow2(grid, br):
     tx, tw, tdy = rand_bits(T, H, 51), rand_bits(G * F, H, 52), rand_bits(T, F, 53)
     qx, rx = compare_quant(tx, 0, cx, with_rotated=False)
     qw, rw = compare_quant(tw, 0, cx, with_rotated=False)
-    Y = U.ufp4_gemm_fprop_grouped(qx, qw, off).cpu().numpy()
     dxq, dwq = oracle_dequant64(rx, cx), oracle_dequant64(rw, cx)
-    for g in range(G):
-        if off[g + 1] > off[g]:
-            ref = O.gemm_ref(dxq[off[g]:off[g + 1]], dwq[g * F:(g + 1) * F])
-            assert O.rel_fro(Y[off[g]:off[g + 1]], ref) <= GEMM_TOL, ("fprop", g)
+    for ws in (False, True):   # scaled matrix cores; FP6 operands through a workspace
+        Y = (U.ufp4_gemm_ws(U.UFP4_GEMM_FPROP, qx, qw, offsets=off) if ws
+             else U.ufp4_gemm_fprop_grouped(qx, qw, off)).cpu().numpy()
+        for g in range(G):
+            if off[g + 1] > off[g]:
+                ref = O.gemm_ref(dxq[off[g]:off[g + 1]], dwq[g * F:(g + 1) * F])
+                assert O.rel_fro(Y[off[g]:off[g + 1]], ref) <= GEMM_TOL, ("fprop", ws, g)
+    need = U.ufp4_gemm_workspace_bytes(U.UFP4_GEMM_FPROP, qx, qw, G)
+    assert need == (0 if grid == U.UFP4_E2M1 else (T * H + 255) // 256 * 256 + G * F * H)
     # DGRAD: B = W^T of every expert.  1 x 32: per-expert column-wise
     # quantization (segmented); 32 x 32: each expert's W quantized once and
     # reused transposed (S(B) = S(B^T)), stacked.
@@ -716,12 +720,54 @@ def test_grouped_gemms_pow2(grid, br):
         rwe = O.quantize(tw, 0, spec_of(cwt))
         dwe = oracle_dequant64(rwe, cwt)
         dwt = [np.ascontiguousarray(dwe[g * F:(g + 1) * F].T) for g in range(G)]
-    dX = U.ufp4_gemm_dgrad_grouped(qdy, qwt, off).cpu().numpy()
     ddy = oracle_dequant64(rdy, cd.copy(sign_seed=46))
-    for g in range(G):
-        if off[g + 1] > off[g]:
-            ref = O.gemm_ref(ddy[off[g]:off[g + 1]], dwt[g])
-            assert O.rel_fro(dX[off[g]:off[g + 1]], ref) <= GEMM_TOL, ("dgrad", g)
+    for ws in (False, True):
+        dX = (U.ufp4_gemm_ws(U.UFP4_GEMM_DGRAD, qdy, qwt, offsets=off) if ws
+              else U.ufp4_gemm_dgrad_grouped(qdy, qwt, off)).cpu().numpy()
+        for g in range(G):
+            if off[g + 1] > off[g]:
+                ref = O.gemm_ref(ddy[off[g]:off[g + 1]], dwt[g])
+                assert O.rel_fro(dX[off[g]:off[g + 1]], ref) <= GEMM_TOL, ("dgrad", ws, g)
+
+
+@pytest.mark.parametrize("grid", GRIDS)
+def test_grouped_wgrad_pow2(grid):
+    """Grouped WGRAD with 1 x 32 E8M0 blocks on the scaled matrix cores: four
+    token segments (one empty) of the segmented column-wise quantizations of
+    dY and X, plain and through the workspace; segment lengths that are not
+    multiples of 128 are refused (UFP4_ERR_UNSUPPORTED)."""
+    _print_case("grouped wgrad pow2", grid)
+    G, H, F = 4, 288, 160
+    off = [0, 128, 128, 384, 640]
+    T = off[-1]
+    cdt = U.make_cfg(grid, U.UFP4_SR, U.UFP4_SCALE_POW2, 1, 32, 32, sign_seed=61, sr_seed=3, sr_stream=1)
+    cxt = U.make_cfg(grid, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 32, sign_seed=61)
+    tdy, tx = rand_bits(T, F, 62), rand_bits(T, H, 63)
+    qdyt = U.ufp4_rht_quant_segmented(dev_bf16(tdy), off, cdt)
+    qxt = U.ufp4_rht_quant_segmented(dev_bf16(tx), off, cxt)
+    r_dyt = O.quantize_segmented(tdy, off, spec_of(cdt))
+    r_xt = O.quantize_segmented(tx, off, spec_of(cxt))
+    assert np.array_equal(qdyt.codes.cpu().numpy(), np.concatenate([r["codes"].ravel() for r in r_dyt]))
+    assert np.array_equal(qdyt.scales.cpu().numpy(), np.concatenate([r["scales"].ravel() for r in r_dyt]))
+    for ws in (False, True):
+        dW = torch.full((G * F, H), 7.0, dtype=torch.float32, device="cuda")
+        if ws:
+            U.ufp4_gemm_ws(U.UFP4_GEMM_WGRAD, qdyt, qxt, offsets=off, out=dW)
+        else:
+            U.ufp4_gemm_wgrad_grouped(qdyt, qxt, off, out=dW)
+        dW = dW.cpu().numpy()
+        for g in range(G):
+            if off[g + 1] == off[g]:
+                assert np.all(dW[g * F:(g + 1) * F] == 0), ("empty", ws)
+                continue
+            ref = O.gemm_ref(oracle_dequant64(r_dyt[g], cdt), oracle_dequant64(r_xt[g], cxt))
+            assert O.rel_fro(dW[g * F:(g + 1) * F], ref) <= GEMM_TOL, ("wgrad", ws, g)
+    off2 = [0, 96, 96, 384, 640]
+    qdy2 = U.ufp4_rht_quant_segmented(dev_bf16(tdy), off2, cdt)
+    qx2 = U.ufp4_rht_quant_segmented(dev_bf16(tx), off2, cxt)
+    with pytest.raises(U.UFP4Error) as e:
+        U.ufp4_gemm_wgrad_grouped(qdy2, qx2, off2)
+    assert e.value.status == U.UFP4_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("grid", GRIDS)
