@@ -16,7 +16,9 @@ from typing import Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "librht_ufp4.so")
+# UFP4_LIBRARY names another build of the same library (the sanitizer build
+# of rht_bit_block_amd.build for CPU runs of the ABI tests).
+LIB_PATH = os.environ.get("UFP4_LIBRARY") or os.path.join(_HERE, "librht_ufp4.so")
 
 UFP4_E1M2, UFP4_INT4, UFP4_E2M1, UFP4_E4M3 = 0, 1, 2, 3
 UFP4_RTNE, UFP4_SR = 0, 1

@@ -1,7 +1,18 @@
-"""Build librht_ufp4.so (HIP kernels + C ABI) in-tree for gfx950.
+r"""Build librht_ufp4.so (HIP kernels + C ABI) in-tree for gfx950.
 
 Run as `python -m rht_bit_block_amd.build` or through __graft_entry__.build().
 Objects are compiled in parallel; the library is written next to this file.
+
+`python -m rht_bit_block_amd.build --sanitize` builds a second library,
+_build/sanitize/librht_ufp4.so, whose host code (argument validation, launch
+set-up) is instrumented with AddressSanitizer and UndefinedBehaviorSanitizer
+(device code unchanged).  It is for CPU runs of the ABI tests only, with the
+compiler's own sanitizer runtime preloaded (it carries the UBSan handlers too)
+and Python's small-object allocator off (so host arrays get redzones):
+  PYTHONMALLOC=malloc UFP4_LIBRARY=_build/sanitize/librht_ufp4.so \
+  LD_PRELOAD=$(/opt/rocm/llvm/bin/clang -print-file-name=libclang_rt.asan-x86_64.so) \
+  ASAN_OPTIONS=detect_leaks=0:halt_on_error=1 UBSAN_OPTIONS=halt_on_error=1 \
+  python -m pytest tests/test_abi.py tests/test_binding_checks.py
 """
 import os
 import subprocess
@@ -36,29 +47,38 @@ def _hipcc():
     return "hipcc"
 
 
-def _compile(src):
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side sanitizers only: each flag goes to the host compilation.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def _compile(src, out_dir=BUILD_DIR, extra=()):
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    cmd = [_hipcc(), *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-6000:]}")
     return obj
 
 
-def build(verbose=True):
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose=True, sanitize=False):
+    out_dir = os.path.join(BUILD_DIR, "sanitize") if sanitize else BUILD_DIR
+    lib_path = os.path.join(out_dir, LIB_NAME) if sanitize else LIB_PATH
+    extra = SANITIZE if sanitize else ()
+    os.makedirs(out_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, out_dir, extra), SOURCES))
+    tmp = lib_path + ".tmp"
+    # a sanitized shared library leaves the runtime to the process (preloaded)
     cmd = [_hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr[-4000:])
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
     if verbose:
-        print("built", LIB_PATH, file=sys.stderr)
-    return LIB_PATH
+        print("built", lib_path, file=sys.stderr)
+    return lib_path
 
 
 if __name__ == "__main__":
-    build()
+    build(sanitize="--sanitize" in sys.argv[1:])
