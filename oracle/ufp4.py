@@ -79,6 +79,7 @@ class QuantSpec:
     sign_seed: int = 0
     sr_seed: int = 0
     sr_stream: int = 0
+    tensor_scale: float = 0.0   # two-level scaling (power-of-two blocks only); 0: none
 
 
 # ---------------------------------------------------------------------------
@@ -372,10 +373,21 @@ def quantize(t_bits, along, spec, elem_base=0, row_index=None, col_index=None, K
             v = (y / np.where(s_full == 0, np.float32(1), s_full)).astype(np.float32)
         v = np.where(s_full == 0, np.float32(0), v)
     else:
+        # Two-level scaling ([UFP4] Method: the scaling hierarchy -- single,
+        # two-level or block -- is orthogonal to the format).  READING: a
+        # per-tensor fp32 factor s_T > 0 over the power-of-two block scales:
+        # the rotated values are first multiplied by m_T = RN_fp32(1 / s_T),
+        # u = RN_fp32(y * m_T), and u is quantized with power-of-two block
+        # scales as above; an element stands for level * 2^e * s_T.
+        u = y
+        if spec.tensor_scale:
+            m_t = np.float32(1.0) / np.float32(spec.tensor_scale)
+            u = (y.astype(np.float64) * np.float64(m_t)).astype(np.float32)
+            M = block_absmax(u, br, bc)
         e_blk = scale_pow2_exponent(M, grid)
         scales = (e_blk + 127).astype(np.uint8)
         s_full = _expand(np.exp2(e_blk.astype(np.float64)).astype(np.float32), br, bc)
-        v = (y / s_full).astype(np.float32)      # power-of-two divisor
+        v = (u / s_full).astype(np.float32)      # power-of-two divisor
     v = np.minimum(np.maximum(v, -qmax), qmax)
 
     m = np.abs(v).astype(np.float64)
@@ -446,7 +458,10 @@ def scale_per_element(scales, spec, P, K):
         s = np.asarray(scales, dtype=np.float32).reshape(P // br, K // bc)
         return _expand(s, br, bc).astype(np.float64)
     e = np.asarray(scales, dtype=np.int64).reshape(P // br, K // bc) - 127
-    return _expand(np.exp2(e.astype(np.float64)), br, bc)
+    s = _expand(np.exp2(e.astype(np.float64)), br, bc)
+    if spec.tensor_scale:                        # two-level: 2^e * s_T, exact in float64
+        s = s * np.float64(np.float32(spec.tensor_scale))
+    return s
 
 
 def dequant(codes_packed, scales, spec, P, K):

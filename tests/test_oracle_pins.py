@@ -634,3 +634,59 @@ def test_mxfp8_lossless_on_grid():
     q = O.quantize(bits, 0, spec)
     assert np.all(q["scales"] == 127)
     assert np.array_equal(O.dequant(q["codes"], q["scales"], spec, 16, 64)[1], y.astype(np.float64))
+
+
+# ---------------------------------------------------------------------------
+# Two-level scaling ([UFP4] Method: the scaling hierarchy -- single-level,
+# two-level or block -- is orthogonal to the format): a per-tensor fp32
+# factor s_T over power-of-two block scales, an element standing for
+# level * 2^e * s_T.
+# ---------------------------------------------------------------------------
+TWO_LEVEL_CASES = [(O.E1M2, 1, 32), (O.INT4, 1, 32), (O.E2M1, 32, 32), (O.E4M3, 1, 32)]
+
+
+@pytest.mark.parametrize("grid,br,bc", TWO_LEVEL_CASES)
+@pytest.mark.parametrize("j", [-3, 5])
+def test_two_level_power_of_two_factor_shifts_exponents(grid, br, bc, j):
+    """s_T = 2^j only moves every block exponent by -j: the codes and the
+    dequantized values equal the single-level ones (a factor applied the
+    wrong way round, or left out of the dequantization, changes them)."""
+    t = _tensor_bits(64, 128, 21 + grid)
+    n = 1 if br > 1 else 32
+    one = O.QuantSpec(grid, O.RTNE, O.SCALE_POW2, br, bc, n, 3)
+    two = O.QuantSpec(grid, O.RTNE, O.SCALE_POW2, br, bc, n, 3, tensor_scale=float(2.0 ** j))
+    q1, q2 = O.quantize(t, 0, one), O.quantize(t, 0, two)
+    assert np.array_equal(q1["codes"], q2["codes"])
+    assert np.array_equal(q2["scales"].astype(np.int64), q1["scales"].astype(np.int64) - j)
+    d1 = O.dequant(q1["codes"], q1["scales"], one, 64, 128)[1]
+    d2 = O.dequant(q2["codes"], q2["scales"], two, 64, 128)[1]
+    assert np.array_equal(d1, d2)
+    unit = O.QuantSpec(grid, O.RTNE, O.SCALE_POW2, br, bc, n, 3, tensor_scale=1.0)
+    qu = O.quantize(t, 0, unit)
+    assert np.array_equal(qu["codes"], q1["codes"]) and np.array_equal(qu["scales"], q1["scales"])
+
+
+@pytest.mark.parametrize("grid,br,bc", TWO_LEVEL_CASES)
+@pytest.mark.parametrize("s_t", [0.7, 1.3, 3.0e-3])
+def test_two_level_block_scale_brackets_and_error(grid, br, bc, s_t):
+    """For any s_T the block scale is the least power-of-two multiple of s_T
+    whose q_max multiple covers the block (up to the fp32 rounding of the
+    normalization, 2^-23 relative), and every RTNE-dequantized element lies
+    within half the widest level gap times that scale of its rotated value."""
+    t = _tensor_bits(64, 128, 31 + grid)
+    n = 1 if br > 1 else 32
+    spec = O.QuantSpec(grid, O.RTNE, O.SCALE_POW2, br, bc, n, 9, tensor_scale=s_t)
+    q = O.quantize(t, 0, spec)
+    st = float(np.float32(s_t))
+    d = O.dequant(q["codes"], q["scales"], spec, 64, 128)[1]
+    s = O.scale_per_element(q["scales"], spec, 64, 128)          # 2^e * s_T
+    y = q["rotated"].astype(np.float64)
+    M = O.block_absmax(y.astype(np.float32), br, bc).astype(np.float64)
+    S = s.reshape(64 // br, br, 128 // bc, bc)[:, 0, :, 0]
+    qmax = O.QMAX[grid]
+    tol = 2.0 ** -22
+    assert np.all(M <= qmax * S * (1 + tol))                    # the scale covers the block
+    assert np.all(qmax * S / 2 < M * (1 + tol))                 # and no smaller one would
+    gap = np.max(np.diff(O.LEVELS[grid]))
+    assert np.all(np.abs(d - y) <= 0.5 * gap * s * (1 + tol) + 1e-30)
+    assert np.allclose(s / st, np.exp2(np.round(np.log2(s / st))), rtol=0, atol=0)
