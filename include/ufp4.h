@@ -87,7 +87,16 @@ enum {
  *               Both operands of a GEMM must use the same sign_seed and rht_n.
  *   sr_seed, sr_stream : key and stream of the stochastic-rounding draws;
  *               stream 0xFFFFFFFF is reserved.
- *   reserved  : must be 0. */
+ *   tensor_scale : 0 for single-level scaling, or (power-of-two scales only)
+ *               a per-tensor fp32 factor s_T > 0, finite and normal, over
+ *               the block scales -- two-level scaling ([UFP4] Method: the
+ *               scaling hierarchy is orthogonal to the format).  The rotated
+ *               values are multiplied by m_T = RN_fp32(1 / s_T) before the
+ *               block exponents are chosen, and an element then stands for
+ *               level * 2^e * s_T (dequantization and the GEMMs apply s_T;
+ *               the E8M0 bytes are stored as without it).  Anything else is
+ *               UFP4_ERR_INVALID_ARG, a nonzero s_T with fp32 scales
+ *               UFP4_ERR_UNSUPPORTED. */
 typedef struct ufp4_quant_cfg {
   int32_t grid;
   int32_t rounding;
@@ -98,7 +107,7 @@ typedef struct ufp4_quant_cfg {
   uint64_t sign_seed;
   uint64_t sr_seed;
   uint32_t sr_stream;
-  uint32_t reserved;
+  float tensor_scale;
 } ufp4_quant_cfg;
 
 /* A quantized logical operand (device codes and scales, layout above). */

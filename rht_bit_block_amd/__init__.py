@@ -51,7 +51,7 @@ class QuantCfg(ctypes.Structure):
                 ("scale_mode", ctypes.c_int32), ("block_rows", ctypes.c_int32),
                 ("block_cols", ctypes.c_int32), ("rht_n", ctypes.c_int32),
                 ("sign_seed", ctypes.c_uint64), ("sr_seed", ctypes.c_uint64),
-                ("sr_stream", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+                ("sr_stream", ctypes.c_uint32), ("tensor_scale", ctypes.c_float)]
 
     def copy(self, **kw):
         c = QuantCfg()
@@ -62,9 +62,11 @@ class QuantCfg(ctypes.Structure):
 
 
 def make_cfg(grid=UFP4_E1M2, rounding=UFP4_RTNE, scale_mode=UFP4_SCALE_F32, block_rows=1,
-             block_cols=16, rht_n=16, sign_seed=0, sr_seed=0, sr_stream=0):
+             block_cols=16, rht_n=16, sign_seed=0, sr_seed=0, sr_stream=0, tensor_scale=0.0):
+    """tensor_scale: 0 (single-level) or the per-tensor fp32 factor of
+    two-level scaling over power-of-two block scales."""
     return QuantCfg(int(grid), int(rounding), int(scale_mode), int(block_rows), int(block_cols),
-                    int(rht_n), int(sign_seed), int(sr_seed), int(sr_stream), 0)
+                    int(rht_n), int(sign_seed), int(sr_seed), int(sr_stream), float(tensor_scale))
 
 
 class QTensorC(ctypes.Structure):

@@ -24,8 +24,12 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 int check_cfg(const ufp4_quant_cfg* c) {
   if (!c) return UFP4_ERR_INVALID_ARG;
   if (c->grid < 0 || c->grid > 3 || c->rounding < 0 || c->rounding > 1 || c->scale_mode < 0 ||
-      c->scale_mode > 1 || c->reserved != 0)
+      c->scale_mode > 1)
     return UFP4_ERR_INVALID_ARG;
+  // two-level scaling: a positive, finite, normal per-tensor factor
+  if (c->tensor_scale != 0.0f && !(std::isnormal(c->tensor_scale) && c->tensor_scale > 0.0f))
+    return UFP4_ERR_INVALID_ARG;
+  if (c->tensor_scale != 0.0f && c->scale_mode != UFP4_SCALE_POW2) return UFP4_ERR_UNSUPPORTED;
   if (!is_pow2(c->rht_n) || c->rht_n > 128) return UFP4_ERR_SHAPE;
   if (c->sr_stream == kSignStream) return UFP4_ERR_UNSUPPORTED;
   const bool one_d = c->block_rows == 1 && (c->block_cols == 16 || c->block_cols == 32);
@@ -65,6 +69,15 @@ void sign_patterns(const ufp4_quant_cfg* c, int W, uint32_t out[4]) {
   }
 }
 
+// Two-level scaling: the multiplier m_T = RN_fp32(1 / s_T) of the rotated
+// values (IEEE fp32 division), 1 for single-level scaling.
+float tensor_mul(const ufp4_quant_cfg* c) {
+  return c->tensor_scale != 0.0f ? 1.0f / c->tensor_scale : 1.0f;
+}
+
+// Factor on a GEMM's output: the product of the operands' tensor factors.
+float tensor_factor(const ufp4_quant_cfg& c) { return c.tensor_scale != 0.0f ? c.tensor_scale : 1.0f; }
+
 void fill_common(QuantLaunch& q, const void* x, int64_t rows, int64_t cols, int64_t ld,
                  const ufp4_quant_cfg* c, uint8_t* codes, void* scales, float* rotated) {
   std::memset(&q, 0, sizeof(q));
@@ -86,6 +99,7 @@ void fill_common(QuantLaunch& q, const void* x, int64_t rows, int64_t cols, int6
   q.bc = c->block_cols;
   q.sr_seed = c->sr_seed;
   q.sr_stream = c->sr_stream;
+  q.tmul = tensor_mul(c);
   sign_patterns(c, c->block_rows == 32 ? 32 : lane_width(c->rht_n, c->block_cols), q.sign_pat);
 }
 
@@ -134,6 +148,7 @@ void fill_gemm(GemmLaunch& g, const ufp4_qtensor* a, const ufp4_qtensor* b, floa
   g.PA = a->P;
   g.PB = b->P;
   g.K = a->K;
+  g.c_mul = tensor_factor(a->cfg) * tensor_factor(b->cfg);   // two-level: s_TA * s_TB
 }
 
 constexpr int64_t kTile = 256;
@@ -449,6 +464,7 @@ int ufp4_rht_quant_dual(const void* x, int64_t rows, int64_t cols, int64_t ld,
   r.cn = q.cn;
   r.sr_seed = cfg_row->sr_seed;
   r.sr_stream = cfg_row->sr_stream;
+  r.tmul = tensor_mul(cfg_row);
   sign_patterns(cfg_row, lane_width(cfg_row->rht_n, cfg_row->block_cols), r.sign_pat);
   return hip_status(launch_quant_dual(q, r, (hipStream_t)stream));
 }
@@ -499,8 +515,8 @@ int ufp4_dequant(const ufp4_qtensor* q, float* out, int64_t ldo, void* stream) {
   if (!out) return UFP4_ERR_INVALID_ARG;
   if (!aligned(q->codes, q->cfg.grid == UFP4_E4M3 ? 8 : 4)) return UFP4_ERR_INVALID_ARG;
   return hip_status(launch_dequant(q->codes, q->scales, q->P, q->K, q->cfg.grid,
-                                   q->cfg.scale_mode, q->cfg.block_rows, q->cfg.block_cols, out,
-                                   ldo, (hipStream_t)stream));
+                                   q->cfg.scale_mode, q->cfg.block_rows, q->cfg.block_cols,
+                                   tensor_factor(q->cfg), out, ldo, (hipStream_t)stream));
 }
 
 int ufp4_gemm_fprop(const ufp4_qtensor* X, const ufp4_qtensor* W, float* Y, int64_t ldy,

@@ -366,6 +366,7 @@ __global__ __launch_bounds__(kThreads8) void k_gemm8(GemmLaunch g) {
     const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
     const int rv = (int)(pr.a_rows - row0 < TM ? pr.a_rows - row0 : TM);
     const int cv = (int)(pr.b_rows - col0 < TN ? pr.b_rows - col0 : TN);
+    scale_acc<4, 2>(acc, g.c_mul);
     store_c<4, 2>(pr.c + row0 * g.ldc + col0, g.ldc, rv, cv, wm * 128, wn * 64, lane, acc);
   }
 }

@@ -106,6 +106,17 @@ __device__ __forceinline__ void store_c_plain(float* c_tile, int64_t ldc, int ro
   }
 }
 
+// C times a factor m (two-level scaling: the operands' tensor factors; 1 for
+// single-level scaling, which skips the multiply: the branch is uniform).
+template <int NI, int NJ>
+__device__ __forceinline__ void scale_acc(c_floatx16 (&acc)[NI][NJ], float m) {
+  if (m == 1.0f) return;
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] *= m;
+}
+
 template <int NI, int NJ>
 __device__ __forceinline__ void store_c(float* c_tile, int64_t ldc, int rows_valid,
                                         int cols_valid, int r0, int c0, int lane,

@@ -44,7 +44,7 @@
 //   k_gemm_mx4 (E2M1, K % 128 == 0): K step 128, the same copy with 4 stages.
 //   k_gemm_mx<GRID> (E1M2, INT4): K step 128; codes are loaded into registers
 //     two steps ahead, converted to E4M3 and written to LDS (two stages).
-//   k_gemm_mxrow<FMT, X4> (one byte per element per row, copied HBM -> LDS
+//   k_gemm_mxrow<FMT> (one byte per element per row, copied HBM -> LDS
 //     untouched, K step 128): FMT 0 = MXFP8 E4M3 codes; FMT 2 = E1M2 / INT4
 //     levels as FP6 E2M3 operands, written beforehand by k_fp6_expand into a
 //     caller workspace (32-byte slot per 32-element block: 24 bytes of 6-bit
@@ -357,6 +357,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(GemmLaunch g) {
     if (step < c.nsteps) body(step, y, x);
   }
 
+  scale_acc<4, 4>(acc, g.c_mul);
   store_c<4, 4>(t.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
                 lane, acc);
 }
@@ -566,6 +567,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx4(GemmLaunch g) {
     wait_vmcnt<0>();   // drain the clamped prefetches before the workgroup ends
   }
 
+  scale_acc<4, 4>(acc, g.c_mul);
   store_c<4, 4>(t.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
                 lane, acc);
 }
@@ -715,6 +717,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx4w(GemmLaunch g) {
     }
   }
 
+  scale_acc<4, 4>(acc, g.c_mul);
   store_c<4, 4>(t.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
                 lane, acc);
 }
@@ -807,7 +810,7 @@ __device__ __forceinline__ void f8_mfma(floatx16 (&acc)[4][4], const F4Frags& f,
                                                                   FMT, 0, xa[i], 0, xb[j]);
 }
 
-template <int FMT, bool X4>
+template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_gemm_mxrow(GemmLaunch g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
@@ -876,12 +879,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxrow(GemmLaunch g) {
     }
   }
 
-  if constexpr (X4) {   // INT4 operands entered as n / 2
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] *= 4.0f;
-  }
+  scale_acc<4, 4>(acc, g.c_mul);
   store_c<4, 4>(t.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
                 lane, acc);
 }
@@ -920,13 +918,13 @@ __global__ __launch_bounds__(256) void k_fp6_expand(const uint8_t* __restrict__ 
   }
 }
 
-template <int FMT, bool X4>
+template <int FMT>
 hipError_t launch_mxrow(const GemmLaunch& g, hipStream_t s) {
   constexpr int bytes = 2 * W8_STAGE;
   static std::atomic<uint64_t> lds_set{0};
-  const hipError_t e = set_lds_limit((const void*)k_gemm_mxrow<FMT, X4>, bytes, lds_set);
+  const hipError_t e = set_lds_limit((const void*)k_gemm_mxrow<FMT>, bytes, lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gemm_mxrow<FMT, X4>), dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
+  hipLaunchKernelGGL((k_gemm_mxrow<FMT>), dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
   return hipGetLastError();
 }
 
@@ -1013,7 +1011,8 @@ hipError_t launch_gemm_mx6(const GemmLaunch& g, uint8_t* ws, hipStream_t s) {
   e = g.grid == 0 ? launch_fp6_expand<0>(g.b_codes, const_cast<uint8_t*>(x.b_codes), g.PB, g.K, s)
                   : launch_fp6_expand<1>(g.b_codes, const_cast<uint8_t*>(x.b_codes), g.PB, g.K, s);
   if (e != hipSuccess) return e;
-  return g.grid == 0 ? launch_mxrow<2, false>(x, s) : launch_mxrow<2, true>(x, s);
+  if (g.grid == 1) x.c_mul = g.c_mul * 4.0f;   // INT4 operands entered as n / 2 (exact)
+  return launch_mxrow<2>(x, s);
 }
 
 hipError_t launch_gemm_mx(const GemmLaunch& g, hipStream_t s) {
@@ -1021,7 +1020,7 @@ hipError_t launch_gemm_mx(const GemmLaunch& g, hipStream_t s) {
   switch (g.grid) {
     case 0: return launch_mx<0>(g, s);
     case 1: return launch_mx<1>(g, s);
-    case 3: return launch_mxrow<0, false>(g, s);
+    case 3: return launch_mxrow<0>(g, s);
     default: return k_multiple(g, KW) ? launch_mx4w(g, s) : launch_mx4(g, s);
   }
 }

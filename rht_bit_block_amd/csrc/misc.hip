@@ -33,7 +33,7 @@ __device__ __forceinline__ float level_of(uint32_t c, int grid) {
 
 // out[p][k] = RN(level(code) * s) -- one thread per 8 elements.
 __global__ void k_dequant(const uint8_t* codes, const void* scales, int64_t P, int64_t K,
-                          int grid, int smode, int br, int bc, float* out, int64_t ldo) {
+                          int grid, int smode, int br, int bc, float ts, float* out, int64_t ldo) {
   const int64_t n8 = P * (K / 8);
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8;
        i += (int64_t)gridDim.x * blockDim.x) {
@@ -53,7 +53,9 @@ __global__ void k_dequant(const uint8_t* codes, const void* scales, int64_t P, i
         const uint8_t e = reinterpret_cast<const uint8_t*>(scales)[(p / br) * (K / bc) + k / bc];
         s = ldexpf(1.0f, (int)e - 127);
       }
-      out[p * ldo + k] = __fmul_rn(level_of(c, grid), s);
+      // level * 2^e is exact, so with two-level scaling one rounding of
+      // level * 2^e * s_T (ts = 1 otherwise: exact)
+      out[p * ldo + k] = __fmul_rn(__fmul_rn(level_of(c, grid), s), ts);
     }
   }
 }
@@ -198,12 +200,12 @@ int grid_for(int64_t work, int threads) {
 }  // namespace
 
 hipError_t launch_dequant(const uint8_t* codes, const void* scales, int64_t P, int64_t K,
-                          int32_t grid, int32_t smode, int32_t br, int32_t bc, float* out,
-                          int64_t ldo, hipStream_t s) {
+                          int32_t grid, int32_t smode, int32_t br, int32_t bc, float ts,
+                          float* out, int64_t ldo, hipStream_t s) {
   const int64_t n8 = P * (K / 8);
   if (n8 == 0) return hipSuccess;
   hipLaunchKernelGGL(k_dequant, dim3(grid_for(n8, 256)), dim3(256), 0, s, codes, scales, P, K,
-                     (int)grid, (int)smode, (int)br, (int)bc, out, ldo);
+                     (int)grid, (int)smode, (int)br, (int)bc, ts, out, ldo);
   return hipGetLastError();
 }
 

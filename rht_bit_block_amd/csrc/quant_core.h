@@ -295,7 +295,8 @@ __device__ __forceinline__ uint8_t* code_ptr(uint8_t* base, uint64_t e0) {
 // Quantize the W values of one lane whose blocks are 1 x B; writes codes
 // (W/2 bytes) and W/B scales.  RND bit 0: stochastic rounding; RND bit 1:
 // power-of-two scales stored as E8M0 bytes (1 x 32 blocks), else fp32
-// absmax scales.  FOLD (fp32 scales only): y holds the
+// absmax scales.  With power-of-two scales c is the two-level multiplier
+// m_T = RN(1 / s_T) (1 for single-level scaling).  FOLD (fp32 scales only): y holds the
 // unnormalized transform x, the rotated values are c * x with c a power of
 // two, and RN(c x / s_c) = RN(x / s_x), s_c = c s_x whenever nothing
 // underflows; blocks with c * absmax < 2^-100 redo the literal computation.
@@ -358,10 +359,13 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
     for (int j = 0; j < B; ++j) M = fmaxf(M, fabsf(y[blk * B + j]));
     float v[B];
     if constexpr (POW2) {
+      // two-level scaling: c = m_T, the values are u = RN(y m_T) and
+      // max |u| = RN(M m_T) since rounding is monotone (m_T = 1: unchanged)
+      M = __fmul_rn(M, c);
       const int e = pow2_exponent<GRID>(M);
       const float inv = ldexpf(1.0f, -e);   // exact power of two
 #pragma unroll
-      for (int j = 0; j < B; ++j) v[j] = __fmul_rn(y[blk * B + j], inv);
+      for (int j = 0; j < B; ++j) v[j] = __fmul_rn(__fmul_rn(y[blk * B + j], c), inv);
       if (e == 127) {   // only there can |v| exceed qmax
 #pragma unroll
         for (int j = 0; j < B; ++j) v[j] = fminf(fmaxf(v[j], -qmax), qmax);
@@ -489,7 +493,8 @@ __device__ __forceinline__ void finish_lane(float (&y)[W], const Q& q, uint64_t 
   }
   if constexpr (N > 1) scale_by<W>(y, q.cn);
   if (q.rotated) store_rotated<W>(q.rotated + e0, y);
-  quantize_1d<W, B, GRID, RND, false>(y, 1.0f, e0, q.sr_seed, q.sr_stream, codes_out, scales_out);
+  quantize_1d<W, B, GRID, RND, false>(y, q.tmul, e0, q.sr_seed, q.sr_stream, codes_out,
+                                      scales_out);
 }
 
 // Address of scale number i of a 1D quantization (fp32 or E8M0 byte).
@@ -588,7 +593,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_diag(QuantLaunch q, FastDiv 
                                                nullptr, nullptr, &d);
     } else {
       if constexpr (N > 1) scale_by<W>(y, q.cn);
-      quantize_1d<W, B, GRID, RND, false, true>(y, 1.0f, e0, q.sr_seed, q.sr_stream, nullptr,
+      quantize_1d<W, B, GRID, RND, false, true>(y, q.tmul, e0, q.sr_seed, q.sr_stream, nullptr,
                                                 nullptr, &d);
     }
   }
@@ -975,6 +980,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows_2d(QuantLaunch q, uint3
 #pragma unroll
     for (int m = 1; m < 32; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
     if (!valid) continue;
+    M = __fmul_rn(M, q.tmul);            // two-level: max |RN(y m_T)| = RN(M m_T)
     const int e = pow2_exponent<GRID>(M);
     const float inv = ldexpf(1.0f, -e);  // exact power of two (2^-127 is a subnormal)
     const uint64_t e0 = (uint64_t)p * K + k0;
@@ -985,7 +991,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows_2d(QuantLaunch q, uint3
 #pragma unroll
     for (int j = 0; j < W; ++j) {
       // power-of-two scale: |v| <= qmax exactly unless e hit its clamp at 127
-      float v = __fmul_rn(y[j], inv);
+      float v = __fmul_rn(__fmul_rn(y[j], q.tmul), inv);
       if (e == 127) v = fminf(fmaxf(v, -qmax), qmax);
       uint32_t word;
       if constexpr (RND == 0) {

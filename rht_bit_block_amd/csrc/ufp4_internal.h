@@ -90,6 +90,7 @@ struct QuantLaunch {
   int32_t grid, rounding, scale_mode, br, bc;
   uint64_t sr_seed;
   uint32_t sr_stream;
+  float tmul;            // two-level scaling: RN(1 / s_T); 1 for single-level
   // segmented column-wise
   int32_t nseg;
   int64_t seg_off[kMaxSegments + 1];
@@ -110,6 +111,7 @@ struct RowSide {
   float cn;
   uint64_t sr_seed;
   uint32_t sr_stream;
+  float tmul;       // two-level scaling: RN(1 / s_T); 1 for single-level
 };
 
 hipError_t launch_quant_rows(const QuantLaunch& q, hipStream_t s);
@@ -145,6 +147,7 @@ struct GemmLaunch {
   int64_t off[kMaxGroups + 1];
   int32_t tile_start[kMaxGroups + 1];
   int32_t total_tiles;
+  float c_mul;      // factor on C: the operands' tensor factors (two-level scaling), 1 if none
 };
 
 // Raises a kernel's dynamic LDS limit to `bytes` once per kernel and device
@@ -179,9 +182,10 @@ bool gemm_mx6_supported(const GemmLaunch& g);
 int64_t gemm_mx6_workspace(const GemmLaunch& g);
 hipError_t launch_gemm_mx6(const GemmLaunch& g, uint8_t* ws, hipStream_t s);
 
+// `ts`: the two-level tensor factor s_T (1 for single-level scaling).
 hipError_t launch_dequant(const uint8_t* codes, const void* scales, int64_t P, int64_t K,
-                          int32_t grid, int32_t scale_mode, int32_t br, int32_t bc, float* out,
-                          int64_t ldo, hipStream_t s);
+                          int32_t grid, int32_t scale_mode, int32_t br, int32_t bc, float ts,
+                          float* out, int64_t ldo, hipStream_t s);
 hipError_t launch_transpose(const uint8_t* codes, const void* scales, int64_t P, int64_t K,
                             int32_t b, int32_t scale_mode, uint8_t* dcodes, void* dscales,
                             hipStream_t s);

@@ -12,7 +12,8 @@ GEMM_TOL = 1e-4   # relative Frobenius error vs the oracle's fp64 product
 
 def spec_of(cfg):
     return O.QuantSpec(cfg.grid, cfg.rounding, cfg.scale_mode, cfg.block_rows, cfg.block_cols,
-                       cfg.rht_n, cfg.sign_seed, cfg.sr_seed, cfg.sr_stream)
+                       cfg.rht_n, cfg.sign_seed, cfg.sr_seed, cfg.sr_stream,
+                       tensor_scale=float(cfg.tensor_scale))
 
 
 def dev_bf16(bits):

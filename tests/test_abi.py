@@ -40,9 +40,9 @@ def test_struct_layout_matches_header():
 #include <stddef.h>
 #include "ufp4.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(ufp4_quant_cfg), offsetof(ufp4_quant_cfg, sign_seed),
-         offsetof(ufp4_quant_cfg, sr_stream), sizeof(ufp4_qtensor), offsetof(ufp4_qtensor, P),
-         offsetof(ufp4_qtensor, cfg));
+  printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(ufp4_quant_cfg), offsetof(ufp4_quant_cfg, sign_seed),
+         offsetof(ufp4_quant_cfg, sr_stream), offsetof(ufp4_quant_cfg, tensor_scale),
+         sizeof(ufp4_qtensor), offsetof(ufp4_qtensor, P), offsetof(ufp4_qtensor, cfg));
   return 0;
 }
 """
@@ -53,7 +53,8 @@ int main(void) {
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
     got = [int(v) for v in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
     want = [ctypes.sizeof(U.QuantCfg), U.QuantCfg.sign_seed.offset, U.QuantCfg.sr_stream.offset,
-            ctypes.sizeof(U.QTensorC), U.QTensorC.P.offset, U.QTensorC.cfg.offset]
+            U.QuantCfg.tensor_scale.offset, ctypes.sizeof(U.QTensorC), U.QTensorC.P.offset,
+            U.QTensorC.cfg.offset]
     assert got == want
 
 
@@ -93,6 +94,12 @@ def test_quant_argument_errors():
     assert _quant(lib, cfg=bad) == E.UFP4_ERR_UNSUPPORTED
     # 1D power-of-two scales only with the 1 x 32 MX block
     assert _quant(lib, cfg=U.make_cfg(scale_mode=U.UFP4_SCALE_POW2, block_cols=16)) == E.UFP4_ERR_UNSUPPORTED
+    # two-level scaling: a positive, finite, normal factor, power-of-two scales only
+    pow2 = U.make_cfg(scale_mode=U.UFP4_SCALE_POW2, block_cols=32, rht_n=32)
+    for ts in (-1.0, float("nan"), float("inf"), 1e-40):
+        assert _quant(lib, cfg=pow2.copy(tensor_scale=ts)) == E.UFP4_ERR_INVALID_ARG, ts
+    assert _quant(lib, cfg=U.make_cfg(tensor_scale=0.5)) == E.UFP4_ERR_UNSUPPORTED   # fp32 scales
+    assert _quant(lib, rows=0, cfg=pow2.copy(tensor_scale=0.5)) == E.UFP4_OK
     # empty inputs are a successful no-op (no HIP call is made)
     assert _quant(lib, rows=0) == E.UFP4_OK
     assert _quant(lib, cols=0, ld=0) == E.UFP4_OK

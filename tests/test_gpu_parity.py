@@ -861,3 +861,62 @@ def test_gemm_ws_fp6_every_code(grid):
     assert O.rel_fro(C, ref) <= GEMM_TOL
     C0 = U.ufp4_gemm_fprop(qa, qb).cpu().numpy()
     assert O.rel_fro(C0, ref) <= GEMM_TOL
+
+
+TWO_LEVEL = [(U.UFP4_E1M2, 1, 32), (U.UFP4_INT4, 1, 32), (U.UFP4_E2M1, 1, 32),
+             (U.UFP4_E1M2, 32, 1), (U.UFP4_E2M1, 32, 1), (U.UFP4_E4M3, 1, 32)]
+
+
+@pytest.mark.parametrize("grid,br,n", TWO_LEVEL)
+@pytest.mark.parametrize("rnd", [U.UFP4_RTNE, U.UFP4_SR])
+def test_two_level_quant(grid, br, n, rnd):
+    """Two-level scaling (a per-tensor fp32 factor over power-of-two block
+    scales): bit-exact codes, E8M0 bytes and dequantized values row-wise
+    and column-wise (1D), and both sides of a dual-axis call with different
+    factors."""
+    if grid == U.UFP4_E4M3 and rnd == U.UFP4_SR:
+        pytest.skip("MXFP8 rounds to nearest even only")
+    _print_case("two-level quant", grid, br, n, rnd)
+    ts = 0.37
+    cfg = U.make_cfg(grid, rnd, U.UFP4_SCALE_POW2, br, 32, n, sign_seed=71, sr_seed=72,
+                     tensor_scale=ts)
+    bits = rand_bits(96, 192, 73)
+    for along in ((0, 1) if br == 1 else (0,)):
+        q, ref = compare_quant(bits, along, cfg, with_rotated=True)
+        d = U.ufp4_dequant(q).cpu().numpy()
+        want = O.dequant(ref["codes"], ref["scales"], spec_of(cfg), q.P, q.K)[0]
+        assert f32_bits_equal(d, want), ("dequant", along)
+    if br == 1 and grid != U.UFP4_E4M3:
+        cr = cfg.copy(tensor_scale=1.9)
+        cc = cfg.copy(tensor_scale=3.0e-4, sign_seed=74, sr_stream=1)
+        qr, qc = U.ufp4_rht_quant_dual(dev_bf16(bits), cr, cc)
+        for q, ref in ((qr, O.quantize(bits, 0, spec_of(cr))), (qc, O.quantize(bits, 1, spec_of(cc)))):
+            assert np.array_equal(q.scales.cpu().numpy().reshape(-1), np.asarray(ref["scales"]).reshape(-1))
+            assert np.array_equal(q.codes.cpu().numpy().reshape(-1), np.asarray(ref["codes"]).reshape(-1))
+
+
+@pytest.mark.parametrize("grid,br,n", [c for c in TWO_LEVEL if c[0] != U.UFP4_E4M3] +
+                         [(U.UFP4_E4M3, 1, 32)])
+@pytest.mark.parametrize("K", [256, 160])
+def test_two_level_gemm(grid, br, n, K):
+    """GEMMs of two-level operands (different factors on A and B) against
+    the oracle's product of the dequantized operands: the scaled matrix
+    cores (K = 256), FP6 through a workspace (E1M2 / INT4), and the general
+    kernel (K = 160; MXFP8 refuses it)."""
+    _print_case("two-level gemm", grid, br, n, K)
+    ca = U.make_cfg(grid, U.UFP4_RTNE, U.UFP4_SCALE_POW2, br, 32, n, sign_seed=81, tensor_scale=0.021)
+    cb = ca.copy(tensor_scale=5.5)
+    ta, tb = rand_bits(320, K, 82), rand_bits(288, K, 83)
+    qa, ra = compare_quant(ta, 0, ca, with_rotated=False)
+    qb, rb = compare_quant(tb, 0, cb, with_rotated=False)
+    ref = O.gemm_ref(oracle_dequant64(ra, ca), oracle_dequant64(rb, cb))
+    if grid == U.UFP4_E4M3 and K % 128:
+        with pytest.raises(U.UFP4Error):
+            U.ufp4_gemm_fprop(qa, qb)
+        return
+    C = U.ufp4_gemm_fprop(qa, qb).cpu().numpy()
+    assert O.rel_fro(C, ref) <= GEMM_TOL
+    if grid in (U.UFP4_E1M2, U.UFP4_INT4) and K % 128 == 0:
+        assert U.ufp4_gemm_workspace_bytes(U.UFP4_GEMM_FPROP, qa, qb) > 0
+        C6 = U.ufp4_gemm_ws(U.UFP4_GEMM_FPROP, qa, qb).cpu().numpy()
+        assert O.rel_fro(C6, ref) <= GEMM_TOL
