@@ -538,6 +538,33 @@ def square_blocks(U, torch, reps=10):
                             "expansion of both operands into the workspace)"}
             del c
         del qs, qwt, qxt, qdyt
+    # 16 x 16 square blocks (E2M1, SR): the quantization of X and FPROP, which
+    # runs on the general kernel (the scaled matrix cores take 32-element blocks)
+    c16 = U.make_cfg(U.UFP4_E2M1, U.UFP4_SR, U.UFP4_SCALE_POW2, 16, 16, 1,
+                     sr_seed=wl.meta["sr_seed"], sr_stream=0)
+    keep.append(c16)
+    q16 = {}
+    for tn, t in (("x", X), ("w", W)):
+        q, _ = U.ufp4_rht_quant(t, 0, c16)
+        q16[tn] = q
+    rows, cols = X.shape
+    args = (ctypes.c_void_p(X.data_ptr()), rows, cols, X.stride(0), 0, ctypes.byref(c16),
+            ctypes.c_void_p(q16["x"].codes.data_ptr()), ctypes.c_void_p(q16["x"].scales.data_ptr()),
+            None, cs)
+    ms = _timed(torch, _raw(U, "quant_2d_16", lib.ufp4_rht_quant, args), reps)
+    bpe16 = 2.0 + 0.5 + 1.0 / 256
+    out[f"quant_2d_16x16_e2m1_x_{rows}x{cols}"] = {
+        "ms": round(ms, 4), "GB/s": round(bpe16 * X.numel() / ms / 1e6, 1),
+        "frac_hbm_peak": round(bpe16 * X.numel() / ms / 1e6 / HBM_PEAK_GBPS, 4),
+        "bytes_per_elem": round(bpe16, 5)}
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ms = _timed(torch, gemm_call("fprop", q16["x"], q16["w"], c), reps)
+    tf = 2.0 * M * N * K / ms / 1e9
+    out[f"gemm_2d_16x16_{M}x{K}x{N}_e2m1_fprop"] = {
+        "ms": round(ms, 4), "TFLOP/s": round(tf, 1), "peak": FP8_PEAK_TFLOPS,
+        "frac": round(tf / FP8_PEAK_TFLOPS, 4),
+        "mfma": "general kernel: split-bf16 operands on v_mfma_f32_32x32x16_bf16"}
+    del c, q16
     del wl, X, W, dY
     torch.cuda.empty_cache()
     wl2 = workloads.config2("cuda")

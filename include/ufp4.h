@@ -17,7 +17,10 @@
  *     HOST arrays.  The library allocates no memory and keeps no data
  *     between calls (only per-device kernel attributes, set once), so every
  *     entry point is safe to call from several host threads and on several
- *     streams at once, as long as the calls do not write the same buffers.
+ *     streams at once, as long as the calls do not write the same buffers
+ *     (workspaces included).  The one exception is ufp4_quant_diag_noalloc,
+ *     whose partial sums live in a per-GPU array of the library: its calls
+ *     on one GPU must not overlap.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *     default stream).  Nothing synchronizes inside the library.
  *   - Every function returns UFP4_OK (0) or a negative status; arguments are
@@ -73,16 +76,17 @@ enum {
 /* Parameters of one quantization.
  *   grid, rounding, scale_mode : the enums above.
  *   block_rows x block_cols    : 1 x 16 or 1 x 32 (1D groups along K,
- *                                [2DFP4] root cause), or 32 x 32 square
- *                                blocks ([2DFP4] 2D section).  Power-of-two
- *                                scales go with 32 x 32 blocks or 1 x 32
- *                                blocks (the OCP-MX block: one E8M0 byte
- *                                per row and 32 elements); fp32 scales
- *                                with 1 x 16 or 1 x 32 blocks; any other
- *                                pairing is UFP4_ERR_UNSUPPORTED.
+ *                                [2DFP4] root cause), or 16 x 16 or 32 x 32
+ *                                square blocks ([2DFP4] 2D section; its
+ *                                block-size comparison favours 16 to 32).
+ *                                Power-of-two scales go with square blocks
+ *                                or 1 x 32 blocks (the OCP-MX block: one
+ *                                E8M0 byte per row and 32 elements); fp32
+ *                                scales with 1 x 16 or 1 x 32 blocks; any
+ *                                other pairing is UFP4_ERR_UNSUPPORTED.
  *   rht_n     : Hadamard size along K, a power of two in [1, 128]; 1 = no
- *               rotation ([UFP4] Method, Sylvester recursion).  32 x 32
- *               blocks accept rht_n <= 32.
+ *               rotation ([UFP4] Method, Sylvester recursion).  Square
+ *               blocks accept rht_n up to their size.
  *   sign_seed : seed of the random sign diagonal S_n ([UFP4] Method, H' = S H).
  *               Both operands of a GEMM must use the same sign_seed and rht_n.
  *   sr_seed, sr_stream : key and stream of the stochastic-rounding draws;

@@ -33,11 +33,13 @@ int check_cfg(const ufp4_quant_cfg* c) {
   if (!is_pow2(c->rht_n) || c->rht_n > 128) return UFP4_ERR_SHAPE;
   if (c->sr_stream == kSignStream) return UFP4_ERR_UNSUPPORTED;
   const bool one_d = c->block_rows == 1 && (c->block_cols == 16 || c->block_cols == 32);
-  const bool two_d = c->block_rows == 32 && c->block_cols == 32;
+  const bool two_d = c->block_rows == c->block_cols && (c->block_rows == 16 || c->block_rows == 32);
   if (!one_d && !two_d) return UFP4_ERR_UNSUPPORTED;
   // 1D power-of-two scales only for the MX block shape 1 x 32
   if (one_d && c->scale_mode != UFP4_SCALE_F32 && c->block_cols != 32) return UFP4_ERR_UNSUPPORTED;
-  if (two_d && (c->scale_mode != UFP4_SCALE_POW2 || c->rht_n > 32)) return UFP4_ERR_UNSUPPORTED;
+  // square blocks: power-of-two scales, Hadamard chunks inside a block row
+  if (two_d && (c->scale_mode != UFP4_SCALE_POW2 || c->rht_n > c->block_cols))
+    return UFP4_ERR_UNSUPPORTED;
   // MXFP8 (E4M3 elements): 1 x 32 power-of-two blocks, round to nearest even
   if (c->grid == UFP4_E4M3 && (!one_d || c->block_cols != 32 || c->scale_mode != UFP4_SCALE_POW2 ||
                                c->rounding != UFP4_RTNE))
@@ -100,7 +102,8 @@ void fill_common(QuantLaunch& q, const void* x, int64_t rows, int64_t cols, int6
   q.sr_seed = c->sr_seed;
   q.sr_stream = c->sr_stream;
   q.tmul = tensor_mul(c);
-  sign_patterns(c, c->block_rows == 32 ? 32 : lane_width(c->rht_n, c->block_cols), q.sign_pat);
+  sign_patterns(c, c->block_rows > 1 ? c->block_rows : lane_width(c->rht_n, c->block_cols),
+                q.sign_pat);
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? UFP4_OK : UFP4_ERR_HIP; }
@@ -365,14 +368,15 @@ int ufp4_rht_quant(const void* x, int64_t rows, int64_t cols, int64_t ld, int32_
   if (!aligned(x, 16) || ld % 8 || !aligned(codes, 16) || !aligned(scales, 4) ||
       (rotated && !aligned(rotated, 16)))
     return UFP4_ERR_INVALID_ARG;
-  const bool two_d = cfg->block_rows == 32;
+  const int64_t bs = cfg->block_rows;       // square block size; 1 for 1D blocks
+  const bool two_d = bs > 1;
   if (two_d && along == 1) return UFP4_ERR_UNSUPPORTED;  // quantize once, then transpose
   QuantLaunch q;
   fill_common(q, x, rows, cols, ld, cfg, codes, scales, rotated);
   q.P = P;
   q.K = K;
   if (two_d) {
-    if ((P / 32) * cdiv(K / 32, 2) > (int64_t)UINT32_MAX) return UFP4_ERR_UNSUPPORTED;
+    if ((P / bs) * cdiv(K / bs, 64 / bs) > (int64_t)UINT32_MAX) return UFP4_ERR_UNSUPPORTED;
     return hip_status(launch_quant_rows_2d(q, (hipStream_t)stream));
   }
   if (along == 0) {

@@ -202,7 +202,7 @@ __device__ __forceinline__ OperandCursor make_cursor(const uint8_t* codes, const
   } else {
     c.scales = reinterpret_cast<const uint8_t*>(scales) + (row / br) * nb;
     c.pow2 = 1;
-    c.per_step = 1;
+    c.per_step = TK / bc;
   }
   return c;
 }
@@ -226,7 +226,10 @@ __device__ __forceinline__ Fetched fetch(const OperandCursor& c, int step) {
   f.c0 = *reinterpret_cast<const uint2*>(p);
   f.c1 = *reinterpret_cast<const uint2*>(p + (half ? 0 : 8));
   if constexpr (SMODE == 1) {
-    f.s0 = f.s1 = c.scales[st];
+    // E8M0 bytes: one per 32-wide step (32-element blocks) or two (16)
+    const int i0 = st * c.per_step;
+    f.s0 = c.scales[i0];
+    f.s1 = c.scales[i0 + ((c.per_step == 2 && !half) ? 1 : 0)];
   } else {
     // branch-free: 1x16 blocks -> scales 2st, 2st+1; 1x32 -> scale st twice
     const uint32_t* q = reinterpret_cast<const uint32_t*>(c.scales);

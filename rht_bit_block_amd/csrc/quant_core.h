@@ -938,28 +938,29 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide 
 }
 
 // ---------------------------------------------------------------------------
-// Row-wise, 32 x 32 square blocks with power-of-two (E8M0) scales
-// ([2DFP4] 2D section).  A wave covers 32 rows x 64 columns: lane l takes
-// row (l & 31) of the block in column half (l >> 5); the block absmax is a
-// 32-lane reduction.  The scale is the least e with M <= qmax 2^e.
+// Row-wise, BS x BS square blocks (BS = 16 or 32) with power-of-two (E8M0)
+// scales ([2DFP4] 2D section).  A wave covers BS rows x 64 columns: lane l
+// takes row (l % BS) of block column (l / BS); the block absmax is a
+// BS-lane reduction.  The scale is the least e with M <= qmax 2^e.
 // ---------------------------------------------------------------------------
-template <int N, int GRID, int RND>
-__global__ __launch_bounds__(kThreads) void k_quant_rows_2d(QuantLaunch q, uint32_t kpairs,
+template <int BS, int N, int GRID, int RND>
+__global__ __launch_bounds__(kThreads) void k_quant_rows_2d(QuantLaunch q, uint32_t kgroups,
                                                             uint32_t nwaves) {
-  constexpr int W = 32;
+  constexpr int W = BS;
+  constexpr uint32_t kPerWave = 64 / BS;   // block columns per wave
   constexpr float qmax = Grid<GRID>::qmax;
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   uint32_t pm[W / 2];
   sign_masks<W>(q.sign_pat[0], pm);
   const uint32_t K = (uint32_t)q.K;
-  const uint32_t kblocks = K / 32;
+  const uint32_t kblocks = K / BS;
   for (uint32_t wv = wave; wv < nwaves; wv += gridDim.x * (kThreads / 64)) {
-    const uint32_t pb = wv / kpairs;
-    const uint32_t kb = (wv - pb * kpairs) * 2 + (lane >> 5);
+    const uint32_t pb = wv / kgroups;
+    const uint32_t kb = (wv - pb * kgroups) * kPerWave + lane / BS;
     const bool valid = kb < kblocks;
-    const uint32_t p = pb * 32 + (lane & 31u);
-    const uint32_t k0 = kb * 32;
+    const uint32_t p = pb * BS + lane % BS;
+    const uint32_t k0 = kb * BS;
     float y[W];
     float M = 0.0f;
     if (valid) {
@@ -976,9 +977,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows_2d(QuantLaunch q, uint3
 #pragma unroll
       for (int j = 0; j < W; ++j) M = fmaxf(M, fabsf(y[j]));
     }
-    // absmax over the 32 rows of the block (lanes sharing bit 5)
+    // absmax over the BS rows of the block (lanes sharing l / BS)
 #pragma unroll
-    for (int m = 1; m < 32; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+    for (int m = 1; m < BS; m <<= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
     if (!valid) continue;
     M = __fmul_rn(M, q.tmul);            // two-level: max |RN(y m_T)| = RN(M m_T)
     const int e = pow2_exponent<GRID>(M);
@@ -987,7 +988,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows_2d(QuantLaunch q, uint3
     if (q.rotated) store_rotated<W>(q.rotated + e0, y);
     uint32_t rw[W / 2];
     if constexpr (RND == 1) sr_draws<W>(e0, q.sr_seed, q.sr_stream, rw);
-    uint32_t packed[4] = {0u, 0u, 0u, 0u};
+    uint32_t packed[W / 8];
+#pragma unroll
+    for (int i = 0; i < W / 8; ++i) packed[i] = 0u;
 #pragma unroll
     for (int j = 0; j < W; ++j) {
       // power-of-two scale: |v| <= qmax exactly unless e hit its clamp at 127
@@ -1002,10 +1005,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows_2d(QuantLaunch q, uint3
       packed[j >> 3] += word << (4 * (j & 7));
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) packed[i] = finish_codes<GRID>(unbias_words(packed[i]));
-    *reinterpret_cast<uint4*>(q.codes + (e0 >> 1)) =
-        make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    if ((lane & 31u) == 0u)
+    for (int i = 0; i < W / 8; ++i) packed[i] = finish_codes<GRID>(unbias_words(packed[i]));
+    if constexpr (BS == 32)
+      *reinterpret_cast<uint4*>(q.codes + (e0 >> 1)) =
+          make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    else
+      *reinterpret_cast<uint2*>(q.codes + (e0 >> 1)) = make_uint2(packed[0], packed[1]);
+    if (lane % BS == 0u)
       reinterpret_cast<uint8_t*>(q.scales)[(uint64_t)pb * kblocks + kb] = (uint8_t)(e + 127);
   }
 }
@@ -1169,28 +1175,36 @@ hipError_t run_1d(const QuantLaunch& q, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <int G>
-hipError_t run_2d(const QuantLaunch& q, hipStream_t s) {
-  const uint32_t kblocks = (uint32_t)(q.K / 32);
-  const uint32_t kpairs = (kblocks + 1) / 2;
-  const uint64_t nwaves = (uint64_t)(q.P / 32) * kpairs;
+template <int BS, int G>
+hipError_t run_2d_bs(const QuantLaunch& q, hipStream_t s) {
+  constexpr uint32_t kPerWave = 64 / BS;
+  const uint32_t kblocks = (uint32_t)(q.K / BS);
+  const uint32_t kgroups = (kblocks + kPerWave - 1) / kPerWave;
+  const uint64_t nwaves = (uint64_t)(q.P / BS) * kgroups;
   if (nwaves == 0) return hipSuccess;
   const uint64_t blocks_needed = (nwaves + 3) / 4;
   const uint64_t cap = (uint64_t)device_grid_limit() * 16;
   const uint32_t blocks = (uint32_t)(blocks_needed < cap ? blocks_needed : cap);
 #define UFP4_2D(N_)                                                                             \
-  if (q.n == N_) {                                                                              \
-    if (q.rounding == 0)                                                                        \
-      hipLaunchKernelGGL((k_quant_rows_2d<N_, G, 0>), dim3(blocks), dim3(kThreads), 0, s, q,   \
-                         kpairs, (uint32_t)nwaves);                                             \
-    else                                                                                        \
-      hipLaunchKernelGGL((k_quant_rows_2d<N_, G, 1>), dim3(blocks), dim3(kThreads), 0, s, q,   \
-                         kpairs, (uint32_t)nwaves);                                             \
-    return hipGetLastError();                                                                   \
+  if constexpr (N_ <= BS) {                                                                     \
+    if (q.n == N_) {                                                                            \
+      if (q.rounding == 0)                                                                      \
+        hipLaunchKernelGGL((k_quant_rows_2d<BS, N_, G, 0>), dim3(blocks), dim3(kThreads), 0, s, \
+                           q, kgroups, (uint32_t)nwaves);                                       \
+      else                                                                                      \
+        hipLaunchKernelGGL((k_quant_rows_2d<BS, N_, G, 1>), dim3(blocks), dim3(kThreads), 0, s, \
+                           q, kgroups, (uint32_t)nwaves);                                       \
+      return hipGetLastError();                                                                 \
+    }                                                                                           \
   }
   UFP4_2D(1) UFP4_2D(2) UFP4_2D(4) UFP4_2D(8) UFP4_2D(16) UFP4_2D(32)
 #undef UFP4_2D
   return hipErrorInvalidValue;
+}
+
+template <int G>
+hipError_t run_2d(const QuantLaunch& q, hipStream_t s) {
+  return q.br == 16 ? run_2d_bs<16, G>(q, s) : run_2d_bs<32, G>(q, s);
 }
 
 }  // namespace qk

@@ -92,6 +92,12 @@ def test_quant_argument_errors():
     assert _quant(lib, rows=48, cfg=two_d) == E.UFP4_ERR_SHAPE      # P % 32
     bad = two_d.copy(scale_mode=U.UFP4_SCALE_F32)
     assert _quant(lib, cfg=bad) == E.UFP4_ERR_UNSUPPORTED
+    sq16 = two_d.copy(block_rows=16, block_cols=16)
+    assert _quant(lib, rows=40, cfg=sq16) == E.UFP4_ERR_SHAPE      # P % 16
+    assert _quant(lib, along=1, cfg=sq16) == E.UFP4_ERR_UNSUPPORTED
+    assert _quant(lib, cfg=sq16.copy(rht_n=32)) == E.UFP4_ERR_UNSUPPORTED
+    assert _quant(lib, cfg=sq16.copy(scale_mode=U.UFP4_SCALE_F32)) == E.UFP4_ERR_UNSUPPORTED
+    assert _quant(lib, cfg=two_d.copy(block_rows=16)) == E.UFP4_ERR_UNSUPPORTED   # 16 x 32
     # 1D power-of-two scales only with the 1 x 32 MX block
     assert _quant(lib, cfg=U.make_cfg(scale_mode=U.UFP4_SCALE_POW2, block_cols=16)) == E.UFP4_ERR_UNSUPPORTED
     # two-level scaling: a positive, finite, normal factor, power-of-two scales only

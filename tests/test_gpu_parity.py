@@ -55,11 +55,14 @@ def test_quant_cols(n, b, grid, rnd):
 
 @pytest.mark.parametrize("grid", GRIDS)
 @pytest.mark.parametrize("rnd", [U.UFP4_RTNE, U.UFP4_SR])
-@pytest.mark.parametrize("n", [1, 16, 32])
-def test_quant_2d(grid, rnd, n):
-    _print_case("2d", grid, rnd, n)
-    bits = rand_bits(96, 160, seed=grid + 10 * rnd + n)   # K/32 = 5: odd block count
-    cfg = U.make_cfg(grid, rnd, U.UFP4_SCALE_POW2, 32, 32, n, sign_seed=5, sr_seed=5201)
+@pytest.mark.parametrize("n,b", [(1, 32), (16, 32), (32, 32), (1, 16), (8, 16), (16, 16)])
+def test_quant_2d(grid, rnd, n, b):
+    """Square blocks: K / b = 5 or 10 block columns (a wave takes 64 / b of
+    them, so the last wave is partial for b = 32 and for b = 16 with K = 160:
+    10 = 2 x 4 + 2)."""
+    _print_case("2d", grid, rnd, n, b)
+    bits = rand_bits(96, 160, seed=grid + 10 * rnd + n + b)
+    cfg = U.make_cfg(grid, rnd, U.UFP4_SCALE_POW2, b, b, n, sign_seed=5, sr_seed=5201)
     compare_quant(bits, 0, cfg)
 
 
@@ -103,11 +106,11 @@ def test_quant_empty():
 
 
 @pytest.mark.parametrize("grid", GRIDS)
-@pytest.mark.parametrize("two_d", [False, True])
+@pytest.mark.parametrize("two_d", [0, 16, 32])
 def test_dequant_bit_exact(grid, two_d):
     _print_case("dequant", grid, two_d)
     bits = rand_bits(64, 192, seed=grid)
-    cfg = (U.make_cfg(grid, U.UFP4_SR, U.UFP4_SCALE_POW2, 32, 32, 1, sr_seed=9) if two_d
+    cfg = (U.make_cfg(grid, U.UFP4_SR, U.UFP4_SCALE_POW2, two_d, two_d, 1, sr_seed=9) if two_d
            else U.make_cfg(grid, U.UFP4_SR, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=8, sr_seed=9))
     q, ref = compare_quant(bits, 0, cfg, with_rotated=False)
     d = U.ufp4_dequant(q).cpu().numpy()
@@ -144,10 +147,13 @@ def test_gemm_mixed_blocks_and_sr():
 
 
 @pytest.mark.parametrize("grid", [U.UFP4_E2M1, U.UFP4_E1M2])
-def test_gemm_2d_and_transpose(grid):
-    """2D square blocks: quantize once, reuse transposed (S(B) = S(B^T))."""
-    _print_case("2d gemm", grid)
-    cfg = U.make_cfg(grid, U.UFP4_SR, U.UFP4_SCALE_POW2, 32, 32, 1, sr_seed=5201)
+@pytest.mark.parametrize("b", [16, 32])
+def test_gemm_2d_and_transpose(grid, b):
+    """2D square blocks: quantize once, reuse transposed (S(B) = S(B^T));
+    16 x 16 blocks run on the general kernel (the scaled matrix cores take
+    32-element blocks)."""
+    _print_case("2d gemm", grid, b)
+    cfg = U.make_cfg(grid, U.UFP4_SR, U.UFP4_SCALE_POW2, b, b, 1, sr_seed=5201)
     tx, tw = rand_bits(320, 256, 1), rand_bits(288, 256, 2)
     qx, rx = compare_quant(tx, 0, cfg, with_rotated=False)
     qw, rw = compare_quant(tw, 0, cfg, with_rotated=False)
@@ -201,17 +207,18 @@ def test_quant_diag_empty_and_reuse():
         assert np.array_equal(stats.cpu().numpy(), want)
 
 
-@pytest.mark.parametrize("P,K", [(32, 32), (288, 544), (1056, 800), (4096, 4096)])
-def test_transpose_shapes(P, K):
+@pytest.mark.parametrize("P,K,b", [(32, 32, 32), (288, 544, 32), (1056, 800, 32), (4096, 4096, 32),
+                                   (288, 544, 16), (16, 48, 16)])
+def test_transpose_shapes(P, K, b):
     """The square-block transpose on tile-ragged shapes and a full-size
     operand: codes and scale grid exactly the transposed ones.  The operand is
     built from seeded random codes and E8M0 scales (a transpose only moves
     them)."""
-    _print_case("transpose", P, K)
+    _print_case("transpose", P, K, b)
     rng = np.random.default_rng(P * 7 + K)
     codes = rng.integers(0, 16, (P, K), dtype=np.uint8)
-    scales = rng.integers(100, 150, (P // 32, K // 32), dtype=np.uint8)
-    cfg = U.make_cfg(U.UFP4_E2M1, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 32, 32, 1)
+    scales = rng.integers(100, 150, (P // b, K // b), dtype=np.uint8)
+    cfg = U.make_cfg(U.UFP4_E2M1, U.UFP4_RTNE, U.UFP4_SCALE_POW2, b, b, 1)
     q = U.QTensor(torch.from_numpy(O.pack_nibbles(codes)).cuda(), torch.from_numpy(scales).cuda(),
                   P, K, cfg)
     qt = U.ufp4_transpose_qtensor(q)

@@ -206,10 +206,12 @@ def test_e1m2_equals_int4_over_four():
 
 
 @pytest.mark.parametrize("grid", [O.E2M1, O.E1M2])
-def test_square_block_scale_transpose_invariant(grid):
-    """[2DFP4] 2D section: S(B) = S(B^T) for square blocks."""
+@pytest.mark.parametrize("b", [16, 32])
+def test_square_block_scale_transpose_invariant(grid, b):
+    """[2DFP4] 2D section: S(B) = S(B^T) for square blocks (its block-size
+    comparison favours 16 x 16 to 32 x 32)."""
     t = _tensor_bits(128, 96, 4)
-    spec = O.QuantSpec(grid, O.RTNE, O.SCALE_POW2, 32, 32, 1)
+    spec = O.QuantSpec(grid, O.RTNE, O.SCALE_POW2, b, b, 1)
     a = O.quantize(t, 0, spec)
     b = O.quantize(t, 1, spec)          # logical operand T^T
     assert np.array_equal(a["scales"].T, b["scales"])
