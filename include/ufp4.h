@@ -271,7 +271,7 @@ int ufp4_gemm_wgrad_grouped(const ufp4_qtensor* dYt, const ufp4_qtensor* Xt, int
  * workspace.  The uniform grids (E1M2, INT4) with power-of-two scales on
  * 32-element K blocks (1 x 32 or 32 x 32) are contracted on the scaled
  * matrix cores as FP6 E2M3 operands -- every E1M2 level k/4 and every INT4
- * level n/2 is an E2M3 value ([UFP4] chatpaper abstract: uniform grids as
+ * level n in -7..7 is an E2M3 value ([UFP4] chatpaper abstract: uniform grids as
  * first-class hardware primitives; [UFP4] Method: the GEMM contracts the
  * quantized operands): both operands are first expanded from their codes
  * into `workspace` (device memory, 256-byte aligned, at least

@@ -226,7 +226,10 @@ __device__ __forceinline__ Fetched fetch(const OperandCursor& c, int step) {
   f.c0 = *reinterpret_cast<const uint2*>(p);
   f.c1 = *reinterpret_cast<const uint2*>(p + (half ? 0 : 8));
   if constexpr (SMODE == 1) {
-    // E8M0 bytes: one per 32-wide step (32-element blocks) or two (16)
+    // E8M0 bytes of 32-element blocks: one per 32-wide step
+    f.s0 = f.s1 = c.scales[st];
+  } else if constexpr (SMODE == 2) {
+    // E8M0 bytes, 16- or 32-element blocks: one or two per 32-wide step
     const int i0 = st * c.per_step;
     f.s0 = c.scales[i0];
     f.s1 = c.scales[i0 + ((c.per_step == 2 && !half) ? 1 : 0)];
@@ -246,7 +249,7 @@ __device__ __forceinline__ Fetched fetch(const OperandCursor& c, int step) {
 template <int SMODE>
 __device__ __forceinline__ float finalize_scale(uint32_t raw, float v) {
   float s;
-  if constexpr (SMODE == 1) {
+  if constexpr (SMODE != 0) {
     // 2^(e - 127): e >= 1 -> exponent field e; e == 0 -> subnormal 2^-127
     s = __uint_as_float(raw ? (raw << 23) : 0x00400000u);
   } else {
@@ -369,8 +372,8 @@ __global__ __launch_bounds__(kThreads8) void k_gemm8(GemmLaunch g) {
     const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
     const int rv = (int)(pr.a_rows - row0 < TM ? pr.a_rows - row0 : TM);
     const int cv = (int)(pr.b_rows - col0 < TN ? pr.b_rows - col0 : TN);
-    scale_acc<4, 2>(acc, g.c_mul);
-    store_c<4, 2>(pr.c + row0 * g.ldc + col0, g.ldc, rv, cv, wm * 128, wn * 64, lane, acc);
+    store_c<4, 2>(pr.c + row0 * g.ldc + col0, g.ldc, rv, cv, wm * 128, wn * 64, lane, acc,
+                  g.c_mul);
   }
 }
 
@@ -388,14 +391,19 @@ hipError_t launch_one(const GemmLaunch& g, hipStream_t s) {
 hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s) {
   if (g.total_tiles == 0) return hipSuccess;
   if (gemm_rd_supported(g)) return launch_gemm_rd(g, s);
-  const int key = g.grid * 2 + g.scale_mode;
-  switch (key) {
+  // scale modes: 0 fp32; 1 E8M0 with 32-element blocks on both operands; 2 E8M0
+  // with a 16-element block on either
+  const int sm = g.scale_mode == 0 ? 0 : (g.a_bc == 32 && g.b_bc == 32 ? 1 : 2);
+  switch (g.grid * 3 + sm) {
     case 0: return launch_one<0, 0>(g, s);
     case 1: return launch_one<0, 1>(g, s);
-    case 2: return launch_one<1, 0>(g, s);
-    case 3: return launch_one<1, 1>(g, s);
-    case 4: return launch_one<2, 0>(g, s);
-    default: return launch_one<2, 1>(g, s);
+    case 2: return launch_one<0, 2>(g, s);
+    case 3: return launch_one<1, 0>(g, s);
+    case 4: return launch_one<1, 1>(g, s);
+    case 5: return launch_one<1, 2>(g, s);
+    case 6: return launch_one<2, 0>(g, s);
+    case 7: return launch_one<2, 1>(g, s);
+    default: return launch_one<2, 2>(g, s);
   }
 }
 

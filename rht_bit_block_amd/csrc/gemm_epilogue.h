@@ -60,7 +60,7 @@ __device__ __forceinline__ bool c_fits_buffer(int64_t ldc, int rows) {
 template <int NI, int NJ>
 __device__ __forceinline__ void store_c_tile(float* c_tile, int64_t ldc, int rows_valid,
                                              int cols_valid, int r0, int c0, int lane,
-                                             const c_floatx16 (&acc)[NI][NJ]) {
+                                             const c_floatx16 (&acc)[NI][NJ], float m) {
   const uint32_t ld4 = (uint32_t)ldc * 4u;
   const uint32_t bound = (uint32_t)rows_valid * ld4;
   const __amdgpu_buffer_rsrc_t rs =
@@ -81,7 +81,8 @@ __device__ __forceinline__ void store_c_tile(float* c_tile, int64_t ldc, int row
         // written once and not read back by the kernel, so it streams out
         // without displacing the operand strips other tiles still read
         // (the dense layer's step measured 0.8 % faster, 6 of 6 same-box pairs).
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), rs, (int)off, 0, 2);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r] * m), rs, (int)off, 0,
+                                              2);
       }
     }
   }
@@ -91,7 +92,7 @@ __device__ __forceinline__ void store_c_tile(float* c_tile, int64_t ldc, int row
 template <int NI, int NJ>
 __device__ __forceinline__ void store_c_plain(float* c_tile, int64_t ldc, int rows_valid,
                                               int cols_valid, int r0, int c0, int lane,
-                                              const c_floatx16 (&acc)[NI][NJ]) {
+                                              const c_floatx16 (&acc)[NI][NJ], float m) {
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int col = c0 + j * 32 + (lane & 31);
@@ -101,30 +102,21 @@ __device__ __forceinline__ void store_c_plain(float* c_tile, int64_t ldc, int ro
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = r0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < rows_valid) c_tile[(int64_t)row * ldc + col] = acc[i][j][r];
+        if (row < rows_valid) c_tile[(int64_t)row * ldc + col] = acc[i][j][r] * m;
       }
   }
 }
 
-// C times a factor m (two-level scaling: the operands' tensor factors; 1 for
-// single-level scaling, which skips the multiply: the branch is uniform).
-template <int NI, int NJ>
-__device__ __forceinline__ void scale_acc(c_floatx16 (&acc)[NI][NJ], float m) {
-  if (m == 1.0f) return;
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] *= m;
-}
-
+// m: a factor on every element of C (two-level scaling: the operands'
+// tensor factors; 1 otherwise, an exact multiply).
 template <int NI, int NJ>
 __device__ __forceinline__ void store_c(float* c_tile, int64_t ldc, int rows_valid,
                                         int cols_valid, int r0, int c0, int lane,
-                                        const c_floatx16 (&acc)[NI][NJ]) {
+                                        const c_floatx16 (&acc)[NI][NJ], float m = 1.0f) {
   if (c_fits_buffer(ldc, 256))
-    store_c_tile<NI, NJ>(c_tile, ldc, rows_valid, cols_valid, r0, c0, lane, acc);
+    store_c_tile<NI, NJ>(c_tile, ldc, rows_valid, cols_valid, r0, c0, lane, acc, m);
   else
-    store_c_plain<NI, NJ>(c_tile, ldc, rows_valid, cols_valid, r0, c0, lane, acc);
+    store_c_plain<NI, NJ>(c_tile, ldc, rows_valid, cols_valid, r0, c0, lane, acc, m);
 }
 
 }  // namespace ufp4

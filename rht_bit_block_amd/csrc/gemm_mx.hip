@@ -47,15 +47,16 @@
 //   k_gemm_mxrow<FMT> (one byte per element per row, copied HBM -> LDS
 //     untouched, K step 128): FMT 0 = MXFP8 E4M3 codes; FMT 2 = E1M2 / INT4
 //     levels as FP6 E2M3 operands, written beforehand by k_fp6_expand into a
-//     caller workspace (32-byte slot per 32-element block: 24 bytes of 6-bit
-//     fields, element j at bits 6j..6j+5, then 8 zero bytes), so the matrix
-//     cores run at the FP6 rate with no decode in the main loop.
+//     caller workspace (a 32-byte slot per 32-element block: 24 bytes of
+//     6-bit fields, element j at bits 6j..6j+5, then 8 zero bytes), so the
+//     matrix cores run at the FP6 rate with no decode in the main loop.
+//     (Packing two blocks into 48 bytes saves a quarter of the operand bytes
+//     but made the main loop slower on the GPU: the fragment of a block then
+//     spans two LDS chunks at different swizzle positions.)
 //
 // FP6 E2M3 embedding (sign, 2 exponent bits with bias 1, 3 mantissa bits; the
-// subnormal step is 1/8): E1M2 level k/4 is the E2M3 code 2k; INT4 level n is
-// taken as n/2 (|n|/2 in {0, 0.5, ..., 3.5}, all E2M3 values; the nibble 8,
-// no code of the symmetric grid, would still come out as -8) and the product
-// of two INT4 operands is multiplied by 4 on the way out.  FP6 operand in the instruction (checked on the GPU against a
+// subnormal step is 1/8): E1M2 level k/4 is the E2M3 code 2k, and every INT4
+// level n in -7..7 is an E2M3 value (4..7 = 4 x 1, 1.25, 1.5, 1.75).  FP6 operand in the instruction (checked on the GPU against a
 // host model): lane l holds row l % 32 and the 32 elements of one 32-element
 // block (lane half h = block 2s + h of the 64-wide substep s) as 6-bit
 // fields in its first 6 registers.
@@ -125,7 +126,7 @@ __device__ __forceinline__ uint32_t off128(int row, int c) {   // 128-byte rows
 // (grouped along A's rows): rows off[g] .. off[g+1] of A against rows
 // g*R .. g*R + R of B; mode 2 (grouped along K): segment g of both operands,
 // stored [P][L_g] at element offset P*off[g] with 1 x 32 scales at P*off[g]/32.
-// CPE2 = code bytes per two elements (1: packed nibbles, 2: byte rows).
+// CPE4 = code bytes per four elements (2: packed nibbles, 4: byte rows).
 struct MxTile {
   const uint8_t* a_codes;
   const uint8_t* b_codes;
@@ -136,7 +137,19 @@ struct MxTile {
   int tm, tn;
 };
 
-template <int CPE2>
+// The dense case alone (no group search, fewer live scalar values).
+__device__ __forceinline__ MxTile mx_dense(const GemmLaunch& g, int b) {
+  MxTile t;
+  t.a_codes = g.a_codes; t.b_codes = g.b_codes;
+  t.a_scales = reinterpret_cast<const uint8_t*>(g.a_scales);
+  t.b_scales = reinterpret_cast<const uint8_t*>(g.b_scales);
+  t.a_rows = g.PA; t.b_rows = g.PB; t.K = g.K; t.c = g.c;
+  tile_order(b, g.total_tiles, (int)((g.PA + TM - 1) / TM), (int)((g.PB + TN - 1) / TN), t.tm,
+             t.tn);
+  return t;
+}
+
+template <int CPE4>
 __device__ __forceinline__ MxTile mx_resolve(const GemmLaunch& g, int b) {
   const int tile = xcd_linear(b, g.total_tiles);
   int grp = 0;
@@ -150,16 +163,16 @@ __device__ __forceinline__ MxTile mx_resolve(const GemmLaunch& g, int b) {
     t.a_rows = g.PA; t.b_rows = g.PB; t.K = g.K; t.c = g.c;
   } else if (g.mode == 1) {
     const int64_t r0 = g.off[grp], rb0 = (int64_t)grp * g.b_rows_per_group;
-    t.a_codes = g.a_codes + r0 * g.K * CPE2 / 2;
-    t.b_codes = g.b_codes + rb0 * g.K * CPE2 / 2;
+    t.a_codes = g.a_codes + r0 * g.K * CPE4 / 4;
+    t.b_codes = g.b_codes + rb0 * g.K * CPE4 / 4;
     t.a_scales = sa + (r0 / g.a_br) * (g.K / 32);
     t.b_scales = sb + (rb0 / g.b_br) * (g.K / 32);
     t.a_rows = g.off[grp + 1] - r0; t.b_rows = g.b_rows_per_group; t.K = g.K;
     t.c = g.c + r0 * g.ldc;
   } else {
     const int64_t e = g.off[grp];
-    t.a_codes = g.a_codes + g.PA * e * CPE2 / 2;
-    t.b_codes = g.b_codes + g.PB * e * CPE2 / 2;
+    t.a_codes = g.a_codes + g.PA * e * CPE4 / 4;
+    t.b_codes = g.b_codes + g.PB * e * CPE4 / 4;
     t.a_scales = sa + g.PA * (e / 32);
     t.b_scales = sb + g.PB * (e / 32);
     t.a_rows = g.PA; t.b_rows = g.PB; t.K = g.off[grp + 1] - e;
@@ -275,12 +288,12 @@ __device__ __forceinline__ void mfma_substep(floatx16 (&acc)[4][4], Frags& f,
   }
 }
 
-template <int GRID>
+template <int GRID, bool GROUPED, bool SCALED>
 __global__ __launch_bounds__(kThreads) void k_gemm_mx(GemmLaunch g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int STAGE = 2 * TM * 128;
 
-  const MxTile t = mx_resolve<1>(g, blockIdx.x);
+  const MxTile t = GROUPED ? mx_resolve<2>(g, blockIdx.x) : mx_dense(g, blockIdx.x);
   const int tm = t.tm, tn = t.tn;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -315,51 +328,51 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(GemmLaunch g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
 
-  if (c.nsteps > 0) {   // an empty K segment leaves C = 0
-    StepLoads x, y;
-    uint32_t cs_a[4], cs_b[4];     // scale words of the step being multiplied
+  StepLoads x{}, y{};
+  uint32_t cs_a[4], cs_b[4];     // scale words of the step being multiplied
+  // an empty K segment (grouped along K) reads nothing and leaves C = 0: the
+  // step loop below does not run, and what the prologue stages is never used
+  if (c.nsteps > 0) {
     fetch(c, 0, x);
     fetch(c, 1, y);
-    stage<GRID>(lds, x, tid);
-  #pragma unroll
-    for (int i = 0; i < 4; ++i) { cs_a[i] = x.sa[i]; cs_b[i] = x.sb[i]; }
-    __syncthreads();
-    Frags f;
-  #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f.a[i] = load_frag(lds, 0, 0, lane, wm, i);
-      f.b[i] = load_frag(lds, 1, 0, lane, wn, i);
-    }
-
-    // Step i: LDS stage i&1 holds step i; `nx` holds the loads of step i+1;
-    // `fr` receives the loads of step i+2.
-    auto body = [&](int step, StepLoads& nx, StepLoads& fr) {
-      const uint8_t* cur = lds + (step & 1) * STAGE;
-      uint8_t* nxt = lds + ((step + 1) & 1) * STAGE;
-      fetch(c, step + 2, fr);
-      mfma_substep<GRID>(acc, f, cs_a, cs_b, 0, h, cur, 1, lane, wm, wn);
-      stage<GRID>(nxt, nx, tid);
-      mfma_substep<GRID>(acc, f, cs_a, cs_b, 1, h, nullptr, 0, lane, wm, wn);
-  #pragma unroll
-      for (int i = 0; i < 4; ++i) { cs_a[i] = nx.sa[i]; cs_b[i] = nx.sb[i]; }
-      __syncthreads();
-  #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f.a[i] = load_frag(nxt, 0, 0, lane, wm, i);
-        f.b[i] = load_frag(nxt, 1, 0, lane, wn, i);
-      }
-    };
-    int step = 0;
-    for (; step + 1 < c.nsteps; step += 2) {
-      body(step, y, x);
-      body(step + 1, x, y);
-    }
-    if (step < c.nsteps) body(step, y, x);
+  }
+  stage<GRID>(lds, x, tid);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { cs_a[i] = x.sa[i]; cs_b[i] = x.sb[i]; }
+  __syncthreads();
+  Frags f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f.a[i] = load_frag(lds, 0, 0, lane, wm, i);
+    f.b[i] = load_frag(lds, 1, 0, lane, wn, i);
   }
 
-  scale_acc<4, 4>(acc, g.c_mul);
+  // Step i: LDS stage i&1 holds step i; `nx` holds the loads of step i+1;
+  // `fr` receives the loads of step i+2.
+  auto body = [&](int step, StepLoads& nx, StepLoads& fr) {
+    const uint8_t* cur = lds + (step & 1) * STAGE;
+    uint8_t* nxt = lds + ((step + 1) & 1) * STAGE;
+    fetch(c, step + 2, fr);
+    mfma_substep<GRID>(acc, f, cs_a, cs_b, 0, h, cur, 1, lane, wm, wn);
+    stage<GRID>(nxt, nx, tid);
+    mfma_substep<GRID>(acc, f, cs_a, cs_b, 1, h, nullptr, 0, lane, wm, wn);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { cs_a[i] = nx.sa[i]; cs_b[i] = nx.sb[i]; }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f.a[i] = load_frag(nxt, 0, 0, lane, wm, i);
+      f.b[i] = load_frag(nxt, 1, 0, lane, wn, i);
+    }
+  };
+  int step = 0;
+  for (; step + 1 < c.nsteps; step += 2) {
+    body(step, y, x);
+    body(step + 1, x, y);
+  }
+  if (step < c.nsteps) body(step, y, x);
   store_c<4, 4>(t.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
-                lane, acc);
+                lane, acc, SCALED ? g.c_mul : 1.0f);
 }
 
 // ---------------------------------------------------------------------------
@@ -483,10 +496,11 @@ __device__ __forceinline__ void f4_mfma(floatx16 (&acc)[4][4], const F4Frags& f,
                                                                   0, xa[i], 0, xb[j]);
 }
 
+template <bool SCALED>
 __global__ __launch_bounds__(kThreads) void k_gemm_mx4(GemmLaunch g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  const MxTile t = mx_resolve<1>(g, blockIdx.x);
+  const MxTile t = mx_resolve<2>(g, blockIdx.x);
   const int tm = t.tm, tn = t.tn;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -567,18 +581,22 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx4(GemmLaunch g) {
     wait_vmcnt<0>();   // drain the clamped prefetches before the workgroup ends
   }
 
-  scale_acc<4, 4>(acc, g.c_mul);
   store_c<4, 4>(t.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
-                lane, acc);
+                lane, acc, SCALED ? g.c_mul : 1.0f);
+}
+
+template <bool SCALED>
+hipError_t launch_mx4_s(const GemmLaunch& g, hipStream_t s) {
+  constexpr int bytes = NST * F4_STAGE;
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = set_lds_limit((const void*)k_gemm_mx4<SCALED>, bytes, lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_gemm_mx4<SCALED>), dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_mx4(const GemmLaunch& g, hipStream_t s) {
-  constexpr int bytes = NST * F4_STAGE;
-  static std::atomic<uint64_t> lds_set{0};
-  const hipError_t e = set_lds_limit((const void*)k_gemm_mx4, bytes, lds_set);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_gemm_mx4, dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
-  return hipGetLastError();
+  return g.c_mul == 1.0f ? launch_mx4_s<false>(g, s) : launch_mx4_s<true>(g, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -645,10 +663,11 @@ __device__ __forceinline__ void w4_scales(const uint8_t* stage, int lane, int wm
     }
 }
 
+template <bool SCALED>
 __global__ __launch_bounds__(kThreads) void k_gemm_mx4w(GemmLaunch g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  const MxTile t = mx_resolve<1>(g, blockIdx.x);
+  const MxTile t = mx_resolve<2>(g, blockIdx.x);
   const int tm = t.tm, tn = t.tn;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -717,20 +736,20 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx4w(GemmLaunch g) {
     }
   }
 
-  scale_acc<4, 4>(acc, g.c_mul);
   store_c<4, 4>(t.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
-                lane, acc);
+                lane, acc, SCALED ? g.c_mul : 1.0f);
 }
 
 // ---------------------------------------------------------------------------
-// Byte-row kernels: one byte per element (MXFP8 E4M3 codes, or FP6 E2M3
-// fields in 32-byte slots), copied HBM -> LDS untouched as in k_gemm_mx4w.
-// K step 128 = one 128-byte line per row; two 66 KiB stages (codes 2 x 32 KiB,
-// one scale word per row and operand).  FP8 fragments and the scale operand
-// as in the FP8 path of k_gemm_mx: lane l takes 16 bytes of blocks 2s and
-// 2s+1 (chunks 4s + h and 4s + 2 + h) and supplies the scale of row l % 32,
-// block 2s + h.  FP6 fragments: lane l takes the 24 bytes of block 2s + h
-// (chunk 4s + 2h and the first half of chunk 4s + 2h + 1), same scale.
+// Byte-row kernels: one byte per element per row (MXFP8 E4M3 codes, or FP6
+// E2M3 fields in 32-byte slots), copied HBM -> LDS untouched as in
+// k_gemm_mx4w.  K step 128 = one 128-byte line per row; two 66 KiB stages
+// (codes 2 x 32 KiB, one scale word per row and operand).  FP8 fragments and
+// the scale operand as in the FP8 path of k_gemm_mx: lane l takes 16 bytes of
+// blocks 2s and 2s+1 (chunks 4s + h and 4s + 2 + h) and supplies the scale of
+// row l % 32, block 2s + h.  FP6 fragments: lane l takes the 24 bytes of
+// block 2s + h (chunk 4s + 2h and the first half of chunk 4s + 2h + 1), same
+// scale.
 // ---------------------------------------------------------------------------
 constexpr int K8 = 128;
 constexpr int W8_CODES = 2 * TM * 128;
@@ -810,11 +829,11 @@ __device__ __forceinline__ void f8_mfma(floatx16 (&acc)[4][4], const F4Frags& f,
                                                                   FMT, 0, xa[i], 0, xb[j]);
 }
 
-template <int FMT>
+template <int FMT, bool GROUPED, bool SCALED>
 __global__ __launch_bounds__(kThreads) void k_gemm_mxrow(GemmLaunch g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  const MxTile t = mx_resolve<2>(g, blockIdx.x);
+  const MxTile t = GROUPED ? mx_resolve<4>(g, blockIdx.x) : mx_dense(g, blockIdx.x);
   const int tm = t.tm, tn = t.tn;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -840,8 +859,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxrow(GemmLaunch g) {
   const int lrow = lane >> 3;
   const uint32_t chunk = (uint32_t)((lane & 7) ^ lrow);
 #pragma unroll
-  for (int q = 0; q < 8; ++q)
-    c.code_voff[q] = (uint32_t)(wave * 64 + q * 8 + lrow) * rs + 16u * chunk;
+  for (int q = 0; q < 8; ++q) c.code_voff[q] = (uint32_t)(wave * 64 + q * 8 + lrow) * rs + 16u * chunk;
   {
     int64_t ra = row0 + wave * 64 + lane, rb = col0 + wave * 64 + lane;
     if (ra >= t.a_rows) ra = t.a_rows - 1;   // codes of such rows read as zero; any scale works
@@ -856,36 +874,37 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxrow(GemmLaunch g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
 
-  if (c.nsteps > 0) {   // an empty K segment leaves C = 0
-    w8_issue(c, 0, 0);
+  // an empty K segment (grouped along K) reads nothing and leaves C = 0: the
+  // step loop below does not run, and what the prologue stages is never used
+  if (c.nsteps > 0) w8_issue(c, 0, 0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  F4Frags f0, f1;
+  uint32_t sa[4], sb[4];
+  w8_frags<FMT>(lds, 0, lane, wm, wn, f0);
+  w8_scales(lds, lane, wm, wn, sa, sb);
+
+  for (int step = 0; step < c.nsteps; ++step) {
+    const uint8_t* cur = lds + (step & 1) * W8_STAGE;
+    w8_issue(c, step + 1, (step + 1) & 1);
+    w8_frags<FMT>(cur, 1, lane, wm, wn, f1);
+    f8_mfma<FMT>(acc, f0, sa, sb, 0, h);
+    f8_mfma<FMT>(acc, f1, sa, sb, 1, h);
     wait_vmcnt<0>();
     __syncthreads();
-    F4Frags f0, f1;
-    uint32_t sa[4], sb[4];
-    w8_frags<FMT>(lds, 0, lane, wm, wn, f0);
-    w8_scales(lds, lane, wm, wn, sa, sb);
-
-    for (int step = 0; step < c.nsteps; ++step) {
-      const uint8_t* cur = lds + (step & 1) * W8_STAGE;
-      w8_issue(c, step + 1, (step + 1) & 1);
-      w8_frags<FMT>(cur, 1, lane, wm, wn, f1);
-      f8_mfma<FMT>(acc, f0, sa, sb, 0, h);
-      f8_mfma<FMT>(acc, f1, sa, sb, 1, h);
-      wait_vmcnt<0>();
-      __syncthreads();
-      const uint8_t* nxt = lds + ((step + 1) & 1) * W8_STAGE;
-      w8_frags<FMT>(nxt, 0, lane, wm, wn, f0);
-      w8_scales(nxt, lane, wm, wn, sa, sb);
-    }
+    const uint8_t* nxt = lds + ((step + 1) & 1) * W8_STAGE;
+    w8_frags<FMT>(nxt, 0, lane, wm, wn, f0);
+    w8_scales(nxt, lane, wm, wn, sa, sb);
   }
 
-  scale_acc<4, 4>(acc, g.c_mul);
   store_c<4, 4>(t.c + row0 * g.ldc + col0, g.ldc, (int)rows_a, (int)rows_b, wm * 128, wn * 128,
-                lane, acc);
+                lane, acc, SCALED ? g.c_mul : 1.0f);
 }
 
 // E2M3 field of a 4-bit code (see the header): E1M2 sign-magnitude s|k ->
-// s<<5 | 2k; INT4 two's complement n -> sign<<5 | E2M3(|n| / 2).
+// s<<5 | 2k; INT4 two's complement n -> sign<<5 | E2M3(|n|):
+// 1 -> 8, 2 -> 16, 3 -> 20, 4..7 -> 24, 26, 28, 30.  The nibble 8 (-8, no
+// code of the symmetric grid) has no E2M3 value and reads as -7.5 (63).
 template <int GRID>
 __device__ __forceinline__ uint32_t fp6_field(uint32_t c) {
   if constexpr (GRID == 0) {
@@ -893,39 +912,63 @@ __device__ __forceinline__ uint32_t fp6_field(uint32_t c) {
   } else {
     const uint32_t neg = c >> 3;
     const uint32_t m = neg ? 16u - c : c;       // |n| in 0..8
-    return (neg << 5) | (m <= 4u ? 4u * m : 2u * m + 8u);
+    const uint32_t f = m >= 4u ? 2u * m + 16u : (m >= 2u ? 4u * m + 8u : 8u * m);
+    return (neg << 5) | (m == 8u ? 31u : f);
   }
 }
 
-// One thread per 32-element block: 16 code bytes in, one 32-byte FP6 slot out.
+// Six 32-bit words of 6-bit E2M3 fields (element j at bits 6j) from the
+// 32 code nibbles of one block.
+template <int GRID>
+__device__ __forceinline__ void fp6_block(const v4i& w, uint32_t (&o)[6]) {
+  uint32_t t[7] = {0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const uint32_t f = fp6_field<GRID>(((uint32_t)w[j >> 3] >> (4 * (j & 7))) & 15u);
+    const int bit = 6 * j, wi = bit >> 5, sh = bit & 31;
+    t[wi] |= f << sh;
+    if (sh > 26) t[wi + 1] |= f >> (32 - sh);
+  }
+#pragma unroll
+  for (int i = 0; i < 6; ++i) o[i] = t[i];
+}
+
+// One thread per 32-element block: 16 code bytes in, one 32-byte slot out.
 template <int GRID>
 __global__ __launch_bounds__(256) void k_fp6_expand(const uint8_t* __restrict__ codes,
                                                     uint8_t* __restrict__ out, int64_t nblk) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t bk = (int64_t)blockIdx.x * 256 + threadIdx.x; bk < nblk; bk += stride) {
-    const v4i w = *reinterpret_cast<const v4i*>(codes + bk * 16);
-    uint32_t o[7] = {0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const uint32_t f = fp6_field<GRID>(((uint32_t)w[j >> 3] >> (4 * (j & 7))) & 15u);
-      const int bit = 6 * j, wi = bit >> 5, sh = bit & 31;
-      o[wi] |= f << sh;
-      if (sh > 26) o[wi + 1] |= f >> (32 - sh);
-    }
+    uint32_t a[6];
+    fp6_block<GRID>(*reinterpret_cast<const v4i*>(codes + bk * 16), a);
     v4i* dst = reinterpret_cast<v4i*>(out + bk * 32);
-    dst[0] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-    dst[1] = v4i{(int)o[4], (int)o[5], 0, 0};
+    dst[0] = v4i{(int)a[0], (int)a[1], (int)a[2], (int)a[3]};
+    dst[1] = v4i{(int)a[4], (int)a[5], 0, 0};
   }
 }
 
-template <int FMT>
-hipError_t launch_mxrow(const GemmLaunch& g, hipStream_t s) {
+template <int FMT, bool GROUPED, bool SCALED>
+hipError_t launch_mxrow_s(const GemmLaunch& g, hipStream_t s) {
   constexpr int bytes = 2 * W8_STAGE;
   static std::atomic<uint64_t> lds_set{0};
-  const hipError_t e = set_lds_limit((const void*)k_gemm_mxrow<FMT>, bytes, lds_set);
+  const hipError_t e =
+      set_lds_limit((const void*)k_gemm_mxrow<FMT, GROUPED, SCALED>, bytes, lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gemm_mxrow<FMT>), dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
+  hipLaunchKernelGGL((k_gemm_mxrow<FMT, GROUPED, SCALED>), dim3(g.total_tiles), dim3(kThreads),
+                     bytes, s, g);
   return hipGetLastError();
+}
+
+// MXFP8 (FMT 0) is dense only; the FP6 operands may be grouped.
+template <int FMT>
+hipError_t launch_mxrow(const GemmLaunch& g, hipStream_t s) {
+  const bool scaled = g.c_mul != 1.0f;
+  if constexpr (FMT == 2) {
+    if (g.mode != 0)
+      return scaled ? launch_mxrow_s<FMT, true, true>(g, s)
+                    : launch_mxrow_s<FMT, true, false>(g, s);
+  }
+  return scaled ? launch_mxrow_s<FMT, false, true>(g, s) : launch_mxrow_s<FMT, false, false>(g, s);
 }
 
 template <int GRID>
@@ -939,23 +982,37 @@ hipError_t launch_fp6_expand(const uint8_t* codes, uint8_t* out, int64_t P, int6
   return hipGetLastError();
 }
 
-hipError_t launch_mx4w(const GemmLaunch& g, hipStream_t s) {
+template <bool SCALED>
+hipError_t launch_mx4w_s(const GemmLaunch& g, hipStream_t s) {
   constexpr int bytes = 2 * W4_STAGE;
   static std::atomic<uint64_t> lds_set{0};
-  const hipError_t e = set_lds_limit((const void*)k_gemm_mx4w, bytes, lds_set);
+  const hipError_t e = set_lds_limit((const void*)k_gemm_mx4w<SCALED>, bytes, lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_gemm_mx4w, dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
+  hipLaunchKernelGGL((k_gemm_mx4w<SCALED>), dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx4w(const GemmLaunch& g, hipStream_t s) {
+  return g.c_mul == 1.0f ? launch_mx4w_s<false>(g, s) : launch_mx4w_s<true>(g, s);
+}
+
+template <int GRID, bool GROUPED, bool SCALED>
+hipError_t launch_mx_g(const GemmLaunch& g, hipStream_t s) {
+  constexpr int bytes = 2 * 2 * TM * 128;   // 2 stages x 2 operands
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e =
+      set_lds_limit((const void*)k_gemm_mx<GRID, GROUPED, SCALED>, bytes, lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_gemm_mx<GRID, GROUPED, SCALED>), dim3(g.total_tiles), dim3(kThreads),
+                     bytes, s, g);
   return hipGetLastError();
 }
 
 template <int GRID>
 hipError_t launch_mx(const GemmLaunch& g, hipStream_t s) {
-  constexpr int bytes = 2 * 2 * TM * 128;   // 2 stages x 2 operands
-  static std::atomic<uint64_t> lds_set{0};
-  const hipError_t e = set_lds_limit((const void*)k_gemm_mx<GRID>, bytes, lds_set);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gemm_mx<GRID>), dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
-  return hipGetLastError();
+  if (g.c_mul != 1.0f)
+    return g.mode == 0 ? launch_mx_g<GRID, false, true>(g, s) : launch_mx_g<GRID, true, true>(g, s);
+  return g.mode == 0 ? launch_mx_g<GRID, false, false>(g, s) : launch_mx_g<GRID, true, false>(g, s);
 }
 
 }  // namespace
@@ -972,14 +1029,14 @@ bool k_multiple(const GemmLaunch& g, int64_t step) {
 }
 
 // Block shapes, grouping and 32-bit buffer sizes the scaled-MFMA kernels
-// take (`bpe2`: code bytes per two elements of the kernel's operand rows).
-bool mx_layout_ok(const GemmLaunch& g, int64_t step, int64_t bpe2) {
+// take (`bpe4`: code bytes per four elements of the kernel's operand rows).
+bool mx_layout_ok(const GemmLaunch& g, int64_t step, int64_t bpe4) {
   if (g.scale_mode != 1 || g.a_bc != 32 || g.b_bc != 32) return false;
   const bool rows_ok = (g.a_br == 1 || g.a_br == 32) && (g.b_br == 1 || g.b_br == 32);
   if (g.mode == 0 && !rows_ok) return false;
   if (g.mode == 1 && !(rows_ok && g.b_rows_per_group % g.b_br == 0)) return false;
   if (g.mode == 2 && !(g.a_br == 1 && g.b_br == 1)) return false;
-  return k_multiple(g, step) && g.K * bpe2 / 2 * (int64_t)TM <= INT32_MAX &&
+  return k_multiple(g, step) && g.K * bpe4 / 4 * (int64_t)TM <= INT32_MAX &&
          ((g.PA - 1) / g.a_br + 1) * (g.K / 32) <= INT32_MAX &&
          ((g.PB - 1) / g.b_br + 1) * (g.K / 32) <= INT32_MAX;
 }
@@ -988,14 +1045,16 @@ bool mx_layout_ok(const GemmLaunch& g, int64_t step, int64_t bpe2) {
 
 bool gemm_mx_supported(const GemmLaunch& g) {
   if (g.grid == 3)   // MXFP8: dense, 1 x 32 blocks, byte codes
-    return g.mode == 0 && g.a_br == 1 && g.b_br == 1 && mx_layout_ok(g, K8, 2);
-  return mx_layout_ok(g, KS, 1);
+    return g.mode == 0 && g.a_br == 1 && g.b_br == 1 && mx_layout_ok(g, K8, 4);
+  return mx_layout_ok(g, KS, 2);
 }
 
 bool gemm_mx6_supported(const GemmLaunch& g) {
-  return (g.grid == 0 || g.grid == 1) && mx_layout_ok(g, K8, 2);
+  return (g.grid == 0 || g.grid == 1) && mx_layout_ok(g, K8, 4);
 }
 
+// FP6 operands: one 32-byte slot per 32-element block (one byte per element),
+// A then B at a 256-byte boundary.
 int64_t gemm_mx6_workspace(const GemmLaunch& g) {
   return ((g.PA * g.K + 255) / 256) * 256 + g.PB * g.K;
 }
@@ -1011,7 +1070,6 @@ hipError_t launch_gemm_mx6(const GemmLaunch& g, uint8_t* ws, hipStream_t s) {
   e = g.grid == 0 ? launch_fp6_expand<0>(g.b_codes, const_cast<uint8_t*>(x.b_codes), g.PB, g.K, s)
                   : launch_fp6_expand<1>(g.b_codes, const_cast<uint8_t*>(x.b_codes), g.PB, g.K, s);
   if (e != hipSuccess) return e;
-  if (g.grid == 1) x.c_mul = g.c_mul * 4.0f;   // INT4 operands entered as n / 2 (exact)
   return launch_mxrow<2>(x, s);
 }
 

@@ -148,7 +148,7 @@ def test_gemm_workspace_errors():
     pow2 = U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_POW2, 1, 32, 1)
     a, b = _qt(300, 256, pow2), _qt(64, 256, pow2)
     wb = lib.ufp4_gemm_workspace_bytes
-    need = (300 * 256 + 255) // 256 * 256 + 64 * 256
+    need = (300 * 256 + 255) // 256 * 256 + 64 * 256      # FP6: one byte per element
     for op in (U.UFP4_GEMM_FPROP, U.UFP4_GEMM_DGRAD, U.UFP4_GEMM_WGRAD):
         assert wb(op, ctypes.byref(a), ctypes.byref(b), 0) == need
     assert wb(3, ctypes.byref(a), ctypes.byref(b), 0) == 0

@@ -872,17 +872,17 @@ def test_gemm_ws_fp6_every_code(grid):
 
 TWO_LEVEL = [(U.UFP4_E1M2, 1, 32), (U.UFP4_INT4, 1, 32), (U.UFP4_E2M1, 1, 32),
              (U.UFP4_E1M2, 32, 1), (U.UFP4_E2M1, 32, 1), (U.UFP4_E4M3, 1, 32)]
+# MXFP8 rounds to nearest even only
+TWO_LEVEL_CASES = [(g, br, n, r) for g, br, n in TWO_LEVEL for r in (U.UFP4_RTNE, U.UFP4_SR)
+                   if not (g == U.UFP4_E4M3 and r == U.UFP4_SR)]
 
 
-@pytest.mark.parametrize("grid,br,n", TWO_LEVEL)
-@pytest.mark.parametrize("rnd", [U.UFP4_RTNE, U.UFP4_SR])
+@pytest.mark.parametrize("grid,br,n,rnd", TWO_LEVEL_CASES)
 def test_two_level_quant(grid, br, n, rnd):
     """Two-level scaling (a per-tensor fp32 factor over power-of-two block
     scales): bit-exact codes, E8M0 bytes and dequantized values row-wise
     and column-wise (1D), and both sides of a dual-axis call with different
     factors."""
-    if grid == U.UFP4_E4M3 and rnd == U.UFP4_SR:
-        pytest.skip("MXFP8 rounds to nearest even only")
     _print_case("two-level quant", grid, br, n, rnd)
     ts = 0.37
     cfg = U.make_cfg(grid, rnd, U.UFP4_SCALE_POW2, br, 32, n, sign_seed=71, sr_seed=72,
