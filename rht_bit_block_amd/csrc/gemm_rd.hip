@@ -11,18 +11,20 @@
 //   sum_k dA[p][k] dB[q][k] = (sA[p] sB[q]) * sum_k lA[p][k] lB[q][k].
 // The level dot products P come from v_mfma_f32_32x32x16_fp8_fp8 on the
 // levels as E4M3 bytes: every level of the three codebooks is an E4M3 number,
-// so P is exact in fp32.  The scale products S come from a second MFMA,
-// v_mfma_f32_32x32x16_bf16, on bf16 pieces of the scales: s = s0 + s1 + s2
-// exactly (s0 = bf16(s), s1 = bf16(s - s0), s2 = s - s0 - s1), and the K
-// slots pair six of the nine cross products (all but s1 t2, s2 t1, s2 t2,
-// each below 2^-25 of s t).  C += P * S is one fp32 fma per element.  The
-// result differs from the exact one by fp32 rounding only (a few 2^-24
-// relative per step).
+// so P is exact in fp32.  The scale products S come from a second MFMA on
+// bf16 pieces of the scales: s = s0 + s1 + s2 exactly (s0 = bf16(s),
+// s1 = bf16(s - s0), s2 = s - s0 - s1), and the eight K slots pair six of the
+// nine cross products (all but s1 t2, s2 t1, s2 t2, each below 2^-25 of s t).
+// In the 16-wide kernel that MFMA is v_mfma_f32_32x32x8_bf16 (lane half h
+// supplies slots 4h .. 4h + 3: two registers per operand); k_gemm_rd32 uses
+// v_mfma_f32_32x32x16_bf16 with the slots in the lower lane half.  C += P * S
+// is one fp32 fma per element.  The result differs from the exact one by fp32
+// rounding only (a few 2^-24 relative per step).
 //
 // Both MFMAs take fresh accumulators and are independent: a step costs two
-// MFMAs (64 matrix-core cycles) and 16 fmas (64 VALU cycles) per 32 x 32
-// tile, and the two units work side by side across the two waves of a SIMD
-// (one wave's fmas while the other's MFMAs execute).
+// MFMAs and 16 fmas per 32 x 32 tile, and the two units work side by side
+// within a wave (fmas of tile t while the products of tile t+1 execute) and
+// across the two waves of a SIMD.
 //
 // Data flow: the packed codes and the fp32 scales are copied HBM -> LDS
 // untouched by buffer_load ... lds (M0-based direct loads; four lanes per
@@ -38,10 +40,12 @@
 // during the first tile (its raw inputs were read from LDS during step i-1),
 // one barrier, then the fragments of step i+1 are read as registers free up,
 // so the LDS reads of a step are hidden under the tiles of the one before.
-// Inside a step the 16-wide kernel walks its 8 tiles column by column and
-// issues the level product of tile t+1 before the fmas of tile t (level
-// products double-buffered, the scale product of tile t+1 after them); each
-// operand fragment is reloaded right after its last product is issued.
+// Inside a step the 16-wide kernel walks its 8 tiles column by column; both
+// products are double-buffered, and the products of tile t+1 are issued
+// around the first half of tile t's fmas (level product, 8 fmas, scale
+// product, 8 fmas, in that order), so no fma waits on an MFMA issued just
+// before it; each operand fragment is reloaded right after its last product
+// is issued.
 //
 // With 1 x 32 blocks one scale covers two 16-wide halves, so k_gemm_rd32
 // takes 32-wide steps: two chained level MFMAs, one scale product and one set
@@ -110,8 +114,8 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 }
 
 // bf16 pieces of a block scale for the scale-product MFMA: s = s0 + s1 + s2
-// (each rounding leaves an exact fp32 residual).  K slots 0..7 (lower lane
-// half; the upper half is zero), A side x B side:
+// (each rounding leaves an exact fp32 residual).  K slots 0..7, A side x B
+// side:
 //   A: s0 s0 s0 s1 s1 s2 0 0        B: t0 t1 t2 t0 t1 t0 0 0
 // sum = s0 (t0 + t1 + t2) + s1 (t0 + t1) + s2 t0.
 template <int OP>
@@ -168,13 +172,10 @@ template <int BC> struct Layout {
   static constexpr int SPW = SLOADS / 8;          // per wave
   static constexpr int VMEM = 4 + SPW;            // loads per wave per raw stage
   // decoded buffer: levels [op][K half][row] x 8 E4M3, then scale pieces
-  // [op][row] x 8 bf16, then the zero slots the upper lane half reads for the
-  // scale operand, at ZERO + 512 t for t = 0..3 (the stride of a 32-row tile of
-  // scale pieces, so every fragment address is a base plus 512 t)
+  // [op][row] x 8 bf16 (lane half h of a fragment reads pieces 4h .. 4h + 3)
   static constexpr int LEV = 2 * 2 * TM * 8;
   static constexpr int PCS = 2 * TM * 16;
-  static constexpr int ZERO = LEV + PCS;
-  static constexpr int DEC = ZERO + 3 * 512 + 16;
+  static constexpr int DEC = LEV + PCS;
   static constexpr int TOTAL = NRAW * RAW + 2 * DEC;
 };
 
@@ -234,21 +235,28 @@ __device__ __forceinline__ void decode_store(const DecIn& d, uint8_t* dec, int o
       op ? scale_pieces<1>(d.s) : scale_pieces<0>(d.s);
 }
 
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+// Operand fragment of the 16-wide kernel: 8 E4M3 levels (level product) and
+// the lane half's four scale pieces (scale product).
 struct Frag {
-  long code;      // 8 E4M3 levels
-  bf16x8 pc;      // scale pieces (lower lane half) or zeros (upper half)
+  long code;
+  short4_t pc;
 };
 
 __device__ __forceinline__ Frag frag_at(const uint8_t* dec, uint32_t code_off, uint32_t pc_off) {
   Frag f;
   f.code = *reinterpret_cast<const long*>(dec + code_off);
-  f.pc = *reinterpret_cast<const bf16x8*>(dec + pc_off);
+  f.pc = *reinterpret_cast<const short4_t*>(dec + pc_off);
   return f;
 }
 
-__device__ __forceinline__ void mfma_tile(const Frag& a, const Frag& b, floatx16& p, floatx16& q) {
-  p = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a.code, b.code, floatx16{}, 0, 0, 0);
-  q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.pc, b.pc, floatx16{}, 0, 0, 0);
+__device__ __forceinline__ floatx16 level_product(const Frag& a, const Frag& b) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a.code, b.code, floatx16{}, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx16 scale_product(const Frag& a, const Frag& b) {
+  return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a.pc, b.pc, floatx16{}, 0, 0, 0);
 }
 
 struct Operands {
@@ -369,9 +377,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
   const int64_t K = ts.o.K;
   uint8_t* decb = lds + NRAW * L::RAW;   // two decoded buffers
 
-  if (tid < 8)
-    *reinterpret_cast<uint4*>(decb + (tid >> 2) * L::DEC + L::ZERO + (tid & 3) * 512) = make_uint4(0, 0, 0, 0);
-
   floatx16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -387,8 +392,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
   // fragment offsets in a decoded buffer; tile t adds 256 t (levels), 512 t (pieces)
   const uint32_t code_a = (uint32_t)(((0 + h) * TM + wm * 128 + r32) * 8);
   const uint32_t code_b = (uint32_t)(((2 + h) * TM + wn * 64 + r32) * 8);
-  const uint32_t pc_a = h ? (uint32_t)L::ZERO : (uint32_t)(L::LEV + (wm * 128 + r32) * 16);
-  const uint32_t pc_b = h ? (uint32_t)L::ZERO : (uint32_t)(L::LEV + (TM + wn * 64 + r32) * 16);
+  const uint32_t pc_a = (uint32_t)(L::LEV + (wm * 128 + r32) * 16 + 8 * h);
+  const uint32_t pc_b = (uint32_t)(L::LEV + (TM + wn * 64 + r32) * 16 + 8 * h);
   if (nsteps > 0) {
     issue_stage<BC>(c, 0, 0);
     issue_stage<BC>(c, 1, 1);
@@ -403,14 +408,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) fb[t] = frag_at(decb, code_b + 256 * t, pc_b + 512 * t);
     // Tiles of a step in column order: u = 0..7 is (A tile u & 3, B tile u >> 2).
-    // The products of tile u+1 are issued before the fmas of tile u (two sets
+    // The products of tile u+1 are issued during the fmas of tile u (two sets
     // in flight), the next step's tile 0 during tile 7.  An operand is
     // reloaded for the next step after its last product was issued: fb[0]
     // after u = 2, fa[k] after u = 3 + k, fb[1] after u = 6 -- all after the
     // step's barrier, which follows the decode of the next step (u = 0).
-    floatx16 p[2], q;
-    p[0] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(fa[0].code, fb[0].code, floatx16{}, 0, 0, 0);
-    q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0].pc, fb[0].pc, floatx16{}, 0, 0, 0);
+    floatx16 p[2], q[2];
+    p[0] = level_product(fa[0], fb[0]);
+    q[0] = scale_product(fa[0], fb[0]);
 #pragma clang loop unroll(disable)
     for (int i = 0; i < nsteps; ++i) {
       if (i > 0 && (i & 7) == 0) issue_stage<BC>(c, (i >> 3) + 1, ((i >> 3) + 1) & 1);
@@ -420,19 +425,25 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
       const bool more = i + 1 < nsteps;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        // level product of the next tile first, then this tile's fmas, then
-        // the next tile's scale product (only the level products are
-        // double-buffered)
+        // the next tile's level product, the first half of this tile's fmas,
+        // the next tile's scale product, the second half (the scheduling
+        // barriers keep this order: left to itself the compiler moves the
+        // products to the end of the fmas, and the next tile's fmas then
+        // wait for them)
         const Frag& na = u + 1 < 8 ? fa[(u + 1) & 3] : fa[0];
         const Frag& nb = u + 1 < 8 ? fb[(u + 1) >> 2] : fb[0];
-        if (u + 1 < 8 || more)
-          p[(u + 1) & 1] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(na.code, nb.code, floatx16{}, 0, 0, 0);
+        if (u + 1 < 8 || more) p[(u + 1) & 1] = level_product(na, nb);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          acc[u & 3][u >> 2][r] = __builtin_fmaf(p[u & 1][r], q[r], acc[u & 3][u >> 2][r]);
+        for (int r = 0; r < 8; ++r)
+          acc[u & 3][u >> 2][r] = __builtin_fmaf(p[u & 1][r], q[u & 1][r], acc[u & 3][u >> 2][r]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (u + 1 < 8 || more) q[(u + 1) & 1] = scale_product(na, nb);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 8; r < 16; ++r)
+          acc[u & 3][u >> 2][r] = __builtin_fmaf(p[u & 1][r], q[u & 1][r], acc[u & 3][u >> 2][r]);
         asm volatile("" : "+v"(acc[u & 3][u >> 2]));   // the fmas stay here
-        if (u + 1 < 8 || more)
-          q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(na.pc, nb.pc, floatx16{}, 0, 0, 0);
         if (u == 0) decode_store<GRID, BC>(din, decb + (n & 1) * L::DEC, dop, drow);
         if (u == 1) {
           if (((i + 2) & 7) == 0) wait_vmcnt<0>();   // raw stage of step i+2 has landed
