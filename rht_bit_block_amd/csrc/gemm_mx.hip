@@ -48,7 +48,7 @@
 //     untouched, K step 128): FMT 0 = MXFP8 E4M3 codes; FMT 2 = E1M2 / INT4
 //     levels as FP6 E2M3 operands, written beforehand by k_fp6_expand into a
 //     caller workspace (a 32-byte slot per 32-element block: 24 bytes of
-//     6-bit fields, element j at bits 6j..6j+5, then 8 zero bytes), so the
+//     6-bit fields, element j at bits 6j..6j+5, then 8 unused bytes), so the
 //     matrix cores run at the FP6 rate with no decode in the main loop.
 //     (Packing two blocks into 48 bytes saves a quarter of the operand bytes
 //     but made the main loop slower on the GPU: the fragment of a block then
@@ -901,49 +901,77 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mxrow(GemmLaunch g) {
                 lane, acc, SCALED ? g.c_mul : 1.0f);
 }
 
-// E2M3 field of a 4-bit code (see the header): E1M2 sign-magnitude s|k ->
-// s<<5 | 2k; INT4 two's complement n -> sign<<5 | E2M3(|n|):
-// 1 -> 8, 2 -> 16, 3 -> 20, 4..7 -> 24, 26, 28, 30.  The nibble 8 (-8, no
-// code of the symmetric grid) has no E2M3 value and reads as -7.5 (63).
+// E2M3 fields of four 4-bit codes, one per byte (bits 0..3 of each byte in,
+// bits 0..5 out; see the header): E1M2 sign-magnitude s|k -> s<<5 | 2k, which
+// is 2 (c + (c & 8)); INT4 two's complement n -> sign<<5 | E2M3(|n|) through two
+// 8-entry byte tables (nibbles 0..7 and 8..15) and a per-byte select:
+// 1 -> 8, 2 -> 16, 3 -> 20, 4..7 -> 24, 26, 28, 30.  The nibble 8 (-8, no code
+// of the symmetric grid) has no E2M3 value and reads as -7.5 (63).
 template <int GRID>
-__device__ __forceinline__ uint32_t fp6_field(uint32_t c) {
+__device__ __forceinline__ uint32_t fp6_fields4(uint32_t c) {
   if constexpr (GRID == 0) {
-    return ((c & 8u) << 2) | ((c & 7u) << 1);
+    return (c + (c & 0x08080808u)) << 1;
   } else {
-    const uint32_t neg = c >> 3;
-    const uint32_t m = neg ? 16u - c : c;       // |n| in 0..8
-    const uint32_t f = m >= 4u ? 2u * m + 16u : (m >= 2u ? 4u * m + 8u : 8u * m);
-    return (neg << 5) | (m == 8u ? 31u : f);
+    const uint32_t m = c & 0x07070707u;
+    const uint32_t pos = __builtin_amdgcn_perm(0x1E1C1A18u, 0x14100800u, m);   // nibbles 0..7
+    const uint32_t neg = __builtin_amdgcn_perm(0x28303438u, 0x3A3C3E3Fu, m);   // nibbles 8..15
+    const uint32_t b = (c >> 3) & 0x01010101u;
+    const uint32_t sel = (b << 8) - b;   // 0xFF in the bytes of negative nibbles
+    return (neg & sel) | (pos & ~sel);
   }
+}
+
+// The eight fields of one code word (element j at bits 4j) as 48 bits,
+// element j at bits 6j: lo = bits 0..31, hi = bits 32..47.  Fields of the
+// even and odd elements come one per byte; [f0 f1 f4 f5] and [f2 f3 f6 f7]
+// are gathered by byte permutes, each byte pair closes up to 12 bits, and the
+// four 12-bit groups are laid end to end.
+template <int GRID>
+__device__ __forceinline__ void fp6_word(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const uint32_t fe = fp6_fields4<GRID>(w & 0x0F0F0F0Fu);          // f0 f2 f4 f6
+  const uint32_t fo = fp6_fields4<GRID>((w >> 4) & 0x0F0F0F0Fu);   // f1 f3 f5 f7
+  const uint32_t a = __builtin_amdgcn_perm(fo, fe, 0x06020400u);     // f0 f1 f4 f5
+  const uint32_t b = __builtin_amdgcn_perm(fo, fe, 0x07030501u);     // f2 f3 f6 f7
+  const uint32_t ga = (a & 0x003F003Fu) | ((a >> 2) & 0x0FC00FC0u);  // g01 | g45 << 16
+  const uint32_t gb = (b & 0x003F003Fu) | ((b >> 2) & 0x0FC00FC0u);  // g23 | g67 << 16
+  lo = (ga & 0xFFFu) | ((gb & 0xFFFu) << 12) | ((ga & 0x00FF0000u) << 8);
+  hi = (ga >> 24) | (gb >> 12);
 }
 
 // Six 32-bit words of 6-bit E2M3 fields (element j at bits 6j) from the
-// 32 code nibbles of one block.
+// 32 code nibbles of one block (four 48-bit runs).
 template <int GRID>
 __device__ __forceinline__ void fp6_block(const v4i& w, uint32_t (&o)[6]) {
-  uint32_t t[7] = {0, 0, 0, 0, 0, 0, 0};
+  uint32_t lo[4], hi[4];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const uint32_t f = fp6_field<GRID>(((uint32_t)w[j >> 3] >> (4 * (j & 7))) & 15u);
-    const int bit = 6 * j, wi = bit >> 5, sh = bit & 31;
-    t[wi] |= f << sh;
-    if (sh > 26) t[wi + 1] |= f >> (32 - sh);
-  }
-#pragma unroll
-  for (int i = 0; i < 6; ++i) o[i] = t[i];
+  for (int i = 0; i < 4; ++i) fp6_word<GRID>((uint32_t)w[i], lo[i], hi[i]);
+  o[0] = lo[0];
+  o[1] = hi[0] | (lo[1] << 16);
+  o[2] = (lo[1] >> 16) | (hi[1] << 16);
+  o[3] = lo[2];
+  o[4] = hi[2] | (lo[3] << 16);
+  o[5] = (lo[3] >> 16) | (hi[3] << 16);
 }
 
-// One thread per 32-element block: 16 code bytes in, one 32-byte slot out.
+// One thread per 32-element block: 16 code bytes in, the 24 field bytes of
+// its 32-byte slot out (the last 8 bytes of a slot are copied into LDS with
+// the rest but no fragment reads them, so they are left unwritten).  Blocks
+// 0 .. na-1 come from `a` (into `oa`), the rest from `b` (into `ob`): both
+// operands in one launch.
 template <int GRID>
-__global__ __launch_bounds__(256) void k_fp6_expand(const uint8_t* __restrict__ codes,
-                                                    uint8_t* __restrict__ out, int64_t nblk) {
+__global__ __launch_bounds__(256) void k_fp6_expand(const uint8_t* __restrict__ a,
+                                                    uint8_t* __restrict__ oa, int64_t na,
+                                                    const uint8_t* __restrict__ b,
+                                                    uint8_t* __restrict__ ob, int64_t nb) {
   const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t bk = (int64_t)blockIdx.x * 256 + threadIdx.x; bk < nblk; bk += stride) {
-    uint32_t a[6];
-    fp6_block<GRID>(*reinterpret_cast<const v4i*>(codes + bk * 16), a);
-    v4i* dst = reinterpret_cast<v4i*>(out + bk * 32);
-    dst[0] = v4i{(int)a[0], (int)a[1], (int)a[2], (int)a[3]};
-    dst[1] = v4i{(int)a[4], (int)a[5], 0, 0};
+  for (int64_t bk = (int64_t)blockIdx.x * 256 + threadIdx.x; bk < na + nb; bk += stride) {
+    const bool in_a = bk < na;
+    const int64_t k = in_a ? bk : bk - na;
+    uint32_t f[6];
+    fp6_block<GRID>(*reinterpret_cast<const v4i*>((in_a ? a : b) + k * 16), f);
+    uint8_t* dst = (in_a ? oa : ob) + k * 32;
+    *reinterpret_cast<v4i*>(dst) = v4i{(int)f[0], (int)f[1], (int)f[2], (int)f[3]};
+    *reinterpret_cast<v2i*>(dst + 16) = v2i{(int)f[4], (int)f[5]};
   }
 }
 
@@ -971,14 +999,14 @@ hipError_t launch_mxrow(const GemmLaunch& g, hipStream_t s) {
   return scaled ? launch_mxrow_s<FMT, false, true>(g, s) : launch_mxrow_s<FMT, false, false>(g, s);
 }
 
+// Both operands' codes (PA x K and PB x K) into FP6 slots at oa and ob.
 template <int GRID>
-hipError_t launch_fp6_expand(const uint8_t* codes, uint8_t* out, int64_t P, int64_t K,
-                             hipStream_t s) {
-  const int64_t nblk = P * (K / 32);
-  if (nblk == 0) return hipSuccess;
-  const int64_t blocks = std::min<int64_t>((nblk + 255) / 256, 8192);
-  hipLaunchKernelGGL((k_fp6_expand<GRID>), dim3((unsigned)blocks), dim3(256), 0, s, codes, out,
-                     nblk);
+hipError_t launch_fp6_expand(const GemmLaunch& g, uint8_t* oa, uint8_t* ob, hipStream_t s) {
+  const int64_t na = g.PA * (g.K / 32), nb = g.PB * (g.K / 32);
+  if (na + nb == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((na + nb + 255) / 256, 8192);
+  hipLaunchKernelGGL((k_fp6_expand<GRID>), dim3((unsigned)blocks), dim3(256), 0, s, g.a_codes,
+                     oa, na, g.b_codes, ob, nb);
   return hipGetLastError();
 }
 
@@ -1064,11 +1092,9 @@ hipError_t launch_gemm_mx6(const GemmLaunch& g, uint8_t* ws, hipStream_t s) {
   GemmLaunch x = g;
   x.a_codes = ws;
   x.b_codes = ws + ((g.PA * g.K + 255) / 256) * 256;
-  hipError_t e = g.grid == 0 ? launch_fp6_expand<0>(g.a_codes, ws, g.PA, g.K, s)
-                             : launch_fp6_expand<1>(g.a_codes, ws, g.PA, g.K, s);
-  if (e != hipSuccess) return e;
-  e = g.grid == 0 ? launch_fp6_expand<0>(g.b_codes, const_cast<uint8_t*>(x.b_codes), g.PB, g.K, s)
-                  : launch_fp6_expand<1>(g.b_codes, const_cast<uint8_t*>(x.b_codes), g.PB, g.K, s);
+  uint8_t* wb = const_cast<uint8_t*>(x.b_codes);
+  const hipError_t e = g.grid == 0 ? launch_fp6_expand<0>(g, ws, wb, s)
+                                   : launch_fp6_expand<1>(g, ws, wb, s);
   if (e != hipSuccess) return e;
   return launch_mxrow<2>(x, s);
 }
