@@ -117,8 +117,10 @@ __device__ __forceinline__ void fwht_inlane(float (&y)[W]) {
 // element: the lane with the bit clear keeps a + b, the other b - a, where
 // a is its own value and b the partner's.  Computed as b + (+-a) so both
 // lanes run the same instruction (IEEE: x - y == x + (-y), and a + b == b + a).
+// Three instructions per element (DPP move, sign, add); exact in every bit,
+// used when the rotated values are written out.
 template <int W, int CTRL>
-__device__ __forceinline__ void fwht_xlane(float (&y)[W], uint32_t negmask) {
+__device__ __forceinline__ void fwht_xlane_exact(float (&y)[W], uint32_t negmask) {
 #pragma unroll
   for (int i = 0; i < W; ++i) {
     const float b = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y[i]), CTRL, 0xF, 0xF, false));
@@ -127,12 +129,71 @@ __device__ __forceinline__ void fwht_xlane(float (&y)[W], uint32_t negmask) {
   }
 }
 
+// The same stage in one v_fmac_f32_dpp per element: y = y[L ^ m] * sgn + y,
+// with sgn = +1 in the lane with the bit clear and -1 in the other.  The
+// first lane gets a + b, the second -(b - a): the stage's result negated
+// (an fma with a factor +-1 rounds once, as the add; x - y == -(y - x) for
+// x != y).  If both lanes held their values negated, both results come out
+// negated too.  Only the sign of an exact zero can differ from the negated
+// result (a - a is +0 in either order), and no quotient, scale or code
+// depends on it.  The compiler does not fold a DPP move into an fma, so the
+// instruction is written out: sixteen elements per block, behind the two
+// wait states a DPP read needs after a VALU write of its source.
+#define UFP4_DPP_FMAC(i, ctrl) "v_fmac_f32_dpp %" #i ", %" #i ", %16 " ctrl " row_mask:0xf bank_mask:0xf\n\t"
+#define UFP4_DPP_FMAC16(ctrl)                                                               \
+  "s_nop 1\n\t" UFP4_DPP_FMAC(0, ctrl) UFP4_DPP_FMAC(1, ctrl) UFP4_DPP_FMAC(2, ctrl)     \
+      UFP4_DPP_FMAC(3, ctrl) UFP4_DPP_FMAC(4, ctrl) UFP4_DPP_FMAC(5, ctrl)                \
+          UFP4_DPP_FMAC(6, ctrl) UFP4_DPP_FMAC(7, ctrl) UFP4_DPP_FMAC(8, ctrl)            \
+              UFP4_DPP_FMAC(9, ctrl) UFP4_DPP_FMAC(10, ctrl) UFP4_DPP_FMAC(11, ctrl)      \
+                  UFP4_DPP_FMAC(12, ctrl) UFP4_DPP_FMAC(13, ctrl) UFP4_DPP_FMAC(14, ctrl) \
+                      UFP4_DPP_FMAC(15, ctrl)
+template <int W, int M>
+__device__ __forceinline__ void fwht_xlane(float (&y)[W], uint32_t negmask) {
+  static_assert(W % 16 == 0 && (M == 1 || M == 2), "16-element blocks; partner lane ^ 1 or ^ 2");
+  const float sgn = __uint_as_float(0x3F800000u | negmask);
+#pragma unroll
+  for (int b = 0; b < W; b += 16) {
+#define UFP4_DPP_OPS                                                                       \
+  : "+v"(y[b]), "+v"(y[b + 1]), "+v"(y[b + 2]), "+v"(y[b + 3]), "+v"(y[b + 4]),            \
+    "+v"(y[b + 5]), "+v"(y[b + 6]), "+v"(y[b + 7]), "+v"(y[b + 8]), "+v"(y[b + 9]),        \
+    "+v"(y[b + 10]), "+v"(y[b + 11]), "+v"(y[b + 12]), "+v"(y[b + 13]), "+v"(y[b + 14]),   \
+    "+v"(y[b + 15])                                                                        \
+  : "v"(sgn)
+    if constexpr (M == 1)
+      asm(UFP4_DPP_FMAC16("quad_perm:[1,0,3,2]") UFP4_DPP_OPS);
+    else
+      asm(UFP4_DPP_FMAC16("quad_perm:[2,3,0,1]") UFP4_DPP_OPS);
+#undef UFP4_DPP_OPS
+  }
+}
+#undef UFP4_DPP_FMAC16
+#undef UFP4_DPP_FMAC
+
 // All butterfly stages of n (lanes of a chunk are adjacent: n / W of them).
+// Returns the lane's sign state: 0x80000000 if its values come out negated
+// (an odd number of fused cross-lane stages in which its bit was set), else
+// 0.  `exact` (uniform across the launch: the rotated values are written
+// out) takes the three-instruction stages, whose results are the rotated
+// values in every bit, zero signs included (sign state 0).
 template <int W, int N>
-__device__ __forceinline__ void fwht(float (&y)[W], uint32_t neg1, uint32_t neg2) {
+__device__ __forceinline__ uint32_t fwht(float (&y)[W], uint32_t neg1, uint32_t neg2,
+                                         bool exact) {
   fwht_inlane<W, N>(y);
-  if constexpr (N >= 2 * W) fwht_xlane<W, 0xB1>(y, neg1);  // quad_perm [1,0,3,2]: lane ^ 1
-  if constexpr (N >= 4 * W) fwht_xlane<W, 0x4E>(y, neg2);  // quad_perm [2,3,0,1]: lane ^ 2
+  uint32_t sig = 0u;
+  if constexpr (N >= 2 * W) {
+    if (exact) {
+      fwht_xlane_exact<W, 0xB1>(y, neg1);                             // lane ^ 1
+      if constexpr (N >= 4 * W) fwht_xlane_exact<W, 0x4E>(y, neg2);   // lane ^ 2
+      return 0u;
+    }
+    fwht_xlane<W, 1>(y, neg1);
+    sig ^= neg1;
+    if constexpr (N >= 4 * W) {
+      fwht_xlane<W, 2>(y, neg2);
+      sig ^= neg2;
+    }
+  }
+  return sig;
 }
 
 template <int W>
@@ -333,8 +394,11 @@ __device__ __forceinline__ void diag_accumulate(DiagLds* d, uint32_t nib, float 
             (unsigned long long)(long long)efx);
 }
 
+// `sig` is the lane's sign state from fwht: when set, y holds the negated
+// rotated values, and the quotients use the negated divisor (or reciprocal),
+// which gives the same RN(y / s): rounding is symmetric.
 template <int W, int B, int GRID, int RND, bool FOLD, bool DIAG = false>
-__device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64_t e0,
+__device__ __forceinline__ void quantize_1d(const float (&y)[W], uint32_t sig, float c, uint64_t e0,
                                             uint64_t seed, uint32_t stream, uint8_t* codes_out,
                                             void* scales_out, DiagLds* diag = nullptr) {
   constexpr float qmax = Grid<GRID>::qmax;
@@ -363,7 +427,7 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
       // max |u| = RN(M m_T) since rounding is monotone (m_T = 1: unchanged)
       M = __fmul_rn(M, c);
       const int e = pow2_exponent<GRID>(M);
-      const float inv = ldexpf(1.0f, -e);   // exact power of two
+      const float inv = __uint_as_float(__float_as_uint(ldexpf(1.0f, -e)) ^ sig);   // +-2^-e
 #pragma unroll
       for (int j = 0; j < B; ++j) v[j] = __fmul_rn(__fmul_rn(y[blk * B + j], c), inv);
       if (e == 127) {   // only there can |v| exceed qmax
@@ -380,6 +444,8 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
       const bool zero = s == 0.0f;
       const float sd = zero ? 1.0f : s;
       const float r = zero ? 0.0f : __fdiv_rn(1.0f, sd);
+      const float sdn = __uint_as_float(__float_as_uint(sd) ^ sig);   // divisor and
+      const float rn = __uint_as_float(__float_as_uint(r) ^ sig);     // reciprocal, signed
       // Markstein: with r = RN(1/s) and q within an ulp of y/s, the fma
       // remainder is exact and RN(q + e r) = RN(y/s).  Preconditions: no
       // underflow of q or of the remainder.
@@ -393,14 +459,14 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
 #pragma unroll
       for (int j = 0; j < B; ++j) {
         const float yy = y[blk * B + j];
-        const float q = __fmul_rn(yy, r);
-        const float e = __fmaf_rn(-q, sd, yy);
-        v[j] = __fmaf_rn(e, r, q);
+        const float q = __fmul_rn(yy, rn);
+        const float e = __fmaf_rn(-q, sdn, yy);
+        v[j] = __fmaf_rn(e, rn, q);
         if constexpr (kTinyExact) slow |= fabsf(yy) < thr;
       }
       if (__builtin_expect(slow, 0)) {
 #pragma unroll
-        for (int j = 0; j < B; ++j) v[j] = zero ? 0.0f : __fdiv_rn(y[blk * B + j], sd);
+        for (int j = 0; j < B; ++j) v[j] = zero ? 0.0f : __fdiv_rn(y[blk * B + j], sdn);
       }
     }
     if constexpr (FOLD) {
@@ -410,9 +476,10 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
 #pragma unroll
         for (int j = 0; j < B; ++j) M2 = fmaxf(M2, fabsf(__fmul_rn(y[blk * B + j], c)));
         s = __fdiv_rn(M2, qmax);
+        const float s2 = __uint_as_float(__float_as_uint(s) ^ sig);
 #pragma unroll
         for (int j = 0; j < B; ++j)
-          v[j] = s == 0.0f ? 0.0f : __fdiv_rn(__fmul_rn(y[blk * B + j], c), s);
+          v[j] = s == 0.0f ? 0.0f : __fdiv_rn(__fmul_rn(y[blk * B + j], c), s2);
       } else {
         s = __fmul_rn(s, c);   // exact: power of two, no underflow
       }
@@ -471,29 +538,31 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], float c, uint64
   }
 }
 
+// The rotated values of a lane (un-negated by its sign state).
 template <int W>
-__device__ __forceinline__ void store_rotated(float* dst, const float (&y)[W]) {
+__device__ __forceinline__ void store_rotated(float* dst, const float (&y)[W], uint32_t sig) {
+  auto f = [&](int i) { return __uint_as_float(__float_as_uint(y[i]) ^ sig); };
 #pragma unroll
   for (int i = 0; i < W; i += 4)
-    *reinterpret_cast<float4*>(dst + i) = make_float4(y[i], y[i + 1], y[i + 2], y[i + 3]);
+    *reinterpret_cast<float4*>(dst + i) = make_float4(f(i), f(i + 1), f(i + 2), f(i + 3));
 }
 
 // After the butterflies: normalize (or fold), optionally store the rotated
 // values, quantize.  scales_out points at the lane's first scale (fp32 or
 // E8M0 byte, by RND bit 1).
 template <int W, int B, int N, int GRID, int RND, class Q>
-__device__ __forceinline__ void finish_lane(float (&y)[W], const Q& q, uint64_t e0,
+__device__ __forceinline__ void finish_lane(float (&y)[W], uint32_t sig, const Q& q, uint64_t e0,
                                             uint8_t* codes_out, void* scales_out) {
   if constexpr (Rht<N>::fold && (RND & 2) == 0) {
     if (q.rotated == nullptr) {
-      quantize_1d<W, B, GRID, RND, true>(y, Rht<N>::c, e0, q.sr_seed, q.sr_stream, codes_out,
-                                         scales_out);
+      quantize_1d<W, B, GRID, RND, true>(y, sig, Rht<N>::c, e0, q.sr_seed, q.sr_stream,
+                                         codes_out, scales_out);
       return;
     }
   }
   if constexpr (N > 1) scale_by<W>(y, q.cn);
-  if (q.rotated) store_rotated<W>(q.rotated + e0, y);
-  quantize_1d<W, B, GRID, RND, false>(y, q.tmul, e0, q.sr_seed, q.sr_stream, codes_out,
+  if (q.rotated) store_rotated<W>(q.rotated + e0, y, sig);
+  quantize_1d<W, B, GRID, RND, false>(y, sig, q.tmul, e0, q.sr_seed, q.sr_stream, codes_out,
                                       scales_out);
 }
 
@@ -534,9 +603,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantLaunch q, FastDiv 
     }
     float y[W];
     unpack<W>(w, pm, y);
-    fwht<W, N>(y, neg1, neg2);
+    const uint32_t sig = fwht<W, N>(y, neg1, neg2, q.rotated != nullptr);
     const uint64_t e0 = (uint64_t)p * K + k0;
-    finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, q, e0, code_ptr<GRID>(q.codes, e0),
+    finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, sig, q, e0, code_ptr<GRID>(q.codes, e0),
                                     scale_at<RND>(q.scales, (uint64_t)p * (K / B) + k0 / B));
   }
 }
@@ -586,15 +655,15 @@ __global__ __launch_bounds__(kThreads) void k_quant_diag(QuantLaunch q, FastDiv 
     }
     float y[W];
     unpack<W>(w, pm, y);
-    fwht<W, N>(y, neg1, neg2);
+    const uint32_t sig = fwht<W, N>(y, neg1, neg2, false);
     const uint64_t e0 = (uint64_t)p * K + k0;
     if constexpr (Rht<N>::fold && (RND & 2) == 0) {
-      quantize_1d<W, B, GRID, RND, true, true>(y, Rht<N>::c, e0, q.sr_seed, q.sr_stream,
+      quantize_1d<W, B, GRID, RND, true, true>(y, sig, Rht<N>::c, e0, q.sr_seed, q.sr_stream,
                                                nullptr, nullptr, &d);
     } else {
       if constexpr (N > 1) scale_by<W>(y, q.cn);
-      quantize_1d<W, B, GRID, RND, false, true>(y, q.tmul, e0, q.sr_seed, q.sr_stream, nullptr,
-                                                nullptr, &d);
+      quantize_1d<W, B, GRID, RND, false, true>(y, sig, q.tmul, e0, q.sr_seed, q.sr_stream,
+                                                nullptr, nullptr, &d);
     }
   }
   __syncthreads();
@@ -714,11 +783,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantLaunch q) {
     }
     float y[W];
     unpack<W>(w, pm, y);
-    fwht<W, N>(y, neg1, neg2);
+    const uint32_t sig = fwht<W, N>(y, neg1, neg2, q.rotated != nullptr);
     const int64_t p = p0 + col;
     const int64_t k = k0 + kr;
     const uint64_t e0 = (uint64_t)C * seg0 + (uint64_t)p * L + k;   // global draw index
-    finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, q, e0, code_ptr<GRID>(q.codes, e0),
+    finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, sig, q, e0, code_ptr<GRID>(q.codes, e0),
                                     scale_at<RND>(q.scales, e0 / B));
   }
 }
@@ -864,9 +933,9 @@ __device__ __forceinline__ void dual_quantize(const QuantLaunch& q, const RowSid
       }
       float y[W];
       unpack<W>(w, pm, y);
-      fwht<W, N>(y, neg1, neg2);
+      const uint32_t sig = fwht<W, N>(y, neg1, neg2, q.rotated != nullptr);
       const uint64_t e0 = (uint64_t)C * d.seg0 + (uint64_t)(d.p0 + col) * d.L + (d.k0 + kr);
-      finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, q, e0, code_ptr<GRID>(q.codes, e0),
+      finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, sig, q, e0, code_ptr<GRID>(q.codes, e0),
                                                    scale_at<RND>(q.scales, e0 / B));
     }
   }
@@ -891,9 +960,9 @@ __device__ __forceinline__ void dual_quantize(const QuantLaunch& q, const RowSid
       }
       float y[W];
       unpack<W>(w, pm, y);
-      fwht<W, N>(y, neg1, neg2);
+      const uint32_t sig = fwht<W, N>(y, neg1, neg2, rside.rotated != nullptr);
       const uint64_t e0 = (uint64_t)(d.seg0 + d.k0 + row) * (uint64_t)C + (uint64_t)(d.p0 + c0);
-      finish_lane<W, B, N, GRID, RND, RowSide>(y, rside, e0, code_ptr<GRID>(rside.codes, e0),
+      finish_lane<W, B, N, GRID, RND, RowSide>(y, sig, rside, e0, code_ptr<GRID>(rside.codes, e0),
                                                scale_at<RND>(rside.scales, e0 / B));
     }
   }
@@ -972,7 +1041,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows_2d(QuantLaunch q, uint3
         w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
       }
       unpack<W>(w, pm, y);
-      fwht<W, N>(y, 0u, 0u);
+      fwht<W, N>(y, 0u, 0u, true);   // N <= W: no cross-lane stage, sign state 0
       if constexpr (N > 1) scale_by<W>(y, q.cn);
 #pragma unroll
       for (int j = 0; j < W; ++j) M = fmaxf(M, fabsf(y[j]));
@@ -985,7 +1054,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows_2d(QuantLaunch q, uint3
     const int e = pow2_exponent<GRID>(M);
     const float inv = ldexpf(1.0f, -e);  // exact power of two (2^-127 is a subnormal)
     const uint64_t e0 = (uint64_t)p * K + k0;
-    if (q.rotated) store_rotated<W>(q.rotated + e0, y);
+    if (q.rotated) store_rotated<W>(q.rotated + e0, y, 0u);
     uint32_t rw[W / 2];
     if constexpr (RND == 1) sr_draws<W>(e0, q.sr_seed, q.sr_stream, rw);
     uint32_t packed[W / 8];

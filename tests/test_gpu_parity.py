@@ -99,6 +99,29 @@ def test_quant_edge_values(grid, rnd, n):
     compare_quant(bits, 0, cfg2)
 
 
+@pytest.mark.parametrize("n,b", [(64, 16), (128, 16), (64, 32), (128, 32)])
+@pytest.mark.parametrize("grid", GRIDS)
+@pytest.mark.parametrize("rnd", [U.UFP4_RTNE, U.UFP4_SR])
+def test_quant_fused_stages(n, b, grid, rnd):
+    """Without the rotated output the cross-lane butterflies run fused (one
+    DPP fma per element, values negated in half the lanes, the quotients
+    taken with the negated divisor): codes and scales stay bit-exact, for
+    fp32 and power-of-two scales, two-level scaling, rows and columns, and
+    the edge values (exact zeros, where only the sign of zero could differ)."""
+    _print_case("fused", n, b, grid, rnd)
+    rows = rand_bits(40, 384, seed=n + b + grid)
+    cols = rand_bits(384, 72, seed=n + b + grid + 1)
+    cfg = U.make_cfg(grid, rnd, U.UFP4_SCALE_F32, 1, b, n, sign_seed=3000 + n, sr_seed=79, sr_stream=5)
+    compare_quant(rows, 0, cfg, with_rotated=False)
+    compare_quant(cols, 1, cfg, with_rotated=False)
+    compare_quant(_edge_bits(), 0, cfg, with_rotated=False)
+    if b == 32:
+        pow2 = U.make_cfg(grid, rnd, U.UFP4_SCALE_POW2, 1, 32, n, sign_seed=3100 + n, sr_seed=80)
+        compare_quant(rows, 0, pow2, with_rotated=False)
+        compare_quant(cols, 1, pow2, with_rotated=False)
+        compare_quant(rows, 0, pow2.copy(tensor_scale=0.37), with_rotated=False)
+
+
 def test_quant_empty():
     x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
     q, _ = U.ufp4_rht_quant(x, 0, U.make_cfg())
