@@ -36,10 +36,11 @@
 // elements does not change the sum, so a K half holds its even elements then
 // its odd ones, the same for A and B.
 //
-// Pipeline of step i (its fragments in registers): the decode of step i+1
-// during the first tile (its raw inputs were read from LDS during step i-1),
-// one barrier, then the fragments of step i+1 are read as registers free up,
-// so the LDS reads of a step are hidden under the tiles of the one before.
+// Pipeline of step i (its fragments in registers): the decode of step i+2
+// during the first tile (its raw inputs were read from LDS during step i-1)
+// into one of four decoded buffers, a barrier on even steps, then the
+// fragments of step i+1 are read as registers free up, so the LDS reads of a
+// step are hidden under the tiles of the one before.
 // Inside a step the 16-wide kernel walks its 8 tiles column by column; both
 // products are double-buffered, and the products of tile t+1 are issued
 // around the first half of tile t's fmas (level product, 8 fmas, scale
@@ -176,7 +177,7 @@ template <int BC> struct Layout {
   static constexpr int LEV = 2 * 2 * TM * 8;
   static constexpr int PCS = 2 * TM * 16;
   static constexpr int DEC = LEV + PCS;
-  static constexpr int TOTAL = NRAW * RAW + 2 * DEC;
+  static constexpr int TOTAL = NRAW * RAW + 4 * DEC;   // 160 KiB for 1 x 16 blocks
 };
 
 struct RdCtx {
@@ -400,7 +401,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
     wait_vmcnt<L::VMEM>();
     __syncthreads();
     decode_store<GRID, BC>(decode_load<BC>(lds, dop, drow, 0), decb, dop, drow);
-    DecIn dnx = decode_load<BC>(lds, dop, drow, 1);   // step 1 (stage 0 has landed)
+    decode_store<GRID, BC>(decode_load<BC>(lds, dop, drow, 1), decb + L::DEC, dop, drow);
+    DecIn dnx = decode_load<BC>(lds, dop, drow, 2);   // step 2 (stage 0 has landed)
     __syncthreads();
     Frag fa[4], fb[2];
 #pragma unroll
@@ -411,17 +413,23 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
     // The products of tile u+1 are issued during the fmas of tile u (two sets
     // in flight), the next step's tile 0 during tile 7.  An operand is
     // reloaded for the next step after its last product was issued: fb[0]
-    // after u = 2, fa[k] after u = 3 + k, fb[1] after u = 6 -- all after the
-    // step's barrier, which follows the decode of the next step (u = 0).
+    // after u = 2, fa[k] after u = 3 + k, fb[1] after u = 6.
+    // Four decoded buffers, step m in buffer m % 4: step i decodes step i+2
+    // (u = 0) and reads the fragments of step i+1 (u >= 3); a barrier on even
+    // steps only (u = 1).  Between the decode of step m (step m-2) and its
+    // fragment reads (step m-1) lies the barrier of m-2 or m-1, whichever is
+    // even; between the last reads of a buffer (step m-5) and its next decode
+    // (step m-2) the barrier of m-4 or m-3.  A raw stage is waited for on the
+    // even step before its first decode load (step 8 s - 4 for stage s).
     floatx16 p[2], q[2];
     p[0] = level_product(fa[0], fb[0]);
     q[0] = scale_product(fa[0], fb[0]);
 #pragma clang loop unroll(disable)
     for (int i = 0; i < nsteps; ++i) {
       if (i > 0 && (i & 7) == 0) issue_stage<BC>(c, (i >> 3) + 1, ((i >> 3) + 1) & 1);
-      const int n = i + 1;   // decoded during this step (past the end: unused)
+      const int n = i + 2;   // decoded during this step (past the end: unused)
       const DecIn din = dnx;   // step n's raw inputs, loaded during the step before
-      const uint8_t* dn = decb + (n & 1) * L::DEC;
+      const uint8_t* dn = decb + ((i + 1) & 3) * L::DEC;   // fragments of step i+1
       const bool more = i + 1 < nsteps;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -444,12 +452,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
         for (int r = 8; r < 16; ++r)
           acc[u & 3][u >> 2][r] = __builtin_fmaf(p[u & 1][r], q[u & 1][r], acc[u & 3][u >> 2][r]);
         asm volatile("" : "+v"(acc[u & 3][u >> 2]));   // the fmas stay here
-        if (u == 0) decode_store<GRID, BC>(din, decb + (n & 1) * L::DEC, dop, drow);
+        if (u == 0) decode_store<GRID, BC>(din, decb + (n & 3) * L::DEC, dop, drow);
         if (u == 1) {
-          if (((i + 2) & 7) == 0) wait_vmcnt<0>();   // raw stage of step i+2 has landed
-          __syncthreads();
-          // raw inputs of step i+2 (its stage has landed for every wave)
-          dnx = decode_load<BC>(lds + (((i + 2) >> 3) & 1) * L::RAW, dop, drow, (i + 2) & 7);
+          if ((i & 1) == 0) {   // uniform: every wave takes the same barriers
+            if (((i + 4) & 7) == 0) wait_vmcnt<0>();   // raw stage of step i+4 has landed
+            __syncthreads();
+          }
+          // raw inputs of step i+3 (its stage has landed for every wave)
+          dnx = decode_load<BC>(lds + (((i + 3) >> 3) & 1) * L::RAW, dop, drow, (i + 3) & 7);
         }
         if (u == 3) fb[0] = frag_at(dn, code_b, pc_b);
         if (u >= 4) fa[u - 4] = frag_at(dn, code_a + 256 * (u - 4), pc_a + 512 * (u - 4));
