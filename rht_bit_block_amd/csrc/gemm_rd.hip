@@ -118,17 +118,21 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 // (each rounding leaves an exact fp32 residual).  K slots 0..7, A side x B
 // side:
 //   A: s0 s0 s0 s1 s1 s2 0 0        B: t0 t1 t2 t0 t1 t0 0 0
-// sum = s0 (t0 + t1 + t2) + s1 (t0 + t1) + s2 t0.
-template <int OP>
-__device__ __forceinline__ uint4 scale_pieces(float s) {
-  const uint32_t p00 = pk_bf16(s, s);
-  const float r1 = s - __uint_as_float(p00 << 16);
-  const uint32_t p11 = pk_bf16(r1, r1);
-  const float r2 = r1 - __uint_as_float(p11 << 16);
-  if constexpr (OP == 0)
-    return make_uint4(p00, __builtin_amdgcn_perm(p11, p00, 0x05040100u), pk_bf16(r1, r2), 0u);
-  else
-    return make_uint4(pk_bf16(s, r1), pk_bf16(r2, s), pk_bf16(r1, s), 0u);
+// sum = s0 (t0 + t1 + t2) + s1 (t0 + t1) + s2 t0.  Both sides' slot pairs are
+// byte permutes of [s0 s0] and [s1 s2]; `op` (uniform across the wave) picks
+// the selectors, so a wave converts only its own side.
+__device__ __forceinline__ uint4 scale_pieces(float s, int op) {
+  const uint32_t u0 = pk_bf16(s, s);                        // [s0 s0]
+  const float r1 = s - __uint_as_float(u0 << 16);
+  const uint32_t u1 = pk_bf16(r1, r1);
+  const float r2 = r1 - __uint_as_float(u1 << 16);
+  const uint32_t g = pk_bf16(r1, r2);                       // [s1 s2]
+  // bytes of {g, u0}: 0-3 = s0 s0, 4-5 = s1, 6-7 = s2
+  const uint32_t sel0 = op ? 0x05040100u : 0x01000100u;    // t0 t1 | s0 s0
+  const uint32_t sel1 = op ? 0x01000706u : 0x05040100u;    // t2 t0 | s0 s1
+  const uint32_t sel2 = op ? 0x01000504u : 0x07060504u;    // t1 t0 | s1 s2
+  return make_uint4(__builtin_amdgcn_perm(g, u0, sel0), __builtin_amdgcn_perm(g, u0, sel1),
+                    __builtin_amdgcn_perm(g, u0, sel2), 0u);
 }
 
 // --- direct HBM -> LDS loads -----------------------------------------------
@@ -233,7 +237,7 @@ __device__ __forceinline__ void decode_store(const DecIn& d, uint8_t* dec, int o
   *reinterpret_cast<uint2*>(dec + ((op * 2 + 0) * TM + row) * 8) = levels8<GRID>(d.w.x);
   *reinterpret_cast<uint2*>(dec + ((op * 2 + 1) * TM + row) * 8) = levels8<GRID>(d.w.y);
   *reinterpret_cast<uint4*>(dec + L::LEV + (op * TM + row) * 16) =
-      op ? scale_pieces<1>(d.s) : scale_pieces<0>(d.s);
+      scale_pieces(d.s, op);
 }
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -522,7 +526,7 @@ __device__ __forceinline__ void decode_store32(const DecIn32& d, uint8_t* dec, i
   *reinterpret_cast<uint2*>(dec + (((op * 2 + 1) * 2 + 0) * TM + row) * 8) = levels8<GRID>(d.w.z);
   *reinterpret_cast<uint2*>(dec + (((op * 2 + 1) * 2 + 1) * TM + row) * 8) = levels8<GRID>(d.w.w);
   *reinterpret_cast<uint4*>(dec + L::LEV + (op * TM + row) * 16) =
-      op ? scale_pieces<1>(d.s) : scale_pieces<0>(d.s);
+      scale_pieces(d.s, op);
 }
 
 struct Frag32 {
