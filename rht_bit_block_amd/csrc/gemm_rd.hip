@@ -15,9 +15,8 @@
 // bf16 pieces of the scales: s = s0 + s1 + s2 exactly (s0 = bf16(s),
 // s1 = bf16(s - s0), s2 = s - s0 - s1), and the eight K slots pair six of the
 // nine cross products (all but s1 t2, s2 t1, s2 t2, each below 2^-25 of s t).
-// In the 16-wide kernel that MFMA is v_mfma_f32_32x32x8_bf16 (lane half h
-// supplies slots 4h .. 4h + 3: two registers per operand); k_gemm_rd32 uses
-// v_mfma_f32_32x32x16_bf16 with the slots in the lower lane half.  C += P * S
+// That MFMA is v_mfma_f32_32x32x8_bf16: lane half h supplies slots 4h .. 4h + 3
+// (two registers per operand).  C += P * S
 // is one fp32 fma per element.  The result differs from the exact one by fp32
 // rounding only (a few 2^-24 relative per step).
 //
@@ -493,12 +492,11 @@ hipError_t launch_rd(const GemmLaunch& g, hipStream_t s) {
 // MFMAs (K halves 0-15 and 16-31 of the block), one scale-product MFMA and one
 // set of 16 fmas per tile: half the fmas and three quarters of the MFMAs of
 // two 16-wide steps.  Decoded buffer: levels [op][16-wide half][K half][row] x
-// 8 E4M3, scale pieces [op][row] x 8 bf16, zero slots at ZERO + 512 t.
+// 8 E4M3, scale pieces [op][row] x 8 bf16 (lane half h reads pieces 4h..4h+3).
 struct Layout32 {
   static constexpr int LEV = 2 * 2 * 2 * TM * 8;
   static constexpr int PCS = 2 * TM * 16;
-  static constexpr int ZERO = LEV + PCS;
-  static constexpr int DEC = ZERO + 3 * 512 + 16;
+  static constexpr int DEC = LEV + PCS;
   static constexpr int TOTAL = NRAW * Layout<32>::RAW + 2 * DEC;
 };
 
@@ -531,7 +529,7 @@ __device__ __forceinline__ void decode_store32(const DecIn32& d, uint8_t* dec, i
 
 struct Frag32 {
   long c0, c1;    // E4M3 levels of the two 16-wide halves
-  bf16x8 pc;      // scale pieces (lower lane half) or zeros (upper half)
+  short4_t pc;    // the lane half's four scale pieces (K = 8 scale product)
 };
 
 // code_off: the first half's levels; the second half's are 2 TM x 8 bytes on.
@@ -539,8 +537,12 @@ __device__ __forceinline__ Frag32 frag32_at(const uint8_t* dec, uint32_t code_of
   Frag32 f;
   f.c0 = *reinterpret_cast<const long*>(dec + code_off);
   f.c1 = *reinterpret_cast<const long*>(dec + code_off + 2 * TM * 8);
-  f.pc = *reinterpret_cast<const bf16x8*>(dec + pc_off);
+  f.pc = *reinterpret_cast<const short4_t*>(dec + pc_off);
   return f;
+}
+
+__device__ __forceinline__ floatx16 scale_product32(const Frag32& a, const Frag32& b) {
+  return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a.pc, b.pc, floatx16{}, 0, 0, 0);
 }
 
 template <int GRID>
@@ -555,9 +557,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd32(GemmLaunch g) {
   const int wave = ts.wave, wm = ts.wm, wn = ts.wn;
   const int64_t K = ts.o.K;
   uint8_t* decb = lds + NRAW * L::RAW;   // two decoded buffers
-
-  if (tid < 8)
-    *reinterpret_cast<uint4*>(decb + (tid >> 2) * D::DEC + D::ZERO + (tid & 3) * 512) = make_uint4(0, 0, 0, 0);
 
   floatx16 acc[4][2];
 #pragma unroll
@@ -574,53 +573,75 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd32(GemmLaunch g) {
   // fragment offsets in a decoded buffer; tile t adds 256 t (levels), 512 t (pieces)
   const uint32_t code_a = (uint32_t)(((0 + h) * TM + wm * 128 + r32) * 8);
   const uint32_t code_b = (uint32_t)(((4 + h) * TM + wn * 64 + r32) * 8);
-  const uint32_t pc_a = h ? (uint32_t)D::ZERO : (uint32_t)(D::LEV + (wm * 128 + r32) * 16);
-  const uint32_t pc_b = h ? (uint32_t)D::ZERO : (uint32_t)(D::LEV + (TM + wn * 64 + r32) * 16);
+  const uint32_t pc_a = (uint32_t)(D::LEV + (wm * 128 + r32) * 16 + 8 * h);
+  const uint32_t pc_b = (uint32_t)(D::LEV + (TM + wn * 64 + r32) * 16 + 8 * h);
   if (nsteps > 0) {
     issue_stage<32>(c, 0, 0);
     issue_stage<32>(c, 1, 1);
     wait_vmcnt<L::VMEM>();
     __syncthreads();
     decode_store32<GRID>(decode_load32(lds, dop, drow, 0), decb, dop, drow);
+    DecIn32 dnx = decode_load32(lds, dop, drow, 1);   // step 1 (stage 0 has landed)
     __syncthreads();
-    Frag32 fa[4], fb[2], fbn[2];
+    Frag32 fa[4], fb[2];
 #pragma unroll
     for (int t = 0; t < 4; ++t) fa[t] = frag32_at(decb, code_a + 256 * t, pc_a + 512 * t);
 #pragma unroll
     for (int t = 0; t < 2; ++t) fb[t] = frag32_at(decb, code_b + 256 * t, pc_b + 512 * t);
-    // Step i as in the 16-wide kernel: decode of step i+1 during tiles 0-1,
-    // barrier, then step i+1's fragments as registers free up.  A raw stage
-    // holds 4 steps: stage s is issued at step 4 (s - 1) and waited for two
-    // steps later.
+    // As in the 16-wide kernel: tiles in column order (u = 0..7 is A tile
+    // u & 3, B tile u >> 2), the products of tile u+1 issued during the fmas
+    // of tile u (level product of the first half, 8 fmas, scale product, 4
+    // fmas, level product of the second half chained on the first, 4 fmas),
+    // each fragment reloaded after its last product; decode of step i+1 at
+    // u = 0 (inputs read one step ahead), one barrier per step at u = 1.  A
+    // raw stage holds 4 steps: stage s is issued at step 4 (s - 1) and waited
+    // for at step 4 s - 2.
+    floatx16 p[2], q[2];
+    p[0] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(fa[0].c0, fb[0].c0, floatx16{}, 0, 0, 0);
+    q[0] = scale_product32(fa[0], fb[0]);
+    p[0] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(fa[0].c1, fb[0].c1, p[0], 0, 0, 0);
 #pragma clang loop unroll(disable)
     for (int i = 0; i < nsteps; ++i) {
       if (i > 0 && (i & 3) == 0) issue_stage<32>(c, (i >> 2) + 1, ((i >> 2) + 1) & 1);
       const int n = i + 1;   // decoded during this step (past the end: unused)
-      const DecIn32 din = decode_load32(lds + ((n >> 2) & 1) * L::RAW, dop, drow, n & 3);
+      const DecIn32 din = dnx;   // step n's raw inputs, loaded during the step before
       const uint8_t* dn = decb + (n & 1) * D::DEC;
+      const bool more = i + 1 < nsteps;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const Frag32& a = fa[t >> 1];
-        const Frag32& b = fb[t & 1];
-        floatx16 p = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a.c0, b.c0, floatx16{}, 0, 0, 0);
-        const floatx16 q = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.pc, b.pc, floatx16{}, 0, 0, 0);
-        p = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a.c1, b.c1, p, 0, 0, 0);
+      for (int u = 0; u < 8; ++u) {
+        const Frag32& na = u + 1 < 8 ? fa[(u + 1) & 3] : fa[0];
+        const Frag32& nb = u + 1 < 8 ? fb[(u + 1) >> 2] : fb[0];
+        const bool go = u + 1 < 8 || more;
+        if (go) p[(u + 1) & 1] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(na.c0, nb.c0, floatx16{}, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          acc[t >> 1][t & 1][r] = __builtin_fmaf(p[r], q[r], acc[t >> 1][t & 1][r]);
-        asm volatile("" : "+v"(acc[t >> 1][t & 1]));   // the fmas stay here
-        if (t == 0) decode_store32<GRID>(din, decb + (n & 1) * D::DEC, dop, drow);
-        if (t == 1) {
+        for (int r = 0; r < 8; ++r)
+          acc[u & 3][u >> 2][r] = __builtin_fmaf(p[u & 1][r], q[u & 1][r], acc[u & 3][u >> 2][r]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (go) q[(u + 1) & 1] = scale_product32(na, nb);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 8; r < 12; ++r)
+          acc[u & 3][u >> 2][r] = __builtin_fmaf(p[u & 1][r], q[u & 1][r], acc[u & 3][u >> 2][r]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (go) p[(u + 1) & 1] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(na.c1, nb.c1, p[(u + 1) & 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 12; r < 16; ++r)
+          acc[u & 3][u >> 2][r] = __builtin_fmaf(p[u & 1][r], q[u & 1][r], acc[u & 3][u >> 2][r]);
+        asm volatile("" : "+v"(acc[u & 3][u >> 2]));   // the fmas stay here
+        if (u == 0) decode_store32<GRID>(din, decb + (n & 1) * D::DEC, dop, drow);
+        if (u == 1) {
           if (((i + 2) & 3) == 0) wait_vmcnt<0>();   // raw stage of step i+2 has landed
           __syncthreads();
-#pragma unroll
-          for (int u = 0; u < 2; ++u) fbn[u] = frag32_at(dn, code_b + 256 * u, pc_b + 512 * u);
+          // raw inputs of step i+2 (its stage has landed for every wave)
+          dnx = decode_load32(lds + (((i + 2) >> 2) & 1) * L::RAW, dop, drow, (i + 2) & 3);
         }
-        if (t & 1) fa[t >> 1] = frag32_at(dn, code_a + 256 * (t >> 1), pc_a + 512 * (t >> 1));
+        if (u == 3) fb[0] = frag32_at(dn, code_b, pc_b);
+        if (u >= 4) fa[u - 4] = frag32_at(dn, code_a + 256 * (u - 4), pc_a + 512 * (u - 4));
+        if (u == 7) fb[1] = frag32_at(dn, code_b + 256, pc_b + 512);
         __builtin_amdgcn_sched_barrier(0);
       }
-      fb[0] = fbn[0];
-      fb[1] = fbn[1];
     }
   }
 
