@@ -60,12 +60,12 @@ _GEMM_SRC = ("gemm_rd.hip", "gemm_epilogue.h", "ufp4_internal.h")
 _QUANT_SRC = ("quant_core.h", "ufp4_internal.h")
 MEASURED_TRAFFIC = {
     # (workload, kernel): (sources, sha256[:16] of them, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    ("moe16", "fprop"): (_GEMM_SRC, "a898200a9b9a3604", 1563544.4, 1577805.0),
-    ("moe16", "dgrad"): (_GEMM_SRC, "a898200a9b9a3604", 722950.9, 5258967.6),
-    ("moe16", "wgrad"): (_GEMM_SRC, "a898200a9b9a3604", 1226897.8, 491572.5),
-    ("moe16", "quant_x"): (_QUANT_SRC, "39c06c7ebd22c317", 1314817.0, 2307972.7),
-    ("moe16", "quant_w"): (_QUANT_SRC, "39c06c7ebd22c317", 123150.1, 217184.2),
-    ("moe16", "quant_dy"): (_QUANT_SRC, "39c06c7ebd22c317", 395272.0, 700987.1),
+    ("moe16", "fprop"): (_GEMM_SRC, "ddf176223547331f", 1564365.1, 1577685.9),
+    ("moe16", "dgrad"): (_GEMM_SRC, "ddf176223547331f", 704706.0, 5258975.6),
+    ("moe16", "wgrad"): (_GEMM_SRC, "ddf176223547331f", 1226695.6, 491603.1),
+    ("moe16", "quant_x"): (_QUANT_SRC, "39c06c7ebd22c317", 1314816.9, 2309025.2),
+    ("moe16", "quant_w"): (_QUANT_SRC, "39c06c7ebd22c317", 123150.2, 217117.6),
+    ("moe16", "quant_dy"): (_QUANT_SRC, "39c06c7ebd22c317", 395270.8, 700406.1),
 }
 
 
