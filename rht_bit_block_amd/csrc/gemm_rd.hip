@@ -36,7 +36,7 @@
 // its odd ones, the same for A and B.
 //
 // Pipeline of step i (its fragments in registers): the decode of step i+2
-// during the first tile (its raw inputs were read from LDS during step i-1)
+// during the first two tiles (its raw inputs were read from LDS during step i-1)
 // into one of four decoded buffers, a barrier on even steps, then the
 // fragments of step i+1 are read as registers free up, so the LDS reads of a
 // step are hidden under the tiles of the one before.
@@ -418,12 +418,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
     // reloaded for the next step after its last product was issued: fb[0]
     // after u = 2, fa[k] after u = 3 + k, fb[1] after u = 6.
     // Four decoded buffers, step m in buffer m % 4: step i decodes step i+2
-    // (u = 0) and reads the fragments of step i+1 (u >= 3); a barrier on even
-    // steps only (u = 1).  Between the decode of step m (step m-2) and its
-    // fragment reads (step m-1) lies the barrier of m-2 or m-1, whichever is
-    // even; between the last reads of a buffer (step m-5) and its next decode
-    // (step m-2) the barrier of m-4 or m-3.  A raw stage is waited for on the
-    // even step before its first decode load (step 8 s - 4 for stage s).
+    // (levels at u = 0, scale pieces at u = 1, so the decode's VALU work is
+    // split over two tiles) and reads the fragments of step i+1 (u >= 3); a
+    // barrier on even steps only (u = 2).  Between the decode of step m (step
+    // m-2) and its fragment reads (step m-1) lies the barrier of m-2 or m-1,
+    // whichever is even; between the last reads of a buffer (step m-5) and its
+    // next decode (step m-2) the barrier of m-4 or m-3.  A raw stage is waited
+    // for on the even step before its first decode load (step 8 s - 4 for
+    // stage s).
     floatx16 p[2], q[2];
     p[0] = level_product(fa[0], fb[0]);
     q[0] = scale_product(fa[0], fb[0]);
@@ -455,8 +457,16 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
         for (int r = 8; r < 16; ++r)
           acc[u & 3][u >> 2][r] = __builtin_fmaf(p[u & 1][r], q[u & 1][r], acc[u & 3][u >> 2][r]);
         asm volatile("" : "+v"(acc[u & 3][u >> 2]));   // the fmas stay here
-        if (u == 0) decode_store<GRID, BC>(din, decb + (n & 3) * L::DEC, dop, drow);
+        if (u == 0) {   // levels of step i+2 (scale pieces during the next tile)
+          uint8_t* dec = decb + (n & 3) * L::DEC;
+          *reinterpret_cast<uint2*>(dec + ((dop * 2 + 0) * TM + drow) * 8) = levels8<GRID>(din.w.x);
+          *reinterpret_cast<uint2*>(dec + ((dop * 2 + 1) * TM + drow) * 8) = levels8<GRID>(din.w.y);
+        }
         if (u == 1) {
+          uint8_t* dec = decb + (n & 3) * L::DEC;
+          *reinterpret_cast<uint4*>(dec + L::LEV + (dop * TM + drow) * 16) = scale_pieces(din.s, dop);
+        }
+        if (u == 2) {
           if ((i & 1) == 0) {   // uniform: every wave takes the same barriers
             if (((i + 4) & 7) == 0) wait_vmcnt<0>();   // raw stage of step i+4 has landed
             __syncthreads();
