@@ -123,6 +123,8 @@ def parse():
                    help="input buffer sets rotated across steps (each > the 256 MB MALL)")
     p.add_argument("--only-step", action="store_true",
                    help="time the step and its kernels only (no context sections, no CPU oracle)")
+    p.add_argument("--serial", action="store_true",
+                   help="run the step's calls in order on one stream (no WGRAD overlap)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-context", action="store_true", help="skip every context section")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -136,11 +138,18 @@ class MoELayer:
     calls with prebuilt ctypes arguments, for each input buffer set.  Used for
     the 16-expert share (the step) and the 64-expert Zipf layer (context)."""
 
-    def __init__(self, U, torch, wl, grid, n, b, nsets=1, dual=True):
+    def __init__(self, U, torch, wl, grid, n, b, nsets=1, dual=True, overlap=False):
         import workloads
         self.U, self.torch = U, torch
         self.stream = torch.cuda.current_stream()
         cs = ctypes.c_void_p(self.stream.cuda_stream)
+        # WGRAD needs only the quantized copies, so with overlap it runs on a
+        # second stream (default priority) beside FPROP and DGRAD: the long
+        # WGRAD workgroups and the short ones of the other two fill each
+        # other's last, partly empty rounds of the 256 CUs
+        self.side = torch.cuda.Stream() if overlap else None
+        ss = ctypes.c_void_p(self.side.cuda_stream) if overlap else None
+        self.side_calls = []
         X, W, dYp = wl.tensors["X"], wl.tensors["W"], wl.tensors["dY_perm"]
         self.off = [int(v) for v in wl.meta["offsets"].tolist()]
         self.counts = [int(c) for c in wl.meta["counts"]]
@@ -223,7 +232,11 @@ class MoELayer:
                 args = (ctypes.byref(qa), ctypes.byref(qb), E, goff,
                         ctypes.c_void_p(out.data_ptr()), out.stride(0), cs)
                 calls.append((name, _raw(U, name, getattr(lib, f"ufp4_gemm_{name}_grouped"), args)))
+                if name == "wgrad" and overlap:
+                    self.side_calls.append(_raw(U, name, lib.ufp4_gemm_wgrad_grouped, args[:-1] + (ss,)))
             self.calls.append(calls)
+        if overlap:
+            self.ev_fork, self.ev_join = torch.cuda.Event(), torch.cuda.Event()
         tokens = sum(self.counts)
         self.tokens = tokens
         f = 2.0 * tokens * F * H                 # unpadded token rows
@@ -238,8 +251,20 @@ class MoELayer:
         self.bpe = bpe
 
     def step(self, i):
-        for _, fn in self.calls[i % len(self.calls)]:
-            fn()
+        calls = self.calls[i % len(self.calls)]
+        if self.side is None:
+            for _, fn in calls:
+                fn()
+            return
+        for name, fn in calls:
+            if name == "fprop":   # every quantization is enqueued: fork WGRAD
+                self.ev_fork.record(self.stream)
+                self.side.wait_event(self.ev_fork)
+                self.side_calls[i % len(self.side_calls)]()
+            if name != "wgrad":
+                fn()
+        self.ev_join.record(self.side)
+        self.stream.wait_event(self.ev_join)
 
     def names(self):
         return [c[0] for c in self.calls[0]]
@@ -301,6 +326,7 @@ class DenseLayer:
         import workloads
         self.U, self.torch = U, torch
         self.stream = torch.cuda.current_stream()
+        self.side = None   # every GEMM of this layer fills whole rounds of the CUs
         cs = ctypes.c_void_p(self.stream.cuda_stream)
         base = workloads.config2("cuda")
         self.sets = [base.tensors] + [{k: v.clone() for k, v in base.tensors.items()}
@@ -754,7 +780,8 @@ def main():
 
     # ---- the step: the 16-expert MoE layer --------------------------------
     wl = workloads.config4("cuda")
-    layer = MoELayer(U, torch, wl, U.UFP4_INT4, 128, 16, nsets=max(1, args.sets))
+    layer = MoELayer(U, torch, wl, U.UFP4_INT4, 128, 16, nsets=max(1, args.sets),
+                     overlap=not args.serial)
     del wl
     torch.cuda.synchronize()
     print(f"[bench] step: 16-expert layer, {layer.T} padded token rows, "
@@ -794,7 +821,8 @@ def main():
                                                    ("e2m1", U.UFP4_E2M1))}),
             ("fprop_256", lambda: fprop_256(U, torch)),
             ("moe64_zipf_e1m2_1x32_n32", lambda: layer_report(
-                torch, MoELayer(U, torch, workloads.config3("cuda"), U.UFP4_E1M2, 32, 32, nsets=2),
+                torch, MoELayer(U, torch, workloads.config3("cuda"), U.UFP4_E1M2, 32, 32, nsets=2,
+                                overlap=not args.serial),
                 10, 3, "moe64")[0]),
             ("square_blocks", lambda: square_blocks(U, torch)),
             ("rht_cost", lambda: rht_cost(U, torch)),
@@ -830,7 +858,10 @@ def main():
                                "dY) + grouped FPROP/DGRAD/WGRAD",
                    "global_batch": 32768, "seq_len": None, "parallelism": "single GPU",
                    "experts": step_info["experts"], "tokens_x_topk": step_info["tokens_x_topk"],
-                   "padded_rows": step_info["padded_rows"], "input_sets": max(1, args.sets)},
+                   "padded_rows": step_info["padded_rows"], "input_sets": max(1, args.sets),
+                   "schedule": ("one stream, calls in order" if args.serial else
+                                "quantizations, then WGRAD on a second stream beside FPROP and "
+                                "DGRAD; the step ends when both streams are done")},
         "roofline": roof,
         "quant": {"GB/s": round(quant_gbps, 1), "frac_hbm_peak": round(quant_gbps / HBM_PEAK_GBPS, 4),
                   "ms": round(quant_ms, 4), "bytes_per_elem": round(layer_bpe, 4)},
