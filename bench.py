@@ -123,8 +123,9 @@ def parse():
                    help="input buffer sets rotated across steps (each > the 256 MB MALL)")
     p.add_argument("--only-step", action="store_true",
                    help="time the step and its kernels only (no context sections, no CPU oracle)")
-    p.add_argument("--serial", action="store_true",
-                   help="run the step's calls in order on one stream (no WGRAD overlap)")
+    p.add_argument("--overlap", action="store_true",
+                   help="run WGRAD on a second stream beside FPROP and DGRAD (default: the "
+                        "step's calls in order on one stream)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-context", action="store_true", help="skip every context section")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -144,9 +145,10 @@ class MoELayer:
         self.stream = torch.cuda.current_stream()
         cs = ctypes.c_void_p(self.stream.cuda_stream)
         # WGRAD needs only the quantized copies, so with overlap it runs on a
-        # second stream (default priority) beside FPROP and DGRAD: the long
-        # WGRAD workgroups and the short ones of the other two fill each
-        # other's last, partly empty rounds of the 256 CUs
+        # second stream (default priority) beside FPROP and DGRAD, and the
+        # workgroups of each fill the others' partly empty last rounds.  Off by
+        # default: the GEMMs split their own half-empty last rounds, and with
+        # that the one-stream order measured as fast or faster
         self.side = torch.cuda.Stream() if overlap else None
         ss = ctypes.c_void_p(self.side.cuda_stream) if overlap else None
         self.side_calls = []
@@ -781,7 +783,7 @@ def main():
     # ---- the step: the 16-expert MoE layer --------------------------------
     wl = workloads.config4("cuda")
     layer = MoELayer(U, torch, wl, U.UFP4_INT4, 128, 16, nsets=max(1, args.sets),
-                     overlap=not args.serial)
+                     overlap=args.overlap)
     del wl
     torch.cuda.synchronize()
     print(f"[bench] step: 16-expert layer, {layer.T} padded token rows, "
@@ -822,7 +824,7 @@ def main():
             ("fprop_256", lambda: fprop_256(U, torch)),
             ("moe64_zipf_e1m2_1x32_n32", lambda: layer_report(
                 torch, MoELayer(U, torch, workloads.config3("cuda"), U.UFP4_E1M2, 32, 32, nsets=2,
-                                overlap=not args.serial),
+                                overlap=args.overlap),
                 10, 3, "moe64")[0]),
             ("square_blocks", lambda: square_blocks(U, torch)),
             ("rht_cost", lambda: rht_cost(U, torch)),
@@ -859,9 +861,9 @@ def main():
                    "global_batch": 32768, "seq_len": None, "parallelism": "single GPU",
                    "experts": step_info["experts"], "tokens_x_topk": step_info["tokens_x_topk"],
                    "padded_rows": step_info["padded_rows"], "input_sets": max(1, args.sets),
-                   "schedule": ("one stream, calls in order" if args.serial else
-                                "quantizations, then WGRAD on a second stream beside FPROP and "
-                                "DGRAD; the step ends when both streams are done")},
+                   "schedule": ("quantizations, then WGRAD on a second stream beside FPROP and "
+                                "DGRAD; the step ends when both streams are done" if args.overlap
+                                else "one stream, calls in order")},
         "roofline": roof,
         "quant": {"GB/s": round(quant_gbps, 1), "frac_hbm_peak": round(quant_gbps / HBM_PEAK_GBPS, 4),
                   "ms": round(quant_ms, 4), "bytes_per_elem": round(layer_bpe, 4)},

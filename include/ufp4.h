@@ -234,7 +234,11 @@ int ufp4_dequant(const ufp4_qtensor* q, float* out, int64_t ldo, void* stream);
  *   dgrad: A = dY (M x N),     B = W^T (K_in x N)    -> dX [M][K_in]
  *   wgrad: A = dY^T (N x M),   B = X^T (K_in x M)    -> dW [N][K_in]
  * Operands must agree on K, grid, scale_mode, rht_n and sign_seed
- * (UFP4_ERR_MISMATCH otherwise).  Block shapes may differ between operands. */
+ * (UFP4_ERR_MISMATCH otherwise).  Block shapes may differ between operands.
+ * With fp32 block scales, a launch whose last round of workgroups (one per
+ * compute unit) would be at most half full computes those tiles as two K
+ * halves added into C, zeroed first by the same call (two addends on zero:
+ * the same result whatever the timing).  This and the grouped forms. */
 int ufp4_gemm_fprop(const ufp4_qtensor* X, const ufp4_qtensor* W, float* Y, int64_t ldy,
                     void* stream);
 int ufp4_gemm_dgrad(const ufp4_qtensor* dY, const ufp4_qtensor* Wt, float* dX, int64_t ldx,

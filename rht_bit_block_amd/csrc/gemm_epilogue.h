@@ -107,6 +107,26 @@ __device__ __forceinline__ void store_c_plain(float* c_tile, int64_t ldc, int ro
   }
 }
 
+// Add a wave's partial sums into C (one of the two K halves of a split tile;
+// C was zeroed before the launch).  Hardware fp32 atomic adds: with exactly
+// two addends on an exact zero the result is the same in either order.
+template <int NI, int NJ>
+__device__ __forceinline__ void add_c(float* c_tile, int64_t ldc, int rows_valid, int cols_valid,
+                                      int r0, int c0, int lane, const c_floatx16 (&acc)[NI][NJ]) {
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int col = c0 + j * 32 + (lane & 31);
+    if (col >= cols_valid) continue;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = r0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < rows_valid) unsafeAtomicAdd(c_tile + (int64_t)row * ldc + col, acc[i][j][r]);
+      }
+  }
+}
+
 // m: a factor on every element of C (two-level scaling: the operands'
 // tensor factors; 1 otherwise, an exact multiply).
 template <int NI, int NJ>

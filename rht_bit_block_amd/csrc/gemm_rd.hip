@@ -56,6 +56,16 @@
 // gives each XCD a contiguous range of tiles in grouped order, so the tiles
 // resident at once on an XCD share operand strips in its L2.  Rows past the
 // operand read as zeros (buffer bound).
+//
+// Last round: one workgroup per CU fits (160 KiB of LDS), so a launch of T
+// tiles runs in rounds of CU-count workgroups.  When the last round would be
+// at most half full and the tiles are long (1024 K elements or more on
+// average), each of its tiles is computed by two workgroups, one per half of
+// K (split on a 128-element stage boundary), so the round keeps every CU
+// busy for half as long.  Both halves add their fp32 partial sums into C,
+// which a fill kernel has zeroed: with two addends on an exact zero the sum
+// is the same in either order, so the result does not depend on timing (it
+// is the rounding of P_first + P_second instead of one running sum).
 #include "ufp4_internal.h"
 #include "gemm_epilogue.h"
 
@@ -320,6 +330,8 @@ __device__ __forceinline__ Operands resolve(const GemmLaunch& g, int b, int& tm,
 struct TileCtx {
   Operands o;
   int64_t row0, col0, rows_a, rows_b;
+  int64_t klen;   // K elements this workgroup sums (all of K unless split)
+  int half;       // -1, or the K half of a split tile
   RdCtx c;
   int wave, wm, wn;
 };
@@ -329,26 +341,42 @@ __device__ __forceinline__ TileCtx tile_ctx(const GemmLaunch& g, const uint8_t* 
   using L = Layout<BC>;
   TileCtx t;
   int tm, tn;
-  t.o = resolve(g, blockIdx.x, tm, tn);
+  // workgroups past split_first come in pairs: slot split_first + j / 2, K half j % 2
+  int slot = blockIdx.x;
+  t.half = -1;
+  if (slot >= g.split_first) {
+    const int j = slot - g.split_first;
+    slot = g.split_first + (j >> 1);
+    t.half = j & 1;
+  }
+  t.o = resolve(g, slot, tm, tn);
   const int lane = tid & 63;
   t.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   t.wm = t.wave >> 2;
   t.wn = t.wave & 3;
-  const int64_t K = t.o.K;
+  const int64_t K = t.o.K;   // the operands' row length
+  int64_t kbeg = 0;
+  t.klen = K;                // this workgroup's part of it
+  if (t.half >= 0) {
+    const int64_t kh = (K / (2 * KST)) * KST;   // a stage boundary
+    kbeg = t.half ? kh : 0;
+    t.klen = t.half ? K - kh : kh;
+  }
   t.row0 = (int64_t)tm * TM;
   t.col0 = (int64_t)tn * TN;
   t.rows_a = t.o.a_rows - t.row0 < TM ? t.o.a_rows - t.row0 : TM;
   t.rows_b = t.o.b_rows - t.col0 < TN ? t.o.b_rows - t.col0 : TN;
   const uint32_t rs = (uint32_t)(K / 2), srs = (uint32_t)(K / BC) * 4u;
+  const uint32_t cb = (uint32_t)(kbeg / 2), sb = (uint32_t)(kbeg / BC) * 4u;   // K offsets
   RdCtx& c = t.c;
   c.wave = t.wave;
-  c.nst = (int)((K + KST - 1) / KST);
-  c.ra = rsrc4(t.o.a_codes + t.row0 * rs, (uint32_t)(t.rows_a * rs));
-  c.rb = rsrc4(t.o.b_codes + t.col0 * rs, (uint32_t)(t.rows_b * rs));
-  c.rsa = rsrc4(reinterpret_cast<const uint8_t*>(t.o.a_scales) + t.row0 * srs,
-                (uint32_t)(t.rows_a * srs));
-  c.rsb = rsrc4(reinterpret_cast<const uint8_t*>(t.o.b_scales) + t.col0 * srs,
-                (uint32_t)(t.rows_b * srs));
+  c.nst = (int)((t.klen + KST - 1) / KST);
+  c.ra = rsrc4(t.o.a_codes + t.row0 * rs + cb, (uint32_t)(t.rows_a * rs) - cb);
+  c.rb = rsrc4(t.o.b_codes + t.col0 * rs + cb, (uint32_t)(t.rows_b * rs) - cb);
+  c.rsa = rsrc4(reinterpret_cast<const uint8_t*>(t.o.a_scales) + t.row0 * srs + sb,
+                (uint32_t)(t.rows_a * srs) - sb);
+  c.rsb = rsrc4(reinterpret_cast<const uint8_t*>(t.o.b_scales) + t.col0 * srs + sb,
+                (uint32_t)(t.rows_b * srs) - sb);
   c.lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds;
   // codes: lane i of wave load q -> row 32 w + 16 q + i / 4, the chunk whose
   // swizzled slot is i % 4
@@ -378,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
   const TileCtx ts = tile_ctx<BC>(g, lds, tid);
   const RdCtx& c = ts.c;
   const int wave = ts.wave, wm = ts.wm, wn = ts.wn;
-  const int64_t K = ts.o.K;
+  const int64_t K = ts.klen;
   uint8_t* decb = lds + NRAW * L::RAW;   // two decoded buffers
 
   floatx16 acc[4][2];
@@ -482,17 +510,20 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd(GemmLaunch g) {
     }
   }
 
-  store_c<4, 2>(ts.o.c + ts.row0 * g.ldc + ts.col0, g.ldc, (int)ts.rows_a, (int)ts.rows_b,
-                wm * 128, wn * 64, lane, acc);
+  float* ct = ts.o.c + ts.row0 * g.ldc + ts.col0;
+  if (ts.half < 0)
+    store_c<4, 2>(ct, g.ldc, (int)ts.rows_a, (int)ts.rows_b, wm * 128, wn * 64, lane, acc);
+  else
+    add_c<4, 2>(ct, g.ldc, (int)ts.rows_a, (int)ts.rows_b, wm * 128, wn * 64, lane, acc);
 }
 
 template <int GRID, int BC>
-hipError_t launch_rd(const GemmLaunch& g, hipStream_t s) {
+hipError_t launch_rd(const GemmLaunch& g, int grid, hipStream_t s) {
   constexpr int bytes = Layout<BC>::TOTAL;
   static std::atomic<uint64_t> lds_set{0};
   const hipError_t e = set_lds_limit((const void*)k_gemm_rd<GRID, BC>, bytes, lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gemm_rd<GRID, BC>), dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
+  hipLaunchKernelGGL((k_gemm_rd<GRID, BC>), dim3(grid), dim3(kThreads), bytes, s, g);
   return hipGetLastError();
 }
 
@@ -565,7 +596,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd32(GemmLaunch g) {
   const TileCtx ts = tile_ctx<32>(g, lds, tid);
   const RdCtx& c = ts.c;
   const int wave = ts.wave, wm = ts.wm, wn = ts.wn;
-  const int64_t K = ts.o.K;
+  const int64_t K = ts.klen;
   uint8_t* decb = lds + NRAW * L::RAW;   // two decoded buffers
 
   floatx16 acc[4][2];
@@ -655,18 +686,48 @@ __global__ __launch_bounds__(kThreads) void k_gemm_rd32(GemmLaunch g) {
     }
   }
 
-  store_c<4, 2>(ts.o.c + ts.row0 * g.ldc + ts.col0, g.ldc, (int)ts.rows_a, (int)ts.rows_b,
-                wm * 128, wn * 64, lane, acc);
+  float* ct = ts.o.c + ts.row0 * g.ldc + ts.col0;
+  if (ts.half < 0)
+    store_c<4, 2>(ct, g.ldc, (int)ts.rows_a, (int)ts.rows_b, wm * 128, wn * 64, lane, acc);
+  else
+    add_c<4, 2>(ct, g.ldc, (int)ts.rows_a, (int)ts.rows_b, wm * 128, wn * 64, lane, acc);
 }
 
 template <int GRID>
-hipError_t launch_rd32(const GemmLaunch& g, hipStream_t s) {
+hipError_t launch_rd32(const GemmLaunch& g, int grid, hipStream_t s) {
   constexpr int bytes = Layout32::TOTAL;
   static std::atomic<uint64_t> lds_set{0};
   const hipError_t e = set_lds_limit((const void*)k_gemm_rd32<GRID>, bytes, lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_gemm_rd32<GRID>), dim3(g.total_tiles), dim3(kThreads), bytes, s, g);
+  hipLaunchKernelGGL((k_gemm_rd32<GRID>), dim3(grid), dim3(kThreads), bytes, s, g);
   return hipGetLastError();
+}
+
+// Zeros the C regions of the split tiles (slots split_first .. total_tiles-1).
+__global__ __launch_bounds__(256) void k_zero_split(GemmLaunch g) {
+  int tm, tn;
+  const Operands o = resolve(g, g.split_first + (int)blockIdx.x, tm, tn);
+  const int64_t row0 = (int64_t)tm * TM, col0 = (int64_t)tn * TN;
+  const int rows = (int)(o.a_rows - row0 < TM ? o.a_rows - row0 : TM);
+  const int cols = (int)(o.b_rows - col0 < TN ? o.b_rows - col0 : TN);
+  float* c = o.c + row0 * g.ldc + col0;
+  for (int r = (int)threadIdx.x >> 6; r < rows; r += 4)
+    for (int k = (int)threadIdx.x & 63; k < cols; k += 64) c[(int64_t)r * g.ldc + k] = 0.0f;
+}
+
+// Compute units of the current device (cached per device id).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 }  // namespace
@@ -677,16 +738,30 @@ bool gemm_rd_supported(const GemmLaunch& g) {
          (g.K / 2) * (int64_t)TM <= INT32_MAX;
 }
 
-hipError_t launch_gemm_rd(const GemmLaunch& g, hipStream_t s) {
-  if (g.total_tiles == 0) return hipSuccess;
+hipError_t launch_gemm_rd(const GemmLaunch& g0, hipStream_t s) {
+  if (g0.total_tiles == 0) return hipSuccess;
+  // split the tiles of a last round that is at most half full (long tiles only:
+  // 1024 K elements or more on average, so the zero fill is a small cost)
+  GemmLaunch g = g0;
+  const int T = g.total_tiles, cus = cu_count();
+  const int rem = cus > 0 ? T % cus : 0;
+  const int64_t kavg = g.mode == 2 ? (g.off[g.ngroups] - g.off[0]) / g.ngroups : g.K;
+  g.split_first = rem > 0 && rem <= cus / 2 && kavg >= 1024 ? T - rem : T;
+  const int nsplit = T - g.split_first;
+  if (nsplit > 0) {
+    hipLaunchKernelGGL(k_zero_split, dim3(nsplit), dim3(256), 0, s, g);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int grid = T + nsplit;
   const int key = g.grid * 2 + (g.a_bc == 32 ? 1 : 0);
   switch (key) {
-    case 0: return launch_rd<0, 16>(g, s);
-    case 1: return launch_rd32<0>(g, s);
-    case 2: return launch_rd<1, 16>(g, s);
-    case 3: return launch_rd32<1>(g, s);
-    case 4: return launch_rd<2, 16>(g, s);
-    default: return launch_rd32<2>(g, s);
+    case 0: return launch_rd<0, 16>(g, grid, s);
+    case 1: return launch_rd32<0>(g, grid, s);
+    case 2: return launch_rd<1, 16>(g, grid, s);
+    case 3: return launch_rd32<1>(g, grid, s);
+    case 4: return launch_rd<2, 16>(g, grid, s);
+    default: return launch_rd32<2>(g, grid, s);
   }
 }
 

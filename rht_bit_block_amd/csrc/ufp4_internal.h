@@ -148,6 +148,10 @@ struct GemmLaunch {
   int32_t tile_start[kMaxGroups + 1];
   int32_t total_tiles;
   float c_mul;      // factor on C: the operands' tensor factors (two-level scaling), 1 if none
+  // fp32-scale kernels only, set by their launcher: tile slots from
+  // split_first on are each computed by two workgroups, one per half of K,
+  // whose partial sums are added into a zeroed C (total_tiles: no split)
+  int32_t split_first;
 };
 
 // Raises a kernel's dynamic LDS limit to `bytes` once per kernel and device

@@ -618,6 +618,82 @@ def test_gemm_fp32_scale_accuracy(grid, bc, rnd):
 
 
 # ---------------------------------------------------------------------------
+# Last-round split of the fp32-scale GEMMs: when a launch's last round of
+# workgroups (one per CU) is at most half full and tiles average 1024 or more
+# K elements, each tile of that round is computed by two workgroups, one per
+# K half, whose partial sums are added into C zeroed beforehand.  Here every
+# tile is in the last round (fewer tiles than CUs).  Against the oracle at the
+# fp32-scale bar, halves of unequal length (K = 1152), both kernels (1 x 16,
+# 1 x 32), grouped launches with an empty expert, and bit-identical results
+# on a second call.
+# ---------------------------------------------------------------------------
+def _assert_split(tiles, kavg):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rem = tiles % cus
+    assert 0 < rem <= cus // 2 and kavg >= 1024, "the shape does not take the split path"
+
+
+@pytest.mark.parametrize("grid,bc,K", [(U.UFP4_INT4, 16, 1152), (U.UFP4_E1M2, 32, 1024),
+                                       (U.UFP4_E2M1, 16, 1024)])
+def test_gemm_split_last_round(grid, bc, K):
+    _print_case("split last round", grid, bc, K)
+    PA, PB = 700, 300                                     # 3 x 2 ragged tiles
+    _assert_split(3 * 2, K)
+    cfg = U.make_cfg(grid, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, bc, 16, sign_seed=41)
+    qa, ra = compare_quant(_wide_range_bits(PA, K, 300 + grid, bc), 0, cfg, with_rotated=False)
+    qb, rb = compare_quant(_wide_range_bits(PB, K, 400 + grid, bc), 0, cfg, with_rotated=False)
+    C1 = U.ufp4_gemm_fprop(qa, qb)
+    C2 = U.ufp4_gemm_fprop(qa, qb)
+    assert torch.equal(C1, C2)
+    ref = O.gemm_ref(oracle_dequant64(ra, cfg), oracle_dequant64(rb, cfg))
+    err = O.rel_fro(C1.cpu().numpy(), ref)
+    print(f"  rel. Frobenius error {err:.3e}", flush=True)
+    assert err <= F32_SCALE_TOL, err
+
+
+def test_grouped_split_last_round():
+    _print_case("grouped split last round")
+    cfg = U.make_cfg(U.UFP4_INT4, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=43)
+    # FPROP grouped along rows: experts of 384 and 256 tokens, F = 160 (3 tiles), K = 1024
+    off, H, F = [0, 384, 640], 1024, 160
+    _assert_split(3, H)
+    qx, rx = compare_quant(rand_bits(off[-1], H, 50), 0, cfg, with_rotated=False)
+    qw, rw = compare_quant(rand_bits(2 * F, H, 51), 0, cfg, with_rotated=False)
+    Y1 = U.ufp4_gemm_fprop_grouped(qx, qw, off)
+    Y2 = U.ufp4_gemm_fprop_grouped(qx, qw, off)
+    assert torch.equal(Y1, Y2)
+    Y = Y1.cpu().numpy()
+    dx, dw = oracle_dequant64(rx, cfg), oracle_dequant64(rw, cfg)
+    for g in range(2):
+        ref = O.gemm_ref(dx[off[g]:off[g + 1]], dw[g * F:(g + 1) * F])
+        assert O.rel_fro(Y[off[g]:off[g + 1]], ref) <= F32_SCALE_TOL, g
+    # WGRAD grouped along K: experts of 1280, 256, 0 and 2560 tokens (1024 on
+    # average), N = 96, H = 160 (one tile per expert)
+    off, N, H = [0, 1280, 1536, 1536, 4096], 96, 160
+    _assert_split(4, off[-1] // 4)
+    cs = U.make_cfg(U.UFP4_INT4, U.UFP4_SR, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=44, sr_seed=5,
+                    sr_stream=1)
+    cr = U.make_cfg(U.UFP4_INT4, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=44)
+    tdy, tx = rand_bits(off[-1], N, 52), rand_bits(off[-1], H, 53)
+    qdyt = U.ufp4_rht_quant_segmented(dev_bf16(tdy), off, cs)
+    qxt = U.ufp4_rht_quant_segmented(dev_bf16(tx), off, cr)
+    dW = torch.full((4 * N, H), 7.0, dtype=torch.float32, device="cuda")
+    U.ufp4_gemm_wgrad_grouped(qdyt, qxt, off, out=dW)
+    dW2 = U.ufp4_gemm_wgrad_grouped(qdyt, qxt, off)
+    assert torch.equal(dW, dW2)
+    dW = dW.cpu().numpy()
+    r_dyt = O.quantize_segmented(tdy, off, spec_of(cs))
+    r_xt = O.quantize_segmented(tx, off, spec_of(cr))
+    for g in range(4):
+        blk = dW[g * N:(g + 1) * N]
+        if off[g + 1] == off[g]:
+            assert np.all(blk == 0.0), g
+            continue
+        ref = O.gemm_ref(oracle_dequant64(r_dyt[g], cs), oracle_dequant64(r_xt[g], cr))
+        assert O.rel_fro(blk, ref) <= F32_SCALE_TOL, g
+
+
+# ---------------------------------------------------------------------------
 # fp32-scale GEMMs whose K ends inside a 128-wide raw stage (and K of a single
 # step), for 16- and 32-wide K steps; ragged row tiles on both operands.
 # ---------------------------------------------------------------------------
