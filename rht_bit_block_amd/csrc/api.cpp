@@ -7,6 +7,7 @@
 // [2DFP4] = "Stable FP4 Training via Transposition-Invariant Block
 // Quantization" (agifrontier tutorial: 2D square-block quantization).
 #include <cmath>
+#include <algorithm>
 #include <cstring>
 
 #include "../../include/ufp4.h"
@@ -292,6 +293,12 @@ int gemm_grouped_k(const ufp4_qtensor* dYt, const ufp4_qtensor* Xt, int32_t G,
     g.tile_start[i] = (int32_t)(per * i);
   }
   g.total_tiles = (int32_t)(per * G);
+  // longest segments first (ties in index order): their tiles start first and
+  // the short ones fill the end
+  for (int i = 0; i < G; ++i) g.gorder[i] = i;
+  std::stable_sort(g.gorder, g.gorder + G, [&](int32_t x, int32_t y) {
+    return offsets[x + 1] - offsets[x] > offsets[y + 1] - offsets[y];
+  });
   // the general kernels take fp32 scales only when grouped along K
   if (g.scale_mode == UFP4_SCALE_POW2 && !(mx_route(g) || (ws && fp6_bytes(dYt, Xt, g) > 0)))
     return UFP4_ERR_UNSUPPORTED;

@@ -147,6 +147,9 @@ struct GemmLaunch {
   int64_t off[kMaxGroups + 1];
   int32_t tile_start[kMaxGroups + 1];
   int32_t total_tiles;
+  // mode 2 (every group has the same tile count): the groups in the order the
+  // fp32-scale kernels walk them, longest segment first
+  int32_t gorder[kMaxGroups];
   float c_mul;      // factor on C: the operands' tensor factors (two-level scaling), 1 if none
   // fp32-scale kernels only, set by their launcher: tile slots from
   // split_first on are each computed by two workgroups, one per half of K,
