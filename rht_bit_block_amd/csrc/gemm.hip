@@ -53,10 +53,8 @@ struct Problem {
 
 // Resolve which group a tile belongs to and the group's operand views.
 __device__ __forceinline__ Problem resolve(const GemmLaunch& g, int b, int& tm, int& tn) {
-  const int tile = xcd_linear(b, g.total_tiles);   // XCD-contiguous tile ranges
-  int grp = 0;
-  while (grp + 1 < g.ngroups && g.tile_start[grp + 1] <= tile) ++grp;
-  const int local = tile - g.tile_start[grp];
+  int grp, local;
+  slot_tile(g, b, grp, local);
   Problem pr;
   if (g.mode == 0) {
     pr.a_codes = g.a_codes; pr.b_codes = g.b_codes;

@@ -42,6 +42,27 @@ __device__ __forceinline__ void grouped_order(int w, int tiles_m, int tiles_n, i
   tn = u / gm;
 }
 
+// Group and tile index inside it of launch slot b.  Dense and row-grouped
+// launches (tiles of equal cost): position xcd_linear(b) of the launch's
+// tiles, so each XCD works through a contiguous range (whole experts).
+// K-grouped launches (mode 2: every group has the same tile count, and a
+// tile costs in proportion to its group's segment): the groups longest first
+// (gorder, set by the host) and consecutive slots -- one group's tiles -- on
+// consecutive XCDs, so every XCD gets an equal share of every group and the
+// short tiles fill the end.
+__device__ __forceinline__ void slot_tile(const GemmLaunch& g, int b, int& grp, int& local) {
+  if (g.mode == 2) {
+    const int per = g.tile_start[1];
+    grp = g.gorder[b / per];
+    local = b % per;
+    return;
+  }
+  const int tile = xcd_linear(b, g.total_tiles);
+  grp = 0;
+  while (grp + 1 < g.ngroups && g.tile_start[grp + 1] <= tile) ++grp;
+  local = tile - g.tile_start[grp];
+}
+
 // Tile (tm, tn) that workgroup b of a dense T-tile launch computes.
 __device__ __forceinline__ void tile_order(int b, int T, int tiles_m, int tiles_n, int& tm,
                                            int& tn) {

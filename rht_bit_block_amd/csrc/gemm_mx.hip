@@ -154,10 +154,8 @@ __device__ __forceinline__ MxTile mx_dense(const GemmLaunch& g, int b) {
 
 template <int CPE4>
 __device__ __forceinline__ MxTile mx_resolve(const GemmLaunch& g, int b) {
-  const int tile = xcd_linear(b, g.total_tiles);
-  int grp = 0;
-  while (grp + 1 < g.ngroups && g.tile_start[grp + 1] <= tile) ++grp;
-  const int local = tile - g.tile_start[grp];
+  int grp, local;
+  slot_tile(g, b, grp, local);
   const uint8_t* sa = reinterpret_cast<const uint8_t*>(g.a_scales);
   const uint8_t* sb = reinterpret_cast<const uint8_t*>(g.b_scales);
   MxTile t;

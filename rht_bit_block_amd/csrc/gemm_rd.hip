@@ -283,26 +283,12 @@ struct Operands {
 };
 
 // The problem a tile belongs to (dense, grouped along A's rows, or grouped
-// along K) and the tile's coordinates inside it.  Dense and row-grouped
-// launches (tiles of equal cost): slot b takes position xcd_linear(b) of the
-// launch's tiles, so each XCD works through a contiguous range (whole experts
-// of a grouped launch), each problem in grouped order.  K-grouped launches:
-// see below.
+// along K) and the tile's coordinates inside it, each problem in grouped
+// order; slot_tile() picks the tile of slot b (XCD-contiguous ranges, or for
+// K-grouped launches the experts longest first, dealt over the XCDs).
 __device__ __forceinline__ Operands resolve(const GemmLaunch& g, int b, int& tm, int& tn) {
-  int grp = 0, local;
-  if (g.mode == 2) {
-    // grouped along K: tiles cost in proportion to their group's segment, so
-    // slots walk the groups longest first and consecutive slots (one group's
-    // tiles in grouped order) go to consecutive XCDs: every XCD gets an equal
-    // share of every group
-    const int per = g.tile_start[1];
-    grp = g.gorder[b / per];
-    local = b % per;
-  } else {
-    const int tile = xcd_linear(b, g.total_tiles);
-    while (grp + 1 < g.ngroups && g.tile_start[grp + 1] <= tile) ++grp;
-    local = tile - g.tile_start[grp];
-  }
+  int grp, local;
+  slot_tile(g, b, grp, local);
   Operands o;
   const float* sa = reinterpret_cast<const float*>(g.a_scales);
   const float* sb = reinterpret_cast<const float*>(g.b_scales);
