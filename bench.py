@@ -60,12 +60,12 @@ _GEMM_SRC = ("gemm_rd.hip", "gemm_epilogue.h", "ufp4_internal.h")
 _QUANT_SRC = ("quant_core.h", "ufp4_internal.h")
 MEASURED_TRAFFIC = {
     # (workload, kernel): (sources, sha256[:16] of them, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    ("moe16", "fprop"): (_GEMM_SRC, "0beb8c8d475927f4", 1568007.8, 1577654.6),
-    ("moe16", "dgrad"): (_GEMM_SRC, "0beb8c8d475927f4", 723454.4, 5259017.6),
-    ("moe16", "wgrad"): (_GEMM_SRC, "0beb8c8d475927f4", 1226746.8, 491574.1),
-    ("moe16", "quant_x"): (_QUANT_SRC, "39c06c7ebd22c317", 1314818.6, 2317888.6),
-    ("moe16", "quant_w"): (_QUANT_SRC, "39c06c7ebd22c317", 123149.9, 217078.4),
-    ("moe16", "quant_dy"): (_QUANT_SRC, "39c06c7ebd22c317", 395280.6, 700269.8),
+    ("moe16", "fprop"): (_GEMM_SRC, "ac018e30620e1339", 1568448.6, 1590521.9),
+    ("moe16", "dgrad"): (_GEMM_SRC, "ac018e30620e1339", 723982.8, 5258792.6),
+    ("moe16", "wgrad"): (_GEMM_SRC, "ac018e30620e1339", 1228758.3, 524338.0),
+    ("moe16", "quant_x"): (_QUANT_SRC, "247563b6fa1a1687", 1314817.1, 2308785.4),
+    ("moe16", "quant_w"): (_QUANT_SRC, "247563b6fa1a1687", 123149.4, 217006.9),
+    ("moe16", "quant_dy"): (_QUANT_SRC, "247563b6fa1a1687", 395277.4, 700256.9),
 }
 
 

@@ -262,6 +262,35 @@ int gemm_grouped_rows(const ufp4_qtensor* A, const ufp4_qtensor* B, int32_t G,
   return launch_any(A, B, g, ws, ws_bytes, stream);
 }
 
+// K-grouped launch (every group `per` tiles, a tile's cost proportional to its
+// segment): keep contiguous XCD ranges of whole groups unless the busiest of
+// the 8 ranges has over 5 % more work than the mean; then deal runs of tiles
+// (an eighth of a group, or one column of its grouped order, tiles_m tiles at
+// most 8) to the XCDs in turn, groups longest first.
+void plan_deal(GemmLaunch& g, int64_t per, int64_t tiles_m) {
+  const int G = g.ngroups;
+  const int64_t T = g.total_tiles;
+  double work[8] = {}, total = 0;
+  for (int x = 0; x < 8; ++x) {
+    const int64_t lo = x * (T / 8) + std::min<int64_t>(x, T % 8);
+    const int64_t hi = lo + T / 8 + (x < T % 8 ? 1 : 0);
+    for (int grp = 0; grp < G; ++grp) {
+      const int64_t a = std::max<int64_t>(lo, grp * per), b = std::min<int64_t>(hi, (grp + 1) * per);
+      if (b > a) work[x] += (double)(b - a) * (double)(g.off[grp + 1] - g.off[grp]);
+    }
+    total += work[x];
+  }
+  double worst = 0;
+  for (int x = 0; x < 8; ++x) worst = std::max(worst, work[x]);
+  g.deal = 0;
+  if (total <= 0 || worst <= 1.05 * total / 8) return;
+  g.deal = (int32_t)(per % 8 == 0 ? per / 8 : std::min<int64_t>(8, tiles_m));
+  for (int i = 0; i < G; ++i) g.gorder[i] = i;
+  std::stable_sort(g.gorder, g.gorder + G, [&](int32_t x, int32_t y) {
+    return g.off[x + 1] - g.off[x] > g.off[y + 1] - g.off[y];
+  });
+}
+
 // Grouped along K: wgrad (segmented column-wise operands).  fp32 scales run
 // on the general kernels; 1 x 32 E8M0 blocks on the scaled matrix cores when
 // every segment length is a multiple of 128, else UFP4_ERR_UNSUPPORTED.
@@ -293,12 +322,7 @@ int gemm_grouped_k(const ufp4_qtensor* dYt, const ufp4_qtensor* Xt, int32_t G,
     g.tile_start[i] = (int32_t)(per * i);
   }
   g.total_tiles = (int32_t)(per * G);
-  // longest segments first (ties in index order): their tiles start first and
-  // the short ones fill the end
-  for (int i = 0; i < G; ++i) g.gorder[i] = i;
-  std::stable_sort(g.gorder, g.gorder + G, [&](int32_t x, int32_t y) {
-    return offsets[x + 1] - offsets[x] > offsets[y + 1] - offsets[y];
-  });
+  plan_deal(g, per, cdiv(dYt->P, kTile));
   // the general kernels take fp32 scales only when grouped along K
   if (g.scale_mode == UFP4_SCALE_POW2 && !(mx_route(g) || (ws && fp6_bytes(dYt, Xt, g) > 0)))
     return UFP4_ERR_UNSUPPORTED;

@@ -42,22 +42,27 @@ __device__ __forceinline__ void grouped_order(int w, int tiles_m, int tiles_n, i
   tn = u / gm;
 }
 
-// Group and tile index inside it of launch slot b.  Dense and row-grouped
-// launches (tiles of equal cost): position xcd_linear(b) of the launch's
-// tiles, so each XCD works through a contiguous range (whole experts).
-// K-grouped launches (mode 2: every group has the same tile count, and a
-// tile costs in proportion to its group's segment): the groups longest first
-// (gorder, set by the host) and consecutive slots -- one group's tiles -- on
-// consecutive XCDs, so every XCD gets an equal share of every group and the
-// short tiles fill the end.
+// Group and tile index inside it of launch slot b.  Default: position
+// xcd_linear(b) of the launch's tiles in group order, so each XCD works
+// through a contiguous range (whole experts).  K-grouped launches whose
+// contiguous ranges would be unbalanced (deal > 0: a tile costs in proportion
+// to its group's segment, and the host found one XCD's range well above the
+// mean): the groups in gorder, longest first, and runs of `deal` consecutive
+// tiles (a share of one group, in grouped order) dealt to the XCDs in turn,
+// so every XCD gets an equal part of every group and the short tiles fill the
+// end; a last partial round of runs takes contiguous ranges.
 __device__ __forceinline__ void slot_tile(const GemmLaunch& g, int b, int& grp, int& local) {
-  if (g.mode == 2) {
-    const int per = g.tile_start[1];
-    grp = g.gorder[b / per];
-    local = b % per;
+  const int T = g.total_tiles;
+  if (g.mode == 2 && g.deal > 0) {
+    const int per = g.tile_start[1], c = g.deal;
+    const int j = b / 8, x = b % 8, R = T / (8 * c);
+    const int s = j < R * c ? ((j / c) * 8 + x) * c + j % c
+                            : 8 * c * R + xcd_linear(b - 8 * c * R, T - 8 * c * R);
+    grp = g.gorder[s / per];
+    local = s % per;
     return;
   }
-  const int tile = xcd_linear(b, g.total_tiles);
+  const int tile = xcd_linear(b, T);
   grp = 0;
   while (grp + 1 < g.ngroups && g.tile_start[grp + 1] <= tile) ++grp;
   local = tile - g.tile_start[grp];

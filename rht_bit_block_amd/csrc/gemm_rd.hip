@@ -285,7 +285,7 @@ struct Operands {
 // The problem a tile belongs to (dense, grouped along A's rows, or grouped
 // along K) and the tile's coordinates inside it, each problem in grouped
 // order; slot_tile() picks the tile of slot b (XCD-contiguous ranges, or for
-// K-grouped launches the experts longest first, dealt over the XCDs).
+// unbalanced K-grouped launches runs of tiles dealt over the XCDs).
 __device__ __forceinline__ Operands resolve(const GemmLaunch& g, int b, int& tm, int& tn) {
   int grp, local;
   slot_tile(g, b, grp, local);

@@ -147,8 +147,10 @@ struct GemmLaunch {
   int64_t off[kMaxGroups + 1];
   int32_t tile_start[kMaxGroups + 1];
   int32_t total_tiles;
-  // mode 2 (every group has the same tile count): the groups in the order the
-  // fp32-scale kernels walk them, longest segment first
+  // mode 2 (every group has the same tile count), set when contiguous XCD
+  // ranges would be unbalanced: deal > 0 tiles at a time go to each XCD in
+  // turn, walking the groups in gorder (longest segment first); 0: contiguous
+  int32_t deal;
   int32_t gorder[kMaxGroups];
   float c_mul;      // factor on C: the operands' tensor factors (two-level scaling), 1 if none
   // fp32-scale kernels only, set by their launcher: tile slots from

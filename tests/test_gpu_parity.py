@@ -693,6 +693,37 @@ def test_grouped_split_last_round():
         assert O.rel_fro(blk, ref) <= F32_SCALE_TOL, g
 
 
+def test_grouped_wgrad_dealt_tiles():
+    """Skewed experts (one holds most tokens, one is empty): contiguous ranges
+    of whole experts over the 8 XCDs would be unbalanced, so the tiles are
+    dealt in runs over the XCDs, experts longest first (8 tiles per expert,
+    16 experts).  Every expert's dW against the oracle, and a repeat."""
+    _print_case("grouped wgrad dealt tiles")
+    lens = [640, 32, 64, 0, 96, 32, 32, 128, 32, 64, 32, 32, 160, 32, 64, 32]
+    off = [0]
+    for n in lens:
+        off.append(off[-1] + n)
+    G, N, H = len(lens), 296, 800                        # 2 x 4 tiles per expert
+    cs = U.make_cfg(U.UFP4_E1M2, U.UFP4_SR, U.UFP4_SCALE_F32, 1, 16, 32, sign_seed=45, sr_seed=6,
+                    sr_stream=1)
+    cr = U.make_cfg(U.UFP4_E1M2, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 16, 32, sign_seed=45)
+    tdy, tx = rand_bits(off[-1], N, 54), rand_bits(off[-1], H, 55)
+    qdyt = U.ufp4_rht_quant_segmented(dev_bf16(tdy), off, cs)
+    qxt = U.ufp4_rht_quant_segmented(dev_bf16(tx), off, cr)
+    dW = U.ufp4_gemm_wgrad_grouped(qdyt, qxt, off)
+    assert torch.equal(dW, U.ufp4_gemm_wgrad_grouped(qdyt, qxt, off))
+    dW = dW.cpu().numpy()
+    r_dyt = O.quantize_segmented(tdy, off, spec_of(cs))
+    r_xt = O.quantize_segmented(tx, off, spec_of(cr))
+    for g in range(G):
+        blk = dW[g * N:(g + 1) * N]
+        if lens[g] == 0:
+            assert np.all(blk == 0.0), g
+            continue
+        ref = O.gemm_ref(oracle_dequant64(r_dyt[g], cs), oracle_dequant64(r_xt[g], cr))
+        assert O.rel_fro(blk, ref) <= F32_SCALE_TOL, g
+
+
 # ---------------------------------------------------------------------------
 # fp32-scale GEMMs whose K ends inside a 128-wide raw stage (and K of a single
 # step), for 16- and 32-wide K steps; ragged row tiles on both operands.
