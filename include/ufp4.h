@@ -238,7 +238,9 @@ int ufp4_dequant(const ufp4_qtensor* q, float* out, int64_t ldo, void* stream);
  * With fp32 block scales, a launch whose last round of workgroups (one per
  * compute unit) would be at most half full computes those tiles as two K
  * halves added into C, zeroed first by the same call (two addends on zero:
- * the same result whatever the timing).  This and the grouped forms. */
+ * the same result whatever the timing).  This and the grouped forms.  C
+ * must be ordinary device memory (hipMalloc, torch's CUDA tensors): those
+ * additions are the hardware's fp32 atomics. */
 int ufp4_gemm_fprop(const ufp4_qtensor* X, const ufp4_qtensor* W, float* Y, int64_t ldy,
                     void* stream);
 int ufp4_gemm_dgrad(const ufp4_qtensor* dY, const ufp4_qtensor* Wt, float* dX, int64_t ldx,
