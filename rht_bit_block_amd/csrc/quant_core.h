@@ -704,9 +704,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_diag(QuantLaunch q, FastDiv 
 constexpr int kTK = 128, kTP = 64;
 
 __device__ __forceinline__ int col_swz(int pr, int col) { return col ^ (((pr >> 3) & 7) << 2); }
+// (A lane's column segment starts at pair row kr / 2 = W / 2 * kseg, a multiple of
+// 8 for W = 16 and 32: its pair rows come in groups of 8 with one swizzle each.)
 
 template <int W, int B, int N, int GRID, int RND>
 __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantLaunch q) {
+  static_assert(W % 16 == 0, "column segments of whole 8-pair swizzle groups");
   __shared__ uint32_t tile[(kTK / 2) * kTP];
   constexpr int lpc = N > W ? N / W : 1;
   // which segment / tile
@@ -775,11 +778,14 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantLaunch q) {
     const int col = u / kSegsPerCol;
     const int kr = kseg * W;
     if (kr >= krows || col >= pcols) continue;  // whole chunks drop out together
+    // row pairs kr/2 .. kr/2 + W/2 - 1 in groups of 8 that share one swizzle
     uint32_t w[W / 2];
 #pragma unroll
-    for (int i = 0; i < W / 2; ++i) {
-      const int pr = kr / 2 + i;
-      w[i] = tile[pr * kTP + col_swz(pr, col)];
+    for (int h = 0; h < W / 16; ++h) {
+      const int pr = kr / 2 + 8 * h;
+      const uint32_t* base = tile + pr * kTP + col_swz(pr, col);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[8 * h + i] = base[i * kTP];
     }
     float y[W];
     unpack<W>(w, pm, y);
@@ -925,11 +931,15 @@ __device__ __forceinline__ void dual_quantize(const QuantLaunch& q, const RowSid
       const int col = u / kSegsPerCol;
       const int kr = kseg * W;
       if (kr >= d.krows || col >= d.pcols) continue;
+      // row pairs kr/2 .. kr/2 + W/2 - 1: kr/2 is a multiple of 8 (W >= 16), so each
+      // group of 8 shares one swizzle and the 8 reads are one base plus constants
       uint32_t w[W / 2];
 #pragma unroll
-      for (int i = 0; i < W / 2; ++i) {
-        const int pr = kr / 2 + i;
-        w[i] = tile[pr * TP + col_swz(pr, col)];
+      for (int h = 0; h < W / 16; ++h) {
+        const int pr = kr / 2 + 8 * h;
+        const uint32_t* base = tile + pr * TP + col_swz(pr, col);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[8 * h + i] = base[i * TP];
       }
       float y[W];
       unpack<W>(w, pm, y);
@@ -970,6 +980,7 @@ __device__ __forceinline__ void dual_quantize(const QuantLaunch& q, const RowSid
 
 template <int W, int B, int N, int GRID, int RND>
 __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide rside) {
+  static_assert(W % 16 == 0, "column segments of whole 8-pair swizzle groups");
   constexpr int TP = dual_tile_cols(N);
   __shared__ uint32_t tile[(kTK / 2) * TP];
   static_assert(N <= TP, "row-wise Hadamard chunks must fit the tile width");
