@@ -60,12 +60,12 @@ _GEMM_SRC = ("gemm_rd.hip", "gemm_epilogue.h", "ufp4_internal.h")
 _QUANT_SRC = ("quant_core.h", "ufp4_internal.h")
 MEASURED_TRAFFIC = {
     # (workload, kernel): (sources, sha256[:16] of them, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    ("moe16", "fprop"): (_GEMM_SRC, "ac018e30620e1339", 1568448.6, 1590521.9),
-    ("moe16", "dgrad"): (_GEMM_SRC, "ac018e30620e1339", 723982.8, 5258792.6),
-    ("moe16", "wgrad"): (_GEMM_SRC, "ac018e30620e1339", 1228758.3, 524338.0),
-    ("moe16", "quant_x"): (_QUANT_SRC, "247563b6fa1a1687", 1314817.1, 2308785.4),
-    ("moe16", "quant_w"): (_QUANT_SRC, "247563b6fa1a1687", 123149.4, 217006.9),
-    ("moe16", "quant_dy"): (_QUANT_SRC, "247563b6fa1a1687", 395277.4, 700256.9),
+    ("moe16", "fprop"): (_GEMM_SRC, "ac018e30620e1339", 1568950.2, 1590782.5),
+    ("moe16", "dgrad"): (_GEMM_SRC, "ac018e30620e1339", 711175.3, 5259012.9),
+    ("moe16", "wgrad"): (_GEMM_SRC, "ac018e30620e1339", 1228757.5, 524376.9),
+    ("moe16", "quant_x"): (_QUANT_SRC, "b6caa7ae85fd7abc", 1314786.4, 2308789.8),
+    ("moe16", "quant_w"): (_QUANT_SRC, "b6caa7ae85fd7abc", 123124.4, 217652.4),
+    ("moe16", "quant_dy"): (_QUANT_SRC, "b6caa7ae85fd7abc", 395237.8, 690435.8),
 }
 
 
