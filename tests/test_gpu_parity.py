@@ -634,7 +634,9 @@ def _assert_split(tiles, kavg):
 
 
 @pytest.mark.parametrize("grid,bc,K", [(U.UFP4_INT4, 16, 1152), (U.UFP4_E1M2, 32, 1024),
-                                       (U.UFP4_E2M1, 16, 1024)])
+                                       (U.UFP4_E2M1, 16, 1024),
+                                       # second halves ending inside a 128-element stage
+                                       (U.UFP4_INT4, 16, 1040), (U.UFP4_E1M2, 32, 1056)])
 def test_gemm_split_last_round(grid, bc, K):
     _print_case("split last round", grid, bc, K)
     PA, PB = 700, 300                                     # 3 x 2 ragged tiles
