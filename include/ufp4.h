@@ -15,7 +15,8 @@
  *   - Pointers named x, codes, scales, rotated, out, workspace, Y, dX, dW
  *     are DEVICE pointers owned by the caller; arrays named *_offsets are
  *     HOST arrays.  The library allocates no memory and keeps no data
- *     between calls (only per-device kernel attributes, set once), so every
+ *     between calls (only per-device kernel attributes and compute-unit
+ *     counts, each set or read once), so every
  *     entry point is safe to call from several host threads and on several
  *     streams at once, as long as the calls do not write the same buffers
  *     (workspaces included).  The one exception is ufp4_quant_diag_noalloc,
