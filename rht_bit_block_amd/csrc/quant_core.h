@@ -169,6 +169,18 @@ __device__ __forceinline__ void fwht_xlane(float (&y)[W], uint32_t negmask) {
 #undef UFP4_DPP_FMAC16
 #undef UFP4_DPP_FMAC
 
+// Runs f with the butterfly variant as a compile-time constant: exact (the
+// rotated values are written out) or fused.  Taken once around a loop, so the
+// loop body holds one variant and no merge of the two variants' registers.
+template <bool V> struct ExactTag { static constexpr bool value = V; };
+template <typename F>
+__device__ __forceinline__ void with_exact(bool exact, F&& f) {
+  if (exact)
+    f(ExactTag<true>{});
+  else
+    f(ExactTag<false>{});
+}
+
 // All butterfly stages of n (lanes of a chunk are adjacent: n / W of them).
 // Returns the lane's sign state: 0x80000000 if its values come out negated
 // (an odd number of fused cross-lane stages in which its bit was set), else
@@ -590,24 +602,26 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(QuantLaunch q, FastDiv 
   const uint32_t neg1 = (qpos & 1u) ? 0x80000000u : 0u;
   const uint32_t neg2 = (qpos & 2u) ? 0x80000000u : 0u;
   const uint32_t K = (uint32_t)q.K;
-  for (uint32_t seg = tid; seg < nseg; seg += stride) {
-    const uint32_t p = fdiv_u32(seg, segs_per_row);
-    const uint32_t kseg = seg - p * segs_per_row.d;
-    const uint32_t k0 = kseg * W;
-    const uint16_t* src = q.x + (int64_t)p * q.ld + k0;
-    uint32_t w[W / 2];
+  with_exact(q.rotated != nullptr, [&](auto ex) {
+    for (uint32_t seg = tid; seg < nseg; seg += stride) {
+      const uint32_t p = fdiv_u32(seg, segs_per_row);
+      const uint32_t kseg = seg - p * segs_per_row.d;
+      const uint32_t k0 = kseg * W;
+      const uint16_t* src = q.x + (int64_t)p * q.ld + k0;
+      uint32_t w[W / 2];
 #pragma unroll
-    for (int i = 0; i < W / 8; ++i) {
-      const uint4 v = ld16(reinterpret_cast<const uint4*>(src) + i);
-      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+      for (int i = 0; i < W / 8; ++i) {
+        const uint4 v = ld16(reinterpret_cast<const uint4*>(src) + i);
+        w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+      }
+      float y[W];
+      unpack<W>(w, pm, y);
+      const uint32_t sig = fwht<W, N>(y, neg1, neg2, decltype(ex)::value);
+      const uint64_t e0 = (uint64_t)p * K + k0;
+      finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, sig, q, e0, code_ptr<GRID>(q.codes, e0),
+                                      scale_at<RND>(q.scales, (uint64_t)p * (K / B) + k0 / B));
     }
-    float y[W];
-    unpack<W>(w, pm, y);
-    const uint32_t sig = fwht<W, N>(y, neg1, neg2, q.rotated != nullptr);
-    const uint64_t e0 = (uint64_t)p * K + k0;
-    finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, sig, q, e0, code_ptr<GRID>(q.codes, e0),
-                                    scale_at<RND>(q.scales, (uint64_t)p * (K / B) + k0 / B));
-  }
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -770,32 +784,34 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantLaunch q) {
   sign_masks<W>(select_pattern(q, qpos), pm);
   const uint32_t neg1 = (qpos & 1u) ? 0x80000000u : 0u;
   const uint32_t neg2 = (qpos & 2u) ? 0x80000000u : 0u;
-  for (int u = threadIdx.x; u < kTP * kSegsPerCol; u += kThreads) {
-    // consecutive lanes take consecutive W-segments of one column, so a
-    // column's codes and scales are written by adjacent lanes (contiguous
-    // stores), and the lanes of one Hadamard chunk are adjacent
-    const int kseg = u % kSegsPerCol;
-    const int col = u / kSegsPerCol;
-    const int kr = kseg * W;
-    if (kr >= krows || col >= pcols) continue;  // whole chunks drop out together
-    // row pairs kr/2 .. kr/2 + W/2 - 1 in groups of 8 that share one swizzle
-    uint32_t w[W / 2];
+  with_exact(q.rotated != nullptr, [&](auto ex) {
+    for (int u = threadIdx.x; u < kTP * kSegsPerCol; u += kThreads) {
+      // consecutive lanes take consecutive W-segments of one column, so a
+      // column's codes and scales are written by adjacent lanes (contiguous
+      // stores), and the lanes of one Hadamard chunk are adjacent
+      const int kseg = u % kSegsPerCol;
+      const int col = u / kSegsPerCol;
+      const int kr = kseg * W;
+      if (kr >= krows || col >= pcols) continue;  // whole chunks drop out together
+      // row pairs kr/2 .. kr/2 + W/2 - 1 in groups of 8 that share one swizzle
+      uint32_t w[W / 2];
 #pragma unroll
-    for (int h = 0; h < W / 16; ++h) {
-      const int pr = kr / 2 + 8 * h;
-      const uint32_t* base = tile + pr * kTP + col_swz(pr, col);
+      for (int h = 0; h < W / 16; ++h) {
+        const int pr = kr / 2 + 8 * h;
+        const uint32_t* base = tile + pr * kTP + col_swz(pr, col);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) w[8 * h + i] = base[i * kTP];
+        for (int i = 0; i < 8; ++i) w[8 * h + i] = base[i * kTP];
+      }
+      float y[W];
+      unpack<W>(w, pm, y);
+      const uint32_t sig = fwht<W, N>(y, neg1, neg2, decltype(ex)::value);
+      const int64_t p = p0 + col;
+      const int64_t k = k0 + kr;
+      const uint64_t e0 = (uint64_t)C * seg0 + (uint64_t)p * L + k;   // global draw index
+      finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, sig, q, e0, code_ptr<GRID>(q.codes, e0),
+                                      scale_at<RND>(q.scales, e0 / B));
     }
-    float y[W];
-    unpack<W>(w, pm, y);
-    const uint32_t sig = fwht<W, N>(y, neg1, neg2, q.rotated != nullptr);
-    const int64_t p = p0 + col;
-    const int64_t k = k0 + kr;
-    const uint64_t e0 = (uint64_t)C * seg0 + (uint64_t)p * L + k;   // global draw index
-    finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, sig, q, e0, code_ptr<GRID>(q.codes, e0),
-                                    scale_at<RND>(q.scales, e0 / B));
-  }
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -926,55 +942,59 @@ __device__ __forceinline__ void dual_quantize(const QuantLaunch& q, const RowSid
     uint32_t pm[W / 2];
     sign_masks<W>(select_pattern(q, qpos), pm);
     constexpr int kSegsPerCol = kTK / W;
-    for (int u = threadIdx.x; u < TP * kSegsPerCol; u += kThreads) {
-      const int kseg = u % kSegsPerCol;
-      const int col = u / kSegsPerCol;
-      const int kr = kseg * W;
-      if (kr >= d.krows || col >= d.pcols) continue;
-      // row pairs kr/2 .. kr/2 + W/2 - 1: kr/2 is a multiple of 8 (W >= 16), so each
-      // group of 8 shares one swizzle and the 8 reads are one base plus constants
-      uint32_t w[W / 2];
+    with_exact(q.rotated != nullptr, [&](auto ex) {
+      for (int u = threadIdx.x; u < TP * kSegsPerCol; u += kThreads) {
+        const int kseg = u % kSegsPerCol;
+        const int col = u / kSegsPerCol;
+        const int kr = kseg * W;
+        if (kr >= d.krows || col >= d.pcols) continue;
+        // row pairs kr/2 .. kr/2 + W/2 - 1: kr/2 is a multiple of 8 (W >= 16), so each
+        // group of 8 shares one swizzle and the 8 reads are one base plus constants
+        uint32_t w[W / 2];
 #pragma unroll
-      for (int h = 0; h < W / 16; ++h) {
-        const int pr = kr / 2 + 8 * h;
-        const uint32_t* base = tile + pr * TP + col_swz(pr, col);
+        for (int h = 0; h < W / 16; ++h) {
+          const int pr = kr / 2 + 8 * h;
+          const uint32_t* base = tile + pr * TP + col_swz(pr, col);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w[8 * h + i] = base[i * TP];
+          for (int i = 0; i < 8; ++i) w[8 * h + i] = base[i * TP];
+        }
+        float y[W];
+        unpack<W>(w, pm, y);
+        const uint32_t sig = fwht<W, N>(y, neg1, neg2, decltype(ex)::value);
+        const uint64_t e0 = (uint64_t)C * d.seg0 + (uint64_t)(d.p0 + col) * d.L + (d.k0 + kr);
+        finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, sig, q, e0, code_ptr<GRID>(q.codes, e0),
+                                                     scale_at<RND>(q.scales, e0 / B));
       }
-      float y[W];
-      unpack<W>(w, pm, y);
-      const uint32_t sig = fwht<W, N>(y, neg1, neg2, q.rotated != nullptr);
-      const uint64_t e0 = (uint64_t)C * d.seg0 + (uint64_t)(d.p0 + col) * d.L + (d.k0 + kr);
-      finish_lane<W, B, N, GRID, RND, QuantLaunch>(y, sig, q, e0, code_ptr<GRID>(q.codes, e0),
-                                                   scale_at<RND>(q.scales, e0 / B));
-    }
+    });
   }
   // row-wise: A = X, K = the columns
   {
     uint32_t pm[W / 2];
     sign_masks<W>(select_pattern(rside, qpos), pm);
     constexpr int kSegsPerRow = TP / W;
-    for (int u = threadIdx.x; u < kTK * kSegsPerRow; u += kThreads) {
-      const int seg = u % kSegsPerRow;
-      const int row = u / kSegsPerRow;
-      const int c0 = seg * W;
-      if (row >= d.krows || c0 >= d.pcols) continue;   // whole chunks drop out together
-      const int pr = row >> 1;
-      const uint32_t sel = (row & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t w[W / 2];
+    with_exact(rside.rotated != nullptr, [&](auto ex) {
+      for (int u = threadIdx.x; u < kTK * kSegsPerRow; u += kThreads) {
+        const int seg = u % kSegsPerRow;
+        const int row = u / kSegsPerRow;
+        const int c0 = seg * W;
+        if (row >= d.krows || c0 >= d.pcols) continue;   // whole chunks drop out together
+        const int pr = row >> 1;
+        const uint32_t sel = (row & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t w[W / 2];
 #pragma unroll
-      for (int j = 0; j < W / 4; ++j) {
-        const uint4 v = *reinterpret_cast<const uint4*>(tile + pr * TP + col_swz(pr, c0 + 4 * j));
-        w[2 * j] = __builtin_amdgcn_perm(v.y, v.x, sel);
-        w[2 * j + 1] = __builtin_amdgcn_perm(v.w, v.z, sel);
+        for (int j = 0; j < W / 4; ++j) {
+          const uint4 v = *reinterpret_cast<const uint4*>(tile + pr * TP + col_swz(pr, c0 + 4 * j));
+          w[2 * j] = __builtin_amdgcn_perm(v.y, v.x, sel);
+          w[2 * j + 1] = __builtin_amdgcn_perm(v.w, v.z, sel);
+        }
+        float y[W];
+        unpack<W>(w, pm, y);
+        const uint32_t sig = fwht<W, N>(y, neg1, neg2, decltype(ex)::value);
+        const uint64_t e0 = (uint64_t)(d.seg0 + d.k0 + row) * (uint64_t)C + (uint64_t)(d.p0 + c0);
+        finish_lane<W, B, N, GRID, RND, RowSide>(y, sig, rside, e0, code_ptr<GRID>(rside.codes, e0),
+                                                 scale_at<RND>(rside.scales, e0 / B));
       }
-      float y[W];
-      unpack<W>(w, pm, y);
-      const uint32_t sig = fwht<W, N>(y, neg1, neg2, rside.rotated != nullptr);
-      const uint64_t e0 = (uint64_t)(d.seg0 + d.k0 + row) * (uint64_t)C + (uint64_t)(d.p0 + c0);
-      finish_lane<W, B, N, GRID, RND, RowSide>(y, sig, rside, e0, code_ptr<GRID>(rside.codes, e0),
-                                               scale_at<RND>(rside.scales, e0 / B));
-    }
+    });
   }
 }
 
