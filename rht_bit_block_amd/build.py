@@ -77,7 +77,24 @@ def build(verbose=True, sanitize=False):
     os.replace(tmp, lib_path)
     if verbose:
         print("built", lib_path, file=sys.stderr)
+    if not sanitize:
+        build_test_helpers(verbose)
     return lib_path
+
+
+def build_test_helpers(verbose=True):
+    """tests/libufp4_hwcheck.so: GPU checks of arithmetic identities the
+    kernels rely on (a test library, not part of the product)."""
+    src = os.path.join(ROOT, "tests", "hw_identities.hip")
+    out = os.path.join(ROOT, "tests", "libufp4_hwcheck.so")
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), *CFLAGS, "-shared", src, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for tests/hw_identities.hip:\n" + r.stderr[-4000:])
+    os.replace(tmp, out)
+    if verbose:
+        print("built", out, file=sys.stderr)
 
 
 if __name__ == "__main__":

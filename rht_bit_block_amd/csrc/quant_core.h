@@ -409,6 +409,22 @@ __device__ __forceinline__ void diag_accumulate(DiagLds* d, uint32_t nib, float 
 // `sig` is the lane's sign state from fwht: when set, y holds the negated
 // rotated values, and the quotients use the negated divisor (or reciprocal),
 // which gives the same RN(y / s): rounding is symmetric.
+// s = RN(M / qmax) for the codebook's constant qmax (1.75, 7 or 6): the
+// product M * RN(1/qmax) corrected once through its exact fma remainder
+// (Markstein's division by a known divisor).  It equals the IEEE quotient for
+// every float M in [1, 4) for each of the three divisors (an exhaustive host
+// check in the tests); the sequence and the quotient both scale exactly with
+// M by powers of two while the remainder stays normal, so this holds for every
+// M in [2^-100, FLT_MAX] and for M = 0.  Other M (tiny, inf, NaN) divide.
+template <int GRID>
+__device__ __forceinline__ float div_qmax(float M) {
+  constexpr float qmax = Grid<GRID>::qmax, rq = 1.0f / qmax;
+  if (__builtin_expect(!((M >= 0x1p-100f || M == 0.0f) && M <= 0x1.fffffep127f), 0))
+    return __fdiv_rn(M, qmax);
+  const float q0 = __fmul_rn(M, rq);
+  return __fmaf_rn(__fmaf_rn(-q0, qmax, M), rq, q0);
+}
+
 template <int W, int B, int GRID, int RND, bool FOLD, bool DIAG = false>
 __device__ __forceinline__ void quantize_1d(const float (&y)[W], uint32_t sig, float c, uint64_t e0,
                                             uint64_t seed, uint32_t stream, uint8_t* codes_out,
@@ -448,14 +464,16 @@ __device__ __forceinline__ void quantize_1d(const float (&y)[W], uint32_t sig, f
       }
       if constexpr (!DIAG) reinterpret_cast<uint8_t*>(scales_out)[blk] = (uint8_t)(e + 127);
     } else {
-    float s = __fdiv_rn(M, qmax);  // s_B = RN(absmax / qmax)
+    float s = div_qmax<GRID>(M);  // s_B = RN(absmax / qmax)
     {
       // s = 0 (all-zero block, or absmax / qmax below the subnormal range):
       // every v is 0.  Running the quotient below with divisor 1 and
       // reciprocal 0 gives q = +-0, e = y, v = e * 0 + q = +-0 without a branch.
       const bool zero = s == 0.0f;
       const float sd = zero ? 1.0f : s;
-      const float r = zero ? 0.0f : __fdiv_rn(1.0f, sd);
+      // RN(1/sd); outside [2^-60, 2^60] the quotients below take the IEEE
+      // division and r is not used
+      const float r = zero ? 0.0f : rcp_rn(sd);
       const float sdn = __uint_as_float(__float_as_uint(sd) ^ sig);   // divisor and
       const float rn = __uint_as_float(__float_as_uint(r) ^ sig);     // reciprocal, signed
       // Markstein: with r = RN(1/s) and q within an ulp of y/s, the fma

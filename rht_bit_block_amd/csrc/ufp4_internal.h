@@ -61,6 +61,17 @@ __device__ __forceinline__ void philox4x32_10_dev(uint32_t c[4], uint32_t k0,
   }
 }
 
+// RN(1/d) for d in [2^-60, 2^60]: gfx950's reciprocal (within one ulp) with
+// one Newton correction through its exact fma residual.  On gfx950 this
+// equals the IEEE quotient 1/d for every mantissa, checked exhaustively in
+// binades from 2^-60 to 2^59 (the raw reciprocal misses RN on about one
+// mantissa in nine, the same ones in every binade; one correction removes all
+// of them).  A GPU test repeats the check.
+__device__ __forceinline__ float rcp_rn(float d) {
+  const float y = __builtin_amdgcn_rcpf(d);
+  return __builtin_fmaf(__builtin_fmaf(-d, y, 1.0f), y, y);
+}
+
 // Unsigned 32-bit division by a launch constant d >= 1, as a multiply-high
 // (Granlund & Montgomery, "Division by invariant integers using
 // multiplication", PLDI'94): q = (umulhi(m, n) + n) >> l with l = ceil(log2 d),
