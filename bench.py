@@ -60,12 +60,12 @@ _GEMM_SRC = ("gemm_rd.hip", "gemm_epilogue.h", "ufp4_internal.h")
 _QUANT_SRC = ("quant_core.h", "ufp4_internal.h")
 MEASURED_TRAFFIC = {
     # (workload, kernel): (sources, sha256[:16] of them, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    ("moe16", "fprop"): (_GEMM_SRC, "ac018e30620e1339", 1568950.2, 1590782.5),
-    ("moe16", "dgrad"): (_GEMM_SRC, "ac018e30620e1339", 711175.3, 5259012.9),
-    ("moe16", "wgrad"): (_GEMM_SRC, "ac018e30620e1339", 1228757.5, 524376.9),
-    ("moe16", "quant_x"): (_QUANT_SRC, "b6caa7ae85fd7abc", 1314786.4, 2308789.8),
-    ("moe16", "quant_w"): (_QUANT_SRC, "b6caa7ae85fd7abc", 123124.4, 217652.4),
-    ("moe16", "quant_dy"): (_QUANT_SRC, "b6caa7ae85fd7abc", 395237.8, 690435.8),
+    ("moe16", "fprop"): (_GEMM_SRC, "2d47725275a5634d", 1564556.3, 1590577.0),
+    ("moe16", "dgrad"): (_GEMM_SRC, "2d47725275a5634d", 722450.8, 5258871.2),
+    ("moe16", "wgrad"): (_GEMM_SRC, "2d47725275a5634d", 1228769.9, 524375.8),
+    ("moe16", "quant_x"): (_QUANT_SRC, "e261fffb149eab2f", 1314780.7, 2190923.3),
+    ("moe16", "quant_w"): (_QUANT_SRC, "e261fffb149eab2f", 123118.8, 204240.6),
+    ("moe16", "quant_dy"): (_QUANT_SRC, "e261fffb149eab2f", 395337.0, 687025.6),
 }
 
 
