@@ -695,6 +695,49 @@ def test_grouped_split_last_round():
         assert O.rel_fro(blk, ref) <= F32_SCALE_TOL, g
 
 
+def test_split_beside_full_rounds():
+    """Full rounds and a split last round in one launch: dense FPROP of 16 x 19
+    = 304 tiles (48 split on 256 CUs) and WGRAD grouped along K with 3 experts
+    of 6 x 16 = 96 tiles each (288 tiles, 32 split), every element against the
+    oracle at the fp32-scale bar."""
+    _print_case("split beside full rounds")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    cfg = U.make_cfg(U.UFP4_INT4, U.UFP4_RTNE, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=46)
+    PA, PB, K = 4096, 4864, 1024
+    T = (PA // 256) * (PB // 256)
+    assert T > cus, "no full round before the split one"
+    _assert_split(T, K)
+    qa, ra = compare_quant(rand_bits(PA, K, 60), 0, cfg, with_rotated=False)
+    qb, rb = compare_quant(rand_bits(PB, K, 61), 0, cfg, with_rotated=False)
+    C = U.ufp4_gemm_fprop(qa, qb).cpu().numpy()
+    ref = O.gemm_ref(oracle_dequant64(ra, cfg), oracle_dequant64(rb, cfg))
+    assert O.rel_fro(C, ref) <= F32_SCALE_TOL
+    # per-tile check: every 256 x 256 tile, so a wrong split tile cannot hide
+    for i in range(0, PA, 256):
+        for j in range(0, PB, 256):
+            assert O.rel_fro(C[i:i + 256, j:j + 256], ref[i:i + 256, j:j + 256]) <= F32_SCALE_TOL, (i, j)
+    assert np.array_equal(C, U.ufp4_gemm_fprop(qa, qb).cpu().numpy())
+    off, N, H = [0, 1024, 2048, 3072], 1536, 4096          # 6 x 16 tiles per expert
+    assert 3 * (N // 256) * (H // 256) > cus
+    _assert_split(3 * (N // 256) * (H // 256), 1024)
+    cs = U.make_cfg(U.UFP4_INT4, U.UFP4_SR, U.UFP4_SCALE_F32, 1, 16, 16, sign_seed=46, sr_seed=8,
+                    sr_stream=1)
+    tdy, tx = rand_bits(off[-1], N, 62), rand_bits(off[-1], H, 63)
+    qdyt = U.ufp4_rht_quant_segmented(dev_bf16(tdy), off, cs)
+    qxt = U.ufp4_rht_quant_segmented(dev_bf16(tx), off, cfg)
+    dW = U.ufp4_gemm_wgrad_grouped(qdyt, qxt, off)
+    assert torch.equal(dW, U.ufp4_gemm_wgrad_grouped(qdyt, qxt, off))
+    dW = dW.cpu().numpy()
+    r_dyt = O.quantize_segmented(tdy, off, spec_of(cs))
+    r_xt = O.quantize_segmented(tx, off, spec_of(cfg))
+    for g in range(3):
+        ref = O.gemm_ref(oracle_dequant64(r_dyt[g], cs), oracle_dequant64(r_xt[g], cfg))
+        blk = dW[g * N:(g + 1) * N]
+        for i in range(0, N, 256):
+            for j in range(0, H, 256):
+                assert O.rel_fro(blk[i:i + 256, j:j + 256], ref[i:i + 256, j:j + 256]) <= F32_SCALE_TOL, (g, i, j)
+
+
 def test_grouped_wgrad_dealt_tiles():
     """Skewed experts (one holds most tokens, one is empty): contiguous ranges
     of whole experts over the 8 XCDs would be unbalanced, so the tiles are
