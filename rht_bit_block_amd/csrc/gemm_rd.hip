@@ -103,9 +103,10 @@ __device__ __forceinline__ uint32_t nib_to_e4m3(uint32_t v) {
   const uint32_t pos = __builtin_amdgcn_perm(Lut<GRID>::hi, Lut<GRID>::lo, m);
   if constexpr (GRID == 1) {
     const uint32_t neg = __builtin_amdgcn_perm(Lut<1>::nhi, Lut<1>::nlo, m);
-    const uint32_t b = (v >> 3) & 0x01010101u;
-    const uint32_t sel = (b << 8) - b;   // 0xFF in the bytes of negative nibbles
-    return (neg & sel) | (pos & ~sel);
+    // byte i from pos (selector i) or, where the nibble's bit 3 is set, from
+    // neg (selector i + 4)
+    const uint32_t sel = ((v >> 1) & 0x04040404u) | 0x03020100u;
+    return __builtin_amdgcn_perm(neg, pos, sel);
   } else {
     return pos | ((v & 0x08080808u) << 4);
   }
@@ -198,8 +199,31 @@ struct RdCtx {
   uint32_t lds0;
   uint32_t code_voff[2];     // wave code load q: row * (K/2) + 16 * chunk
   uint32_t scale_voff[2];    // wave scale load q
+  uint32_t rs, srs;          // row strides of the codes and the scales (bytes)
   int wave, nst;
 };
+
+// Per-lane byte offsets of a wave's raw-stage loads.  Codes: lane i of wave
+// load q -> row 32 w + 16 q + i / 4, the chunk whose swizzled slot is i % 4.
+// Scales: wave load g covers 1024 / SB rows of operand g / (SLOADS/2); lane i
+// -> row i / (SB/16), part i % (SB/16).
+template <int BC>
+__device__ __forceinline__ void load_offsets(int wave, uint32_t lane, uint32_t rs, uint32_t srs,
+                                             uint32_t* code_voff, uint32_t* scale_voff) {
+  using L = Layout<BC>;
+  const uint32_t lr = lane >> 2;
+  const uint32_t chunk = (lane & 3) ^ ((lr >> 1) & 3);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) code_voff[q] = ((uint32_t)(wave * 32 + q * 16) + lr) * rs + 16u * chunk;
+  constexpr uint32_t PER = L::SB / 16;
+  constexpr uint32_t ROWS = 64 / PER;
+#pragma unroll
+  for (int q = 0; q < L::SPW; ++q) {
+    const int gl = wave + 8 * q;
+    const uint32_t row = (uint32_t)(gl % (L::SLOADS / 2)) * ROWS + lane / PER;
+    scale_voff[q] = row * srs + 16u * (lane % PER);
+  }
+}
 
 template <int BC>
 __device__ __forceinline__ void issue_stage(const RdCtx& c, int stage, int slot) {
@@ -207,18 +231,28 @@ __device__ __forceinline__ void issue_stage(const RdCtx& c, int stage, int slot)
   const int s = stage < c.nst ? stage : c.nst - 1;   // past the end: re-read, unused
   const uint32_t base = c.lds0 + (uint32_t)slot * L::RAW;
   const uint32_t koff = (uint32_t)s * 64u;
+  uint32_t cv[2] = {c.code_voff[0], c.code_voff[1]};
+  uint32_t sv[2] = {c.scale_voff[0], c.scale_voff[1]};
+  if constexpr (BC == 32) {
+    // The 32-wide kernel's loop has no register to spare (kept live, these
+    // offsets were spilled, and the reload's wait then also waited for the
+    // stage's own loads): recompute them from the lane id once per stage.
+    uint32_t lane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+    load_offsets<BC>(c.wave, lane, c.rs, c.srs, cv, sv);
+  }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const uint32_t blk = (uint32_t)(c.wave * 2 + q) * 1024u;   // 16 rows x 64 B
-    lds_load16(base + blk, c.ra, c.code_voff[q], koff);
-    lds_load16(base + TM * 64 + blk, c.rb, c.code_voff[q], koff);
+    lds_load16(base + blk, c.ra, cv[q], koff);
+    lds_load16(base + TM * 64 + blk, c.rb, cv[q], koff);
   }
   const uint32_t soff = (uint32_t)s * L::SB;
 #pragma unroll
   for (int q = 0; q < L::SPW; ++q) {
     const int g = c.wave + 8 * q;                 // scale wave load, A loads first
     const bool is_b = g >= L::SLOADS / 2;
-    lds_load16(base + L::CODES + (uint32_t)g * 1024u, is_b ? c.rsb : c.rsa, c.scale_voff[q], soff);
+    lds_load16(base + L::CODES + (uint32_t)g * 1024u, is_b ? c.rsb : c.rsa, sv[q], soff);
   }
 }
 
@@ -376,22 +410,10 @@ __device__ __forceinline__ TileCtx tile_ctx(const GemmLaunch& g, const uint8_t* 
   c.rsb = rsrc4(reinterpret_cast<const uint8_t*>(t.o.b_scales) + t.col0 * srs + sb,
                 (uint32_t)(t.rows_b * srs) - sb);
   c.lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds;
-  // codes: lane i of wave load q -> row 32 w + 16 q + i / 4, the chunk whose
-  // swizzled slot is i % 4
-  const int lr = lane >> 2;
-  const uint32_t chunk = (uint32_t)((lane & 3) ^ ((lr >> 1) & 3));
-#pragma unroll
-  for (int q = 0; q < 2; ++q) c.code_voff[q] = (uint32_t)(t.wave * 32 + q * 16 + lr) * rs + 16u * chunk;
-  // scales: wave load g covers 1024 / SB rows of operand g / (SLOADS/2);
-  // lane i -> row i / (SB/16), part i % (SB/16)
-  constexpr int PER = L::SB / 16;
-  constexpr int ROWS = 64 / PER;
-#pragma unroll
-  for (int q = 0; q < L::SPW; ++q) {
-    const int gl = t.wave + 8 * q;
-    const int row = (gl % (L::SLOADS / 2)) * ROWS + lane / PER;
-    c.scale_voff[q] = (uint32_t)row * srs + 16u * (uint32_t)(lane % PER);
-  }
+  c.rs = rs;
+  c.srs = srs;
+  c.scale_voff[1] = 0;
+  load_offsets<BC>(t.wave, (uint32_t)lane, rs, srs, c.code_voff, c.scale_voff);
   return t;
 }
 
