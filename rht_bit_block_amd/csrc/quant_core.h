@@ -728,14 +728,20 @@ __global__ __launch_bounds__(kThreads) void k_quant_diag(QuantLaunch q, FastDiv 
 // rows (2i, 2i+1) of one column -- exactly the packed bf16 pairs the
 // quantizer consumes -- so a lane reads W/2 words; the staging thread forms
 // the pairs of 8 columns from two 16-byte row loads with 8 byte permutes.
-// Words are [pair row][column], columns XOR-swizzled in groups of 4 by bits
-// 3..5 of the pair row: the 4-word staging writes stay contiguous, and lanes
-// reading pair rows 8 apart (one Hadamard chunk spread over adjacent lanes)
-// hit different banks.
+// Words are [pair row][column], columns XOR-swizzled in groups of 4 (bits 2..4
+// of the column) by bits 3..5 of the pair row and bits 5..7 of the column: the
+// 4-word staging writes stay contiguous; lanes reading pair rows 8 apart (one
+// Hadamard chunk spread over adjacent lanes) hit different banks; and the
+// 16-byte reads of one pair row's 32-column segments, and the staging writes
+// of 8 consecutive 8-column groups, fall on different banks (a pair row is a
+// multiple of 32 words, so without the column term every such access of a
+// pair row would land on the same four banks).
 // ---------------------------------------------------------------------------
 constexpr int kTK = 128, kTP = 64;
 
-__device__ __forceinline__ int col_swz(int pr, int col) { return col ^ (((pr >> 3) & 7) << 2); }
+__device__ __forceinline__ int col_swz(int pr, int col) {
+  return col ^ ((((pr >> 3) ^ (col >> 5)) & 7) << 2);
+}
 // (A lane's column segment starts at pair row kr / 2 = W / 2 * kseg, a multiple of
 // 8 for W = 16 and 32: its pair rows come in groups of 8 with one swizzle each.)
 
