@@ -60,12 +60,12 @@ _GEMM_SRC = ("gemm_rd.hip", "gemm_epilogue.h", "ufp4_internal.h")
 _QUANT_SRC = ("quant_core.h", "ufp4_internal.h")
 MEASURED_TRAFFIC = {
     # (workload, kernel): (sources, sha256[:16] of them, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    ("moe16", "fprop"): (_GEMM_SRC, "2d47725275a5634d", 1564556.3, 1590577.0),
-    ("moe16", "dgrad"): (_GEMM_SRC, "2d47725275a5634d", 722450.8, 5258871.2),
-    ("moe16", "wgrad"): (_GEMM_SRC, "2d47725275a5634d", 1228769.9, 524375.8),
-    ("moe16", "quant_x"): (_QUANT_SRC, "e261fffb149eab2f", 1314780.7, 2190923.3),
-    ("moe16", "quant_w"): (_QUANT_SRC, "e261fffb149eab2f", 123118.8, 204240.6),
-    ("moe16", "quant_dy"): (_QUANT_SRC, "e261fffb149eab2f", 395337.0, 687025.6),
+    ("moe16", "fprop"): (_GEMM_SRC, "7ae132ace46eff1f", 1564082.2, 1590699.2),
+    ("moe16", "dgrad"): (_GEMM_SRC, "7ae132ace46eff1f", 721683.2, 5258796.9),
+    ("moe16", "wgrad"): (_GEMM_SRC, "7ae132ace46eff1f", 1228733.8, 524348.6),
+    ("moe16", "quant_x"): (_QUANT_SRC, "403732f048a694c8", 1314789.9, 2317553.8),
+    ("moe16", "quant_w"): (_QUANT_SRC, "403732f048a694c8", 123115.4, 218083.2),
+    ("moe16", "quant_dy"): (_QUANT_SRC, "403732f048a694c8", 396039.1, 690822.1),
 }
 
 
@@ -444,7 +444,7 @@ def rht_cost(U, torch, reps=10):
     (32768 x 8192 N(0,1), seeded) quantized row-wise (RTNE, 1 x 16 fp32
     scales, INT4) with the Hadamard size n = 1 (no rotation) and n = 16, 32,
     64, 128, plus SR at n = 16 and 128, next to a plain 1 GiB device copy
-    timed the same way.  GB/s count 2.75 B per element (the copy: 2 B per
+    (torch's, and the library's streaming copy kernel) timed the same way.  GB/s count 2.75 B per element (the copy: 2 B per
     byte copied).  The pages say fusing the RHT into the FP4 quantizer adds
     only a modest overhead (no hardware named); ratio_vs_n1 is that overhead
     here."""
@@ -479,6 +479,12 @@ def rht_cost(U, torch, reps=10):
     gbps = 2.0 * n / ms / 1e6
     out["device_copy_1GiB"] = {"ms": round(ms, 4), "GB/s": round(gbps, 1),
                                "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    args = (ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), n, cs)
+    ms = _timed(torch, _raw(U, "stream_copy", lib.ufp4_stream_copy, args), reps)
+    gbps = 2.0 * n / ms / 1e6
+    out["stream_copy_1GiB"] = {"ms": round(ms, 4), "GB/s": round(gbps, 1),
+                               "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                               "kernel": "the library's streaming copy (ufp4_stream_copy)"}
     del src, dst
     torch.cuda.empty_cache()
     return out

@@ -316,6 +316,21 @@ size_t ufp4_scales_bytes(int64_t P, int64_t K, const ufp4_quant_cfg* cfg);
 int ufp4_philox_fill(uint64_t seed, uint32_t stream_id, uint64_t first, int64_t n,
                      uint16_t* out, void* stream);
 
+/* Device-to-device copy of nbytes bytes from src to dst, written as a
+ * streaming kernel (one 16-byte vector per thread over a grid that covers
+ * the buffer, non-temporal loads and stores; bytes past the last whole vector
+ * copied one by one).  A
+ * measurement aid: the HBM bandwidth a pass that reads and writes every byte
+ * once reaches, the yardstick for the quantizers, which read their input once
+ * and write their outputs once (the pages put the cost of fusing the
+ * rotation into the quantizer at a modest overhead, [UFP4] experiments
+ * section).  src and dst are
+ * device pointers, 16-byte aligned, whose ranges do not overlap; the caller
+ * owns both.  nbytes = 0 does nothing.  Errors (no launch):
+ * UFP4_ERR_INVALID_ARG for nbytes < 0, a null pointer with nbytes > 0,
+ * misalignment or overlapping ranges.  Asynchronous on `stream`. */
+int ufp4_stream_copy(const void* src, void* dst, int64_t nbytes, void* stream);
+
 /* Name of a status code (static string). */
 const char* ufp4_status_string(int status);
 

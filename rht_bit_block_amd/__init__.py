@@ -35,7 +35,7 @@ EXPORTED = [
     "ufp4_gemm_fprop_grouped", "ufp4_gemm_dgrad_grouped", "ufp4_gemm_wgrad_grouped",
     "ufp4_gemm_workspace_bytes", "ufp4_gemm_ws",
     "ufp4_transpose_qtensor", "ufp4_codes_bytes", "ufp4_scales_bytes",
-    "ufp4_philox_fill", "ufp4_status_string",
+    "ufp4_philox_fill", "ufp4_stream_copy", "ufp4_status_string",
 ]
 
 
@@ -124,6 +124,7 @@ def _lib():
             "ufp4_gemm_ws": [i32, qtp, qtp, i32, i64p, vp, i64, vp, ctypes.c_size_t, vp],
             "ufp4_transpose_qtensor": [qtp, vp, vp, vp],
             "ufp4_philox_fill": [u64, u32, u64, i64, vp, vp],
+            "ufp4_stream_copy": [vp, vp, i64, vp],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -487,6 +488,23 @@ def ufp4_philox_fill(seed, stream_id, first, n, device="cuda"):
                                  _stream(out))
     _check("ufp4_philox_fill", st)
     return out
+
+
+def ufp4_stream_copy(src, dst):
+    """Copy the bytes of the contiguous device tensor src into dst (same
+    number of bytes) with the library's streaming copy kernel."""
+    if not (src.is_cuda and dst.is_cuda):
+        raise ValueError("ufp4_stream_copy: src and dst must be device tensors")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("ufp4_stream_copy: src and dst must be contiguous")
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("ufp4_stream_copy: src and dst differ in size")
+    if src.device != dst.device:
+        raise ValueError("ufp4_stream_copy: src and dst are on different devices")
+    st = _lib().ufp4_stream_copy(_ptr(src), _ptr(dst), n, _stream(dst))
+    _check("ufp4_stream_copy", st)
+    return dst
 
 
 def ufp4_codes_bytes(P, K):

@@ -629,6 +629,17 @@ int ufp4_transpose_qtensor(const ufp4_qtensor* src, uint8_t* dst_codes, void* ds
                                      (hipStream_t)stream));
 }
 
+int ufp4_stream_copy(const void* src, void* dst, int64_t nbytes, void* stream) {
+  if (nbytes < 0) return UFP4_ERR_INVALID_ARG;
+  if (nbytes == 0) return UFP4_OK;
+  if (!src || !dst) return UFP4_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) % 16)
+    return UFP4_ERR_INVALID_ARG;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + (uintptr_t)nbytes && b < a + (uintptr_t)nbytes) return UFP4_ERR_INVALID_ARG;
+  return hip_status(launch_stream_copy(src, dst, nbytes, (hipStream_t)stream));
+}
+
 int ufp4_philox_fill(uint64_t seed, uint32_t stream_id, uint64_t first, int64_t n,
                      uint16_t* out, void* stream) {
   if (!out || n < 0) return UFP4_ERR_INVALID_ARG;

@@ -191,6 +191,23 @@ __global__ void k_zero_c(float* c, int64_t rows, int64_t cols, int64_t ld) {
   }
 }
 
+// Streaming copy of n16 16-byte vectors: one vector per thread and a grid
+// that covers the buffer (a grid-stride loop only past 2^24 workgroups), with
+// non-temporal loads and stores (nothing is reused); the bytes past the last
+// whole vector are copied one by one.  Measured on gfx950 (1 GiB): this form
+// reaches 6.5 TB/s, grid-stride loops over 2048 - 65536 workgroups with one to
+// eight vectors in flight per thread 4.3 - 5.6 TB/s.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void k_stream_copy(const u32x4* __restrict__ src,
+                                                     u32x4* __restrict__ dst, int64_t n16,
+                                                     const uint8_t* __restrict__ tsrc,
+                                                     uint8_t* __restrict__ tdst, int tail) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+  if (blockIdx.x == 0 && threadIdx.x < tail) tdst[threadIdx.x] = tsrc[threadIdx.x];
+}
+
 int grid_for(int64_t work, int threads) {
   int64_t b = (work + threads - 1) / threads;
   if (b > 65536) b = 65536;
@@ -238,6 +255,20 @@ hipError_t launch_zero_c(float* c, int64_t rows, int64_t cols, int64_t ld, hipSt
   if (rows == 0 || cols == 0) return hipSuccess;
   hipLaunchKernelGGL(k_zero_c, dim3(grid_for(rows * cols, 256)), dim3(256), 0, s, c, rows, cols,
                      ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t nbytes, hipStream_t s) {
+  if (nbytes == 0) return hipSuccess;
+  const int64_t n16 = nbytes / 16;
+  const int tail = (int)(nbytes - n16 * 16);
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > ((int64_t)1 << 24)) blocks = (int64_t)1 << 24;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_stream_copy, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16,
+                     static_cast<const uint8_t*>(src) + n16 * 16,
+                     static_cast<uint8_t*>(dst) + n16 * 16, tail);
   return hipGetLastError();
 }
 

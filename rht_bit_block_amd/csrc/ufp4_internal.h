@@ -212,6 +212,7 @@ hipError_t launch_transpose(const uint8_t* codes, const void* scales, int64_t P,
 // Writes zeros into C [rows][ld] (columns 0 .. cols-1): a GEMM whose shared
 // dimension is empty.
 hipError_t launch_zero_c(float* c, int64_t rows, int64_t cols, int64_t ld, hipStream_t s);
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t nbytes, hipStream_t s);
 hipError_t launch_philox_fill(uint64_t seed, uint32_t stream_id, uint64_t first, int64_t n,
                               uint16_t* out, hipStream_t s);
 

@@ -202,6 +202,20 @@ def test_segmented_and_misc_errors():
     assert lib.ufp4_dequant(ctypes.byref(q), None, 64, None) == U.UFP4_ERR_INVALID_ARG
 
 
+def test_stream_copy_errors():
+    lib = U.lib_handle()
+    vp = ctypes.c_void_p
+    assert lib.ufp4_stream_copy(None, None, 0, None) == U.UFP4_OK              # nothing to do
+    assert lib.ufp4_stream_copy(vp(FAKE), vp(FAKE + 4096), -1, None) == U.UFP4_ERR_INVALID_ARG
+    assert lib.ufp4_stream_copy(None, vp(FAKE), 16, None) == U.UFP4_ERR_INVALID_ARG
+    assert lib.ufp4_stream_copy(vp(FAKE), None, 16, None) == U.UFP4_ERR_INVALID_ARG
+    assert lib.ufp4_stream_copy(vp(FAKE + 8), vp(FAKE + 4096), 16, None) == U.UFP4_ERR_INVALID_ARG
+    assert lib.ufp4_stream_copy(vp(FAKE), vp(FAKE + 4104), 16, None) == U.UFP4_ERR_INVALID_ARG
+    # overlapping ranges, either order
+    assert lib.ufp4_stream_copy(vp(FAKE), vp(FAKE + 64), 128, None) == U.UFP4_ERR_INVALID_ARG
+    assert lib.ufp4_stream_copy(vp(FAKE + 64), vp(FAKE), 128, None) == U.UFP4_ERR_INVALID_ARG
+
+
 def test_size_helpers():
     cfg = U.make_cfg()
     assert U.ufp4_codes_bytes(8192, 2048) == 8192 * 1024

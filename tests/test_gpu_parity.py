@@ -33,6 +33,22 @@ def test_philox_fill_matches_oracle():
         assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("nbytes", [1, 15, 16, 17, 4096, 65536 * 16 + 5, (64 << 20) + 48 + 9])
+def test_stream_copy(nbytes):
+    """The streaming copy reproduces every byte (whole 16-byte vectors, one
+    per thread, and the bytes past the last vector) and writes nothing past
+    the end."""
+    _print_case("stream copy", nbytes)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(nbytes)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+    guard = torch.full((nbytes + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    dst = guard[:nbytes]
+    U.ufp4_stream_copy(src, dst)
+    assert torch.equal(dst, src)
+    assert torch.all(guard[nbytes:] == 0xA5)
+
+
 @pytest.mark.parametrize("n,b", NB)
 @pytest.mark.parametrize("grid", GRIDS)
 @pytest.mark.parametrize("rnd", [U.UFP4_RTNE, U.UFP4_SR])
