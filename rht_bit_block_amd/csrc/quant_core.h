@@ -849,10 +849,14 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantLaunch q) {
 // outputs.  Hadamard chunks along the row must fit the tile width: tiles are
 // 128 x 64 for n <= 64 and 128 x 128 for n = 128 (dual_tile_cols).
 //
-// A workgroup takes two consecutive tiles.  When both are whole (no ragged
-// rows or columns) the second tile's HBM loads are issued together with the
-// first's and are in flight while the first is quantized; otherwise each
-// tile is loaded and staged in turn.
+// A workgroup takes one tile, or two consecutive tiles (dual_tiles_per_wg).
+// With two, when both are whole (no ragged rows or columns) the second tile's
+// HBM loads are issued together with the first's and are in flight while the
+// first is quantized; otherwise each tile is loaded and staged in turn.
+// Measured on gfx950: the short RTNE tiles of n <= 64 (128 x 64) run 17-35 %
+// faster two to a workgroup, while SR tiles (more work per tile) and n = 128
+// tiles (128 x 128) run 2-9 % faster one to a workgroup, with twice the
+// workgroups.
 // ---------------------------------------------------------------------------
 struct DualTile {
   int64_t seg0, L, k0, p0;
@@ -1024,6 +1028,8 @@ __device__ __forceinline__ void dual_quantize(const QuantLaunch& q, const RowSid
   }
 }
 
+constexpr int dual_tiles_per_wg(int n, int rnd) { return (n == 128 || (rnd & 1)) ? 1 : 2; }
+
 template <int W, int B, int N, int GRID, int RND>
 __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide rside) {
   static_assert(W % 16 == 0, "column segments of whole 8-pair swizzle groups");
@@ -1032,23 +1038,31 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide 
   static_assert(N <= TP, "row-wise Hadamard chunks must fit the tile width");
   static_assert(stage_tasks<TP>() * kThreads == (kTK / 2) * (TP / 8), "staging tasks per thread");
   const int total = q.tile_start[q.nseg];
-  const int b0 = 2 * blockIdx.x;
-  const bool two = b0 + 1 < total;
+  constexpr int kTiles = dual_tiles_per_wg(N, RND);
+  const int b0 = kTiles * blockIdx.x;
+  const bool two = kTiles == 2 && b0 + 1 < total;
   const DualTile d0 = dual_tile<TP>(q, b0);
   const DualTile d1 = dual_tile<TP>(q, two ? b0 + 1 : b0);
   const bool whole = d0.krows == kTK && d0.pcols == TP && d1.krows == kTK && d1.pcols == TP;
   if (whole) {
-    DualRegs<TP> r0, r1;
+    DualRegs<TP> r0;
     load_whole<TP>(q, d0, r0);
-    load_whole<TP>(q, d1, r1);   // (the first tile again when there is no second)
-    stage_whole<TP>(r0, tile);
-    __syncthreads();
-    dual_quantize<W, B, N, GRID, RND, TP>(q, rside, d0, tile);
-    if (two) {
-      __syncthreads();   // every lane is done reading the first tile
-      stage_whole<TP>(r1, tile);
+    if constexpr (kTiles == 2) {
+      DualRegs<TP> r1;
+      load_whole<TP>(q, d1, r1);   // (the first tile again when there is no second)
+      stage_whole<TP>(r0, tile);
       __syncthreads();
-      dual_quantize<W, B, N, GRID, RND, TP>(q, rside, d1, tile);
+      dual_quantize<W, B, N, GRID, RND, TP>(q, rside, d0, tile);
+      if (two) {
+        __syncthreads();   // every lane is done reading the first tile
+        stage_whole<TP>(r1, tile);
+        __syncthreads();
+        dual_quantize<W, B, N, GRID, RND, TP>(q, rside, d1, tile);
+      }
+    } else {
+      stage_whole<TP>(r0, tile);
+      __syncthreads();
+      dual_quantize<W, B, N, GRID, RND, TP>(q, rside, d0, tile);
     }
   } else {
     load_stage_any<TP>(q, d0, tile);
@@ -1242,7 +1256,9 @@ template <int W, int B, int N, int G, int R>
 hipError_t run_dual(const QuantLaunch& q, const RowSide& r, hipStream_t s) {
   const int total = q.tile_start[q.nseg];
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_quant_dual<W, B, N, G, R>), dim3((total + 1) / 2), dim3(kThreads), 0, s,
+  constexpr int kTiles = dual_tiles_per_wg(N, R);
+  hipLaunchKernelGGL((k_quant_dual<W, B, N, G, R>), dim3((total + kTiles - 1) / kTiles),
+                     dim3(kThreads), 0, s,
                      q, r);
   return hipGetLastError();
 }
