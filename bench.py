@@ -63,9 +63,9 @@ MEASURED_TRAFFIC = {
     ("moe16", "fprop"): (_GEMM_SRC, "7ae132ace46eff1f", 1564996.9, 1590543.6),
     ("moe16", "dgrad"): (_GEMM_SRC, "7ae132ace46eff1f", 717470.9, 5258969.6),
     ("moe16", "wgrad"): (_GEMM_SRC, "7ae132ace46eff1f", 1228766.4, 524362.9),
-    ("moe16", "quant_x"): (_QUANT_SRC, "60f581ffbebd6fab", 1314699.2, 2077052.7),
-    ("moe16", "quant_w"): (_QUANT_SRC, "60f581ffbebd6fab", 123024.7, 185821.2),
-    ("moe16", "quant_dy"): (_QUANT_SRC, "60f581ffbebd6fab", 394842.9, 592626.8),
+    ("moe16", "quant_x"): (_QUANT_SRC, "1db68f7e106e33ee", 1314699.2, 2077052.7),
+    ("moe16", "quant_w"): (_QUANT_SRC, "1db68f7e106e33ee", 123024.7, 185821.2),
+    ("moe16", "quant_dy"): (_QUANT_SRC, "1db68f7e106e33ee", 394842.9, 592626.8),
 }
 
 

@@ -853,10 +853,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(QuantLaunch q) {
 // With two, when both are whole (no ragged rows or columns) the second tile's
 // HBM loads are issued together with the first's and are in flight while the
 // first is quantized; otherwise each tile is loaded and staged in turn.
-// Measured on gfx950: the short RTNE tiles of n <= 64 (128 x 64) run 17-35 %
-// faster two to a workgroup, while SR tiles (more work per tile) and n = 128
-// tiles (128 x 128) run 2-9 % faster one to a workgroup, with twice the
-// workgroups.
+// Measured on gfx950: the 128 x 64 tiles of n <= 64 run 17-35 % (RTNE) and
+// 0-2 % (SR) faster two to a workgroup, while the 128 x 128 tiles of n = 128
+// run 2-9 % faster one to a workgroup, with twice the workgroups and without
+// the second tile's registers.
 // ---------------------------------------------------------------------------
 struct DualTile {
   int64_t seg0, L, k0, p0;
@@ -1028,7 +1028,7 @@ __device__ __forceinline__ void dual_quantize(const QuantLaunch& q, const RowSid
   }
 }
 
-constexpr int dual_tiles_per_wg(int n, int rnd) { return (n == 128 || (rnd & 1)) ? 1 : 2; }
+constexpr int dual_tiles_per_wg(int n) { return n == 128 ? 1 : 2; }
 
 template <int W, int B, int N, int GRID, int RND>
 __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide rside) {
@@ -1038,7 +1038,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(QuantLaunch q, RowSide 
   static_assert(N <= TP, "row-wise Hadamard chunks must fit the tile width");
   static_assert(stage_tasks<TP>() * kThreads == (kTK / 2) * (TP / 8), "staging tasks per thread");
   const int total = q.tile_start[q.nseg];
-  constexpr int kTiles = dual_tiles_per_wg(N, RND);
+  constexpr int kTiles = dual_tiles_per_wg(N);
   const int b0 = kTiles * blockIdx.x;
   const bool two = kTiles == 2 && b0 + 1 < total;
   const DualTile d0 = dual_tile<TP>(q, b0);
@@ -1256,7 +1256,7 @@ template <int W, int B, int N, int G, int R>
 hipError_t run_dual(const QuantLaunch& q, const RowSide& r, hipStream_t s) {
   const int total = q.tile_start[q.nseg];
   if (total == 0) return hipSuccess;
-  constexpr int kTiles = dual_tiles_per_wg(N, R);
+  constexpr int kTiles = dual_tiles_per_wg(N);
   hipLaunchKernelGGL((k_quant_dual<W, B, N, G, R>), dim3((total + kTiles - 1) / kTiles),
                      dim3(kThreads), 0, s,
                      q, r);
