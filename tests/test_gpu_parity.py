@@ -972,10 +972,10 @@ def test_grouped_wgrad_pow2(grid):
 @pytest.mark.parametrize("rnd", [U.UFP4_RTNE, U.UFP4_SR])
 @pytest.mark.parametrize("b", [16, 32])
 def test_quant_dual_n128(grid, rnd, b):
-    """Dual-axis calls with n = 128 (128 x 128 tiles): 384 x 256 (six tiles, the
-    workgroup pairs whole) and 384 x 128 (three tiles, the last workgroup with
-    one), and expert segments of 256, 0 and 128 rows, against the oracle's
-    row-wise and (per-segment) column-wise quantizations."""
+    """Dual-axis calls with n = 128 (128 x 128 tiles, one per workgroup; both
+    dimensions are multiples of 128, so every tile is whole): 384 x 256 (six
+    tiles) and 384 x 128 (three), and expert segments of 256, 0 and 128 rows,
+    against the oracle's row-wise and (per-segment) column-wise quantizations."""
     _print_case("dual n128", grid, rnd, b)
     cr = U.make_cfg(grid, rnd, U.UFP4_SCALE_F32, 1, b, 128, sign_seed=61, sr_seed=5, sr_stream=0)
     cc = U.make_cfg(grid, rnd, U.UFP4_SCALE_F32, 1, b, 128, sign_seed=62, sr_seed=5, sr_stream=1)
